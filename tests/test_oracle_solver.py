@@ -1,0 +1,167 @@
+"""Pins of the scipy parameter reference (oracle/solver_ref.py).
+
+What fixes the numbers: Table 3 of the arXiv page (exact Theorem-4 pairs and
+the Algorithm-1 surrogates, App. B), worked examples stated in the text,
+exhaustive enumeration of every S-subset at tiny N (the exact law of R, no
+formula reused), Corollary 5 minimality, and simulation of the rank of the
+t-th sampled entry.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import comb
+
+from oracle import method_ref, solver_ref
+
+
+def load_table3(golden_dir):
+    rows = []
+    with open(os.path.join(golden_dir, "table3.tsv")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            p = line.split()
+            rows.append(dict(N=1 << int(p[0]), k=int(p[1]), S=int(p[2]), t_star=int(p[3]),
+                             t_fast=int(p[4]), M_star=int(p[5]), M_fast=int(p[6]),
+                             pf_exact=float(p[7]), pf_fast=float(p[8])))
+    return rows
+
+
+def same_to_3_digits(value, printed):
+    return float(f"{value:.2e}") == printed
+
+
+def test_table3_exact_parameters(golden_dir):
+    rows = load_table3(golden_dir)
+    assert len(rows) == 21
+    for r in rows:
+        p = solver_ref.solve(r["N"], r["k"], 1e-3, S=r["S"])
+        assert p.t_star == r["t_star"], r
+        assert p.M_star == r["M_star"], r
+        pf = (solver_ref.hyp_sf(p.t_star - 1, r["N"], r["k"] - 1, r["S"])
+              + solver_ref.hyp_cdf(p.t_star - 1, r["N"], p.M_star, r["S"]))
+        assert same_to_3_digits(pf, r["pf_exact"]), (r, pf)
+
+
+def test_table3_surrogate_parameters(golden_dir):
+    for r in load_table3(golden_dir):
+        t, M = solver_ref.surrogate_params(r["N"], r["k"], r["S"], 1e-3)
+        assert (t, M) == (r["t_fast"], r["M_fast"]), r
+        pf = (solver_ref.hyp_sf(t - 1, r["N"], r["k"] - 1, r["S"])
+              + solver_ref.hyp_cdf(t - 1, r["N"], M, r["S"]))
+        assert same_to_3_digits(pf, r["pf_fast"]), (r, pf)
+
+
+def test_worked_examples(golden_dir):
+    ex = json.load(open(os.path.join(golden_dir, "worked_examples.json")))
+    e = ex["z_example"]
+    p = solver_ref.solve(1 << 24, 32, e["eps"])
+    assert abs(p.z - e["z"]) <= e["abs_tol"]
+    e = ex["sample_size_example"]
+    raw, S = solver_ref.s_rule(e["N"], e["k"], 1e-3)
+    assert abs(raw - e["S_star_approx"]) <= e["rel_tol"] * e["S_star_approx"]
+    assert S == solver_ref.S_MIN_DEFAULT  # the clamp then lifts it to S_min
+    e = ex["sparse_t1_example"]
+    # S is not printed there; 2^14 (the arXiv page's S_min) is the reading used
+    N, S = 1 << e["log2N"], 1 << 14
+    t = solver_ref.t_star(N, e["k"], S, e["eps"] / 2)
+    assert t == e["t_star"]
+    assert abs(solver_ref.hyp_sf(t - 1, N, e["k"] - 1, S) - e["p_recall"]) <= e["abs_tol"]
+    e = ex["k1_exact"]
+    for N, S in ((1 << 20, 8192), (1 << 30, 32768)):
+        t = solver_ref.t_star(N, e["k"], S, 5e-4)
+        assert t == e["t"]
+        assert solver_ref.hyp_sf(t - 1, N, 0, S) == 0.0  # Pr(R < 1) = 0
+
+
+def exhaustive_rank_law(N, S, t):
+    """Exact distribution of R (rank of the t-th best sampled entry) over all
+    C(N, S) equally likely subsets, by enumeration."""
+    counts = np.zeros(N + 2, dtype=np.int64)
+    for sub in itertools.combinations(range(1, N + 1), S):
+        counts[sub[t - 1]] += 1
+    return counts / counts.sum()
+
+
+@pytest.mark.parametrize("N,S", [(9, 3), (12, 4), (13, 5)])
+def test_failure_probabilities_match_enumeration(N, S):
+    for t in range(1, S + 1):
+        law = exhaustive_rank_law(N, S, t)
+        cdf = np.cumsum(law)
+        for k in range(1, N + 1):
+            p_rec = cdf[k - 1]  # Pr(R < k) = Pr(R <= k-1)
+            assert math.isclose(solver_ref.hyp_sf(t - 1, N, k - 1, S), p_rec, abs_tol=1e-12)
+            for M in range(k, N + 1):
+                p_ovf = 1.0 - cdf[M]
+                assert math.isclose(solver_ref.hyp_cdf(t - 1, N, M, S), p_ovf, abs_tol=1e-12)
+        # P2 Lemma 1 moments, against the enumerated law
+        r = np.arange(N + 2)
+        mean = float((law * r).sum())
+        var = float((law * (r - mean) ** 2).sum())
+        assert math.isclose(mean, (N + 1) * t / (S + 1), rel_tol=1e-12)
+        v = t * (S - t + 1) * (N + 1) * (N - S) / ((S + 1) ** 2 * (S + 2))
+        assert math.isclose(var, v, rel_tol=1e-9, abs_tol=1e-12)
+        # P2 Lemma 1 PMF (negative hypergeometric)
+        for rr in range(t, N - S + t + 1):
+            pmf = comb(rr - 1, t - 1, exact=True) * comb(N - rr, S - t, exact=True) / comb(N, S, exact=True)
+            assert math.isclose(law[rr], pmf, rel_tol=1e-12)
+
+
+@pytest.mark.parametrize("N,k,S,eps", [(1 << 22, 32, 32768, 1e-3), (1 << 26, 1024, 32768, 1e-3),
+                                       (1 << 30, 32768, 32768, 1e-3), (1 << 20, 64, 32768, 1e-3 / 1024),
+                                       (1 << 24, 2048, 20650, 1e-3)])
+def test_corollary5_minimality(N, k, S, eps):
+    ea = eb = eps / 2
+    t = solver_ref.t_star(N, k, S, ea)
+    M = solver_ref.m_star(N, k, S, t, eb)
+    assert solver_ref.hyp_sf(t - 1, N, k - 1, S) <= ea
+    if t > 1:
+        assert solver_ref.hyp_sf(t - 2, N, k - 1, S) > ea  # t*-1 breaks the recall budget
+    assert solver_ref.hyp_cdf(t - 1, N, M, S) <= eb
+    if M > k:
+        assert solver_ref.hyp_cdf(t - 1, N, M - 1, S) > eb  # M*-1 breaks the overflow budget
+
+
+def test_operating_point_is_within_budget_for_the_workloads():
+    # (N, k, eps) of the five workloads (per-row eps for the batched one)
+    for N, k, eps in [(1 << 22, 32, 1e-3), (1 << 26, 32, 1e-3), (1 << 26, 1024, 1e-3),
+                      (1 << 26, 32768, 1e-3), (50331648, 131072, 1e-3), (1 << 30, 32, 1e-3),
+                      (1 << 30, 1 << 15, 1e-3), (1 << 30, 1 << 19, 1e-3), (1 << 20, 64, 1e-3 / 1024),
+                      (1 << 30, 1 << 19, 1e-4)]:
+        p = solver_ref.solve(N, k, eps)
+        assert p.p_recall + p.p_overflow <= eps
+        assert p.M >= p.M_cf  # the closed form of P2 Cor. 4 is a lower bound here
+        assert p.M == p.M_star
+
+
+def test_rank_moments_by_simulation():
+    # P2 Lemma 1 at the first workload's size: mean and variance of R within 5 standard errors
+    N, S, t, n = 1 << 22, 32768, 4, 1500
+    R = method_ref.simulate_rank(N, S, t, n, np.random.default_rng(2024))
+    mean = (N + 1) * t / (S + 1)
+    var = t * (S - t + 1) * (N + 1) * (N - S) / ((S + 1) ** 2 * (S + 2))
+    assert abs(R.mean() - mean) <= 5 * math.sqrt(var / n)
+    m4 = float(((R - R.mean()) ** 4).mean())
+    assert abs(R.var() - var) <= 5 * math.sqrt(max(m4 - var * var, 0.0) / n)
+
+
+def test_rank_pmf_chi_square():
+    # P2 Lemma 1 PMF at N = 64, S = 8, t = 3, simulated with numpy permutations
+    from scipy.stats import chi2
+    N, S, t, n = 64, 8, 3, 60000
+    rng = np.random.default_rng(99)
+    keys = rng.random((n, N))
+    sub = np.argpartition(keys, S, axis=1)[:, :S] + 1  # a uniform S-subset of ranks 1..N per row
+    R = np.sort(sub, axis=1)[:, t - 1]
+    obs = np.bincount(R, minlength=N + 1)
+    rr = np.arange(t, N - S + t + 1)
+    pmf = np.array([comb(r - 1, t - 1, exact=True) * comb(N - r, S - t, exact=True) for r in rr],
+                   dtype=np.float64) / comb(N, S, exact=True)
+    exp = pmf * n
+    keep = exp >= 5
+    stat = float((((obs[rr] - exp) ** 2) / exp)[keep].sum())
+    assert stat < chi2.ppf(0.9999, int(keep.sum()) - 1)
