@@ -1,0 +1,182 @@
+/*
+ * profk.h: C ABI of the MI355X (gfx950) Prof-K exact top-k library.
+ *
+ * The method is "Prof-K: Probabilistic One-Pass Filtering for Efficient
+ * Top-k Selection" (arXiv HTML page, cited below as P1; its earlier version
+ * on the bittide mirror is P2).  A uniform sample of S indices sets a
+ * threshold tau at the t-th largest sampled entry; one streaming pass keeps
+ * every entry at or above tau in a candidate buffer of capacity M and counts
+ * them exactly (R); an exact selection on the buffer gives the top k.  When
+ * the run-time check k <= R <= M fails the sample is redrawn; after the last
+ * attempt an exact full-tensor selection runs.  The result is always the
+ * exact top-k (P1 abstract, §3 stage 4).
+ *
+ * Order and ties.  The pages assume distinct entries (P1 §4 "Notation and
+ * Conventions").  This library uses the total order "larger value first,
+ * then lower index"; -0.0 and +0.0 compare equal; every NaN ranks above
+ * +inf and NaNs tie with each other (broken by index).  Outputs are sorted
+ * in that order; out_vals[j] is a bit copy of x[out_idx[j]].
+ *
+ * Memory.  Every x / out pointer is a DEVICE pointer owned by the caller.
+ * The library owns a workspace per (device, stream), sized O(S + M + k)
+ * (never O(N)), grown on demand and freed by profk_release().  Pointers to
+ * option / parameter / stats structs are HOST pointers.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Work is enqueued on it.  The exact-mode call synchronises the
+ * stream once per attempt to read the count R (P1 App. D "Cost of the
+ * Run-Time Check"); on return the outputs are complete.
+ *
+ * Errors.  Every entry point returns a status code; nothing throws across
+ * the ABI.  profk_strerror() gives a message (HIP errors include the HIP
+ * error string of the failing call, kept per thread).
+ *
+ * Limits.  N < 2^32 per row (indices are 32-bit inside the keys);
+ * N >= 2^32 returns PROFK_EUNSUPPORTED.
+ */
+#ifndef PROFK_H
+#define PROFK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PROFK_OK 0
+#define PROFK_EINVAL (-1)       /* bad argument (null pointer, k < 1, k > N, eps outside (0,1), ld < N ...) */
+#define PROFK_EUNSUPPORTED (-2) /* N >= 2^32 per row */
+#define PROFK_ENOMEM (-3)       /* workspace allocation failed */
+#define PROFK_EHIP (-4)         /* a HIP runtime call failed */
+#define PROFK_EINTERNAL (-5)    /* a device-side consistency check failed */
+
+/* Overrides for tests and experiments.  Zero-initialise for defaults. */
+typedef struct profk_options {
+  int64_t s_override;     /* > 0: use this sample size S instead of the rule */
+  int64_t s_min;          /* 0: 32768 (P2 §4 "Optimal Sample Size") */
+  int64_t s_max;          /* 0: 131072 (same place) */
+  double s_prefactor;     /* <= 0: 1.0; c in S*_raw = c (k (N-k))^(1/3) */
+  int64_t force_t;        /* > 0: threshold rank t instead of Theorem 4's t* */
+  int64_t force_M;        /* > 0: buffer capacity M (>= k) instead of M* */
+  int32_t max_attempts;   /* < 0 or unset (0 with use_max_attempts = 0): 6 (P1 §3 stage 4) */
+  int32_t use_max_attempts; /* nonzero: max_attempts is taken as given (0 = straight to the exact path) */
+  int32_t force_fallback; /* nonzero: skip the sampled attempts, run the exact full selection */
+  int32_t timing;         /* nonzero: time the filter kernel with HIP events (stats.filter_ms) */
+} profk_options;
+
+/* The parameter choice for one (N, k, eps) (P1 §4 Theorem 4; P2 §4). */
+typedef struct profk_params {
+  int64_t N, k;
+  double eps;
+  double eps_a, eps_b; /* budget split eps/2 + eps/2 */
+  double z_a;          /* Phi^-1(1 - eps_a) */
+  double z;            /* z_A + z_B (P2 Algorithm 1) */
+  double S_raw;        /* c (k (N-k))^(1/3) before the clamp */
+  int64_t S;           /* sample size used */
+  int64_t t_star;      /* P1 Eq. 7 */
+  int64_t M_star;      /* P1 Eq. 7 */
+  double M_cf;         /* P2 Corollary 4, Eq. 12 */
+  int64_t t_eq6;       /* P2 Eq. 6 (reported only) */
+  int64_t t, M;        /* operating pair: t = t*, M = max(M*, ceil(M_cf)) unless forced */
+  double p_recall;     /* Pr(R < k) at (t, M), P1 Eq. 5 */
+  double p_overflow;   /* Pr(R > M) at (t, M), P1 Eq. 6 */
+  double E_R, Var_R;   /* P2 Lemma 1, Eq. 2 */
+  int32_t direct_exact; /* 1: sampling cannot pay off here; the call runs the exact full selection */
+  int32_t reserved;
+} profk_params;
+
+#define PROFK_STATS_ATTEMPTS 8
+typedef struct profk_stats {
+  int32_t attempts;       /* sampled attempts made */
+  int32_t fallback;       /* 1: the exact full selection produced the output */
+  int64_t S, t, M;        /* operating parameters */
+  int64_t R[PROFK_STATS_ATTEMPTS];         /* exact filter count per attempt (row 0 when batched) */
+  int32_t fail_mode[PROFK_STATS_ATTEMPTS]; /* 0 ok, 1 R < k, 2 R > M */
+  uint64_t workspace_bytes; /* bytes of device workspace held for this (device, stream) */
+  double filter_ms;       /* filter kernel time of the last attempt (options.timing) */
+  int64_t rows_retried;   /* batched: rows that needed more than one attempt */
+  int64_t rows_fallback;  /* batched: rows finished by the exact full selection */
+} profk_stats;
+
+/*
+ * profk_topk: exact top-k of one flat fp32 tensor x[0..N) (P1 §3, Algorithm
+ * "The Prof-K Algorithm", stages 1-4, with the retry of stage 4).
+ *   x        device, N floats, any alignment
+ *   N        1 <= N < 2^32
+ *   k        1 <= k <= N
+ *   eps      failure budget per attempt, 0 < eps < 1 (P1 §4 Theorem 4)
+ *   seed     64-bit seed of the sampler's Philox stream; attempt a uses
+ *            counter space a.  The output does not depend on it.
+ *   out_vals device, k floats; out_idx device, k int64 (sorted, see top)
+ */
+int profk_topk(const float* x, int64_t N, int64_t k, double eps, uint64_t seed, float* out_vals,
+               int64_t* out_idx, void* stream);
+
+/* profk_topk with overrides (opt may be NULL) and statistics (st may be NULL). */
+int profk_topk_ex(const float* x, int64_t N, int64_t k, double eps, uint64_t seed, float* out_vals,
+                  int64_t* out_idx, void* stream, const profk_options* opt, profk_stats* st);
+
+/*
+ * profk_topk_batched: row-wise exact top-k of B rows (P1 §3: the procedure
+ * is applied to each batch element; App. C: per-row threshold, buffer and
+ * counter).  Row r is x[r*ld_x .. r*ld_x + N).  The budget is split eps/B
+ * per row so that the whole call meets eps (P1 App. E.2).  Only the rows
+ * that fail the check are redrawn.
+ *   out_vals device B*k floats, out_idx device B*k int64 column indices in [0, N)
+ */
+int profk_topk_batched(const float* x, int64_t B, int64_t N, int64_t ld_x, int64_t k, double eps,
+                       uint64_t seed, float* out_vals, int64_t* out_idx, void* stream);
+
+int profk_topk_batched_ex(const float* x, int64_t B, int64_t N, int64_t ld_x, int64_t k, double eps,
+                          uint64_t seed, float* out_vals, int64_t* out_idx, void* stream,
+                          const profk_options* opt, profk_stats* st);
+
+/*
+ * profk_solve: host-only parameter choice (P1 §4 Theorem 4 / Eq. 5-7; the
+ * S rule and closed forms of P2 §4 Theorem 5, Corollary 4, Algorithm 1).
+ * Memoised per (N, k, eps, options) (P1 §4 "Fast Approximate Parameter
+ * Computation": parameters are cached per configuration).  No GPU needed.
+ */
+int profk_solve(int64_t N, int64_t k, double eps, const profk_options* opt, profk_params* out);
+
+/*
+ * Stage entry points: each runs one stage of the hot path on the GPU, for
+ * inspection and parity tests.  All array pointers are device pointers.
+ *
+ * profk_stage_sample: stage 1 (P1 §3): the S distinct indices of the
+ *   sample of (seed, attempt), in unspecified order, into out_idx[0..S).
+ *   1 <= S <= N/2.
+ */
+int profk_stage_sample(const float* x, int64_t N, int64_t S, uint64_t seed, int32_t attempt,
+                       int64_t* out_idx, void* stream);
+
+/*
+ * profk_stage_threshold: stages 1-2 (P1 §3): tau = the t-th entry, in the
+ *   total order, of the sample of (seed, attempt).  out_tau_val (1 float),
+ *   out_tau_idx (1 int64).  1 <= t <= S <= N/2.
+ */
+int profk_stage_threshold(const float* x, int64_t N, int64_t S, int64_t t, uint64_t seed,
+                          int32_t attempt, float* out_tau_val, int64_t* out_tau_idx, void* stream);
+
+/*
+ * profk_stage_filter: stage 3 (P1 §3; App. C "The Filter Kernel"): with the
+ *   given tau = (tau_val, tau_idx), out_R[0] = R = number of entries at or
+ *   before tau in the total order (exact, even past capacity), and the
+ *   indices of min(R, M) of them in out_cand_idx[0..min(R,M)) (unspecified
+ *   order; which ones are kept on overflow is unspecified).
+ */
+int profk_stage_filter(const float* x, int64_t N, float tau_val, int64_t tau_idx, int64_t M,
+                       int64_t* out_cand_idx, int64_t* out_R, void* stream);
+
+/* Message for a status code (thread-local detail for PROFK_EHIP). */
+const char* profk_strerror(int code);
+
+/* Frees every cached workspace (all devices and streams).  Not thread-safe
+ * against concurrent calls. */
+void profk_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PROFK_H */

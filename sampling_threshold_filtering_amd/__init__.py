@@ -1,0 +1,241 @@
+"""Prof-K exact top-k for MI355X (gfx950): thin Python binding over libprofk.so.
+
+Every step of the selection runs in the library's HIP kernels; this module only
+marshals arguments.  PyTorch supplies device memory and the stream handle.
+The library must have been built (``python -m
+sampling_threshold_filtering_amd.build_native`` or ``__graft_entry__.build()``);
+there is no fallback of any kind when it is missing.
+
+Functions mirror include/profk.h:
+  topk(x, k, eps=1e-3, seed=0, options=None, stats=False)
+  topk_batched(x2d, k, eps=1e-3, seed=0, options=None, stats=False)
+  solve(N, k, eps=1e-3, options=None) -> dict
+  stage_sample / stage_threshold / stage_filter  (one stage each, for inspection)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libprofk.so")
+
+PROFK_OK = 0
+PROFK_EINVAL = -1
+PROFK_EUNSUPPORTED = -2
+PROFK_ENOMEM = -3
+PROFK_EHIP = -4
+PROFK_EINTERNAL = -5
+
+STATS_ATTEMPTS = 8
+
+EXPORTED = ("profk_topk", "profk_topk_ex", "profk_topk_batched", "profk_topk_batched_ex", "profk_solve",
+            "profk_stage_sample", "profk_stage_threshold", "profk_stage_filter", "profk_strerror",
+            "profk_release")
+
+
+class Options(ctypes.Structure):
+    _fields_ = [
+        ("s_override", ctypes.c_int64),
+        ("s_min", ctypes.c_int64),
+        ("s_max", ctypes.c_int64),
+        ("s_prefactor", ctypes.c_double),
+        ("force_t", ctypes.c_int64),
+        ("force_M", ctypes.c_int64),
+        ("max_attempts", ctypes.c_int32),
+        ("use_max_attempts", ctypes.c_int32),
+        ("force_fallback", ctypes.c_int32),
+        ("timing", ctypes.c_int32),
+    ]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int64), ("k", ctypes.c_int64), ("eps", ctypes.c_double),
+        ("eps_a", ctypes.c_double), ("eps_b", ctypes.c_double), ("z_a", ctypes.c_double),
+        ("z", ctypes.c_double), ("S_raw", ctypes.c_double), ("S", ctypes.c_int64),
+        ("t_star", ctypes.c_int64), ("M_star", ctypes.c_int64), ("M_cf", ctypes.c_double),
+        ("t_eq6", ctypes.c_int64), ("t", ctypes.c_int64), ("M", ctypes.c_int64),
+        ("p_recall", ctypes.c_double), ("p_overflow", ctypes.c_double), ("E_R", ctypes.c_double),
+        ("Var_R", ctypes.c_double), ("direct_exact", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [
+        ("attempts", ctypes.c_int32), ("fallback", ctypes.c_int32),
+        ("S", ctypes.c_int64), ("t", ctypes.c_int64), ("M", ctypes.c_int64),
+        ("R", ctypes.c_int64 * STATS_ATTEMPTS), ("fail_mode", ctypes.c_int32 * STATS_ATTEMPTS),
+        ("workspace_bytes", ctypes.c_uint64), ("filter_ms", ctypes.c_double),
+        ("rows_retried", ctypes.c_int64), ("rows_fallback", ctypes.c_int64),
+    ]
+
+
+class ProfkError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"profk error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library():
+    """Load libprofk.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m sampling_threshold_filtering_amd.build_native`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, f64, u64, i32, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p
+    lib.profk_topk.argtypes = [vp, i64, i64, f64, u64, vp, vp, vp]
+    lib.profk_topk_ex.argtypes = [vp, i64, i64, f64, u64, vp, vp, vp, ctypes.POINTER(Options),
+                                  ctypes.POINTER(Stats)]
+    lib.profk_topk_batched.argtypes = [vp, i64, i64, i64, i64, f64, u64, vp, vp, vp]
+    lib.profk_topk_batched_ex.argtypes = [vp, i64, i64, i64, i64, f64, u64, vp, vp, vp, ctypes.POINTER(Options),
+                                          ctypes.POINTER(Stats)]
+    lib.profk_solve.argtypes = [i64, i64, f64, ctypes.POINTER(Options), ctypes.POINTER(Params)]
+    lib.profk_stage_sample.argtypes = [vp, i64, i64, u64, i32, vp, vp]
+    lib.profk_stage_threshold.argtypes = [vp, i64, i64, i64, u64, i32, vp, vp, vp]
+    lib.profk_stage_filter.argtypes = [vp, i64, ctypes.c_float, i64, i64, vp, vp, vp]
+    lib.profk_strerror.argtypes = [ctypes.c_int]
+    lib.profk_strerror.restype = ctypes.c_char_p
+    lib.profk_release.argtypes = []
+    lib.profk_release.restype = None
+    for name in ("profk_topk", "profk_topk_ex", "profk_topk_batched", "profk_topk_batched_ex", "profk_solve",
+                 "profk_stage_sample", "profk_stage_threshold", "profk_stage_filter"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != PROFK_OK:
+        msg = load_library().profk_strerror(rc).decode()
+        raise ProfkError(rc, msg)
+
+
+def make_options(**kw) -> Options:
+    o = Options()
+    for k, v in kw.items():
+        if not hasattr(o, k):
+            raise KeyError(k)
+        setattr(o, k, v)
+    return o
+
+
+def _opt_ptr(options):
+    if options is None:
+        return None
+    if isinstance(options, dict):
+        options = make_options(**options)
+    return ctypes.byref(options)
+
+
+def stats_to_dict(st: Stats) -> dict:
+    n = min(st.attempts, STATS_ATTEMPTS)
+    return dict(attempts=st.attempts, fallback=bool(st.fallback), S=st.S, t=st.t, M=st.M,
+                R=[st.R[i] for i in range(n)], fail_mode=[st.fail_mode[i] for i in range(n)],
+                workspace_bytes=st.workspace_bytes, filter_ms=st.filter_ms,
+                rows_retried=st.rows_retried, rows_fallback=st.rows_fallback)
+
+
+def _stream_ptr(torch, device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def topk(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, stats: bool = False):
+    """Exact top-k of a 1-D float32 CUDA tensor: (values, int64 indices), sorted
+    (value descending, ties to the lower index)."""
+    import torch
+    if x.dim() != 1 or x.dtype != torch.float32 or not x.is_cuda:
+        raise ValueError("x must be a 1-D float32 device tensor")
+    x = x.contiguous()
+    lib = load_library()
+    vals = torch.empty(k, dtype=torch.float32, device=x.device)
+    idx = torch.empty(k, dtype=torch.int64, device=x.device)
+    st = Stats()
+    with torch.cuda.device(x.device):
+        rc = lib.profk_topk_ex(ctypes.c_void_p(x.data_ptr()), x.numel(), k, eps, seed & (2**64 - 1),
+                               ctypes.c_void_p(vals.data_ptr()), ctypes.c_void_p(idx.data_ptr()),
+                               _stream_ptr(torch, x.device), _opt_ptr(options), ctypes.byref(st))
+    _check(rc)
+    if stats:
+        return vals, idx, stats_to_dict(st)
+    return vals, idx
+
+
+def topk_batched(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, stats: bool = False):
+    """Row-wise exact top-k of a 2-D float32 CUDA tensor (rows may be strided):
+    (values [B,k], int64 column indices [B,k])."""
+    import torch
+    if x.dim() != 2 or x.dtype != torch.float32 or not x.is_cuda:
+        raise ValueError("x must be a 2-D float32 device tensor")
+    if x.stride(1) != 1:
+        x = x.contiguous()
+    B, N = x.shape
+    ld = x.stride(0) if B > 1 else N
+    lib = load_library()
+    vals = torch.empty((B, k), dtype=torch.float32, device=x.device)
+    idx = torch.empty((B, k), dtype=torch.int64, device=x.device)
+    st = Stats()
+    with torch.cuda.device(x.device):
+        rc = lib.profk_topk_batched_ex(ctypes.c_void_p(x.data_ptr()), B, N, ld, k, eps, seed & (2**64 - 1),
+                                       ctypes.c_void_p(vals.data_ptr()), ctypes.c_void_p(idx.data_ptr()),
+                                       _stream_ptr(torch, x.device), _opt_ptr(options), ctypes.byref(st))
+    _check(rc)
+    if stats:
+        return vals, idx, stats_to_dict(st)
+    return vals, idx
+
+
+def solve(N: int, k: int, eps: float = 1e-3, options=None) -> dict:
+    """Host-only parameter choice (no GPU needed)."""
+    p = Params()
+    _check(load_library().profk_solve(N, k, eps, _opt_ptr(options), ctypes.byref(p)))
+    return {name: getattr(p, name) for name, _ in Params._fields_ if name != "reserved"}
+
+
+def stage_sample(x, S: int, seed: int = 0, attempt: int = 0):
+    """The S sampled indices (unordered int64 tensor) of (seed, attempt)."""
+    import torch
+    out = torch.empty(S, dtype=torch.int64, device=x.device)
+    with torch.cuda.device(x.device):
+        rc = load_library().profk_stage_sample(ctypes.c_void_p(x.data_ptr()), x.numel(), S, seed, attempt,
+                                               ctypes.c_void_p(out.data_ptr()), _stream_ptr(torch, x.device))
+    _check(rc)
+    return out
+
+
+def stage_threshold(x, S: int, t: int, seed: int = 0, attempt: int = 0):
+    """tau = (value, index) of the t-th largest sampled entry."""
+    import torch
+    v = torch.empty(1, dtype=torch.float32, device=x.device)
+    i = torch.empty(1, dtype=torch.int64, device=x.device)
+    with torch.cuda.device(x.device):
+        rc = load_library().profk_stage_threshold(ctypes.c_void_p(x.data_ptr()), x.numel(), S, t, seed, attempt,
+                                                  ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(i.data_ptr()),
+                                                  _stream_ptr(torch, x.device))
+    _check(rc)
+    return v, i
+
+
+def stage_filter(x, tau_val: float, tau_idx: int, M: int):
+    """(R, candidate indices of the min(R, M) kept entries, unordered)."""
+    import torch
+    cand = torch.empty(M, dtype=torch.int64, device=x.device)
+    R = torch.empty(1, dtype=torch.int64, device=x.device)
+    with torch.cuda.device(x.device):
+        rc = load_library().profk_stage_filter(ctypes.c_void_p(x.data_ptr()), x.numel(), ctypes.c_float(tau_val),
+                                               tau_idx, M, ctypes.c_void_p(cand.data_ptr()),
+                                               ctypes.c_void_p(R.data_ptr()), _stream_ptr(torch, x.device))
+    _check(rc)
+    r = int(R.item())
+    return r, cand[: min(r, M)]
+
+
+def release():
+    load_library().profk_release()

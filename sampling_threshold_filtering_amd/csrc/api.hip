@@ -1,0 +1,476 @@
+// Host controller and C ABI of the Prof-K exact top-k library (see include/profk.h).
+//
+// Control flow of one call ("Prof-K: Probabilistic One-Pass Filtering for Efficient
+// Top-k Selection", §3 stages 1-4 and the retry of stage 4):
+//   parameters (memoised)          -> S, t, M
+//   for attempt a = 0 .. max-1:
+//     enqueue sample(seed, a), threshold select, filter (+ check on device),
+//             refinement select, compaction, sort + output write
+//     copy the 16-byte attempt record back and synchronise the stream once
+//     ok -> return; R < k or R > M -> next attempt with a fresh Philox stream
+//   exact full selection over all N values (radix select + compaction + sort)
+// The refinement is enqueued before the single synchronisation and skips itself
+// on device when the check failed, so a successful attempt costs one round trip.
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "launch.h"
+#include "profk.h"
+#include "solver.h"
+
+namespace profk {
+namespace {
+
+thread_local std::string t_err;
+
+int hip_fail(hipError_t e, const char* what) {
+  t_err = std::string(what) + ": " + hipGetErrorString(e);
+  return PROFK_EHIP;
+}
+
+#define HIPCHK(call, what)                        \
+  do {                                            \
+    hipError_t e_ = (call);                       \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+constexpr int kDefaultAttempts = 6;  // P1 §3 stage 4: exact fallback after six failures
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+u64 pow2_at_least(u64 v) {
+  u64 p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+struct Layout {
+  size_t hash = 0, ctl = 0, sel = 0, rec = 0, ticket = 0, keys = 0, cand = 0, col = 0, topk0 = 0, topk1 = 0,
+         hist = 0, rows = 0, total = 0;
+  u64 hash_slots = 0;
+};
+
+// The hash region always spans the allocation's whole hash capacity, so that the
+// offsets of every other region depend only on the allocation and the request,
+// and no region ever overlaps stale hash slots.
+Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 hash_cap) {
+  Layout L;
+  L.hash_slots = pow2_at_least(2 * (S ? S : 1));
+  if (L.hash_slots < hash_cap) L.hash_slots = hash_cap;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.hash = take(L.hash_slots * sizeof(u64));
+  L.ctl = take(B * sizeof(RowCtl));
+  L.sel = take(B * sizeof(SelState));
+  L.rec = take(B * sizeof(AttemptRecord));
+  L.ticket = take(kTickets * sizeof(u32));
+  L.keys = take((S ? S : 1) * sizeof(u64));
+  L.cand = take(B * (M ? M : 1) * sizeof(u64));
+  L.col = take((size_t)kCollectCap * sizeof(u64));
+  L.topk0 = take((k ? k : 1) * sizeof(u64));
+  L.topk1 = take((k ? k : 1) * sizeof(u64));
+  L.hist = take(sort_hist_words(k) * sizeof(u32));
+  L.rows = take(B * sizeof(int));
+  L.total = off;
+  return L;
+}
+
+struct Workspace {
+  int device = -1;
+  hipStream_t stream = nullptr;
+  char* dev = nullptr;
+  size_t bytes = 0;
+  u64 hash_cap = 0;  // slots of the hash region at offset 0
+  AttemptRecord* host = nullptr;
+  size_t host_n = 0;
+  u32 gen = 0;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace*> g_ws;
+
+struct Need {
+  u64 B, S, M, k;
+};
+
+int get_workspace(hipStream_t s, const Need& need, Workspace** out, Layout* out_layout) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev), "hipGetDevice");
+  const u64 rows = need.B;
+  std::lock_guard<std::mutex> g(g_ws_mu);
+  Workspace*& w = g_ws[std::make_pair(dev, s)];
+  if (!w) {
+    w = new Workspace();
+    w->device = dev;
+    w->stream = s;
+  }
+  Layout L = make_layout(need.B, need.S, need.M, need.k, w->hash_cap);
+  if (w->bytes < L.total || w->hash_cap < L.hash_slots) {
+    if (w->dev) {
+      HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+      HIPCHK(hipFree(w->dev), "hipFree");
+      w->dev = nullptr;
+      w->bytes = 0;
+    }
+    size_t want = L.total + L.total / 4;
+    void* p = nullptr;
+    if (hipMalloc(&p, want) != hipSuccess) {
+      (void)hipGetLastError();
+      want = L.total;
+      if (hipMalloc(&p, want) != hipSuccess) {
+        (void)hipGetLastError();
+        t_err = "workspace allocation failed";
+        return PROFK_ENOMEM;
+      }
+    }
+    w->dev = (char*)p;
+    w->bytes = want;
+    w->hash_cap = L.hash_slots;
+    // zero everything once: hash generations, selection histograms, counters
+    HIPCHK(hipMemsetAsync(w->dev, 0, want, s), "hipMemsetAsync");
+    w->gen = 0;
+  }
+  if (w->host_n < rows) {
+    if (w->host) (void)hipHostFree(w->host);
+    w->host = nullptr;
+    w->host_n = 0;
+    HIPCHK(hipHostMalloc((void**)&w->host, rows * sizeof(AttemptRecord), hipHostMallocDefault), "hipHostMalloc");
+    w->host_n = rows;
+  }
+  if (!w->ev0) {
+    HIPCHK(hipEventCreate(&w->ev0), "hipEventCreate");
+    HIPCHK(hipEventCreate(&w->ev1), "hipEventCreate");
+  }
+  *out = w;
+  *out_layout = L;
+  return PROFK_OK;
+}
+
+// Next hash generation; clears the table when the 32-bit tag wraps.
+int next_gen(Workspace* w, hipStream_t s) {
+  if (++w->gen == 0) {
+    HIPCHK(hipMemsetAsync(w->dev, 0, w->hash_cap * sizeof(u64), s), "hipMemsetAsync");
+    w->gen = 1;
+  }
+  return PROFK_OK;
+}
+
+template <class T>
+T* at(Workspace* w, size_t off) {
+  return reinterpret_cast<T*>(w->dev + off);
+}
+
+int validate(const float* x, int64_t N, int64_t k, double eps, const void* ov, const void* oi) {
+  if (!x || !ov || !oi) return PROFK_EINVAL;
+  if (N < 1 || k < 1 || k > N) return PROFK_EINVAL;
+  if (!(eps > 0.0 && eps < 1.0)) return PROFK_EINVAL;
+  if (N >= (int64_t(1) << 32)) return PROFK_EUNSUPPORTED;
+  return PROFK_OK;
+}
+
+int max_attempts_of(const profk_options* opt) {
+  if (opt && opt->force_fallback) return 0;
+  if (opt && opt->use_max_attempts) return opt->max_attempts < 0 ? 0 : opt->max_attempts;
+  if (opt && opt->max_attempts > 0) return opt->max_attempts;
+  return kDefaultAttempts;
+}
+
+// Exact full selection of one row (radix select over all N keys formed on the fly).
+int run_exact(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, float* out_vals, int64_t* out_idx,
+              hipStream_t s) {
+  RowCtl* ctl = at<RowCtl>(w, L.ctl);
+  SelState* sel = at<SelState>(w, L.sel);
+  AttemptRecord* rec = at<AttemptRecord>(w, L.rec);
+  HIPCHK(launch_attempt_init(ctl, sel, rec, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
+  HIPCHK(launch_arm_select(sel, k, N, ctl, s), "launch arm_select");
+  HIPCHK(launch_select_x(x, N, sel, at<u64>(w, L.col), &ctl->kth, &ctl->status, s), "launch select_x");
+  HIPCHK(launch_compact_x(x, N, ctl, at<u64>(w, L.topk0), k, s), "launch compact_x");
+  HIPCHK(launch_sort_and_write(at<u64>(w, L.topk0), at<u64>(w, L.topk1), at<u32>(w, L.hist), (u32)k, x, N,
+                               out_vals, out_idx, ctl, rec, s),
+         "launch sort");
+  HIPCHK(hipMemcpyAsync(w->host, rec, sizeof(AttemptRecord), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+  HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  if (w->host[0].error || w->host[0].status != 0) {
+    t_err = "exact selection: device consistency check failed";
+    return PROFK_EINTERNAL;
+  }
+  return PROFK_OK;
+}
+
+// One sampled attempt of one row, enqueued; returns after the record is back.
+int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, const profk_params& p, u64 seed,
+                u32 attempt, float* out_vals, int64_t* out_idx, hipStream_t s, bool timing, AttemptRecord* out_rec,
+                float* filter_ms) {
+  RowCtl* ctl = at<RowCtl>(w, L.ctl);
+  SelState* sel = at<SelState>(w, L.sel);
+  AttemptRecord* rec = at<AttemptRecord>(w, L.rec);
+  const u64 S = (u64)p.S, M = (u64)p.M, t = (u64)p.t;
+  int rc = next_gen(w, s);
+  if (rc) return rc;
+  HIPCHK(launch_attempt_init(ctl, sel, rec, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
+  HIPCHK(launch_sample(x, N, S, seed, attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
+                       at<u64>(w, L.keys), ctl, sel, t, s),
+         "launch sample");
+  HIPCHK(launch_select_keys(at<u64>(w, L.keys), &ctl->D, S, sel, at<u64>(w, L.col), &ctl->tau, &ctl->status, s),
+         "launch select(sample)");
+  FilterArgs fa{};
+  fa.x = x;
+  fa.ld = N;
+  fa.N = N;
+  fa.rows = nullptr;
+  fa.nrows = 1;
+  fa.ctls = ctl;
+  fa.cand = at<u64>(w, L.cand);
+  fa.M = M;
+  fa.k = k;
+  fa.ticket = at<u32>(w, L.ticket);
+  fa.rec = rec;
+  fa.sels = sel;
+  if (timing) HIPCHK(hipEventRecord(w->ev0, s), "hipEventRecord");
+  HIPCHK(launch_filter(fa, 0, s), "launch filter");
+  if (timing) HIPCHK(hipEventRecord(w->ev1, s), "hipEventRecord");
+  HIPCHK(launch_select_keys(at<u64>(w, L.cand), &ctl->R, M, sel, at<u64>(w, L.col), &ctl->kth, &ctl->status, s),
+         "launch select(candidates)");
+  HIPCHK(launch_compact_keys(at<u64>(w, L.cand), &ctl->R, M, ctl, at<u64>(w, L.topk0), k, s), "launch compact");
+  HIPCHK(launch_sort_and_write(at<u64>(w, L.topk0), at<u64>(w, L.topk1), at<u32>(w, L.hist), (u32)k, x, N,
+                               out_vals, out_idx, ctl, rec, s),
+         "launch sort");
+  HIPCHK(hipMemcpyAsync(w->host, rec, sizeof(AttemptRecord), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+  HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  *out_rec = w->host[0];
+  if (timing && filter_ms) {
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, w->ev0, w->ev1), "hipEventElapsedTime");
+    *filter_ms = ms;
+  }
+  return PROFK_OK;
+}
+
+int topk_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* out_vals, int64_t* out_idx, hipStream_t s,
+             const profk_options* opt, profk_stats* st) {
+  profk_params p{};
+  int rc = solve_memo((int64_t)N, (int64_t)k, eps, opt, &p);
+  if (rc) return rc;
+  const int max_att = max_attempts_of(opt);
+  const bool sampled = !p.direct_exact && max_att > 0;
+  Layout L;
+  Workspace* w = nullptr;
+  rc = get_workspace(s, Need{1, sampled ? (u64)p.S : 0, sampled ? (u64)p.M : 0, k}, &w, &L);
+  if (rc) return rc;
+  if (st) {
+    st->S = p.S;
+    st->t = p.t;
+    st->M = p.M;
+    st->workspace_bytes = w->bytes;
+  }
+  if (sampled) {
+    for (int a = 0; a < max_att; ++a) {
+      AttemptRecord r{};
+      float fms = 0.f;
+      rc = run_attempt(w, L, x, N, k, p, seed, (u32)a, out_vals, out_idx, s, opt && opt->timing, &r, &fms);
+      if (rc) return rc;
+      if (st) {
+        st->attempts = a + 1;
+        if (a < PROFK_STATS_ATTEMPTS) {
+          st->R[a] = (int64_t)r.R;
+          st->fail_mode[a] = (int32_t)r.status;
+        }
+        st->filter_ms = fms;
+      }
+      if (r.error || r.status == 3) {
+        t_err = "sampled attempt: device consistency check failed";
+        return PROFK_EINTERNAL;
+      }
+      if (r.status == 0) return PROFK_OK;
+    }
+  }
+  if (st) st->fallback = 1;
+  return run_exact(w, L, x, N, k, out_vals, out_idx, s);
+}
+
+}  // namespace
+}  // namespace profk
+
+using namespace profk;
+
+extern "C" {
+
+int profk_solve(int64_t N, int64_t k, double eps, const profk_options* opt, profk_params* out) {
+  return solve_memo(N, k, eps, opt, out);
+}
+
+int profk_topk_ex(const float* x, int64_t N, int64_t k, double eps, uint64_t seed, float* out_vals,
+                  int64_t* out_idx, void* stream, const profk_options* opt, profk_stats* st) {
+  int rc = validate(x, N, k, eps, out_vals, out_idx);
+  if (rc) return rc;
+  if (st) std::memset(st, 0, sizeof(*st));
+  return topk_row(x, (u64)N, (u64)k, eps, seed, out_vals, out_idx, (hipStream_t)stream, opt, st);
+}
+
+int profk_topk(const float* x, int64_t N, int64_t k, double eps, uint64_t seed, float* out_vals, int64_t* out_idx,
+               void* stream) {
+  return profk_topk_ex(x, N, k, eps, seed, out_vals, out_idx, stream, nullptr, nullptr);
+}
+
+int profk_topk_batched_ex(const float* x, int64_t B, int64_t N, int64_t ld_x, int64_t k, double eps, uint64_t seed,
+                          float* out_vals, int64_t* out_idx, void* stream, const profk_options* opt,
+                          profk_stats* st) {
+  int rc = validate(x, N, k, eps, out_vals, out_idx);
+  if (rc) return rc;
+  if (B < 1 || ld_x < N) return PROFK_EINVAL;
+  if (st) std::memset(st, 0, sizeof(*st));
+  const double eps_row = eps / (double)B;  // P1 App. E.2: budget split per row
+  for (int64_t r = 0; r < B; ++r) {
+    profk_stats rs{};
+    rc = topk_row(x + r * ld_x, (u64)N, (u64)k, eps_row, seed, out_vals + r * k, out_idx + r * k,
+                  (hipStream_t)stream, opt, &rs);
+    if (rc) return rc;
+    if (st) {
+      if (r == 0) *st = rs;
+      if (rs.attempts > 1) st->rows_retried++;
+      if (rs.fallback) st->rows_fallback++;
+      if (rs.attempts > st->attempts) st->attempts = rs.attempts;
+    }
+  }
+  return PROFK_OK;
+}
+
+int profk_topk_batched(const float* x, int64_t B, int64_t N, int64_t ld_x, int64_t k, double eps, uint64_t seed,
+                       float* out_vals, int64_t* out_idx, void* stream) {
+  return profk_topk_batched_ex(x, B, N, ld_x, k, eps, seed, out_vals, out_idx, stream, nullptr, nullptr);
+}
+
+int profk_stage_sample(const float* x, int64_t N, int64_t S, uint64_t seed, int32_t attempt, int64_t* out_idx,
+                       void* stream) {
+  if (!x || !out_idx || N < 2 || S < 1 || 2 * S > N || attempt < 0) return PROFK_EINVAL;
+  if (N >= (int64_t(1) << 32)) return PROFK_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  Layout L;
+  Workspace* w = nullptr;
+  int rc = get_workspace(s, Need{1, (u64)S, 1, 1}, &w, &L);
+  if (rc) return rc;
+  rc = next_gen(w, s);
+  if (rc) return rc;
+  RowCtl* ctl = at<RowCtl>(w, L.ctl);
+  SelState* sel = at<SelState>(w, L.sel);
+  HIPCHK(launch_attempt_init(ctl, sel, nullptr, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
+  HIPCHK(launch_sample(x, (u64)N, (u64)S, seed, (u32)attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
+                       at<u64>(w, L.keys), ctl, sel, 1, s),
+         "launch sample");
+  HIPCHK(launch_keys_to_index(at<u64>(w, L.keys), &ctl->D, (u64)S, out_idx, s), "launch keys_to_index");
+  HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  return PROFK_OK;
+}
+
+int profk_stage_threshold(const float* x, int64_t N, int64_t S, int64_t t, uint64_t seed, int32_t attempt,
+                          float* out_tau_val, int64_t* out_tau_idx, void* stream) {
+  if (!x || !out_tau_val || !out_tau_idx || N < 2 || S < 1 || 2 * S > N || t < 1 || t > S || attempt < 0)
+    return PROFK_EINVAL;
+  if (N >= (int64_t(1) << 32)) return PROFK_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  Layout L;
+  Workspace* w = nullptr;
+  int rc = get_workspace(s, Need{1, (u64)S, 1, 1}, &w, &L);
+  if (rc) return rc;
+  rc = next_gen(w, s);
+  if (rc) return rc;
+  RowCtl* ctl = at<RowCtl>(w, L.ctl);
+  SelState* sel = at<SelState>(w, L.sel);
+  HIPCHK(launch_attempt_init(ctl, sel, nullptr, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
+  HIPCHK(launch_sample(x, (u64)N, (u64)S, seed, (u32)attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
+                       at<u64>(w, L.keys), ctl, sel, (u64)t, s),
+         "launch sample");
+  HIPCHK(launch_select_keys(at<u64>(w, L.keys), &ctl->D, (u64)S, sel, at<u64>(w, L.col), &ctl->tau, &ctl->status, s),
+         "launch select");
+  HIPCHK(launch_tau_to_output(x, (u64)N, ctl, out_tau_val, out_tau_idx, s), "launch tau_to_output");
+  u32 status = 0;
+  HIPCHK(hipMemcpyAsync(&status, &ctl->status, sizeof(u32), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+  HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  if (status != 0) {
+    t_err = "threshold: device consistency check failed";
+    return PROFK_EINTERNAL;
+  }
+  return PROFK_OK;
+}
+
+int profk_stage_filter(const float* x, int64_t N, float tau_val, int64_t tau_idx, int64_t M, int64_t* out_cand_idx,
+                       int64_t* out_R, void* stream) {
+  if (!x || !out_cand_idx || !out_R || N < 1 || M < 1 || tau_idx < 0 || tau_idx >= N) return PROFK_EINVAL;
+  if (N >= (int64_t(1) << 32)) return PROFK_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  Layout L;
+  Workspace* w = nullptr;
+  int rc = get_workspace(s, Need{1, 1, (u64)M, 1}, &w, &L);
+  if (rc) return rc;
+  RowCtl* ctl = at<RowCtl>(w, L.ctl);
+  u32 bits;
+  std::memcpy(&bits, &tau_val, sizeof(bits));
+  HIPCHK(launch_set_tau(ctl, at<u32>(w, L.ticket), bits, (u32)tau_idx, s), "launch set_tau");
+  FilterArgs fa{};
+  fa.x = x;
+  fa.ld = (u64)N;
+  fa.N = (u64)N;
+  fa.nrows = 1;
+  fa.ctls = ctl;
+  fa.cand = at<u64>(w, L.cand);
+  fa.M = (u64)M;
+  fa.k = 1;
+  fa.ticket = at<u32>(w, L.ticket);
+  fa.rec = nullptr;
+  fa.sels = nullptr;
+  HIPCHK(launch_filter(fa, 0, s), "launch filter");
+  HIPCHK(launch_keys_to_index(at<u64>(w, L.cand), &ctl->R, (u64)M, out_cand_idx, s), "launch keys_to_index");
+  HIPCHK(launch_r_to_output(ctl, out_R, s), "launch r_to_output");
+  HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  return PROFK_OK;
+}
+
+const char* profk_strerror(int code) {
+  switch (code) {
+    case PROFK_OK:
+      return "ok";
+    case PROFK_EINVAL:
+      return "invalid argument";
+    case PROFK_EUNSUPPORTED:
+      return "unsupported size (N >= 2^32 per row)";
+    case PROFK_ENOMEM:
+      return "device workspace allocation failed";
+    case PROFK_EHIP:
+      return t_err.empty() ? "HIP runtime error" : t_err.c_str();
+    case PROFK_EINTERNAL:
+      return t_err.empty() ? "device consistency check failed" : t_err.c_str();
+    default:
+      return "unknown status";
+  }
+}
+
+void profk_release(void) {
+  std::lock_guard<std::mutex> g(g_ws_mu);
+  for (auto& kv : g_ws) {
+    Workspace* w = kv.second;
+    if (!w) continue;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(w->device);
+    if (w->dev) {
+      (void)hipStreamSynchronize(w->stream);
+      (void)hipFree(w->dev);
+    }
+    if (w->host) (void)hipHostFree(w->host);
+    if (w->ev0) (void)hipEventDestroy(w->ev0);
+    if (w->ev1) (void)hipEventDestroy(w->ev1);
+    (void)hipSetDevice(cur);
+    delete w;
+  }
+  g_ws.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,245 @@
+// Stage 3 of Prof-K ("Prof-K: Probabilistic One-Pass Filtering for Efficient Top-k
+// Selection", §3 stage 3 and App. C "The Filter Kernel"): one streaming pass over
+// every row keeps each entry at or above the row's threshold tau in a candidate
+// buffer of capacity M and counts them exactly.  The counter R is incremented by
+// the full number of kept entries while stores stop at M, so R is the exact rank
+// of tau even when the buffer overflows, and the run-time check k <= R <= M needs
+// no second pass (App. C).
+//
+// gfx950 design (the page's Triton kernel is prior art for another GPU):
+//   * Work unit: a wave-tile of 64 lanes x U float4 (U = 8: 2048 values, 8 KB)
+//     read with dwordx4 loads; wavefronts stride over the wave-tiles of all rows.
+//   * Fast pre-test per value: !(x < tau_value), one float compare.  Only a
+//     wavefront whose tile has a hit evaluates the exact key test
+//     key(x_i, i) >= tau (value, then lower index first: the total order that makes
+//     every key distinct).
+//   * Compaction: ballot + mbcnt give each hit its slot; hits are staged in a
+//     per-wavefront LDS ring (512 keys) and flushed with ONE global atomic on the
+//     row counter per flush, so dense tiles cost one atomic per ~512 hits.
+//   * The last block to finish (ticket) evaluates k <= R <= M per row, writes the
+//     host-visible record, and arms the refinement selection of each row.
+#include "launch.h"
+
+namespace profk {
+
+namespace {
+
+constexpr int kFilterThreads = 256;
+constexpr int kWavesPerBlock = kFilterThreads / kWave;
+constexpr u32 kStageCap = 512;
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+struct RowGeom {
+  const float* row;  // row base
+  u64 head;          // scalar values before the first 16-byte boundary
+  u64 nvec;          // float4 vectors after it
+  u64 tail;          // scalar values after the vectors
+};
+
+__device__ __forceinline__ RowGeom row_geom(const float* x, u64 ld, u64 N, u64 r) {
+  RowGeom g;
+  g.row = x + r * ld;
+  const u64 mis = ((u64)(uintptr_t)g.row >> 2) & 3ull;
+  u64 head = (4ull - mis) & 3ull;
+  if (head > N) head = N;
+  g.head = head;
+  g.nvec = (N - head) >> 2;
+  g.tail = N - head - 4 * g.nvec;
+  return g;
+}
+
+struct Stage {
+  u64* buf;  // this wavefront's LDS ring
+  u32 n;     // staged keys
+  u32 row;   // row the staged keys belong to
+};
+
+__device__ __forceinline__ void stage_flush(Stage& st, RowCtl* ctls, u64* cand, u64 M) {
+  if (st.n == 0) return;
+  wave_lds_sync();
+  u64 base = 0;
+  if (lane_id() == 0) base = atomicAdd(&ctls[st.row].R, (u64)st.n);
+  base = __shfl(base, 0);
+  u64* dst = cand + (u64)st.row * M;
+  for (u32 j = lane_id(); j < st.n; j += kWave)
+    if (base + j < M) dst[base + j] = st.buf[j];
+  wave_lds_sync();
+  st.n = 0;
+}
+
+// Route the hits of one batch (nmask ballots, hits[] per lane) into the stage.
+template <int NB>
+__device__ __forceinline__ void stage_hits(Stage& st, u32 row, const u64 (&masks)[NB], const bool (&hit)[NB],
+                                           const u64 (&key)[NB], RowCtl* ctls, u64* cand, u64 M) {
+  u32 total = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) total += (u32)__popcll(masks[b]);
+  if (total == 0) return;
+  if (st.n != 0 && (st.row != row || st.n + total > kStageCap)) stage_flush(st, ctls, cand, M);
+  if (total > kStageCap) {
+    // dense batch: straight to the row's buffer with one atomic
+    u64 base = 0;
+    if (lane_id() == 0) base = atomicAdd(&ctls[row].R, (u64)total);
+    base = __shfl(base, 0);
+    u64* dst = cand + (u64)row * M;
+    u32 run = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (hit[b]) {
+        const u64 pos = base + run + count_below(masks[b]);
+        if (pos < M) dst[pos] = key[b];
+      }
+      run += (u32)__popcll(masks[b]);
+    }
+    return;
+  }
+  st.row = row;
+  u32 run = st.n;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (hit[b]) st.buf[run + count_below(masks[b])] = key[b];
+    run += (u32)__popcll(masks[b]);
+  }
+  st.n = run;
+}
+
+}  // namespace
+
+template <int U, bool NT>
+__global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
+  __shared__ u64 s_stage[kWavesPerBlock][kStageCap];
+  __shared__ u32 s_last;
+  const u32 wid = threadIdx.x / kWave;
+  const u32 lane = lane_id();
+  Stage st{s_stage[wid], 0u, 0u};
+
+  const u64 nwaves = (u64)gridDim.x * kWavesPerBlock;
+  for (u64 g = (u64)blockIdx.x * kWavesPerBlock + wid; g < a.total_tiles; g += nwaves) {
+    const u64 lr = g / a.tiles_per_row;
+    const u64 tile = g - lr * a.tiles_per_row;
+    const u32 row = a.rows ? (u32)a.rows[lr] : (u32)lr;
+    const RowGeom geo = row_geom(a.x, a.ld, a.N, row);
+    const u64 tau = a.ctls[row].tau;
+    const u32 tk = (u32)(tau >> 32);
+    const u32 ti = key_index(tau);
+    const float tv = __uint_as_float(bits_of_ord32(tk));
+    const f4* pv = reinterpret_cast<const f4*>(geo.row + geo.head);
+
+    f4 v[U];
+    bool valid[U];
+    const u64 v0 = tile * (u64)(U * kWave);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u64 vi = v0 + (u64)u * kWave + lane;
+      valid[u] = vi < geo.nvec;
+      if (valid[u]) {
+        if (NT)
+          v[u] = __builtin_nontemporal_load(pv + vi);
+        else
+          v[u] = pv[vi];
+      } else {
+        v[u] = f4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    bool maybe = false;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool m = !(v[u].x < tv) | !(v[u].y < tv) | !(v[u].z < tv) | !(v[u].w < tv);
+      maybe |= valid[u] & m;
+    }
+    if (__ballot(maybe)) {
+      // exact test, one float4 slot at a time (4 ballots each)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const u64 vi = v0 + (u64)u * kWave + lane;
+        const u32 i0 = (u32)(geo.head + 4 * vi);
+        const float c[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        u64 masks[4];
+        bool hit[4];
+        u64 key[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32 o = ord32(__float_as_uint(c[q]));
+          const u32 i = i0 + q;
+          hit[q] = valid[u] && (o > tk || (o == tk && i <= ti));
+          key[q] = ((u64)o << 32) | (u64)(~i);
+          masks[q] = __ballot(hit[q]);
+        }
+        stage_hits<4>(st, row, masks, hit, key, a.ctls, a.cand, a.M);
+      }
+    }
+    if (tile == 0 && (geo.head | geo.tail)) {
+      // scalar edge values of this row: lanes [0, head) take the head, then the tail
+      const u64 e = lane;
+      bool in = false;
+      u32 i = 0;
+      if (e < geo.head) {
+        in = true;
+        i = (u32)e;
+      } else if (e < geo.head + geo.tail) {
+        in = true;
+        i = (u32)(geo.head + 4 * geo.nvec + (e - geo.head));
+      }
+      u64 masks[1];
+      bool hit[1];
+      u64 key[1];
+      const u32 o = in ? ord32(__float_as_uint(geo.row[i])) : 0u;
+      hit[0] = in && (o > tk || (o == tk && i <= ti));
+      key[0] = ((u64)o << 32) | (u64)(~i);
+      masks[0] = __ballot(hit[0]);
+      stage_hits<1>(st, row, masks, hit, key, a.ctls, a.cand, a.M);
+    }
+  }
+  stage_flush(st, a.ctls, a.cand, a.M);
+
+  // last block: run-time check per row, host record, arm the refinement selection
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = (atomicAdd(a.ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (u64 lr = threadIdx.x; lr < a.nrows; lr += blockDim.x) {
+    const u32 row = a.rows ? (u32)a.rows[lr] : (u32)lr;
+    RowCtl* c = &a.ctls[row];
+    const u64 R = atomic_load_agent(&c->R);
+    u32 status = c->status;
+    if (status == 0) status = R < a.k ? 1u : (R > a.M ? 2u : 0u);
+    c->status = status;
+    if (a.rec) {
+      a.rec[row].R = R;
+      a.rec[row].status = status;
+    }
+    if (a.sels) {
+      SelState* s = &a.sels[row];
+      s->prefix = 0;
+      s->mask = 0;
+      s->rank = a.k;
+      s->count = R < a.M ? R : a.M;
+      s->done = status ? 1u : 0u;
+      s->digit = 0;
+      s->ticket = 0;
+      s->ncol = 0;
+    }
+  }
+  if (threadIdx.x == 0) *a.ticket = 0;
+}
+
+hipError_t launch_filter(const FilterArgs& a0, u32 grid, hipStream_t s) {
+  FilterArgs a = a0;
+  constexpr int U = 8;
+  const u64 vec_per_tile = (u64)U * kWave;
+  const u64 max_vec = (a.N >> 2) + 1;
+  a.tiles_per_row = (max_vec + vec_per_tile - 1) / vec_per_tile;
+  if (a.tiles_per_row == 0) a.tiles_per_row = 1;
+  a.total_tiles = a.tiles_per_row * a.nrows;
+  u64 need = (a.total_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (need < 1) need = 1;
+  if (grid == 0) grid = 2048;
+  if ((u64)grid > need) grid = (u32)need;
+  filter_kernel<U, true><<<grid, kFilterThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace profk

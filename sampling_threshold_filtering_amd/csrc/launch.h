@@ -1,0 +1,53 @@
+// Host-side launchers of the Prof-K kernels (one declaration per launch group).
+#pragma once
+
+#include "profk_device.h"
+
+namespace profk {
+
+constexpr u32 kSmallSort = 8192;  // keys sorted by one workgroup in LDS (64 KB)
+constexpr u32 kTickets = 64;      // u32 last-block tickets in the workspace, cleared every attempt
+
+struct FilterArgs {
+  const float* x;      // row 0
+  u64 ld;              // row stride (elements)
+  u64 N;               // values per row
+  const int* rows;     // rows to process (device), or nullptr for rows 0..nrows-1
+  u64 nrows;
+  RowCtl* ctls;        // per row: tau in, R / status out
+  u64* cand;           // per row M keys, row stride M
+  u64 M;
+  u64 k;
+  u32* ticket;         // zero before the launch; left zero after it
+  AttemptRecord* rec;  // per row, or nullptr
+  SelState* sels;      // per row refinement selection to arm, or nullptr
+  u64 tiles_per_row;   // set by launch_filter
+  u64 total_tiles;
+};
+
+hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u32* tickets, u32 nrows,
+                               hipStream_t s);
+hipError_t launch_sample(const float* x, u64 N, u64 S, u64 seed, u32 attempt, u32 row, u64* table, u64 tmask,
+                         u32 gen, u64* keys, RowCtl* ctl, SelState* sel, u64 t, hipStream_t s);
+hipError_t launch_keys_to_index(const u64* keys, const u64* n_ptr, u64 n_cap, int64_t* out, hipStream_t s);
+hipError_t launch_tau_to_output(const float* x, u64 N, const RowCtl* ctl, float* out_val, int64_t* out_idx,
+                                hipStream_t s);
+hipError_t launch_set_tau(RowCtl* ctl, u32* tickets, u32 tau_bits, u32 tau_idx, hipStream_t s);
+hipError_t launch_r_to_output(const RowCtl* ctl, int64_t* out_R, hipStream_t s);
+
+hipError_t launch_select_keys(const u64* keys, const u64* n_ptr, u64 n_cap, SelState* st, u64* col, u64* result,
+                              u32* status, hipStream_t s);
+hipError_t launch_select_x(const float* x, u64 N, SelState* st, u64* col, u64* result, u32* status,
+                           hipStream_t s);
+hipError_t launch_compact_keys(const u64* keys, const u64* n_ptr, u64 n_cap, RowCtl* ctl, u64* out, u64 k,
+                               hipStream_t s);
+hipError_t launch_compact_x(const float* x, u64 N, RowCtl* ctl, u64* out, u64 k, hipStream_t s);
+hipError_t launch_arm_select(SelState* st, u64 rank, u64 count, RowCtl* ctl, hipStream_t s);
+
+hipError_t launch_filter(const FilterArgs& a, u32 grid, hipStream_t s);
+
+hipError_t launch_sort_and_write(u64* buf0, u64* buf1, u32* hist, u32 k, const float* row, u64 N, float* out_vals,
+                                 int64_t* out_idx, RowCtl* ctl, AttemptRecord* rec, hipStream_t s);
+u64 sort_hist_words(u64 k);
+
+}  // namespace profk

@@ -1,0 +1,180 @@
+// Device-side building blocks shared by the Prof-K kernels (gfx950, wave64).
+//
+// Keys.  Every entry x_i of a row is compared through the 64-bit composite key
+//     key(i) = (ord32(x_i) << 32) | (~i & 0xFFFFFFFF)
+// where ord32 maps the fp32 bits to an unsigned integer of the same order
+// (-0.0 folded onto +0.0, every NaN onto the largest code).  A larger key ranks
+// first; equal values are ordered by lower index first.  All keys of a row are
+// distinct, which makes the pages' distinct-entries assumption ("Prof-K:
+// Probabilistic One-Pass Filtering for Efficient Top-k Selection", §4 "Notation
+// and Conventions") hold for every input: the rank law of the threshold and the
+// exact parameters of Theorem 4 then apply unchanged.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace profk {
+
+typedef unsigned long long u64;
+typedef unsigned int u32;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ u32 ord32(u32 bits) {
+  if (bits == 0x80000000u) bits = 0u;                          // -0.0 -> +0.0
+  if ((bits & 0x7FFFFFFFu) > 0x7F800000u) bits = 0x7FFFFFFFu;  // NaN -> one code above +inf
+  return bits ^ ((u32)((int)bits >> 31) | 0x80000000u);
+}
+
+__device__ __forceinline__ u64 make_key(u32 bits, u32 idx) {
+  return ((u64)ord32(bits) << 32) | (u64)(~idx);
+}
+
+__device__ __forceinline__ u32 key_index(u64 key) { return ~(u32)key; }
+
+// Inverse of ord32 on the canonical codes (used for the fast float pre-test).
+__device__ __forceinline__ u32 bits_of_ord32(u32 o) {
+  return (o & 0x80000000u) ? (o ^ 0x80000000u) : ~o;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11), written from its published definition:
+// per round, with A = 0xD2511F53 and B = 0xCD9E8D57,
+//   (c0,c1,c2,c3) -> (hi(B c2) ^ c1 ^ k0, lo(B c2), hi(A c0) ^ c3 ^ k1, lo(A c0)),
+// and the key advances by (0x9E3779B9, 0xBB67AE85) between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, u32 k0, u32 k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const u32 hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+    const u32 hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+  }
+  return c;
+}
+
+// Draw j of the sample stream of (seed, attempt, row): counter (j, row, attempt, 0),
+// key (seed lo, seed hi); r = w0 + 2^32 w1 is mapped to floor(r * N / 2^64).
+__device__ __forceinline__ u64 sample_draw(u64 j, u32 row, u32 attempt, u64 seed, u64 N) {
+  const uint4 w = philox4x32_10(make_uint4((u32)j, row, attempt, 0u), (u32)seed, (u32)(seed >> 32));
+  const u64 r = (u64)w.x | ((u64)w.y << 32);
+  return __umul64hi(r, N);
+}
+
+// ---------------------------------------------------------------------------
+// Wave helpers
+__device__ __forceinline__ u32 lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ u32 count_below(u64 mask) {
+  // number of set bits of mask in lanes below this one
+  return __builtin_amdgcn_mbcnt_hi((u32)(mask >> 32), __builtin_amdgcn_mbcnt_lo((u32)mask, 0u));
+}
+
+// Order the wave's LDS accesses around a cross-lane exchange through LDS.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <class T>
+__device__ __forceinline__ T atomic_load_agent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class T>
+__device__ __forceinline__ void atomic_store_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One atomicAdd per wave for the lanes with pred set; returns this lane's slot.
+__device__ __forceinline__ u64 wave_reserve(u64* counter, bool pred) {
+  const u64 m = __ballot(pred);
+  u64 base = 0;
+  if (m) {
+    const u32 leader = __ffsll((long long)m) - 1;
+    if (lane_id() == leader) base = atomicAdd(counter, (u64)__popcll(m));
+    base = __shfl(base, leader);
+  }
+  return base + count_below(m);
+}
+
+__device__ __forceinline__ u32 wave_reserve32(u32* counter, bool pred) {
+  const u64 m = __ballot(pred);
+  u32 base = 0;
+  if (m) {
+    const u32 leader = __ffsll((long long)m) - 1;
+    if (lane_id() == leader) base = atomicAdd(counter, (u32)__popcll(m));
+    base = __shfl(base, leader);
+  }
+  return base + count_below(m);
+}
+
+// Lanes with equal 8-bit digit (among those with active set): mask of those lanes.
+__device__ __forceinline__ u64 wave_match8(u32 digit, bool active) {
+  u64 same = __ballot(active);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (digit >> b) & 1u;
+    const u64 bb = __ballot(bit);
+    same &= bit ? bb : ~bb;
+  }
+  return same;
+}
+
+// Histogram increment of an LDS histogram, one LDS atomic per distinct digit in the wave.
+__device__ __forceinline__ void wave_hist_add(u32* hist, u32 digit, bool active) {
+  const u64 same = wave_match8(digit, active);
+  if (active && lane_id() == (u32)(__ffsll((long long)same) - 1)) atomicAdd(&hist[digit], (u32)__popcll(same));
+}
+
+// ---------------------------------------------------------------------------
+// Device-resident control blocks.
+
+// State of one multi-pass radix selection ("which key has rank `rank` in
+// descending order among n distinct keys").  Each pass either fixes the next
+// 8-bit digit (histogram of the keys that match the fixed prefix) or, once at
+// most kCollectCap keys match, collects them and finishes in LDS.
+constexpr u32 kCollectCap = 2048;
+
+struct SelState {
+  u64 prefix;   // fixed high bits
+  u64 mask;     // which bits are fixed
+  u64 rank;     // 1-based rank of the target among the keys matching prefix
+  u64 count;    // number of keys matching prefix
+  u32 done;     // 1: result holds the exact key
+  u32 digit;    // digits fixed so far (0..8)
+  u32 ticket;   // last-block election
+  u32 ncol;     // collected keys
+  u32 error;    // inconsistent state seen (should never happen)
+  u32 pad[3];
+  u32 hist[256];
+};
+
+// Per-row control of one sampled attempt.
+struct RowCtl {
+  u64 D;        // distinct sample indices drawn so far
+  u64 tau;      // composite threshold key
+  u64 R;        // exact filter count
+  u64 kth;      // composite key of the k-th largest candidate
+  u64 nsel;     // keys written by the compaction
+  u64 key_or;   // OR / AND of the selected keys (which digits vary)
+  u64 key_and;
+  u32 status;   // 0 ok, 1 R < k, 2 R > M, 3 internal error
+  u32 cur;      // ping-pong buffer of the sort
+  u32 ticket;   // last-block election of the sort passes
+  u32 pad;
+};
+
+// Host-visible summary of an attempt, copied back once per attempt.
+struct AttemptRecord {
+  u64 R;
+  u32 status;
+  u32 error;
+};
+
+}  // namespace profk

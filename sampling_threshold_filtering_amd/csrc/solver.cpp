@@ -1,0 +1,210 @@
+// Host-side parameter choice of Prof-K, in double precision.
+//
+// Pages: P1 = "Prof-K: Probabilistic One-Pass Filtering for Efficient Top-k
+// Selection" (arXiv HTML page); P2 = its earlier version (bittide mirror).
+//
+//  * eps_A = eps_B = eps / 2                            (P1 §4, after Theorem 4)
+//  * z_A = Phi^-1(1 - eps_A), z = z_A + z_B             (P2 Algorithm 1, step 1)
+//  * S*_raw = c (k (N-k))^(1/3), default c = 1; S = round-to-nearest, clamped to
+//    [S_min, S_max] = [32768, 131072], at most N         (P2 Theorem 5, Eq. 14 and
+//    the text after it; the prefactor c = 1 is the one that reproduces the worked
+//    example N = 1e9, k = 100 -> S* about 4,600)
+//  * t* = F^-1_{N,k-1,S}(1 - eps_A) + 1,
+//    M* = min{M in [k, N] : F_{N,M,S}(t* - 1) <= eps_B}  (P1 Theorem 4, Eq. 7),
+//    M* by binary search since G(M) = F_{N,M,S}(t-1) is nonincreasing in M (P1 Lemma 1)
+//  * M_cf = k + z sqrt(k (N-k) / S (1 - S/N))          (P2 Corollary 4, Eq. 12)
+//  * operating t = t*, M = max(M*, ceil(M_cf)); the closed form is kept as a lower
+//    bound only, since with P2's own t it exceeds the budget in the sparse regime
+//  * Pr(R < k) = 1 - F_{N,k-1,S}(t-1)  (P1 Eq. 5);  Pr(R > M) = F_{N,M,S}(t-1)  (P1 Eq. 6)
+//  * E[R], Var[R] of the negative hypergeometric rank  (P2 Lemma 1, Eq. 2)
+//
+// Hypergeometric CDF numerics: log P(X = 0) = sum_{i<S} log1p(-K / (N - i)), then the
+// ratio recurrence P(j+1)/P(j) = (K-j)(S-j) / ((j+1)(N-K-S+j+1)) in log space.  lgamma
+// differences are avoided in the main regime: at N = 2^30 they lose about 1e-6.
+#include "solver.h"
+
+#include <algorithm>
+#include <cmath>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+namespace profk {
+
+namespace {
+
+// log P(X = jmin) for X ~ Hyp(N, K, S), jmin = max(0, S + K - N).
+double log_pmf_at_min(int64_t N, int64_t K, int64_t S, int64_t jmin) {
+  if (jmin == 0) {
+    // P(X = 0) = prod_{i<S} (N - K - i) / (N - i)
+    if (K == 0) return 0.0;
+    long double acc = 0.0L;
+    const double Kd = (double)K;
+    for (int64_t i = 0; i < S; ++i) acc += (long double)std::log1p(-Kd / (double)(N - i));
+    return (double)acc;
+  }
+  // K + S > N: P(X = jmin) = C(K, jmin) C(N-K, S-jmin) / C(N, S) with S - jmin = N - K,
+  // so C(N-K, N-K) = 1.  Only reached far from the operating point (M near N).
+  auto lc = [](double n, double r) { return std::lgamma(n + 1) - std::lgamma(r + 1) - std::lgamma(n - r + 1); };
+  return lc((double)K, (double)jmin) - lc((double)N, (double)S);
+}
+
+}  // namespace
+
+double hyp_cdf(int64_t j, int64_t N, int64_t K, int64_t S) {
+  if (j < 0) return 0.0;
+  const int64_t jmin = std::max<int64_t>(0, S + K - N);
+  const int64_t jmax = std::min<int64_t>(K, S);
+  if (j >= jmax) return 1.0;
+  if (j < jmin) return 0.0;
+  double lp = log_pmf_at_min(N, K, S, jmin);
+  // sum_{i=jmin}^{j} exp(lp_i), with a running max shift
+  double mx = lp, sum = 1.0;  // sum of exp(lp_i - mx)
+  for (int64_t i = jmin; i < j; ++i) {
+    const double num = (double)(K - i) * (double)(S - i);
+    const double den = (double)(i + 1) * (double)(N - K - S + i + 1);
+    lp += std::log(num) - std::log(den);
+    if (lp > mx) {
+      sum = sum * std::exp(mx - lp) + 1.0;
+      mx = lp;
+    } else {
+      sum += std::exp(lp - mx);
+    }
+  }
+  const double r = std::exp(mx + std::log(sum));
+  return r > 1.0 ? 1.0 : r;
+}
+
+double hyp_upper_tail(int64_t j, int64_t N, int64_t K, int64_t S) {
+  // Pr(X > j) = 1 - F(j)
+  return 1.0 - hyp_cdf(j, N, K, S);
+}
+
+int64_t hyp_quantile(double p, int64_t N, int64_t K, int64_t S) {
+  // min{j in 0..min(K,S) : F(j) >= p} (P1 Eq. 2), walking the pmf upward
+  const int64_t jmin = std::max<int64_t>(0, S + K - N);
+  const int64_t jmax = std::min<int64_t>(K, S);
+  double lp = log_pmf_at_min(N, K, S, jmin);
+  double cdf = std::exp(lp);
+  int64_t j = jmin;
+  while (j < jmax && cdf < p) {
+    const double num = (double)(K - j) * (double)(S - j);
+    const double den = (double)(j + 1) * (double)(N - K - S + j + 1);
+    lp += std::log(num) - std::log(den);
+    ++j;
+    cdf += std::exp(lp);
+  }
+  return j;
+}
+
+double normal_upper_quantile(double q) {
+  // z with Q(z) = 0.5 erfc(z / sqrt 2) = q, 0 < q < 1, by bisection (Q is decreasing)
+  double lo = -40.0, hi = 40.0;
+  for (int it = 0; it < 200; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    const double Q = 0.5 * std::erfc(mid / std::sqrt(2.0));
+    if (Q > q)
+      lo = mid;
+    else
+      hi = mid;
+    if (hi - lo <= 1e-15 * std::max(1.0, std::fabs(mid))) break;
+  }
+  return 0.5 * (lo + hi);
+}
+
+int solve(int64_t N, int64_t k, double eps, const profk_options* opt, profk_params* out) {
+  if (!out) return PROFK_EINVAL;
+  if (N < 1 || k < 1 || k > N || !(eps > 0.0 && eps < 1.0)) return PROFK_EINVAL;
+  if (N >= (int64_t(1) << 32)) return PROFK_EUNSUPPORTED;
+  profk_params p{};
+  p.N = N;
+  p.k = k;
+  p.eps = eps;
+  p.eps_a = eps / 2.0;
+  p.eps_b = eps / 2.0;
+  p.z_a = normal_upper_quantile(p.eps_a);
+  p.z = 2.0 * p.z_a;
+
+  const int64_t s_min = (opt && opt->s_min > 0) ? opt->s_min : 32768;
+  const int64_t s_max = (opt && opt->s_max > 0) ? opt->s_max : 131072;
+  const double c = (opt && opt->s_prefactor > 0.0) ? opt->s_prefactor : 1.0;
+  p.S_raw = c * std::cbrt((double)k * (double)(N - k));
+  int64_t S = (int64_t)std::floor(p.S_raw + 0.5);
+  S = std::max(s_min, std::min(s_max, S));
+  if (opt && opt->s_override > 0) S = opt->s_override;
+  S = std::min(S, N);
+  p.S = S;
+
+  p.t_star = hyp_quantile(1.0 - p.eps_a, N, k - 1, S) + 1;
+  // If t* > S the recall budget cannot be met (Theorem 4's condition on eps_A fails).
+  const bool t_ok = p.t_star <= S;
+  if (t_ok) {
+    int64_t lo = k, hi = N;  // F_{N,N,S}(t-1) = 0 since X = S >= t
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (hyp_cdf(p.t_star - 1, N, mid, S) <= p.eps_b)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    p.M_star = lo;
+  } else {
+    p.M_star = N;
+  }
+  p.M_cf = (double)k + p.z * std::sqrt((double)k * (double)(N - k) / (double)S * (1.0 - (double)S / (double)N));
+  const double a = (double)k / (double)N, f = 1.0 - (double)S / (double)N;
+  p.t_eq6 = (int64_t)std::ceil((double)S * a + p.z_a * std::sqrt((double)S * a * (1.0 - a) * f));
+
+  p.t = std::min<int64_t>(p.t_star, S);
+  p.M = std::max<int64_t>(p.M_star, (int64_t)std::ceil(p.M_cf));
+  if (opt && opt->force_t > 0) p.t = std::min<int64_t>(opt->force_t, S);
+  if (opt && opt->force_M > 0) p.M = std::max<int64_t>(opt->force_M, k);
+  p.M = std::min<int64_t>(p.M, N);
+
+  p.p_recall = hyp_upper_tail(p.t - 1, N, k - 1, S);
+  p.p_overflow = hyp_cdf(p.t - 1, N, p.M, S);
+  p.E_R = (double)(N + 1) * (double)p.t / (double)(S + 1);
+  p.Var_R = (double)p.t * (double)(S - p.t + 1) * (double)(N + 1) * (double)(N - S) /
+            (((double)S + 1.0) * ((double)S + 1.0) * ((double)S + 2.0));
+
+  // The sampled path pays for itself only while sample and buffer are small next to N
+  // (P2 "Graceful Degradation via Fallback": fall back to the exact selection when
+  // the conditions are not met economically).
+  const bool forced = opt && (opt->force_t > 0 || opt->force_M > 0);
+  p.direct_exact = (!t_ok || 2 * S > N || (!forced && 2 * p.M > N)) ? 1 : 0;
+  *out = p;
+  return PROFK_OK;
+}
+
+namespace {
+std::mutex g_memo_mu;
+std::map<std::tuple<int64_t, int64_t, double, int64_t, int64_t, int64_t, double, int64_t, int64_t>,
+         profk_params>
+    g_memo;
+}  // namespace
+
+int solve_memo(int64_t N, int64_t k, double eps, const profk_options* opt, profk_params* out) {
+  profk_options o{};
+  if (opt) o = *opt;
+  auto key = std::make_tuple(N, k, eps, o.s_override, o.s_min, o.s_max, o.s_prefactor, o.force_t, o.force_M);
+  {
+    std::lock_guard<std::mutex> g(g_memo_mu);
+    auto it = g_memo.find(key);
+    if (it != g_memo.end()) {
+      if (out) *out = it->second;
+      return PROFK_OK;
+    }
+  }
+  profk_params p{};
+  int rc = solve(N, k, eps, opt, &p);
+  if (rc != PROFK_OK) return rc;
+  {
+    std::lock_guard<std::mutex> g(g_memo_mu);
+    if (g_memo.size() > 4096) g_memo.clear();
+    g_memo[key] = p;
+  }
+  if (out) *out = p;
+  return PROFK_OK;
+}
+
+}  // namespace profk

@@ -1,0 +1,193 @@
+"""GPU parity of every stage of the HIP path against the CPU oracle.
+
+Bar: bit-exact (indices, value bits, counts, sample sets).  Each test prints
+its case before touching the GPU.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sampling_threshold_filtering_amd as stf
+from oracle import method_ref
+from workloads import edge_case, generate
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def check_topk(x_np, vals, idx, k):
+    ov, oi = oracle.topk(x_np, k, nthreads=8)
+    np.testing.assert_array_equal(host(idx), oi)
+    np.testing.assert_array_equal(host(vals).view(np.uint32), ov.view(np.uint32))
+
+
+# ----------------------------------------------------------------------------- stage 1
+@pytest.mark.parametrize("N,S,seed,attempt", [(1 << 20, 32768, 0, 0), (1 << 20, 32768, 7, 3), (5000, 2500, 1, 0),
+                                              (4096, 2048, 2, 1), (123457, 1000, 99, 0), (1 << 22, 131072, 5, 0)])
+def test_sample_matches_oracle(N, S, seed, attempt):
+    say("sample", N, S, seed, attempt)
+    x = generate("uniform", N, seed=1)
+    got = np.sort(host(stf.stage_sample(dev(x), S, seed=seed, attempt=attempt)))
+    ref = method_ref.sample_indices(N, S, seed=seed, attempt=attempt)
+    np.testing.assert_array_equal(got, ref)
+
+
+# ----------------------------------------------------------------------------- stage 2
+@pytest.mark.parametrize("kind,N,S,t,seed", [("uniform", 1 << 20, 32768, 4, 0), ("normal", 1 << 20, 32768, 118, 3),
+                                             ("few_levels", 100000, 20000, 500, 1),
+                                             ("adv_noise", 1 << 20, 32768, 7, 2),
+                                             ("signed_zeros", 50000, 10000, 3000, 4),
+                                             ("uniform", 1 << 22, 131072, 1, 9)])
+def test_threshold_matches_oracle(kind, N, S, t, seed):
+    say("threshold", kind, N, S, t, seed)
+    x = edge_case(kind, N, 5) if kind in ("few_levels", "signed_zeros") else generate(kind, N, seed=5)
+    v, i = stf.stage_threshold(dev(x), S, t, seed=seed)
+    sample = method_ref.sample_indices(N, S, seed=seed)
+    rv, ri = method_ref.threshold(x, sample, t)
+    assert int(host(i)[0]) == ri
+    assert host(v).view(np.uint32)[0] == np.float32(rv).view(np.uint32)
+
+
+# ----------------------------------------------------------------------------- stage 3
+@pytest.mark.parametrize("kind,N,offset,M,rank", [("normal", 1 << 20, 0, 5000, 3000), ("normal", 1000003, 1, 5000, 3000),
+                                                  ("uniform", 1 << 22, 3, 100000, 70000),
+                                                  ("few_levels", 65537, 2, 70000, 40000),
+                                                  ("normal", 300001, 0, 100, 2000),  # overflow: R > M
+                                                  ("normal", 7, 1, 8, 5), ("normal", 3, 0, 4, 2),
+                                                  ("with_nan", 100000, 0, 1000, 500)])
+def test_filter_matches_oracle(kind, N, offset, M, rank):
+    say("filter", kind, N, offset, M, rank)
+    x = generate(kind, N + offset, seed=11) if kind in ("normal", "uniform") else edge_case(kind, N + offset, 11)
+    xs = x[offset:]
+    order = np.array(sorted(range(N), key=lambda i: method_ref.order_key(float(xs[i]), i))) if N < 2000 else None
+    if order is not None:
+        tau_i = int(order[rank - 1])
+    else:
+        # tau = the rank-th entry in the total order, from the oracle top-k
+        _, oi = oracle.topk(xs, rank, nthreads=8)
+        tau_i = int(oi[-1])
+    tau_v = xs[tau_i]
+    xd = dev(x)[offset:]  # misaligned views exercise the scalar head
+    R, cand = stf.stage_filter(xd, float(tau_v), tau_i, M)
+    assert R == oracle.count_at_or_before(xs, tau_v, tau_i) == rank
+    got = np.sort(host(cand))
+    ref = method_ref.candidate_set(xs, tau_v, tau_i)
+    if R <= M:
+        np.testing.assert_array_equal(got, ref)
+    else:
+        assert len(got) == M and len(np.unique(got)) == M and np.isin(got, ref).all()
+
+
+# ----------------------------------------------------------------------------- end to end
+SMALL = [
+    ("uniform", 1 << 22, 32, {}),                       # first workload, default parameters
+    ("normal", 1 << 20, 1, {"s_override": 8192}),
+    ("normal", 1 << 20, 1000, {"s_override": 8192}),
+    ("normal", 1 << 20, 9000, {"s_override": 16384}),   # multi-block sort path (k > 8192)
+    ("few_levels", 300007, 777, {"s_override": 4096}),  # heavy ties
+    ("adv_noise", 1 << 20, 5000, {"s_override": 8192}),  # all values share the top 24 bits
+    ("adv_levels", 1 << 21, 2048, {"s_override": 8192}),
+    ("signed_zeros", 200000, 100, {"s_override": 4096}),
+    ("with_inf", 500000, 300, {"s_override": 8192}),
+    ("with_nan", 500000, 300, {"s_override": 8192}),
+    ("negative", 400000, 64, {"s_override": 8192}),
+    ("ascending", 1 << 20, 100, {"s_override": 8192}),
+    ("descending", 1 << 20, 100, {"s_override": 8192}),
+]
+
+
+@pytest.mark.parametrize("kind,N,k,opts", SMALL)
+def test_topk_matches_oracle(kind, N, k, opts):
+    say("topk", kind, N, k, opts)
+    x = generate(kind, N, seed=21) if kind in ("uniform", "normal", "adv_noise", "adv_levels") else edge_case(kind, N, 21)
+    vals, idx, st = stf.topk(dev(x), k, eps=1e-3, seed=3, options=opts or None, stats=True)
+    check_topk(x, vals, idx, k)
+    assert not st["fallback"] and st["attempts"] >= 1
+
+
+@pytest.mark.parametrize("N,k,offset", [(1, 1, 0), (5, 3, 1), (1000, 1000, 2), (4096, 17, 3), (100003, 5000, 1)])
+def test_exact_path_small_and_misaligned(N, k, offset):
+    say("exact path", N, k, offset)
+    x = generate("normal", N + offset, seed=N)
+    vals, idx, st = stf.topk(dev(x)[offset:], k, stats=True)
+    check_topk(x[offset:], vals, idx, k)
+    assert st["fallback"]  # N too small for sampling: the exact selection runs
+
+
+def test_forced_overflow_goes_to_fallback_and_stays_exact():
+    say("forced overflow M = k")
+    N, k = 1 << 22, 4096
+    x = generate("adv_levels", N, seed=8)
+    vals, idx, st = stf.topk(dev(x), k, options={"force_M": k}, stats=True)
+    check_topk(x, vals, idx, k)
+    assert st["attempts"] == 6 and st["fallback"]
+    assert all(m == 2 for m in st["fail_mode"])  # every attempt overflowed (R > M)
+
+
+def test_forced_recall_failure_retries():
+    say("forced recall failure t = 1")
+    N, k = 1 << 22, 1 << 14
+    x = generate("normal", N, seed=9)
+    vals, idx, st = stf.topk(dev(x), k, options={"force_t": 1}, stats=True)
+    check_topk(x, vals, idx, k)
+    assert st["fail_mode"][0] == 1  # R < k with t = 1 at this k
+
+
+def test_forced_fallback_and_max_attempts_zero():
+    say("force_fallback")
+    x = generate("pareto", 1 << 21, seed=4)
+    for opts in ({"force_fallback": 1}, {"use_max_attempts": 1, "max_attempts": 0}):
+        vals, idx, st = stf.topk(dev(x), 3000, options=opts, stats=True)
+        check_topk(x, vals, idx, 3000)
+        assert st["fallback"] and st["attempts"] == 0
+
+
+def test_fallback_with_huge_tie_group():
+    say("fallback, 256-value input")
+    x = generate("adv_noise", 1 << 22, seed=6)
+    vals, idx = stf.topk(dev(x), 20000, options={"force_fallback": 1})
+    check_topk(x, vals, idx, 20000)
+
+
+def test_seed_does_not_change_result_and_repeats_are_identical():
+    say("determinism")
+    x = generate("normal", 1 << 22, seed=12)
+    xd = dev(x)
+    v0, i0 = stf.topk(xd, 1000, seed=0)
+    for seed in (1, 2, 12345678901234):
+        v, i = stf.topk(xd, 1000, seed=seed)
+        assert (host(i) == host(i0)).all() and (host(v) == host(v0)).all()
+    check_topk(x, v0, i0, 1000)
+
+
+def test_batched_matches_oracle():
+    say("batched 16 x 2^18, k = 64")
+    B, N, k = 16, 1 << 18, 64
+    x = generate("normal", B * N, seed=13).reshape(B, N)
+    vals, idx = stf.topk_batched(dev(x), k, options={"s_override": 4096})
+    ov, oi = oracle.topk_batched(x, k)
+    np.testing.assert_array_equal(host(idx), oi)
+    np.testing.assert_array_equal(host(vals).view(np.uint32), ov.view(np.uint32))
+
+
+def test_rejects_bad_arguments_on_device():
+    import torch
+    x = torch.zeros(100, device="cuda")
+    with pytest.raises(stf.ProfkError):
+        stf.topk(x, 0)
+    with pytest.raises(stf.ProfkError):
+        stf.topk(x, 101)
+    with pytest.raises(stf.ProfkError):
+        stf.topk(x, 10, eps=0.0)

@@ -1,0 +1,113 @@
+"""CPU-side checks of libprofk.so: it loads, exports the declared ABI, and its
+host-only parameter solver agrees with the oracle's scipy reference.
+
+The solver follows "Prof-K: Probabilistic One-Pass Filtering for Efficient
+Top-k Selection": Theorem 4 / Eq. 5-7 of the arXiv page for (t*, M*) and the
+failure probabilities; the earlier version's Algorithm 1, Theorem 5 and
+Corollary 4 for z, the S rule and the closed-form M.
+"""
+import math
+import os
+import re
+
+import pytest
+
+import sampling_threshold_filtering_amd as stf
+from oracle import solver_ref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "profk.h")).read()
+    return sorted(set(re.findall(r"\b(profk_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = stf.load_library()
+    names = declared_functions()
+    assert set(names) == set(stf.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_messages():
+    lib = stf.load_library()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.profk_strerror(code)
+
+
+WORKLOADS = [(1 << 22, 32, 1e-3), (1 << 26, 32, 1e-3), (1 << 26, 1024, 1e-3), (1 << 26, 32768, 1e-3),
+             (50331648, 131072, 1e-3), (1 << 30, 32, 1e-3), (1 << 30, 1024, 1e-3), (1 << 30, 32768, 1e-3),
+             (1 << 30, 1 << 19, 1e-3), (1 << 20, 64, 1e-3 / 1024), (1 << 30, 1 << 19, 1e-4),
+             (1 << 24, 8192, 1e-2), (123457, 17, 0.05)]
+
+
+@pytest.mark.parametrize("N,k,eps", WORKLOADS)
+def test_solver_matches_reference(N, k, eps):
+    lib_p = stf.solve(N, k, eps)
+    ref = solver_ref.solve(N, k, eps)
+    for name in ("S", "t_star", "M_star", "t_eq6", "t", "M"):
+        assert lib_p[name] == getattr(ref, name), (name, lib_p[name], getattr(ref, name))
+    for lname, rname in (("z", "z"), ("z_a", "z_a"), ("S_raw", "S_raw"), ("M_cf", "M_cf"),
+                         ("E_R", "E_R"), ("Var_R", "Var_R")):
+        assert math.isclose(lib_p[lname], getattr(ref, rname), rel_tol=1e-6), lname
+    # probabilities: relative 1e-6, or absolute 1e-12 where they are tiny
+    assert math.isclose(lib_p["p_recall"], ref.p_recall, rel_tol=1e-6, abs_tol=1e-12)
+    assert math.isclose(lib_p["p_overflow"], ref.p_overflow, rel_tol=1e-6, abs_tol=1e-12)
+    assert lib_p["p_recall"] + lib_p["p_overflow"] <= eps
+
+
+def test_solver_reproduces_table3(golden_dir):
+    from tests.test_oracle_solver import load_table3
+    for r in load_table3(golden_dir):
+        p = stf.solve(r["N"], r["k"], 1e-3, options={"s_override": r["S"]})
+        assert p["S"] == r["S"]
+        assert p["t_star"] == r["t_star"], r
+        assert p["M_star"] == r["M_star"], r
+
+
+def test_solver_worked_example_and_clamp():
+    p = stf.solve(10**9, 100, 1e-3)
+    assert abs(p["S_raw"] - 4600) <= 0.02 * 4600  # earlier version, text after Theorem 5
+    assert p["S"] == 32768
+    assert abs(p["z"] - 6.58) < 0.005
+    p = stf.solve((1 << 32) - 1, 1 << 20, 1e-3)
+    assert p["S"] == 131072  # upper clamp
+
+
+def test_solver_options_and_degenerate_cases():
+    p = stf.solve(1 << 24, 100, 1e-3, options={"force_t": 1, "force_M": 100})
+    assert p["t"] == 1 and p["M"] == 100
+    # t = 1 fails recall iff some sample lands in the top k-1 = 99 (P1 Proposition 2)
+    assert math.isclose(p["p_recall"], solver_ref.hyp_sf(0, 1 << 24, 99, p["S"]), rel_tol=1e-6)
+    # small N: the sample would be more than half the input, go straight to the exact path
+    assert stf.solve(50000, 10, 1e-3)["direct_exact"] == 1
+    # buffer larger than half the input: exact path
+    assert stf.solve(1 << 20, 1 << 19, 1e-3)["direct_exact"] == 1
+    assert stf.solve(1 << 26, 1024, 1e-3)["direct_exact"] == 0
+    # k = 1: t* = 1 and no recall failure is possible
+    p = stf.solve(1 << 26, 1, 1e-3)
+    assert p["t_star"] == 1 and p["p_recall"] == 0.0
+
+
+def test_solver_rejects_bad_arguments():
+    for args in ((0, 1, 1e-3), (10, 0, 1e-3), (10, 11, 1e-3), (10, 2, 0.0), (10, 2, 1.0), (10, 2, float("nan"))):
+        with pytest.raises(stf.ProfkError) as e:
+            stf.solve(*args)
+        assert e.value.code == stf.PROFK_EINVAL
+    with pytest.raises(stf.ProfkError) as e:
+        stf.solve(1 << 32, 10, 1e-3)
+    assert e.value.code == stf.PROFK_EUNSUPPORTED
+
+
+def test_product_package_does_not_reference_the_oracle():
+    pkg = os.path.join(ROOT, "sampling_threshold_filtering_amd")
+    for dirpath, _, files in os.walk(pkg):
+        if "_build" in dirpath:
+            continue
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "topk_oracle" not in text and "liboracle" not in text, f
