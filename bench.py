@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Throughput of Prof-K exact top-k on one MI355X.
+
+Workload: one flat fp32 tensor of N = 2^30 Pareto(alpha = 1.5, x_m = 1) values
+(seed 0, generated on the host by workloads.py and copied to HBM before
+timing), exact top-k for k in {2^5, 2^10, 2^15, 2^19}, eps = 1e-3.  One
+"step" is the whole k sweep: four exact top-k calls over the resident tensor,
+each including its sampling, threshold, filter, refinement and the one host
+synchronisation that reads the count R.  `value` = 4 N / step time in Gelem/s.
+
+Also printed (same JSON line):
+  per_k        ms, Gelem/s and algorithmic GB/s (4N bytes per call) per k
+  roofline     the filter kernel: algorithmic bytes (4N read + 8R written) per
+               launch / its launch time from HIP events recorded by the library
+               around the filter on the same stream; peak 8 TB/s
+  batched      1024 rows x 2^20, top-64 per row (same tensor, reshaped)
+  cpu_baseline the CPU oracle (plain C heap top-k) on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+KS = (1 << 5, 1 << 10, 1 << 15, 1 << 19)
+EPS = 1e-3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--log2n", type=int, default=30, help="input size (default: the 2^30 workload)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-batched", action="store_true", help="skip the batched variant")
+    return ap.parse_args()
+
+
+def filter_source_hash() -> str:
+    p = os.path.join(ROOT, "sampling_threshold_filtering_amd", "csrc", "k_filter.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_record(n: int):
+    """HBM bytes per filter launch from the committed rocprofv3 counter summary, if it
+    was taken on the current filter source and at this size; else None."""
+    p = os.path.join(ROOT, "profiles", "filter_traffic_pareto_2p30.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if rec.get("filter_source_sha256_16") != filter_source_hash() or rec.get("N") != n:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(x: np.ndarray):
+    import oracle
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(16, cores))
+    n = min(x.size, 1 << 27)
+    sample = x[:n]
+    oracle.topk(sample[: 1 << 20], 32, nthreads=threads)  # warm the library and pages
+    t0 = time.perf_counter()
+    for k in KS:
+        oracle.topk(sample, k, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(KS) * n / dt / 1e9, 4), "unit": "Gelem/s", "cores": threads, "kind": "oracle",
+            "sample": f"first 2^{n.bit_length() - 1} values of the same tensor, k sweep {list(KS)}, "
+                      f"{dt:.2f} s total; plain C heap top-k, {threads} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes of the design document); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sampling_threshold_filtering_amd as stf
+    from workloads import generate
+
+    N = 1 << args.log2n
+    t_gen = time.perf_counter()
+    x = generate("pareto", N, seed=0)
+    gen_s = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    xd = torch.from_numpy(x).to(dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    opts = stf.make_options(timing=1)
+
+    per_k = {}
+    filt_bytes = 0.0
+    filt_ms = 0.0
+    total_ms = 0.0
+    retries = 0
+    for k in KS:
+        for _ in range(args.warmup):
+            stf.topk(xd, k, eps=EPS, seed=0, options=opts)
+        torch.cuda.synchronize()
+        times = []
+        for s in range(args.steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            _, _, st = stf.topk(xd, k, eps=EPS, seed=s, options=opts, stats=True)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+            filt_ms += st["filter_ms"]
+            filt_bytes += 4.0 * N + 8.0 * st["R"][-1]
+            retries += st["attempts"] - 1
+        ms = float(np.mean(times))
+        total_ms += ms
+        per_k[str(k)] = {"ms": round(ms, 4), "gelem_s": round(N / ms / 1e6, 2),
+                         "alg_GBps": round(4.0 * N / ms / 1e6, 1),
+                         "frac_of_hbm_peak": round(4.0 * N / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+    torch.cuda.synchronize()
+
+    n_filter = args.steps * len(KS)
+    achieved = filt_bytes / n_filter / (filt_ms / n_filter / 1e3) / 1e9
+    traffic = traffic_record(N)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "filter_kernel", "filter_ms_avg": round(filt_ms / n_filter, 4),
+                "bytes_per_launch_alg": round(filt_bytes / n_filter)}
+
+    batched = None
+    if not args.no_batched and N >= (1 << 20) * 16:
+        B = min(1024, N >> 20)
+        xb = xd[: B << 20].view(B, 1 << 20)
+        for _ in range(max(1, args.warmup)):
+            stf.topk_batched(xb, 64, eps=EPS, seed=0)
+        torch.cuda.synchronize()
+        bt = []
+        for s in range(max(1, args.steps // 2)):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            stf.topk_batched(xb, 64, eps=EPS, seed=s)
+            e1.record(stream)
+            e1.synchronize()
+            bt.append(e0.elapsed_time(e1))
+        bms = float(np.mean(bt))
+        batched = {"rows": B, "row_len": 1 << 20, "k": 64, "ms": round(bms, 4),
+                   "gelem_s": round((B << 20) / bms / 1e6, 2)}
+
+    cpu = None if args.no_cpu else cpu_baseline(x)
+
+    value = len(KS) * N / (total_ms / 1e3) / 1e9
+    line = {
+        "metric": "Gelem/s + % of HBM peak, exact top-k N=2^30 fp32, k=2^5..2^19, 1 GPU",
+        "value": round(value, 2),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"Pareto(1.5) fp32 flat tensor N=2^{args.log2n}, seed 0, exact top-k k sweep "
+                               f"{list(KS)}, eps=1e-3", "N": N, "ks": list(KS), "eps": EPS},
+        "hbm_frac_alg": round(4.0 * N * len(KS) / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "per_k": per_k,
+        "retries": retries,
+        "roofline": roofline,
+        "batched": batched,
+        "cpu_baseline": cpu,
+        "host_gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -217,10 +217,8 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   if (rc) return rc;
   HIPCHK(launch_attempt_init(ctl, sel, rec, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
   HIPCHK(launch_sample(x, N, S, seed, attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
-                       at<u64>(w, L.keys), ctl, sel, t, s),
+                       at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, t, s),
          "launch sample");
-  HIPCHK(launch_select_keys(at<u64>(w, L.keys), &ctl->D, S, sel, at<u64>(w, L.col), &ctl->tau, &ctl->status, s),
-         "launch select(sample)");
   FilterArgs fa{};
   fa.x = x;
   fa.ld = N;
@@ -363,7 +361,7 @@ int profk_stage_sample(const float* x, int64_t N, int64_t S, uint64_t seed, int3
   SelState* sel = at<SelState>(w, L.sel);
   HIPCHK(launch_attempt_init(ctl, sel, nullptr, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
   HIPCHK(launch_sample(x, (u64)N, (u64)S, seed, (u32)attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
-                       at<u64>(w, L.keys), ctl, sel, 1, s),
+                       at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, 0, s),
          "launch sample");
   HIPCHK(launch_keys_to_index(at<u64>(w, L.keys), &ctl->D, (u64)S, out_idx, s), "launch keys_to_index");
   HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
@@ -386,10 +384,8 @@ int profk_stage_threshold(const float* x, int64_t N, int64_t S, int64_t t, uint6
   SelState* sel = at<SelState>(w, L.sel);
   HIPCHK(launch_attempt_init(ctl, sel, nullptr, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
   HIPCHK(launch_sample(x, (u64)N, (u64)S, seed, (u32)attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
-                       at<u64>(w, L.keys), ctl, sel, (u64)t, s),
+                       at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, (u64)t, s),
          "launch sample");
-  HIPCHK(launch_select_keys(at<u64>(w, L.keys), &ctl->D, (u64)S, sel, at<u64>(w, L.col), &ctl->tau, &ctl->status, s),
-         "launch select");
   HIPCHK(launch_tau_to_output(x, (u64)N, ctl, out_tau_val, out_tau_idx, s), "launch tau_to_output");
   u32 status = 0;
   HIPCHK(hipMemcpyAsync(&status, &ctl->status, sizeof(u32), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");

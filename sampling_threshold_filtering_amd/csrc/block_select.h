@@ -1,0 +1,135 @@
+// Radix selection by ONE workgroup: the key of a given rank (descending) among n
+// distinct 64-bit keys in global memory, and an LDS bitonic sort.
+//
+// Used where the whole selection is small enough for one compute unit: the
+// threshold tau of Prof-K ("Prof-K: Probabilistic One-Pass Filtering for Efficient
+// Top-k Selection", §3 stage 2: the t-th largest of the S sampled values, S at most
+// 131072) and the per-row stages of the batched form.  Each pass reads the keys
+// that still match the fixed prefix from L2, histograms the next 8-bit digit in
+// LDS (one LDS atomic per distinct digit per wavefront) and fixes it; once at most
+// `cap` keys match they are gathered into LDS and sorted, and the answer is read
+// off.  Every launch-free pass costs one read of the keys.
+#pragma once
+
+#include "profk_device.h"
+
+namespace profk {
+
+// Descending bitonic sort of s[0..P), P a power of two, by the whole block.
+__device__ inline void block_bitonic_desc(u64* s, u32 P) {
+  for (u32 k = 2; k <= P; k <<= 1) {
+    for (u32 j = k >> 1; j > 0; j >>= 1) {
+      for (u32 i = threadIdx.x; i < P; i += blockDim.x) {
+        const u32 ixj = i ^ j;
+        if (ixj > i) {
+          const u64 a = s[i], b = s[ixj];
+          const bool up = (i & k) == 0;
+          if (up ? (a < b) : (a > b)) {
+            s[i] = b;
+            s[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+struct BlockSelectLds {
+  u32 hist[256];
+  u32 ncol;
+  u32 pick;
+  u64 prefix, mask, rank, count;
+  u32 ok;
+};
+
+// Returns the key of 1-based rank `rank` (descending) among keys[0..n); `buf` is an
+// LDS array of `cap` keys (cap a power of two).  All threads get the result; *ok is
+// false when the state turned out inconsistent (never for distinct keys).
+__device__ inline u64 block_select_rank(const u64* keys, u64 n, u64 rank, u64* buf, u32 cap, BlockSelectLds* L,
+                                        bool* ok_out) {
+  if (threadIdx.x == 0) {
+    L->prefix = 0;
+    L->mask = 0;
+    L->rank = rank;
+    L->count = n;
+    L->ok = (rank >= 1 && rank <= n) ? 1u : 0u;
+  }
+  __syncthreads();
+  for (u32 digit = 0; digit < 8 && L->ok; ++digit) {
+    const u64 prefix = L->prefix, mask = L->mask, count = L->count;
+    if (count <= cap) break;
+    const u32 shift = 56u - 8u * digit;
+    for (u32 b = threadIdx.x; b < 256; b += blockDim.x) L->hist[b] = 0;
+    __syncthreads();
+    for (u64 base = 0; base < n; base += blockDim.x) {
+      const u64 i = base + threadIdx.x;
+      const bool in = i < n;
+      const u64 key = in ? keys[i] : 0ull;
+      const bool match = in && ((key & mask) == prefix);
+      wave_hist_add(L->hist, (u32)(key >> shift) & 255u, match);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      u64 cum = 0;
+      int b = 255;
+      for (; b >= 0; --b) {
+        const u64 c = L->hist[b];
+        if (cum + c >= L->rank) break;
+        cum += c;
+      }
+      if (b < 0) {
+        L->ok = 0;
+      } else {
+        L->rank -= cum;
+        L->count = L->hist[b];
+        L->prefix = prefix | ((u64)b << shift);
+        L->mask = mask | (0xFFull << shift);
+      }
+    }
+    __syncthreads();
+  }
+  u64 result = 0;
+  if (L->ok) {
+    const u64 prefix = L->prefix, mask = L->mask, count = L->count;
+    if (count > cap || count == 0) {
+      if (threadIdx.x == 0) L->ok = 0;
+    } else {
+      if (threadIdx.x == 0) L->ncol = 0;
+      __syncthreads();
+      for (u64 base = 0; base < n; base += blockDim.x) {
+        const u64 i = base + threadIdx.x;
+        const bool in = i < n;
+        const u64 key = in ? keys[i] : 0ull;
+        const bool match = in && ((key & mask) == prefix);
+        const u64 m = __ballot(match);
+        u32 slot = 0;
+        if (m) {
+          const u32 leader = __ffsll((long long)m) - 1;
+          if (lane_id() == leader) slot = atomicAdd(&L->ncol, (u32)__popcll(m));
+          slot = __shfl(slot, leader) + count_below(m);
+        }
+        if (match && slot < cap) buf[slot] = key;
+      }
+      __syncthreads();
+      const u32 m = L->ncol;
+      if (m != count) {
+        if (threadIdx.x == 0) L->ok = 0;
+      } else {
+        u32 P = 1;
+        while (P < m) P <<= 1;
+        for (u32 i = m + threadIdx.x; i < P; i += blockDim.x) buf[i] = 0ull;
+        __syncthreads();
+        block_bitonic_desc(buf, P);
+      }
+    }
+  }
+  __syncthreads();
+  const bool ok = L->ok != 0;
+  if (ok) result = buf[L->rank - 1];
+  __syncthreads();
+  *ok_out = ok;
+  return result;
+}
+
+}  // namespace profk

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
 
   const u64 nwaves = (u64)gridDim.x * kWavesPerBlock;
   for (u64 g = (u64)blockIdx.x * kWavesPerBlock + wid; g < a.total_tiles; g += nwaves) {
-    const u64 lr = g / a.tiles_per_row;
+    const u64 lr = a.nrows == 1 ? 0 : g / a.tiles_per_row;
     const u64 tile = g - lr * a.tiles_per_row;
     const u32 row = a.rows ? (u32)a.rows[lr] : (u32)lr;
     const RowGeom geo = row_geom(a.x, a.ld, a.N, row);
@@ -191,10 +191,45 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
       stage_hits<1>(st, row, masks, hit, key, a.ctls, a.cand, a.M);
     }
   }
-  stage_flush(st, a.ctls, a.cand, a.M);
+  // End of the stream: the block's waves reserve their staged keys with one
+  // atomic per row they hold (one in the flat case) instead of one per wave.
+  __shared__ u32 s_n[kWavesPerBlock], s_row[kWavesPerBlock];
+  __shared__ u64 s_base[kWavesPerBlock];
+  if (lane == 0) {
+    s_n[wid] = st.n;
+    s_row[wid] = st.row;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      if (s_n[w] == 0) continue;
+      bool first = true;
+      for (int v = 0; v < w; ++v)
+        if (s_n[v] && s_row[v] == s_row[w]) first = false;
+      if (!first) continue;
+      u64 tot = 0;
+      for (int v = w; v < kWavesPerBlock; ++v)
+        if (s_n[v] && s_row[v] == s_row[w]) {
+          s_base[v] = tot;
+          tot += s_n[v];
+        }
+      const u64 b = atomicAdd(&a.ctls[s_row[w]].R, tot);  // returns: performed at the coherence point
+      for (int v = w; v < kWavesPerBlock; ++v)
+        if (s_n[v] && s_row[v] == s_row[w]) s_base[v] += b;
+    }
+  }
+  __syncthreads();
+  if (st.n) {
+    const u64 base = s_base[wid];
+    u64* dst = a.cand + (u64)st.row * a.M;
+    for (u32 j = lane; j < st.n; j += kWave)
+      if (base + j < a.M) dst[base + j] = st.buf[j];
+  }
 
-  // last block: run-time check per row, host record, arm the refinement selection
-  __threadfence();
+  // Last block: run-time check per row, host record, arm the refinement selection.
+  // Every R update above and in stage_flush is an atomic whose result was consumed
+  // before this block's ticket, so the counts are complete when the last ticket is
+  // drawn; no release fence (an L2 write-back on this part) is needed per block.
   __syncthreads();
   if (threadIdx.x == 0) s_last = (atomicAdd(a.ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
   __syncthreads();
@@ -203,7 +238,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   for (u64 lr = threadIdx.x; lr < a.nrows; lr += blockDim.x) {
     const u32 row = a.rows ? (u32)a.rows[lr] : (u32)lr;
     RowCtl* c = &a.ctls[row];
-    const u64 R = atomic_load_agent(&c->R);
+    const u64 R = atomicAdd(&c->R, 0ull);  // read at the coherence point
     u32 status = c->status;
     if (status == 0) status = R < a.k ? 1u : (R > a.M ? 2u : 0u);
     c->status = status;
@@ -236,7 +271,7 @@ hipError_t launch_filter(const FilterArgs& a0, u32 grid, hipStream_t s) {
   a.total_tiles = a.tiles_per_row * a.nrows;
   u64 need = (a.total_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
   if (need < 1) need = 1;
-  if (grid == 0) grid = 2048;
+  if (grid == 0) grid = kFilterBlocksPerCU * device_cu_count();
   if ((u64)grid > need) grid = (u32)need;
   filter_kernel<U, true><<<grid, kFilterThreads, 0, s>>>(a);
   return hipGetLastError();

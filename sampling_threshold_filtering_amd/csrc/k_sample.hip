@@ -6,15 +6,18 @@
 // (see profk_device.h for the draw).  That rule is symmetric under relabelling of
 // [N], so every S-subset is equally likely, and it is deterministic per seed.
 //
-//   sample_draw_kernel   draws 0..S-1 in parallel; each index goes into a hash set in
-//                        device memory (open addressing, 64-bit slots tagged with a
-//                        per-attempt generation so the table never needs clearing);
-//                        the first insert of each index gathers x[idx] into a key.
-//   sample_topup_kernel  one wavefront: while fewer than S distinct indices are held,
-//                        takes further draws S, S+1, ... in order, 64 at a time,
-//                        keeping those that are new and not repeated earlier in the
-//                        same chunk, until exactly S are held.  Expected extra draws
-//                        are about S^2 / (2N).
+//   sample_kernel   one thread per draw 0..S-1: each index goes into a hash set in
+//                   device memory (open addressing, 64-bit slots tagged with a
+//                   per-attempt generation so the table never needs clearing); the
+//                   first insert of each index gathers x[idx] into a key, and each
+//                   block reserves its key slots with one atomic.  The last block
+//                   then (a) tops up: while fewer than S distinct indices are held,
+//                   wavefront 0 takes further draws S, S+1, ... in order, 64 at a
+//                   time, keeping those that are new and not repeated earlier in the
+//                   same chunk (expected extra draws about S^2 / (2N)); and (b) selects
+//                   tau, the t-th largest of the S keys, by a one-workgroup radix
+//                   select (stage 2), so stages 1 and 2 cost a single launch.
+#include "block_select.h"
 #include "launch.h"
 
 namespace profk {
@@ -86,67 +89,107 @@ __global__ __launch_bounds__(64) void attempt_init_kernel(RowCtl* ctl, SelState*
   }
 }
 
-__global__ __launch_bounds__(256) void sample_draw_kernel(const float* __restrict__ x, u64 N, u64 S, u64 seed,
-                                                          u32 attempt, u32 row, u64* table, u64 tmask, u32 gen,
-                                                          u64* __restrict__ keys, RowCtl* ctl) {
-  const u64 j = (u64)blockIdx.x * blockDim.x + threadIdx.x;
+constexpr u32 kSampleThreads = 1024;
+constexpr u32 kTauCap = 8192;  // keys the last block sorts in LDS (64 KB)
+
+// Draws 0..S-1 (one per thread), dedupes them through the hash set and gathers
+// the keys of the first inserts; the block reserves its slots with ONE atomic.
+// The last block to finish then tops the sample up to exactly S distinct indices
+// (wavefront 0, draws S, S+1, ... in order) and, when t > 0, selects
+// tau = the t-th largest sampled key (P1 §3 stage 2) into ctl->tau.
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __restrict__ x, u64 N, u64 S,
+                                                                u64 seed, u32 attempt, u32 row, u64* table,
+                                                                u64 tmask, u32 gen, u64* __restrict__ keys,
+                                                                RowCtl* ctl, u32* ticket, u64 t) {
+  __shared__ u64 s_buf[kTauCap];
+  __shared__ BlockSelectLds s_sel;
+  __shared__ u32 s_wcnt[kSampleThreads / kWave];
+  __shared__ u64 s_base;
+  __shared__ u64 s_D;
+  __shared__ u32 s_last;
+  const u32 lane = lane_id(), wid = threadIdx.x / kWave;
+  const u64 j = (u64)blockIdx.x * kSampleThreads + threadIdx.x;
   bool fresh = false;
   u32 idx = 0;
   if (j < S) {
     idx = (u32)sample_draw(j, row, attempt, seed, N);
     fresh = hash_insert(table, tmask, gen, idx);
   }
-  const u64 slot = wave_reserve(&ctl->D, fresh);
-  if (fresh && slot < S) keys[slot] = make_key(__float_as_uint(x[idx]), idx);
-}
+  const u64 m = __ballot(fresh);
+  if (lane == 0) s_wcnt[wid] = (u32)__popcll(m);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    u32 tot = 0;
+    for (u32 w = 0; w < kSampleThreads / kWave; ++w) {
+      const u32 c = s_wcnt[w];
+      s_wcnt[w] = tot;
+      tot += c;
+    }
+    s_base = tot ? atomicAdd(&ctl->D, (u64)tot) : 0ull;
+  }
+  __syncthreads();
+  if (fresh) {
+    const u64 slot = s_base + s_wcnt[wid] + count_below(m);
+    if (slot < S) keys[slot] = make_key(__float_as_uint(x[idx]), idx);
+  }
+  // release this block's keys, then elect the last block
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    s_last = (atomicAdd(ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
 
-// One wavefront.  Also arms the threshold selection (rank t among the S keys).
-__global__ __launch_bounds__(64) void sample_topup_kernel(const float* __restrict__ x, u64 N, u64 S, u64 seed,
-                                                          u32 attempt, u32 row, u64* table, u64 tmask, u32 gen,
-                                                          u64* __restrict__ keys, RowCtl* ctl, SelState* sel,
-                                                          u64 t) {
-  const u32 lane = lane_id();
-  u64 D = ctl->D;
-  u64 j0 = S;
-  u32 guard = 0;
-  bool failed = false;
-  while (D < S) {
-    const u32 idx = (u32)sample_draw(j0 + lane, row, attempt, seed, N);
-    const bool held = hash_contains(table, tmask, gen, idx);
-    bool repeat = false;
-    for (int d = 1; d < kWave; ++d) {
-      const u32 other = __shfl_up(idx, d, kWave);
-      if ((int)lane >= d && other == idx) repeat = true;
+  // top-up by wavefront 0
+  if (wid == 0) {
+    u64 D = atomicAdd(&ctl->D, 0ull);
+    u64 j0 = S;
+    u32 guard = 0;
+    bool failed = false;
+    while (D < S) {
+      const u32 idx2 = (u32)sample_draw(j0 + lane, row, attempt, seed, N);
+      const bool held = hash_contains(table, tmask, gen, idx2);
+      bool repeat = false;
+      for (int d = 1; d < kWave; ++d) {
+        const u32 other = __shfl_up(idx2, d, kWave);
+        if ((int)lane >= d && other == idx2) repeat = true;
+      }
+      const bool ok2 = !held && !repeat;
+      const u64 m2 = __ballot(ok2);
+      const u64 need = S - D;
+      const u32 r = count_below(m2);
+      if (ok2 && r < need) {
+        hash_insert(table, tmask, gen, idx2);
+        keys[D + r] = make_key(__float_as_uint(x[idx2]), idx2);
+      }
+      const u64 got = (u64)__popcll(m2);
+      D += got < need ? got : need;
+      j0 += kWave;
+      if (++guard > (1u << 22)) {  // bounded: S <= N/2 makes each draw new with prob >= 1/2
+        failed = true;
+        break;
+      }
     }
-    const bool fresh = !held && !repeat;
-    const u64 m = __ballot(fresh);
-    const u64 need = S - D;
-    const u32 r = count_below(m);
-    if (fresh && r < need) {
-      hash_insert(table, tmask, gen, idx);
-      keys[D + r] = make_key(__float_as_uint(x[idx]), idx);
-    }
-    const u64 got = (u64)__popcll(m);
-    D += got < need ? got : need;
-    j0 += kWave;
-    if (++guard > (1u << 22)) {  // bounded: S <= N/2 makes each draw new with prob >= 1/2
-      failed = true;
-      break;
+    if (lane == 0) {
+      s_D = failed ? ~0ull : D;
+      ctl->D = D;
     }
   }
-  if (lane == 0) {
-    ctl->D = D;
-    if (failed) ctl->status = 3;
-    sel->prefix = 0;
-    sel->mask = 0;
-    sel->rank = t;
-    sel->count = D;
-    sel->done = failed ? 1u : 0u;
-    sel->digit = 0;
-    sel->ticket = 0;
-    sel->ncol = 0;
-    sel->error = failed ? 1u : 0u;
+  __syncthreads();
+  const bool sample_ok = s_D == S;
+  if (t > 0) {
+    bool ok = false;
+    const u64 tau = sample_ok ? block_select_rank(keys, S, t, s_buf, kTauCap, &s_sel, &ok) : 0ull;
+    if (threadIdx.x == 0) {
+      ctl->tau = tau;
+      if (!ok) ctl->status = 3;
+    }
+  } else if (threadIdx.x == 0 && !sample_ok) {
+    ctl->status = 3;
   }
+  if (threadIdx.x == 0) *ticket = 0;
 }
 
 // Stage-level helpers: keys -> int64 indices, tau -> (value, index).
@@ -193,10 +236,10 @@ hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u
 }
 
 hipError_t launch_sample(const float* x, u64 N, u64 S, u64 seed, u32 attempt, u32 row, u64* table, u64 tmask,
-                         u32 gen, u64* keys, RowCtl* ctl, SelState* sel, u64 t, hipStream_t s) {
-  const u32 blocks = (u32)((S + 255) / 256);
-  sample_draw_kernel<<<blocks, 256, 0, s>>>(x, N, S, seed, attempt, row, table, tmask, gen, keys, ctl);
-  sample_topup_kernel<<<1, 64, 0, s>>>(x, N, S, seed, attempt, row, table, tmask, gen, keys, ctl, sel, t);
+                         u32 gen, u64* keys, RowCtl* ctl, u32* ticket, u64 t, hipStream_t s) {
+  const u32 blocks = (u32)((S + kSampleThreads - 1) / kSampleThreads);
+  sample_kernel<<<blocks, kSampleThreads, 0, s>>>(x, N, S, seed, attempt, row, table, tmask, gen, keys, ctl, ticket,
+                                                  t);
   return hipGetLastError();
 }
 

@@ -177,26 +177,56 @@ __global__ __launch_bounds__(kSelThreads) void select_pass_kernel(Src src, SelSt
 // Writes every key >= *kth_ptr (exactly k of them when the selection is
 // consistent) to out[], and folds the OR / AND of the written keys into ctl
 // (which digits vary, for the sort).
+// Each block owns a contiguous range of the keys: it counts its selected keys,
+// reserves them with ONE atomic, then writes them in range order.
 template <class Src>
 __global__ __launch_bounds__(256) void compact_kernel(Src src, RowCtl* ctl, u64* __restrict__ out, u64 k) {
+  __shared__ u32 s_w[256 / kWave];
+  __shared__ u64 s_base;
   if (ctl->status != 0) return;
   const u64 kth = ctl->kth;
   const u64 n = src.size();
+  const u64 per = (n + gridDim.x - 1) / gridDim.x;
+  const u64 lo = (u64)blockIdx.x * per;
+  const u64 hi = lo + per < n ? lo + per : n;
+  const u32 wid = threadIdx.x / kWave;
+  u32 cnt = 0;
+  for (u64 i = lo + threadIdx.x; i < hi; i += blockDim.x) cnt += src.key(i) >= kth ? 1u : 0u;
+  for (int d = 32; d >= 1; d >>= 1) cnt += __shfl_xor(cnt, d);
+  if (lane_id() == 0) s_w[wid] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    u32 tot = 0;
+    for (u32 w = 0; w < blockDim.x / kWave; ++w) tot += s_w[w];
+    s_base = tot ? atomicAdd(&ctl->nsel, (u64)tot) : 0ull;
+  }
+  __syncthreads();
+  u64 run = s_base;
   u64 v_or = 0, v_and = ~0ull;
   bool any = false;
-  const u64 stride = (u64)gridDim.x * blockDim.x;
-  for (u64 base = (u64)blockIdx.x * blockDim.x; base < n; base += stride) {
+  for (u64 base = lo; base < hi; base += blockDim.x) {
     const u64 i = base + threadIdx.x;
-    const bool in = i < n;
+    const bool in = i < hi;
     const u64 key = in ? src.key(i) : 0ull;
     const bool sel = in && key >= kth;
-    const u64 slot = wave_reserve(&ctl->nsel, sel);
+    const u64 m = __ballot(sel);
+    __syncthreads();
+    if (lane_id() == 0) s_w[wid] = (u32)__popcll(m);
+    __syncthreads();
+    u64 off = run;
+    u32 tot = 0;
+    for (u32 w = 0; w < blockDim.x / kWave; ++w) {
+      if (w < wid) off += s_w[w];
+      tot += s_w[w];
+    }
     if (sel) {
+      const u64 slot = off + count_below(m);
       if (slot < k) out[slot] = key;
       v_or |= key;
       v_and &= key;
       any = true;
     }
+    run += tot;
   }
   // wave reduction of or / and
   for (int d = 32; d >= 1; d >>= 1) {
@@ -212,6 +242,11 @@ __global__ __launch_bounds__(256) void compact_kernel(Src src, RowCtl* ctl, u64*
 
 // ---------------------------------------------------------------------------
 namespace {
+// Few blocks per selection pass: every block adds its nonzero bins to the global
+// histogram with atomics, and hundreds of blocks contend on the same 256 words.
+constexpr u32 kSelMaxBlocks = 128;
+constexpr u32 kCompactMaxBlocks = 256;
+
 u32 select_grid(u64 n_max, u32 cap) {
   u64 g = (n_max + 1023) / 1024;  // about four keys per thread
   if (g < 1) g = 1;
@@ -223,7 +258,7 @@ u32 select_grid(u64 n_max, u32 cap) {
 hipError_t launch_select_keys(const u64* keys, const u64* n_ptr, u64 n_cap, SelState* st, u64* col, u64* result,
                               u32* status, hipStream_t s) {
   KeyArraySrc src{keys, n_ptr, n_cap};
-  const u32 g = select_grid(n_cap, 1024);
+  const u32 g = select_grid(n_cap, kSelMaxBlocks);
   for (int p = 0; p < 8; ++p) select_pass_kernel<KeyArraySrc><<<g, kSelThreads, 0, s>>>(src, st, col, result, status);
   return hipGetLastError();
 }
@@ -238,14 +273,14 @@ hipError_t launch_select_x(const float* x, u64 N, SelState* st, u64* col, u64* r
 hipError_t launch_compact_keys(const u64* keys, const u64* n_ptr, u64 n_cap, RowCtl* ctl, u64* out, u64 k,
                                hipStream_t s) {
   KeyArraySrc src{keys, n_ptr, n_cap};
-  const u32 g = select_grid(n_cap, 1024);
+  const u32 g = select_grid(n_cap, kCompactMaxBlocks);
   compact_kernel<KeyArraySrc><<<g, 256, 0, s>>>(src, ctl, out, k);
   return hipGetLastError();
 }
 
 hipError_t launch_compact_x(const float* x, u64 N, RowCtl* ctl, u64* out, u64 k, hipStream_t s) {
   FloatSrc src{x, N};
-  const u32 g = select_grid(N, 4096);
+  const u32 g = select_grid(N, 4 * kCompactMaxBlocks);
   compact_kernel<FloatSrc><<<g, 256, 0, s>>>(src, ctl, out, k);
   return hipGetLastError();
 }

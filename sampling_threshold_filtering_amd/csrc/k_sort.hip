@@ -10,8 +10,8 @@
 //     digit (per-block digit counts; one-block scan; stable scatter with
 //     wavefront match-ranking), skipping every digit that is equal across all
 //     k keys (known from the OR / AND folded by the compaction); then the output
-//     write.  Buffers ping-pong by a device-side index so skipped digits cost
-//     nothing but an early return.
+//     write.  The buffer a pass reads is the parity of the varying digits below
+//     it, so skipped digits cost nothing but an early return.
 #include "launch.h"
 
 namespace profk {
@@ -23,6 +23,14 @@ constexpr u32 kSortTile = kSortThreads * kSortItems;  // keys per block
 
 __device__ __forceinline__ bool digit_varies(const RowCtl* c, u32 d) {
   return (((c->key_or ^ c->key_and) >> (8u * d)) & 0xFFull) != 0;
+}
+
+// Which ping-pong buffer holds the keys before digit d is processed: every digit
+// that varies moves them once, the others are skipped.
+__device__ __forceinline__ u32 buffer_before(const RowCtl* c, u32 d) {
+  u32 moves = 0;
+  for (u32 i = 0; i < d; ++i) moves += digit_varies(c, i) ? 1u : 0u;
+  return moves & 1u;
 }
 
 __device__ __forceinline__ void write_one(const u64 key, u64 i, const float* row, u64 N, float* out_vals,
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(kSortThreads) void lsd_hist_kernel(u64* buf0, u64* 
                                                                 const RowCtl* ctl) {
   __shared__ u32 s_h[256];
   if (ctl->status != 0 || !digit_varies(ctl, d)) return;
-  const u64* src = ctl->cur ? buf1 : buf0;
+  const u64* src = buffer_before(ctl, d) ? buf1 : buf0;
   for (u32 b = threadIdx.x; b < 256; b += blockDim.x) s_h[b] = 0;
   __syncthreads();
   const u32 lo = blockIdx.x * kSortTile;
@@ -88,40 +96,43 @@ __global__ __launch_bounds__(kSortThreads) void lsd_hist_kernel(u64* buf0, u64* 
   for (u32 b = threadIdx.x; b < 256; b += blockDim.x) hist[b * G + blockIdx.x] = s_h[b];
 }
 
-// Exclusive scan over (digit, block) in digit-major order: hist -> offsets.
-__global__ __launch_bounds__(256) void lsd_scan_kernel(u32* hist, u32 G, u32 d, const RowCtl* ctl) {
-  __shared__ u32 s_tot[256];
+// Exclusive scan over (digit, block) in digit-major order: hist -> offsets.  The
+// digit-major layout makes this one exclusive scan of the 256*G words in array
+// order: each thread scans a contiguous run, the run totals are scanned in LDS.
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void lsd_scan_kernel(u32* hist, u32 G, u32 d, const RowCtl* ctl) {
+  __shared__ u32 s_tot[kScanThreads];
   if (ctl->status != 0 || !digit_varies(ctl, d)) return;
-  const u32 t = threadIdx.x;
+  const u32 total = 256u * G;
+  const u32 per = (total + kScanThreads - 1) / kScanThreads;
+  const u32 lo = threadIdx.x * per;
+  const u32 hi = lo + per < total ? lo + per : total;
   u32 run = 0;
-  for (u32 b = 0; b < G; ++b) {
-    const u32 c = hist[t * G + b];
-    hist[t * G + b] = run;
-    run += c;
-  }
-  s_tot[t] = run;
+  for (u32 i = lo; i < hi; ++i) run += hist[i];
+  s_tot[threadIdx.x] = run;
   __syncthreads();
-  if (t == 0) {
-    u32 acc = 0;
-    for (u32 i = 0; i < 256; ++i) {
-      const u32 c = s_tot[i];
-      s_tot[i] = acc;
-      acc += c;
-    }
+  // Hillis-Steele inclusive scan of the run totals
+  for (u32 off = 1; off < kScanThreads; off <<= 1) {
+    const u32 v = threadIdx.x >= off ? s_tot[threadIdx.x - off] : 0u;
+    __syncthreads();
+    s_tot[threadIdx.x] += v;
+    __syncthreads();
   }
-  __syncthreads();
-  const u32 base = s_tot[t];
-  for (u32 b = 0; b < G; ++b) hist[t * G + b] += base;
+  u32 acc = threadIdx.x ? s_tot[threadIdx.x - 1] : 0u;
+  for (u32 i = lo; i < hi; ++i) {
+    const u32 c = hist[i];
+    hist[i] = acc;
+    acc += c;
+  }
 }
 
-// Stable scatter of digit d; the last block flips the ping-pong index.
+// Stable scatter of digit d.
 __global__ __launch_bounds__(kSortThreads) void lsd_scatter_kernel(u64* buf0, u64* buf1, u32 n, u32 d,
-                                                                   const u32* hist, RowCtl* ctl) {
+                                                                   const u32* hist, const RowCtl* ctl) {
   __shared__ u32 s_run[256];
   __shared__ u32 s_cnt[kSortThreads / kWave][256];
-  __shared__ u32 s_last;
   if (ctl->status != 0 || !digit_varies(ctl, d)) return;
-  const u32 cur = ctl->cur;
+  const u32 cur = buffer_before(ctl, d);
   const u64* src = cur ? buf1 : buf0;
   u64* dst = cur ? buf0 : buf1;
   const u32 w = threadIdx.x / kWave;
@@ -159,15 +170,6 @@ __global__ __launch_bounds__(kSortThreads) void lsd_scatter_kernel(u64* buf0, u6
       for (u32 ww = 0; ww < kSortThreads / kWave; ++ww) s_cnt[ww][b] = 0;
     __syncthreads();
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&ctl->ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
-  __syncthreads();
-  if (s_last && threadIdx.x == 0) {
-    __threadfence();
-    ctl->cur = cur ^ 1u;
-    ctl->ticket = 0;
-  }
 }
 
 __global__ __launch_bounds__(256) void write_outputs_kernel(u64* buf0, u64* buf1, u32 k, const float* row,
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256) void write_outputs_kernel(u64* buf0, u64* buf1
     if (blockIdx.x == 0 && threadIdx.x == 0 && rec) rec->error = 1;
     return;
   }
-  const u64* src = ctl->cur ? buf1 : buf0;
+  const u64* src = buffer_before(ctl, 8) ? buf1 : buf0;
   for (u32 i = blockIdx.x * blockDim.x + threadIdx.x; i < k; i += gridDim.x * blockDim.x)
     write_one(src[i], i, row, N, out_vals, out_idx);
 }
@@ -195,7 +197,7 @@ hipError_t launch_sort_and_write(u64* buf0, u64* buf1, u32* hist, u32 k, const f
   const u32 G = (k + kSortTile - 1) / kSortTile;
   for (u32 d = 0; d < 8; ++d) {
     lsd_hist_kernel<<<G, kSortThreads, 0, s>>>(buf0, buf1, k, d, hist, ctl);
-    lsd_scan_kernel<<<1, 256, 0, s>>>(hist, G, d, ctl);
+    lsd_scan_kernel<<<1, kScanThreads, 0, s>>>(hist, G, d, ctl);
     lsd_scatter_kernel<<<G, kSortThreads, 0, s>>>(buf0, buf1, k, d, hist, ctl);
   }
   u32 wg = (k + 255) / 256;

@@ -7,6 +7,20 @@ namespace profk {
 
 constexpr u32 kSmallSort = 8192;  // keys sorted by one workgroup in LDS (64 KB)
 constexpr u32 kTickets = 64;      // u32 last-block tickets in the workspace, cleared every attempt
+constexpr u32 kFilterBlocksPerCU = 2;  // persistent filter grid: 2 blocks x 4 waves per CU
+
+// Compute units of the current device (cached per device).
+inline u32 device_cu_count() {
+  static u32 cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = (u32)n;
+  }
+  return cache[dev];
+}
 
 struct FilterArgs {
   const float* x;      // row 0
@@ -28,7 +42,7 @@ struct FilterArgs {
 hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u32* tickets, u32 nrows,
                                hipStream_t s);
 hipError_t launch_sample(const float* x, u64 N, u64 S, u64 seed, u32 attempt, u32 row, u64* table, u64 tmask,
-                         u32 gen, u64* keys, RowCtl* ctl, SelState* sel, u64 t, hipStream_t s);
+                         u32 gen, u64* keys, RowCtl* ctl, u32* ticket, u64 t, hipStream_t s);
 hipError_t launch_keys_to_index(const u64* keys, const u64* n_ptr, u64 n_cap, int64_t* out, hipStream_t s);
 hipError_t launch_tau_to_output(const float* x, u64 N, const RowCtl* ctl, float* out_val, int64_t* out_idx,
                                 hipStream_t s);

@@ -1,0 +1,149 @@
+"""Bit-exact parity at the full workload sizes, plus statistical checks of the
+threshold rank R and of the retry rate.
+
+Workloads (inputs from workloads.py, oracle = the plain C heap top-k):
+  uniform 2^22, k = 32                          (smoke-size workload)
+  normal / uniform 2^26, k in {32, 1024, 32768}
+  SAE-shaped pool 4096 x 12288, k = 131072 -> (row, latent, value)
+  Pareto(1.5) 2^30, k in {2^5, 2^10, 2^15, 2^19}; batched 1024 x 2^20, k = 64
+  radix-adversarial 2^30 (levels / noise), k = 2^19, eps = 1e-4; forced overflow M = k
+Statistics follow "Prof-K: Probabilistic One-Pass Filtering for Efficient Top-k
+Selection": the rank law of the earlier version's Lemma 1 (mean and variance)
+and the exact failure probabilities of the arXiv page's Propositions 2-3.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy.stats import binom
+
+import oracle
+import sampling_threshold_filtering_amd as stf
+from workloads import SAE_COLS, generate, sae_pool
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def check(x_np, vals, idx, k, nthreads=16):
+    ov, oi = oracle.topk(x_np, k, nthreads=nthreads)
+    np.testing.assert_array_equal(host(idx), oi)
+    np.testing.assert_array_equal(host(vals).view(np.uint32), ov.view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", ["normal", "uniform"])
+def test_2p26_k_sweep(kind):
+    x = generate(kind, 1 << 26, seed=0)
+    xd = dev(x)
+    for k in (32, 1024, 32768):
+        say("2^26", kind, k)
+        vals, idx, st = stf.topk(xd, k, eps=1e-3, seed=0, stats=True)
+        check(x, vals, idx, k)
+        assert not st["fallback"]
+
+
+def test_sae_pool():
+    say("sae 4096 x 12288, k = 131072")
+    pool = sae_pool(0)
+    x = pool.reshape(-1)
+    k = 32 * 4096
+    vals, idx, st = stf.topk(dev(x), k, eps=1e-3, seed=0, stats=True)
+    check(x, vals, idx, k)
+    i = host(idx)
+    rows, latents = i // SAE_COLS, i % SAE_COLS
+    np.testing.assert_array_equal(pool[rows, latents].view(np.uint32), host(vals).view(np.uint32))
+    assert (host(vals) > 0).all()  # the ~81% exact zeros never enter the top k
+
+
+@pytest.fixture(scope="module")
+def pareto_2p30():
+    return generate("pareto", 1 << 30, seed=0)
+
+
+def test_pareto_2p30_k_sweep(pareto_2p30):
+    x = pareto_2p30
+    xd = dev(x)
+    for k in (1 << 5, 1 << 10, 1 << 15, 1 << 19):
+        say("pareto 2^30", k)
+        vals, idx, st = stf.topk(xd, k, eps=1e-3, seed=0, stats=True)
+        check(x, vals, idx, k)
+        assert not st["fallback"]
+    del xd
+
+
+def test_pareto_batched_1024_rows(pareto_2p30):
+    say("pareto batched 1024 x 2^20, k = 64")
+    x = pareto_2p30.reshape(1024, 1 << 20)
+    vals, idx = stf.topk_batched(dev(x), 64, eps=1e-3, seed=0)
+    ov, oi = oracle.topk_batched(x, 64, nthreads=16)
+    np.testing.assert_array_equal(host(idx), oi)
+    np.testing.assert_array_equal(host(vals).view(np.uint32), ov.view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", ["adv_levels", "adv_noise"])
+def test_adversarial_2p30(kind):
+    x = generate(kind, 1 << 30, seed=0)
+    xd = dev(x)
+    k = 1 << 19
+    say("adversarial 2^30", kind, k)
+    vals, idx, st = stf.topk(xd, k, eps=1e-4, seed=0, stats=True)
+    check(x, vals, idx, k)
+    if kind == "adv_levels":
+        say("adversarial 2^30 forced overflow M = k")
+        vals, idx, st = stf.topk(xd, k, eps=1e-4, seed=0, options={"force_M": k}, stats=True)
+        check(x, vals, idx, k)
+        assert st["fallback"] and st["attempts"] == 6
+
+
+def test_threshold_rank_moments_on_gpu():
+    # R of the first attempt over many seeds vs the negative-hypergeometric mean / variance
+    N, k = 1 << 22, 32
+    x = generate("uniform", N, seed=0)
+    xd = dev(x)
+    p = stf.solve(N, k, 1e-3)
+    S, t = p["S"], p["t"]
+    n = 3000
+    R = np.empty(n)
+    say("R moments", N, k, S, t, n)
+    for seed in range(n):
+        _, _, st = stf.topk(xd, k, seed=seed, stats=True)
+        R[seed] = st["R"][0]
+    mean = (N + 1) * t / (S + 1)
+    var = t * (S - t + 1) * (N + 1) * (N - S) / ((S + 1) ** 2 * (S + 2))
+    assert abs(R.mean() - mean) <= 5 * math.sqrt(var / n)
+    m4 = float(((R - R.mean()) ** 4).mean())
+    assert abs(R.var() - var) <= 5 * math.sqrt(max(m4 - var * var, 0.0) / n)
+
+
+def test_retry_rate_matches_exact_prediction():
+    # first-attempt failures over 10^4 seeds: at most the 0.999 quantile of
+    # Binomial(n, p_pred), split into R < k and R > M
+    N, k, eps = 1 << 22, 32, 1e-3
+    x = generate("uniform", N, seed=0)
+    xd = dev(x)
+    p = stf.solve(N, k, eps)
+    p_pred = p["p_recall"] + p["p_overflow"]
+    assert p_pred <= eps
+    n = 10000
+    fails = {1: 0, 2: 0}
+    say("retry rate", N, k, n)
+    for seed in range(n):
+        vals, idx, st = stf.topk(xd, k, eps=eps, seed=seed, stats=True)
+        if st["fail_mode"][0]:
+            fails[st["fail_mode"][0]] += 1
+    total = fails[1] + fails[2]
+    print(f"observed R<k: {fails[1]}, R>M: {fails[2]} of {n}; predicted {n * p['p_recall']:.2f} / "
+          f"{n * p['p_overflow']:.2f}", flush=True)
+    assert total <= binom.ppf(0.999, n, p_pred)
