@@ -217,7 +217,7 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   if (rc) return rc;
   HIPCHK(launch_attempt_init(ctl, sel, rec, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
   HIPCHK(launch_sample(x, N, S, seed, attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
-                       at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, t, s),
+                       at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, sel->hist, t, s),
          "launch sample");
   FilterArgs fa{};
   fa.x = x;
@@ -361,7 +361,7 @@ int profk_stage_sample(const float* x, int64_t N, int64_t S, uint64_t seed, int3
   SelState* sel = at<SelState>(w, L.sel);
   HIPCHK(launch_attempt_init(ctl, sel, nullptr, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
   HIPCHK(launch_sample(x, (u64)N, (u64)S, seed, (u32)attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
-                       at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, 0, s),
+                       at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, sel->hist, 0, s),
          "launch sample");
   HIPCHK(launch_keys_to_index(at<u64>(w, L.keys), &ctl->D, (u64)S, out_idx, s), "launch keys_to_index");
   HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
@@ -384,7 +384,7 @@ int profk_stage_threshold(const float* x, int64_t N, int64_t S, int64_t t, uint6
   SelState* sel = at<SelState>(w, L.sel);
   HIPCHK(launch_attempt_init(ctl, sel, nullptr, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
   HIPCHK(launch_sample(x, (u64)N, (u64)S, seed, (u32)attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
-                       at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, (u64)t, s),
+                       at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, sel->hist, (u64)t, s),
          "launch sample");
   HIPCHK(launch_tau_to_output(x, (u64)N, ctl, out_tau_val, out_tau_idx, s), "launch tau_to_output");
   u32 status = 0;

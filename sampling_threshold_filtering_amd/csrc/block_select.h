@@ -5,10 +5,10 @@
 // threshold tau of Prof-K ("Prof-K: Probabilistic One-Pass Filtering for Efficient
 // Top-k Selection", §3 stage 2: the t-th largest of the S sampled values, S at most
 // 131072) and the per-row stages of the batched form.  Each pass reads the keys
-// that still match the fixed prefix from L2, histograms the next 8-bit digit in
-// LDS (one LDS atomic per distinct digit per wavefront) and fixes it; once at most
-// `cap` keys match they are gathered into LDS and sorted, and the answer is read
-// off.  Every launch-free pass costs one read of the keys.
+// that still match the fixed prefix from L2 (four loads in flight per thread),
+// histograms the next 8-bit digit in LDS (one LDS atomic per distinct digit per
+// wavefront) and fixes it; once at most `cap` keys match they are gathered into
+// LDS and sorted, and the answer is read off.
 #pragma once
 
 #include "profk_device.h"
@@ -38,36 +38,75 @@ __device__ inline void block_bitonic_desc(u64* s, u32 P) {
 struct BlockSelectLds {
   u32 hist[256];
   u32 ncol;
-  u32 pick;
+  u32 digit;
   u64 prefix, mask, rank, count;
   u32 ok;
 };
 
-// Returns the key of 1-based rank `rank` (descending) among keys[0..n); `buf` is an
-// LDS array of `cap` keys (cap a power of two).  All threads get the result; *ok is
-// false when the state turned out inconsistent (never for distinct keys).
-__device__ inline u64 block_select_rank(const u64* keys, u64 n, u64 rank, u64* buf, u32 cap, BlockSelectLds* L,
-                                        bool* ok_out) {
-  if (threadIdx.x == 0) {
-    L->prefix = 0;
-    L->mask = 0;
-    L->rank = rank;
-    L->count = n;
-    L->ok = (rank >= 1 && rank <= n) ? 1u : 0u;
+// State after the top digit has been fixed from a histogram of it (hist[b] = number
+// of keys whose top 8 bits are b).  Called by thread 0 only.
+__device__ inline void block_select_start_from_top_hist(BlockSelectLds* L, const u32* hist, u64 n, u64 rank) {
+  L->ok = (rank >= 1 && rank <= n) ? 1u : 0u;
+  L->prefix = 0;
+  L->mask = 0;
+  L->rank = rank;
+  L->count = n;
+  L->digit = 0;
+  if (!L->ok) return;
+  u64 cum = 0;
+  int b = 255;
+  for (; b >= 0; --b) {
+    const u64 c = hist[b];
+    if (cum + c >= rank) break;
+    cum += c;
   }
-  __syncthreads();
-  for (u32 digit = 0; digit < 8 && L->ok; ++digit) {
-    const u64 prefix = L->prefix, mask = L->mask, count = L->count;
-    if (count <= cap) break;
-    const u32 shift = 56u - 8u * digit;
+  if (b < 0) {
+    L->ok = 0;
+    return;
+  }
+  L->rank = rank - cum;
+  L->count = hist[b];
+  L->prefix = (u64)b << 56;
+  L->mask = 0xFFull << 56;
+  L->digit = 1;
+}
+
+__device__ inline void block_select_start(BlockSelectLds* L, u64 n, u64 rank) {
+  L->ok = (rank >= 1 && rank <= n) ? 1u : 0u;
+  L->prefix = 0;
+  L->mask = 0;
+  L->rank = rank;
+  L->count = n;
+  L->digit = 0;
+}
+
+constexpr u32 kBlockSelectILP = 4;
+
+// Finishes the selection whose state is in *L (set by one of the start functions and
+// visible to every thread); returns the key of the requested rank to all threads.
+// `buf` is an LDS array of `cap` keys (cap a power of two).  *ok_out is false when the
+// state turned out inconsistent (never for distinct keys).
+__device__ inline u64 block_select_finish(const u64* keys, u64 n, u64* buf, u32 cap, BlockSelectLds* L,
+                                          bool* ok_out) {
+  const u64 span = (u64)blockDim.x * kBlockSelectILP;
+  while (L->ok && L->digit < 8 && L->count > cap) {
+    const u64 prefix = L->prefix, mask = L->mask;
+    const u32 shift = 56u - 8u * L->digit;
     for (u32 b = threadIdx.x; b < 256; b += blockDim.x) L->hist[b] = 0;
     __syncthreads();
-    for (u64 base = 0; base < n; base += blockDim.x) {
-      const u64 i = base + threadIdx.x;
-      const bool in = i < n;
-      const u64 key = in ? keys[i] : 0ull;
-      const bool match = in && ((key & mask) == prefix);
-      wave_hist_add(L->hist, (u32)(key >> shift) & 255u, match);
+    for (u64 base = 0; base < n; base += span) {
+      u64 kk[kBlockSelectILP];
+#pragma unroll
+      for (u32 q = 0; q < kBlockSelectILP; ++q) {
+        const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
+        kk[q] = i < n ? keys[i] : 0ull;
+      }
+#pragma unroll
+      for (u32 q = 0; q < kBlockSelectILP; ++q) {
+        const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
+        const bool match = i < n && ((kk[q] & mask) == prefix);
+        wave_hist_add(L->hist, (u32)(kk[q] >> shift) & 255u, match);
+      }
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -85,35 +124,44 @@ __device__ inline u64 block_select_rank(const u64* keys, u64 n, u64 rank, u64* b
         L->count = L->hist[b];
         L->prefix = prefix | ((u64)b << shift);
         L->mask = mask | (0xFFull << shift);
+        L->digit += 1;
       }
     }
     __syncthreads();
   }
-  u64 result = 0;
   if (L->ok) {
     const u64 prefix = L->prefix, mask = L->mask, count = L->count;
     if (count > cap || count == 0) {
+      __syncthreads();
       if (threadIdx.x == 0) L->ok = 0;
     } else {
       if (threadIdx.x == 0) L->ncol = 0;
       __syncthreads();
-      for (u64 base = 0; base < n; base += blockDim.x) {
-        const u64 i = base + threadIdx.x;
-        const bool in = i < n;
-        const u64 key = in ? keys[i] : 0ull;
-        const bool match = in && ((key & mask) == prefix);
-        const u64 m = __ballot(match);
-        u32 slot = 0;
-        if (m) {
-          const u32 leader = __ffsll((long long)m) - 1;
-          if (lane_id() == leader) slot = atomicAdd(&L->ncol, (u32)__popcll(m));
-          slot = __shfl(slot, leader) + count_below(m);
+      for (u64 base = 0; base < n; base += span) {
+        u64 kk[kBlockSelectILP];
+#pragma unroll
+        for (u32 q = 0; q < kBlockSelectILP; ++q) {
+          const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
+          kk[q] = i < n ? keys[i] : 0ull;
         }
-        if (match && slot < cap) buf[slot] = key;
+#pragma unroll
+        for (u32 q = 0; q < kBlockSelectILP; ++q) {
+          const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
+          const bool match = i < n && ((kk[q] & mask) == prefix);
+          const u64 m = __ballot(match);
+          u32 slot = 0;
+          if (m) {
+            const u32 leader = __ffsll((long long)m) - 1;
+            if (lane_id() == leader) slot = atomicAdd(&L->ncol, (u32)__popcll(m));
+            slot = __shfl(slot, leader) + count_below(m);
+          }
+          if (match && slot < cap) buf[slot] = kk[q];
+        }
       }
       __syncthreads();
       const u32 m = L->ncol;
       if (m != count) {
+        __syncthreads();
         if (threadIdx.x == 0) L->ok = 0;
       } else {
         u32 P = 1;
@@ -126,10 +174,18 @@ __device__ inline u64 block_select_rank(const u64* keys, u64 n, u64 rank, u64* b
   }
   __syncthreads();
   const bool ok = L->ok != 0;
-  if (ok) result = buf[L->rank - 1];
+  const u64 result = ok ? buf[L->rank - 1] : 0ull;
   __syncthreads();
   *ok_out = ok;
   return result;
+}
+
+// Convenience: the whole selection from scratch.
+__device__ inline u64 block_select_rank(const u64* keys, u64 n, u64 rank, u64* buf, u32 cap, BlockSelectLds* L,
+                                        bool* ok_out) {
+  if (threadIdx.x == 0) block_select_start(L, n, rank);
+  __syncthreads();
+  return block_select_finish(keys, n, buf, cap, L, ok_out);
 }
 
 }  // namespace profk

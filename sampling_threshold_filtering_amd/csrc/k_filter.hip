@@ -143,15 +143,19 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
       }
     }
     bool maybe = false;
+    bool mu[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool m = !(v[u].x < tv) | !(v[u].y < tv) | !(v[u].z < tv) | !(v[u].w < tv);
-      maybe |= valid[u] & m;
+      mu[u] = valid[u] & m;
+      maybe |= mu[u];
     }
     if (__ballot(maybe)) {
-      // exact test, one float4 slot at a time (4 ballots each)
+      // exact test, only for the float4 slots where some lane may hold a hit
+      // (4 ballots each); a sparse tile usually has one such slot
 #pragma unroll
       for (int u = 0; u < U; ++u) {
+        if (!__ballot(mu[u])) continue;
         const u64 vi = v0 + (u64)u * kWave + lane;
         const u32 i0 = (u32)(geo.head + 4 * vi);
         const float c[4] = {v[u].x, v[u].y, v[u].z, v[u].w};

@@ -100,7 +100,7 @@ constexpr u32 kTauCap = 8192;  // keys the last block sorts in LDS (64 KB)
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __restrict__ x, u64 N, u64 S,
                                                                 u64 seed, u32 attempt, u32 row, u64* table,
                                                                 u64 tmask, u32 gen, u64* __restrict__ keys,
-                                                                RowCtl* ctl, u32* ticket, u64 t) {
+                                                                RowCtl* ctl, u32* ticket, u32* top_hist, u64 t) {
   __shared__ u64 s_buf[kTauCap];
   __shared__ BlockSelectLds s_sel;
   __shared__ u32 s_wcnt[kSampleThreads / kWave];
@@ -128,10 +128,20 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __r
     s_base = tot ? atomicAdd(&ctl->D, (u64)tot) : 0ull;
   }
   __syncthreads();
+  u64 key = 0;
   if (fresh) {
+    key = make_key(__float_as_uint(x[idx]), idx);
     const u64 slot = s_base + s_wcnt[wid] + count_below(m);
-    if (slot < S) keys[slot] = make_key(__float_as_uint(x[idx]), idx);
+    if (slot < S) keys[slot] = key;
   }
+  // histogram of the top 8 bits of this block's keys: the first digit of the
+  // threshold selection, so the last block starts one pass further on
+  for (u32 b = threadIdx.x; b < 256; b += blockDim.x) s_sel.hist[b] = 0;
+  __syncthreads();
+  wave_hist_add(s_sel.hist, (u32)(key >> 56), fresh);
+  __syncthreads();
+  for (u32 b = threadIdx.x; b < 256; b += blockDim.x)
+    if (s_sel.hist[b]) atomicAdd(&top_hist[b], s_sel.hist[b]);
   // release this block's keys, then elect the last block
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -162,7 +172,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __r
       const u32 r = count_below(m2);
       if (ok2 && r < need) {
         hash_insert(table, tmask, gen, idx2);
-        keys[D + r] = make_key(__float_as_uint(x[idx2]), idx2);
+        const u64 key2 = make_key(__float_as_uint(x[idx2]), idx2);
+        keys[D + r] = key2;
+        atomicAdd(&top_hist[key2 >> 56], 1u);
       }
       const u64 got = (u64)__popcll(m2);
       D += got < need ? got : need;
@@ -179,9 +191,16 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __r
   }
   __syncthreads();
   const bool sample_ok = s_D == S;
+  for (u32 b = threadIdx.x; b < 256; b += blockDim.x) {
+    s_sel.hist[b] = atomicAdd(&top_hist[b], 0u);
+    top_hist[b] = 0;  // left zero for the next attempt
+  }
+  __syncthreads();
   if (t > 0) {
+    if (threadIdx.x == 0) block_select_start_from_top_hist(&s_sel, s_sel.hist, sample_ok ? S : 0, t);
+    __syncthreads();
     bool ok = false;
-    const u64 tau = sample_ok ? block_select_rank(keys, S, t, s_buf, kTauCap, &s_sel, &ok) : 0ull;
+    const u64 tau = block_select_finish(keys, S, s_buf, kTauCap, &s_sel, &ok);
     if (threadIdx.x == 0) {
       ctl->tau = tau;
       if (!ok) ctl->status = 3;
@@ -236,10 +255,10 @@ hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u
 }
 
 hipError_t launch_sample(const float* x, u64 N, u64 S, u64 seed, u32 attempt, u32 row, u64* table, u64 tmask,
-                         u32 gen, u64* keys, RowCtl* ctl, u32* ticket, u64 t, hipStream_t s) {
+                         u32 gen, u64* keys, RowCtl* ctl, u32* ticket, u32* top_hist, u64 t, hipStream_t s) {
   const u32 blocks = (u32)((S + kSampleThreads - 1) / kSampleThreads);
   sample_kernel<<<blocks, kSampleThreads, 0, s>>>(x, N, S, seed, attempt, row, table, tmask, gen, keys, ctl, ticket,
-                                                  t);
+                                                  top_hist, t);
   return hipGetLastError();
 }
 

@@ -85,10 +85,17 @@ __global__ __launch_bounds__(kSortThreads) void lsd_hist_kernel(u64* buf0, u64* 
   for (u32 b = threadIdx.x; b < 256; b += blockDim.x) s_h[b] = 0;
   __syncthreads();
   const u32 lo = blockIdx.x * kSortTile;
+  u64 keys[kSortItems];
+#pragma unroll
+  for (u32 c = 0; c < kSortItems; ++c) {  // all loads in flight before any ballot
+    const u32 i = lo + c * kSortThreads + threadIdx.x;
+    keys[c] = i < n ? src[i] : 0ull;
+  }
+#pragma unroll
   for (u32 c = 0; c < kSortItems; ++c) {
     const u32 i = lo + c * kSortThreads + threadIdx.x;
     const bool in = i < n;
-    const u32 dd = in ? 255u - (u32)((src[i] >> (8u * d)) & 0xFFu) : 0u;
+    const u32 dd = in ? 255u - (u32)((keys[c] >> (8u * d)) & 0xFFu) : 0u;
     wave_hist_add(s_h, dd, in);
   }
   __syncthreads();
@@ -103,12 +110,18 @@ constexpr int kScanThreads = 1024;
 __global__ __launch_bounds__(kScanThreads) void lsd_scan_kernel(u32* hist, u32 G, u32 d, const RowCtl* ctl) {
   __shared__ u32 s_tot[kScanThreads];
   if (ctl->status != 0 || !digit_varies(ctl, d)) return;
+  // Each thread's run is a whole number of 16-word groups (256 * G is a multiple
+  // of 256), read as uint4 so that all of a thread's loads are in flight at once.
   const u32 total = 256u * G;
-  const u32 per = (total + kScanThreads - 1) / kScanThreads;
-  const u32 lo = threadIdx.x * per;
+  const u32 per = ((total + kScanThreads - 1) / kScanThreads + 15u) & ~15u;
+  const u32 lo = threadIdx.x * per < total ? threadIdx.x * per : total;
   const u32 hi = lo + per < total ? lo + per : total;
   u32 run = 0;
-  for (u32 i = lo; i < hi; ++i) run += hist[i];
+  for (u32 i = lo; i < hi; i += 16) {
+    const uint4* p = reinterpret_cast<const uint4*>(hist + i);
+    const uint4 a = p[0], b = p[1], c = p[2], e = p[3];
+    run += a.x + a.y + a.z + a.w + b.x + b.y + b.z + b.w + c.x + c.y + c.z + c.w + e.x + e.y + e.z + e.w;
+  }
   s_tot[threadIdx.x] = run;
   __syncthreads();
   // Hillis-Steele inclusive scan of the run totals
@@ -119,10 +132,22 @@ __global__ __launch_bounds__(kScanThreads) void lsd_scan_kernel(u32* hist, u32 G
     __syncthreads();
   }
   u32 acc = threadIdx.x ? s_tot[threadIdx.x - 1] : 0u;
-  for (u32 i = lo; i < hi; ++i) {
-    const u32 c = hist[i];
-    hist[i] = acc;
-    acc += c;
+  for (u32 i = lo; i < hi; i += 16) {
+    uint4* p = reinterpret_cast<uint4*>(hist + i);
+    uint4 q[4] = {p[0], p[1], p[2], p[3]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 c = q[j];
+      q[j].x = acc;
+      q[j].y = acc + c.x;
+      q[j].z = acc + c.x + c.y;
+      q[j].w = acc + c.x + c.y + c.z;
+      acc += c.x + c.y + c.z + c.w;
+    }
+    p[0] = q[0];
+    p[1] = q[1];
+    p[2] = q[2];
+    p[3] = q[3];
   }
 }
 
@@ -143,10 +168,17 @@ __global__ __launch_bounds__(kSortThreads) void lsd_scatter_kernel(u64* buf0, u6
   }
   __syncthreads();
   const u32 lo = blockIdx.x * kSortTile;
+  u64 keys[kSortItems];
+#pragma unroll
+  for (u32 c = 0; c < kSortItems; ++c) {  // all loads in flight before any ballot
+    const u32 i = lo + c * kSortThreads + threadIdx.x;
+    keys[c] = i < n ? src[i] : 0ull;
+  }
+#pragma unroll
   for (u32 c = 0; c < kSortItems; ++c) {
     const u32 i = lo + c * kSortThreads + threadIdx.x;
     const bool in = i < n;
-    const u64 key = in ? src[i] : 0ull;
+    const u64 key = keys[c];
     const u32 dd = in ? 255u - (u32)((key >> (8u * d)) & 0xFFu) : 0u;
     const u64 same = wave_match8(dd, in);
     const u32 r = count_below(same);

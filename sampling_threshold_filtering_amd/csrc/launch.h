@@ -42,7 +42,7 @@ struct FilterArgs {
 hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u32* tickets, u32 nrows,
                                hipStream_t s);
 hipError_t launch_sample(const float* x, u64 N, u64 S, u64 seed, u32 attempt, u32 row, u64* table, u64 tmask,
-                         u32 gen, u64* keys, RowCtl* ctl, u32* ticket, u64 t, hipStream_t s);
+                         u32 gen, u64* keys, RowCtl* ctl, u32* ticket, u32* top_hist, u64 t, hipStream_t s);
 hipError_t launch_keys_to_index(const u64* keys, const u64* n_ptr, u64 n_cap, int64_t* out, hipStream_t s);
 hipError_t launch_tau_to_output(const float* x, u64 N, const RowCtl* ctl, float* out_val, int64_t* out_idx,
                                 hipStream_t s);
