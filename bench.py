@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--log2n", type=int, default=30, help="input size (default: the 2^30 workload)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-batched", action="store_true", help="skip the batched variant")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FILTER_FETCH_CSV", "FILTER_WRITE_CSV", "COPY_FETCH_CSV",
+                                                         "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs into the traffic record")
     return ap.parse_args()
 
 
@@ -66,6 +71,58 @@ def traffic_record(n: int):
     return rec.get("bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30
+
+
+def calibrate_copy():
+    """A plain device copy of known size, profiled with the same counters as the filter."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}), flush=True)
+
+
+def _pmc_rows(path, name_pattern):
+    """(kernel name, counter value) rows of a rocprofv3 counter_collection.csv."""
+    import csv
+    import re
+    out = []
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name") or row.get("Kernel-Name") or ""
+            if re.search(name_pattern, name):
+                out.append(float(row.get("Counter_Value") or row.get("Counter-Value")))
+    return out
+
+
+def summarize_pmc(paths):
+    """Scale the filter's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same
+    counters read for a copy of known size, and write the traffic record."""
+    ff, fw, cf, cw = paths
+    f_fetch = _pmc_rows(ff, "filter_kernel")
+    f_write = _pmc_rows(fw, "filter_kernel")
+    c_fetch = _pmc_rows(cf, "copyBuffer")
+    c_write = _pmc_rows(cw, "copyBuffer")
+    kib = 1024.0
+    fetch_scale = COPY_BYTES / (max(c_fetch) * kib)
+    write_scale = COPY_BYTES / (max(c_write) * kib)
+    fetch = float(np.mean(f_fetch)) * kib * fetch_scale
+    write = float(np.mean(f_write)) * kib * write_scale
+    N = 1 << 30
+    rec = {"N": N, "filter_source_sha256_16": filter_source_hash(),
+           "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+           "bytes_per_launch": round(fetch + write), "fetch_scale": round(fetch_scale, 4),
+           "write_scale": round(write_scale, 4), "filter_dispatches": [len(f_fetch), len(f_write)],
+           "read_bytes_algorithmic": 4 * N}
+    out = os.path.join(ROOT, "profiles", "filter_traffic_pareto_2p30.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(x: np.ndarray):
     import oracle
     try:
@@ -73,7 +130,7 @@ def cpu_baseline(x: np.ndarray):
     except AttributeError:
         cores = os.cpu_count() or 1
     threads = max(1, min(16, cores))
-    n = min(x.size, 1 << 27)
+    n = x.size
     sample = x[:n]
     oracle.topk(sample[: 1 << 20], 32, nthreads=threads)  # warm the library and pages
     t0 = time.perf_counter()
@@ -81,12 +138,18 @@ def cpu_baseline(x: np.ndarray):
         oracle.topk(sample, k, nthreads=threads)
     dt = time.perf_counter() - t0
     return {"value": round(len(KS) * n / dt / 1e9, 4), "unit": "Gelem/s", "cores": threads, "kind": "oracle",
-            "sample": f"first 2^{n.bit_length() - 1} values of the same tensor, k sweep {list(KS)}, "
+            "sample": f"the same 2^{n.bit_length() - 1}-value tensor, k sweep {list(KS)}, "
                       f"{dt:.2f} s total; plain C heap top-k, {threads} threads"}
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see the sharding notes of the design document); run with --gpus 1", file=sys.stderr)
