@@ -16,6 +16,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "launch.h"
 #include "profk.h"
@@ -49,14 +50,14 @@ u64 pow2_at_least(u64 v) {
 
 struct Layout {
   size_t hash = 0, ctl = 0, sel = 0, rec = 0, ticket = 0, keys = 0, cand = 0, col = 0, topk0 = 0, topk1 = 0,
-         hist = 0, rows = 0, total = 0;
+         hist = 0, rows = 0, scratch = 0, total = 0;
   u64 hash_slots = 0;
 };
 
 // The hash region always spans the allocation's whole hash capacity, so that the
 // offsets of every other region depend only on the allocation and the request,
 // and no region ever overlaps stale hash slots.
-Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 hash_cap) {
+Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap) {
   Layout L;
   L.hash_slots = pow2_at_least(2 * (S ? S : 1));
   if (L.hash_slots < hash_cap) L.hash_slots = hash_cap;
@@ -78,6 +79,7 @@ Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 hash_cap) {
   L.topk1 = take((k ? k : 1) * sizeof(u64));
   L.hist = take(sort_hist_words(k) * sizeof(u32));
   L.rows = take(B * sizeof(int));
+  L.scratch = take((scratch_words ? scratch_words : 1) * sizeof(u64));
   L.total = off;
   return L;
 }
@@ -90,6 +92,8 @@ struct Workspace {
   u64 hash_cap = 0;  // slots of the hash region at offset 0
   AttemptRecord* host = nullptr;
   size_t host_n = 0;
+  int* host_rows = nullptr;  // pinned list of rows to redraw (batched form)
+  size_t host_rows_n = 0;
   u32 gen = 0;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
 };
@@ -99,6 +103,7 @@ std::map<std::pair<int, hipStream_t>, Workspace*> g_ws;
 
 struct Need {
   u64 B, S, M, k;
+  u64 scratch_words = 0;
 };
 
 int get_workspace(hipStream_t s, const Need& need, Workspace** out, Layout* out_layout) {
@@ -112,7 +117,7 @@ int get_workspace(hipStream_t s, const Need& need, Workspace** out, Layout* out_
     w->device = dev;
     w->stream = s;
   }
-  Layout L = make_layout(need.B, need.S, need.M, need.k, w->hash_cap);
+  Layout L = make_layout(need.B, need.S, need.M, need.k, need.scratch_words, w->hash_cap);
   if (w->bytes < L.total || w->hash_cap < L.hash_slots) {
     if (w->dev) {
       HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
@@ -144,6 +149,13 @@ int get_workspace(hipStream_t s, const Need& need, Workspace** out, Layout* out_
     w->host_n = 0;
     HIPCHK(hipHostMalloc((void**)&w->host, rows * sizeof(AttemptRecord), hipHostMallocDefault), "hipHostMalloc");
     w->host_n = rows;
+  }
+  if (w->host_rows_n < rows) {
+    if (w->host_rows) (void)hipHostFree(w->host_rows);
+    w->host_rows = nullptr;
+    w->host_rows_n = 0;
+    HIPCHK(hipHostMalloc((void**)&w->host_rows, rows * sizeof(int), hipHostMallocDefault), "hipHostMalloc");
+    w->host_rows_n = rows;
   }
   if (!w->ev0) {
     HIPCHK(hipEventCreate(&w->ev0), "hipEventCreate");
@@ -294,6 +306,135 @@ int topk_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* out_vals
   return run_exact(w, L, x, N, k, out_vals, out_idx, s);
 }
 
+// Batched form with per-row kernels (rows of at most kBatchedMaxN values whose
+// buffer fits one workgroup's LDS sort).  Returns PROFK_EUNSUPPORTED when the shape
+// is outside those limits, so that the caller takes the row-by-row path.
+int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u64 seed, float* out_vals,
+                      int64_t* out_idx, hipStream_t s, const profk_options* opt, profk_stats* st) {
+  if (B >= (1ull << 31)) return PROFK_EUNSUPPORTED;
+  if (N <= kSmallSort) {
+    // rows this short: exact top-k by an LDS sort of each row
+    Layout L;
+    Workspace* w = nullptr;
+    int rc = get_workspace(s, Need{B, 0, 0, 1}, &w, &L);
+    if (rc) return rc;
+    BatchedArgs a{};
+    a.x = x;
+    a.ld = ld;
+    a.N = N;
+    a.nrows = B;
+    a.k = k;
+    a.out_vals = out_vals;
+    a.out_idx = out_idx;
+    HIPCHK(launch_b_rowsort(a, s), "launch b_rowsort");
+    HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+    if (st) {
+      st->fallback = 1;
+      st->rows_fallback = (int64_t)B;
+    }
+    return PROFK_OK;
+  }
+  profk_params p{};
+  int rc = solve_memo((int64_t)N, (int64_t)k, eps / (double)B, opt, &p);  // P1 App. E.2: eps / B per row
+  if (rc) return rc;
+  const int max_att = max_attempts_of(opt);
+  if (p.direct_exact || max_att == 0 || N > kBatchedMaxN || (u64)p.M > kSmallSort || (u64)p.S > kBatchedMaxN / 8)
+    return PROFK_EUNSUPPORTED;
+  const u64 S = (u64)p.S, M = (u64)p.M, t = (u64)p.t;
+  const u64 G = batched_sample_blocks(B);
+  Layout L;
+  Workspace* w = nullptr;
+  rc = get_workspace(s, Need{B, 0, M, 1, G * S}, &w, &L);
+  if (rc) return rc;
+  RowCtl* ctl = at<RowCtl>(w, L.ctl);
+  AttemptRecord* rec = at<AttemptRecord>(w, L.rec);
+  int* rows_dev = at<int>(w, L.rows);
+  if (st) {
+    st->S = p.S;
+    st->t = p.t;
+    st->M = p.M;
+    st->workspace_bytes = w->bytes;
+  }
+  HIPCHK(launch_attempt_init(ctl, nullptr, rec, at<u32>(w, L.ticket), (u32)B, s), "launch attempt_init");
+  const int* rows = nullptr;  // all rows on the first attempt
+  u64 nrows = B;
+  std::vector<int> failed;
+  for (int att = 0; att < max_att && nrows > 0; ++att) {
+    BatchedArgs a{};
+    a.x = x;
+    a.ld = ld;
+    a.N = N;
+    a.rows = rows;
+    a.nrows = nrows;
+    a.S = S;
+    a.t = t;
+    a.seed = seed;
+    a.attempt = (u32)att;
+    a.ctls = ctl;
+    a.scratch = at<u64>(w, L.scratch);
+    a.cand = at<u64>(w, L.cand);
+    a.M = M;
+    a.k = k;
+    a.out_vals = out_vals;
+    a.out_idx = out_idx;
+    HIPCHK(launch_b_sample(a, s), "launch b_sample");
+    FilterArgs fa{};
+    fa.x = x;
+    fa.ld = ld;
+    fa.N = N;
+    fa.rows = rows;
+    fa.nrows = nrows;
+    fa.ctls = ctl;
+    fa.cand = a.cand;
+    fa.M = M;
+    fa.k = k;
+    fa.ticket = at<u32>(w, L.ticket);
+    fa.rec = rec;
+    fa.sels = nullptr;
+    HIPCHK(launch_filter(fa, 0, s), "launch filter");
+    HIPCHK(launch_b_refine(a, s), "launch b_refine");
+    HIPCHK(hipMemcpyAsync(w->host, rec, B * sizeof(AttemptRecord), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+    HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+    failed.clear();
+    for (u64 li = 0; li < nrows; ++li) {
+      const int r = rows ? w->host_rows[li] : (int)li;
+      const AttemptRecord& rr = w->host[r];
+      if (rr.status == 3 || rr.error) {
+        t_err = "batched attempt: device consistency check failed";
+        return PROFK_EINTERNAL;
+      }
+      if (rr.status != 0) failed.push_back(r);
+    }
+    if (st) {
+      st->attempts = att + 1;
+      if (att < PROFK_STATS_ATTEMPTS) {
+        st->R[att] = (int64_t)w->host[rows ? w->host_rows[0] : 0].R;
+        st->fail_mode[att] = (int32_t)w->host[rows ? w->host_rows[0] : 0].status;
+      }
+      if (att == 1) st->rows_retried = (int64_t)nrows;
+    }
+    nrows = failed.size();
+    if (nrows) {
+      std::memcpy(w->host_rows, failed.data(), nrows * sizeof(int));
+      HIPCHK(hipMemcpyAsync(rows_dev, w->host_rows, nrows * sizeof(int), hipMemcpyHostToDevice, s), "hipMemcpyAsync");
+      rows = rows_dev;
+    }
+  }
+  if (nrows == 0) return PROFK_OK;
+  // rows that failed every attempt: exact full selection, row by row
+  std::vector<int> rest(failed);
+  if (st) st->rows_fallback = (int64_t)rest.size();
+  profk_options o{};
+  if (opt) o = *opt;
+  o.force_fallback = 1;
+  for (int r : rest) {
+    rc = topk_row(x + (u64)r * ld, N, k, eps / (double)B, seed, out_vals + (u64)r * k, out_idx + (u64)r * k, s, &o,
+                  nullptr);
+    if (rc) return rc;
+  }
+  return PROFK_OK;
+}
+
 }  // namespace
 }  // namespace profk
 
@@ -324,6 +465,10 @@ int profk_topk_batched_ex(const float* x, int64_t B, int64_t N, int64_t ld_x, in
   int rc = validate(x, N, k, eps, out_vals, out_idx);
   if (rc) return rc;
   if (B < 1 || ld_x < N) return PROFK_EINVAL;
+  if (st) std::memset(st, 0, sizeof(*st));
+  rc = topk_batched_rows(x, (u64)B, (u64)N, (u64)ld_x, (u64)k, eps, seed, out_vals, out_idx, (hipStream_t)stream, opt,
+                         st);
+  if (rc != PROFK_EUNSUPPORTED) return rc;
   if (st) std::memset(st, 0, sizeof(*st));
   const double eps_row = eps / (double)B;  // P1 App. E.2: budget split per row
   for (int64_t r = 0; r < B; ++r) {
@@ -461,6 +606,7 @@ void profk_release(void) {
       (void)hipFree(w->dev);
     }
     if (w->host) (void)hipHostFree(w->host);
+    if (w->host_rows) (void)hipHostFree(w->host_rows);
     if (w->ev0) (void)hipEventDestroy(w->ev0);
     if (w->ev1) (void)hipEventDestroy(w->ev1);
     (void)hipSetDevice(cur);

@@ -69,13 +69,15 @@ __device__ bool hash_contains(const u64* table, u64 tmask, u32 gen, u32 idx) {
 __global__ __launch_bounds__(64) void attempt_init_kernel(RowCtl* ctl, SelState* sel, AttemptRecord* rec,
                                                           u32* tickets, u32 nrows) {
   if (tickets && threadIdx.x < kTickets) tickets[threadIdx.x] = 0;
-  for (u32 r = 0; r < nrows; ++r)
-    for (u32 b = threadIdx.x; b < 256; b += blockDim.x) sel[r].hist[b] = 0;
+  if (sel)
+    for (u32 r = 0; r < nrows; ++r)
+      for (u32 b = threadIdx.x; b < 256; b += blockDim.x) sel[r].hist[b] = 0;
   for (u32 r = threadIdx.x; r < nrows; r += blockDim.x) {
     RowCtl c{};
     c.key_and = ~0ull;
     ctl[r] = c;
     if (rec) rec[r] = AttemptRecord{0ull, 0u, 0u};
+    if (!sel) continue;
     SelState* s = &sel[r];
     s->prefix = 0;
     s->mask = 0;

@@ -60,6 +60,32 @@ hipError_t launch_arm_select(SelState* st, u64 rank, u64 count, RowCtl* ctl, hip
 
 hipError_t launch_filter(const FilterArgs& a, u32 grid, hipStream_t s);
 
+// Batched form (k_batched.hip): rows of at most kBatchedMaxN values.
+constexpr u64 kBatchedMaxN = 1ull << 20;
+
+struct BatchedArgs {
+  const float* x;  // row 0
+  u64 ld;          // row stride (elements)
+  u64 N;           // values per row
+  const int* rows; // rows to process (device), or nullptr for rows 0..nrows-1
+  u64 nrows;
+  u64 S, t;        // sample size and threshold rank per row
+  u64 seed;
+  u32 attempt;
+  RowCtl* ctls;    // per row
+  u64* scratch;    // sample keys: S per sampling workgroup
+  u64* cand;       // per row M keys (row stride M)
+  u64 M;
+  u64 k;
+  float* out_vals; // B x k
+  int64_t* out_idx;
+};
+
+u32 batched_sample_blocks(u64 nrows);
+hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s);
+hipError_t launch_b_refine(const BatchedArgs& a, hipStream_t s);
+hipError_t launch_b_rowsort(const BatchedArgs& a, hipStream_t s);
+
 hipError_t launch_sort_and_write(u64* buf0, u64* buf1, u32* hist, u32 k, const float* row, u64 N, float* out_vals,
                                  int64_t* out_idx, RowCtl* ctl, AttemptRecord* rec, hipStream_t s);
 u64 sort_hist_words(u64 k);

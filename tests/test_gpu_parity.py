@@ -183,6 +183,45 @@ def test_batched_matches_oracle():
     np.testing.assert_array_equal(host(vals).view(np.uint32), ov.view(np.uint32))
 
 
+def check_batched(x2d, vals, idx, k):
+    ov, oi = oracle.topk_batched(np.ascontiguousarray(x2d), k, nthreads=8)
+    np.testing.assert_array_equal(host(idx), oi)
+    np.testing.assert_array_equal(host(vals).view(np.uint32), ov.view(np.uint32))
+
+
+@pytest.mark.parametrize("kind,B,N,k,opts", [
+    ("normal", 64, 1 << 20, 64, {}),                   # per-row kernels, default S
+    ("few_levels", 40, 200003, 100, {"s_override": 8192}),  # ties inside rows, odd row length
+    ("uniform", 300, 5000, 17, {}),                    # short rows: per-row LDS sort
+    ("normal", 5, 8192, 8192, {}),                     # k = N at the short-row limit
+    ("normal", 7, 1, 1, {}),
+    ("normal", 2, 1 << 21, 300, {}),                   # rows longer than the per-row kernels take
+])
+def test_batched_shapes(kind, B, N, k, opts):
+    say("batched", kind, B, N, k, opts)
+    x = (generate(kind, B * N, seed=31) if kind in ("normal", "uniform") else edge_case(kind, B * N, 31)).reshape(B, N)
+    vals, idx, st = stf.topk_batched(dev(x), k, options=opts or None, stats=True)
+    check_batched(x, vals, idx, k)
+
+
+def test_batched_strided_rows():
+    say("batched strided ld = N + 3")
+    B, N, ld, k = 24, 1 << 18, (1 << 18) + 3, 50
+    full = generate("normal", B * ld, seed=32).reshape(B, ld)
+    xd = dev(full)[:, :N]  # row stride ld, rows misaligned
+    vals, idx = stf.topk_batched(xd, k, options={"s_override": 4096})
+    check_batched(full[:, :N], vals, idx, k)
+
+
+def test_batched_forced_overflow_falls_back_per_row():
+    say("batched forced overflow")
+    B, N, k = 6, 1 << 18, 40
+    x = generate("normal", B * N, seed=33).reshape(B, N)
+    vals, idx, st = stf.topk_batched(dev(x), k, options={"s_override": 4096, "force_M": k}, stats=True)
+    check_batched(x, vals, idx, k)
+    assert st["rows_fallback"] == B and st["attempts"] == 6
+
+
 def test_rejects_bad_arguments_on_device():
     import torch
     x = torch.zeros(100, device="cuda")
