@@ -96,6 +96,8 @@ typedef struct profk_stats {
   double filter_ms;       /* filter kernel time of the last attempt (options.timing) */
   int64_t rows_retried;   /* batched: rows that needed more than one attempt */
   int64_t rows_fallback;  /* batched: rows finished by the exact full selection */
+  int64_t refine_multipass; /* attempts whose refinement needed the multi-pass radix select
+                               (a value bin too large for one workgroup: ties, narrow ranges) */
 } profk_stats;
 
 /*

@@ -15,7 +15,9 @@ Definitions followed (plain readings, listed again in the design notes):
   S* about 4,600) only this prefactor reproduces; P2 Eq. 14's own prefactor
   (z rho log2 k / 2)^(2/3) is kept as an option.  S = clamp(round(S*_raw),
   S_min, S_max), S_min = 32768, S_max = 131072 (P2 §4 "Optimal Sample
-  Size"), round to nearest (P2 Algorithm 1, step 4), then at most N.
+  Size"), round to nearest (P2 Algorithm 1, step 4), then at most N/128 (the
+  S column of P1 App. B Table 3 at N = 2^20 is 8192 = N/128; the cap only
+  bites below N = 2^22).
 * t* = F^-1_{N,k-1,S}(1 - eps_A) + 1 and
   M* = min{M in [k, N] : F_{N,M,S}(t* - 1) <= eps_B}  (P1 §4 Theorem 4, Eq. 7),
   with F the hypergeometric CDF of P1 Eq. 1-2.
@@ -79,6 +81,9 @@ def s_rule(N: int, k: int, eps: float, s_min: int = S_MIN_DEFAULT, s_max: int = 
         raw = prefactor * base
     S = int(math.floor(raw + 0.5))
     S = max(s_min, min(s_max, S))
+    # short inputs: at most N/128 samples (P1 App. B Table 3 uses S = 8192 = N/128 at
+    # N = 2^20); no effect for N >= 2^22
+    S = min(S, max(1, N // 128))
     S = min(S, N)
     return raw, S
 

@@ -17,7 +17,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libprofk.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "k_sample.hip", "k_select.hip", "k_filter.hip", "k_sort.hip", "k_batched.hip", "solver.cpp"]
+SOURCES = ["api.hip", "k_sample.hip", "k_select.hip", "k_filter.hip", "k_refine.hip", "k_sort.hip", "k_batched.hip",
+           "solver.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

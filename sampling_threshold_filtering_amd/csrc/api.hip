@@ -50,7 +50,7 @@ u64 pow2_at_least(u64 v) {
 
 struct Layout {
   size_t hash = 0, ctl = 0, sel = 0, rec = 0, ticket = 0, keys = 0, cand = 0, col = 0, topk0 = 0, topk1 = 0,
-         hist = 0, rows = 0, scratch = 0, total = 0;
+         hist = 0, rows = 0, scratch = 0, rtmp = 0, rhist = 0, rbin_off = 0, rbin_cnt = 0, rcursor = 0, total = 0;
   u64 hash_slots = 0;
 };
 
@@ -80,6 +80,11 @@ Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap) 
   L.hist = take(sort_hist_words(k) * sizeof(u32));
   L.rows = take(B * sizeof(int));
   L.scratch = take((scratch_words ? scratch_words : 1) * sizeof(u64));
+  L.rtmp = take((M ? M : 1) * sizeof(u64));
+  L.rhist = take(kBins * sizeof(u32));
+  L.rbin_off = take(kBins * sizeof(u32));
+  L.rbin_cnt = take(kBins * sizeof(u32));
+  L.rcursor = take(kBins * sizeof(u32));
   L.total = off;
   return L;
 }
@@ -201,7 +206,7 @@ int run_exact(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, float
   RowCtl* ctl = at<RowCtl>(w, L.ctl);
   SelState* sel = at<SelState>(w, L.sel);
   AttemptRecord* rec = at<AttemptRecord>(w, L.rec);
-  HIPCHK(launch_attempt_init(ctl, sel, rec, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
+  HIPCHK(launch_attempt_init(ctl, sel, rec, at<u32>(w, L.ticket), 1, at<u32>(w, L.rhist), s), "launch attempt_init");
   HIPCHK(launch_arm_select(sel, k, N, ctl, s), "launch arm_select");
   HIPCHK(launch_select_x(x, N, sel, at<u64>(w, L.col), &ctl->kth, &ctl->status, s), "launch select_x");
   HIPCHK(launch_compact_x(x, N, ctl, at<u64>(w, L.topk0), k, s), "launch compact_x");
@@ -227,7 +232,7 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   const u64 S = (u64)p.S, M = (u64)p.M, t = (u64)p.t;
   int rc = next_gen(w, s);
   if (rc) return rc;
-  HIPCHK(launch_attempt_init(ctl, sel, rec, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
+  HIPCHK(launch_attempt_init(ctl, sel, rec, at<u32>(w, L.ticket), 1, at<u32>(w, L.rhist), s), "launch attempt_init");
   HIPCHK(launch_sample(x, N, S, seed, attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
                        at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, sel->hist, t, s),
          "launch sample");
@@ -247,14 +252,38 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   if (timing) HIPCHK(hipEventRecord(w->ev0, s), "hipEventRecord");
   HIPCHK(launch_filter(fa, 0, s), "launch filter");
   if (timing) HIPCHK(hipEventRecord(w->ev1, s), "hipEventRecord");
-  HIPCHK(launch_select_keys(at<u64>(w, L.cand), &ctl->R, M, sel, at<u64>(w, L.col), &ctl->kth, &ctl->status, s),
-         "launch select(candidates)");
-  HIPCHK(launch_compact_keys(at<u64>(w, L.cand), &ctl->R, M, ctl, at<u64>(w, L.topk0), k, s), "launch compact");
-  HIPCHK(launch_sort_and_write(at<u64>(w, L.topk0), at<u64>(w, L.topk1), at<u32>(w, L.hist), (u32)k, x, N,
-                               out_vals, out_idx, ctl, rec, s),
-         "launch sort");
+  RefineArgs ra{};
+  ra.ctl = ctl;
+  ra.cand = at<u64>(w, L.cand);
+  ra.M = M;
+  ra.k = k;
+  ra.N = N;
+  ra.x = x;
+  ra.tmp = at<u64>(w, L.rtmp);
+  ra.hist = at<u32>(w, L.rhist);
+  ra.bin_off = at<u32>(w, L.rbin_off);
+  ra.bin_cnt = at<u32>(w, L.rbin_cnt);
+  ra.cursor = at<u32>(w, L.rcursor);
+  ra.ticket = at<u32>(w, L.ticket) + 2;
+  ra.rec = rec;
+  ra.out_vals = out_vals;
+  ra.out_idx = out_idx;
+  HIPCHK(launch_refine(ra, s), "launch refine");
   HIPCHK(hipMemcpyAsync(w->host, rec, sizeof(AttemptRecord), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
   HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  if (w->host[0].status == 0 && !w->host[0].error && w->host[0].generic) {
+    // a needed bin is too large for one LDS sort (ties, narrow ranges): the
+    // multi-pass refinement over the same candidates, then one more read-back
+    HIPCHK(launch_select_keys(at<u64>(w, L.cand), &ctl->R, M, sel, at<u64>(w, L.col), &ctl->kth, &ctl->status, s),
+           "launch select(candidates)");
+    HIPCHK(launch_compact_keys(at<u64>(w, L.cand), &ctl->R, M, ctl, at<u64>(w, L.topk0), k, s), "launch compact");
+    HIPCHK(launch_sort_and_write(at<u64>(w, L.topk0), at<u64>(w, L.topk1), at<u32>(w, L.hist), (u32)k, x, N,
+                                 out_vals, out_idx, ctl, rec, s),
+           "launch sort");
+    HIPCHK(hipMemcpyAsync(w->host, rec, sizeof(AttemptRecord), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+    HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+    w->host[0].generic = 1;
+  }
   *out_rec = w->host[0];
   if (timing && filter_ms) {
     float ms = 0.f;
@@ -294,6 +323,7 @@ int topk_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* out_vals
           st->fail_mode[a] = (int32_t)r.status;
         }
         st->filter_ms = fms;
+        if (r.generic) st->refine_multipass++;
       }
       if (r.error || r.status == 3) {
         t_err = "sampled attempt: device consistency check failed";
@@ -355,7 +385,7 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     st->M = p.M;
     st->workspace_bytes = w->bytes;
   }
-  HIPCHK(launch_attempt_init(ctl, nullptr, rec, at<u32>(w, L.ticket), (u32)B, s), "launch attempt_init");
+  HIPCHK(launch_attempt_init(ctl, nullptr, rec, at<u32>(w, L.ticket), (u32)B, nullptr, s), "launch attempt_init");
   const int* rows = nullptr;  // all rows on the first attempt
   u64 nrows = B;
   std::vector<int> failed;
@@ -504,7 +534,7 @@ int profk_stage_sample(const float* x, int64_t N, int64_t S, uint64_t seed, int3
   if (rc) return rc;
   RowCtl* ctl = at<RowCtl>(w, L.ctl);
   SelState* sel = at<SelState>(w, L.sel);
-  HIPCHK(launch_attempt_init(ctl, sel, nullptr, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
+  HIPCHK(launch_attempt_init(ctl, sel, nullptr, at<u32>(w, L.ticket), 1, at<u32>(w, L.rhist), s), "launch attempt_init");
   HIPCHK(launch_sample(x, (u64)N, (u64)S, seed, (u32)attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
                        at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, sel->hist, 0, s),
          "launch sample");
@@ -527,7 +557,7 @@ int profk_stage_threshold(const float* x, int64_t N, int64_t S, int64_t t, uint6
   if (rc) return rc;
   RowCtl* ctl = at<RowCtl>(w, L.ctl);
   SelState* sel = at<SelState>(w, L.sel);
-  HIPCHK(launch_attempt_init(ctl, sel, nullptr, at<u32>(w, L.ticket), 1, s), "launch attempt_init");
+  HIPCHK(launch_attempt_init(ctl, sel, nullptr, at<u32>(w, L.ticket), 1, at<u32>(w, L.rhist), s), "launch attempt_init");
   HIPCHK(launch_sample(x, (u64)N, (u64)S, seed, (u32)attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
                        at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, sel->hist, (u64)t, s),
          "launch sample");

@@ -5,7 +5,7 @@
 // threshold tau of Prof-K ("Prof-K: Probabilistic One-Pass Filtering for Efficient
 // Top-k Selection", §3 stage 2: the t-th largest of the S sampled values, S at most
 // 131072) and the per-row stages of the batched form.  Each pass reads the keys
-// that still match the fixed prefix from L2 (four loads in flight per thread),
+// that still match the fixed prefix from L2 (eight loads in flight per thread),
 // histograms the next 8-bit digit in LDS (one LDS atomic per distinct digit per
 // wavefront) and fixes it; once at most `cap` keys match they are gathered into
 // LDS and sorted, and the answer is read off.
@@ -80,7 +80,7 @@ __device__ inline void block_select_start(BlockSelectLds* L, u64 n, u64 rank) {
   L->digit = 0;
 }
 
-constexpr u32 kBlockSelectILP = 4;
+constexpr u32 kBlockSelectILP = 8;
 
 // Finishes the selection whose state is in *L (set by one of the start functions and
 // visible to every thread); returns the key of the requested rank to all threads.

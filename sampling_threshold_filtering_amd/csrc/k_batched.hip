@@ -11,8 +11,9 @@
 //                     sample up, and the workgroup selects tau (LDS reused as the
 //                     sort buffer).  It also clears the row's counter for the filter.
 //   filter_kernel     (k_filter.hip) one streaming pass over all listed rows.
-//   b_refine_kernel   one workgroup per row: the min(R, M) <= 8192 candidates are
-//                     sorted in LDS and the first k written out.
+//   b_refine_kernel   one 256-thread workgroup per row: the min(R, M) <= 8192
+//                     candidates are sorted in LDS (sized to M) and the first k
+//                     written out.
 //   b_rowsort_kernel  rows of at most 8192 values: exact top-k by sorting the row
 //                     in LDS (the sample would not pay off there).
 #include "block_select.h"
@@ -134,8 +135,10 @@ __global__ __launch_bounds__(kBThreads) void b_sample_kernel(BatchedArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kBThreads) void b_refine_kernel(BatchedArgs a) {
-  __shared__ u64 s[kSmallSort];
+// LDS: pow2(M) keys (dynamic), so that several rows share a compute unit.
+constexpr u32 kRefineThreads = 256;
+__global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a) {
+  extern __shared__ u64 s[];
   for (u64 li = blockIdx.x; li < a.nrows; li += gridDim.x) {
     const u32 row = a.rows ? (u32)a.rows[li] : (u32)li;
     const RowCtl* c = &a.ctls[row];
@@ -188,7 +191,9 @@ hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_b_refine(const BatchedArgs& a, hipStream_t s) {
-  b_refine_kernel<<<row_grid(a.nrows, 2), kBThreads, 0, s>>>(a);
+  u32 P = 1;
+  while (P < a.M) P <<= 1;  // M <= kSmallSort: at most 64 KB
+  b_refine_kernel<<<row_grid(a.nrows, 8), kRefineThreads, (size_t)P * sizeof(u64), s>>>(a);
   return hipGetLastError();
 }
 

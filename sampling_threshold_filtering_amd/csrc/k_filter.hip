@@ -53,14 +53,28 @@ struct Stage {
   u64* buf;  // this wavefront's LDS ring
   u32 n;     // staged keys
   u32 row;   // row the staged keys belong to
+  u64 kmax;  // per lane: largest key staged by this lane (0 when the stage is empty)
 };
+
+__device__ __forceinline__ u64 wave_max_u64(u64 v) {
+  for (int d = 32; d >= 1; d >>= 1) {
+    const u64 o = __shfl_xor(v, d);
+    v = o > v ? o : v;
+  }
+  return v;
+}
 
 __device__ __forceinline__ void stage_flush(Stage& st, RowCtl* ctls, u64* cand, u64 M) {
   if (st.n == 0) return;
   wave_lds_sync();
+  const u64 mx = wave_max_u64(st.kmax);
   u64 base = 0;
-  if (lane_id() == 0) base = atomicAdd(&ctls[st.row].R, (u64)st.n);
+  if (lane_id() == 0) {
+    base = atomicAdd(&ctls[st.row].R, (u64)st.n);
+    atomicMax(&ctls[st.row].cmax, mx);
+  }
   base = __shfl(base, 0);
+  st.kmax = 0;
   u64* dst = cand + (u64)st.row * M;
   for (u32 j = lane_id(); j < st.n; j += kWave)
     if (base + j < M) dst[base + j] = st.buf[j];
@@ -79,8 +93,16 @@ __device__ __forceinline__ void stage_hits(Stage& st, u32 row, const u64 (&masks
   if (st.n != 0 && (st.row != row || st.n + total > kStageCap)) stage_flush(st, ctls, cand, M);
   if (total > kStageCap) {
     // dense batch: straight to the row's buffer with one atomic
+    u64 lmax = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (hit[b] && key[b] > lmax) lmax = key[b];
+    const u64 mx = wave_max_u64(lmax);
     u64 base = 0;
-    if (lane_id() == 0) base = atomicAdd(&ctls[row].R, (u64)total);
+    if (lane_id() == 0) {
+      base = atomicAdd(&ctls[row].R, (u64)total);
+      atomicMax(&ctls[row].cmax, mx);
+    }
     base = __shfl(base, 0);
     u64* dst = cand + (u64)row * M;
     u32 run = 0;
@@ -98,7 +120,10 @@ __device__ __forceinline__ void stage_hits(Stage& st, u32 row, const u64 (&masks
   u32 run = st.n;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    if (hit[b]) st.buf[run + count_below(masks[b])] = key[b];
+    if (hit[b]) {
+      st.buf[run + count_below(masks[b])] = key[b];
+      if (key[b] > st.kmax) st.kmax = key[b];
+    }
     run += (u32)__popcll(masks[b]);
   }
   st.n = run;
@@ -112,12 +137,30 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   __shared__ u32 s_last;
   const u32 wid = threadIdx.x / kWave;
   const u32 lane = lane_id();
-  Stage st{s_stage[wid], 0u, 0u};
+  Stage st{s_stage[wid], 0u, 0u, 0ull};
 
+  // One row: wavefronts stride over the tiles.  Several rows: each wavefront takes a
+  // contiguous run of tiles, so it changes rows (and flushes its stage) rarely.
   const u64 nwaves = (u64)gridDim.x * kWavesPerBlock;
-  for (u64 g = (u64)blockIdx.x * kWavesPerBlock + wid; g < a.total_tiles; g += nwaves) {
-    const u64 lr = a.nrows == 1 ? 0 : g / a.tiles_per_row;
-    const u64 tile = g - lr * a.tiles_per_row;
+  const u64 gw = (u64)blockIdx.x * kWavesPerBlock + wid;
+  u64 g, gend, gstep;
+  if (a.nrows == 1) {
+    g = gw;
+    gend = a.total_tiles;
+    gstep = nwaves;
+  } else {
+    const u64 per = (a.total_tiles + nwaves - 1) / nwaves;
+    g = gw * per;
+    gend = g + per < a.total_tiles ? g + per : a.total_tiles;
+    gstep = 1;
+  }
+  u64 lr = g < gend ? g / a.tiles_per_row : 0;
+  u64 tile = g - lr * a.tiles_per_row;
+  for (; g < gend; g += gstep) {
+    if (tile >= a.tiles_per_row) {  // next row (contiguous runs only)
+      tile -= a.tiles_per_row;
+      ++lr;
+    }
     const u32 row = a.rows ? (u32)a.rows[lr] : (u32)lr;
     const RowGeom geo = row_geom(a.x, a.ld, a.N, row);
     const u64 tau = a.ctls[row].tau;
@@ -194,14 +237,17 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
       masks[0] = __ballot(hit[0]);
       stage_hits<1>(st, row, masks, hit, key, a.ctls, a.cand, a.M);
     }
+    tile += gstep;
   }
   // End of the stream: the block's waves reserve their staged keys with one
   // atomic per row they hold (one in the flat case) instead of one per wave.
   __shared__ u32 s_n[kWavesPerBlock], s_row[kWavesPerBlock];
-  __shared__ u64 s_base[kWavesPerBlock];
+  __shared__ u64 s_base[kWavesPerBlock], s_max[kWavesPerBlock];
+  const u64 wmax = wave_max_u64(st.kmax);
   if (lane == 0) {
     s_n[wid] = st.n;
     s_row[wid] = st.row;
+    s_max[wid] = wmax;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -211,13 +257,17 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
       for (int v = 0; v < w; ++v)
         if (s_n[v] && s_row[v] == s_row[w]) first = false;
       if (!first) continue;
-      u64 tot = 0;
+      u64 tot = 0, mx = 0;
       for (int v = w; v < kWavesPerBlock; ++v)
         if (s_n[v] && s_row[v] == s_row[w]) {
           s_base[v] = tot;
           tot += s_n[v];
+          mx = s_max[v] > mx ? s_max[v] : mx;
         }
-      const u64 b = atomicAdd(&a.ctls[s_row[w]].R, tot);  // returns: performed at the coherence point
+      // R's atomic returns, so it is performed before this block's ticket; cmax is
+      // only read by the next kernel
+      const u64 b = atomicAdd(&a.ctls[s_row[w]].R, tot);
+      atomicMax(&a.ctls[s_row[w]].cmax, mx);
       for (int v = w; v < kWavesPerBlock; ++v)
         if (s_n[v] && s_row[v] == s_row[w]) s_base[v] += b;
     }

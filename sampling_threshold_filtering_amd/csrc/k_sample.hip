@@ -66,9 +66,11 @@ __device__ bool hash_contains(const u64* table, u64 tmask, u32 gen, u32 idx) {
 
 // Clears every per-attempt counter, record and selection state (histograms
 // included) so that nothing depends on what the workspace held before.
-__global__ __launch_bounds__(64) void attempt_init_kernel(RowCtl* ctl, SelState* sel, AttemptRecord* rec,
-                                                          u32* tickets, u32 nrows) {
+__global__ __launch_bounds__(1024) void attempt_init_kernel(RowCtl* ctl, SelState* sel, AttemptRecord* rec,
+                                                          u32* tickets, u32 nrows, u32* refine_hist) {
   if (tickets && threadIdx.x < kTickets) tickets[threadIdx.x] = 0;
+  if (refine_hist)
+    for (u32 b = threadIdx.x; b < kBins; b += blockDim.x) refine_hist[b] = 0;
   if (sel)
     for (u32 r = 0; r < nrows; ++r)
       for (u32 b = threadIdx.x; b < 256; b += blockDim.x) sel[r].hist[b] = 0;
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(64) void attempt_init_kernel(RowCtl* ctl, SelState*
     RowCtl c{};
     c.key_and = ~0ull;
     ctl[r] = c;
-    if (rec) rec[r] = AttemptRecord{0ull, 0u, 0u};
+    if (rec) rec[r] = AttemptRecord{0ull, 0u, 0u, 0u, 0u};
     if (!sel) continue;
     SelState* s = &sel[r];
     s->prefix = 0;
@@ -251,8 +253,8 @@ __global__ void r_to_output_kernel(const RowCtl* ctl, int64_t* out_R) {
 
 // ---------------------------------------------------------------------------
 hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u32* tickets, u32 nrows,
-                               hipStream_t s) {
-  attempt_init_kernel<<<1, 64, 0, s>>>(ctl, sel, rec, tickets, nrows);
+                               u32* refine_hist, hipStream_t s) {
+  attempt_init_kernel<<<1, 1024, 0, s>>>(ctl, sel, rec, tickets, nrows, refine_hist);
   return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@ struct FilterArgs {
 };
 
 hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u32* tickets, u32 nrows,
-                               hipStream_t s);
+                               u32* refine_hist, hipStream_t s);
 hipError_t launch_sample(const float* x, u64 N, u64 S, u64 seed, u32 attempt, u32 row, u64* table, u64 tmask,
                          u32 gen, u64* keys, RowCtl* ctl, u32* ticket, u32* top_hist, u64 t, hipStream_t s);
 hipError_t launch_keys_to_index(const u64* keys, const u64* n_ptr, u64 n_cap, int64_t* out, hipStream_t s);
@@ -59,6 +59,31 @@ hipError_t launch_compact_x(const float* x, u64 N, RowCtl* ctl, u64* out, u64 k,
 hipError_t launch_arm_select(SelState* st, u64 rank, u64 count, RowCtl* ctl, hipStream_t s);
 
 hipError_t launch_filter(const FilterArgs& a, u32 grid, hipStream_t s);
+
+// Binned refinement (k_refine.hip).
+constexpr u32 kBinBits = 14;
+constexpr u32 kBins = 1u << kBinBits;
+constexpr u32 kBinCap = 4096;  // keys one sorting workgroup holds in LDS (32 KB)
+
+struct RefineArgs {
+  RowCtl* ctl;
+  const u64* cand;  // min(R, M) candidate keys
+  u64 M;
+  u64 k;
+  u64 N;
+  const float* x;   // the row (outputs copy x[idx])
+  u64* tmp;         // M keys: candidates of bins >= b* in bin order
+  u32* hist;        // kBins, zero on entry, left zero
+  u32* bin_off;     // kBins
+  u32* bin_cnt;     // kBins
+  u32* cursor;      // kBins
+  u32* ticket;      // zero on entry, left zero
+  AttemptRecord* rec;
+  float* out_vals;
+  int64_t* out_idx;
+};
+
+hipError_t launch_refine(const RefineArgs& a, hipStream_t s);
 
 // Batched form (k_batched.hip): rows of at most kBatchedMaxN values.
 constexpr u64 kBatchedMaxN = 1ull << 20;

@@ -164,9 +164,14 @@ struct RowCtl {
   u64 nsel;     // keys written by the compaction
   u64 key_or;   // OR / AND of the selected keys (which digits vary)
   u64 key_and;
+  u64 cmax;     // largest candidate key (filter)
   u32 status;   // 0 ok, 1 R < k, 2 R > M, 3 internal error
   u32 cur;      // ping-pong buffer of the sort
   u32 ticket;   // last-block election of the sort passes
+  u32 bin_shift;  // refinement bins: bin = min(kBins - 1, (key - tau) >> bin_shift)
+  u32 bstar;      // bin holding the k-th largest candidate
+  u32 c_above;    // candidates in the bins above bstar
+  u32 generic;    // 1: a needed bin is larger than one workgroup sorts in LDS
   u32 pad;
 };
 
@@ -175,6 +180,8 @@ struct AttemptRecord {
   u64 R;
   u32 status;
   u32 error;
+  u32 generic;  // the binned refinement deferred to the multi-pass one
+  u32 pad;
 };
 
 }  // namespace profk

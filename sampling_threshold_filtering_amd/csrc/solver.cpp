@@ -131,6 +131,9 @@ int solve(int64_t N, int64_t k, double eps, const profk_options* opt, profk_para
   p.S_raw = c * std::cbrt((double)k * (double)(N - k));
   int64_t S = (int64_t)std::floor(p.S_raw + 0.5);
   S = std::max(s_min, std::min(s_max, S));
+  // Short inputs: at most N/128 samples (P1 App. B Table 3 samples N/128 = 8192 at
+  // N = 2^20; the clamp above is stated for large tensors).  No effect for N >= 2^22.
+  S = std::min<int64_t>(S, std::max<int64_t>(1, N / 128));
   if (opt && opt->s_override > 0) S = opt->s_override;
   S = std::min(S, N);
   p.S = S;

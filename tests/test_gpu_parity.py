@@ -115,6 +115,7 @@ def test_topk_matches_oracle(kind, N, k, opts):
     vals, idx, st = stf.topk(dev(x), k, eps=1e-3, seed=3, options=opts or None, stats=True)
     check_topk(x, vals, idx, k)
     assert not st["fallback"] and st["attempts"] >= 1
+    print("[case] refine_multipass", st["refine_multipass"], flush=True)
 
 
 @pytest.mark.parametrize("N,k,offset", [(1, 1, 0), (5, 3, 1), (1000, 1000, 2), (4096, 17, 3), (100003, 5000, 1)])
@@ -125,6 +126,25 @@ def test_exact_path_small_and_misaligned(N, k, offset):
     check_topk(x[offset:], vals, idx, k)
     # where the sample would not pay off the solver routes the call to the exact selection
     assert st["fallback"] == bool(stf.solve(N, k, 1e-3)["direct_exact"])
+
+
+def test_binned_and_multipass_refinement_both_run():
+    say("refinement paths")
+    # continuous values: every needed value bin fits one LDS sort
+    x = generate("normal", 1 << 22, seed=40)
+    vals, idx, st = stf.topk(dev(x), 3000, stats=True)
+    check_topk(x, vals, idx, 3000)
+    assert st["refine_multipass"] == 0
+    # one tie group: the index part of the keys spreads it over the bins
+    x = generate("adv_noise", 1 << 22, seed=41)
+    vals, idx, st = stf.topk(dev(x), 3000, stats=True)
+    check_topk(x, vals, idx, 3000)
+    assert st["refine_multipass"] == 0
+    # two values, 419K copies of the larger: its bin is too large for one LDS sort
+    x = edge_case("two_levels", 1 << 22, 42)
+    vals, idx, st = stf.topk(dev(x), 500000, stats=True)
+    check_topk(x, vals, idx, 500000)
+    assert st["refine_multipass"] >= 1
 
 
 def test_forced_overflow_goes_to_fallback_and_stays_exact():

@@ -81,8 +81,12 @@ def test_solver_options_and_degenerate_cases():
     assert p["t"] == 1 and p["M"] == 100
     # t = 1 fails recall iff some sample lands in the top k-1 = 99 (P1 Proposition 2)
     assert math.isclose(p["p_recall"], solver_ref.hyp_sf(0, 1 << 24, 99, p["S"]), rel_tol=1e-6)
-    # small N: the sample would be more than half the input, go straight to the exact path
-    assert stf.solve(50000, 10, 1e-3)["direct_exact"] == 1
+    # tiny N: no threshold rank can meet the recall budget with N/128 samples, exact path
+    assert stf.solve(200, 10, 1e-3)["direct_exact"] == 1
+    # the sample is capped at N/128 below N = 2^22 (P1 Table 3: S = 8192 at N = 2^20)
+    assert stf.solve(1 << 20, 64, 1e-3)["S"] == 8192
+    assert stf.solve(1 << 22, 32, 1e-3)["S"] == 32768
+    assert stf.solve(50000, 10, 1e-3)["S"] == 50000 // 128
     # buffer larger than half the input: exact path
     assert stf.solve(1 << 20, 1 << 19, 1e-3)["direct_exact"] == 1
     assert stf.solve(1 << 26, 1024, 1e-3)["direct_exact"] == 0

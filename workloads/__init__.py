@@ -156,6 +156,8 @@ def edge_case(name: str, n: int, seed: int = 0) -> np.ndarray:
         x = rng.standard_normal(n, dtype=np.float32)
         x[rng.integers(0, n, max(1, n // 1000))] = np.nan
         return x
+    if name == "two_levels":  # 10% exactly 2.0, 90% exactly 1.0
+        return np.where(rng.random(n) < 0.1, np.float32(2.0), np.float32(1.0)).astype(np.float32)
     if name == "negative":
         return -np.abs(rng.standard_normal(n, dtype=np.float32)) - 1.0
     raise ValueError(name)
