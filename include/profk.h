@@ -23,9 +23,13 @@
  * option / parameter / stats structs are HOST pointers.
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
- * stream).  Work is enqueued on it.  The exact-mode call synchronises the
- * stream once per attempt to read the count R (P1 App. D "Cost of the
- * Run-Time Check"); on return the outputs are complete.
+ * stream).  Work is enqueued on it.  The host waits once per attempt for the
+ * count R and the check k <= R <= M (P1 App. D "Cost of the Run-Time Check"),
+ * which the device publishes into pinned host memory; profk_topk /
+ * profk_topk_ex then return while the last kernel, which sorts and writes the
+ * outputs, may still run.  The outputs are complete in stream order: any later
+ * work on the same stream (or after synchronising it) sees them.  The batched,
+ * stage and fallback paths synchronise the stream before returning.
  *
  * Errors.  Every entry point returns a status code; nothing throws across
  * the ABI.  profk_strerror() gives a message (HIP errors include the HIP

@@ -149,21 +149,41 @@ def _stream_ptr(torch, device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def topk(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, stats: bool = False):
+def _check_out(out, shape, device):
+    import torch
+    vals, idx = out
+    if (tuple(vals.shape) != shape or tuple(idx.shape) != shape or vals.dtype != torch.float32
+            or idx.dtype != torch.int64 or vals.device != device or idx.device != device
+            or not vals.is_contiguous() or not idx.is_contiguous()):
+        raise ValueError(f"out must be contiguous float32 / int64 tensors of shape {shape} on {device}")
+    return vals, idx
+
+
+def topk(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, stats: bool = False, out=None):
     """Exact top-k of a 1-D float32 CUDA tensor: (values, int64 indices), sorted
-    (value descending, ties to the lower index)."""
+    (value descending, ties to the lower index).  `out=(values, indices)` reuses
+    caller buffers.  The outputs are complete in stream order on return."""
     import torch
     if x.dim() != 1 or x.dtype != torch.float32 or not x.is_cuda:
         raise ValueError("x must be a 1-D float32 device tensor")
-    x = x.contiguous()
-    lib = load_library()
-    vals = torch.empty(k, dtype=torch.float32, device=x.device)
-    idx = torch.empty(k, dtype=torch.int64, device=x.device)
-    st = Stats()
-    with torch.cuda.device(x.device):
-        rc = lib.profk_topk_ex(ctypes.c_void_p(x.data_ptr()), x.numel(), k, eps, seed & (2**64 - 1),
-                               ctypes.c_void_p(vals.data_ptr()), ctypes.c_void_p(idx.data_ptr()),
-                               _stream_ptr(torch, x.device), _opt_ptr(options), ctypes.byref(st))
+    if not x.is_contiguous():
+        x = x.contiguous()
+    lib = _lib if _lib is not None else load_library()
+    dev = x.device
+    if out is None:
+        vals = torch.empty(k, dtype=torch.float32, device=dev)
+        idx = torch.empty(k, dtype=torch.int64, device=dev)
+    else:
+        vals, idx = _check_out(out, (k,), dev)
+    st = Stats() if stats else None
+    args = (ctypes.c_void_p(x.data_ptr()), x.numel(), k, eps, seed & (2**64 - 1), ctypes.c_void_p(vals.data_ptr()),
+            ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream),
+            _opt_ptr(options), ctypes.byref(st) if st is not None else None)
+    if dev.index == torch.cuda.current_device():
+        rc = lib.profk_topk_ex(*args)
+    else:
+        with torch.cuda.device(dev):
+            rc = lib.profk_topk_ex(*args)
     _check(rc)
     if stats:
         return vals, idx, stats_to_dict(st)

@@ -11,6 +11,8 @@
 //   exact full selection over all N values (radix select + compaction + sort)
 // The refinement is enqueued before the single synchronisation and skips itself
 // on device when the check failed, so a successful attempt costs one round trip.
+#include <immintrin.h>
+
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -49,30 +51,43 @@ u64 pow2_at_least(u64 v) {
 }
 
 struct Layout {
-  size_t hash = 0, ctl = 0, sel = 0, rec = 0, ticket = 0, keys = 0, cand = 0, col = 0, topk0 = 0, topk1 = 0,
-         hist = 0, rows = 0, scratch = 0, rtmp = 0, rhist = 0, rbin_off = 0, rbin_cnt = 0, rcursor = 0, total = 0;
-  u64 hash_slots = 0;
+  size_t hash = 0, ctl = 0, sel = 0, rec = 0, ticket = 0, keys = 0, tops = 0, cand = 0, col = 0, topk0 = 0,
+         topk1 = 0, hist = 0, rows = 0, scratch = 0, rtmp = 0, rhist = 0, rbin_off = 0, rbin_cnt = 0, rcursor = 0,
+         total = 0;
+  u64 hash_slots = 0;  // slots of the hash region (the allocation's capacity)
+  u64 rows_cap = 0;    // rows of the control regions (the allocation's capacity)
+  u64 hash_used = 0;   // slots this request's sample uses: a power of two >= 2S
 };
 
-// The hash region always spans the allocation's whole hash capacity, so that the
-// offsets of every other region depend only on the allocation and the request,
-// and no region ever overlaps stale hash slots.
-Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap) {
+// Regions that kernels leave zero for the next call (hash set, tickets and counters,
+// selection and refinement histograms) and the per-row control blocks sit first, at
+// offsets that depend only on the allocation's capacities (hash slots, rows); the
+// per-request regions follow.  A later request with other sizes therefore finds them
+// where the previous call cleaned them.
+Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap, u64 rows_cap) {
   Layout L;
-  L.hash_slots = pow2_at_least(2 * (S ? S : 1));
-  if (L.hash_slots < hash_cap) L.hash_slots = hash_cap;
+  L.hash_used = pow2_at_least(2 * (S ? S : 1));
+  L.hash_slots = L.hash_used < hash_cap ? hash_cap : L.hash_used;
+  const u64 rows = B < rows_cap ? rows_cap : B;
+  L.rows_cap = rows;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off = align256(off + bytes);
     return o;
   };
-  L.hash = take(L.hash_slots * sizeof(u64));
-  L.ctl = take(B * sizeof(RowCtl));
-  L.sel = take(B * sizeof(SelState));
-  L.rec = take(B * sizeof(AttemptRecord));
+  L.hash = take(L.hash_slots * sizeof(u32));
+  L.ctl = take(rows * sizeof(RowCtl));
+  L.sel = take(rows * sizeof(SelState));
+  L.rec = take(rows * sizeof(AttemptRecord));
   L.ticket = take(kTickets * sizeof(u32));
-  L.keys = take((S ? S : 1) * sizeof(u64));
+  L.rhist = take(kBins * sizeof(u32));
+  L.rbin_off = take(kBins * sizeof(u32));
+  L.rbin_cnt = take(kBins * sizeof(u32));
+  L.rcursor = take(kBins * sizeof(u32));
+  L.tops = take((size_t)kTopBlocks * kTopT * sizeof(u64));
+  // per request
+  L.keys = take(2 * (S ? S : 1) * sizeof(u64));  // S draw slots + the top-up
   L.cand = take(B * (M ? M : 1) * sizeof(u64));
   L.col = take((size_t)kCollectCap * sizeof(u64));
   L.topk0 = take((k ? k : 1) * sizeof(u64));
@@ -81,10 +96,6 @@ Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap) 
   L.rows = take(B * sizeof(int));
   L.scratch = take((scratch_words ? scratch_words : 1) * sizeof(u64));
   L.rtmp = take((M ? M : 1) * sizeof(u64));
-  L.rhist = take(kBins * sizeof(u32));
-  L.rbin_off = take(kBins * sizeof(u32));
-  L.rbin_cnt = take(kBins * sizeof(u32));
-  L.rcursor = take(kBins * sizeof(u32));
   L.total = off;
   return L;
 }
@@ -95,11 +106,17 @@ struct Workspace {
   char* dev = nullptr;
   size_t bytes = 0;
   u64 hash_cap = 0;  // slots of the hash region at offset 0
+  u64 rows_cap = 0;  // rows of the control regions after it
   AttemptRecord* host = nullptr;
   size_t host_n = 0;
   int* host_rows = nullptr;  // pinned list of rows to redraw (batched form)
   size_t host_rows_n = 0;
-  u32 gen = 0;
+  HostRecord* hrec = nullptr;      // pinned record the refinement publishes (host address)
+  HostRecord* hrec_dev = nullptr;  // the same memory as the device addresses it
+  u32 seq = 0;                     // last sequence number asked of the device
+  // Set while a call's kernels may have left counters, tickets or the hash set
+  // nonzero (an error between launches); the next call then clears them first.
+  bool dirty = false;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
 };
 
@@ -122,8 +139,8 @@ int get_workspace(hipStream_t s, const Need& need, Workspace** out, Layout* out_
     w->device = dev;
     w->stream = s;
   }
-  Layout L = make_layout(need.B, need.S, need.M, need.k, need.scratch_words, w->hash_cap);
-  if (w->bytes < L.total || w->hash_cap < L.hash_slots) {
+  Layout L = make_layout(need.B, need.S, need.M, need.k, need.scratch_words, w->hash_cap, w->rows_cap);
+  if (w->bytes < L.total || w->hash_cap < L.hash_slots || w->rows_cap < L.rows_cap) {
     if (w->dev) {
       HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
       HIPCHK(hipFree(w->dev), "hipFree");
@@ -144,9 +161,11 @@ int get_workspace(hipStream_t s, const Need& need, Workspace** out, Layout* out_
     w->dev = (char*)p;
     w->bytes = want;
     w->hash_cap = L.hash_slots;
-    // zero everything once: hash generations, selection histograms, counters
+    w->rows_cap = L.rows_cap;
+    // zero everything once: hash set, selection histograms, counters; every kernel
+    // leaves what it uses zero again
     HIPCHK(hipMemsetAsync(w->dev, 0, want, s), "hipMemsetAsync");
-    w->gen = 0;
+    w->dirty = false;
   }
   if (w->host_n < rows) {
     if (w->host) (void)hipHostFree(w->host);
@@ -162,6 +181,13 @@ int get_workspace(hipStream_t s, const Need& need, Workspace** out, Layout* out_
     HIPCHK(hipHostMalloc((void**)&w->host_rows, rows * sizeof(int), hipHostMallocDefault), "hipHostMalloc");
     w->host_rows_n = rows;
   }
+  if (!w->hrec) {
+    HIPCHK(hipHostMalloc((void**)&w->hrec, sizeof(HostRecord), hipHostMallocMapped | hipHostMallocCoherent),
+           "hipHostMalloc");
+    std::memset(w->hrec, 0, sizeof(HostRecord));
+    HIPCHK(hipHostGetDevicePointer((void**)&w->hrec_dev, w->hrec, 0), "hipHostGetDevicePointer");
+    w->seq = 0;
+  }
   if (!w->ev0) {
     HIPCHK(hipEventCreate(&w->ev0), "hipEventCreate");
     HIPCHK(hipEventCreate(&w->ev1), "hipEventCreate");
@@ -171,18 +197,62 @@ int get_workspace(hipStream_t s, const Need& need, Workspace** out, Layout* out_
   return PROFK_OK;
 }
 
-// Next hash generation; clears the table when the 32-bit tag wraps.
-int next_gen(Workspace* w, hipStream_t s) {
-  if (++w->gen == 0) {
-    HIPCHK(hipMemsetAsync(w->dev, 0, w->hash_cap * sizeof(u64), s), "hipMemsetAsync");
-    w->gen = 1;
-  }
-  return PROFK_OK;
-}
-
 template <class T>
 T* at(Workspace* w, size_t off) {
   return reinterpret_cast<T*>(w->dev + off);
+}
+
+// After a call that stopped between launches: clear the hash set, tickets, control
+// blocks and histograms that its kernels would have left zero.
+int clean_if_dirty(Workspace* w, const Layout& L, hipStream_t s) {
+  if (!w->dirty) return PROFK_OK;
+  HIPCHK(hipMemsetAsync(w->dev + L.hash, 0, L.hash_slots * sizeof(u32), s), "hipMemsetAsync");
+  HIPCHK(launch_attempt_init(at<RowCtl>(w, L.ctl), at<SelState>(w, L.sel), at<AttemptRecord>(w, L.rec),
+                             at<u32>(w, L.ticket), 1, at<u32>(w, L.rhist), s),
+         "launch attempt_init");
+  w->dirty = false;
+  return PROFK_OK;
+}
+
+// Waits until the device has published record number `want` (spinning on the pinned
+// host word; a stream that finishes without publishing it is an error, not a hang).
+int wait_record(Workspace* w, hipStream_t s, u32 want) {
+  const u32* seq = &w->hrec->seq;
+  for (u64 it = 0;; ++it) {
+    if (__atomic_load_n(seq, __ATOMIC_ACQUIRE) == want) return PROFK_OK;
+    if ((it & 255) == 255) {
+      const hipError_t q = hipStreamQuery(s);
+      if (q == hipSuccess) {
+        if (__atomic_load_n(seq, __ATOMIC_ACQUIRE) == want) return PROFK_OK;
+        t_err = "sampled attempt: the attempt record was not published";
+        return PROFK_EINTERNAL;
+      }
+      if (q != hipErrorNotReady) return hip_fail(q, "hipStreamQuery");
+    }
+    _mm_pause();
+  }
+}
+
+SampleArgs sample_args(Workspace* w, const Layout& L, const float* x, u64 N, u64 S, u64 t, u64 seed, u32 attempt) {
+  SampleArgs a{};
+  a.x = x;
+  a.N = N;
+  a.S = S;
+  a.seed = seed;
+  a.attempt = attempt;
+  a.row = 0;
+  a.table = at<u32>(w, L.hash);
+  a.tmask = L.hash_used - 1;
+  a.keys = at<u64>(w, L.keys);
+  a.tops = at<u64>(w, L.tops);
+  a.ctl = at<RowCtl>(w, L.ctl);
+  a.rec = nullptr;
+  a.ticket = at<u32>(w, L.ticket) + kTicketSample;
+  a.dcount = at<u32>(w, L.ticket) + kCountSample;
+  a.top_hist = at<SelState>(w, L.sel)->hist;
+  a.t = t;
+  a.fast = (t >= 1 && t <= kTopT && sample_blocks(S) <= kTopBlocks) ? 1u : 0u;
+  return a;
 }
 
 int validate(const float* x, int64_t N, int64_t k, double eps, const void* ov, const void* oi) {
@@ -206,6 +276,9 @@ int run_exact(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, float
   RowCtl* ctl = at<RowCtl>(w, L.ctl);
   SelState* sel = at<SelState>(w, L.sel);
   AttemptRecord* rec = at<AttemptRecord>(w, L.rec);
+  int rc = clean_if_dirty(w, L, s);
+  if (rc) return rc;
+  w->dirty = true;
   HIPCHK(launch_attempt_init(ctl, sel, rec, at<u32>(w, L.ticket), 1, at<u32>(w, L.rhist), s), "launch attempt_init");
   HIPCHK(launch_arm_select(sel, k, N, ctl, s), "launch arm_select");
   HIPCHK(launch_select_x(x, N, sel, at<u64>(w, L.col), &ctl->kth, &ctl->status, s), "launch select_x");
@@ -215,6 +288,7 @@ int run_exact(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, float
          "launch sort");
   HIPCHK(hipMemcpyAsync(w->host, rec, sizeof(AttemptRecord), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
   HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  w->dirty = false;
   if (w->host[0].error || w->host[0].status != 0) {
     t_err = "exact selection: device consistency check failed";
     return PROFK_EINTERNAL;
@@ -230,12 +304,14 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   SelState* sel = at<SelState>(w, L.sel);
   AttemptRecord* rec = at<AttemptRecord>(w, L.rec);
   const u64 S = (u64)p.S, M = (u64)p.M, t = (u64)p.t;
-  int rc = next_gen(w, s);
+  int rc = clean_if_dirty(w, L, s);
   if (rc) return rc;
-  HIPCHK(launch_attempt_init(ctl, sel, rec, at<u32>(w, L.ticket), 1, at<u32>(w, L.rhist), s), "launch attempt_init");
-  HIPCHK(launch_sample(x, N, S, seed, attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
-                       at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, sel->hist, t, s),
-         "launch sample");
+  // The sampling kernel resets the attempt's control state; every kernel leaves its
+  // tickets, counters and histograms zero, and the refinement clears the hash set.
+  w->dirty = true;
+  SampleArgs sa = sample_args(w, L, x, N, S, t, seed, attempt);
+  sa.rec = rec;
+  HIPCHK(launch_sample(sa, s), "launch sample");
   FilterArgs fa{};
   fa.x = x;
   fa.ld = N;
@@ -246,7 +322,7 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   fa.cand = at<u64>(w, L.cand);
   fa.M = M;
   fa.k = k;
-  fa.ticket = at<u32>(w, L.ticket);
+  fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
   fa.rec = rec;
   fa.sels = sel;
   if (timing) HIPCHK(hipEventRecord(w->ev0, s), "hipEventRecord");
@@ -264,13 +340,22 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   ra.bin_off = at<u32>(w, L.rbin_off);
   ra.bin_cnt = at<u32>(w, L.rbin_cnt);
   ra.cursor = at<u32>(w, L.rcursor);
-  ra.ticket = at<u32>(w, L.ticket) + 2;
+  ra.table = at<u32>(w, L.hash);
+  ra.table_slots = L.hash_used;
+  ra.hrec = w->hrec_dev;
+  ra.seq = ++w->seq;
   ra.rec = rec;
   ra.out_vals = out_vals;
   ra.out_idx = out_idx;
   HIPCHK(launch_refine(ra, s), "launch refine");
-  HIPCHK(hipMemcpyAsync(w->host, rec, sizeof(AttemptRecord), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
-  HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  // The scan publishes the record once the check is known; the last refinement
+  // launch (sorting and writing the outputs) may still run when this returns.
+  rc = wait_record(w, s, ra.seq);
+  if (rc) return rc;
+  w->host[0].R = w->hrec->R;
+  w->host[0].status = w->hrec->status;
+  w->host[0].error = w->hrec->error;
+  w->host[0].generic = w->hrec->generic;
   if (w->host[0].status == 0 && !w->host[0].error && w->host[0].generic) {
     // a needed bin is too large for one LDS sort (ties, narrow ranges): the
     // multi-pass refinement over the same candidates, then one more read-back
@@ -284,6 +369,7 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
     HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
     w->host[0].generic = 1;
   }
+  w->dirty = false;
   *out_rec = w->host[0];
   if (timing && filter_ms) {
     float ms = 0.f;
@@ -385,6 +471,9 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     st->M = p.M;
     st->workspace_bytes = w->bytes;
   }
+  rc = clean_if_dirty(w, L, s);
+  if (rc) return rc;
+  w->dirty = true;
   HIPCHK(launch_attempt_init(ctl, nullptr, rec, at<u32>(w, L.ticket), (u32)B, nullptr, s), "launch attempt_init");
   const int* rows = nullptr;  // all rows on the first attempt
   u64 nrows = B;
@@ -418,7 +507,7 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     fa.cand = a.cand;
     fa.M = M;
     fa.k = k;
-    fa.ticket = at<u32>(w, L.ticket);
+    fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
     fa.rec = rec;
     fa.sels = nullptr;
     HIPCHK(launch_filter(fa, 0, s), "launch filter");
@@ -450,6 +539,7 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
       rows = rows_dev;
     }
   }
+  w->dirty = false;
   if (nrows == 0) return PROFK_OK;
   // rows that failed every attempt: exact full selection, row by row
   std::vector<int> rest(failed);
@@ -530,16 +620,23 @@ int profk_stage_sample(const float* x, int64_t N, int64_t S, uint64_t seed, int3
   Workspace* w = nullptr;
   int rc = get_workspace(s, Need{1, (u64)S, 1, 1}, &w, &L);
   if (rc) return rc;
-  rc = next_gen(w, s);
+  rc = clean_if_dirty(w, L, s);
   if (rc) return rc;
+  w->dirty = true;
   RowCtl* ctl = at<RowCtl>(w, L.ctl);
-  SelState* sel = at<SelState>(w, L.sel);
-  HIPCHK(launch_attempt_init(ctl, sel, nullptr, at<u32>(w, L.ticket), 1, at<u32>(w, L.rhist), s), "launch attempt_init");
-  HIPCHK(launch_sample(x, (u64)N, (u64)S, seed, (u32)attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
-                       at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, sel->hist, 0, s),
-         "launch sample");
-  HIPCHK(launch_keys_to_index(at<u64>(w, L.keys), &ctl->D, (u64)S, out_idx, s), "launch keys_to_index");
+  u32* tickets = at<u32>(w, L.ticket);
+  HIPCHK(launch_sample(sample_args(w, L, x, (u64)N, (u64)S, 0, seed, (u32)attempt), s), "launch sample");
+  HIPCHK(launch_keys_to_index_compact(at<u64>(w, L.keys), &ctl->D, 2 * (u64)S, out_idx, tickets + kCountStage, s),
+         "launch keys_to_index");
+  HIPCHK(launch_clear_sample(at<u32>(w, L.hash), L.hash_used, tickets, s), "launch clear_sample");
+  u32 status = 0;
+  HIPCHK(hipMemcpyAsync(&status, &ctl->status, sizeof(u32), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
   HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  w->dirty = false;
+  if (status != 0) {
+    t_err = "sample: device consistency check failed";
+    return PROFK_EINTERNAL;
+  }
   return PROFK_OK;
 }
 
@@ -553,18 +650,17 @@ int profk_stage_threshold(const float* x, int64_t N, int64_t S, int64_t t, uint6
   Workspace* w = nullptr;
   int rc = get_workspace(s, Need{1, (u64)S, 1, 1}, &w, &L);
   if (rc) return rc;
-  rc = next_gen(w, s);
+  rc = clean_if_dirty(w, L, s);
   if (rc) return rc;
+  w->dirty = true;
   RowCtl* ctl = at<RowCtl>(w, L.ctl);
-  SelState* sel = at<SelState>(w, L.sel);
-  HIPCHK(launch_attempt_init(ctl, sel, nullptr, at<u32>(w, L.ticket), 1, at<u32>(w, L.rhist), s), "launch attempt_init");
-  HIPCHK(launch_sample(x, (u64)N, (u64)S, seed, (u32)attempt, 0u, at<u64>(w, L.hash), L.hash_slots - 1, w->gen,
-                       at<u64>(w, L.keys), ctl, at<u32>(w, L.ticket) + 1, sel->hist, (u64)t, s),
-         "launch sample");
+  HIPCHK(launch_sample(sample_args(w, L, x, (u64)N, (u64)S, (u64)t, seed, (u32)attempt), s), "launch sample");
   HIPCHK(launch_tau_to_output(x, (u64)N, ctl, out_tau_val, out_tau_idx, s), "launch tau_to_output");
+  HIPCHK(launch_clear_sample(at<u32>(w, L.hash), L.hash_used, at<u32>(w, L.ticket), s), "launch clear_sample");
   u32 status = 0;
   HIPCHK(hipMemcpyAsync(&status, &ctl->status, sizeof(u32), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
   HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  w->dirty = false;
   if (status != 0) {
     t_err = "threshold: device consistency check failed";
     return PROFK_EINTERNAL;
@@ -581,6 +677,9 @@ int profk_stage_filter(const float* x, int64_t N, float tau_val, int64_t tau_idx
   Workspace* w = nullptr;
   int rc = get_workspace(s, Need{1, 1, (u64)M, 1}, &w, &L);
   if (rc) return rc;
+  rc = clean_if_dirty(w, L, s);
+  if (rc) return rc;
+  w->dirty = true;
   RowCtl* ctl = at<RowCtl>(w, L.ctl);
   u32 bits;
   std::memcpy(&bits, &tau_val, sizeof(bits));
@@ -594,13 +693,14 @@ int profk_stage_filter(const float* x, int64_t N, float tau_val, int64_t tau_idx
   fa.cand = at<u64>(w, L.cand);
   fa.M = (u64)M;
   fa.k = 1;
-  fa.ticket = at<u32>(w, L.ticket);
+  fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
   fa.rec = nullptr;
   fa.sels = nullptr;
   HIPCHK(launch_filter(fa, 0, s), "launch filter");
   HIPCHK(launch_keys_to_index(at<u64>(w, L.cand), &ctl->R, (u64)M, out_cand_idx, s), "launch keys_to_index");
   HIPCHK(launch_r_to_output(ctl, out_R, s), "launch r_to_output");
   HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  w->dirty = false;
   return PROFK_OK;
 }
 
@@ -637,6 +737,7 @@ void profk_release(void) {
     }
     if (w->host) (void)hipHostFree(w->host);
     if (w->host_rows) (void)hipHostFree(w->host_rows);
+    if (w->hrec) (void)hipHostFree(w->hrec);
     if (w->ev0) (void)hipEventDestroy(w->ev0);
     if (w->ev1) (void)hipEventDestroy(w->ev1);
     (void)hipSetDevice(cur);

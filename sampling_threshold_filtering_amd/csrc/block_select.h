@@ -35,6 +35,41 @@ __device__ inline void block_bitonic_desc(u64* s, u32 P) {
   }
 }
 
+// Lists j = 0..nl-1 of T keys each (T a power of two), each sorted descending, at
+// s + j*T.  Leaves the T largest keys of their union, sorted descending, in s[0..T).
+// Pairwise tree: merging descending lists A and B, max(A[i], B[T-1-i]) holds exactly
+// the T largest of A and B as a bitonic sequence (the first half-cleaner of the
+// bitonic merge of A followed by B reversed), and log2 T half-cleaners sort it.
+__device__ inline void block_merge_lists(u64* s, u32 nl, u32 T) {
+  u32 lt = 0;
+  while ((1u << lt) < T) ++lt;
+  for (u32 l = 0; nl > 1; ++l) {
+    const u32 pairs = nl >> 1;
+    for (u32 e = threadIdx.x; e < (pairs << lt); e += blockDim.x) {
+      const u32 p = e >> lt, i = e & (T - 1);
+      u64* A = s + ((u64)(2 * p) << (l + lt));
+      const u64* B = s + ((u64)(2 * p + 1) << (l + lt));
+      const u64 a = A[i], b = B[T - 1 - i];
+      A[i] = a > b ? a : b;
+    }
+    __syncthreads();
+    for (u32 h = T >> 1; h > 0; h >>= 1) {
+      for (u32 e = threadIdx.x; e < (pairs << lt) >> 1; e += blockDim.x) {
+        const u32 p = e >> (lt - 1), r = e & ((T >> 1) - 1);
+        const u32 i = ((r & ~(h - 1)) << 1) | (r & (h - 1));  // the pair (i, i + h), bit h of i clear
+        u64* A = s + ((u64)(2 * p) << (l + lt));
+        const u64 x0 = A[i], x1 = A[i + h];
+        if (x0 < x1) {
+          A[i] = x1;
+          A[i + h] = x0;
+        }
+      }
+      __syncthreads();
+    }
+    nl = (nl + 1) >> 1;
+  }
+}
+
 struct BlockSelectLds {
   u32 hist[256];
   u32 ncol;
@@ -84,8 +119,10 @@ constexpr u32 kBlockSelectILP = 8;
 
 // Finishes the selection whose state is in *L (set by one of the start functions and
 // visible to every thread); returns the key of the requested rank to all threads.
-// `buf` is an LDS array of `cap` keys (cap a power of two).  *ok_out is false when the
-// state turned out inconsistent (never for distinct keys).
+// keys[0..n) may hold empty slots (key 0, which no valid key equals); the count given
+// to the start functions is that of the valid keys.  `buf` is an LDS array of `cap`
+// keys (cap a power of two).  *ok_out is false when the state turned out inconsistent
+// (never for distinct keys).
 __device__ inline u64 block_select_finish(const u64* keys, u64 n, u64* buf, u32 cap, BlockSelectLds* L,
                                           bool* ok_out) {
   const u64 span = (u64)blockDim.x * kBlockSelectILP;
@@ -104,7 +141,7 @@ __device__ inline u64 block_select_finish(const u64* keys, u64 n, u64* buf, u32 
 #pragma unroll
       for (u32 q = 0; q < kBlockSelectILP; ++q) {
         const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
-        const bool match = i < n && ((kk[q] & mask) == prefix);
+        const bool match = i < n && kk[q] != 0 && ((kk[q] & mask) == prefix);
         wave_hist_add(L->hist, (u32)(kk[q] >> shift) & 255u, match);
       }
     }
@@ -147,7 +184,7 @@ __device__ inline u64 block_select_finish(const u64* keys, u64 n, u64* buf, u32 
 #pragma unroll
         for (u32 q = 0; q < kBlockSelectILP; ++q) {
           const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
-          const bool match = i < n && ((kk[q] & mask) == prefix);
+          const bool match = i < n && kk[q] != 0 && ((kk[q] & mask) == prefix);
           const u64 m = __ballot(match);
           u32 slot = 0;
           if (m) {

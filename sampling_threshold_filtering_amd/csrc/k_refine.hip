@@ -5,16 +5,22 @@
 //
 //   refine_hist_kernel     histogram of the candidates over kBins equal bins of the
 //                          key range [tau, cmax] (cmax = the largest candidate key,
-//                          tracked by the filter).  The last block scans the bins
-//                          from the top: the bin b* that holds the k-th largest
-//                          candidate, the candidates above it, and the output
-//                          offset of every bin >= b*.  If one of those bins holds
-//                          more keys than one workgroup sorts in LDS (ties,
-//                          narrow-range inputs), it marks the row for the
-//                          multi-pass refinement instead.
-//   refine_scatter_kernel  writes the candidates of bins >= b* into bin order.
+//                          tracked by the filter), added into a global histogram.
+//   refine_scatter_kernel  every block scans the global histogram from the top bin
+//                          down in LDS: the bin b* that holds the k-th largest
+//                          candidate and the output offset of every bin >= b*
+//                          (block 0 publishes them).  If one of those bins holds more
+//                          keys than one workgroup sorts in LDS (ties, narrow-range
+//                          inputs), the row is marked for the multi-pass refinement
+//                          instead.  Otherwise each block writes its candidates of
+//                          bins >= b* into bin order: one global atomic per (block,
+//                          bin) reserves the run, LDS atomics place the keys.  Block 0
+//                          also publishes the attempt record (R, check, multi-pass
+//                          flag) to the host, which needs nothing later to decide.
 //   refine_binsort_kernel  sorts every bin >= b* in LDS (four 256-thread workgroups
-//                          per CU) and writes out_vals / out_idx for positions < k.
+//                          per CU) and writes out_vals / out_idx for positions < k;
+//                          it also leaves the histogram and the sampler's hash set
+//                          zero for the next attempt.
 // Bins partition the keys by value, so sorted bins laid out from the top bin down
 // are the sorted candidates; positions < k are the exact top-k in order.
 #include "block_select.h"
@@ -25,161 +31,289 @@ namespace profk {
 namespace {
 constexpr u32 kHistThreads = 1024;
 constexpr u32 kSortThreads = 256;
+constexpr u32 kPer = kBins / kHistThreads;  // bins per thread in the scan
+
+// LDS position of descending bin position q: one spare word per kPer, so that the
+// kPer consecutive positions of each thread fall in distinct banks across a wave.
+__device__ __forceinline__ u32 pad_q(u32 q) { return q + q / kPer; }
 
 __device__ __forceinline__ u32 bin_of(u64 key, u64 tau, u32 shift) {
   const u64 b = (key - tau) >> shift;
   return b < kBins ? (u32)b : kBins - 1u;
 }
 
+__device__ __forceinline__ u32 bin_shift_of(const RowCtl* c) {
+  const u64 range = c->cmax - c->tau;
+  return range < kBins ? 0u : (u32)(64 - __clzll((long long)range)) - kBinBits;
+}
+
 __device__ __forceinline__ u64 cand_count(const RowCtl* c, u64 M) { return c->R < M ? c->R : M; }
+
+// Attempt record into pinned host memory; seq last, released at system scope.
+__device__ __forceinline__ void publish(const RefineArgs& a, const RowCtl* c, u32 generic) {
+  if (!a.hrec) return;
+  HostRecord* h = a.hrec;
+  h->R = c->R;
+  h->status = c->status;
+  h->error = 0;
+  h->generic = generic;
+  __hip_atomic_store(&h->seq, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+constexpr u32 kILP = 8;  // candidate loads in flight per thread
+
+// Block blockIdx.x's contiguous share [lo, hi) of n candidates.
+__device__ __forceinline__ void block_range(u64 n, u64* lo, u64* hi) {
+  const u64 per = (n + gridDim.x - 1) / gridDim.x;
+  *lo = (u64)blockIdx.x * per;
+  *hi = *lo + per < n ? *lo + per : n;
+  if (*lo > n) *lo = n;
+}
+
+// Output value of a candidate key: the value bits follow from the key's order code
+// except for the two codes that fold several encodings (+-0, NaN), which are read back.
+__device__ __forceinline__ u32 value_bits(u64 key, const float* x, u32 idx) {
+  const u32 o = (u32)(key >> 32);
+  if (o == 0x80000000u || o == 0xFFFFFFFFu) return reinterpret_cast<const u32*>(x)[idx];
+  return bits_of_ord32(o);
+}
 }  // namespace
 
 __global__ __launch_bounds__(kHistThreads) void refine_hist_kernel(RefineArgs a) {
   __shared__ u32 s_h[kBins];
-  __shared__ u32 s_part[kHistThreads];
-  __shared__ u32 s_last;
-  RowCtl* c = a.ctl;
+  // the scatter reserves from zero
+  for (u32 b = blockIdx.x * blockDim.x + threadIdx.x; b < kBins; b += gridDim.x * blockDim.x) a.cursor[b] = 0;
+  const RowCtl* c = a.ctl;
   if (c->status != 0) return;
   const u64 n = cand_count(c, a.M);
   const u64 tau = c->tau;
-  const u64 range = c->cmax - tau;
-  const u32 shift = range < kBins ? 0u : (u32)(64 - __clzll((long long)range)) - kBinBits;
+  const u32 shift = bin_shift_of(c);
   for (u32 b = threadIdx.x; b < kBins; b += blockDim.x) s_h[b] = 0;
   __syncthreads();
-  const u64 stride = (u64)gridDim.x * blockDim.x;
-  for (u64 i = (u64)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-    atomicAdd(&s_h[bin_of(a.cand[i], tau, shift)], 1u);
+  u64 lo, hi;
+  block_range(n, &lo, &hi);
+  for (u64 base = lo; base < hi; base += (u64)blockDim.x * kILP) {
+    u64 kk[kILP];
+#pragma unroll
+    for (u32 q = 0; q < kILP; ++q) {
+      const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
+      kk[q] = i < hi ? a.cand[i] : 0ull;
+    }
+#pragma unroll
+    for (u32 q = 0; q < kILP; ++q)
+      if (base + (u64)q * blockDim.x + threadIdx.x < hi) atomicAdd(&s_h[bin_of(kk[q], tau, shift)], 1u);
+  }
   __syncthreads();
   for (u32 b = threadIdx.x; b < kBins; b += blockDim.x)
     if (s_h[b]) atomicAdd(&a.hist[b], s_h[b]);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    s_last = (atomicAdd(a.ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
+}
+
+__global__ __launch_bounds__(kHistThreads) void refine_scatter_kernel(RefineArgs a) {
+  __shared__ u32 s_off[kBins + kBins / kPer + 1];  // by padded descending position; last = total
+  __shared__ u32 s_pos[kBins];
+  __shared__ u32 s_wsum[kHistThreads / kWave];
+  __shared__ u32 s_q, s_big;
+  RowCtl* c = a.ctl;
+  if (c->status != 0) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) publish(a, c, 0u);
+    return;
+  }
+  const u32 tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  const u64 n = cand_count(c, a.M);
+  const u64 tau = c->tau;
+  const u32 shift = bin_shift_of(c);
+  {
+    u32 v[kPer];  // all loads in flight, then the LDS stores
+#pragma unroll
+    for (u32 j = 0; j < kPer; ++j) v[j] = a.hist[j * kHistThreads + tid];
+#pragma unroll
+    for (u32 j = 0; j < kPer; ++j) s_off[pad_q(kBins - 1u - (j * kHistThreads + tid))] = v[j];
+  }
+  if (tid == 0) {
+    s_q = 0xFFFFFFFFu;
+    s_big = 0;
   }
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // Last block.  Thread t owns the kBins / kHistThreads bins counted from the top:
-  // descending position q = kBins-1-b.  Suffix sums over descending positions give
-  // each bin's output offset.
-  constexpr u32 per = kBins / kHistThreads;
-  u32 cnt[per];
+  // exclusive offsets over descending positions: thread tid owns q = tid*kPer + j
+  u32 cnt[kPer];
   u32 sum = 0;
 #pragma unroll
-  for (u32 j = 0; j < per; ++j) {  // independent loads, all in flight together
-    const u32 b = kBins - 1u - (threadIdx.x * per + j);
-    cnt[j] = atomic_load_agent(&a.hist[b]);
-  }
-#pragma unroll
-  for (u32 j = 0; j < per; ++j) {
-    a.hist[kBins - 1u - (threadIdx.x * per + j)] = 0;  // left zero for the next call
+  for (u32 j = 0; j < kPer; ++j) {
+    cnt[j] = s_off[pad_q(tid * kPer + j)];
     sum += cnt[j];
   }
-  s_part[threadIdx.x] = sum;
-  __syncthreads();
-  for (u32 off = 1; off < kHistThreads; off <<= 1) {  // inclusive scan of the parts
-    const u32 v = threadIdx.x >= off ? s_part[threadIdx.x - off] : 0u;
-    __syncthreads();
-    s_part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  u32 run = threadIdx.x ? s_part[threadIdx.x - 1] : 0u;  // keys in the bins above this thread's
-  if (threadIdx.x == 0) {
-    s_h[0] = 0xFFFFFFFFu;  // b* (as a descending position)
-    s_h[1] = 0;            // generic flag
-  }
-  __syncthreads();
-  const u64 k = a.k;
-  u32 offs[per];
+  u32 incl = sum;
 #pragma unroll
-  for (u32 j = 0; j < per; ++j) {
-    const u32 q = threadIdx.x * per + j;
-    offs[j] = run;
-    if (run < k && run + cnt[j] >= k) {  // exactly one bin holds the k-th largest
-      s_h[0] = q;
-      c->bstar = kBins - 1u - q;
-      c->c_above = run;
-    }
+  for (u32 d = 1; d < (u32)kWave; d <<= 1) {
+    const u32 v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  if (lane == kWave - 1) s_wsum[wid] = incl;
+  __syncthreads();
+  u32 run = incl - sum;
+  for (u32 w = 0; w < wid; ++w) run += s_wsum[w];
+  const u64 k = a.k;
+#pragma unroll
+  for (u32 j = 0; j < kPer; ++j) {
+    const u32 q = tid * kPer + j;
+    s_off[pad_q(q)] = run;
+    if (run < k && run + cnt[j] >= k) s_q = q;  // exactly one bin holds the k-th largest
     run += cnt[j];
   }
+  if (tid == blockDim.x - 1) s_off[pad_q(kBins)] = run;
   __syncthreads();
-  const u32 qstar = s_h[0];
-  // offsets and counts are read only for the bins at or above b*
-#pragma unroll
-  for (u32 j = 0; j < per; ++j) {
-    const u32 q = threadIdx.x * per + j;
-    if (q <= qstar) {
-      const u32 b = kBins - 1u - q;
-      a.bin_off[b] = offs[j];
-      a.bin_cnt[b] = cnt[j];
-      a.cursor[b] = 0;
-    }
-  }
+  const u32 qstar = s_q;
   // every bin at or above b* must fit one sorting workgroup
   bool big = qstar == 0xFFFFFFFFu;
 #pragma unroll
-  for (u32 j = 0; j < per; ++j) {
-    const u32 q = threadIdx.x * per + j;
-    if (q <= qstar && cnt[j] > kBinCap) big = true;
-  }
-  if (big) s_h[1] = 1;
+  for (u32 j = 0; j < kPer; ++j)
+    if (tid * kPer + j <= qstar && cnt[j] > kBinCap) big = true;
+  if (big) s_big = 1;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    c->bin_shift = shift;
-    c->generic = s_h[1];
-    if (a.rec) a.rec->generic = s_h[1];
-    *a.ticket = 0;
+  const bool generic = s_big != 0;
+  if (blockIdx.x == 0) {
+    if (!generic)
+      for (u32 q = tid; q <= qstar; q += blockDim.x) {
+        const u32 b = kBins - 1u - q;
+        a.bin_off[b] = s_off[pad_q(q)];
+        a.bin_cnt[b] = s_off[pad_q(q + 1)] - s_off[pad_q(q)];
+      }
+    if (tid == 0) {
+      c->bin_shift = shift;
+      c->bstar = generic ? 0u : kBins - 1u - qstar;
+      c->c_above = generic ? 0u : s_off[pad_q(qstar)];
+      c->generic = generic ? 1u : 0u;
+      if (a.rec) a.rec->generic = generic ? 1u : 0u;
+      publish(a, c, generic ? 1u : 0u);
+    }
   }
-}
+  if (generic) return;
+  const u32 bstar = kBins - 1u - qstar;
 
-// Each block owns a contiguous range of candidates: it counts them per bin in LDS,
-// reserves each (block, bin) run with ONE global atomic, then places its keys with
-// LDS atomics.
-constexpr u32 kScatterThreads = 1024;
-__global__ __launch_bounds__(kScatterThreads) void refine_scatter_kernel(RefineArgs a) {
-  __shared__ u32 s_pos[kBins];
-  const RowCtl* c = a.ctl;
-  if (c->status != 0 || c->generic) return;
-  const u64 n = cand_count(c, a.M);
-  const u64 tau = c->tau;
-  const u32 shift = c->bin_shift, bstar = c->bstar;
-  const u64 per = (n + gridDim.x - 1) / gridDim.x;
-  const u64 lo = (u64)blockIdx.x * per;
-  const u64 hi = lo + per < n ? lo + per : n;
-  for (u32 b = threadIdx.x; b < kBins; b += blockDim.x) s_pos[b] = 0;
+  // this block's contiguous range of candidates, counted per bin >= b*
+  u64 lo, hi;
+  block_range(n, &lo, &hi);
+  for (u32 b = bstar + tid; b < kBins; b += blockDim.x) s_pos[b] = 0;
   __syncthreads();
-  for (u64 i = lo + threadIdx.x; i < hi; i += blockDim.x) {
-    const u32 b = bin_of(a.cand[i], tau, shift);
-    if (b >= bstar) atomicAdd(&s_pos[b], 1u);
+  for (u64 base = lo; base < hi; base += (u64)blockDim.x * kILP) {
+    u64 kk[kILP];
+#pragma unroll
+    for (u32 q = 0; q < kILP; ++q) {
+      const u64 i = base + (u64)q * blockDim.x + tid;
+      kk[q] = i < hi ? a.cand[i] : 0ull;
+    }
+#pragma unroll
+    for (u32 q = 0; q < kILP; ++q) {
+      const u32 b = bin_of(kk[q], tau, shift);
+      if (base + (u64)q * blockDim.x + tid < hi && b >= bstar) atomicAdd(&s_pos[b], 1u);
+    }
   }
   __syncthreads();
-  for (u32 b = threadIdx.x; b < kBins; b += blockDim.x) {
-    const u32 cnt = s_pos[b];
-    if (cnt) s_pos[b] = a.bin_off[b] + atomicAdd(&a.cursor[b], cnt);
+  {
+    // reserve each (block, bin) run: all of this thread's atomics in flight together
+    u32 m[kPer], got[kPer];
+#pragma unroll
+    for (u32 j = 0; j < kPer; ++j) {
+      const u32 b = bstar + tid + j * kHistThreads;
+      m[j] = b < kBins ? s_pos[b] : 0u;
+    }
+#pragma unroll
+    for (u32 j = 0; j < kPer; ++j) got[j] = m[j] ? atomicAdd(&a.cursor[bstar + tid + j * kHistThreads], m[j]) : 0u;
+#pragma unroll
+    for (u32 j = 0; j < kPer; ++j) {
+      const u32 b = bstar + tid + j * kHistThreads;
+      if (m[j]) s_pos[b] = s_off[pad_q(kBins - 1u - b)] + got[j];
+    }
   }
   __syncthreads();
-  for (u64 i = lo + threadIdx.x; i < hi; i += blockDim.x) {
-    const u64 key = a.cand[i];
-    const u32 b = bin_of(key, tau, shift);
-    if (b >= bstar) {
-      const u32 pos = atomicAdd(&s_pos[b], 1u);
-      if (pos < a.M) a.tmp[pos] = key;
+  for (u64 base = lo; base < hi; base += (u64)blockDim.x * kILP) {
+    u64 kk[kILP];
+#pragma unroll
+    for (u32 q = 0; q < kILP; ++q) {
+      const u64 i = base + (u64)q * blockDim.x + tid;
+      kk[q] = i < hi ? a.cand[i] : 0ull;
+    }
+#pragma unroll
+    for (u32 q = 0; q < kILP; ++q) {
+      const u32 b = bin_of(kk[q], tau, shift);
+      if (base + (u64)q * blockDim.x + tid < hi && b >= bstar) {
+        const u32 pos = atomicAdd(&s_pos[b], 1u);
+        if (pos < a.M) a.tmp[pos] = kk[q];
+      }
     }
   }
 }
 
+constexpr u32 kWaveBin = 1024;  // largest bin one wavefront sorts in registers (16 keys per lane)
+
+__device__ __forceinline__ void write_out(const RefineArgs& a, u64 p, u64 key) {
+  const u32 idx = key_index(key);
+  a.out_idx[p] = idx < a.N ? (int64_t)idx : -1;
+  if (idx < a.N) reinterpret_cast<u32*>(a.out_vals)[p] = value_bits(key, a.x, idx);
+}
+
+// One bin of cnt <= 64*M keys at tmp[start..), sorted by one wavefront in registers;
+// positions below lim are written out.
+template <int M>
+__device__ __forceinline__ void wave_bin(const RefineArgs& a, u32 start, u32 cnt, u64 lim) {
+  const u32 lane = lane_id();
+  u64 v[M];
+#pragma unroll
+  for (int r = 0; r < M; ++r) {
+    const u32 i = (u32)r * kWave + lane;
+    v[r] = i < cnt ? a.tmp[start + i] : 0ull;
+  }
+  wave_sort_regs_desc<M>(v);
+#pragma unroll
+  for (int r = 0; r < M; ++r) {
+    const u32 i = (u32)r * kWave + lane;
+    if (i < lim) write_out(a, (u64)start + i, v[r]);
+  }
+}
+
+// Bins of up to kWaveBin keys: one wavefront each, sorted in registers.  Larger bins
+// (up to kBinCap): the whole workgroup in LDS.
 __global__ __launch_bounds__(kSortThreads) void refine_binsort_kernel(RefineArgs a) {
   __shared__ u64 s[kBinCap];
+  __shared__ u32 s_big[kSortThreads];
+  __shared__ u32 s_nbig;
+  {  // leave the histogram and the sampler's hash set zero for the next attempt
+    const u64 gt = (u64)blockIdx.x * blockDim.x + threadIdx.x, gs = (u64)gridDim.x * blockDim.x;
+    for (u64 i = gt; i < kBins; i += gs) a.hist[i] = 0;
+    if (a.table)
+      for (u64 i = gt; i < a.table_slots; i += gs) a.table[i] = 0;
+  }
   const RowCtl* c = a.ctl;
   if (c->status != 0 || c->generic) return;
   const int bstar = (int)c->bstar;
   const u64 k = a.k;
-  for (int b = (int)kBins - 1 - (int)blockIdx.x; b >= bstar; b -= (int)gridDim.x) {
+  const u32 lane = lane_id();
+  const u32 wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nwaves = (int)(gridDim.x * (kSortThreads / kWave));
+  if (threadIdx.x == 0) s_nbig = 0;
+  __syncthreads();
+  for (int b = (int)kBins - 1 - (int)(blockIdx.x * (kSortThreads / kWave) + wid); b >= bstar; b -= nwaves) {
     const u32 cnt = a.bin_cnt[b];
     const u32 start = a.bin_off[b];
-    if (cnt == 0 || start >= k || cnt > kBinCap || start + (u64)cnt > a.M) continue;  // uniform per workgroup
+    if (cnt == 0 || start >= k || start + (u64)cnt > a.M) continue;  // uniform per wavefront
+    if (cnt > kWaveBin) {
+      if (lane == 0) s_big[atomicAdd(&s_nbig, 1u)] = (u32)b;  // at most one per wavefront pass
+      continue;
+    }
+    const u64 lim = k - start < cnt ? k - start : cnt;
+    if (cnt <= 64) wave_bin<1>(a, start, cnt, lim);
+    else if (cnt <= 128) wave_bin<2>(a, start, cnt, lim);
+    else if (cnt <= 256) wave_bin<4>(a, start, cnt, lim);
+    else if (cnt <= 512) wave_bin<8>(a, start, cnt, lim);
+    else wave_bin<16>(a, start, cnt, lim);
+  }
+  __syncthreads();
+  const u32 nbig = s_nbig;
+  for (u32 q = 0; q < nbig; ++q) {
+    const u32 b = s_big[q];
+    const u32 cnt = a.bin_cnt[b];
+    const u32 start = a.bin_off[b];
+    if (cnt > kBinCap) continue;  // the scan sent such rows to the multi-pass refinement
     u32 P = 1;
     while (P < cnt) P <<= 1;
     __syncthreads();
@@ -187,22 +321,21 @@ __global__ __launch_bounds__(kSortThreads) void refine_binsort_kernel(RefineArgs
     __syncthreads();
     block_bitonic_desc(s, P);
     const u64 lim = k - start < cnt ? k - start : cnt;
-    for (u32 i = threadIdx.x; i < lim; i += blockDim.x) {
-      const u32 idx = key_index(s[i]);
-      const u64 p = start + i;
-      a.out_idx[p] = idx < a.N ? (int64_t)idx : -1;
-      if (idx < a.N) reinterpret_cast<u32*>(a.out_vals)[p] = reinterpret_cast<const u32*>(a.x)[idx];
-    }
+    for (u32 i = threadIdx.x; i < lim; i += blockDim.x) write_out(a, start + i, s[i]);
   }
 }
 
 hipError_t launch_refine(const RefineArgs& a, hipStream_t s) {
   u32 gh = (u32)((a.M + 16383) / 16384);  // about 16 candidates per thread
   if (gh < 1) gh = 1;
-  if (gh > 32) gh = 32;  // each block adds its nonzero bins to the global histogram
+  if (gh > 32) gh = 32;  // each block adds its nonzero bins to the global histogram and scans it
   refine_hist_kernel<<<gh, kHistThreads, 0, s>>>(a);
-  refine_scatter_kernel<<<gh, kScatterThreads, 0, s>>>(a);
-  refine_binsort_kernel<<<4 * device_cu_count(), kSortThreads, 0, s>>>(a);
+  refine_scatter_kernel<<<gh, kHistThreads, 0, s>>>(a);
+  // at least 64 workgroups: a workgroup then meets at most kSortThreads bins above
+  // one wavefront's share (s_big)
+  u32 gs = 4 * device_cu_count();
+  if (gs < 64) gs = 64;
+  refine_binsort_kernel<<<gs, kSortThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

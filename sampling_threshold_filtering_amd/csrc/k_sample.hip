@@ -1,22 +1,27 @@
 // Stage 1 of Prof-K ("Prof-K: Probabilistic One-Pass Filtering for Efficient Top-k
-// Selection", §3, stage 1): S indices drawn uniformly without replacement.
+// Selection", §3, stage 1): S indices drawn uniformly without replacement, and
+// stage 2: tau = the t-th largest sampled entry.
 //
 // The pages leave the procedure open.  The sample here is the set of the first S
 // distinct indices of the Philox stream of (seed, attempt, row) in draw order
 // (see profk_device.h for the draw).  That rule is symmetric under relabelling of
 // [N], so every S-subset is equally likely, and it is deterministic per seed.
 //
-//   sample_kernel   one thread per draw 0..S-1: each index goes into a hash set in
-//                   device memory (open addressing, 64-bit slots tagged with a
-//                   per-attempt generation so the table never needs clearing); the
-//                   first insert of each index gathers x[idx] into a key, and each
-//                   block reserves its key slots with one atomic.  The last block
-//                   then (a) tops up: while fewer than S distinct indices are held,
-//                   wavefront 0 takes further draws S, S+1, ... in order, 64 at a
-//                   time, keeping those that are new and not repeated earlier in the
-//                   same chunk (expected extra draws about S^2 / (2N)); and (b) selects
-//                   tau, the t-th largest of the S keys, by a one-workgroup radix
-//                   select (stage 2), so stages 1 and 2 cost a single launch.
+//   sample_kernel   one thread per draw 0..S-1.  Each index goes into a hash set of
+//                   32-bit slots in device memory (idx + 1, 0 = empty, one CAS per
+//                   probe; the set is zero on entry and cleared again after the
+//                   attempt), while the gather of x[idx] is already in flight.  Draw
+//                   j keeps its key in keys[j], or 0 when it repeats an earlier draw
+//                   (no valid key is 0).  For t <= kTopT each block also sorts its
+//                   wavefronts' keys in registers and stores its own t largest keys.
+//                   The last block (a) tops up: while fewer than S distinct indices
+//                   are held, wavefront 0 takes further draws S, S+1, ... in order,
+//                   64 at a time, keeping those that are new and not repeated earlier
+//                   in the same chunk (expected extra draws about S^2 / (2N)), into
+//                   keys[S..]; and (b) selects tau.  With the per-block lists, every
+//                   key among the t largest is at least L = the largest block-local
+//                   t-th key, so only the listed keys >= L are sorted.  Otherwise a
+//                   one-workgroup radix select over all key slots runs.
 #include "block_select.h"
 #include "launch.h"
 
@@ -34,29 +39,25 @@ __device__ __forceinline__ u32 mix32(u32 h) {
   return h;
 }
 
+// Open-addressing set of 32-bit slots holding idx + 1 (0 = empty), linear probing.
 // Returns true when idx was not in the set (and is now).
-__device__ bool hash_insert(u64* table, u64 tmask, u32 gen, u32 idx) {
-  const u64 mine = ((u64)gen << 32) | idx;
+__device__ bool hash_insert(u32* table, u64 tmask, u32 idx) {
+  const u32 mine = idx + 1u;
   u64 h = mix32(idx) & tmask;
   for (u64 probe = 0; probe <= tmask; ++probe) {
-    u64 cur = atomic_load_agent(&table[h]);
-    while ((u32)(cur >> 32) != gen) {  // stale slot of an older generation: free
-      const u64 prev = atomicCAS(&table[h], cur, mine);
-      if (prev == cur) return true;
-      cur = prev;
-    }
-    if ((u32)cur == idx) return false;
+    const u32 prev = atomicCAS(&table[h], 0u, mine);
+    if (prev == 0u || prev == mine) return prev == 0u;
     h = (h + 1) & tmask;
   }
   return false;  // unreachable: the table holds at least 2S slots
 }
 
-__device__ bool hash_contains(const u64* table, u64 tmask, u32 gen, u32 idx) {
+__device__ bool hash_contains(const u32* table, u64 tmask, u32 idx) {
+  const u32 mine = idx + 1u;
   u64 h = mix32(idx) & tmask;
   for (u64 probe = 0; probe <= tmask; ++probe) {
-    const u64 cur = atomic_load_agent(&table[h]);
-    if ((u32)(cur >> 32) != gen) return false;
-    if ((u32)cur == idx) return true;
+    const u32 cur = atomic_load_agent(&table[h]);
+    if (cur == 0u || cur == mine) return cur == mine;
     h = (h + 1) & tmask;
   }
   return false;
@@ -94,77 +95,82 @@ __global__ __launch_bounds__(1024) void attempt_init_kernel(RowCtl* ctl, SelStat
 }
 
 constexpr u32 kSampleThreads = 1024;
-constexpr u32 kTauCap = 8192;  // keys the last block sorts in LDS (64 KB)
+constexpr u32 kSampleWaves = kSampleThreads / kWave;
+constexpr u32 kTauCap = 8192;  // keys the last block sorts or selects from in LDS (64 KB)
 
-// Draws 0..S-1 (one per thread), dedupes them through the hash set and gathers
-// the keys of the first inserts; the block reserves its slots with ONE atomic.
-// The last block to finish then tops the sample up to exactly S distinct indices
-// (wavefront 0, draws S, S+1, ... in order) and, when t > 0, selects
-// tau = the t-th largest sampled key (P1 §3 stage 2) into ctl->tau.
-__global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __restrict__ x, u64 N, u64 S,
-                                                                u64 seed, u32 attempt, u32 row, u64* table,
-                                                                u64 tmask, u32 gen, u64* __restrict__ keys,
-                                                                RowCtl* ctl, u32* ticket, u32* top_hist, u64 t) {
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
   __shared__ u64 s_buf[kTauCap];
   __shared__ BlockSelectLds s_sel;
-  __shared__ u32 s_wcnt[kSampleThreads / kWave];
-  __shared__ u64 s_base;
-  __shared__ u64 s_D;
+  __shared__ u32 s_wcnt[kSampleWaves];
+  __shared__ u32 s_n;
   __shared__ u32 s_last;
+  __shared__ u64 s_D, s_E;
   const u32 lane = lane_id(), wid = threadIdx.x / kWave;
+  const bool select = a.t > 0;
+  const bool use_hist = select && !a.fast;
+  for (u32 b = threadIdx.x; b < 256; b += blockDim.x) s_sel.hist[b] = 0;
+  if (threadIdx.x == 0) s_n = 0;
+
+  // one draw per thread
   const u64 j = (u64)blockIdx.x * kSampleThreads + threadIdx.x;
   bool fresh = false;
-  u32 idx = 0;
-  if (j < S) {
-    idx = (u32)sample_draw(j, row, attempt, seed, N);
-    fresh = hash_insert(table, tmask, gen, idx);
+  u64 key = 0;
+  if (j < a.S) {
+    const u32 idx = (u32)sample_draw(j, a.row, a.attempt, a.seed, a.N);
+    const u32 bits = __float_as_uint(a.x[idx]);  // issued before the insert: both in flight
+    fresh = hash_insert(a.table, a.tmask, idx);
+    if (fresh) key = make_key(bits, idx);
+    a.keys[j] = key;
   }
-  const u64 m = __ballot(fresh);
-  if (lane == 0) s_wcnt[wid] = (u32)__popcll(m);
+  const u64 fm = __ballot(fresh);
+  if (lane == 0) s_wcnt[wid] = (u32)__popcll(fm);
+  // fast path: lists of T = pow2(t) keys, each sorted descending
+  u32 T = 1;
+  while (T < a.t) T <<= 1;
+  if (a.fast) {
+    key = wave_sort_desc(key);
+    if (lane < T) s_buf[wid * T + lane] = key;  // this wavefront's T largest (0-padded)
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     u32 tot = 0;
-    for (u32 w = 0; w < kSampleThreads / kWave; ++w) {
-      const u32 c = s_wcnt[w];
-      s_wcnt[w] = tot;
-      tot += c;
-    }
-    s_base = tot ? atomicAdd(&ctl->D, (u64)tot) : 0ull;
+    for (u32 w = 0; w < kSampleWaves; ++w) tot += s_wcnt[w];
+    if (tot) atomicAdd(a.dcount, tot);
   }
-  __syncthreads();
-  u64 key = 0;
-  if (fresh) {
-    key = make_key(__float_as_uint(x[idx]), idx);
-    const u64 slot = s_base + s_wcnt[wid] + count_below(m);
-    if (slot < S) keys[slot] = key;
+  if (use_hist) {
+    // histogram of the top 8 bits: the first digit of the radix select
+    wave_hist_add(s_sel.hist, (u32)(key >> 56), fresh);
+    __syncthreads();
+    for (u32 b = threadIdx.x; b < 256; b += blockDim.x)
+      if (s_sel.hist[b]) atomicAdd(&a.top_hist[b], s_sel.hist[b]);
+  } else if (a.fast) {
+    block_merge_lists(s_buf, kSampleWaves, T);  // the block's T largest keys
+    for (u32 i = threadIdx.x; i < T; i += blockDim.x) a.tops[(u64)blockIdx.x * T + i] = s_buf[i];
   }
-  // histogram of the top 8 bits of this block's keys: the first digit of the
-  // threshold selection, so the last block starts one pass further on
-  for (u32 b = threadIdx.x; b < 256; b += blockDim.x) s_sel.hist[b] = 0;
-  __syncthreads();
-  wave_hist_add(s_sel.hist, (u32)(key >> 56), fresh);
-  __syncthreads();
-  for (u32 b = threadIdx.x; b < 256; b += blockDim.x)
-    if (s_sel.hist[b]) atomicAdd(&top_hist[b], s_sel.hist[b]);
-  // release this block's keys, then elect the last block
+  // release this block's keys and lists, then elect the last block
   __syncthreads();
   if (threadIdx.x == 0) {
     __threadfence();
-    s_last = (atomicAdd(ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
+    s_last = (atomicAdd(a.ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
   }
   __syncthreads();
   if (!s_last) return;
   __threadfence();
 
+  if (threadIdx.x == 0) {
+    s_D = atomic_load_agent(a.dcount);
+    *a.dcount = 0;  // left zero for the next launch
+  }
+  __syncthreads();
   // top-up by wavefront 0
   if (wid == 0) {
-    u64 D = atomicAdd(&ctl->D, 0ull);
-    u64 j0 = S;
+    const u64 D = s_D;
+    u64 E = 0, j0 = a.S;
     u32 guard = 0;
     bool failed = false;
-    while (D < S) {
-      const u32 idx2 = (u32)sample_draw(j0 + lane, row, attempt, seed, N);
-      const bool held = hash_contains(table, tmask, gen, idx2);
+    while (D + E < a.S) {
+      const u32 idx2 = (u32)sample_draw(j0 + lane, a.row, a.attempt, a.seed, a.N);
+      const bool held = hash_contains(a.table, a.tmask, idx2);
       bool repeat = false;
       for (int d = 1; d < kWave; ++d) {
         const u32 other = __shfl_up(idx2, d, kWave);
@@ -172,47 +178,134 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const float* __r
       }
       const bool ok2 = !held && !repeat;
       const u64 m2 = __ballot(ok2);
-      const u64 need = S - D;
+      const u64 need = a.S - D - E;
       const u32 r = count_below(m2);
       if (ok2 && r < need) {
-        hash_insert(table, tmask, gen, idx2);
-        const u64 key2 = make_key(__float_as_uint(x[idx2]), idx2);
-        keys[D + r] = key2;
-        atomicAdd(&top_hist[key2 >> 56], 1u);
+        hash_insert(a.table, a.tmask, idx2);
+        const u64 key2 = make_key(__float_as_uint(a.x[idx2]), idx2);
+        a.keys[a.S + E + r] = key2;
+        if (use_hist) atomicAdd(&a.top_hist[key2 >> 56], 1u);
       }
       const u64 got = (u64)__popcll(m2);
-      D += got < need ? got : need;
+      E += got < need ? got : need;
       j0 += kWave;
       if (++guard > (1u << 22)) {  // bounded: S <= N/2 makes each draw new with prob >= 1/2
         failed = true;
         break;
       }
     }
-    if (lane == 0) {
-      s_D = failed ? ~0ull : D;
-      ctl->D = D;
-    }
+    if (lane == 0) s_E = failed ? ~0ull : E;
   }
   __syncthreads();
-  const bool sample_ok = s_D == S;
-  for (u32 b = threadIdx.x; b < 256; b += blockDim.x) {
-    s_sel.hist[b] = atomicAdd(&top_hist[b], 0u);
-    top_hist[b] = 0;  // left zero for the next attempt
-  }
-  __syncthreads();
-  if (t > 0) {
-    if (threadIdx.x == 0) block_select_start_from_top_hist(&s_sel, s_sel.hist, sample_ok ? S : 0, t);
-    __syncthreads();
-    bool ok = false;
-    const u64 tau = block_select_finish(keys, S, s_buf, kTauCap, &s_sel, &ok);
-    if (threadIdx.x == 0) {
-      ctl->tau = tau;
-      if (!ok) ctl->status = 3;
+  const u64 E = s_E;
+  const bool sample_ok = E != ~0ull && s_D + E == a.S;
+  const u64 nslots = a.S + (sample_ok ? E : 0ull);
+  bool ok = sample_ok;
+  u64 tau = 0;
+  if (select) {
+    if (a.fast && sample_ok && a.t + E <= kTauCap) {
+      // merge the blocks' lists: the T largest keys of the draws, sorted
+      const u64 ntops = (u64)gridDim.x * T;  // <= kTopBlocks * kTopT = kTauCap
+      constexpr u32 kILP = 8;
+      for (u64 base = 0; base < ntops; base += (u64)blockDim.x * kILP) {
+        u64 kk[kILP];
+#pragma unroll
+        for (u32 q = 0; q < kILP; ++q) {
+          const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
+          kk[q] = i < ntops ? a.tops[i] : 0ull;
+        }
+#pragma unroll
+        for (u32 q = 0; q < kILP; ++q) {
+          const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
+          if (i < ntops) s_buf[i] = kk[q];
+        }
+      }
+      __syncthreads();
+      block_merge_lists(s_buf, gridDim.x, T);
+      if (E > 0) {
+        // top-up keys: those at or above the t-th largest of the draws join its t
+        // largest, and the t-th of that set is tau
+        const u64 L = s_buf[a.t - 1];
+        if (threadIdx.x == 0) s_n = (u32)a.t;
+        __syncthreads();
+        for (u64 i = threadIdx.x; i < E; i += blockDim.x) {
+          const u64 kk = a.keys[a.S + i];
+          if (kk >= L) s_buf[atomicAdd(&s_n, 1u)] = kk;  // at most t + E <= kTauCap keys
+        }
+        __syncthreads();
+        const u32 nc = s_n;
+        u32 P = 1;
+        while (P < nc) P <<= 1;
+        for (u32 i = nc + threadIdx.x; i < P; i += blockDim.x) s_buf[i] = 0ull;
+        __syncthreads();
+        block_bitonic_desc(s_buf, P);
+      }
+      tau = s_buf[a.t - 1];
+      ok = tau != 0;
+    } else {
+      if (use_hist) {
+        for (u32 b = threadIdx.x; b < 256; b += blockDim.x) {
+          s_sel.hist[b] = atomicAdd(&a.top_hist[b], 0u);
+          a.top_hist[b] = 0;  // left zero for the next launch
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) block_select_start_from_top_hist(&s_sel, s_sel.hist, sample_ok ? a.S : 0, a.t);
+      } else if (threadIdx.x == 0) {
+        block_select_start(&s_sel, sample_ok ? a.S : 0, a.t);
+      }
+      __syncthreads();
+      bool ok2 = false;
+      tau = block_select_finish(a.keys, nslots, s_buf, kTauCap, &s_sel, &ok2);
+      ok = ok && ok2;
     }
-  } else if (threadIdx.x == 0 && !sample_ok) {
-    ctl->status = 3;
   }
-  if (threadIdx.x == 0) *ticket = 0;
+  if (threadIdx.x == 0) {
+    // per-attempt control state for the filter and the refinement
+    RowCtl* c = a.ctl;
+    c->D = nslots;
+    c->tau = tau;
+    c->R = 0;
+    c->kth = 0;
+    c->nsel = 0;
+    c->key_or = 0;
+    c->key_and = ~0ull;
+    c->cmax = 0;
+    c->status = ok ? 0u : 3u;
+    c->cur = 0;
+    c->ticket = 0;
+    c->bin_shift = 0;
+    c->bstar = 0;
+    c->c_above = 0;
+    c->generic = 0;
+    if (a.rec) {
+      a.rec->R = 0;
+      a.rec->status = ok ? 0u : 3u;
+      a.rec->error = 0;
+      a.rec->generic = 0;
+    }
+    *a.ticket = 0;
+  }
+}
+
+// Zeroes the hash slots a sampling launch used and the tickets (stage entry points,
+// which do not run the refinement that clears them otherwise).
+__global__ void clear_sample_kernel(u32* table, u64 slots, u32* tickets) {
+  const u64 gs = (u64)gridDim.x * blockDim.x;
+  for (u64 i = (u64)blockIdx.x * blockDim.x + threadIdx.x; i < slots; i += gs) table[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x < kTickets) tickets[threadIdx.x] = 0;
+}
+
+// Indices of the nonzero keys among keys[0 .. min(*n_ptr, n_cap)), appended in any order.
+__global__ void keys_to_index_compact_kernel(const u64* __restrict__ keys, const u64* n_ptr, u64 n_cap,
+                                             int64_t* __restrict__ out, u32* counter) {
+  u64 n = *n_ptr;
+  if (n > n_cap) n = n_cap;
+  for (u64 i0 = (u64)blockIdx.x * blockDim.x; i0 < n; i0 += (u64)gridDim.x * blockDim.x) {
+    const u64 i = i0 + threadIdx.x;
+    const u64 key = i < n ? keys[i] : 0ull;
+    const u32 slot = wave_reserve32(counter, key != 0);
+    if (key != 0) out[slot] = (int64_t)key_index(key);
+  }
 }
 
 // Stage-level helpers: keys -> int64 indices, tau -> (value, index).
@@ -258,11 +351,28 @@ hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u
   return hipGetLastError();
 }
 
-hipError_t launch_sample(const float* x, u64 N, u64 S, u64 seed, u32 attempt, u32 row, u64* table, u64 tmask,
-                         u32 gen, u64* keys, RowCtl* ctl, u32* ticket, u32* top_hist, u64 t, hipStream_t s) {
-  const u32 blocks = (u32)((S + kSampleThreads - 1) / kSampleThreads);
-  sample_kernel<<<blocks, kSampleThreads, 0, s>>>(x, N, S, seed, attempt, row, table, tmask, gen, keys, ctl, ticket,
-                                                  top_hist, t);
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
+  const u32 blocks = (u32)((a.S + kSampleThreads - 1) / kSampleThreads);
+  sample_kernel<<<blocks, kSampleThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+u32 sample_blocks(u64 S) { return (u32)((S + kSampleThreads - 1) / kSampleThreads); }
+
+hipError_t launch_clear_sample(u32* table, u64 slots, u32* tickets, hipStream_t s) {
+  u64 blocks = (slots + 1023) / 1024;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) blocks = 1;
+  clear_sample_kernel<<<(u32)blocks, 1024, 0, s>>>(table, slots, tickets);
+  return hipGetLastError();
+}
+
+hipError_t launch_keys_to_index_compact(const u64* keys, const u64* n_ptr, u64 n_cap, int64_t* out, u32* counter,
+                                        hipStream_t s) {
+  u32 blocks = (u32)((n_cap + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) blocks = 1;
+  keys_to_index_compact_kernel<<<blocks, 256, 0, s>>>(keys, n_ptr, n_cap, out, counter);
   return hipGetLastError();
 }
 

@@ -6,7 +6,7 @@
 namespace profk {
 
 constexpr u32 kSmallSort = 8192;  // keys sorted by one workgroup in LDS (64 KB)
-constexpr u32 kTickets = 64;      // u32 last-block tickets in the workspace, cleared every attempt
+constexpr u32 kTickets = 64;      // u32 tickets / counters in the workspace; each user leaves its own zero
 constexpr u32 kFilterBlocksPerCU = 2;  // persistent filter grid: 2 blocks x 4 waves per CU
 
 // Compute units of the current device (cached per device).
@@ -41,8 +41,37 @@ struct FilterArgs {
 
 hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u32* tickets, u32 nrows,
                                u32* refine_hist, hipStream_t s);
-hipError_t launch_sample(const float* x, u64 N, u64 S, u64 seed, u32 attempt, u32 row, u64* table, u64 tmask,
-                         u32 gen, u64* keys, RowCtl* ctl, u32* ticket, u32* top_hist, u64 t, hipStream_t s);
+// Stages 1-2 (k_sample.hip).  Ticket slots of the workspace's ticket array:
+constexpr u32 kTicketFilter = 0;  // filter kernel
+constexpr u32 kTicketSample = 1;  // sampling kernel
+constexpr u32 kCountSample = 3;   // distinct draws of the sampling kernel
+constexpr u32 kCountStage = 4;    // output counter of the stage entry points
+constexpr u32 kTopT = 64;         // largest t of the per-block-list threshold path
+constexpr u32 kTopBlocks = 128;   // most sampling blocks of that path (S <= 131072)
+
+struct SampleArgs {
+  const float* x;
+  u64 N, S;
+  u64 seed;
+  u32 attempt, row;
+  u32* table;       // hash set, tmask + 1 slots, zero on entry
+  u64 tmask;
+  u64* keys;        // 2S slots: draw j < S at keys[j] (0 = repeat), top-up from keys[S]
+  u64* tops;        // per block its t largest keys (fast path), kTopBlocks * kTopT
+  RowCtl* ctl;      // tau out; the per-attempt fields are reset
+  AttemptRecord* rec;  // reset, or nullptr
+  u32* ticket;      // zero on entry, left zero
+  u32* dcount;      // zero on entry, left zero
+  u32* top_hist;    // 256 words, zero on entry, left zero
+  u64 t;            // threshold rank (0: sample only)
+  u32 fast;         // 1: per-block lists (t <= kTopT, at most kTopBlocks blocks)
+};
+
+u32 sample_blocks(u64 S);
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
+hipError_t launch_clear_sample(u32* table, u64 slots, u32* tickets, hipStream_t s);
+hipError_t launch_keys_to_index_compact(const u64* keys, const u64* n_ptr, u64 n_cap, int64_t* out, u32* counter,
+                                        hipStream_t s);
 hipError_t launch_keys_to_index(const u64* keys, const u64* n_ptr, u64 n_cap, int64_t* out, hipStream_t s);
 hipError_t launch_tau_to_output(const float* x, u64 N, const RowCtl* ctl, float* out_val, int64_t* out_idx,
                                 hipStream_t s);
@@ -77,7 +106,10 @@ struct RefineArgs {
   u32* bin_off;     // kBins
   u32* bin_cnt;     // kBins
   u32* cursor;      // kBins
-  u32* ticket;      // zero on entry, left zero
+  u32* table;       // sampler hash set cleared by the last launch, or nullptr
+  u64 table_slots;
+  HostRecord* hrec;  // pinned host record published by the scan, or nullptr
+  u32 seq;
   AttemptRecord* rec;
   float* out_vals;
   int64_t* out_idx;

@@ -114,6 +114,62 @@ __device__ __forceinline__ u32 wave_reserve32(u32* counter, bool pred) {
   return base + count_below(m);
 }
 
+// Descending bitonic sort of one key per lane across the wavefront, in registers.
+__device__ __forceinline__ u64 wave_sort_desc(u64 v) {
+  const u32 lane = lane_id();
+#pragma unroll
+  for (u32 k = 2; k <= (u32)kWave; k <<= 1) {
+#pragma unroll
+    for (u32 j = k >> 1; j > 0; j >>= 1) {
+      const u64 p = __shfl_xor(v, (int)j);
+      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+      v = keep_max ? (v > p ? v : p) : (v < p ? v : p);
+    }
+  }
+  return v;
+}
+
+// Descending bitonic sort of 64*M keys held M per lane: element i = r*64 + lane is
+// v[r] of that lane.  Strides below 64 exchange across lanes, larger ones across
+// registers of the same lane; every decision is known at compile time except the lane.
+template <int M>
+__device__ __forceinline__ void wave_sort_regs_desc(u64 (&v)[M]) {
+  const u32 lane = lane_id();
+#pragma unroll
+  for (u32 k = 2; k <= 64u * M; k <<= 1) {
+#pragma unroll
+    for (u32 j = k >> 1; j > 0; j >>= 1) {
+      if (j < (u32)kWave) {
+        // all M exchanges first (independent LDS-crossbar operations in flight),
+        // then the compare-exchanges
+        u64 p[M];
+#pragma unroll
+        for (int r = 0; r < M; ++r) p[r] = __shfl_xor(v[r], (int)j);
+        __builtin_amdgcn_sched_barrier(0);  // keep the exchanges ahead of their uses
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+          const u32 i = (u32)r * kWave + lane;
+          const bool keep_max = ((i & j) == 0) == ((i & k) == 0);
+          if ((v[r] < p[r]) == keep_max) v[r] = p[r];  // take the partner's key
+        }
+      } else {
+        const u32 rj = j / kWave;
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+          if ((r & rj) == 0) {
+            const int r2 = r | (int)rj;
+            const bool up = (((u32)r * kWave) & k) == 0;  // lower element's block direction
+            const u64 x0 = v[r], x1 = v[r2];
+            const u64 hi = x0 > x1 ? x0 : x1, lo = x0 > x1 ? x1 : x0;
+            v[r] = up ? hi : lo;
+            v[r2] = up ? lo : hi;
+          }
+        }
+      }
+    }
+  }
+}
+
 // Lanes with equal 8-bit digit (among those with active set): mask of those lanes.
 __device__ __forceinline__ u64 wave_match8(u32 digit, bool active) {
   u64 same = __ballot(active);
@@ -182,6 +238,18 @@ struct AttemptRecord {
   u32 error;
   u32 generic;  // the binned refinement deferred to the multi-pass one
   u32 pad;
+};
+
+// The attempt record as published into pinned host memory by the refinement: the
+// host waits for `seq` to reach the value of its call instead of synchronising the
+// stream, and returns while the last refinement launch is still writing outputs.
+struct HostRecord {
+  u64 R;
+  u32 status;
+  u32 error;
+  u32 generic;
+  u32 seq;  // written last, with system-scope release
+  u64 pad;
 };
 
 }  // namespace profk

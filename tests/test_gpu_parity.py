@@ -49,10 +49,25 @@ def test_sample_matches_oracle(N, S, seed, attempt):
                                              ("few_levels", 100000, 20000, 500, 1),
                                              ("adv_noise", 1 << 20, 32768, 7, 2),
                                              ("signed_zeros", 50000, 10000, 3000, 4),
-                                             ("uniform", 1 << 22, 131072, 1, 9)])
+                                             ("uniform", 1 << 22, 131072, 1, 9),
+                                             # per-block-list path (t <= 64): boundary t, ragged last block,
+                                             # heavy top-up (S = N/2), special values, ties
+                                             ("pareto", 1 << 24, 131072, 64, 11),
+                                             ("normal", 100003, 3001, 50, 12),
+                                             ("uniform", 5000, 2500, 10, 13),
+                                             ("with_inf", 1 << 20, 32768, 20, 14),
+                                             ("with_nan", 1 << 20, 32768, 2, 15),
+                                             ("all_equal", 100000, 20000, 64, 16),
+                                             ("negative", 1 << 20, 32768, 33, 17),
+                                             ("ascending", 1 << 20, 8192, 64, 18),
+                                             # lists overflow the LDS buffer (128 x 64 + top-up): radix select
+                                             ("uniform", 1 << 22, 131072, 64, 19),
+                                             # t just above the list path
+                                             ("normal", 1 << 20, 32768, 65, 20)])
 def test_threshold_matches_oracle(kind, N, S, t, seed):
     say("threshold", kind, N, S, t, seed)
-    x = edge_case(kind, N, 5) if kind in ("few_levels", "signed_zeros") else generate(kind, N, seed=5)
+    edge = ("few_levels", "signed_zeros", "with_inf", "with_nan", "all_equal", "negative", "ascending")
+    x = edge_case(kind, N, 5) if kind in edge else generate(kind, N, seed=5)
     v, i = stf.stage_threshold(dev(x), S, t, seed=seed)
     sample = method_ref.sample_indices(N, S, seed=seed)
     rv, ri = method_ref.threshold(x, sample, t)
@@ -180,6 +195,50 @@ def test_fallback_with_huge_tie_group():
     x = generate("adv_noise", 1 << 22, seed=6)
     vals, idx = stf.topk(dev(x), 20000, options={"force_fallback": 1})
     check_topk(x, vals, idx, 20000)
+
+
+def test_interleaved_calls_leave_the_workspace_clean():
+    # Every call must leave the hash set, tickets and histograms zero for the next
+    # one, whatever its sizes: alternate shapes, stage calls and batched calls on one
+    # stream and check each result.
+    xs = {N: generate("normal", N, seed=N % 97) for N in (1 << 22, 1 << 20, 300001)}
+    d = {N: dev(x) for N, x in xs.items()}
+    for rep in range(2):
+        for N, k in ((1 << 22, 32), (1 << 20, 1000), (300001, 64), (1 << 22, 5000)):
+            say("interleaved topk", rep, N, k)
+            v, i = stf.topk(d[N], k, seed=rep)
+            check_topk(xs[N], v, i, k)
+        say("interleaved stage_sample", rep)
+        got = np.sort(host(stf.stage_sample(d[1 << 20], 60000, seed=rep)))
+        np.testing.assert_array_equal(got, method_ref.sample_indices(1 << 20, 60000, seed=rep))
+        say("interleaved batched", rep)
+        xb = generate("uniform", 64 * 65536, seed=rep).reshape(64, 65536)
+        vb, ib = stf.topk_batched(dev(xb), 16, seed=rep)
+        ov, oi = oracle.topk_batched(xb, 16, nthreads=8)
+        np.testing.assert_array_equal(host(ib), oi)
+
+
+def test_out_buffers_and_side_stream():
+    # The call returns once its run-time check is known; the outputs are complete in
+    # stream order.  Reuse caller buffers and run on a non-default stream.
+    import torch
+    x = generate("normal", 1 << 22, seed=31)
+    xd = dev(x)
+    s2 = torch.cuda.Stream()
+    for k in (7, 2000, 70000):
+        say("out= on a side stream", k)
+        out = (torch.empty(k, dtype=torch.float32, device="cuda"), torch.empty(k, dtype=torch.int64, device="cuda"))
+        torch.cuda.current_stream().synchronize()
+        with torch.cuda.stream(s2):
+            for rep in range(3):
+                v, i = stf.topk(xd, k, seed=rep, out=out)
+                assert v.data_ptr() == out[0].data_ptr() and i.data_ptr() == out[1].data_ptr()
+            hv, hi = v.cpu(), i.cpu()  # ordered on s2
+        ov, oi = oracle.topk(x, k, nthreads=8)
+        np.testing.assert_array_equal(hi.numpy(), oi)
+        np.testing.assert_array_equal(hv.numpy().view(np.uint32), ov.view(np.uint32))
+    with pytest.raises(ValueError):
+        stf.topk(xd, 5, out=(torch.empty(4, device="cuda"), torch.empty(5, dtype=torch.int64, device="cuda")))
 
 
 def test_seed_does_not_change_result_and_repeats_are_identical():
