@@ -131,11 +131,128 @@ __device__ __forceinline__ void stage_hits(Stage& st, u32 row, const u64 (&masks
 
 }  // namespace
 
+// One wave-tile's place: its row, the row's threshold and the tile's first float4.
+struct TileAt {
+  u32 row;
+  RowGeom geo;
+  u64 tau;
+  u64 v0;
+  u64 tile;
+};
+
+// The current row of a wavefront, reloaded only when the row changes: the row list
+// and the threshold are read with vector loads (the kernel's atomics on the same
+// control blocks rule out scalar ones), and waiting for them would also wait for the
+// tile loads in flight.
+struct RowCache {
+  u64 lr = ~0ull;
+  u32 row = 0;
+  RowGeom geo{};
+  u64 tau = 0;
+  __device__ __forceinline__ TileAt at(const FilterArgs& a, u64 l, u64 tile, u32 U) {
+    if (l != lr) {
+      lr = l;
+      row = a.rows ? (u32)a.rows[l] : (u32)l;
+      geo = row_geom(a.x, a.ld, a.N, row);
+      tau = a.ctls[row].tau;
+    }
+    TileAt t;
+    t.row = row;
+    t.geo = geo;
+    t.tau = tau;
+    t.v0 = tile * (u64)(U * kWave);
+    t.tile = tile;
+    return t;
+  }
+};
+
+// Issues exactly U dwordx4 loads per lane whatever the tile (a lane past the row's
+// vectors reads an in-bounds address and is masked), so the compiler can wait for an
+// older tile with a partial count while this one is in flight.  `safe` is any
+// readable 16 bytes, for rows too short to hold a float4.
+template <int U, bool NT>
+__device__ __forceinline__ void load_tile(const TileAt& t, f4 (&v)[U], bool (&valid)[U], const f4* safe) {
+  const f4* pv = reinterpret_cast<const f4*>(t.geo.row + t.geo.head);
+  const f4* p0 = t.geo.nvec ? pv : safe;
+  const u32 lane = lane_id();
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const u64 vi = t.v0 + (u64)u * kWave + lane;
+    valid[u] = vi < t.geo.nvec;
+    const f4* p = valid[u] ? pv + vi : p0;
+    v[u] = NT ? __builtin_nontemporal_load(p) : *p;
+  }
+}
+
+// Tests one loaded wave-tile (and, on a row's first tile, the row's scalar edges).
+template <int U>
+__device__ __forceinline__ void test_tile(const FilterArgs& a, Stage& st, const TileAt& t, const f4 (&v)[U],
+                                          const bool (&valid)[U]) {
+  const u32 lane = lane_id();
+  const u32 tk = (u32)(t.tau >> 32);
+  const u32 ti = key_index(t.tau);
+  const float tv = __uint_as_float(bits_of_ord32(tk));
+  bool maybe = false;
+  bool mu[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool m = !(v[u].x < tv) | !(v[u].y < tv) | !(v[u].z < tv) | !(v[u].w < tv);
+    mu[u] = valid[u] & m;
+    maybe |= mu[u];
+  }
+  if (__ballot(maybe)) {
+    // exact test, only for the float4 slots where some lane may hold a hit
+    // (4 ballots each); a sparse tile usually has one such slot
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!__ballot(mu[u])) continue;
+      const u64 vi = t.v0 + (u64)u * kWave + lane;
+      const u32 i0 = (u32)(t.geo.head + 4 * vi);
+      const float c[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      u64 masks[4];
+      bool hit[4];
+      u64 key[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32 o = ord32(__float_as_uint(c[q]));
+        const u32 i = i0 + q;
+        hit[q] = valid[u] && (o > tk || (o == tk && i <= ti));
+        key[q] = ((u64)o << 32) | (u64)(~i);
+        masks[q] = __ballot(hit[q]);
+      }
+      stage_hits<4>(st, t.row, masks, hit, key, a.ctls, a.cand, a.M);
+    }
+  }
+  if (t.tile == 0 && (t.geo.head | t.geo.tail)) {
+    // scalar edge values of this row: lanes [0, head) take the head, then the tail
+    const u64 e = lane;
+    bool in = false;
+    u32 i = 0;
+    if (e < t.geo.head) {
+      in = true;
+      i = (u32)e;
+    } else if (e < t.geo.head + t.geo.tail) {
+      in = true;
+      i = (u32)(t.geo.head + 4 * t.geo.nvec + (e - t.geo.head));
+    }
+    u64 masks[1];
+    bool hit[1];
+    u64 key[1];
+    const u32 o = in ? ord32(__float_as_uint(t.geo.row[i])) : 0u;
+    hit[0] = in && (o > tk || (o == tk && i <= ti));
+    key[0] = ((u64)o << 32) | (u64)(~i);
+    masks[0] = __ballot(hit[0]);
+    stage_hits<1>(st, t.row, masks, hit, key, a.ctls, a.cand, a.M);
+  }
+}
+
 template <int U, bool NT>
 __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   __shared__ u64 s_stage[kWavesPerBlock][kStageCap];
   __shared__ u32 s_last;
-  const u32 wid = threadIdx.x / kWave;
+  // wave-uniform: tile coordinates, row, threshold live in scalar registers, and their
+  // loads wait on the scalar counter, not behind the tile's vector loads
+  const u32 wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const u32 lane = lane_id();
   Stage st{s_stage[wid], 0u, 0u, 0ull};
 
@@ -156,88 +273,44 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   }
   u64 lr = g < gend ? g / a.tiles_per_row : 0;
   u64 tile = g - lr * a.tiles_per_row;
-  for (; g < gend; g += gstep) {
-    if (tile >= a.tiles_per_row) {  // next row (contiguous runs only)
-      tile -= a.tiles_per_row;
-      ++lr;
+  // Software pipeline over two register sets (A, B) used in turn, so that no loaded
+  // register is copied: the next tile's loads are issued before the current tile is
+  // tested, and the wavefront keeps U dwordx4 loads in flight while it stages hits.
+  TileAt ta{}, tb{};
+  f4 va[U], vb[U];
+  bool oka[U], okb[U];
+  RowCache rc;
+  const f4* safe = reinterpret_cast<const f4*>(a.ctls);
+  auto advance = [&](u64& gg, u64& ll, u64& tt) {
+    gg += gstep;
+    tt += gstep;
+    if (tt >= a.tiles_per_row && gg < gend) {  // next row (contiguous runs only)
+      tt -= a.tiles_per_row;
+      ++ll;
     }
-    const u32 row = a.rows ? (u32)a.rows[lr] : (u32)lr;
-    const RowGeom geo = row_geom(a.x, a.ld, a.N, row);
-    const u64 tau = a.ctls[row].tau;
-    const u32 tk = (u32)(tau >> 32);
-    const u32 ti = key_index(tau);
-    const float tv = __uint_as_float(bits_of_ord32(tk));
-    const f4* pv = reinterpret_cast<const f4*>(geo.row + geo.head);
-
-    f4 v[U];
-    bool valid[U];
-    const u64 v0 = tile * (u64)(U * kWave);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const u64 vi = v0 + (u64)u * kWave + lane;
-      valid[u] = vi < geo.nvec;
-      if (valid[u]) {
-        if (NT)
-          v[u] = __builtin_nontemporal_load(pv + vi);
-        else
-          v[u] = pv[vi];
-      } else {
-        v[u] = f4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-    bool maybe = false;
-    bool mu[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool m = !(v[u].x < tv) | !(v[u].y < tv) | !(v[u].z < tv) | !(v[u].w < tv);
-      mu[u] = valid[u] & m;
-      maybe |= mu[u];
-    }
-    if (__ballot(maybe)) {
-      // exact test, only for the float4 slots where some lane may hold a hit
-      // (4 ballots each); a sparse tile usually has one such slot
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (!__ballot(mu[u])) continue;
-        const u64 vi = v0 + (u64)u * kWave + lane;
-        const u32 i0 = (u32)(geo.head + 4 * vi);
-        const float c[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-        u64 masks[4];
-        bool hit[4];
-        u64 key[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32 o = ord32(__float_as_uint(c[q]));
-          const u32 i = i0 + q;
-          hit[q] = valid[u] && (o > tk || (o == tk && i <= ti));
-          key[q] = ((u64)o << 32) | (u64)(~i);
-          masks[q] = __ballot(hit[q]);
-        }
-        stage_hits<4>(st, row, masks, hit, key, a.ctls, a.cand, a.M);
-      }
-    }
-    if (tile == 0 && (geo.head | geo.tail)) {
-      // scalar edge values of this row: lanes [0, head) take the head, then the tail
-      const u64 e = lane;
-      bool in = false;
-      u32 i = 0;
-      if (e < geo.head) {
-        in = true;
-        i = (u32)e;
-      } else if (e < geo.head + geo.tail) {
-        in = true;
-        i = (u32)(geo.head + 4 * geo.nvec + (e - geo.head));
-      }
-      u64 masks[1];
-      bool hit[1];
-      u64 key[1];
-      const u32 o = in ? ord32(__float_as_uint(geo.row[i])) : 0u;
-      hit[0] = in && (o > tk || (o == tk && i <= ti));
-      key[0] = ((u64)o << 32) | (u64)(~i);
-      masks[0] = __ballot(hit[0]);
-      stage_hits<1>(st, row, masks, hit, key, a.ctls, a.cand, a.M);
-    }
-    tile += gstep;
+  };
+  if (g < gend) {
+    ta = rc.at(a, lr, tile, U);
+    load_tile<U, NT>(ta, va, oka, safe);
+  }
+  while (g < gend) {
+    u64 g2 = g, lr2 = lr, tile2 = tile;
+    advance(g2, lr2, tile2);
+    // past the end: reload the current tile (the loads stay unconditional)
+    tb = g2 < gend ? rc.at(a, lr2, tile2, U) : ta;
+    load_tile<U, NT>(tb, vb, okb, safe);
+    test_tile<U>(a, st, ta, va, oka);
+    g = g2;
+    lr = lr2;
+    tile = tile2;
+    if (g >= gend) break;
+    advance(g2, lr2, tile2);
+    ta = g2 < gend ? rc.at(a, lr2, tile2, U) : tb;
+    load_tile<U, NT>(ta, va, oka, safe);
+    test_tile<U>(a, st, tb, vb, okb);
+    g = g2;
+    lr = lr2;
+    tile = tile2;
   }
   // End of the stream: the block's waves reserve their staged keys with one
   // atomic per row they hold (one in the flat case) instead of one per wave.
