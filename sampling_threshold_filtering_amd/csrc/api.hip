@@ -66,7 +66,11 @@ struct Layout {
 // where the previous call cleaned them.
 Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap, u64 rows_cap) {
   Layout L;
-  L.hash_used = pow2_at_least(2 * (S ? S : 1));
+  // hash set of the sample: 16 slots per draw (up to 2^21 slots) keeps probes and
+  // contention on the device-scope CAS low; at least 2 per draw for larger samples
+  const u64 s1 = S ? S : 1;
+  const u64 sparse = 16 * s1 < (1ull << 21) ? 16 * s1 : (1ull << 21);
+  L.hash_used = pow2_at_least(sparse > 2 * s1 ? sparse : 2 * s1);
   L.hash_slots = L.hash_used < hash_cap ? hash_cap : L.hash_used;
   const u64 rows = B < rows_cap ? rows_cap : B;
   L.rows_cap = rows;
@@ -189,8 +193,9 @@ int get_workspace(hipStream_t s, const Need& need, Workspace** out, Layout* out_
     w->seq = 0;
   }
   if (!w->ev0) {
-    HIPCHK(hipEventCreate(&w->ev0), "hipEventCreate");
-    HIPCHK(hipEventCreate(&w->ev1), "hipEventCreate");
+    // timing only: no system-scope fences around the filter
+    HIPCHK(hipEventCreateWithFlags(&w->ev0, hipEventDisableSystemFence), "hipEventCreate");
+    HIPCHK(hipEventCreateWithFlags(&w->ev1, hipEventDisableSystemFence), "hipEventCreate");
   }
   *out = w;
   *out_layout = L;
@@ -460,7 +465,7 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
   const u64 G = batched_sample_blocks(B);
   Layout L;
   Workspace* w = nullptr;
-  rc = get_workspace(s, Need{B, 0, M, 1, G * S}, &w, &L);
+  rc = get_workspace(s, Need{B, 0, M, 1, G * 2 * S}, &w, &L);  // per sampling workgroup: S slots + top-up
   if (rc) return rc;
   RowCtl* ctl = at<RowCtl>(w, L.ctl);
   AttemptRecord* rec = at<AttemptRecord>(w, L.rec);

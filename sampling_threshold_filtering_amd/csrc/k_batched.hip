@@ -33,14 +33,154 @@ __device__ __forceinline__ void write_row_out(u64 key, u64 j, const float* row, 
 }
 }  // namespace
 
+constexpr u32 kDrawMax = 8;  // draws per thread held in registers on the fast path
+
+template <int T>
+__device__ __forceinline__ void wave_top_to_list(u64 (&key)[kDrawMax], u64* list, u32 lane) {
+  u64 top[T];
+  wave_top_lanes<kDrawMax, T>(key, top);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < T; ++i) list[i] = top[i];
+  }
+}
+
+// One row of the fast path; s_bits / s_D / s_fail are clear on entry.
+__device__ __forceinline__ void b_sample_fast_row(const BatchedArgs& a, u32 row, const float* xr, u64* keys,
+                                                  u32* s_bits, u64* s_list, BlockSelectLds* s_sel, u32* s_D,
+                                                  u32* s_fail, u32* s_n, u32 T) {
+  const u32 lane = lane_id(), wid = threadIdx.x / kWave;
+  u32 idx[kDrawMax];
+  bool fr[kDrawMax];
+#pragma unroll
+  for (u32 q = 0; q < kDrawMax; ++q) {
+    const u64 j = (u64)q * blockDim.x + threadIdx.x;
+    fr[q] = false;
+    idx[q] = 0;
+    if (j < a.S) {
+      idx[q] = (u32)sample_draw(j, row, a.attempt, a.seed, a.N);
+      const u32 bit = 1u << (idx[q] & 31u);
+      fr[q] = (atomicOr(&s_bits[idx[q] >> 5], bit) & bit) == 0;
+    }
+  }
+  u32 vb[kDrawMax];
+#pragma unroll
+  for (u32 q = 0; q < kDrawMax; ++q) vb[q] = fr[q] ? reinterpret_cast<const u32*>(xr)[idx[q]] : 0u;  // in flight together
+  u64 key[kDrawMax];
+  u32 nf = 0;
+#pragma unroll
+  for (u32 q = 0; q < kDrawMax; ++q) {
+    key[q] = fr[q] ? make_key(vb[q], idx[q]) : 0ull;  // 0: a repeat (no valid key is 0)
+    const u64 j = (u64)q * blockDim.x + threadIdx.x;
+    if (j < a.S) keys[j] = key[q];
+    nf += (u32)__popcll(__ballot(fr[q]));
+  }
+  if (lane == 0 && nf) atomicAdd(s_D, nf);
+  if (T <= kDrawMax) {
+    // per-lane sort, then six merge levels across lanes: only the T largest move
+    switch (T) {
+      case 1: wave_top_to_list<1>(key, s_list + wid * T, lane); break;
+      case 2: wave_top_to_list<2>(key, s_list + wid * T, lane); break;
+      case 4: wave_top_to_list<4>(key, s_list + wid * T, lane); break;
+      default: wave_top_to_list<8>(key, s_list + wid * T, lane); break;
+    }
+  } else {
+    wave_sort_regs_desc<kDrawMax>(key);
+    if (lane < T) s_list[wid * T + lane] = key[0];  // elements 0..T-1 of the sorted wavefront
+  }
+  __syncthreads();
+  const u32 D0 = *s_D;
+  // top-up by wavefront 0 into keys[S..]
+  if (wid == 0) {
+    u64 D = D0;
+    u64 j0 = a.S;
+    u32 guard = 0;
+    while (D < a.S) {
+      const u32 id2 = (u32)sample_draw(j0 + lane, row, a.attempt, a.seed, a.N);
+      const bool held = (s_bits[id2 >> 5] >> (id2 & 31u)) & 1u;
+      bool repeat = false;
+      for (int d = 1; d < kWave; ++d) {
+        const u32 other = __shfl_up(id2, d, kWave);
+        if ((int)lane >= d && other == id2) repeat = true;
+      }
+      const bool ok2 = !held && !repeat;
+      const u64 m2 = __ballot(ok2);
+      const u64 need = a.S - D;
+      const u32 r = count_below(m2);
+      if (ok2 && r < need) {
+        atomicOr(&s_bits[id2 >> 5], 1u << (id2 & 31u));
+        keys[a.S + (D - D0) + r] = make_key(__float_as_uint(xr[id2]), id2);
+      }
+      const u64 got = (u64)__popcll(m2);
+      D += got < need ? got : need;
+      j0 += kWave;
+      if (++guard > (1u << 22)) {  // bounded: S <= N/2 makes each draw new with prob >= 1/2
+        if (lane == 0) *s_fail = 1;
+        break;
+      }
+    }
+    if (lane == 0) *s_D = (u32)D;
+  }
+  __syncthreads();
+  const bool sample_ok = !*s_fail && *s_D == a.S;
+  const u64 E = sample_ok ? a.S - D0 : 0;
+  block_merge_lists(s_list, kBThreads / kWave, T);  // the row's T largest drawn keys
+  u64 tau = 0;
+  bool ok = sample_ok;
+  if (sample_ok && E > 0) {
+    // top-up keys at or above the t-th largest draw join its t largest
+    const u64 L = s_list[a.t - 1];
+    if (threadIdx.x == 0) *s_n = (u32)a.t;
+    __syncthreads();
+    for (u64 i = threadIdx.x; i < E; i += blockDim.x) {
+      const u64 kk = keys[a.S + i];
+      if (kk >= L) {
+        const u32 pos = atomicAdd(s_n, 1u);
+        if (pos < kBThreads) s_list[pos] = kk;
+      }
+    }
+    __syncthreads();
+    const u32 nc = *s_n;
+    if (nc <= kBThreads) {
+      u32 P = 1;
+      while (P < nc) P <<= 1;
+      for (u32 i = nc + threadIdx.x; i < P; i += blockDim.x) s_list[i] = 0ull;
+      __syncthreads();
+      block_bitonic_desc(s_list, P);
+      tau = s_list[a.t - 1];
+    } else {
+      // many top-up keys: radix select over all key slots (repeats are empty slots)
+      if (threadIdx.x == 0) block_select_start(s_sel, a.S, a.t);
+      __syncthreads();
+      tau = block_select_finish(keys, a.S + E, reinterpret_cast<u64*>(s_bits), kBitmapWords / 2, s_sel, &ok);
+    }
+  } else if (sample_ok) {
+    tau = s_list[a.t - 1];
+  }
+  if (threadIdx.x == 0) {
+    RowCtl* c = &a.ctls[row];
+    c->tau = tau;
+    c->R = 0;
+    c->status = ok && tau != 0 ? 0u : 3u;
+  }
+}
+
 __global__ __launch_bounds__(kBThreads) void b_sample_kernel(BatchedArgs a) {
   __shared__ u32 s_bits[kBitmapWords];
   __shared__ BlockSelectLds s_sel;
+  __shared__ u64 s_list[kBThreads];  // fast path: 16 wavefront lists of T <= 64 keys
   __shared__ u32 s_D;
   __shared__ u32 s_fail;
+  __shared__ u32 s_n;
   const u32 lane = lane_id(), wid = threadIdx.x / kWave;
-  u64* keys = a.scratch + (u64)blockIdx.x * a.S;
+  u64* keys = a.scratch + (u64)blockIdx.x * 2 * a.S;  // S draw slots + the top-up
   const u32 nwords = (u32)((a.N + 31) / 32);
+  // Fast path (t <= 64, S <= 1024 * kDrawMax): every thread holds its draws' keys in
+  // registers; each wavefront sorts them and keeps its T = pow2(t) largest, and the
+  // workgroup merges the sixteen lists (bitonic merge tree in LDS).
+  const bool fast = a.t >= 1 && a.t <= 64 && a.S <= (u64)kBThreads * kDrawMax;
+  u32 T = 1;
+  while (T < a.t) T <<= 1;
   for (u64 li = blockIdx.x; li < a.nrows; li += gridDim.x) {
     const u32 row = a.rows ? (u32)a.rows[li] : (u32)li;
     const float* xr = a.x + (u64)row * a.ld;
@@ -52,6 +192,10 @@ __global__ __launch_bounds__(kBThreads) void b_sample_kernel(BatchedArgs a) {
       s_fail = 0;
     }
     __syncthreads();
+    if (fast) {
+      b_sample_fast_row(a, row, xr, keys, s_bits, s_list, &s_sel, &s_D, &s_fail, &s_n, T);
+      continue;
+    }
     // draws 0..S-1, kDrawILP per thread per round
     const u64 span = (u64)blockDim.x * kDrawILP;
     for (u64 base = 0; base < a.S; base += span) {
@@ -135,26 +279,118 @@ __global__ __launch_bounds__(kBThreads) void b_sample_kernel(BatchedArgs a) {
   }
 }
 
-// LDS: pow2(M) keys (dynamic), so that several rows share a compute unit.
+// Rows of at most kWaveRow candidates: one wavefront each, sorted in registers
+// (64*M keys, M per lane).  Larger rows: the whole workgroup; for k <= kWaveRow its
+// wavefronts sort chunks of kWaveRow in registers and a merge tree in LDS combines
+// their k largest (pow2(M) keys of dynamic LDS at most), else one LDS sort.
 constexpr u32 kRefineThreads = 256;
+constexpr u32 kRefineWaves = kRefineThreads / kWave;
+constexpr u32 kWaveRow = 1024;
+
+namespace {
+// Value bits from a key's order code, except the codes that fold encodings (+-0, NaN).
+__device__ __forceinline__ u32 row_value_bits(u64 key, const float* row, u32 idx) {
+  const u32 o = (u32)(key >> 32);
+  if (o == 0x80000000u || o == 0xFFFFFFFFu) return reinterpret_cast<const u32*>(row)[idx];
+  return bits_of_ord32(o);
+}
+
+__device__ __forceinline__ void write_row_key(u64 key, u64 j, const float* row, u64 N, float* ov, int64_t* oi) {
+  const u32 idx = key_index(key);
+  oi[j] = idx < N ? (int64_t)idx : -1;
+  if (idx < N) reinterpret_cast<u32*>(ov)[j] = row_value_bits(key, row, idx);
+}
+
+template <int M>
+__device__ __forceinline__ void wave_row(const BatchedArgs& a, u32 row, const u64* cand, u32 n) {
+  const u32 lane = lane_id();
+  u64 v[M];
+#pragma unroll
+  for (int r = 0; r < M; ++r) {
+    const u32 i = (u32)r * kWave + lane;
+    v[r] = i < n ? cand[i] : 0ull;
+  }
+  wave_sort_regs_desc<M>(v);
+  const float* xr = a.x + (u64)row * a.ld;
+  float* ov = a.out_vals + (u64)row * a.k;
+  int64_t* oi = a.out_idx + (u64)row * a.k;
+#pragma unroll
+  for (int r = 0; r < M; ++r) {
+    const u32 i = (u32)r * kWave + lane;
+    if (i < a.k) write_row_key(v[r], i, xr, a.N, ov, oi);
+  }
+}
+}  // namespace
+
 __global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a) {
   extern __shared__ u64 s[];
-  for (u64 li = blockIdx.x; li < a.nrows; li += gridDim.x) {
+  __shared__ u32 s_big[kRefineThreads];
+  __shared__ u32 s_nbig;
+  const u32 wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const u64 nwaves = (u64)gridDim.x * kRefineWaves;
+  if (threadIdx.x == 0) s_nbig = 0;
+  __syncthreads();
+  u32 nmine = 0;
+  for (u64 li = (u64)blockIdx.x * kRefineWaves + wid; li < a.nrows; li += nwaves) {
     const u32 row = a.rows ? (u32)a.rows[li] : (u32)li;
     const RowCtl* c = &a.ctls[row];
-    if (c->status != 0) continue;  // uniform: one row per workgroup
+    if (c->status != 0) continue;  // uniform per wavefront
     const u64 R = c->R;
     const u32 n = (u32)(R < a.M ? R : a.M);
     const u64* cand = a.cand + (u64)row * a.M;
-    u32 P = 1;
-    while (P < n) P <<= 1;
-    __syncthreads();
-    for (u32 i = threadIdx.x; i < P; i += blockDim.x) s[i] = i < n ? cand[i] : 0ull;
-    __syncthreads();
-    block_bitonic_desc(s, P);
+    if (n > kWaveRow) {
+      if (lane_id() == 0 && nmine < kRefineThreads / kRefineWaves) s_big[atomicAdd(&s_nbig, 1u)] = row;
+      ++nmine;
+      continue;
+    }
+    if (n <= 64) wave_row<1>(a, row, cand, n);
+    else if (n <= 128) wave_row<2>(a, row, cand, n);
+    else if (n <= 256) wave_row<4>(a, row, cand, n);
+    else if (n <= 512) wave_row<8>(a, row, cand, n);
+    else wave_row<16>(a, row, cand, n);
+  }
+  __syncthreads();
+  const u32 nbig = s_nbig;
+  u32 T = 1;
+  while (T < a.k) T <<= 1;
+  for (u32 q = 0; q < nbig; ++q) {
+    const u32 row = s_big[q];
+    const RowCtl* c = &a.ctls[row];
+    const u64 R = c->R;
+    const u32 n = (u32)(R < a.M ? R : a.M);
+    const u64* cand = a.cand + (u64)row * a.M;
     const float* xr = a.x + (u64)row * a.ld;
+    __syncthreads();
+    if (T <= kWaveRow) {
+      // chunks of kWaveRow candidates sorted by the wavefronts in registers, each
+      // keeping its T largest; the lists (at most pow2(M) keys) are then merged
+      const u32 nch = (n + kWaveRow - 1) / kWaveRow;
+      for (u32 ch = wid; ch < nch; ch += kRefineWaves) {
+        const u32 lane = lane_id();
+        u64 v[kWaveRow / kWave];
+#pragma unroll
+        for (u32 r = 0; r < kWaveRow / kWave; ++r) {
+          const u32 i = ch * kWaveRow + r * kWave + lane;
+          v[r] = i < n ? cand[i] : 0ull;
+        }
+        wave_sort_regs_desc<kWaveRow / kWave>(v);
+#pragma unroll
+        for (u32 r = 0; r < kWaveRow / kWave; ++r) {
+          const u32 e = r * kWave + lane;  // element e of the sorted chunk
+          if (e < T) s[ch * T + e] = v[r];
+        }
+      }
+      __syncthreads();
+      block_merge_lists(s, nch, T);
+    } else {
+      u32 P = 1;
+      while (P < n) P <<= 1;
+      for (u32 i = threadIdx.x; i < P; i += blockDim.x) s[i] = i < n ? cand[i] : 0ull;
+      __syncthreads();
+      block_bitonic_desc(s, P);
+    }
     for (u32 j = threadIdx.x; j < a.k; j += blockDim.x)
-      write_row_out(s[j], j, xr, a.N, a.out_vals + (u64)row * a.k, a.out_idx + (u64)row * a.k);
+      write_row_key(s[j], j, xr, a.N, a.out_vals + (u64)row * a.k, a.out_idx + (u64)row * a.k);
   }
 }
 
@@ -193,7 +429,15 @@ hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s) {
 hipError_t launch_b_refine(const BatchedArgs& a, hipStream_t s) {
   u32 P = 1;
   while (P < a.M) P <<= 1;  // M <= kSmallSort: at most 64 KB
-  b_refine_kernel<<<row_grid(a.nrows, 8), kRefineThreads, (size_t)P * sizeof(u64), s>>>(a);
+  // one wavefront per row; each workgroup meets at most kRefineThreads / kRefineWaves
+  // rows per wavefront, which bounds its list of rows for the LDS path
+  u64 g = (a.nrows + kRefineWaves - 1) / kRefineWaves;
+  const u64 gmin = (a.nrows + (u64)kRefineThreads - 1) / kRefineThreads;
+  const u64 gmax = 8ull * device_cu_count();
+  if (g > gmax) g = gmax;
+  if (g < gmin) g = gmin;
+  if (g < 1) g = 1;
+  b_refine_kernel<<<(u32)g, kRefineThreads, (size_t)P * sizeof(u64), s>>>(a);
   return hipGetLastError();
 }
 

@@ -256,23 +256,42 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   const u32 lane = lane_id();
   Stage st{s_stage[wid], 0u, 0u, 0ull};
 
-  // One row: wavefronts stride over the tiles.  Several rows: each wavefront takes a
-  // contiguous run of tiles, so it changes rows (and flushes its stage) rarely.
+  // Tile order: chunks of `run` consecutive tiles, chunk c to wavefront c mod nwaves
+  // (block-cyclic).  One row: run = 1, the wavefronts sweep the row together.
+  // Several rows: short runs keep the waves' concurrent reads close together while a
+  // wavefront changes rows (and flushes its stage) only between chunks.
   const u64 nwaves = (u64)gridDim.x * kWavesPerBlock;
   const u64 gw = (u64)blockIdx.x * kWavesPerBlock + wid;
-  u64 g, gend, gstep;
-  if (a.nrows == 1) {
-    g = gw;
-    gend = a.total_tiles;
-    gstep = nwaves;
-  } else {
-    const u64 per = (a.total_tiles + nwaves - 1) / nwaves;
-    g = gw * per;
-    gend = g + per < a.total_tiles ? g + per : a.total_tiles;
-    gstep = 1;
-  }
-  u64 lr = g < gend ? g / a.tiles_per_row : 0;
-  u64 tile = g - lr * a.tiles_per_row;
+  const u64 run = a.run, gend = a.total_tiles, tpr = a.tiles_per_row;
+  struct Cursor {
+    u64 g, lr, tile, in, chunk;
+  };
+  auto place = [&](Cursor& c) {
+    if (a.nrows == 1) {
+      c.lr = 0;
+      c.tile = c.g;
+    } else {
+      c.lr = c.g / tpr;
+      c.tile = c.g - c.lr * tpr;
+    }
+  };
+  auto advance = [&](Cursor& c) {
+    if (c.in + 1 < run && c.g + 1 < gend) {
+      ++c.in;
+      ++c.g;
+      if (++c.tile == tpr) {
+        c.tile = 0;
+        ++c.lr;
+      }
+    } else {
+      c.in = 0;
+      c.chunk += nwaves;
+      c.g = c.chunk * run;
+      if (c.g < gend) place(c);
+    }
+  };
+  Cursor cur{gw * run, 0, 0, 0, gw};
+  if (cur.g < gend) place(cur);
   // Software pipeline over two register sets (A, B) used in turn, so that no loaded
   // register is copied: the next tile's loads are issued before the current tile is
   // tested, and the wavefront keeps U dwordx4 loads in flight while it stages hits.
@@ -281,36 +300,24 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   bool oka[U], okb[U];
   RowCache rc;
   const f4* safe = reinterpret_cast<const f4*>(a.ctls);
-  auto advance = [&](u64& gg, u64& ll, u64& tt) {
-    gg += gstep;
-    tt += gstep;
-    if (tt >= a.tiles_per_row && gg < gend) {  // next row (contiguous runs only)
-      tt -= a.tiles_per_row;
-      ++ll;
-    }
-  };
-  if (g < gend) {
-    ta = rc.at(a, lr, tile, U);
+  if (cur.g < gend) {
+    ta = rc.at(a, cur.lr, cur.tile, U);
     load_tile<U, NT>(ta, va, oka, safe);
   }
-  while (g < gend) {
-    u64 g2 = g, lr2 = lr, tile2 = tile;
-    advance(g2, lr2, tile2);
+  while (cur.g < gend) {
+    Cursor nx = cur;
+    advance(nx);
     // past the end: reload the current tile (the loads stay unconditional)
-    tb = g2 < gend ? rc.at(a, lr2, tile2, U) : ta;
+    tb = nx.g < gend ? rc.at(a, nx.lr, nx.tile, U) : ta;
     load_tile<U, NT>(tb, vb, okb, safe);
     test_tile<U>(a, st, ta, va, oka);
-    g = g2;
-    lr = lr2;
-    tile = tile2;
-    if (g >= gend) break;
-    advance(g2, lr2, tile2);
-    ta = g2 < gend ? rc.at(a, lr2, tile2, U) : tb;
+    cur = nx;
+    if (cur.g >= gend) break;
+    advance(nx);
+    ta = nx.g < gend ? rc.at(a, nx.lr, nx.tile, U) : tb;
     load_tile<U, NT>(ta, va, oka, safe);
     test_tile<U>(a, st, tb, vb, okb);
-    g = g2;
-    lr = lr2;
-    tile = tile2;
+    cur = nx;
   }
   // End of the stream: the block's waves reserve their staged keys with one
   // atomic per row they hold (one in the flat case) instead of one per wave.
@@ -396,6 +403,7 @@ hipError_t launch_filter(const FilterArgs& a0, u32 grid, hipStream_t s) {
   a.tiles_per_row = (max_vec + vec_per_tile - 1) / vec_per_tile;
   if (a.tiles_per_row == 0) a.tiles_per_row = 1;
   a.total_tiles = a.tiles_per_row * a.nrows;
+  a.run = a.nrows == 1 ? 1 : kFilterRun;
   u64 need = (a.total_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
   if (need < 1) need = 1;
   if (grid == 0) grid = kFilterBlocksPerCU * device_cu_count();

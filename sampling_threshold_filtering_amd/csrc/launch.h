@@ -8,6 +8,7 @@ namespace profk {
 constexpr u32 kSmallSort = 8192;  // keys sorted by one workgroup in LDS (64 KB)
 constexpr u32 kTickets = 64;      // u32 tickets / counters in the workspace; each user leaves its own zero
 constexpr u32 kFilterBlocksPerCU = 2;  // persistent filter grid: 2 blocks x 4 waves per CU
+constexpr u64 kFilterRun = 64;         // consecutive tiles per chunk when there are several rows
 
 // Compute units of the current device (cached per device).
 inline u32 device_cu_count() {
@@ -37,6 +38,7 @@ struct FilterArgs {
   SelState* sels;      // per row refinement selection to arm, or nullptr
   u64 tiles_per_row;   // set by launch_filter
   u64 total_tiles;
+  u64 run;             // tiles per chunk of the block-cyclic order (set by launch_filter)
 };
 
 hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u32* tickets, u32 nrows,

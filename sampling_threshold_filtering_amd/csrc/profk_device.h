@@ -114,60 +114,145 @@ __device__ __forceinline__ u32 wave_reserve32(u32* counter, bool pred) {
   return base + count_below(m);
 }
 
-// Descending bitonic sort of one key per lane across the wavefront, in registers.
-__device__ __forceinline__ u64 wave_sort_desc(u64 v) {
-  const u32 lane = lane_id();
-#pragma unroll
-  for (u32 k = 2; k <= (u32)kWave; k <<= 1) {
-#pragma unroll
-    for (u32 j = k >> 1; j > 0; j >>= 1) {
-      const u64 p = __shfl_xor(v, (int)j);
-      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
-      v = keep_max ? (v > p ? v : p) : (v < p ? v : p);
-    }
+// Exchange with lane ^ J.  Strides 1, 2, 4, 8 use DPP lane moves (plain ALU
+// operations); 16 and 32 go through the LDS crossbar (ds_bpermute).
+template <u32 J>
+__device__ __forceinline__ u32 lane_xor_u32(u32 v, u32 lane) {
+  if constexpr (J == 1) {  // quad_perm [1,0,3,2]
+    return (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  } else if constexpr (J == 2) {  // quad_perm [2,3,0,1]
+    return (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  } else if constexpr (J == 4 || J == 8) {  // within rows of 16: row_shl:J where bit J is clear, row_shr:J else
+    const u32 up = (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x100 | J, 0xF, 0xF, true);
+    const u32 dn = (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x110 | J, 0xF, 0xF, true);
+    return (lane & J) ? dn : up;
+  } else {
+    return (u32)__shfl_xor((int)v, (int)J);
   }
-  return v;
 }
 
-// Descending bitonic sort of 64*M keys held M per lane: element i = r*64 + lane is
-// v[r] of that lane.  Strides below 64 exchange across lanes, larger ones across
-// registers of the same lane; every decision is known at compile time except the lane.
+template <u32 J>
+__device__ __forceinline__ u64 lane_xor(u64 v, u32 lane) {
+  const u32 lo = lane_xor_u32<J>((u32)v, lane);
+  const u32 hi = lane_xor_u32<J>((u32)(v >> 32), lane);
+  return ((u64)hi << 32) | lo;
+}
+
+// One stage (K, J) of a descending bitonic sort of 64*M keys held M per lane
+// (element i = r*64 + lane is v[r]), then the stages (K, J/2) ... (K, 1).  All
+// strides are template constants, so every exchange is resolved at compile time.
+template <int M, u32 K, u32 J>
+__device__ __forceinline__ void bitonic_stage_regs(u64 (&v)[M], u32 lane) {
+  if constexpr (J < (u32)kWave) {
+    // all M exchanges first, then the compare-exchanges
+    u64 p[M];
+#pragma unroll
+    for (int r = 0; r < M; ++r) p[r] = lane_xor<J>(v[r], lane);
+    __builtin_amdgcn_sched_barrier(0);  // keep the exchanges ahead of their uses
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+      const u32 i = (u32)r * kWave + lane;
+      const bool keep_max = ((i & J) == 0) == ((i & K) == 0);
+      if ((v[r] < p[r]) == keep_max) v[r] = p[r];  // take the partner's key
+    }
+  } else {
+    constexpr u32 rj = J / kWave;
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+      if ((r & rj) == 0) {
+        const int r2 = r | (int)rj;
+        const bool up = (((u32)r * kWave) & K) == 0;  // lower element's block direction
+        const u64 x0 = v[r], x1 = v[r2];
+        const u64 hi = x0 > x1 ? x0 : x1, lo = x0 > x1 ? x1 : x0;
+        v[r] = up ? hi : lo;
+        v[r2] = up ? lo : hi;
+      }
+    }
+  }
+  if constexpr (J > 1) bitonic_stage_regs<M, K, J / 2>(v, lane);
+}
+
+template <int M, u32 K>
+__device__ __forceinline__ void bitonic_levels_regs(u64 (&v)[M], u32 lane) {
+  bitonic_stage_regs<M, K, K / 2>(v, lane);
+  if constexpr (K < 64u * (u32)M) bitonic_levels_regs<M, K * 2>(v, lane);
+}
+
+// Descending bitonic sort of 64*M keys held M per lane: afterwards element
+// i = r*64 + lane (v[r] of that lane) is the i-th largest.
 template <int M>
 __device__ __forceinline__ void wave_sort_regs_desc(u64 (&v)[M]) {
-  const u32 lane = lane_id();
+  bitonic_levels_regs<M, 2>(v, lane_id());
+}
+
+// Descending bitonic sort of one key per lane across the wavefront, in registers.
+__device__ __forceinline__ u64 wave_sort_desc(u64 v) {
+  u64 a[1] = {v};
+  wave_sort_regs_desc<1>(a);
+  return a[0];
+}
+
+// Descending bitonic sort of the M keys of one lane (registers only).
+template <int M>
+__device__ __forceinline__ void lane_sort_desc(u64 (&v)[M]) {
 #pragma unroll
-  for (u32 k = 2; k <= 64u * M; k <<= 1) {
+  for (int k = 2; k <= M; k <<= 1) {
 #pragma unroll
-    for (u32 j = k >> 1; j > 0; j >>= 1) {
-      if (j < (u32)kWave) {
-        // all M exchanges first (independent LDS-crossbar operations in flight),
-        // then the compare-exchanges
-        u64 p[M];
+    for (int j = k >> 1; j > 0; j >>= 1) {
 #pragma unroll
-        for (int r = 0; r < M; ++r) p[r] = __shfl_xor(v[r], (int)j);
-        __builtin_amdgcn_sched_barrier(0);  // keep the exchanges ahead of their uses
-#pragma unroll
-        for (int r = 0; r < M; ++r) {
-          const u32 i = (u32)r * kWave + lane;
-          const bool keep_max = ((i & j) == 0) == ((i & k) == 0);
-          if ((v[r] < p[r]) == keep_max) v[r] = p[r];  // take the partner's key
-        }
-      } else {
-        const u32 rj = j / kWave;
-#pragma unroll
-        for (int r = 0; r < M; ++r) {
-          if ((r & rj) == 0) {
-            const int r2 = r | (int)rj;
-            const bool up = (((u32)r * kWave) & k) == 0;  // lower element's block direction
-            const u64 x0 = v[r], x1 = v[r2];
-            const u64 hi = x0 > x1 ? x0 : x1, lo = x0 > x1 ? x1 : x0;
-            v[r] = up ? hi : lo;
-            v[r2] = up ? lo : hi;
-          }
+      for (int i = 0; i < M; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          const bool desc = (i & k) == 0;
+          const u64 a = v[i], b = v[l];
+          const u64 hi = a > b ? a : b, lo = a > b ? b : a;
+          v[i] = desc ? hi : lo;
+          v[l] = desc ? lo : hi;
         }
       }
     }
   }
+}
+
+// Merge step of the lane lists: with v this lane's T largest (descending) and the
+// partner lane ^ D holding another such list, leaves the T largest of both, sorted,
+// in v (max(A[i], B[T-1-i]) is their bitonic top half; log2 T half-cleaners sort it).
+template <int T, u32 D>
+__device__ __forceinline__ void lane_merge_top(u64 (&v)[T], u32 lane) {
+  u64 p[T];
+#pragma unroll
+  for (int i = 0; i < T; ++i) p[i] = lane_xor<D>(v[T - 1 - i], lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < T; ++i) v[i] = v[i] > p[i] ? v[i] : p[i];
+#pragma unroll
+  for (int h = T >> 1; h > 0; h >>= 1) {
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      if ((i & h) == 0) {
+        const u64 a = v[i], b = v[i + h];
+        v[i] = a > b ? a : b;
+        v[i + h] = a > b ? b : a;
+      }
+    }
+  }
+}
+
+// The T largest of the wavefront's 64*M keys (M per lane, T <= M), sorted
+// descending, in top[0..T) of every lane.
+template <int M, int T>
+__device__ __forceinline__ void wave_top_lanes(u64 (&v)[M], u64 (&top)[T]) {
+  static_assert(T <= M, "lists longer than the keys per lane");
+  const u32 lane = lane_id();
+  lane_sort_desc<M>(v);
+#pragma unroll
+  for (int i = 0; i < T; ++i) top[i] = v[i];
+  lane_merge_top<T, 1>(top, lane);
+  lane_merge_top<T, 2>(top, lane);
+  lane_merge_top<T, 4>(top, lane);
+  lane_merge_top<T, 8>(top, lane);
+  lane_merge_top<T, 16>(top, lane);
+  lane_merge_top<T, 32>(top, lane);
 }
 
 // Lanes with equal 8-bit digit (among those with active set): mask of those lanes.

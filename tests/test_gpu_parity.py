@@ -275,6 +275,8 @@ def check_batched(x2d, vals, idx, k):
     ("normal", 5, 8192, 8192, {}),                     # k = N at the short-row limit
     ("normal", 7, 1, 1, {}),
     ("normal", 2, 1 << 21, 300, {}),                   # rows longer than the per-row kernels take
+    ("normal", 16, 1 << 20, 3000, {"s_override": 32768}),  # radix-select sampler (t > 64), LDS row sorts
+    ("with_nan", 24, 100000, 40, {"s_override": 8000}),    # many repeats and a long top-up; NaN at the top
 ])
 def test_batched_shapes(kind, B, N, k, opts):
     say("batched", kind, B, N, k, opts)
