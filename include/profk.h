@@ -66,7 +66,19 @@ typedef struct profk_options {
   int32_t use_max_attempts; /* nonzero: max_attempts is taken as given (0 = straight to the exact path) */
   int32_t force_fallback; /* nonzero: skip the sampled attempts, run the exact full selection */
   int32_t timing;         /* nonzero: time the filter kernel with HIP events (stats.filter_ms) */
+  int32_t param_mode;     /* PROFK_PARAMS_EXACT (0): Theorem 4's (t*, M*), memoised (P1 §4 Eq. 7);
+                             PROFK_PARAMS_FAST: the closed-form surrogates of P1 Algorithm 1 (Eq. 10-12),
+                             elementary arithmetic only, computed on every call and not memoised */
+  int32_t s_rule;         /* PROFK_S_RULE_CUBE_ROOT (0): S = c (k (N-k))^(1/3) clamped to [s_min, s_max]
+                             (P2 Theorem 5); PROFK_S_RULE_COST_MODEL: P1 Algorithm 1 lines 1-4 (the cost
+                             model of Proposition 7 with the calibrated ratio r(k); defaults s_min = 2^14,
+                             s_max = 2^18) */
 } profk_options;
+
+#define PROFK_PARAMS_EXACT 0
+#define PROFK_PARAMS_FAST 1
+#define PROFK_S_RULE_CUBE_ROOT 0
+#define PROFK_S_RULE_COST_MODEL 1
 
 /* The parameter choice for one (N, k, eps) (P1 §4 Theorem 4; P2 §4). */
 typedef struct profk_params {
@@ -77,13 +89,14 @@ typedef struct profk_params {
   double z;            /* z_A + z_B (P2 Algorithm 1) */
   double S_raw;        /* c (k (N-k))^(1/3) before the clamp */
   int64_t S;           /* sample size used */
-  int64_t t_star;      /* P1 Eq. 7 */
-  int64_t M_star;      /* P1 Eq. 7 */
+  int64_t t_star;      /* P1 Eq. 7 (-1 in PROFK_PARAMS_FAST mode: not computed) */
+  int64_t M_star;      /* P1 Eq. 7 (-1 in PROFK_PARAMS_FAST mode) */
   double M_cf;         /* P2 Corollary 4, Eq. 12 */
   int64_t t_eq6;       /* P2 Eq. 6 (reported only) */
-  int64_t t, M;        /* operating pair: t = t*, M = max(M*, ceil(M_cf)) unless forced */
-  double p_recall;     /* Pr(R < k) at (t, M), P1 Eq. 5 */
-  double p_overflow;   /* Pr(R > M) at (t, M), P1 Eq. 6 */
+  int64_t t, M;        /* operating pair: t = t*, M = max(M*, ceil(M_cf)) unless forced; in
+                          PROFK_PARAMS_FAST mode the Algorithm 1 pair (t, M) */
+  double p_recall;     /* Pr(R < k) at (t, M), P1 Eq. 5 (-1 in PROFK_PARAMS_FAST mode: not computed) */
+  double p_overflow;   /* Pr(R > M) at (t, M), P1 Eq. 6 (-1 in PROFK_PARAMS_FAST mode) */
   double E_R, Var_R;   /* P2 Lemma 1, Eq. 2 */
   int32_t direct_exact; /* 1: sampling cannot pay off here; the call runs the exact full selection */
   int32_t reserved;
@@ -141,7 +154,10 @@ int profk_topk_batched_ex(const float* x, int64_t B, int64_t N, int64_t ld_x, in
  * profk_solve: host-only parameter choice (P1 §4 Theorem 4 / Eq. 5-7; the
  * S rule and closed forms of P2 §4 Theorem 5, Corollary 4, Algorithm 1).
  * Memoised per (N, k, eps, options) (P1 §4 "Fast Approximate Parameter
- * Computation": parameters are cached per configuration).  No GPU needed.
+ * Computation": parameters are cached per configuration).  With
+ * opt->param_mode = PROFK_PARAMS_FAST the pair (t, M) comes from the closed
+ * forms of P1 Algorithm 1 instead, in a few microseconds, without the memo.
+ * No GPU needed.
  */
 int profk_solve(int64_t N, int64_t k, double eps, const profk_options* opt, profk_params* out);
 

@@ -151,6 +151,35 @@ def solve(N: int, k: int, eps: float, S: int | None = None, s_min: int = S_MIN_D
     return RefParams(N, k, eps, raw, S, z_a, z, ts, ms, m_cf, t6, t, M, p_rec, p_ovf, e_r, var_r)
 
 
+def inv_cost_ratio(k: int, a: float = 0.594, b: float = 4.29) -> float:
+    """1/r(k) of the cost model (P1 App. E.1): a log2 k - b for k > 2^7, and 0
+    (r infinite) below.  The page prints a = 0.59, b = 4.3; the unrounded
+    a = 0.594, b = 4.29 are the reading, because only they reproduce the S
+    column of P1 App. B Table 3 (all 21 rows)."""
+    if k <= 128:
+        return 0.0
+    return max(0.0, a * math.log2(k) - b)
+
+
+def s_rule_cost_model(N: int, k: int, eps: float, s_min: int = 1 << 14, s_max: int = 1 << 18,
+                      a: float = 0.594, b: float = 4.29) -> int:
+    """P1 Algorithm 1 lines 1-4 (Proposition 7): S1 = (z/r)^(2/3) (kN)^(1/3),
+    S2 = (kappa N / r)^(1/2), kappa = z^2 + 1/2, z = Phi^-1(1 - eps/2);
+    S = clip(floor(max(S1, S2)), S_min, S_max), and S_min when r is infinite or
+    k/N > 2^-10.  Then at most N/128 and at most N, as for the default rule."""
+    z = z_upper(eps / 2.0)
+    kappa = z * z + 0.5
+    inv_r = inv_cost_ratio(k, a, b)
+    if inv_r <= 0.0 or k / N > 2.0 ** -10:
+        S = s_min
+    else:
+        s1 = (z * inv_r) ** (2.0 / 3.0) * (k * N) ** (1.0 / 3.0)
+        s2 = math.sqrt(kappa * N * inv_r)
+        S = max(s_min, min(s_max, int(math.floor(max(s1, s2)))))
+    S = min(S, max(1, N // 128))
+    return min(S, N)
+
+
 def surrogate_params(N: int, k: int, S: int, eps: float) -> tuple[int, int]:
     """P1 Algorithm 1 / App. B closed forms (Eq. 10, 11, 12) for a given S: (t, M).
     Phi^-1 comes from scipy here (the page uses a rational approximation)."""

@@ -47,7 +47,15 @@ class Options(ctypes.Structure):
         ("use_max_attempts", ctypes.c_int32),
         ("force_fallback", ctypes.c_int32),
         ("timing", ctypes.c_int32),
+        ("param_mode", ctypes.c_int32),
+        ("s_rule", ctypes.c_int32),
     ]
+
+
+PARAMS_EXACT = 0
+PARAMS_FAST = 1
+S_RULE_CUBE_ROOT = 0
+S_RULE_COST_MODEL = 1
 
 
 class Params(ctypes.Structure):

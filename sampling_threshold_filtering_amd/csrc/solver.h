@@ -14,6 +14,10 @@ double hyp_upper_tail(int64_t j, int64_t N, int64_t K, int64_t S);
 int64_t hyp_quantile(double p, int64_t N, int64_t K, int64_t S);
 // z with Pr(Z > z) = q for a standard normal Z.
 double normal_upper_quantile(double q);
+// Phi^-1(p) by Acklam's rational approximation.
+double acklam_inv_phi(double p);
+// 1 / r(k) of the cost model (0 when r is infinite).
+double cost_ratio_inverse(int64_t k);
 
 int solve(int64_t N, int64_t k, double eps, const profk_options* opt, profk_params* out);
 int solve_memo(int64_t N, int64_t k, double eps, const profk_options* opt, profk_params* out);

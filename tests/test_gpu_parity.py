@@ -133,6 +133,22 @@ def test_topk_matches_oracle(kind, N, k, opts):
     print("[case] refine_multipass", st["refine_multipass"], flush=True)
 
 
+@pytest.mark.parametrize("kind,N,k,mode,rule", [
+    ("normal", 1 << 22, 32, 1, 0), ("uniform", 1 << 22, 2048, 1, 1), ("pareto", 1 << 24, 16384, 1, 1),
+    ("normal", 1 << 24, 131072, 0, 1), ("normal", 1 << 23, 300, 1, 0),
+])
+def test_fast_parameters_and_cost_model_rule_stay_exact(kind, N, k, mode, rule):
+    """The closed-form surrogates and the cost-model S rule (P1 Algorithm 1) only change
+    (S, t, M); the output is still the exact top-k."""
+    say("topk fast params", kind, N, k, mode, rule)
+    x = generate(kind, N, seed=23)
+    o = stf.make_options(param_mode=mode, s_rule=rule)
+    p = stf.solve(N, k, 1e-3, options=o)
+    vals, idx, st = stf.topk(dev(x), k, eps=1e-3, seed=4, options=o, stats=True)
+    check_topk(x, vals, idx, k)
+    assert (st["S"], st["t"], st["M"]) == (p["S"], p["t"], p["M"])
+
+
 @pytest.mark.parametrize("N,k,offset", [(1, 1, 0), (5, 3, 1), (1000, 1000, 2), (4096, 17, 3), (100003, 5000, 1)])
 def test_exact_path_small_and_misaligned(N, k, offset):
     say("exact path", N, k, offset)

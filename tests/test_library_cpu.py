@@ -115,3 +115,60 @@ def test_product_package_does_not_reference_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "topk_oracle" not in text and "liboracle" not in text, f
+
+
+def test_fast_mode_matches_table3_and_the_oracle(golden_dir):
+    """PROFK_PARAMS_FAST: P1 Algorithm 1's (t, M) for the printed S equal Table 3's
+    surrogate columns and the oracle's closed forms."""
+    from tests.test_oracle_solver import load_table3
+    for r in load_table3(golden_dir):
+        o = stf.make_options(param_mode=stf.PARAMS_FAST, s_override=r["S"])
+        p = stf.solve(r["N"], r["k"], 1e-3, options=o)
+        assert (p["t"], p["M"]) == (r["t_fast"], r["M_fast"]), r
+        assert (p["t"], p["M"]) == solver_ref.surrogate_params(r["N"], r["k"], r["S"], 1e-3)
+        assert p["t_star"] == -1 and p["M_star"] == -1 and p["p_recall"] == -1.0
+
+
+def test_cost_model_rule_matches_table3_sample_sizes(golden_dir):
+    from tests.test_oracle_solver import load_table3
+    for mode in (stf.PARAMS_EXACT, stf.PARAMS_FAST):
+        for r in load_table3(golden_dir):
+            o = stf.make_options(param_mode=mode, s_rule=stf.S_RULE_COST_MODEL)
+            p = stf.solve(r["N"], r["k"], 1e-3, options=o)
+            assert p["S"] == r["S"] == solver_ref.s_rule_cost_model(r["N"], r["k"], 1e-3), r
+            if mode == stf.PARAMS_EXACT:
+                assert (p["t_star"], p["M_star"]) == (r["t_star"], r["M_star"]), r
+
+
+def test_fast_mode_quantile_is_acklam_accurate():
+    """The rational approximation of Phi^-1 (relative error below 1.15e-9) against
+    scipy's quantile, over budgets that reach both of its branches."""
+    from scipy.stats import norm
+    o = stf.make_options(param_mode=stf.PARAMS_FAST)
+    for eps in [10.0 ** -e for e in range(1, 15)] + [0.03, 0.0485, 0.049, 0.2, 0.5, 0.9, 0.99]:
+        z = stf.solve(1 << 24, 64, eps, options=o)["z_a"]
+        ref = float(norm.isf(eps / 2.0))
+        assert abs(z - ref) <= 1.2e-9 * abs(ref) + 1e-15, (eps, z, ref)
+
+
+@pytest.mark.parametrize("N,k,eps", WORKLOADS)
+def test_fast_mode_matches_oracle_surrogates_at_the_workloads(N, k, eps):
+    o = stf.make_options(param_mode=stf.PARAMS_FAST)
+    p = stf.solve(N, k, eps, options=o)
+    ref = solver_ref.solve(N, k, eps)
+    assert p["S"] == ref.S
+    t, M = solver_ref.surrogate_params(N, k, ref.S, eps)
+    assert p["t"] == min(t, ref.S)
+    assert p["M"] == min(max(M, k), N)
+
+
+def test_fast_mode_is_microseconds_and_not_memoised():
+    import time
+    o = stf.make_options(param_mode=stf.PARAMS_FAST)
+    stf.solve(1 << 30, 1 << 15, 1e-3, options=o)
+    n = 2000
+    t0 = time.perf_counter()
+    for i in range(n):
+        stf.solve((1 << 30) - i, 1 << 15, 1e-3, options=o)  # a new configuration every call
+    per_call = (time.perf_counter() - t0) / n
+    assert per_call < 200e-6, per_call  # Python marshalling included
