@@ -136,6 +136,31 @@ int profk_topk_ex(const float* x, int64_t N, int64_t k, double eps, uint64_t see
                   int64_t* out_idx, void* stream, const profk_options* opt, profk_stats* st);
 
 /*
+ * Approximate mode (P1 App. D "Cost of the Run-Time Check"; App. E.2): one
+ * sampled attempt with no host read of the count.  Every step is enqueued on
+ * `stream` and the call returns without waiting, so it can be captured in a
+ * HIP graph once a first call has sized the workspace (a call that must grow
+ * the workspace allocates and is not capturable).  The output is the exact
+ * top-k of the candidates the attempt kept: it is the exact top-k whenever
+ * k <= R <= M held, which fails with probability at most eps.  The outcome of
+ * the check is written, in stream order, to *info (device memory).
+ *   info     device pointer to one profk_approx_info, or NULL
+ *   other arguments as profk_topk_ex (opt may be NULL; max_attempts and
+ *   timing are ignored)
+ */
+typedef struct profk_approx_info {
+  int64_t R;          /* exact filter count of the attempt (N when the exact selection ran) */
+  int64_t M;          /* buffer capacity of the attempt */
+  int32_t status;     /* 0: k <= R <= M held, the output is the exact top-k;
+                         1: R < k: positions R..k-1 hold index -1 and value -inf;
+                         2: R > M: the output is the top-k of the M kept candidates */
+  int32_t exact_path; /* 1: the configuration went to the exact full selection (status 0) */
+} profk_approx_info;
+
+int profk_topk_approx(const float* x, int64_t N, int64_t k, double eps, uint64_t seed, float* out_vals,
+                      int64_t* out_idx, profk_approx_info* info, void* stream, const profk_options* opt);
+
+/*
  * profk_topk_batched: row-wise exact top-k of B rows (P1 §3: the procedure
  * is applied to each batch element; App. C: per-row threshold, buffer and
  * counter).  Row r is x[r*ld_x .. r*ld_x + N).  The budget is split eps/B

@@ -30,7 +30,8 @@ PROFK_EINTERNAL = -5
 
 STATS_ATTEMPTS = 8
 
-EXPORTED = ("profk_topk", "profk_topk_ex", "profk_topk_batched", "profk_topk_batched_ex", "profk_solve",
+EXPORTED = ("profk_topk", "profk_topk_ex", "profk_topk_approx", "profk_topk_batched", "profk_topk_batched_ex",
+            "profk_solve",
             "profk_stage_sample", "profk_stage_threshold", "profk_stage_filter", "profk_strerror",
             "profk_release")
 
@@ -103,6 +104,7 @@ def load_library():
     lib.profk_topk.argtypes = [vp, i64, i64, f64, u64, vp, vp, vp]
     lib.profk_topk_ex.argtypes = [vp, i64, i64, f64, u64, vp, vp, vp, ctypes.POINTER(Options),
                                   ctypes.POINTER(Stats)]
+    lib.profk_topk_approx.argtypes = [vp, i64, i64, f64, u64, vp, vp, vp, vp, ctypes.POINTER(Options)]
     lib.profk_topk_batched.argtypes = [vp, i64, i64, i64, i64, f64, u64, vp, vp, vp]
     lib.profk_topk_batched_ex.argtypes = [vp, i64, i64, i64, i64, f64, u64, vp, vp, vp, ctypes.POINTER(Options),
                                           ctypes.POINTER(Stats)]
@@ -114,7 +116,8 @@ def load_library():
     lib.profk_strerror.restype = ctypes.c_char_p
     lib.profk_release.argtypes = []
     lib.profk_release.restype = None
-    for name in ("profk_topk", "profk_topk_ex", "profk_topk_batched", "profk_topk_batched_ex", "profk_solve",
+    for name in ("profk_topk", "profk_topk_ex", "profk_topk_approx", "profk_topk_batched", "profk_topk_batched_ex",
+                 "profk_solve",
                  "profk_stage_sample", "profk_stage_threshold", "profk_stage_filter"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -196,6 +199,51 @@ def topk(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, stats: bool 
     if stats:
         return vals, idx, stats_to_dict(st)
     return vals, idx
+
+
+APPROX_INFO_WORDS = 3  # profk_approx_info: int64 R, int64 M, int32 status, int32 exact_path
+
+
+def topk_approx(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, out=None, info=None):
+    """Approximate mode: one sampled attempt, enqueued without any host wait (so it
+    can be captured in a CUDA/HIP graph after a first call).  Returns (values,
+    indices, info) where info is an int64 device tensor of 3 words holding the
+    profk_approx_info record; decode it with approx_info().  `out` and `info`
+    reuse caller buffers."""
+    import torch
+    if x.dim() != 1 or x.dtype != torch.float32 or not x.is_cuda:
+        raise ValueError("x must be a 1-D float32 device tensor")
+    if not x.is_contiguous():
+        x = x.contiguous()
+    lib = _lib if _lib is not None else load_library()
+    dev = x.device
+    if out is None:
+        vals = torch.empty(k, dtype=torch.float32, device=dev)
+        idx = torch.empty(k, dtype=torch.int64, device=dev)
+    else:
+        vals, idx = _check_out(out, (k,), dev)
+    if info is None:
+        info = torch.empty(APPROX_INFO_WORDS, dtype=torch.int64, device=dev)
+    elif info.dtype != torch.int64 or info.numel() < APPROX_INFO_WORDS or info.device != dev:
+        raise ValueError("info must be an int64 device tensor of 3 words on the input's device")
+    args = (ctypes.c_void_p(x.data_ptr()), x.numel(), k, eps, seed & (2**64 - 1), ctypes.c_void_p(vals.data_ptr()),
+            ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(info.data_ptr()),
+            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream), _opt_ptr(options))
+    if dev.index == torch.cuda.current_device():
+        rc = lib.profk_topk_approx(*args)
+    else:
+        with torch.cuda.device(dev):
+            rc = lib.profk_topk_approx(*args)
+    _check(rc)
+    return vals, idx, info
+
+
+def approx_info(info) -> dict:
+    """Decode a profk_approx_info record (int64 tensor of 3 words) on the host."""
+    w = [int(v) for v in info.detach().cpu().tolist()[:APPROX_INFO_WORDS]]
+    st = w[2] & 0xFFFFFFFF
+    ex = (w[2] >> 32) & 0xFFFFFFFF
+    return {"R": w[0], "M": w[1], "status": st - (1 << 32) if st >= (1 << 31) else st, "exact_path": ex}
 
 
 def topk_batched(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, stats: bool = False):

@@ -41,6 +41,10 @@ int hip_fail(hipError_t e, const char* what) {
   } while (0)
 
 constexpr int kDefaultAttempts = 6;  // P1 §3 stage 4: exact fallback after six failures
+// Needed value bins up to this many keys are partitioned inside the refinement's last
+// kernel; a larger one (a tie group of that size within a wide value range) is left to
+// the multi-block radix select, which the host enqueues after reading the flag.
+constexpr u32 kMsdCapExact = 1u << 18;
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -53,7 +57,7 @@ u64 pow2_at_least(u64 v) {
 struct Layout {
   size_t hash = 0, ctl = 0, sel = 0, rec = 0, ticket = 0, keys = 0, tops = 0, cand = 0, col = 0, topk0 = 0,
          topk1 = 0, hist = 0, rows = 0, scratch = 0, rtmp = 0, rhist = 0, rbin_off = 0, rbin_cnt = 0, rcursor = 0,
-         total = 0;
+         pool = 0, total = 0;
   u64 hash_slots = 0;  // slots of the hash region (the allocation's capacity)
   u64 rows_cap = 0;    // rows of the control regions (the allocation's capacity)
   u64 hash_used = 0;   // slots this request's sample uses: a power of two >= 2S
@@ -100,6 +104,7 @@ Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap, 
   L.rows = take(B * sizeof(int));
   L.scratch = take((scratch_words ? scratch_words : 1) * sizeof(u64));
   L.rtmp = take((M ? M : 1) * sizeof(u64));
+  L.pool = take(msd_pool_words(M) * sizeof(u64));
   L.total = off;
   return L;
 }
@@ -277,7 +282,7 @@ int max_attempts_of(const profk_options* opt) {
 
 // Exact full selection of one row (radix select over all N keys formed on the fly).
 int run_exact(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, float* out_vals, int64_t* out_idx,
-              hipStream_t s) {
+              hipStream_t s, bool sync = true) {
   RowCtl* ctl = at<RowCtl>(w, L.ctl);
   SelState* sel = at<SelState>(w, L.sel);
   AttemptRecord* rec = at<AttemptRecord>(w, L.rec);
@@ -291,6 +296,10 @@ int run_exact(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, float
   HIPCHK(launch_sort_and_write(at<u64>(w, L.topk0), at<u64>(w, L.topk1), at<u32>(w, L.hist), (u32)k, x, N,
                                out_vals, out_idx, ctl, rec, s),
          "launch sort");
+  if (!sync) {  // approximate mode: stream-ordered, the consistency check is not read back
+    w->dirty = false;
+    return PROFK_OK;
+  }
   HIPCHK(hipMemcpyAsync(w->host, rec, sizeof(AttemptRecord), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
   HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
   w->dirty = false;
@@ -299,6 +308,45 @@ int run_exact(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, float
     return PROFK_EINTERNAL;
   }
   return PROFK_OK;
+}
+
+RefineArgs refine_args(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, u64 M, float* out_vals,
+                       int64_t* out_idx) {
+  RefineArgs ra{};
+  ra.ctl = at<RowCtl>(w, L.ctl);
+  ra.cand = at<u64>(w, L.cand);
+  ra.M = M;
+  ra.k = k;
+  ra.N = N;
+  ra.x = x;
+  ra.tmp = at<u64>(w, L.rtmp);
+  ra.hist = at<u32>(w, L.rhist);
+  ra.bin_off = at<u32>(w, L.rbin_off);
+  ra.bin_cnt = at<u32>(w, L.rbin_cnt);
+  ra.cursor = at<u32>(w, L.rcursor);
+  ra.table = at<u32>(w, L.hash);
+  ra.table_slots = L.hash_used;
+  ra.out_vals = out_vals;
+  ra.out_idx = out_idx;
+  ra.pool = at<u64>(w, L.pool);
+  return ra;
+}
+
+FilterArgs flat_filter_args(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, u64 M) {
+  FilterArgs fa{};
+  fa.x = x;
+  fa.ld = N;
+  fa.N = N;
+  fa.rows = nullptr;
+  fa.nrows = 1;
+  fa.ctls = at<RowCtl>(w, L.ctl);
+  fa.cand = at<u64>(w, L.cand);
+  fa.M = M;
+  fa.k = k;
+  fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
+  fa.rec = at<AttemptRecord>(w, L.rec);
+  fa.sels = at<SelState>(w, L.sel);
+  return fa;
 }
 
 // One sampled attempt of one row, enqueued; returns after the record is back.
@@ -317,41 +365,15 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   SampleArgs sa = sample_args(w, L, x, N, S, t, seed, attempt);
   sa.rec = rec;
   HIPCHK(launch_sample(sa, s), "launch sample");
-  FilterArgs fa{};
-  fa.x = x;
-  fa.ld = N;
-  fa.N = N;
-  fa.rows = nullptr;
-  fa.nrows = 1;
-  fa.ctls = ctl;
-  fa.cand = at<u64>(w, L.cand);
-  fa.M = M;
-  fa.k = k;
-  fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
-  fa.rec = rec;
-  fa.sels = sel;
+  FilterArgs fa = flat_filter_args(w, L, x, N, k, M);
   if (timing) HIPCHK(hipEventRecord(w->ev0, s), "hipEventRecord");
   HIPCHK(launch_filter(fa, 0, s), "launch filter");
   if (timing) HIPCHK(hipEventRecord(w->ev1, s), "hipEventRecord");
-  RefineArgs ra{};
-  ra.ctl = ctl;
-  ra.cand = at<u64>(w, L.cand);
-  ra.M = M;
-  ra.k = k;
-  ra.N = N;
-  ra.x = x;
-  ra.tmp = at<u64>(w, L.rtmp);
-  ra.hist = at<u32>(w, L.rhist);
-  ra.bin_off = at<u32>(w, L.rbin_off);
-  ra.bin_cnt = at<u32>(w, L.rbin_cnt);
-  ra.cursor = at<u32>(w, L.rcursor);
-  ra.table = at<u32>(w, L.hash);
-  ra.table_slots = L.hash_used;
+  RefineArgs ra = refine_args(w, L, x, N, k, M, out_vals, out_idx);
   ra.hrec = w->hrec_dev;
   ra.seq = ++w->seq;
   ra.rec = rec;
-  ra.out_vals = out_vals;
-  ra.out_idx = out_idx;
+  ra.msd_cap = kMsdCapExact;
   HIPCHK(launch_refine(ra, s), "launch refine");
   // The scan publishes the record once the check is known; the last refinement
   // launch (sorting and writing the outputs) may still run when this returns.
@@ -425,6 +447,42 @@ int topk_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* out_vals
   }
   if (st) st->fallback = 1;
   return run_exact(w, L, x, N, k, out_vals, out_idx, s);
+}
+
+// Approximate mode: one sampled attempt, everything enqueued on the stream, no host
+// read (P1 App. D: omitting the check).  The refinement runs on whatever the buffer
+// holds and reports the check's outcome in *info.
+int topk_approx_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* out_vals, int64_t* out_idx,
+                    ApproxInfo* info, hipStream_t s, const profk_options* opt) {
+  profk_params p{};
+  int rc = solve_memo((int64_t)N, (int64_t)k, eps, opt, &p);
+  if (rc) return rc;
+  const bool sampled = !p.direct_exact && !(opt && opt->force_fallback);
+  Layout L;
+  Workspace* w = nullptr;
+  rc = get_workspace(s, Need{1, sampled ? (u64)p.S : 0, sampled ? (u64)p.M : 0, k}, &w, &L);
+  if (rc) return rc;
+  if (!sampled) {
+    rc = run_exact(w, L, x, N, k, out_vals, out_idx, s, false);
+    if (rc) return rc;
+    if (info) HIPCHK(launch_approx_info_exact(info, N, s), "launch approx_info");
+    return PROFK_OK;
+  }
+  const u64 S = (u64)p.S, M = (u64)p.M, t = (u64)p.t;
+  rc = clean_if_dirty(w, L, s);
+  if (rc) return rc;
+  w->dirty = true;
+  SampleArgs sa = sample_args(w, L, x, N, S, t, seed, 0);
+  sa.rec = at<AttemptRecord>(w, L.rec);
+  HIPCHK(launch_sample(sa, s), "launch sample");
+  HIPCHK(launch_filter(flat_filter_args(w, L, x, N, k, M), 0, s), "launch filter");
+  RefineArgs ra = refine_args(w, L, x, N, k, M, out_vals, out_idx);
+  ra.msd_cap = 0xFFFFFFFFu;  // no host to hand an oversized bin to
+  ra.approx = 1;
+  ra.info = info;
+  HIPCHK(launch_refine(ra, s), "launch refine");
+  w->dirty = false;
+  return PROFK_OK;
 }
 
 // Batched form with per-row kernels (rows of at most kBatchedMaxN values whose
@@ -577,6 +635,13 @@ int profk_topk_ex(const float* x, int64_t N, int64_t k, double eps, uint64_t see
   if (rc) return rc;
   if (st) std::memset(st, 0, sizeof(*st));
   return topk_row(x, (u64)N, (u64)k, eps, seed, out_vals, out_idx, (hipStream_t)stream, opt, st);
+}
+
+int profk_topk_approx(const float* x, int64_t N, int64_t k, double eps, uint64_t seed, float* out_vals,
+                      int64_t* out_idx, profk_approx_info* info, void* stream, const profk_options* opt) {
+  int rc = validate(x, N, k, eps, out_vals, out_idx);
+  if (rc) return rc;
+  return topk_approx_row(x, (u64)N, (u64)k, eps, seed, out_vals, out_idx, info, (hipStream_t)stream, opt);
 }
 
 int profk_topk(const float* x, int64_t N, int64_t k, double eps, uint64_t seed, float* out_vals, int64_t* out_idx,

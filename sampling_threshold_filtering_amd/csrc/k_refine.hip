@@ -17,10 +17,17 @@
 //                          bin) reserves the run, LDS atomics place the keys.  Block 0
 //                          also publishes the attempt record (R, check, multi-pass
 //                          flag) to the host, which needs nothing later to decide.
-//   refine_binsort_kernel  sorts every bin >= b* in LDS (four 256-thread workgroups
-//                          per CU) and writes out_vals / out_idx for positions < k;
-//                          it also leaves the histogram and the sampler's hash set
-//                          zero for the next attempt.
+//   refine_binsort_kernel  sorts every bin >= b* (four 256-thread workgroups per CU:
+//                          one wavefront in registers up to kWaveBin keys, a workgroup
+//                          in LDS up to kBinCap) and writes out_vals / out_idx for
+//                          positions < k.  A larger bin (large tie groups, narrow
+//                          ranges) is partitioned by one workgroup on successive
+//                          12-bit digits of (key - tau), from the top down, until every
+//                          part that reaches a position below k fits those sorts.  It
+//                          also leaves the histogram and the sampler's hash set zero
+//                          for the next attempt.
+// Bins larger than RefineArgs::msd_cap are instead left to the multi-pass refinement,
+// which the host enqueues after reading the flag (exact mode only).
 // Bins partition the keys by value, so sorted bins laid out from the top bin down
 // are the sorted candidates; positions < k are the exact top-k in order.
 #include "block_select.h"
@@ -48,6 +55,12 @@ __device__ __forceinline__ u32 bin_shift_of(const RowCtl* c) {
 }
 
 __device__ __forceinline__ u64 cand_count(const RowCtl* c, u64 M) { return c->R < M ? c->R : M; }
+
+// The refinement runs when the check passed, and in approximate mode also when it
+// failed (it then refines whatever the buffer holds).
+__device__ __forceinline__ bool refine_live(const RefineArgs& a, const RowCtl* c) {
+  return c->status == 0 || (a.approx && (c->status == 1u || c->status == 2u));
+}
 
 // Attempt record into pinned host memory; seq last, released at system scope.
 __device__ __forceinline__ void publish(const RefineArgs& a, const RowCtl* c, u32 generic) {
@@ -84,7 +97,7 @@ __global__ __launch_bounds__(kHistThreads) void refine_hist_kernel(RefineArgs a)
   // the scatter reserves from zero
   for (u32 b = blockIdx.x * blockDim.x + threadIdx.x; b < kBins; b += gridDim.x * blockDim.x) a.cursor[b] = 0;
   const RowCtl* c = a.ctl;
-  if (c->status != 0) return;
+  if (!refine_live(a, c)) return;
   const u64 n = cand_count(c, a.M);
   const u64 tau = c->tau;
   const u32 shift = bin_shift_of(c);
@@ -114,7 +127,7 @@ __global__ __launch_bounds__(kHistThreads) void refine_scatter_kernel(RefineArgs
   __shared__ u32 s_wsum[kHistThreads / kWave];
   __shared__ u32 s_q, s_big;
   RowCtl* c = a.ctl;
-  if (c->status != 0) {
+  if (!refine_live(a, c)) {
     if (blockIdx.x == 0 && threadIdx.x == 0) publish(a, c, 0u);
     return;
   }
@@ -162,12 +175,13 @@ __global__ __launch_bounds__(kHistThreads) void refine_scatter_kernel(RefineArgs
   }
   if (tid == blockDim.x - 1) s_off[pad_q(kBins)] = run;
   __syncthreads();
-  const u32 qstar = s_q;
-  // every bin at or above b* must fit one sorting workgroup
+  // fewer than k candidates (approximate mode only): every bin is needed
+  const u32 qstar = s_q == 0xFFFFFFFFu && a.approx ? kBins - 1u : s_q;
+  // every bin at or above b* must fit the in-kernel sorts and partition
   bool big = qstar == 0xFFFFFFFFu;
 #pragma unroll
   for (u32 j = 0; j < kPer; ++j)
-    if (tid * kPer + j <= qstar && cnt[j] > kBinCap) big = true;
+    if (tid * kPer + j <= qstar && cnt[j] > a.msd_cap) big = true;
   if (big) s_big = 1;
   __syncthreads();
   const bool generic = s_big != 0;
@@ -252,16 +266,16 @@ __device__ __forceinline__ void write_out(const RefineArgs& a, u64 p, u64 key) {
   if (idx < a.N) reinterpret_cast<u32*>(a.out_vals)[p] = value_bits(key, a.x, idx);
 }
 
-// One bin of cnt <= 64*M keys at tmp[start..), sorted by one wavefront in registers;
+// One part of cnt <= 64*M keys at src[start..), sorted by one wavefront in registers;
 // positions below lim are written out.
 template <int M>
-__device__ __forceinline__ void wave_bin(const RefineArgs& a, u32 start, u32 cnt, u64 lim) {
+__device__ __forceinline__ void wave_bin(const RefineArgs& a, const u64* src, u32 start, u32 cnt, u64 lim) {
   const u32 lane = lane_id();
   u64 v[M];
 #pragma unroll
   for (int r = 0; r < M; ++r) {
     const u32 i = (u32)r * kWave + lane;
-    v[r] = i < cnt ? a.tmp[start + i] : 0ull;
+    v[r] = i < cnt ? src[start + i] : 0ull;
   }
   wave_sort_regs_desc<M>(v);
 #pragma unroll
@@ -271,12 +285,153 @@ __device__ __forceinline__ void wave_bin(const RefineArgs& a, u32 start, u32 cnt
   }
 }
 
-// Bins of up to kWaveBin keys: one wavefront each, sorted in registers.  Larger bins
-// (up to kBinCap): the whole workgroup in LDS.
+// A part of 1 <= cnt <= kWaveBin keys at src[start..) (wave-uniform arguments).
+__device__ __forceinline__ void wave_part(const RefineArgs& a, const u64* src, u32 start, u32 cnt) {
+  const u64 lim = a.k - start < cnt ? a.k - start : cnt;
+  if (cnt <= 64) wave_bin<1>(a, src, start, cnt, lim);
+  else if (cnt <= 128) wave_bin<2>(a, src, start, cnt, lim);
+  else if (cnt <= 256) wave_bin<4>(a, src, start, cnt, lim);
+  else if (cnt <= 512) wave_bin<8>(a, src, start, cnt, lim);
+  else wave_bin<16>(a, src, start, cnt, lim);
+}
+
+// A part of cnt <= kBinCap keys at src[start..), sorted by the workgroup in LDS.
+__device__ void lds_part(const RefineArgs& a, u64* s, const u64* src, u32 start, u32 cnt) {
+  u32 P = 1;
+  while (P < cnt) P <<= 1;
+  __syncthreads();
+  for (u32 i = threadIdx.x; i < P; i += blockDim.x) s[i] = i < cnt ? src[start + i] : 0ull;
+  __syncthreads();
+  block_bitonic_desc(s, P);
+  const u64 lim = a.k - start < cnt ? a.k - start : cnt;
+  for (u32 i = threadIdx.x; i < lim; i += blockDim.x) write_out(a, start + i, s[i]);
+}
+
+__device__ __forceinline__ u32 msd_digit(u64 key, u64 tau, u32 sub) {
+  return (u32)((key - tau) >> sub) & (kMsdDigits - 1u);
+}
+
+constexpr u32 kMsdMaxLevels = (64 + kMsdBits - 1) / kMsdBits + 1;
+
+struct MsdLds {
+  u32 nlist;  // entries appended to the next level's list
+  u64 ent;    // entry being processed (broadcast)
+  u32 wsum[kSortThreads / kWave];
+};
+
+// Splits the part of c0 keys at src[s0..) by the digit of (key - tau) at bit `sub`
+// into dst[s0..), parts in descending digit order.  Parts of at most kWaveBin keys
+// that reach a position below k are sorted at once by one wavefront; larger ones are
+// appended to nxt.  The digit cursors live in the LDS sort buffer s.
+__device__ void msd_split(const RefineArgs& a, u64* s, const u64* src, u64* dst, u32 s0, u32 c0, u32 sub,
+                          u64 tau, u64* nxt, MsdLds* m) {
+  u32* cur = reinterpret_cast<u32*>(s);
+  const u32 tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  constexpr u32 kPerT = kMsdDigits / kSortThreads;
+  for (u32 d = tid; d < kMsdDigits; d += blockDim.x) cur[d] = 0;
+  __syncthreads();
+  for (u32 i = tid; i < c0; i += blockDim.x) atomicAdd(&cur[msd_digit(src[s0 + i], tau, sub)], 1u);
+  __syncthreads();
+  // start of every part: thread tid owns descending positions [tid*kPerT, tid*kPerT + kPerT)
+  u32 v[kPerT];
+  u32 sum = 0;
+#pragma unroll
+  for (u32 j = 0; j < kPerT; ++j) {
+    v[j] = cur[kMsdDigits - 1u - (tid * kPerT + j)];
+    sum += v[j];
+  }
+  u32 incl = sum;
+#pragma unroll
+  for (u32 d = 1; d < (u32)kWave; d <<= 1) {
+    const u32 o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) m->wsum[wid] = incl;
+  __syncthreads();
+  u32 run = s0 + incl - sum;
+  for (u32 w = 0; w < wid; ++w) run += m->wsum[w];
+#pragma unroll
+  for (u32 j = 0; j < kPerT; ++j) {
+    cur[kMsdDigits - 1u - (tid * kPerT + j)] = run;
+    run += v[j];
+  }
+  __syncthreads();
+  for (u32 i = tid; i < c0; i += blockDim.x) {
+    const u64 key = src[s0 + i];
+    dst[atomicAdd(&cur[msd_digit(key, tau, sub)], 1u)] = key;
+  }
+  __syncthreads();
+  // part d now spans [end of part d + 1, cur[d]); each wavefront takes 64 digits at a time
+  for (u32 ch = wid; ch < kMsdDigits / kWave; ch += kSortThreads / kWave) {
+    const u32 d = kMsdDigits - 1u - (ch * kWave + lane);
+    const u32 en = cur[d];
+    const u32 st = d == kMsdDigits - 1u ? s0 : cur[d + 1];
+    const u32 c = en - st;
+    const bool need = c != 0 && (u64)st < a.k;
+    if (need && c > kWaveBin) nxt[atomicAdd(&m->nlist, 1u)] = (u64)st | ((u64)c << 32);
+    u64 small = __ballot(need && c <= kWaveBin);
+    while (small) {
+      const int l = __ffsll((unsigned long long)small) - 1;
+      small &= small - 1;
+      wave_part(a, dst, (u32)__shfl((int)st, l), (u32)__shfl((int)c, l));
+    }
+  }
+  __syncthreads();
+}
+
+// Bin b of cnt > kBinCap keys at tmp[start..), of key width 2^width: partitioned level
+// by level (ping-pong between tmp and the candidate buffer, which the scatter no longer
+// needs) until every part below position k is sorted.  Parts at one level are disjoint
+// and hold more than kWaveBin keys, so a list never exceeds cnt / 1024 + 1 entries;
+// bins' lists are disjoint pool ranges.  Each level lowers the width by kMsdBits, and a
+// part of width 2^kMsdBits holds at most kMsdDigits <= kBinCap distinct keys, so at most
+// ceil(64 / kMsdBits) levels run.
+__device__ void msd_bin(const RefineArgs& a, u64* s, u32 b, u32 start, u32 cnt, u32 width, u64 tau, MsdLds* m) {
+  const u32 cap = (cnt >> 10) + 1u;
+  u64* cur = a.pool + 2ull * ((u64)(start >> 10) + (kBins - 1u - b));
+  u64* nxt = cur + cap;
+  u64* src = a.tmp;
+  u64* dst = a.cand;
+  if (threadIdx.x == 0) atomic_store_agent(&cur[0], (u64)start | ((u64)cnt << 32));
+  u32 ncur = 1;
+  u32 w = width;
+  // keys are distinct, so a part of width 1 holds one key: the level bound only
+  // guarantees termination
+  for (u32 level = 0; ncur && level < kMsdMaxLevels; ++level) {
+    const u32 sub = w > kMsdBits ? w - kMsdBits : 0u;
+    if (threadIdx.x == 0) m->nlist = 0;
+    __syncthreads();
+    for (u32 e = 0; e < ncur; ++e) {
+      if (threadIdx.x == 0) m->ent = atomic_load_agent(&cur[e]);
+      __syncthreads();
+      const u64 ent = m->ent;
+      __syncthreads();
+      const u32 s0 = (u32)ent, c0 = (u32)(ent >> 32);
+      if (c0 <= kBinCap)
+        lds_part(a, s, src, s0, c0);
+      else
+        msd_split(a, s, src, dst, s0, c0, sub, tau, nxt, m);
+    }
+    __syncthreads();
+    ncur = m->nlist;
+    __syncthreads();  // every thread has the count before thread 0 resets it
+    u64* t = cur;
+    cur = nxt;
+    nxt = t;
+    t = src;
+    src = dst;
+    dst = t;
+    w = sub;
+  }
+}
+
+// Bins of up to kWaveBin keys: one wavefront each, sorted in registers.  Larger bins:
+// the whole workgroup, in LDS up to kBinCap, else by the partition above.
 __global__ __launch_bounds__(kSortThreads) void refine_binsort_kernel(RefineArgs a) {
   __shared__ u64 s[kBinCap];
   __shared__ u32 s_big[kSortThreads];
   __shared__ u32 s_nbig;
+  __shared__ MsdLds s_msd;
   {  // leave the histogram and the sampler's hash set zero for the next attempt
     const u64 gt = (u64)blockIdx.x * blockDim.x + threadIdx.x, gs = (u64)gridDim.x * blockDim.x;
     for (u64 i = gt; i < kBins; i += gs) a.hist[i] = 0;
@@ -284,7 +439,23 @@ __global__ __launch_bounds__(kSortThreads) void refine_binsort_kernel(RefineArgs
       for (u64 i = gt; i < a.table_slots; i += gs) a.table[i] = 0;
   }
   const RowCtl* c = a.ctl;
-  if (c->status != 0 || c->generic) return;
+  if (a.approx) {
+    // approximate mode: the outcome of the check, and padding where fewer than k
+    // candidates were kept
+    const u64 gt = (u64)blockIdx.x * blockDim.x + threadIdx.x, gs = (u64)gridDim.x * blockDim.x;
+    if (gt == 0 && a.info) {
+      a.info->R = (int64_t)c->R;
+      a.info->M = (int64_t)a.M;
+      a.info->status = (int32_t)c->status;
+      a.info->exact_path = 0;
+    }
+    const u64 n = refine_live(a, c) ? cand_count(c, a.M) : 0;
+    for (u64 p = n + gt; p < a.k; p += gs) {
+      a.out_idx[p] = -1;
+      reinterpret_cast<u32*>(a.out_vals)[p] = 0xFF800000u;  // -inf
+    }
+  }
+  if (!refine_live(a, c) || c->generic) return;
   const int bstar = (int)c->bstar;
   const u64 k = a.k;
   const u32 lane = lane_id();
@@ -300,29 +471,35 @@ __global__ __launch_bounds__(kSortThreads) void refine_binsort_kernel(RefineArgs
       if (lane == 0) s_big[atomicAdd(&s_nbig, 1u)] = (u32)b;  // at most one per wavefront pass
       continue;
     }
-    const u64 lim = k - start < cnt ? k - start : cnt;
-    if (cnt <= 64) wave_bin<1>(a, start, cnt, lim);
-    else if (cnt <= 128) wave_bin<2>(a, start, cnt, lim);
-    else if (cnt <= 256) wave_bin<4>(a, start, cnt, lim);
-    else if (cnt <= 512) wave_bin<8>(a, start, cnt, lim);
-    else wave_bin<16>(a, start, cnt, lim);
+    wave_part(a, a.tmp, start, cnt);
   }
   __syncthreads();
   const u32 nbig = s_nbig;
+  const u64 tau = c->tau;
+  const u32 width = c->bin_shift;
   for (u32 q = 0; q < nbig; ++q) {
     const u32 b = s_big[q];
     const u32 cnt = a.bin_cnt[b];
     const u32 start = a.bin_off[b];
-    if (cnt > kBinCap) continue;  // the scan sent such rows to the multi-pass refinement
-    u32 P = 1;
-    while (P < cnt) P <<= 1;
-    __syncthreads();
-    for (u32 i = threadIdx.x; i < P; i += blockDim.x) s[i] = i < cnt ? a.tmp[start + i] : 0ull;
-    __syncthreads();
-    block_bitonic_desc(s, P);
-    const u64 lim = k - start < cnt ? k - start : cnt;
-    for (u32 i = threadIdx.x; i < lim; i += blockDim.x) write_out(a, start + i, s[i]);
+    if (cnt <= kBinCap)
+      lds_part(a, s, a.tmp, start, cnt);
+    else
+      msd_bin(a, s, b, start, cnt, width, tau, &s_msd);
   }
+}
+
+__global__ void approx_info_exact_kernel(ApproxInfo* info, u64 N) {
+  if (threadIdx.x == 0) {
+    info->R = (int64_t)N;
+    info->M = 0;
+    info->status = 0;
+    info->exact_path = 1;
+  }
+}
+
+hipError_t launch_approx_info_exact(ApproxInfo* info, u64 N, hipStream_t s) {
+  approx_info_exact_kernel<<<1, 64, 0, s>>>(info, N);
+  return hipGetLastError();
 }
 
 hipError_t launch_refine(const RefineArgs& a, hipStream_t s) {

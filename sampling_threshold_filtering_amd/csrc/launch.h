@@ -96,9 +96,16 @@ constexpr u32 kBinBits = 14;
 constexpr u32 kBins = 1u << kBinBits;
 constexpr u32 kBinCap = 4096;  // keys one sorting workgroup holds in LDS (32 KB)
 
+constexpr u32 kMsdBits = 12;  // digit of the in-kernel partition of oversized bins
+constexpr u32 kMsdDigits = 1u << kMsdBits;
+
+// Work-list entries (start | count << 32) of the in-kernel partition of oversized
+// bins: two lists per oversized bin, at most kBins + M / 1024 + 2 pairs in all.
+__host__ __device__ inline u64 msd_pool_words(u64 M) { return 2 * (M / 1024 + kBins + 2); }
+
 struct RefineArgs {
   RowCtl* ctl;
-  const u64* cand;  // min(R, M) candidate keys
+  u64* cand;        // min(R, M) candidate keys; reused as the partition's second buffer
   u64 M;
   u64 k;
   u64 N;
@@ -115,9 +122,17 @@ struct RefineArgs {
   AttemptRecord* rec;
   float* out_vals;
   int64_t* out_idx;
+  u64* pool;        // msd_pool_words(M) words: work lists of the oversized-bin partition
+  u32 msd_cap;      // largest needed bin partitioned in-kernel; larger ones defer to the
+                    // multi-pass refinement (the host reads the flag)
+  u32 approx;       // 1: no run-time check (approximate mode): refine whatever the buffer
+                    // holds, pad missing outputs, and report R and the check in *info
+  ApproxInfo* info; // approximate mode: device result of the check, or nullptr
 };
 
 hipError_t launch_refine(const RefineArgs& a, hipStream_t s);
+// Approximate mode routed to the exact selection: *info = {N, 0, 0, 1}.
+hipError_t launch_approx_info_exact(ApproxInfo* info, u64 N, hipStream_t s);
 
 // Batched form (k_batched.hip): rows of at most kBatchedMaxN values.
 constexpr u64 kBatchedMaxN = 1ull << 20;

@@ -13,6 +13,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "profk.h"
 
 namespace profk {
 
@@ -328,6 +329,9 @@ struct AttemptRecord {
 // The attempt record as published into pinned host memory by the refinement: the
 // host waits for `seq` to reach the value of its call instead of synchronising the
 // stream, and returns while the last refinement launch is still writing outputs.
+// Device-side outcome of an approximate-mode call (the public profk_approx_info).
+using ApproxInfo = profk_approx_info;
+
 struct HostRecord {
   u64 R;
   u32 status;

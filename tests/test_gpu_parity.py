@@ -171,7 +171,14 @@ def test_binned_and_multipass_refinement_both_run():
     vals, idx, st = stf.topk(dev(x), 3000, stats=True)
     check_topk(x, vals, idx, 3000)
     assert st["refine_multipass"] == 0
-    # two values, 419K copies of the larger: its bin is too large for one LDS sort
+    # two values, ~210K copies of the larger within a value range that puts each tie
+    # group in one bin: the last refinement kernel partitions those bins itself
+    x = edge_case("two_levels", 1 << 21, 43)
+    vals, idx, st = stf.topk(dev(x), 250000, stats=True)
+    check_topk(x, vals, idx, 250000)
+    assert st["refine_multipass"] == 0
+    # 419K copies of the larger: beyond what one workgroup partitions, so the host hands
+    # the bin to the multi-block radix select
     x = edge_case("two_levels", 1 << 22, 42)
     vals, idx, st = stf.topk(dev(x), 500000, stats=True)
     check_topk(x, vals, idx, 500000)
