@@ -10,6 +10,9 @@ for the count R that the device publishes.  Each k is timed over K calls back
 to back (HIP events on the stream around them; the host calls in turn, each
 returning once its run-time check is known, so the next call queues behind the
 previous refinement); `value` = 4 N / (sum over k of the mean call time).
+The sample size follows the rule calibrated on MI355X (--s-rule 2: Algorithm 1
+of the page with the cost ratio that `--calibrate-s` measures); the same sweep
+under the library's default (k N)^(1/3) rule is printed beside it.
 
 Also printed (same JSON line):
   per_k        ms, Gelem/s and algorithmic GB/s (4N bytes per call) per k
@@ -34,6 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+S_RULE_NAMES = {0: "cube-root (k N)^(1/3), S in [2^15, 2^17]", 1: "Algorithm 1, page cost ratio",
+                2: "Algorithm 1, cost ratio measured on MI355X, S in [2^12, 2^17]"}
 KS = (1 << 5, 1 << 10, 1 << 15, 1 << 19)
 EPS = 1e-3
 
@@ -44,10 +49,17 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--log2n", type=int, default=30, help="input size (default: the 2^30 workload)")
+    ap.add_argument("--s-rule", type=int, default=2, choices=(0, 1, 2),
+                    help="sample-size rule: 0 the (kN)^(1/3) rule clamped to [2^15, 2^17] (the library default), "
+                         "1 Algorithm 1 with the page's cost ratio, 2 Algorithm 1 with the ratio measured on "
+                         "MI355X (default here)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-batched", action="store_true", help="skip the batched variant")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--calibrate-s", metavar="OUT_JSON",
+                    help="sweep the sample size S over an (N, k) grid, fit the cost model of the sample-size "
+                         "rule and write the measurements and the fit to OUT_JSON")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FILTER_FETCH_CSV", "FILTER_WRITE_CSV", "COPY_FETCH_CSV",
                                                          "COPY_WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs into the traffic record")
@@ -137,13 +149,181 @@ def cpu_baseline(x: np.ndarray):
     sample = x[:n]
     oracle.topk(sample[: 1 << 20], 32, nthreads=threads)  # warm the library and pages
     t0 = time.perf_counter()
-    for k in KS:
-        oracle.topk(sample, k, nthreads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": round(len(KS) * n / dt / 1e9, 4), "unit": "Gelem/s", "cores": threads, "kind": "oracle",
-            "sample": f"the same 2^{n.bit_length() - 1}-value tensor, k sweep {list(KS)}, "
+    reps = 0
+    while True:  # whole k sweeps until about 10 s of CPU work
+        for k in KS:
+            oracle.topk(sample, k, nthreads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or reps >= 32:
+            break
+    return {"value": round(reps * len(KS) * n / dt / 1e9, 4), "unit": "Gelem/s", "cores": threads, "kind": "oracle",
+            "sample": f"the same 2^{n.bit_length() - 1}-value tensor, k sweep {list(KS)} repeated {reps} times, "
                       f"{dt:.2f} s total; plain C heap top-k, {threads} threads"}
 
+
+# ---------------------------------------------------------------------------
+# Sample-size calibration ("Prof-K: Probabilistic One-Pass Filtering for Efficient
+# Top-k Selection", App. E.1 "Sample Size"; §4 "Choice of the Sample Size", Eq. 13
+# and Proposition 7).  The overhead beyond the scan is modelled as
+#   C(S) = c + (g + b) S + d(k) M*(S)
+# with one intercept c per (N, k), one sampling cost g + b and one buffer cost d(k)
+# per k; the ratio 1/r(k) = d(k) / (g + b) is what the cost-model S rule takes.
+# The grid is the page's (S = 2^12 .. 2^18 capped at N/32, exact (t*, M*) at
+# eps = 1e-3, standard normal inputs, k = 2^5 .. 2^17) with N up to 2^30 and k = 2^19
+# added.  Besides the page's per-k least-squares fit, one constant 1/r (and the
+# floor S_min) is fitted by direct search: the value whose Proposition-7 rule gives
+# the lowest mean latency relative to the best grid point (the rule without the
+# page's S_min floor for k/N > 2^-10, as the library's MI355X rule takes it).
+CAL_LOG2N = (22, 24, 26, 28, 30)
+CAL_KS = (1 << 5, 1 << 8, 1 << 11, 1 << 14, 1 << 17, 1 << 19)
+CAL_LOG2S = tuple(range(12, 19))
+CAL_CALLS = 10
+
+
+def _time_calls(stf, torch, xd, k, opts, calls, warmup, stream, out):
+    for w in range(warmup):
+        stf.topk(xd, k, eps=EPS, seed=1000 + w, options=opts, out=out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    fms, rs, att = 0.0, 0.0, 0
+    e0.record(stream)
+    for s in range(calls):
+        _, _, st = stf.topk(xd, k, eps=EPS, seed=s, options=opts, stats=True, out=out)
+        fms += st["filter_ms"]
+        rs += st["R"][-1] if st["R"] else 0
+        att += st["attempts"]
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / calls, fms / calls, rs / calls, att / calls
+
+
+def _fit_cost_model(rows):
+    """Least squares of overhead = c[N,k] + gb * S + d[k] * M over the rows whose
+    sampler runs its one-pass form (S <= 2^17 and S <= N/64; beyond that the
+    threshold select and the top-up change the per-sample cost)."""
+    use = [r for r in rows if (1 << 14) <= r["S"] <= (1 << 17) and 64 * r["S"] <= r["N"]]
+    cfgs = sorted({(r["N"], r["k"]) for r in use})
+    ks = sorted({r["k"] for r in use})
+    ncol = len(cfgs) + 1 + len(ks)
+    A = np.zeros((len(use), ncol))
+    y = np.zeros(len(use))
+    for i, r in enumerate(use):
+        A[i, cfgs.index((r["N"], r["k"]))] = 1.0
+        A[i, len(cfgs)] = r["S"]
+        A[i, len(cfgs) + 1 + ks.index(r["k"])] = r["M"]
+        y[i] = r["overhead_ms"] * 1e6  # ns
+    coef, *_ = np.linalg.lstsq(A, y, rcond=None)
+    pred = A @ coef
+    gb = float(coef[len(cfgs)])
+    d = {k: float(coef[len(cfgs) + 1 + j]) for j, k in enumerate(ks)}
+    ss_res = float(np.sum((y - pred) ** 2))
+    ss_tot = float(np.sum((y - y.mean()) ** 2))
+    call_ns = np.array([r["ms"] * 1e6 for r in use])
+    inv_r = {k: (d[k] / gb if gb > 0 and d[k] > 0 else 0.0) for k in ks}
+    return {"sampling_ns_per_elem": gb, "buffer_ns_per_slot": {str(k): v for k, v in d.items()},
+            "inv_r": {str(k): v for k, v in inv_r.items()},
+            "r2_overhead": 1.0 - ss_res / ss_tot if ss_tot > 0 else None,
+            "mean_rel_err_of_call": float(np.mean(np.abs(y - pred) / call_ns)),
+            "mean_rel_err_of_overhead": float(np.mean(np.abs(y - pred) / np.maximum(y, 1.0))),
+            "rows_fitted": len(use)}
+
+
+def _prop7_s(N, k, z, inv_r, s_min, s_max):
+    """Algorithm 1 lines 3-4 for a constant 1/r, without the floor for k/N > 2^-10
+    (the measurement's own copy: it only scores sample sizes on the measured grid)."""
+    if inv_r <= 0.0:
+        S = s_min
+    else:
+        kappa = z * z + 0.5
+        s1 = (z * inv_r) ** (2.0 / 3.0) * (k * N) ** (1.0 / 3.0)
+        s2 = (kappa * N * inv_r) ** 0.5
+        S = max(s_min, min(s_max, int(max(s1, s2))))
+    return min(S, max(1, N // 128))
+
+
+def _fit_constant_ratio(rows, z):
+    """Direct search for one 1/r and S_min: the rule's latency, interpolated in log2 S
+    between grid points, relative to the best grid latency, averaged over (N, k)."""
+    grid = {}
+    for r in rows:
+        grid.setdefault((r["N"], r["k"]), {})[r["S"]] = r["ms"]
+    best = None
+    for s_min in (1 << 12, 1 << 13, 1 << 14):
+        for inv_r in np.geomspace(0.002, 1.0, 61):
+            ratios = []
+            for (N, k), m in grid.items():
+                ss = sorted(m)
+                S = _prop7_s(N, k, z, inv_r, s_min, 1 << 17)
+                lat = float(np.interp(np.log2(S), np.log2(ss), [m[v] for v in ss]))
+                ratios.append(lat / min(m.values()))
+            cand = (float(np.mean(ratios)), float(inv_r), s_min, float(np.max(ratios)))
+            if best is None or cand[0] < best[0]:
+                best = cand
+    return {"inv_r": best[1], "s_min": best[2], "s_max": 1 << 17, "mean_latency_ratio_to_best": best[0],
+            "worst_latency_ratio_to_best": best[3]}
+
+
+def calibrate_s(path: str, calls: int = CAL_CALLS):
+    import torch
+
+    import sampling_threshold_filtering_amd as stf
+    from workloads import generate
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nmax = 1 << max(CAL_LOG2N)
+    x = torch.from_numpy(generate("normal", nmax, seed=0)).to(dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    for ln in CAL_LOG2N:
+        N = 1 << ln
+        xd = x[:N]
+        for k in CAL_KS:
+            out = (torch.empty(k, dtype=torch.float32, device=dev), torch.empty(k, dtype=torch.int64, device=dev))
+            for ls in CAL_LOG2S:
+                S = 1 << ls
+                if S > N // 32:
+                    continue
+                opts = stf.make_options(timing=1, s_override=S)
+                p = stf.solve(N, k, EPS, options=opts)
+                if p["direct_exact"]:
+                    continue
+                ms, fms, r_mean, att = _time_calls(stf, torch, xd, k, opts, calls, 2, stream, out)
+                row = {"N": N, "k": k, "S": S, "t": p["t"], "M": p["M"], "ms": ms, "filter_ms": fms,
+                       "overhead_ms": ms - fms, "R_mean": r_mean, "attempts_mean": att}
+                rows.append(row)
+                print(json.dumps(row), flush=True)
+    z = stf.solve(1 << 30, 32, EPS)["z_a"]
+    fit = _fit_cost_model(rows)
+    const = _fit_constant_ratio(rows, z)
+    print(json.dumps({"fit": fit, "constant_ratio_fit": const}), flush=True)
+    # latency at the S each rule of the library picks, next to the best grid point
+    rules = {"cube_root": {"s_rule": 0}, "cost_model_page": {"s_rule": 1}, "mi355x": {"s_rule": 2}}
+    picks = []
+    for ln in CAL_LOG2N:
+        N = 1 << ln
+        xd = x[:N]
+        for k in CAL_KS:
+            out = (torch.empty(k, dtype=torch.float32, device=dev), torch.empty(k, dtype=torch.int64, device=dev))
+            grid = [r for r in rows if r["N"] == N and r["k"] == k]
+            if not grid:
+                continue
+            best = min(grid, key=lambda r: r["ms"])
+            rec = {"N": N, "k": k, "best_grid_S": best["S"], "best_grid_ms": best["ms"]}
+            for name, kw in rules.items():
+                opts = stf.make_options(timing=1, **kw)
+                p = stf.solve(N, k, EPS, options=opts)
+                ms, _, r_mean, _ = _time_calls(stf, torch, xd, k, opts, calls, 2, stream, out)
+                rec[name] = {"S": p["S"], "ms": ms, "R_mean": r_mean, "direct_exact": p["direct_exact"]}
+            picks.append(rec)
+            print(json.dumps(rec), flush=True)
+    res = {"workload": "standard normal fp32, seed 0, prefixes of one 2^30 tensor", "eps": EPS, "calls": calls,
+           "grid": rows, "fit": fit, "constant_ratio_fit": const, "rules": picks}
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
 
 def main():
     args = parse()
@@ -152,6 +332,9 @@ def main():
         return
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.calibrate_s:
+        calibrate_s(args.calibrate_s)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -171,7 +354,7 @@ def main():
     xd = torch.from_numpy(x).to(dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    opts = stf.make_options(timing=1)
+    opts = stf.make_options(timing=1, s_rule=args.s_rule)
 
     per_k = {}
     filt_bytes = 0.0
@@ -202,6 +385,26 @@ def main():
                          "frac_of_hbm_peak": round(4.0 * N / ms / 1e6 / HBM_PEAK_GBPS, 4)}
     torch.cuda.synchronize()
 
+    # the same sweep with the library's default sample-size rule, for comparison
+    other_rule = None
+    if args.s_rule != 0:
+        other_rule = {}
+        o0 = stf.make_options(s_rule=0)
+        for k in KS:
+            out = (torch.empty(k, dtype=torch.float32, device=dev), torch.empty(k, dtype=torch.int64, device=dev))
+            for _ in range(args.warmup):
+                stf.topk(xd, k, eps=EPS, seed=0, options=o0, out=out)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for s in range(args.steps):
+                stf.topk(xd, k, eps=EPS, seed=s, options=o0, out=out)
+            e1.record(stream)
+            e1.synchronize()
+            other_rule[str(k)] = {"ms": round(e0.elapsed_time(e1) / args.steps, 4),
+                                  "S": stf.solve(N, k, EPS, options=o0)["S"]}
+
     n_filter = args.steps * len(KS)
     achieved = filt_bytes / n_filter / (filt_ms / n_filter / 1e3) / 1e9
     traffic = traffic_record(N)
@@ -214,21 +417,23 @@ def main():
     if not args.no_batched and N >= (1 << 20) * 16:
         B = min(1024, N >> 20)
         xb = xd[: B << 20].view(B, 1 << 20)
+        bopts = stf.make_options(s_rule=args.s_rule)
         for _ in range(max(1, args.warmup)):
-            stf.topk_batched(xb, 64, eps=EPS, seed=0)
+            stf.topk_batched(xb, 64, eps=EPS, seed=0, options=bopts)
         torch.cuda.synchronize()
         nb = max(1, args.steps // 2)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for s in range(nb):
-            stf.topk_batched(xb, 64, eps=EPS, seed=s)
+            stf.topk_batched(xb, 64, eps=EPS, seed=s, options=bopts)
         e1.record(stream)
         e1.synchronize()
         bt = [e0.elapsed_time(e1) / nb]
         bms = float(np.mean(bt))
         batched = {"rows": B, "row_len": 1 << 20, "k": 64, "ms": round(bms, 4),
-                   "gelem_s": round((B << 20) / bms / 1e6, 2)}
+                   "gelem_s": round((B << 20) / bms / 1e6, 2),
+                   "S_per_row": stf.solve(1 << 20, 64, EPS / B, options=bopts)["S"]}
 
     cpu = None if args.no_cpu else cpu_baseline(x)
 
@@ -247,9 +452,12 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"Pareto(1.5) fp32 flat tensor N=2^{args.log2n}, seed 0, exact top-k k sweep "
-                               f"{list(KS)}, eps=1e-3", "N": N, "ks": list(KS), "eps": EPS},
+                               f"{list(KS)}, eps=1e-3", "N": N, "ks": list(KS), "eps": EPS,
+                   "s_rule": S_RULE_NAMES[args.s_rule],
+                   "S": {str(k): stf.solve(N, k, EPS, options=opts)["S"] for k in KS}},
         "hbm_frac_alg": round(4.0 * N * len(KS) / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
         "per_k": per_k,
+        "per_k_cube_root_rule": other_rule,
         "retries": retries,
         "roofline": roofline,
         "batched": batched,

@@ -72,13 +72,18 @@ typedef struct profk_options {
   int32_t s_rule;         /* PROFK_S_RULE_CUBE_ROOT (0): S = c (k (N-k))^(1/3) clamped to [s_min, s_max]
                              (P2 Theorem 5); PROFK_S_RULE_COST_MODEL: P1 Algorithm 1 lines 1-4 (the cost
                              model of Proposition 7 with the calibrated ratio r(k); defaults s_min = 2^14,
-                             s_max = 2^18) */
+                             s_max = 2^18); PROFK_S_RULE_MI355X: the same lines with the cost ratio
+                             measured on MI355X (one constant 1/r = 0.022 for every k, no floor for
+                             k/N > 2^-10; defaults s_min = 2^12, s_max = 2^17) */
+  double cost_a, cost_b;  /* PROFK_S_RULE_COST_MODEL: 1/r(k) = cost_a log2(k) - cost_b for k > 2^7 (P1 App.
+                             E.1); both <= 0: the page's calibration, 0.594 and 4.29 */
 } profk_options;
 
 #define PROFK_PARAMS_EXACT 0
 #define PROFK_PARAMS_FAST 1
 #define PROFK_S_RULE_CUBE_ROOT 0
 #define PROFK_S_RULE_COST_MODEL 1
+#define PROFK_S_RULE_MI355X 2
 
 /* The parameter choice for one (N, k, eps) (P1 §4 Theorem 4; P2 §4). */
 typedef struct profk_params {

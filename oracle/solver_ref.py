@@ -162,15 +162,19 @@ def inv_cost_ratio(k: int, a: float = 0.594, b: float = 4.29) -> float:
 
 
 def s_rule_cost_model(N: int, k: int, eps: float, s_min: int = 1 << 14, s_max: int = 1 << 18,
-                      a: float = 0.594, b: float = 4.29) -> int:
+                      a: float = 0.594, b: float = 4.29, inv_r: float | None = None,
+                      dense_floor: bool = True) -> int:
     """P1 Algorithm 1 lines 1-4 (Proposition 7): S1 = (z/r)^(2/3) (kN)^(1/3),
     S2 = (kappa N / r)^(1/2), kappa = z^2 + 1/2, z = Phi^-1(1 - eps/2);
     S = clip(floor(max(S1, S2)), S_min, S_max), and S_min when r is infinite or
-    k/N > 2^-10.  Then at most N/128 and at most N, as for the default rule."""
+    k/N > 2^-10.  Then at most N/128 and at most N, as for the default rule.
+    1/r is a log2 k - b, or the given constant inv_r for every k; without
+    dense_floor the k/N > 2^-10 clause is left out."""
     z = z_upper(eps / 2.0)
     kappa = z * z + 0.5
-    inv_r = inv_cost_ratio(k, a, b)
-    if inv_r <= 0.0 or k / N > 2.0 ** -10:
+    if inv_r is None:
+        inv_r = inv_cost_ratio(k, a, b)
+    if inv_r <= 0.0 or (dense_floor and k / N > 2.0 ** -10):
         S = s_min
     else:
         s1 = (z * inv_r) ** (2.0 / 3.0) * (k * N) ** (1.0 / 3.0)
@@ -178,6 +182,19 @@ def s_rule_cost_model(N: int, k: int, eps: float, s_min: int = 1 << 14, s_max: i
         S = max(s_min, min(s_max, int(math.floor(max(s1, s2)))))
     S = min(S, max(1, N // 128))
     return min(S, N)
+
+
+# The cost ratio measured on MI355X with the sweep of P1 App. E.1 (bench.py
+# --calibrate-s): one constant for every k, its clip range, and no floor for dense k.
+MI355X_INV_R = 0.022
+MI355X_S_MIN = 1 << 12
+MI355X_S_MAX = 1 << 17
+
+
+def s_rule_mi355x(N: int, k: int, eps: float) -> int:
+    """Algorithm 1 lines 1-4 with the MI355X cost ratio."""
+    return s_rule_cost_model(N, k, eps, s_min=MI355X_S_MIN, s_max=MI355X_S_MAX, inv_r=MI355X_INV_R,
+                             dense_floor=False)
 
 
 def surrogate_params(N: int, k: int, S: int, eps: float) -> tuple[int, int]:

@@ -50,6 +50,8 @@ class Options(ctypes.Structure):
         ("timing", ctypes.c_int32),
         ("param_mode", ctypes.c_int32),
         ("s_rule", ctypes.c_int32),
+        ("cost_a", ctypes.c_double),
+        ("cost_b", ctypes.c_double),
     ]
 
 
@@ -57,6 +59,7 @@ PARAMS_EXACT = 0
 PARAMS_FAST = 1
 S_RULE_CUBE_ROOT = 0
 S_RULE_COST_MODEL = 1
+S_RULE_MI355X = 2
 
 
 class Params(ctypes.Structure):

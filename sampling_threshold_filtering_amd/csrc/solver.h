@@ -17,7 +17,7 @@ double normal_upper_quantile(double q);
 // Phi^-1(p) by Acklam's rational approximation.
 double acklam_inv_phi(double p);
 // 1 / r(k) of the cost model (0 when r is infinite).
-double cost_ratio_inverse(int64_t k);
+double cost_ratio_inverse(int64_t k, double a, double b);
 
 int solve(int64_t N, int64_t k, double eps, const profk_options* opt, profk_params* out);
 int solve_memo(int64_t N, int64_t k, double eps, const profk_options* opt, profk_params* out);

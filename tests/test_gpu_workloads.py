@@ -23,6 +23,10 @@ from workloads import SAE_COLS, generate, sae_pool
 
 pytestmark = pytest.mark.gpu
 
+# sample-size rules: the (k N)^(1/3) default, and Algorithm 1 with the ratio measured on
+# MI355X (the one bench.py times); S changes the work, never the result
+RULES = [0, 2]
+
 
 def dev(a):
     import torch
@@ -43,23 +47,25 @@ def check(x_np, vals, idx, k, nthreads=16):
     np.testing.assert_array_equal(host(vals).view(np.uint32), ov.view(np.uint32))
 
 
+@pytest.mark.parametrize("rule", RULES)
 @pytest.mark.parametrize("kind", ["normal", "uniform"])
-def test_2p26_k_sweep(kind):
+def test_2p26_k_sweep(kind, rule):
     x = generate(kind, 1 << 26, seed=0)
     xd = dev(x)
     for k in (32, 1024, 32768):
-        say("2^26", kind, k)
-        vals, idx, st = stf.topk(xd, k, eps=1e-3, seed=0, stats=True)
+        say("2^26", kind, k, "rule", rule)
+        vals, idx, st = stf.topk(xd, k, eps=1e-3, seed=0, stats=True, options={"s_rule": rule})
         check(x, vals, idx, k)
         assert not st["fallback"]
 
 
-def test_sae_pool():
-    say("sae 4096 x 12288, k = 131072")
+@pytest.mark.parametrize("rule", RULES)
+def test_sae_pool(rule):
+    say("sae 4096 x 12288, k = 131072, rule", rule)
     pool = sae_pool(0)
     x = pool.reshape(-1)
     k = 32 * 4096
-    vals, idx, st = stf.topk(dev(x), k, eps=1e-3, seed=0, stats=True)
+    vals, idx, st = stf.topk(dev(x), k, eps=1e-3, seed=0, stats=True, options={"s_rule": rule})
     check(x, vals, idx, k)
     i = host(idx)
     rows, latents = i // SAE_COLS, i % SAE_COLS
@@ -72,33 +78,36 @@ def pareto_2p30():
     return generate("pareto", 1 << 30, seed=0)
 
 
-def test_pareto_2p30_k_sweep(pareto_2p30):
+@pytest.mark.parametrize("rule", RULES)
+def test_pareto_2p30_k_sweep(pareto_2p30, rule):
     x = pareto_2p30
     xd = dev(x)
     for k in (1 << 5, 1 << 10, 1 << 15, 1 << 19):
-        say("pareto 2^30", k)
-        vals, idx, st = stf.topk(xd, k, eps=1e-3, seed=0, stats=True)
+        say("pareto 2^30", k, "rule", rule)
+        vals, idx, st = stf.topk(xd, k, eps=1e-3, seed=0, stats=True, options={"s_rule": rule, "timing": 1})
         check(x, vals, idx, k)
         assert not st["fallback"]
     del xd
 
 
-def test_pareto_batched_1024_rows(pareto_2p30):
-    say("pareto batched 1024 x 2^20, k = 64")
+@pytest.mark.parametrize("rule", RULES)
+def test_pareto_batched_1024_rows(pareto_2p30, rule):
+    say("pareto batched 1024 x 2^20, k = 64, rule", rule)
     x = pareto_2p30.reshape(1024, 1 << 20)
-    vals, idx = stf.topk_batched(dev(x), 64, eps=1e-3, seed=0)
+    vals, idx = stf.topk_batched(dev(x), 64, eps=1e-3, seed=0, options={"s_rule": rule})
     ov, oi = oracle.topk_batched(x, 64, nthreads=16)
     np.testing.assert_array_equal(host(idx), oi)
     np.testing.assert_array_equal(host(vals).view(np.uint32), ov.view(np.uint32))
 
 
+@pytest.mark.parametrize("rule", RULES)
 @pytest.mark.parametrize("kind", ["adv_levels", "adv_noise"])
-def test_adversarial_2p30(kind):
+def test_adversarial_2p30(kind, rule):
     x = generate(kind, 1 << 30, seed=0)
     xd = dev(x)
     k = 1 << 19
-    say("adversarial 2^30", kind, k)
-    vals, idx, st = stf.topk(xd, k, eps=1e-4, seed=0, stats=True)
+    say("adversarial 2^30", kind, k, "rule", rule)
+    vals, idx, st = stf.topk(xd, k, eps=1e-4, seed=0, stats=True, options={"s_rule": rule})
     check(x, vals, idx, k)
     if kind == "adv_levels":
         say("adversarial 2^30 forced overflow M = k")
@@ -127,20 +136,22 @@ def test_threshold_rank_moments_on_gpu():
     assert abs(R.var() - var) <= 5 * math.sqrt(max(m4 - var * var, 0.0) / n)
 
 
-def test_retry_rate_matches_exact_prediction():
+@pytest.mark.parametrize("rule", RULES)
+def test_retry_rate_matches_exact_prediction(rule):
     # first-attempt failures over 10^4 seeds: at most the 0.999 quantile of
     # Binomial(n, p_pred), split into R < k and R > M
     N, k, eps = 1 << 22, 32, 1e-3
     x = generate("uniform", N, seed=0)
     xd = dev(x)
-    p = stf.solve(N, k, eps)
+    o = {"s_rule": rule}
+    p = stf.solve(N, k, eps, options=o)
     p_pred = p["p_recall"] + p["p_overflow"]
     assert p_pred <= eps
     n = 10000
     fails = {1: 0, 2: 0}
-    say("retry rate", N, k, n)
+    say("retry rate", N, k, n, "rule", rule, "S", p["S"])
     for seed in range(n):
-        vals, idx, st = stf.topk(xd, k, eps=eps, seed=seed, stats=True)
+        vals, idx, st = stf.topk(xd, k, eps=eps, seed=seed, stats=True, options=o)
         if st["fail_mode"][0]:
             fails[st["fail_mode"][0]] += 1
     total = fails[1] + fails[2]

@@ -140,6 +140,43 @@ def test_cost_model_rule_matches_table3_sample_sizes(golden_dir):
                 assert (p["t_star"], p["M_star"]) == (r["t_star"], r["M_star"]), r
 
 
+@pytest.mark.parametrize("a,b", [(0.594, 4.29), (0.25, 1.5), (1.2, 6.0), (0.05, 0.2)])
+def test_cost_model_rule_takes_the_given_cost_ratio(a, b):
+    """The cost-model S rule with explicit 1/r(k) = a log2 k - b coefficients against
+    Proposition 7 as the oracle writes it, over the workload grid; the page's own
+    coefficients are what zero selects."""
+    for N in (1 << 22, 1 << 26, 1 << 30, 50331648):
+        for k in (32, 200, 1 << 11, 1 << 14, 1 << 17, 1 << 19):
+            if k > N:
+                continue
+            o = stf.make_options(s_rule=stf.S_RULE_COST_MODEL, cost_a=a, cost_b=b)
+            assert stf.solve(N, k, 1e-3, options=o)["S"] == solver_ref.s_rule_cost_model(N, k, 1e-3, a=a, b=b)
+    o0 = stf.make_options(s_rule=stf.S_RULE_COST_MODEL)
+    o1 = stf.make_options(s_rule=stf.S_RULE_COST_MODEL, cost_a=0.594, cost_b=4.29)
+    for k in (1 << 8, 1 << 14, 1 << 19):
+        assert stf.solve(1 << 30, k, 1e-3, options=o0)["S"] == stf.solve(1 << 30, k, 1e-3, options=o1)["S"]
+
+
+def test_mi355x_rule_is_proposition_7_with_the_measured_ratio():
+    """The MI355X S rule: Algorithm 1 lines 1-4 with one constant 1/r, clipped to
+    [2^12, 2^17], against the oracle's Proposition 7; S only changes speed, so the
+    exact (t*, M*) for that S must match the oracle too."""
+    for N in (1 << 22, 1 << 24, 1 << 26, 1 << 28, 1 << 30, 50331648, (1 << 32) - 1):
+        for k in (32, 1024, 1 << 15, 1 << 17, 1 << 19):
+            if k > N:
+                continue
+            o = stf.make_options(s_rule=stf.S_RULE_MI355X)
+            p = stf.solve(N, k, 1e-3, options=o)
+            S = solver_ref.s_rule_mi355x(N, k, 1e-3)
+            assert p["S"] == S, (N, k)
+            assert 1 << 12 <= S <= 1 << 17 or S == N // 128
+    # one full exact pair at a small sample: the Theorem 4 pair for the rule's S
+    o = stf.make_options(s_rule=stf.S_RULE_MI355X)
+    p = stf.solve(1 << 30, 32, 1e-3, options=o)
+    ref = solver_ref.solve(1 << 30, 32, 1e-3, S=p["S"])
+    assert (p["t"], p["M"]) == (ref.t, ref.M)
+
+
 def test_fast_mode_quantile_is_acklam_accurate():
     """The rational approximation of Phi^-1 (relative error below 1.15e-9) against
     scipy's quantile, over budgets that reach both of its branches."""
