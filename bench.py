@@ -20,6 +20,7 @@ Also printed (same JSON line):
                launch / its launch time from HIP events recorded by the library
                around the filter on the same stream; peak 8 TB/s
   batched      1024 rows x 2^20, top-64 per row (same tensor, reshaped)
+  large        N = 4.3e9 (beyond 32-bit indexing), k in {2^10, 2^18, 2^22}
   cpu_baseline the CPU oracle (plain C heap top-k) on a bounded sample
 """
 from __future__ import annotations
@@ -55,6 +56,7 @@ def parse():
                          "MI355X (default here)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-batched", action="store_true", help="skip the batched variant")
+    ap.add_argument("--no-large", action="store_true", help="skip the N = 4.3e9 (beyond 2^32) measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--calibrate-s", metavar="OUT_JSON",
@@ -325,6 +327,44 @@ def calibrate_s(path: str, calls: int = CAL_CALLS):
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
 
+LARGE_N = 4_300_000_000
+LARGE_KS = (1 << 10, 1 << 18, 1 << 22)
+
+
+def bench_large(stf, torch, dev, stream, args, opts):
+    """Inputs beyond 2^32 values (the page's Table 4: N = 4.3e9, k = 2^10, 2^18, 2^22):
+    standard normal fp32 drawn on the device by torch's seeded generator (seed 0),
+    exact top-k through the segmented path, mean call time over the timed calls."""
+    free = torch.cuda.mem_get_info(dev)[0]
+    if free < 4 * LARGE_N + (2 << 30):
+        return None
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    x = torch.randn(LARGE_N, dtype=torch.float32, device=dev, generator=gen)
+    res = {"N": LARGE_N, "input": "standard normal fp32, torch.randn on the device, seed 0"}
+    for k in LARGE_KS:
+        out = (torch.empty(k, dtype=torch.float32, device=dev), torch.empty(k, dtype=torch.int64, device=dev))
+        for _ in range(max(1, args.warmup)):
+            stf.topk(x, k, eps=EPS, seed=0, options=opts, out=out)
+        torch.cuda.synchronize()
+        n = max(1, args.steps // 2)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(n):
+            _, _, st = stf.topk(x, k, eps=EPS, seed=s, options=opts, out=out, stats=True)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        res[str(k)] = {"ms": round(ms, 4), "gelem_s": round(LARGE_N / ms / 1e6, 2),
+                       "frac_of_hbm_peak": round(4.0 * LARGE_N / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                       "segments": st["segments"]}
+    del x
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -435,6 +475,8 @@ def main():
                    "gelem_s": round((B << 20) / bms / 1e6, 2),
                    "S_per_row": stf.solve(1 << 20, 64, EPS / B, options=bopts)["S"]}
 
+    large = None if args.no_large else bench_large(stf, torch, dev, stream, args, opts)
+
     cpu = None if args.no_cpu else cpu_baseline(x)
 
     value = len(KS) * N / (total_ms / 1e3) / 1e9
@@ -461,6 +503,7 @@ def main():
         "retries": retries,
         "roofline": roofline,
         "batched": batched,
+        "large": large,
         "cpu_baseline": cpu,
         "host_gen_s": round(gen_s, 2),
     }

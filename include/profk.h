@@ -35,8 +35,11 @@
  * the ABI.  profk_strerror() gives a message (HIP errors include the HIP
  * error string of the failing call, kept per thread).
  *
- * Limits.  N < 2^32 per row (indices are 32-bit inside the keys);
- * N >= 2^32 returns PROFK_EUNSUPPORTED.
+ * Limits.  Indices are 32-bit inside the keys.  profk_topk / profk_topk_ex
+ * take N >= 2^32 (up to about 2^38) by cutting x into segments of fewer than
+ * 2^32 values and merging their exact top-k lists (P1 App. D, Table 4);
+ * profk_topk_approx, the batched form, the stage entry points and
+ * profk_solve return PROFK_EUNSUPPORTED for N >= 2^32 per row.
  */
 #ifndef PROFK_H
 #define PROFK_H
@@ -49,7 +52,7 @@ extern "C" {
 
 #define PROFK_OK 0
 #define PROFK_EINVAL (-1)       /* bad argument (null pointer, k < 1, k > N, eps outside (0,1), ld < N ...) */
-#define PROFK_EUNSUPPORTED (-2) /* N >= 2^32 per row */
+#define PROFK_EUNSUPPORTED (-2) /* N >= 2^32 per row where not supported (see Limits) */
 #define PROFK_ENOMEM (-3)       /* workspace allocation failed */
 #define PROFK_EHIP (-4)         /* a HIP runtime call failed */
 #define PROFK_EINTERNAL (-5)    /* a device-side consistency check failed */
@@ -120,13 +123,17 @@ typedef struct profk_stats {
   int64_t rows_fallback;  /* batched: rows finished by the exact full selection */
   int64_t refine_multipass; /* attempts whose refinement needed the multi-pass radix select
                                (a value bin too large for one workgroup: ties, narrow ranges) */
+  int64_t segments;       /* N >= 2^32: segments the input was cut into (0 otherwise); the
+                             fields above are then segment 0's, except attempts (the most of
+                             any segment), fallback (any), refine_multipass and filter_ms
+                             (summed over segments) */
 } profk_stats;
 
 /*
  * profk_topk: exact top-k of one flat fp32 tensor x[0..N) (P1 §3, Algorithm
  * "The Prof-K Algorithm", stages 1-4, with the retry of stage 4).
  *   x        device, N floats, any alignment
- *   N        1 <= N < 2^32
+ *   N        1 <= N; N >= 2^32 takes the segmented path (see Limits)
  *   k        1 <= k <= N
  *   eps      failure budget per attempt, 0 < eps < 1 (P1 §4 Theorem 4)
  *   seed     64-bit seed of the sampler's Philox stream; attempt a uses

@@ -81,7 +81,7 @@ class Stats(ctypes.Structure):
         ("R", ctypes.c_int64 * STATS_ATTEMPTS), ("fail_mode", ctypes.c_int32 * STATS_ATTEMPTS),
         ("workspace_bytes", ctypes.c_uint64), ("filter_ms", ctypes.c_double),
         ("rows_retried", ctypes.c_int64), ("rows_fallback", ctypes.c_int64),
-        ("refine_multipass", ctypes.c_int64),
+        ("refine_multipass", ctypes.c_int64), ("segments", ctypes.c_int64),
     ]
 
 
@@ -156,7 +156,7 @@ def stats_to_dict(st: Stats) -> dict:
                 R=[st.R[i] for i in range(n)], fail_mode=[st.fail_mode[i] for i in range(n)],
                 workspace_bytes=st.workspace_bytes, filter_ms=st.filter_ms,
                 rows_retried=st.rows_retried, rows_fallback=st.rows_fallback,
-                refine_multipass=st.refine_multipass)
+                refine_multipass=st.refine_multipass, segments=st.segments)
 
 
 def _stream_ptr(torch, device):

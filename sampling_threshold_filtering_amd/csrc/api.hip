@@ -127,6 +127,8 @@ struct Workspace {
   // nonzero (an error between launches); the next call then clears them first.
   bool dirty = false;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  char* seg = nullptr;  // per-segment top-k lists of inputs of 2^32 values or more
+  size_t seg_bytes = 0;
 };
 
 std::mutex g_ws_mu;
@@ -265,13 +267,25 @@ SampleArgs sample_args(Workspace* w, const Layout& L, const float* x, u64 N, u64
   return a;
 }
 
-int validate(const float* x, int64_t N, int64_t k, double eps, const void* ov, const void* oi) {
+int validate_args(const float* x, int64_t N, int64_t k, double eps, const void* ov, const void* oi) {
   if (!x || !ov || !oi) return PROFK_EINVAL;
   if (N < 1 || k < 1 || k > N) return PROFK_EINVAL;
   if (!(eps > 0.0 && eps < 1.0)) return PROFK_EINVAL;
+  return PROFK_OK;
+}
+
+// Rows of fewer than 2^32 values (the 32-bit index inside the keys).
+int validate(const float* x, int64_t N, int64_t k, double eps, const void* ov, const void* oi) {
+  const int rc = validate_args(x, N, k, eps, ov, oi);
+  if (rc) return rc;
   if (N >= (int64_t(1) << 32)) return PROFK_EUNSUPPORTED;
   return PROFK_OK;
 }
+
+// Inputs of 2^32 values or more are cut into segments of at most kSegMax values (a
+// multiple of 64, so every segment starts on the 16-byte phase of x).
+constexpr u64 kSegMax = (1ull << 32) - 64;
+constexpr u64 kMaxSegmentedN = kSegMax * kMaxSegments;  // about 2^38 values (1 TiB of fp32)
 
 int max_attempts_of(const profk_options* opt) {
   if (opt && opt->force_fallback) return 0;
@@ -447,6 +461,87 @@ int topk_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* out_vals
   }
   if (st) st->fallback = 1;
   return run_exact(w, L, x, N, k, out_vals, out_idx, s);
+}
+
+// Device buffer for the per-segment lists, cached with the (device, stream) workspace.
+int get_segment_buffer(hipStream_t s, size_t bytes, char** out) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev), "hipGetDevice");
+  std::lock_guard<std::mutex> g(g_ws_mu);
+  Workspace*& w = g_ws[std::make_pair(dev, s)];
+  if (!w) {
+    w = new Workspace();
+    w->device = dev;
+    w->stream = s;
+  }
+  if (w->seg_bytes < bytes) {
+    if (w->seg) {
+      HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+      HIPCHK(hipFree(w->seg), "hipFree");
+      w->seg = nullptr;
+      w->seg_bytes = 0;
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      t_err = "segment buffer allocation failed";
+      return PROFK_ENOMEM;
+    }
+    w->seg = (char*)p;
+    w->seg_bytes = bytes;
+  }
+  *out = w->seg;
+  return PROFK_OK;
+}
+
+// Exact top-k of an input of 2^32 values or more (P1 App. D, Table 4): G contiguous
+// segments of fewer than 2^32 values, each an exact top-k of its own (the sampled
+// path, budget eps / G, so that a retry anywhere in the call stays within eps), into
+// G sorted lists; the global top-k lies in their union and one merge launch takes it.
+// The segments together read the input once.
+int topk_segmented(const float* x, u64 N, u64 k, double eps, u64 seed, float* out_vals, int64_t* out_idx,
+                   hipStream_t s, const profk_options* opt, profk_stats* st) {
+  if (N > kMaxSegmentedN) {
+    t_err = "input longer than the segmented path supports";
+    return PROFK_EUNSUPPORTED;
+  }
+  const u64 G = (N + kSegMax - 1) / kSegMax;
+  const u64 seg = (((N + G - 1) / G) + 63) & ~63ull;  // <= kSegMax; (G - 1) seg < N
+  const size_t vbytes = align256(G * k * sizeof(float));
+  char* buf = nullptr;
+  int rc = get_segment_buffer(s, vbytes + G * k * sizeof(int64_t), &buf);
+  if (rc) return rc;
+  SegmentLists L{};
+  L.vals = reinterpret_cast<float*>(buf);
+  L.idx = reinterpret_cast<int64_t*>(buf + vbytes);
+  L.stride = k;
+  L.k = k;
+  L.G = (u32)G;
+  for (u64 g = 0; g < G; ++g) {
+    const u64 base = g * seg;
+    const u64 len = base + seg <= N ? seg : N - base;
+    const u64 kg = k < len ? k : len;
+    L.len[g] = kg;
+    L.base[g] = base;
+    profk_stats gs{};
+    rc = topk_row(x + base, len, kg, eps / (double)G, seed ^ (0x9E3779B97F4A7C15ull * (g + 1)),
+                  const_cast<float*>(L.vals) + g * k, const_cast<int64_t*>(L.idx) + g * k, s, opt,
+                  st ? &gs : nullptr);
+    if (rc) return rc;
+    if (!st) continue;
+    if (g == 0) {
+      *st = gs;
+      continue;
+    }
+    if (gs.attempts > st->attempts) st->attempts = gs.attempts;
+    st->fallback |= gs.fallback;
+    st->refine_multipass += gs.refine_multipass;
+    st->filter_ms += gs.filter_ms;
+    if (gs.workspace_bytes > st->workspace_bytes) st->workspace_bytes = gs.workspace_bytes;
+  }
+  if (st) st->segments = (int64_t)G;
+  HIPCHK(launch_merge_segments(L, out_vals, out_idx, s), "launch merge_segments");
+  return PROFK_OK;
 }
 
 // Approximate mode: one sampled attempt, everything enqueued on the stream, no host
@@ -631,9 +726,11 @@ int profk_solve(int64_t N, int64_t k, double eps, const profk_options* opt, prof
 
 int profk_topk_ex(const float* x, int64_t N, int64_t k, double eps, uint64_t seed, float* out_vals,
                   int64_t* out_idx, void* stream, const profk_options* opt, profk_stats* st) {
-  int rc = validate(x, N, k, eps, out_vals, out_idx);
+  int rc = validate_args(x, N, k, eps, out_vals, out_idx);
   if (rc) return rc;
   if (st) std::memset(st, 0, sizeof(*st));
+  if (N >= (int64_t(1) << 32))
+    return topk_segmented(x, (u64)N, (u64)k, eps, seed, out_vals, out_idx, (hipStream_t)stream, opt, st);
   return topk_row(x, (u64)N, (u64)k, eps, seed, out_vals, out_idx, (hipStream_t)stream, opt, st);
 }
 
@@ -781,7 +878,7 @@ const char* profk_strerror(int code) {
     case PROFK_EINVAL:
       return "invalid argument";
     case PROFK_EUNSUPPORTED:
-      return "unsupported size (N >= 2^32 per row)";
+      return "unsupported size (N >= 2^32 outside profk_topk / profk_topk_ex, or beyond their limit)";
     case PROFK_ENOMEM:
       return "device workspace allocation failed";
     case PROFK_EHIP:
@@ -808,6 +905,10 @@ void profk_release(void) {
     if (w->host) (void)hipHostFree(w->host);
     if (w->host_rows) (void)hipHostFree(w->host_rows);
     if (w->hrec) (void)hipHostFree(w->hrec);
+    if (w->seg) {
+      (void)hipStreamSynchronize(w->stream);
+      (void)hipFree(w->seg);
+    }
     if (w->ev0) (void)hipEventDestroy(w->ev0);
     if (w->ev1) (void)hipEventDestroy(w->ev1);
     (void)hipSetDevice(cur);

@@ -160,6 +160,19 @@ hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s);
 hipError_t launch_b_refine(const BatchedArgs& a, hipStream_t s);
 hipError_t launch_b_rowsort(const BatchedArgs& a, hipStream_t s);
 
+// Inputs of 2^32 values or more (k_merge.hip): G sorted per-segment top-k lists.
+constexpr u32 kMaxSegments = 64;
+struct SegmentLists {
+  const float* vals;         // list g at vals + g * stride, sorted by the total order
+  const int64_t* idx;        // indices inside segment g, same layout
+  u64 stride;                // = k
+  u64 k;                     // outputs wanted
+  u32 G;                     // lists
+  u64 len[kMaxSegments];     // entries of list g (min(k, segment length))
+  u64 base[kMaxSegments];    // first global index of segment g
+};
+hipError_t launch_merge_segments(const SegmentLists& L, float* out_vals, int64_t* out_idx, hipStream_t s);
+
 hipError_t launch_sort_and_write(u64* buf0, u64* buf1, u32* hist, u32 k, const float* row, u64 N, float* out_vals,
                                  int64_t* out_idx, RowCtl* ctl, AttemptRecord* rec, hipStream_t s);
 u64 sort_hist_words(u64 k);

@@ -132,3 +132,18 @@ def test_bad_arguments_rejected():
         oracle.topk(x, 5)
     with pytest.raises(ValueError):
         oracle.topk(x, 0)
+
+
+def test_indices_beyond_2p32():
+    """64-bit indices: planted values past 2^32 in an otherwise zero input (the
+    zero pages are shared, so the 17 GB array costs little memory); the expected
+    order is written out from the definition."""
+    N = (1 << 32) + 1000
+    x = np.zeros(N, dtype=np.float32)
+    x[(1 << 32) + 999] = 5.0
+    x[1 << 32] = 4.0
+    x[3] = 4.0
+    x[1 << 31] = -1.0
+    v, i = oracle.topk(x, 5, nthreads=8)
+    np.testing.assert_array_equal(i, np.array([(1 << 32) + 999, 3, 1 << 32, 0, 1], dtype=np.int64))
+    np.testing.assert_array_equal(v, np.array([5.0, 4.0, 4.0, 0.0, 0.0], dtype=np.float32))
