@@ -7,7 +7,7 @@
 // no second pass (App. C).
 //
 // gfx950 design (the page's Triton kernel is prior art for another GPU):
-//   * Work unit: a wave-tile of 64 lanes x U float4 (U = 8: 2048 values, 8 KB)
+//   * Work unit: a wave-tile of 64 lanes x U float4 (U = 4: 1024 values, 4 KB)
 //     read with dwordx4 loads; wavefronts stride over the wave-tiles of all rows.
 //   * Fast pre-test per value: !(x < tau_value), one float compare.  Only a
 //     wavefront whose tile has a hit evaluates the exact key test
@@ -397,7 +397,12 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
 
 hipError_t launch_filter(const FilterArgs& a0, u32 grid, hipStream_t s) {
   FilterArgs a = a0;
-  constexpr int U = 8;
+  // Wave-tiles of 4 float4 per lane (1024 values, 4 KB), three blocks of four
+  // wavefronts per CU.  Measured on MI355X over 2^30 values (sweep of U = 4..16 and 1..8
+  // blocks per CU): the per-CU bytes in flight matter more than the shape, and more
+  // wavefronts hold the rate when many tiles carry hits (large k, batched rows), where a
+  // wavefront spends longer testing between its loads.
+  constexpr int U = 4;
   const u64 vec_per_tile = (u64)U * kWave;
   const u64 max_vec = (a.N >> 2) + 1;
   a.tiles_per_row = (max_vec + vec_per_tile - 1) / vec_per_tile;

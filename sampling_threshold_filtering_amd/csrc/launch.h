@@ -7,7 +7,7 @@ namespace profk {
 
 constexpr u32 kSmallSort = 8192;  // keys sorted by one workgroup in LDS (64 KB)
 constexpr u32 kTickets = 64;      // u32 tickets / counters in the workspace; each user leaves its own zero
-constexpr u32 kFilterBlocksPerCU = 2;  // persistent filter grid: 2 blocks x 4 waves per CU
+constexpr u32 kFilterBlocksPerCU = 3;  // persistent filter grid: 3 blocks x 4 waves per CU
 constexpr u64 kFilterRun = 64;         // consecutive tiles per chunk when there are several rows
 
 // Compute units of the current device (cached per device).
