@@ -88,7 +88,7 @@ Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap, 
   L.ctl = take(rows * sizeof(RowCtl));
   L.sel = take(rows * sizeof(SelState));
   L.rec = take(rows * sizeof(AttemptRecord));
-  L.ticket = take(kTickets * sizeof(u32));
+  L.ticket = take(kTicketWords * sizeof(u32));
   L.rhist = take(kBins * sizeof(u32));
   L.rbin_off = take(kBins * sizeof(u32));
   L.rbin_cnt = take(kBins * sizeof(u32));
@@ -259,8 +259,7 @@ SampleArgs sample_args(Workspace* w, const Layout& L, const float* x, u64 N, u64
   a.tops = at<u64>(w, L.tops);
   a.ctl = at<RowCtl>(w, L.ctl);
   a.rec = nullptr;
-  a.ticket = at<u32>(w, L.ticket) + kTicketSample;
-  a.dcount = at<u32>(w, L.ticket) + kCountSample;
+  a.ticket = reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kTicketSample);
   a.top_hist = at<SelState>(w, L.sel)->hist;
   a.t = t;
   a.fast = (t >= 1 && t <= kTopT && sample_blocks(S) <= kTopBlocks) ? 1u : 0u;
@@ -358,6 +357,7 @@ FilterArgs flat_filter_args(Workspace* w, const Layout& L, const float* x, u64 N
   fa.M = M;
   fa.k = k;
   fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
+  fa.groups = at<u32>(w, L.ticket) + kTickets;
   fa.rec = at<AttemptRecord>(w, L.rec);
   fa.sels = at<SelState>(w, L.sel);
   return fa;
@@ -666,6 +666,7 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     fa.M = M;
     fa.k = k;
     fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
+      fa.groups = at<u32>(w, L.ticket) + kTickets;
     fa.rec = rec;
     fa.sels = nullptr;
     HIPCHK(launch_filter(fa, 0, s), "launch filter");
@@ -861,6 +862,7 @@ int profk_stage_filter(const float* x, int64_t N, float tau_val, int64_t tau_idx
   fa.M = (u64)M;
   fa.k = 1;
   fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
+  fa.groups = at<u32>(w, L.ticket) + kTickets;
   fa.rec = nullptr;
   fa.sels = nullptr;
   HIPCHK(launch_filter(fa, 0, s), "launch filter");

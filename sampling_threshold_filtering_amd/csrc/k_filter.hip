@@ -364,8 +364,22 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   // Every R update above and in stage_flush is an atomic whose result was consumed
   // before this block's ticket, so the counts are complete when the last ticket is
   // drawn; no release fence (an L2 write-back on this part) is needed per block.
+  // The ticket has two levels: block b counts into group b mod G, and the block that
+  // completes its group counts into the single ticket, so that no one counter takes
+  // an atomic from every block when all blocks end at once (short inputs).
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(a.ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
+  if (threadIdx.x == 0) {
+    const u32 ng = gridDim.x < kFilterGroups ? gridDim.x : kFilterGroups;
+    const u32 g = blockIdx.x % ng;
+    const u32 gsize = (gridDim.x - g + ng - 1) / ng;  // blocks b with b mod ng = g
+    u32 last = 0;
+    u32* gc = a.groups + (u64)g * kFilterGroupStride;
+    if (atomicAdd(gc, 1u) == gsize - 1) {
+      atomic_store_agent(gc, 0u);  // every block of the group has counted: left zero
+      last = atomicAdd(a.ticket, 1u) == ng - 1 ? 1u : 0u;
+    }
+    s_last = last;
+  }
   __syncthreads();
   if (!s_last) return;
   __threadfence();
@@ -392,7 +406,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
       s->ncol = 0;
     }
   }
-  if (threadIdx.x == 0) *a.ticket = 0;
+  if (threadIdx.x == 0) atomic_store_agent(a.ticket, 0u);
 }
 
 hipError_t launch_filter(const FilterArgs& a0, u32 grid, hipStream_t s) {

@@ -14,6 +14,7 @@
 //                   j keeps its key in keys[j], or 0 when it repeats an earlier draw
 //                   (no valid key is 0).  For t <= kTopT each block also sorts its
 //                   wavefronts' keys in registers and stores its own t largest keys.
+//                   Each block adds itself and its distinct draws to one 64-bit ticket.
 //                   The last block (a) tops up: while fewer than S distinct indices
 //                   are held, wavefront 0 takes further draws S, S+1, ... in order,
 //                   64 at a time, keeping those that are new and not repeated earlier
@@ -69,7 +70,8 @@ __device__ bool hash_contains(const u32* table, u64 tmask, u32 idx) {
 // included) so that nothing depends on what the workspace held before.
 __global__ __launch_bounds__(1024) void attempt_init_kernel(RowCtl* ctl, SelState* sel, AttemptRecord* rec,
                                                           u32* tickets, u32 nrows, u32* refine_hist) {
-  if (tickets && threadIdx.x < kTickets) tickets[threadIdx.x] = 0;
+  if (tickets)
+    for (u32 i = threadIdx.x; i < kTicketWords; i += blockDim.x) tickets[i] = 0;
   if (refine_hist)
     for (u32 b = threadIdx.x; b < kBins; b += blockDim.x) refine_hist[b] = 0;
   if (sel)
@@ -132,11 +134,6 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
     if (lane < T) s_buf[wid * T + lane] = key;  // this wavefront's T largest (0-padded)
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    u32 tot = 0;
-    for (u32 w = 0; w < kSampleWaves; ++w) tot += s_wcnt[w];
-    if (tot) atomicAdd(a.dcount, tot);
-  }
   if (use_hist) {
     // histogram of the top 8 bits: the first digit of the radix select
     wave_hist_add(s_sel.hist, (u32)(key >> 56), fresh);
@@ -147,21 +144,22 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
     block_merge_lists(s_buf, kSampleWaves, T);  // the block's T largest keys
     for (u32 i = threadIdx.x; i < T; i += blockDim.x) a.tops[(u64)blockIdx.x * T + i] = s_buf[i];
   }
-  // release this block's keys and lists, then elect the last block
+  // release this block's keys and lists, then elect the last block: one atomic adds
+  // the block to the ticket and its distinct draws to the count, so the last block
+  // has the total from the atomic's return value
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
-    s_last = (atomicAdd(a.ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
+    u32 tot = 0;
+    for (u32 w = 0; w < kSampleWaves; ++w) tot += s_wcnt[w];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const u64 old = atomicAdd(a.ticket, (1ull << 32) | (u64)tot);
+    const bool last = (u32)(old >> 32) == gridDim.x - 1;
+    s_last = last ? 1u : 0u;
+    s_D = (u64)(u32)old + tot;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
-
-  if (threadIdx.x == 0) {
-    s_D = atomic_load_agent(a.dcount);
-    *a.dcount = 0;  // left zero for the next launch
-  }
-  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   // top-up by wavefront 0
   if (wid == 0) {
     const u64 D = s_D;
@@ -283,7 +281,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
       a.rec->error = 0;
       a.rec->generic = 0;
     }
-    *a.ticket = 0;
+    *a.ticket = 0ull;
   }
 }
 
@@ -292,7 +290,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
 __global__ void clear_sample_kernel(u32* table, u64 slots, u32* tickets) {
   const u64 gs = (u64)gridDim.x * blockDim.x;
   for (u64 i = (u64)blockIdx.x * blockDim.x + threadIdx.x; i < slots; i += gs) table[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x < kTickets) tickets[threadIdx.x] = 0;
+  if (blockIdx.x == 0)
+    for (u32 i = threadIdx.x; i < kTicketWords; i += blockDim.x) tickets[i] = 0;
 }
 
 // Indices of the nonzero keys among keys[0 .. min(*n_ptr, n_cap)), appended in any order.
@@ -331,7 +330,8 @@ __global__ void tau_to_output_kernel(const float* __restrict__ x, u64 N, const R
 }
 
 __global__ void set_tau_kernel(RowCtl* ctl, u32* tickets, u32 tau_bits, u32 tau_idx) {
-  if (blockIdx.x == 0 && threadIdx.x < kTickets) tickets[threadIdx.x] = 0;
+  if (blockIdx.x == 0)
+    for (u32 i = threadIdx.x; i < kTicketWords; i += blockDim.x) tickets[i] = 0;
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     RowCtl c{};
     c.key_and = ~0ull;

@@ -7,6 +7,11 @@ namespace profk {
 
 constexpr u32 kSmallSort = 8192;  // keys sorted by one workgroup in LDS (64 KB)
 constexpr u32 kTickets = 64;      // u32 tickets / counters in the workspace; each user leaves its own zero
+// The filter's two-level ticket: kFilterGroups counters, each on its own 128-byte line,
+// after the tickets.  Cleared together with them.
+constexpr u32 kFilterGroups = 32;
+constexpr u32 kFilterGroupStride = 32;  // u32 words between group counters
+constexpr u32 kTicketWords = kTickets + kFilterGroups * kFilterGroupStride;
 constexpr u32 kFilterBlocksPerCU = 3;  // persistent filter grid: 3 blocks x 4 waves per CU
 constexpr u64 kFilterRun = 64;         // consecutive tiles per chunk when there are several rows
 
@@ -34,6 +39,7 @@ struct FilterArgs {
   u64 M;
   u64 k;
   u32* ticket;         // zero before the launch; left zero after it
+  u32* groups;         // kFilterGroups counters kFilterGroupStride words apart; zero, left zero
   AttemptRecord* rec;  // per row, or nullptr
   SelState* sels;      // per row refinement selection to arm, or nullptr
   u64 tiles_per_row;   // set by launch_filter
@@ -45,8 +51,8 @@ hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u
                                u32* refine_hist, hipStream_t s);
 // Stages 1-2 (k_sample.hip).  Ticket slots of the workspace's ticket array:
 constexpr u32 kTicketFilter = 0;  // filter kernel
-constexpr u32 kTicketSample = 1;  // sampling kernel
-constexpr u32 kCountSample = 3;   // distinct draws of the sampling kernel
+constexpr u32 kTicketSample = 8;  // sampling kernel: one u64 at slots 8-9 (8-byte aligned),
+                                  // (blocks done << 32) | distinct draws so far
 constexpr u32 kCountStage = 4;    // output counter of the stage entry points
 constexpr u32 kTopT = 64;         // largest t of the per-block-list threshold path
 constexpr u32 kTopBlocks = 128;   // most sampling blocks of that path (S <= 131072)
@@ -62,8 +68,7 @@ struct SampleArgs {
   u64* tops;        // per block its t largest keys (fast path), kTopBlocks * kTopT
   RowCtl* ctl;      // tau out; the per-attempt fields are reset
   AttemptRecord* rec;  // reset, or nullptr
-  u32* ticket;      // zero on entry, left zero
-  u32* dcount;      // zero on entry, left zero
+  u64* ticket;      // (blocks done << 32) | distinct draws; zero on entry, left zero
   u32* top_hist;    // 256 words, zero on entry, left zero
   u64 t;            // threshold rank (0: sample only)
   u32 fast;         // 1: per-block lists (t <= kTopT, at most kTopBlocks blocks)
