@@ -127,6 +127,9 @@ struct Workspace {
   // nonzero (an error between launches); the next call then clears them first.
   bool dirty = false;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  // Relative streaming speed of each die, from the filter's per-die times on earlier
+  // calls (moving average); the filter sizes the dies' shares of the input by it.
+  float xw[kXcds] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
   char* seg = nullptr;  // per-segment top-k lists of inputs of 2^32 values or more
   size_t seg_bytes = 0;
 };
@@ -358,9 +361,37 @@ FilterArgs flat_filter_args(Workspace* w, const Layout& L, const float* x, u64 N
   fa.k = k;
   fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
   fa.groups = at<u32>(w, L.ticket) + kTickets;
+  fa.xtime = reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kXtimeWord);
+  for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[x];
   fa.rec = at<AttemptRecord>(w, L.rec);
   fa.sels = at<SelState>(w, L.sel);
   return fa;
+}
+
+// Moving average of the dies' streaming speeds from the filter's per-die times of the
+// attempt just read back (a performance hint only: the shares never change results).
+void update_die_weights(Workspace* w, const u64* split) {
+  const u64* xt = w->hrec->xt;
+  if (xt[0] == 0) return;
+  double rate[kXcds], mean = 0.0;
+  u32 n = 0;
+  for (u32 x = 0; x < kXcds; ++x) {
+    const u64 work = split[x + 1] - split[x];
+    if (work == 0 || xt[1 + x] <= xt[0]) return;  // a die without work or without a time
+    // work on die x was in proportion to (its blocks) x (its weight), so its speed per
+    // block is in proportion to weight / time
+    rate[x] = (double)w->xw[x] / (double)(xt[1 + x] - xt[0]);
+    mean += rate[x];
+    ++n;
+  }
+  mean /= n;
+  for (u32 x = 0; x < kXcds; ++x) {
+    double v = 0.5 * (double)w->xw[x] + 0.5 * rate[x] / mean;
+    v = v < 0.5 ? 0.5 : (v > 2.0 ? 2.0 : v);
+    w->xw[x] = (float)v;
+  }
+  for (u32 x = 0; x < kXcds; ++x) w->hrec->xt[x + 1] = 0;
+  w->hrec->xt[0] = 0;
 }
 
 // One sampled attempt of one row, enqueued; returns after the record is back.
@@ -380,8 +411,11 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   sa.rec = rec;
   HIPCHK(launch_sample(sa, s), "launch sample");
   FilterArgs fa = flat_filter_args(w, L, x, N, k, M);
+  fa.hrec = w->hrec_dev;
+  fa.sparse = p.E_R * 8192.0 <= (double)N ? 1u : 0u;
+  u64 split[kXcds + 1];
   if (timing) HIPCHK(hipEventRecord(w->ev0, s), "hipEventRecord");
-  HIPCHK(launch_filter(fa, 0, s), "launch filter");
+  HIPCHK(launch_filter(fa, 0, s, split), "launch filter");
   if (timing) HIPCHK(hipEventRecord(w->ev1, s), "hipEventRecord");
   RefineArgs ra = refine_args(w, L, x, N, k, M, out_vals, out_idx);
   ra.hrec = w->hrec_dev;
@@ -393,6 +427,7 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   // launch (sorting and writing the outputs) may still run when this returns.
   rc = wait_record(w, s, ra.seq);
   if (rc) return rc;
+  if (N >= (1ull << 24)) update_die_weights(w, split);
   w->host[0].R = w->hrec->R;
   w->host[0].status = w->hrec->status;
   w->host[0].error = w->hrec->error;
@@ -570,7 +605,9 @@ int topk_approx_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* o
   SampleArgs sa = sample_args(w, L, x, N, S, t, seed, 0);
   sa.rec = at<AttemptRecord>(w, L.rec);
   HIPCHK(launch_sample(sa, s), "launch sample");
-  HIPCHK(launch_filter(flat_filter_args(w, L, x, N, k, M), 0, s), "launch filter");
+  FilterArgs fa = flat_filter_args(w, L, x, N, k, M);
+  fa.sparse = p.E_R * 8192.0 <= (double)N ? 1u : 0u;
+  HIPCHK(launch_filter(fa, 0, s), "launch filter");
   RefineArgs ra = refine_args(w, L, x, N, k, M, out_vals, out_idx);
   ra.msd_cap = 0xFFFFFFFFu;  // no host to hand an oversized bin to
   ra.approx = 1;
@@ -667,6 +704,10 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     fa.k = k;
     fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
       fa.groups = at<u32>(w, L.ticket) + kTickets;
+    fa.xtime = reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kXtimeWord);
+    for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[x];
+  fa.xtime = reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kXtimeWord);
+  for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[x];
     fa.rec = rec;
     fa.sels = nullptr;
     HIPCHK(launch_filter(fa, 0, s), "launch filter");
@@ -863,6 +904,8 @@ int profk_stage_filter(const float* x, int64_t N, float tau_val, int64_t tau_idx
   fa.k = 1;
   fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
   fa.groups = at<u32>(w, L.ticket) + kTickets;
+  fa.xtime = reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kXtimeWord);
+  for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[x];
   fa.rec = nullptr;
   fa.sels = nullptr;
   HIPCHK(launch_filter(fa, 0, s), "launch filter");

@@ -256,17 +256,31 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   const u32 lane = lane_id();
   Stage st{s_stage[wid], 0u, 0u, 0ull};
 
-  // Tile order: chunks of `run` consecutive tiles, chunk c to wavefront c mod nwaves
-  // (block-cyclic).  One row: run = 1, the wavefronts sweep the row together.
-  // Several rows: short runs keep the waves' concurrent reads close together while a
-  // wavefront changes rows (and flushes its stage) only between chunks.
-  const u64 nwaves = (u64)gridDim.x * kWavesPerBlock;
-  const u64 gw = (u64)blockIdx.x * kWavesPerBlock + wid;
+  // Tile order: chunks of `run` consecutive tiles (run = 1 for one row).  Die x (the
+  // blocks b with b mod kXcds = x, which the dispatcher places round-robin on the dies)
+  // owns the contiguous chunk range [split[x], split[x+1]) and deals it block-cyclically
+  // over its wavefronts, which sweep it together.  The dies stream at different rates
+  // on MI355X (up to 15% apart, the same dies every call), so equal shares leave the
+  // slowest die to set the end; the host sizes the ranges from the per-die stream times
+  // this kernel reports.  Several rows: short runs keep a wavefront's reads together
+  // while it changes rows (and flushes its stage) only between chunks.
+  const u32 xcd = blockIdx.x % kXcds;
+  const u64 nbx = (gridDim.x - xcd + kXcds - 1) / kXcds;      // blocks on this die
+  const u64 nwx = nbx * kWavesPerBlock;                        // their wavefronts
+  const u64 wx = (u64)(blockIdx.x / kXcds) * kWavesPerBlock + wid;
+  const u64 cend = a.split[xcd + 1];
   const u64 run = a.run, gend = a.total_tiles, tpr = a.tiles_per_row;
+  // earliest start kept as the largest complement, so that the resting value is zero
+  if (a.xtime && threadIdx.x == 0) atomicMax(&a.xtime[0], ~wall_clock64());
   struct Cursor {
     u64 g, lr, tile, in, chunk;
   };
   auto place = [&](Cursor& c) {
+    if (c.chunk >= cend) {
+      c.g = gend;
+      return;
+    }
+    c.g = c.chunk * run;
     if (a.nrows == 1) {
       c.lr = 0;
       c.tile = c.g;
@@ -285,13 +299,12 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
       }
     } else {
       c.in = 0;
-      c.chunk += nwaves;
-      c.g = c.chunk * run;
-      if (c.g < gend) place(c);
+      c.chunk += nwx;
+      place(c);
     }
   };
-  Cursor cur{gw * run, 0, 0, 0, gw};
-  if (cur.g < gend) place(cur);
+  Cursor cur{0, 0, 0, 0, a.split[xcd] + wx};
+  place(cur);
   // Software pipeline over two register sets (A, B) used in turn, so that no loaded
   // register is copied: the next tile's loads are issued before the current tile is
   // tested, and the wavefront keeps U dwordx4 loads in flight while it stages hits.
@@ -318,6 +331,10 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     load_tile<U, NT>(ta, va, oka, safe);
     test_tile<U>(a, st, tb, vb, okb);
     cur = nx;
+  }
+  if (a.xtime) {
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(&a.xtime[1 + xcd], wall_clock64());
   }
   // End of the stream: the block's waves reserve their staged keys with one
   // atomic per row they hold (one in the flat case) instead of one per wave.
@@ -406,17 +423,22 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
       s->ncol = 0;
     }
   }
-  if (threadIdx.x == 0) atomic_store_agent(a.ticket, 0u);
+  if (threadIdx.x == 0) {
+    if (a.xtime) {
+      // hand the timing to the host with the attempt record, and leave the words zero
+      for (u32 i = 0; i <= kXcds; ++i) {
+        const u64 t = atomicExch(&a.xtime[i], 0ull);
+        if (a.hrec) a.hrec->xt[i] = i == 0 ? (t ? ~t : 0ull) : t;
+      }
+    }
+    atomic_store_agent(a.ticket, 0u);
+  }
 }
 
-hipError_t launch_filter(const FilterArgs& a0, u32 grid, hipStream_t s) {
+namespace {
+template <int U>
+hipError_t launch_filter_shape(const FilterArgs& a0, u32 grid, u32 blocks_per_cu, hipStream_t s, u64* split_out) {
   FilterArgs a = a0;
-  // Wave-tiles of 4 float4 per lane (1024 values, 4 KB), three blocks of four
-  // wavefronts per CU.  Measured on MI355X over 2^30 values (sweep of U = 4..16 and 1..8
-  // blocks per CU): the per-CU bytes in flight matter more than the shape, and more
-  // wavefronts hold the rate when many tiles carry hits (large k, batched rows), where a
-  // wavefront spends longer testing between its loads.
-  constexpr int U = 4;
   const u64 vec_per_tile = (u64)U * kWave;
   const u64 max_vec = (a.N >> 2) + 1;
   a.tiles_per_row = (max_vec + vec_per_tile - 1) / vec_per_tile;
@@ -425,10 +447,42 @@ hipError_t launch_filter(const FilterArgs& a0, u32 grid, hipStream_t s) {
   a.run = a.nrows == 1 ? 1 : kFilterRun;
   u64 need = (a.total_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
   if (need < 1) need = 1;
-  if (grid == 0) grid = kFilterBlocksPerCU * device_cu_count();
+  if (grid == 0) grid = blocks_per_cu * device_cu_count();
   if ((u64)grid > need) grid = (u32)need;
+  // chunk ranges per die, in proportion to (blocks on the die) x (the die's weight)
+  const u64 nchunks = (a.total_tiles + a.run - 1) / a.run;
+  double share[kXcds], tot = 0.0;
+  for (u32 x = 0; x < kXcds; ++x) {
+    const u64 nb = grid > x ? (grid - x + kXcds - 1) / kXcds : 0;
+    const float w = a0.weight[x] > 0.f ? a0.weight[x] : 1.f;
+    share[x] = (double)nb * (double)w;
+    tot += share[x];
+  }
+  double acc = 0.0;
+  a.split[0] = 0;
+  for (u32 x = 0; x < kXcds; ++x) {
+    acc += share[x];
+    a.split[x + 1] = x + 1 == kXcds ? nchunks : (u64)((double)nchunks * acc / tot + 0.5);
+    if (a.split[x + 1] < a.split[x]) a.split[x + 1] = a.split[x];
+    if (a.split[x + 1] > nchunks) a.split[x + 1] = nchunks;
+  }
+  if (split_out)
+    for (u32 x = 0; x <= kXcds; ++x) split_out[x] = a.split[x];
   filter_kernel<U, true><<<grid, kFilterThreads, 0, s>>>(a);
   return hipGetLastError();
+}
+}  // namespace
+
+// Launch shape by the expected share of hits (measured on MI355X over 2^30 values, a
+// sweep of 4..16 float4 per lane and 1..8 blocks per CU): what matters is the bytes in
+// flight per CU.  One block of four wavefronts per CU with 8-float4 tiles streams
+// fastest while hits are rare (598 us against 617 us per 2^30 values at k = 32), but
+// a wavefront that stages hits stops issuing loads, and with one wavefront per SIMD
+// nothing covers for it (939 us at k = 2^19).  Three blocks of 4-float4 tiles keep the
+// rate when many tiles carry hits (645 us at k = 2^19, 1.0 ms for the batched rows).
+hipError_t launch_filter(const FilterArgs& a, u32 grid, hipStream_t s, u64* split_out) {
+  if (a.sparse) return launch_filter_shape<8>(a, grid, 1, s, split_out);
+  return launch_filter_shape<4>(a, grid, kFilterBlocksPerCU, s, split_out);
 }
 
 }  // namespace profk

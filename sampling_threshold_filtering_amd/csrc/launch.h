@@ -11,7 +11,8 @@ constexpr u32 kTickets = 64;      // u32 tickets / counters in the workspace; ea
 // after the tickets.  Cleared together with them.
 constexpr u32 kFilterGroups = 32;
 constexpr u32 kFilterGroupStride = 32;  // u32 words between group counters
-constexpr u32 kTicketWords = kTickets + kFilterGroups * kFilterGroupStride;
+constexpr u32 kTicketWords = kTickets + kFilterGroups * kFilterGroupStride + 32;
+constexpr u32 kXtimeWord = kTickets + kFilterGroups * kFilterGroupStride;  // u64-aligned, 2 x (kXcds + 1) words
 constexpr u32 kFilterBlocksPerCU = 3;  // persistent filter grid: 3 blocks x 4 waves per CU
 constexpr u64 kFilterRun = 64;         // consecutive tiles per chunk when there are several rows
 
@@ -40,6 +41,11 @@ struct FilterArgs {
   u64 k;
   u32* ticket;         // zero before the launch; left zero after it
   u32* groups;         // kFilterGroups counters kFilterGroupStride words apart; zero, left zero
+  u64* xtime;          // kXcds + 1 words: start (min) and per-die stream ends (max); zero, left zero
+  HostRecord* hrec;    // where the last block copies xtime for the host, or nullptr
+  u64 split[kXcds + 1];  // chunk ranges per die (set by launch_filter from weights)
+  float weight[kXcds];   // relative speed of each die (input to launch_filter; 0 = equal)
+  u32 sparse;            // 1: hits are expected in fewer than one value in 8192 (launch shape)
   AttemptRecord* rec;  // per row, or nullptr
   SelState* sels;      // per row refinement selection to arm, or nullptr
   u64 tiles_per_row;   // set by launch_filter
@@ -94,7 +100,8 @@ hipError_t launch_compact_keys(const u64* keys, const u64* n_ptr, u64 n_cap, Row
 hipError_t launch_compact_x(const float* x, u64 N, RowCtl* ctl, u64* out, u64 k, hipStream_t s);
 hipError_t launch_arm_select(SelState* st, u64 rank, u64 count, RowCtl* ctl, hipStream_t s);
 
-hipError_t launch_filter(const FilterArgs& a, u32 grid, hipStream_t s);
+// split_out (host, kXcds + 1 words, or nullptr): the per-die chunk ranges used.
+hipError_t launch_filter(const FilterArgs& a, u32 grid, hipStream_t s, u64* split_out = nullptr);
 
 // Binned refinement (k_refine.hip).
 constexpr u32 kBinBits = 14;

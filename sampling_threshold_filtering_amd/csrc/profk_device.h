@@ -332,6 +332,8 @@ struct AttemptRecord {
 // Device-side outcome of an approximate-mode call (the public profk_approx_info).
 using ApproxInfo = profk_approx_info;
 
+constexpr u32 kXcds = 8;  // accelerator complex dies of the part; blocks go round-robin over them
+
 struct HostRecord {
   u64 R;
   u32 status;
@@ -339,6 +341,9 @@ struct HostRecord {
   u32 generic;
   u32 seq;  // written last, with system-scope release
   u64 pad;
+  // the filter's stream, 100 MHz clock: [0] first block start, [1 + x] last block end of
+  // the blocks on die x (written by the filter's last block; 0 = not measured)
+  u64 xt[kXcds + 1];
 };
 
 }  // namespace profk
