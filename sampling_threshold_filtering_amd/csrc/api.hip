@@ -13,6 +13,7 @@
 // on device when the check failed, so a successful attempt costs one round trip.
 #include <immintrin.h>
 
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -231,9 +232,29 @@ int clean_if_dirty(Workspace* w, const Layout& L, hipStream_t s) {
 
 // Waits until the device has published record number `want` (spinning on the pinned
 // host word; a stream that finishes without publishing it is an error, not a hang).
-int wait_record(Workspace* w, hipStream_t s, u32 want) {
+// With early_cap: the filter's word is enough when the check failed or R <= early_cap
+// (then no value bin can exceed early_cap keys, so nothing later needs the host);
+// *early tells which record was taken.
+int wait_record(Workspace* w, hipStream_t s, u32 want, u64 early_cap = 0, bool* early = nullptr) {
   const u32* seq = &w->hrec->seq;
+  const u64* ew = &w->hrec->early;
+  if (early) *early = false;
   for (u64 it = 0;; ++it) {
+    if (early_cap) {
+      const u64 e = __atomic_load_n(ew, __ATOMIC_ACQUIRE);
+      if ((u32)(e >> 42) == (want & 0x3FFFFFu)) {
+        const u64 R = e & ((1ull << 40) - 1);
+        const u32 status = (u32)(e >> 40) & 3u;
+        if (status != 0 || R <= early_cap) {
+          w->hrec->R = R;  // the fields the caller reads (the scan's copy may follow)
+          w->hrec->status = status;
+          w->hrec->error = 0;
+          w->hrec->generic = 0;
+          *early = true;
+          return PROFK_OK;
+        }
+      }
+    }
     if (__atomic_load_n(seq, __ATOMIC_ACQUIRE) == want) return PROFK_OK;
     if ((it & 255) == 255) {
       const hipError_t q = hipStreamQuery(s);
@@ -394,6 +415,14 @@ void update_die_weights(Workspace* w, const u64* split) {
   w->hrec->xt[0] = 0;
 }
 
+// The filter's launch shape for rare hits pays off only while few tiles carry a hit; R
+// varies a lot from draw to draw at small t (exponential at t = 1), so the test takes
+// a high draw of R, E[R] + 3 sd(R), not its mean.
+u32 sparse_hits(const profk_params& p, u64 N) {
+  const double hi = p.E_R + 3.0 * std::sqrt(p.Var_R > 0.0 ? p.Var_R : 0.0);
+  return hi * 8192.0 <= (double)N ? 1u : 0u;
+}
+
 // One sampled attempt of one row, enqueued; returns after the record is back.
 int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, const profk_params& p, u64 seed,
                 u32 attempt, float* out_vals, int64_t* out_idx, hipStream_t s, bool timing, AttemptRecord* out_rec,
@@ -410,22 +439,27 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   SampleArgs sa = sample_args(w, L, x, N, S, t, seed, attempt);
   sa.rec = rec;
   HIPCHK(launch_sample(sa, s), "launch sample");
+  const u32 seq = ++w->seq;
   FilterArgs fa = flat_filter_args(w, L, x, N, k, M);
   fa.hrec = w->hrec_dev;
-  fa.sparse = p.E_R * 8192.0 <= (double)N ? 1u : 0u;
+  fa.seq = seq;
+  fa.sparse = sparse_hits(p, N);
   u64 split[kXcds + 1];
   if (timing) HIPCHK(hipEventRecord(w->ev0, s), "hipEventRecord");
   HIPCHK(launch_filter(fa, 0, s, split), "launch filter");
   if (timing) HIPCHK(hipEventRecord(w->ev1, s), "hipEventRecord");
   RefineArgs ra = refine_args(w, L, x, N, k, M, out_vals, out_idx);
   ra.hrec = w->hrec_dev;
-  ra.seq = ++w->seq;
+  ra.seq = seq;
   ra.rec = rec;
   ra.msd_cap = kMsdCapExact;
   HIPCHK(launch_refine(ra, s), "launch refine");
-  // The scan publishes the record once the check is known; the last refinement
-  // launch (sorting and writing the outputs) may still run when this returns.
-  rc = wait_record(w, s, ra.seq);
+  // The filter publishes R and the check, the scan the full record; the host needs the
+  // scan's only when a value bin may exceed the in-kernel partition's cap.  The
+  // refinement launches may still run when this returns (outputs are complete in
+  // stream order).
+  bool early = false;
+  rc = wait_record(w, s, seq, kMsdCapExact, &early);
   if (rc) return rc;
   if (N >= (1ull << 24)) update_die_weights(w, split);
   w->host[0].R = w->hrec->R;
@@ -449,6 +483,8 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   *out_rec = w->host[0];
   if (timing && filter_ms) {
     float ms = 0.f;
+    // the filter's word can arrive before its launch has completed on the stream
+    HIPCHK(hipEventSynchronize(w->ev1), "hipEventSynchronize");
     HIPCHK(hipEventElapsedTime(&ms, w->ev0, w->ev1), "hipEventElapsedTime");
     *filter_ms = ms;
   }
@@ -606,7 +642,7 @@ int topk_approx_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* o
   sa.rec = at<AttemptRecord>(w, L.rec);
   HIPCHK(launch_sample(sa, s), "launch sample");
   FilterArgs fa = flat_filter_args(w, L, x, N, k, M);
-  fa.sparse = p.E_R * 8192.0 <= (double)N ? 1u : 0u;
+  fa.sparse = sparse_hits(p, N);
   HIPCHK(launch_filter(fa, 0, s), "launch filter");
   RefineArgs ra = refine_args(w, L, x, N, k, M, out_vals, out_idx);
   ra.msd_cap = 0xFFFFFFFFu;  // no host to hand an oversized bin to

@@ -400,6 +400,13 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   __syncthreads();
   if (!s_last) return;
   __threadfence();
+  if (threadIdx.x == 0 && a.xtime) {
+    // hand the timing to the host with the attempt record, and leave the words zero
+    for (u32 i = 0; i <= kXcds; ++i) {
+      const u64 t = atomicExch(&a.xtime[i], 0ull);
+      if (a.hrec) a.hrec->xt[i] = i == 0 ? (t ? ~t : 0ull) : t;
+    }
+  }
   for (u64 lr = threadIdx.x; lr < a.nrows; lr += blockDim.x) {
     const u32 row = a.rows ? (u32)a.rows[lr] : (u32)lr;
     RowCtl* c = &a.ctls[row];
@@ -410,6 +417,11 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     if (a.rec) {
       a.rec[row].R = R;
       a.rec[row].status = status;
+    }
+    if (lr == 0 && a.hrec && a.seq) {
+      // the host learns the check here, before the refinement runs
+      const u64 word = ((u64)(a.seq & 0x3FFFFFu) << 42) | ((u64)(status & 3u) << 40) | (R & ((1ull << 40) - 1));
+      __hip_atomic_store(&a.hrec->early, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     if (a.sels) {
       SelState* s = &a.sels[row];
@@ -423,16 +435,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
       s->ncol = 0;
     }
   }
-  if (threadIdx.x == 0) {
-    if (a.xtime) {
-      // hand the timing to the host with the attempt record, and leave the words zero
-      for (u32 i = 0; i <= kXcds; ++i) {
-        const u64 t = atomicExch(&a.xtime[i], 0ull);
-        if (a.hrec) a.hrec->xt[i] = i == 0 ? (t ? ~t : 0ull) : t;
-      }
-    }
-    atomic_store_agent(a.ticket, 0u);
-  }
+  if (threadIdx.x == 0) atomic_store_agent(a.ticket, 0u);
 }
 
 namespace {

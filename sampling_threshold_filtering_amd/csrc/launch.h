@@ -43,6 +43,7 @@ struct FilterArgs {
   u32* groups;         // kFilterGroups counters kFilterGroupStride words apart; zero, left zero
   u64* xtime;          // kXcds + 1 words: start (min) and per-die stream ends (max); zero, left zero
   HostRecord* hrec;    // where the last block copies xtime for the host, or nullptr
+  u32 seq;             // with hrec: the attempt's sequence number for hrec->early (row 0)
   u64 split[kXcds + 1];  // chunk ranges per die (set by launch_filter from weights)
   float weight[kXcds];   // relative speed of each die (input to launch_filter; 0 = equal)
   u32 sparse;            // 1: hits are expected in fewer than one value in 8192 (launch shape)

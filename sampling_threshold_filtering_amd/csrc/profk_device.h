@@ -344,6 +344,9 @@ struct HostRecord {
   // the filter's stream, 100 MHz clock: [0] first block start, [1 + x] last block end of
   // the blocks on die x (written by the filter's last block; 0 = not measured)
   u64 xt[kXcds + 1];
+  // the check as soon as the filter knows it, one 64-bit word written by one store:
+  // (seq mod 2^22) << 42 | status << 40 | R  (R < 2^32)
+  u64 early;
 };
 
 }  // namespace profk

@@ -120,6 +120,9 @@ SMALL = [
     ("negative", 400000, 64, {"s_override": 8192}),
     ("ascending", 1 << 20, 100, {"s_override": 8192}),
     ("descending", 1 << 20, 100, {"s_override": 8192}),
+    # rare hits: the filter's one-block, 8-float4 launch shape (E[R] + 3 sd(R) <= N / 8192)
+    ("normal", 1 << 26, 8, {"s_override": 131072}),
+    ("normal", (1 << 24) + 13, 5, {"s_override": 65536}),
 ]
 
 
@@ -335,3 +338,12 @@ def test_rejects_bad_arguments_on_device():
         stf.topk(x, 101)
     with pytest.raises(stf.ProfkError):
         stf.topk(x, 10, eps=0.0)
+
+
+def test_rare_hit_cases_take_the_sparse_filter_shape():
+    """The last two SMALL cases are there for the filter's launch shape for rare hits;
+    keep them in its regime (the library takes it when E[R] + 3 sd(R) <= N / 8192)."""
+    import math
+    for kind, N, k, opts in SMALL[-2:]:
+        p = stf.solve(N, k, 1e-3, options=opts)
+        assert (p["E_R"] + 3 * math.sqrt(p["Var_R"])) * 8192 <= N, (N, k, p["E_R"], p["Var_R"])
