@@ -6,6 +6,7 @@ _build/, then linked into sampling_threshold_filtering_amd/libprofk.so.
 from __future__ import annotations
 
 import os
+import resource
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -39,8 +40,19 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _raise_stack_limit() -> None:
+    """The compiler's interprocedural value analysis recurses once per link of a long
+    select chain (the unrolled register sorting networks); with the usual 8 MB stack
+    it overflows on k_refine.hip.  Child processes inherit the raised soft limit."""
+    soft, hard = resource.getrlimit(resource.RLIMIT_STACK)
+    want = hard if hard == resource.RLIM_INFINITY else max(soft, hard)
+    if soft != resource.RLIM_INFINITY and (want == resource.RLIM_INFINITY or want > soft):
+        resource.setrlimit(resource.RLIMIT_STACK, (want, hard))
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    _raise_stack_limit()
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))

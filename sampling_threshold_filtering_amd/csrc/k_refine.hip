@@ -18,14 +18,14 @@
 //                          also publishes the attempt record (R, check, multi-pass
 //                          flag) to the host, which needs nothing later to decide.
 //   refine_binsort_kernel  sorts every bin >= b* (four 256-thread workgroups per CU:
-//                          one wavefront in registers up to kWaveBin keys, a workgroup
-//                          in LDS up to kBinCap) and writes out_vals / out_idx for
-//                          positions < k.  A larger bin (large tie groups, narrow
-//                          ranges) is partitioned by one workgroup on successive
-//                          12-bit digits of (key - tau), from the top down, until every
-//                          part that reaches a position below k fits those sorts.  It
-//                          also leaves the histogram and the sampler's hash set zero
-//                          for the next attempt.
+//                          one wavefront in registers up to kWaveMax keys, a workgroup
+//                          up to kBinCap by one 8-bit counting pass in LDS) and writes
+//                          out_vals / out_idx for positions < k.  A larger bin (large
+//                          tie groups, narrow ranges) is partitioned by one workgroup
+//                          on successive 12-bit digits of (key - tau), from the top
+//                          down, until every part that reaches a position below k fits
+//                          those sorts.  It also leaves the histogram and the
+//                          sampler's hash set zero for the next attempt.
 // Bins larger than RefineArgs::msd_cap are instead left to the multi-pass refinement,
 // which the host enqueues after reading the flag (exact mode only).
 // Bins partition the keys by value, so sorted bins laid out from the top bin down
@@ -258,7 +258,16 @@ __global__ __launch_bounds__(kHistThreads) void refine_scatter_kernel(RefineArgs
   }
 }
 
-constexpr u32 kWaveBin = 1024;  // largest bin one wavefront sorts in registers (16 keys per lane)
+#ifndef PROFK_WAVE_MAX
+#define PROFK_WAVE_MAX 256
+#endif
+// Bins up to kWaveMax keys are sorted by one wavefront; larger ones by the workgroup
+// (a register sort of 8 keys per lane is a chain of some 4000 instructions on one
+// SIMD, the workgroup's counting pass a few LDS round trips).
+constexpr u32 kWaveMax = PROFK_WAVE_MAX;
+constexpr u32 kSubDigits = 256;  // digit of the workgroup's counting pass (8 bits)
+constexpr u32 kRankScan = 32;    // sub-buckets up to this size are ranked by a scan
+constexpr u32 kHeavyPer = kBinCap / kSortThreads;
 
 __device__ __forceinline__ void write_out(const RefineArgs& a, u64 p, u64 key) {
   const u32 idx = key_index(key);
@@ -266,33 +275,41 @@ __device__ __forceinline__ void write_out(const RefineArgs& a, u64 p, u64 key) {
   if (idx < a.N) reinterpret_cast<u32*>(a.out_vals)[p] = value_bits(key, a.x, idx);
 }
 
-// One part of cnt <= 64*M keys at src[start..), sorted by one wavefront in registers;
-// positions below lim are written out.
+// n <= 64*M keys at src[0..n) (global memory or LDS), sorted by one wavefront in
+// registers; sorted position i goes to output position out0 + i when that is below k.
 template <int M>
-__device__ __forceinline__ void wave_bin(const RefineArgs& a, const u64* src, u32 start, u32 cnt, u64 lim) {
+__device__ __forceinline__ void wave_bin(const RefineArgs& a, const u64* src, u32 n, u64 out0) {
   const u32 lane = lane_id();
   u64 v[M];
 #pragma unroll
   for (int r = 0; r < M; ++r) {
     const u32 i = (u32)r * kWave + lane;
-    v[r] = i < cnt ? src[start + i] : 0ull;
+    v[r] = i < n ? src[i] : 0ull;
   }
   wave_sort_regs_desc<M>(v);
 #pragma unroll
   for (int r = 0; r < M; ++r) {
     const u32 i = (u32)r * kWave + lane;
-    if (i < lim) write_out(a, (u64)start + i, v[r]);
+    if (i < n && out0 + i < a.k) write_out(a, out0 + i, v[r]);
   }
 }
 
-// A part of 1 <= cnt <= kWaveBin keys at src[start..) (wave-uniform arguments).
-__device__ __forceinline__ void wave_part(const RefineArgs& a, const u64* src, u32 start, u32 cnt) {
-  const u64 lim = a.k - start < cnt ? a.k - start : cnt;
-  if (cnt <= 64) wave_bin<1>(a, src, start, cnt, lim);
-  else if (cnt <= 128) wave_bin<2>(a, src, start, cnt, lim);
-  else if (cnt <= 256) wave_bin<4>(a, src, start, cnt, lim);
-  else if (cnt <= 512) wave_bin<8>(a, src, start, cnt, lim);
-  else wave_bin<16>(a, src, start, cnt, lim);
+// 1 <= n <= kWaveBin keys at src[0..n) to output positions from out0 (wave-uniform
+// arguments).
+__device__ __forceinline__ void wave_part(const RefineArgs& a, const u64* src, u32 n, u64 out0) {
+  if (n <= 64) wave_bin<1>(a, src, n, out0);
+  else if (n <= 128) wave_bin<2>(a, src, n, out0);
+  else if (n <= 256) wave_bin<4>(a, src, n, out0);
+  else wave_bin<8>(a, src, n, out0);
+}
+
+// 1 <= n <= kWaveMax keys (kWaveMax <= 256), as wave_part: only the narrow sorts, so
+// that the main loop of the bin sort does not carry the register needs of the wide ones.
+__device__ __forceinline__ void light_part(const RefineArgs& a, const u64* src, u32 n, u64 out0) {
+  static_assert(kWaveMax <= 256, "light bins take at most 4 keys per lane");
+  if (n <= 64) wave_bin<1>(a, src, n, out0);
+  else if (n <= 128) wave_bin<2>(a, src, n, out0);
+  else wave_bin<4>(a, src, n, out0);
 }
 
 // A part of cnt <= kBinCap keys at src[start..), sorted by the workgroup in LDS.
@@ -305,6 +322,99 @@ __device__ void lds_part(const RefineArgs& a, u64* s, const u64* src, u32 start,
   block_bitonic_desc(s, P);
   const u64 lim = a.k - start < cnt ? a.k - start : cnt;
   for (u32 i = threadIdx.x; i < lim; i += blockDim.x) write_out(a, start + i, s[i]);
+}
+
+struct HeavyLds {
+  u32 cnt[kSubDigits];  // keys per sub-digit
+  u32 beg[kSubDigits];  // start of each sub-bucket within the bin, descending digits first
+  u32 cur[kSubDigits];  // placement cursors
+  u32 big[kSubDigits];  // sub-digits whose bucket is ranked by a wavefront sort
+  u32 nbig;
+  u32 over;             // some sub-bucket exceeds kWaveBin
+};
+
+// A bin of kWaveMax < cnt <= kBinCap keys at tmp[start..), by the workgroup: one
+// counting pass on the next 8 bits below the bin's own (bits [sub, sub + 8) of
+// key - tau; higher bits are equal within the bin, so the digit orders the keys
+// coarsely), the keys placed in LDS by descending digit, then each key's position
+// is its sub-bucket's start plus the number of larger keys in the sub-bucket (a scan
+// of at most kRankScan keys); sub-buckets of up to kWaveBin keys are sorted by one
+// wavefront each, and a larger one (long runs of equal values) sends the bin to the
+// LDS bitonic sort.
+__device__ void heavy_part(const RefineArgs& a, u64* s, HeavyLds* L, u32 start, u32 cnt, u64 tau, u32 sub) {
+  const u32 tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  const u64* src = a.tmp + start;
+  __syncthreads();  // the previous user of s and L is done
+  for (u32 d = tid; d < kSubDigits; d += blockDim.x) L->cnt[d] = 0;
+  if (tid == 0) {
+    L->nbig = 0;
+    L->over = 0;
+  }
+  __syncthreads();
+  // the keys are read twice from tmp (L2) rather than held in registers, which would
+  // cost the kernel its occupancy
+#pragma unroll 4
+  for (u32 i = tid; i < cnt; i += kSortThreads) atomicAdd(&L->cnt[(u32)((src[i] - tau) >> sub) & (kSubDigits - 1u)], 1u);
+  __syncthreads();
+  if (wid == 0) {
+    // descending exclusive offsets: lane owns descending positions 4*lane .. 4*lane + 3
+    constexpr u32 kPerL = kSubDigits / kWave;
+    u32 c[kPerL], sum = 0;
+#pragma unroll
+    for (u32 r = 0; r < kPerL; ++r) {
+      c[r] = L->cnt[kSubDigits - 1u - (lane * kPerL + r)];
+      sum += c[r];
+    }
+    u32 incl = sum;
+#pragma unroll
+    for (u32 d = 1; d < (u32)kWave; d <<= 1) {
+      const u32 o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    u32 run = incl - sum;
+#pragma unroll
+    for (u32 r = 0; r < kPerL; ++r) {
+      const u32 d = kSubDigits - 1u - (lane * kPerL + r);
+      L->beg[d] = run;
+      L->cur[d] = run;
+      if (c[r] > kWaveBin) L->over = 1;
+      else if (c[r] > kRankScan) L->big[atomicAdd(&L->nbig, 1u)] = d;
+      run += c[r];
+    }
+  }
+  __syncthreads();
+  if (L->over) {
+    lds_part(a, s, a.tmp, start, cnt);
+    return;
+  }
+#pragma unroll 4
+  for (u32 i = tid; i < cnt; i += kSortThreads) {
+    const u64 key = src[i];
+    s[atomicAdd(&L->cur[(u32)((key - tau) >> sub) & (kSubDigits - 1u)], 1u)] = key;
+  }
+  __syncthreads();
+  for (u32 i = tid; i < cnt; i += kSortThreads) {
+    const u64 key = s[i];
+    const u32 d = (u32)((key - tau) >> sub) & (kSubDigits - 1u);
+    const u32 c = L->cnt[d];
+    if (c > kRankScan) continue;
+    const u32 b0 = L->beg[d];
+    u32 r = 0;
+    for (u32 q = 0; q < c; ++q) r += s[b0 + q] > key ? 1u : 0u;
+    const u64 p = (u64)start + b0 + r;
+    if (p < a.k) write_out(a, p, key);
+  }
+  const u32 nbig = L->nbig;
+  if (nbig == 0) return;
+  // the placed bin back into its own range of tmp, so that one wavefront per large
+  // sub-bucket sorts it from there
+  for (u32 i = tid; i < cnt; i += blockDim.x) a.tmp[start + i] = s[i];
+  __syncthreads();
+  for (u32 e = wid; e < nbig; e += kSortThreads / kWave) {
+    const u32 d = L->big[e];
+    const u32 b0 = L->beg[d];
+    if ((u64)start + b0 < a.k) wave_part(a, a.tmp + start + b0, L->cnt[d], (u64)start + b0);
+  }
 }
 
 __device__ __forceinline__ u32 msd_digit(u64 key, u64 tau, u32 sub) {
@@ -373,7 +483,8 @@ __device__ void msd_split(const RefineArgs& a, u64* s, const u64* src, u64* dst,
     while (small) {
       const int l = __ffsll((unsigned long long)small) - 1;
       small &= small - 1;
-      wave_part(a, dst, (u32)__shfl((int)st, l), (u32)__shfl((int)c, l));
+      const u32 ps = (u32)__shfl((int)st, l), pc = (u32)__shfl((int)c, l);
+      wave_part(a, dst + ps, pc, ps);
     }
   }
   __syncthreads();
@@ -382,13 +493,13 @@ __device__ void msd_split(const RefineArgs& a, u64* s, const u64* src, u64* dst,
 // Bin b of cnt > kBinCap keys at tmp[start..), of key width 2^width: partitioned level
 // by level (ping-pong between tmp and the candidate buffer, which the scatter no longer
 // needs) until every part below position k is sorted.  Parts at one level are disjoint
-// and hold more than kWaveBin keys, so a list never exceeds cnt / 1024 + 1 entries;
+// and hold more than kWaveBin keys, so a list never exceeds cnt / kWaveBin + 1 entries;
 // bins' lists are disjoint pool ranges.  Each level lowers the width by kMsdBits, and a
 // part of width 2^kMsdBits holds at most kMsdDigits <= kBinCap distinct keys, so at most
 // ceil(64 / kMsdBits) levels run.
 __device__ void msd_bin(const RefineArgs& a, u64* s, u32 b, u32 start, u32 cnt, u32 width, u64 tau, MsdLds* m) {
-  const u32 cap = (cnt >> 10) + 1u;
-  u64* cur = a.pool + 2ull * ((u64)(start >> 10) + (kBins - 1u - b));
+  const u32 cap = (cnt >> kWaveBinBits) + 1u;
+  u64* cur = a.pool + 2ull * ((u64)(start >> kWaveBinBits) + (kBins - 1u - b));
   u64* nxt = cur + cap;
   u64* src = a.tmp;
   u64* dst = a.cand;
@@ -425,13 +536,20 @@ __device__ void msd_bin(const RefineArgs& a, u64* s, u32 b, u32 start, u32 cnt, 
   }
 }
 
-// Bins of up to kWaveBin keys: one wavefront each, sorted in registers.  Larger bins:
-// the whole workgroup, in LDS up to kBinCap, else by the partition above.
+// Bin q (descending position; bin kBins - 1 - q) belongs to workgroup q mod G, and
+// within it to wavefront (q / G) mod 4: the heavy bins, which are neighbours (next to
+// tau on skewed inputs), go to different workgroups.  Bins of up to kWaveMax keys are
+// sorted by their wavefront in registers; larger ones by the whole workgroup, after
+// its wavefronts are done: the counting pass above up to kBinCap keys, else the
+// partition by 12-bit digits.
+constexpr u32 kPrefetch = 4;  // bins whose extent a wavefront loads at once
+
 __global__ __launch_bounds__(kSortThreads) void refine_binsort_kernel(RefineArgs a) {
   __shared__ u64 s[kBinCap];
   __shared__ u32 s_big[kSortThreads];
   __shared__ u32 s_nbig;
   __shared__ MsdLds s_msd;
+  __shared__ HeavyLds s_heavy;
   {  // leave the histogram and the sampler's hash set zero for the next attempt
     const u64 gt = (u64)blockIdx.x * blockDim.x + threadIdx.x, gs = (u64)gridDim.x * blockDim.x;
     for (u64 i = gt; i < kBins; i += gs) a.hist[i] = 0;
@@ -456,33 +574,46 @@ __global__ __launch_bounds__(kSortThreads) void refine_binsort_kernel(RefineArgs
     }
   }
   if (!refine_live(a, c) || c->generic) return;
-  const int bstar = (int)c->bstar;
+  const u32 qmax = kBins - 1u - c->bstar;
   const u64 k = a.k;
   const u32 lane = lane_id();
   const u32 wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int nwaves = (int)(gridDim.x * (kSortThreads / kWave));
+  constexpr u32 kWaves = kSortThreads / kWave;
+  const u32 G = gridDim.x;
   if (threadIdx.x == 0) s_nbig = 0;
   __syncthreads();
-  for (int b = (int)kBins - 1 - (int)(blockIdx.x * (kSortThreads / kWave) + wid); b >= bstar; b -= nwaves) {
-    const u32 cnt = a.bin_cnt[b];
-    const u32 start = a.bin_off[b];
-    if (cnt == 0 || start >= k || start + (u64)cnt > a.M) continue;  // uniform per wavefront
-    if (cnt > kWaveBin) {
-      if (lane == 0) s_big[atomicAdd(&s_nbig, 1u)] = (u32)b;  // at most one per wavefront pass
-      continue;
+  for (u32 i = wid; blockIdx.x + (u64)G * i <= qmax; i += kWaves * kPrefetch) {
+    u32 cnt[kPrefetch], start[kPrefetch], bin[kPrefetch];
+#pragma unroll
+    for (u32 r = 0; r < kPrefetch; ++r) {  // unconditional loads, all in flight
+      const u64 q = blockIdx.x + (u64)G * (i + kWaves * r);
+      bin[r] = q <= qmax ? kBins - 1u - (u32)q : kBins;
+      const u32 bl = bin[r] < kBins ? bin[r] : kBins - 1u;
+      cnt[r] = a.bin_cnt[bl];
+      start[r] = a.bin_off[bl];
     }
-    wave_part(a, a.tmp, start, cnt);
+#pragma unroll
+    for (u32 r = 0; r < kPrefetch; ++r) {
+      const u32 n = bin[r] < kBins ? cnt[r] : 0u;
+      if (n == 0 || start[r] >= k || start[r] + (u64)n > a.M) continue;  // uniform per wavefront
+      if (n > kWaveMax) {
+        if (lane == 0) s_big[atomicAdd(&s_nbig, 1u)] = bin[r];  // the block meets at most kSortThreads bins
+        continue;
+      }
+      light_part(a, a.tmp + start[r], n, start[r]);
+    }
   }
   __syncthreads();
   const u32 nbig = s_nbig;
   const u64 tau = c->tau;
   const u32 width = c->bin_shift;
+  const u32 sub = width > 8u ? width - 8u : 0u;
   for (u32 q = 0; q < nbig; ++q) {
     const u32 b = s_big[q];
     const u32 cnt = a.bin_cnt[b];
     const u32 start = a.bin_off[b];
     if (cnt <= kBinCap)
-      lds_part(a, s, a.tmp, start, cnt);
+      heavy_part(a, s, &s_heavy, start, cnt, tau, sub);
     else
       msd_bin(a, s, b, start, cnt, width, tau, &s_msd);
   }
@@ -503,13 +634,17 @@ hipError_t launch_approx_info_exact(ApproxInfo* info, u64 N, hipStream_t s) {
 }
 
 hipError_t launch_refine(const RefineArgs& a, hipStream_t s) {
-  u32 gh = (u32)((a.M + 16383) / 16384);  // about 16 candidates per thread
+  // about 4 candidates per thread at R = M (R is mostly well below M): more blocks keep
+  // more candidate loads in flight, but each adds its nonzero bins to the global
+  // histogram and reserves its runs with atomics (measured on MI355X over 2^30 Pareto
+  // values, k = 2^5..2^19: 64..128 blocks best, 512 worse than 32)
+  u32 gh = (u32)((a.M + 4095) / 4096);
   if (gh < 1) gh = 1;
-  if (gh > 32) gh = 32;  // each block adds its nonzero bins to the global histogram and scans it
+  if (gh > 128) gh = 128;
   refine_hist_kernel<<<gh, kHistThreads, 0, s>>>(a);
   refine_scatter_kernel<<<gh, kHistThreads, 0, s>>>(a);
-  // at least 64 workgroups: a workgroup then meets at most kSortThreads bins above
-  // one wavefront's share (s_big)
+  // at least 64 workgroups: a workgroup then owns at most kBins / 64 = kSortThreads
+  // bins (s_big)
   u32 gs = 4 * device_cu_count();
   if (gs < 64) gs = 64;
   refine_binsort_kernel<<<gs, kSortThreads, 0, s>>>(a);

@@ -112,9 +112,14 @@ constexpr u32 kBinCap = 4096;  // keys one sorting workgroup holds in LDS (32 KB
 constexpr u32 kMsdBits = 12;  // digit of the in-kernel partition of oversized bins
 constexpr u32 kMsdDigits = 1u << kMsdBits;
 
+// Largest part one wavefront sorts in registers (8 keys per lane): a wider register
+// sort would set the bin sort kernel's register count, and with it its occupancy.
+constexpr u32 kWaveBinBits = 9;
+constexpr u32 kWaveBin = 1u << kWaveBinBits;
+
 // Work-list entries (start | count << 32) of the in-kernel partition of oversized
-// bins: two lists per oversized bin, at most kBins + M / 1024 + 2 pairs in all.
-__host__ __device__ inline u64 msd_pool_words(u64 M) { return 2 * (M / 1024 + kBins + 2); }
+// bins: two lists per oversized bin, at most kBins + M / kWaveBin + 2 pairs in all.
+__host__ __device__ inline u64 msd_pool_words(u64 M) { return 2 * (M / kWaveBin + kBins + 2); }
 
 struct RefineArgs {
   RowCtl* ctl;

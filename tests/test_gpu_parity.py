@@ -188,6 +188,39 @@ def test_binned_and_multipass_refinement_both_run():
     assert st["refine_multipass"] >= 1
 
 
+def heavy_bins_input(n: int, seed: int) -> np.ndarray:
+    """Background noise below 1.5, plus clusters that each fill one value bin of the
+    refinement with more keys than one wavefront sorts: 2000 keys within 512 ulps
+    (counting pass, ranks by scan and small sub-bucket sorts), 300 copies of one value
+    among 200 neighbours (a sub-bucket sorted by one wavefront), 1000 copies (a
+    sub-bucket too large for that: the bin goes to the LDS bitonic sort), 5000 copies
+    (a bin beyond one workgroup's LDS: the digit partition), and light bins."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(n) * 0.25).astype(np.float32)
+    def ulps(base, off):
+        return (np.uint32(np.float32(base).view(np.uint32)) + off.astype(np.uint32)).view(np.float32)
+    parts = [
+        rng.uniform(1.5, 8.0, 50).astype(np.float32),
+        ulps(4.0, rng.integers(0, 512, 2000)),
+        np.full(300, 5.0, np.float32), ulps(5.0, rng.integers(1, 600, 200)),
+        np.full(1000, 6.0, np.float32),
+        np.full(5000, 7.0, np.float32),
+        rng.uniform(2.0, 3.0, 3000).astype(np.float32),
+    ]
+    planted = np.concatenate(parts)
+    x[rng.choice(n, planted.size, replace=False)] = planted
+    return x
+
+
+@pytest.mark.parametrize("k", [12000, 9000, 2100])
+def test_heavy_bins_take_every_sort_path(k):
+    say("heavy bins", k)
+    x = heavy_bins_input(1 << 21, 44)
+    vals, idx, st = stf.topk(dev(x), k, stats=True)
+    check_topk(x, vals, idx, k)
+    assert st["refine_multipass"] == 0 and not st["fallback"]
+
+
 def test_forced_overflow_goes_to_fallback_and_stays_exact():
     say("forced overflow M = k")
     N, k = 1 << 22, 4096
