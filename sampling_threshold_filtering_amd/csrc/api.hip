@@ -286,7 +286,7 @@ SampleArgs sample_args(Workspace* w, const Layout& L, const float* x, u64 N, u64
   a.ticket = reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kTicketSample);
   a.top_hist = at<SelState>(w, L.sel)->hist;
   a.t = t;
-  a.fast = (t >= 1 && t <= kTopT && sample_blocks(S) <= kTopBlocks) ? 1u : 0u;
+  a.fast = (t >= 1 && t <= kTopT && sample_blocks(S, t) <= kTopBlocks) ? 1u : 0u;
   return a;
 }
 
@@ -453,6 +453,7 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   ra.seq = seq;
   ra.rec = rec;
   ra.msd_cap = kMsdCapExact;
+  ra.early_cap = kMsdCapExact;  // the same cap wait_record applies to the early word
   HIPCHK(launch_refine(ra, s), "launch refine");
   // The filter publishes R and the check, the scan the full record; the host needs the
   // scan's only when a value bin may exceed the in-kernel partition's cap.  The

@@ -217,6 +217,99 @@ __device__ inline u64 block_select_finish(const u64* keys, u64 n, u64* buf, u32 
   return result;
 }
 
+struct LdsSelect {
+  u32 hist[256];
+  u64 prefix, mask;
+  u32 rank, count, state;  // state: 0 = running, 1 = at most kWave keys match, 2 = too few keys
+  u32 nsmall;
+  u64 small[kWave];
+  u64 result;
+};
+
+// The key of descending rank `rank` (1-based) among the nonzero, distinct keys
+// s[0..n) held in LDS, by the whole block: 8-bit digits from the top, each pass a
+// histogram of the keys that match the digits fixed so far, until at most kWave keys
+// match; those are ranked against each other by one wavefront.  Returns 0 when fewer
+// than `rank` nonzero keys are present.
+__device__ inline u64 lds_select_desc(const u64* s, u32 n, u32 rank, LdsSelect* L) {
+  const u32 tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  if (tid == 0) {
+    L->prefix = 0;
+    L->mask = 0;
+    L->rank = rank;
+    L->count = 0xFFFFFFFFu;
+    L->state = 0;
+    L->nsmall = 0;
+    L->result = 0;
+  }
+  for (u32 d = 0; d < 8; ++d) {
+    for (u32 b = tid; b < 256; b += blockDim.x) L->hist[b] = 0;
+    __syncthreads();
+    const u64 prefix = L->prefix, mask = L->mask;
+    const u32 shift = 56u - 8u * d;
+    for (u32 i = tid; i < n; i += blockDim.x) {
+      const u64 k = s[i];
+      if (k != 0 && (k & mask) == prefix) atomicAdd(&L->hist[(u32)(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wid == 0) {
+      // descending digits: lane owns 255 - 4*lane .. 255 - 4*lane - 3
+      u32 c[4], sum = 0;
+#pragma unroll
+      for (u32 r = 0; r < 4; ++r) {
+        c[r] = L->hist[255u - (4u * lane + r)];
+        sum += c[r];
+      }
+      u32 incl = sum;
+#pragma unroll
+      for (u32 o = 1; o < (u32)kWave; o <<= 1) {
+        const u32 v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+      }
+      const u32 want = L->rank;
+      const u32 total = __shfl(incl, kWave - 1);
+      u32 run = incl - sum;
+#pragma unroll
+      for (u32 r = 0; r < 4; ++r) {
+        if (run < want && run + c[r] >= want) {
+          const u32 dg = 255u - (4u * lane + r);
+          L->rank = want - run;
+          L->count = c[r];
+          L->prefix = prefix | ((u64)dg << shift);
+          L->mask = mask | (0xFFull << shift);
+          L->state = c[r] <= (u32)kWave ? 1u : 0u;
+        }
+        run += c[r];
+      }
+      if (lane == 0 && total < want) L->state = 2;
+    }
+    __syncthreads();
+    if (L->state != 0) break;
+  }
+  if (L->state == 1) {
+    const u64 prefix = L->prefix, mask = L->mask;
+    for (u32 i = tid; i < n; i += blockDim.x) {
+      const u64 k = s[i];
+      if (k != 0 && (k & mask) == prefix) {
+        const u32 slot = atomicAdd(&L->nsmall, 1u);
+        if (slot < (u32)kWave) L->small[slot] = k;
+      }
+    }
+    __syncthreads();
+    const u32 m = L->nsmall < (u32)kWave ? L->nsmall : (u32)kWave;
+    if (wid == 0 && lane < m) {
+      const u64 k = L->small[lane];
+      u32 r = 0;
+      for (u32 j = 0; j < m; ++j) r += L->small[j] > k ? 1u : 0u;
+      if (r + 1u == L->rank) L->result = k;
+    }
+  }
+  __syncthreads();
+  const u64 result = L->result;
+  __syncthreads();
+  return result;
+}
+
 // Convenience: the whole selection from scratch.
 __device__ inline u64 block_select_rank(const u64* keys, u64 n, u64 rank, u64* buf, u32 cap, BlockSelectLds* L,
                                         bool* ok_out) {

@@ -62,9 +62,11 @@ __device__ __forceinline__ bool refine_live(const RefineArgs& a, const RowCtl* c
   return c->status == 0 || (a.approx && (c->status == 1u || c->status == 2u));
 }
 
-// Attempt record into pinned host memory; seq last, released at system scope.
+// Attempt record into pinned host memory; seq last, released at system scope.  Skipped
+// where the host already has what it needs from the filter's early word.
 __device__ __forceinline__ void publish(const RefineArgs& a, const RowCtl* c, u32 generic) {
   if (!a.hrec) return;
+  if (a.early_cap && (c->status != 0 || c->R <= a.early_cap)) return;
   HostRecord* h = a.hrec;
   h->R = c->R;
   h->status = c->status;
@@ -303,13 +305,20 @@ __device__ __forceinline__ void wave_part(const RefineArgs& a, const u64* src, u
   else wave_bin<8>(a, src, n, out0);
 }
 
-// 1 <= n <= kWaveMax keys (kWaveMax <= 256), as wave_part: only the narrow sorts, so
-// that the main loop of the bin sort does not carry the register needs of the wide ones.
-__device__ __forceinline__ void light_part(const RefineArgs& a, const u64* src, u32 n, u64 out0) {
-  static_assert(kWaveMax <= 256, "light bins take at most 4 keys per lane");
-  if (n <= 64) wave_bin<1>(a, src, n, out0);
-  else if (n <= 128) wave_bin<2>(a, src, n, out0);
-  else wave_bin<4>(a, src, n, out0);
+// A light bin of 1 <= n <= 64*M keys already loaded (v[r], element r*64 + lane),
+// sorted by the wavefront in registers and written from output position out0.
+template <int M>
+__device__ __forceinline__ void light_sort(const RefineArgs& a, const u64 (&v)[4], u32 n, u64 out0) {
+  const u32 lane = lane_id();
+  u64 w[M];
+#pragma unroll
+  for (int r = 0; r < M; ++r) w[r] = v[r];
+  wave_sort_regs_desc<M>(w);
+#pragma unroll
+  for (int r = 0; r < M; ++r) {
+    const u32 i = (u32)r * kWave + lane;
+    if (i < n && out0 + i < a.k) write_out(a, out0 + i, w[r]);
+  }
 }
 
 // A part of cnt <= kBinCap keys at src[start..), sorted by the workgroup in LDS.
@@ -592,15 +601,31 @@ __global__ __launch_bounds__(kSortThreads) void refine_binsort_kernel(RefineArgs
       cnt[r] = a.bin_cnt[bl];
       start[r] = a.bin_off[bl];
     }
+    // the keys of every light bin of the group in flight before the first sort
+    static_assert(kWaveMax <= 4 * kWave, "light bins take at most 4 keys per lane");
+    u64 v[kPrefetch][4];
+    u32 n[kPrefetch];
 #pragma unroll
     for (u32 r = 0; r < kPrefetch; ++r) {
-      const u32 n = bin[r] < kBins ? cnt[r] : 0u;
-      if (n == 0 || start[r] >= k || start[r] + (u64)n > a.M) continue;  // uniform per wavefront
-      if (n > kWaveMax) {
+      n[r] = bin[r] < kBins ? cnt[r] : 0u;
+      if (start[r] >= k || start[r] + (u64)n[r] > a.M) n[r] = 0;  // uniform per wavefront
+      const bool light = n[r] <= kWaveMax;
+#pragma unroll
+      for (u32 j = 0; j < 4; ++j) {
+        const u32 e = j * kWave + lane;
+        v[r][j] = light && e < n[r] ? a.tmp[start[r] + e] : 0ull;
+      }
+    }
+#pragma unroll
+    for (u32 r = 0; r < kPrefetch; ++r) {
+      if (n[r] == 0) continue;
+      if (n[r] > kWaveMax) {
         if (lane == 0) s_big[atomicAdd(&s_nbig, 1u)] = bin[r];  // the block meets at most kSortThreads bins
         continue;
       }
-      light_part(a, a.tmp + start[r], n, start[r]);
+      if (n[r] <= kWave) light_sort<1>(a, v[r], n[r], start[r]);
+      else if (n[r] <= 2 * kWave) light_sort<2>(a, v[r], n[r], start[r]);
+      else light_sort<4>(a, v[r], n[r], start[r]);
     }
   }
   __syncthreads();

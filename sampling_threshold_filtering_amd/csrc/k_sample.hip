@@ -7,7 +7,10 @@
 // (see profk_device.h for the draw).  That rule is symmetric under relabelling of
 // [N], so every S-subset is equally likely, and it is deterministic per seed.
 //
-//   sample_kernel   one thread per draw 0..S-1.  Each index goes into a hash set of
+//   sample_kernel   one thread per draw 0..S-1, in workgroups of 256 threads when
+//                   the per-block lists below apply and S <= 32768 (the random
+//                   gathers then spread over 4x as many CUs, which halves their
+//                   latency on MI355X), else 1024.  Each index goes into a hash set of
 //                   32-bit slots in device memory (idx + 1, 0 = empty, one CAS per
 //                   probe; the set is zero on entry and cleared again after the
 //                   attempt), while the gather of x[idx] is already in flight.  Draw
@@ -19,10 +22,11 @@
 //                   are held, wavefront 0 takes further draws S, S+1, ... in order,
 //                   64 at a time, keeping those that are new and not repeated earlier
 //                   in the same chunk (expected extra draws about S^2 / (2N)), into
-//                   keys[S..]; and (b) selects tau.  With the per-block lists, every
-//                   key among the t largest is at least L = the largest block-local
-//                   t-th key, so only the listed keys >= L are sorted.  Otherwise a
-//                   one-workgroup radix select over all key slots runs.
+//                   keys[S..]; and (b) selects tau.  With the per-block lists, only
+//                   the first t keys of each list (and the top-up keys) can be among
+//                   the t largest: those are loaded into LDS and a radix select
+//                   there finds the t-th.  Otherwise a one-workgroup radix select
+//                   over all key slots runs.
 #include "block_select.h"
 #include "launch.h"
 
@@ -96,13 +100,14 @@ __global__ __launch_bounds__(1024) void attempt_init_kernel(RowCtl* ctl, SelStat
   }
 }
 
-constexpr u32 kSampleThreads = 1024;
-constexpr u32 kSampleWaves = kSampleThreads / kWave;
 constexpr u32 kTauCap = 8192;  // keys the last block sorts or selects from in LDS (64 KB)
 
+template <u32 kSampleThreads>
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
+  constexpr u32 kSampleWaves = kSampleThreads / kWave;
   __shared__ u64 s_buf[kTauCap];
   __shared__ BlockSelectLds s_sel;
+  __shared__ LdsSelect s_lsel;
   __shared__ u32 s_wcnt[kSampleWaves];
   __shared__ u32 s_n;
   __shared__ u32 s_last;
@@ -201,44 +206,28 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
   bool ok = sample_ok;
   u64 tau = 0;
   if (select) {
-    if (a.fast && sample_ok && a.t + E <= kTauCap) {
-      // merge the blocks' lists: the T largest keys of the draws, sorted
-      const u64 ntops = (u64)gridDim.x * T;  // <= kTopBlocks * kTopT = kTauCap
+    if (a.fast && sample_ok && (u64)gridDim.x * a.t + E <= kTauCap) {
+      // each block's list holds its T largest draws in descending order, so only its
+      // first t can be among the t largest; with the top-up keys they go into LDS
+      const u32 G = gridDim.x, tt = (u32)a.t, nl = G * tt;
       constexpr u32 kILP = 8;
-      for (u64 base = 0; base < ntops; base += (u64)blockDim.x * kILP) {
+      for (u32 base = 0; base < nl; base += blockDim.x * kILP) {
         u64 kk[kILP];
 #pragma unroll
         for (u32 q = 0; q < kILP; ++q) {
-          const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
-          kk[q] = i < ntops ? a.tops[i] : 0ull;
+          const u32 i = base + q * blockDim.x + threadIdx.x;
+          const u32 b = i / tt;
+          kk[q] = i < nl ? a.tops[(u64)b * T + (i - b * tt)] : 0ull;
         }
 #pragma unroll
         for (u32 q = 0; q < kILP; ++q) {
-          const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
-          if (i < ntops) s_buf[i] = kk[q];
+          const u32 i = base + q * blockDim.x + threadIdx.x;
+          if (i < nl) s_buf[i] = kk[q];
         }
       }
+      for (u64 i = threadIdx.x; i < E; i += blockDim.x) s_buf[nl + i] = a.keys[a.S + i];
       __syncthreads();
-      block_merge_lists(s_buf, gridDim.x, T);
-      if (E > 0) {
-        // top-up keys: those at or above the t-th largest of the draws join its t
-        // largest, and the t-th of that set is tau
-        const u64 L = s_buf[a.t - 1];
-        if (threadIdx.x == 0) s_n = (u32)a.t;
-        __syncthreads();
-        for (u64 i = threadIdx.x; i < E; i += blockDim.x) {
-          const u64 kk = a.keys[a.S + i];
-          if (kk >= L) s_buf[atomicAdd(&s_n, 1u)] = kk;  // at most t + E <= kTauCap keys
-        }
-        __syncthreads();
-        const u32 nc = s_n;
-        u32 P = 1;
-        while (P < nc) P <<= 1;
-        for (u32 i = nc + threadIdx.x; i < P; i += blockDim.x) s_buf[i] = 0ull;
-        __syncthreads();
-        block_bitonic_desc(s_buf, P);
-      }
-      tau = s_buf[a.t - 1];
+      tau = lds_select_desc(s_buf, nl + (u32)E, tt, &s_lsel);
       ok = tau != 0;
     } else {
       if (use_hist) {
@@ -351,13 +340,24 @@ hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u
   return hipGetLastError();
 }
 
-hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
-  const u32 blocks = (u32)((a.S + kSampleThreads - 1) / kSampleThreads);
-  sample_kernel<<<blocks, kSampleThreads, 0, s>>>(a);
-  return hipGetLastError();
+u32 sample_threads(u64 S, u64 t) {
+  const bool lists = t == 0 || t <= kTopT;
+  return lists && (S + 255) / 256 <= kTopBlocks ? 256u : 1024u;
 }
 
-u32 sample_blocks(u64 S) { return (u32)((S + kSampleThreads - 1) / kSampleThreads); }
+u32 sample_blocks(u64 S, u64 t) {
+  const u32 th = sample_threads(S, t);
+  return (u32)((S + th - 1) / th);
+}
+
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
+  const u32 th = sample_threads(a.S, a.t), blocks = sample_blocks(a.S, a.t);
+  if (th == 256)
+    sample_kernel<256><<<blocks, 256, 0, s>>>(a);
+  else
+    sample_kernel<1024><<<blocks, 1024, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_clear_sample(u32* table, u64 slots, u32* tickets, hipStream_t s) {
   u64 blocks = (slots + 1023) / 1024;

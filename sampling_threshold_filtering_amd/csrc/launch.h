@@ -81,7 +81,10 @@ struct SampleArgs {
   u32 fast;         // 1: per-block lists (t <= kTopT, at most kTopBlocks blocks)
 };
 
-u32 sample_blocks(u64 S);
+// Sampling launch shape for (S, t): 256-thread workgroups while the per-block-list
+// threshold path applies and needs at most kTopBlocks of them, else 1024 threads.
+u32 sample_threads(u64 S, u64 t);
+u32 sample_blocks(u64 S, u64 t);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
 hipError_t launch_clear_sample(u32* table, u64 slots, u32* tickets, hipStream_t s);
 hipError_t launch_keys_to_index_compact(const u64* keys, const u64* n_ptr, u64 n_cap, int64_t* out, u32* counter,
@@ -137,6 +140,9 @@ struct RefineArgs {
   u64 table_slots;
   HostRecord* hrec;  // pinned host record published by the scan, or nullptr
   u32 seq;
+  u64 early_cap;    // nonzero: the host takes R and the check from the filter's early
+                    // word when the check failed or R <= early_cap, and the scan then
+                    // skips its record (a system-scope release); 0: always published
   AttemptRecord* rec;
   float* out_vals;
   int64_t* out_idx;

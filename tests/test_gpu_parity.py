@@ -63,7 +63,10 @@ def test_sample_matches_oracle(N, S, seed, attempt):
                                              # lists overflow the LDS buffer (128 x 64 + top-up): radix select
                                              ("uniform", 1 << 22, 131072, 64, 19),
                                              # t just above the list path
-                                             ("normal", 1 << 20, 32768, 65, 20)])
+                                             ("normal", 1 << 20, 32768, 65, 20),
+                                             # 256-thread sampling workgroups up to S = 32768, then 1024
+                                             ("pareto", 1 << 24, 16357, 1, 21), ("pareto", 1 << 24, 16357, 20, 22),
+                                             ("normal", 1 << 20, 32769, 40, 23)])
 def test_threshold_matches_oracle(kind, N, S, t, seed):
     say("threshold", kind, N, S, t, seed)
     edge = ("few_levels", "signed_zeros", "with_inf", "with_nan", "all_equal", "negative", "ascending")
