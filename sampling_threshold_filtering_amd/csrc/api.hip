@@ -740,11 +740,9 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     fa.M = M;
     fa.k = k;
     fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
-      fa.groups = at<u32>(w, L.ticket) + kTickets;
+    fa.groups = at<u32>(w, L.ticket) + kTickets;
     fa.xtime = reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kXtimeWord);
     for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[x];
-  fa.xtime = reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kXtimeWord);
-  for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[x];
     fa.rec = rec;
     fa.sels = nullptr;
     HIPCHK(launch_filter(fa, 0, s), "launch filter");
