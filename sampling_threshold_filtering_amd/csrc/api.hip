@@ -369,6 +369,9 @@ RefineArgs refine_args(Workspace* w, const Layout& L, const float* x, u64 N, u64
   return ra;
 }
 
+// Passes long enough for their per-die stream times to size the dies' shares.
+constexpr u64 kTimedMinN = 1ull << 24;
+
 FilterArgs flat_filter_args(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, u64 M) {
   FilterArgs fa{};
   fa.x = x;
@@ -382,7 +385,8 @@ FilterArgs flat_filter_args(Workspace* w, const Layout& L, const float* x, u64 N
   fa.k = k;
   fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
   fa.groups = at<u32>(w, L.ticket) + kTickets;
-  fa.xtime = reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kXtimeWord);
+  // per-die stream times only where the host updates the die weights from them
+  fa.xtime = N >= kTimedMinN ? reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kXtimeWord) : nullptr;
   for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[x];
   fa.rec = at<AttemptRecord>(w, L.rec);
   fa.sels = at<SelState>(w, L.sel);
@@ -462,7 +466,7 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   bool early = false;
   rc = wait_record(w, s, seq, kMsdCapExact, &early);
   if (rc) return rc;
-  if (N >= (1ull << 24)) update_die_weights(w, split);
+  if (N >= kTimedMinN) update_die_weights(w, split);
   w->host[0].R = w->hrec->R;
   w->host[0].status = w->hrec->status;
   w->host[0].error = w->hrec->error;
@@ -741,7 +745,6 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     fa.k = k;
     fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
     fa.groups = at<u32>(w, L.ticket) + kTickets;
-    fa.xtime = reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kXtimeWord);
     for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[x];
     fa.rec = rec;
     fa.sels = nullptr;
@@ -939,7 +942,6 @@ int profk_stage_filter(const float* x, int64_t N, float tau_val, int64_t tau_idx
   fa.k = 1;
   fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
   fa.groups = at<u32>(w, L.ticket) + kTickets;
-  fa.xtime = reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kXtimeWord);
   for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[x];
   fa.rec = nullptr;
   fa.sels = nullptr;

@@ -270,8 +270,10 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   const u64 wx = (u64)(blockIdx.x / kXcds) * kWavesPerBlock + wid;
   const u64 cend = a.split[xcd + 1];
   const u64 run = a.run, gend = a.total_tiles, tpr = a.tiles_per_row;
-  // earliest start kept as the largest complement, so that the resting value is zero
-  if (a.xtime && threadIdx.x == 0) atomicMax(&a.xtime[0], ~wall_clock64());
+  // earliest start kept as the largest complement, so that the resting value is zero;
+  // taken from the first block of each die only (one address takes an atomic every
+  // ~12 ns, and every block's would queue for ~9 us, which short passes wait out)
+  if (a.xtime && threadIdx.x == 0 && blockIdx.x < kXcds) atomicMax(&a.xtime[0], ~wall_clock64());
   struct Cursor {
     u64 g, lr, tile, in, chunk;
   };

@@ -25,8 +25,9 @@
 //                   keys[S..]; and (b) selects tau.  With the per-block lists, only
 //                   the first t keys of each list (and the top-up keys) can be among
 //                   the t largest: those are loaded into LDS and a radix select
-//                   there finds the t-th.  Otherwise a one-workgroup radix select
-//                   over all key slots runs.
+//                   there finds the t-th.  Otherwise, while all key slots fit in
+//                   LDS, the same select runs over them, and beyond that a
+//                   one-workgroup radix select reads them from L2 pass by pass.
 #include "block_select.h"
 #include "launch.h"
 
@@ -228,6 +229,27 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
       for (u64 i = threadIdx.x; i < E; i += blockDim.x) s_buf[nl + i] = a.keys[a.S + i];
       __syncthreads();
       tau = lds_select_desc(s_buf, nl + (u32)E, tt, &s_lsel);
+      ok = tau != 0;
+    } else if (sample_ok && nslots <= kTauCap) {
+      // every key slot fits in LDS: select there
+      constexpr u32 kILP = 8;
+      for (u64 base = 0; base < nslots; base += (u64)blockDim.x * kILP) {
+        u64 kk[kILP];
+#pragma unroll
+        for (u32 q = 0; q < kILP; ++q) {
+          const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
+          kk[q] = i < nslots ? a.keys[i] : 0ull;
+        }
+#pragma unroll
+        for (u32 q = 0; q < kILP; ++q) {
+          const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
+          if (i < nslots) s_buf[i] = kk[q];
+        }
+      }
+      if (use_hist)
+        for (u32 b = threadIdx.x; b < 256; b += blockDim.x) a.top_hist[b] = 0;  // left zero for the next launch
+      __syncthreads();
+      tau = lds_select_desc(s_buf, (u32)nslots, (u32)a.t, &s_lsel);
       ok = tau != 0;
     } else {
       if (use_hist) {

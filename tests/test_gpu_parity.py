@@ -66,7 +66,11 @@ def test_sample_matches_oracle(N, S, seed, attempt):
                                              ("normal", 1 << 20, 32768, 65, 20),
                                              # 256-thread sampling workgroups up to S = 32768, then 1024
                                              ("pareto", 1 << 24, 16357, 1, 21), ("pareto", 1 << 24, 16357, 20, 22),
-                                             ("normal", 1 << 20, 32769, 40, 23)])
+                                             ("normal", 1 << 20, 32769, 40, 23),
+                                             # t above the list path with every key slot in LDS (with and
+                                             # without a large top-up), and just beyond it
+                                             ("normal", 1 << 20, 8192, 100, 24), ("uniform", 12000, 6000, 300, 25),
+                                             ("uniform", 20000, 8000, 200, 26)])
 def test_threshold_matches_oracle(kind, N, S, t, seed):
     say("threshold", kind, N, S, t, seed)
     edge = ("few_levels", "signed_zeros", "with_inf", "with_nan", "all_equal", "negative", "ascending")
