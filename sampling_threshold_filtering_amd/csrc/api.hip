@@ -239,26 +239,31 @@ int wait_record(Workspace* w, hipStream_t s, u32 want, u64 early_cap = 0, bool* 
   const u32* seq = &w->hrec->seq;
   const u64* ew = &w->hrec->early;
   if (early) *early = false;
+  // the filter's early word settles the attempt when the check failed or R is small
+  // enough; the scan then publishes no record of its own
+  auto take_early = [&]() -> bool {
+    if (!early_cap) return false;
+    const u64 e = __atomic_load_n(ew, __ATOMIC_ACQUIRE);
+    if ((u32)(e >> 42) != (want & 0x3FFFFFu)) return false;
+    const u64 R = e & ((1ull << 40) - 1);
+    const u32 status = (u32)(e >> 40) & 3u;
+    if (status == 0 && R > early_cap) return false;
+    w->hrec->R = R;  // the fields the caller reads
+    w->hrec->status = status;
+    w->hrec->error = 0;
+    w->hrec->generic = 0;
+    if (early) *early = true;
+    return true;
+  };
   for (u64 it = 0;; ++it) {
-    if (early_cap) {
-      const u64 e = __atomic_load_n(ew, __ATOMIC_ACQUIRE);
-      if ((u32)(e >> 42) == (want & 0x3FFFFFu)) {
-        const u64 R = e & ((1ull << 40) - 1);
-        const u32 status = (u32)(e >> 40) & 3u;
-        if (status != 0 || R <= early_cap) {
-          w->hrec->R = R;  // the fields the caller reads (the scan's copy may follow)
-          w->hrec->status = status;
-          w->hrec->error = 0;
-          w->hrec->generic = 0;
-          *early = true;
-          return PROFK_OK;
-        }
-      }
-    }
+    if (take_early()) return PROFK_OK;
     if (__atomic_load_n(seq, __ATOMIC_ACQUIRE) == want) return PROFK_OK;
     if ((it & 255) == 255) {
       const hipError_t q = hipStreamQuery(s);
       if (q == hipSuccess) {
+        // everything has run: one of the two words must be there now (the early word
+        // may have landed after the first look above)
+        if (take_early()) return PROFK_OK;
         if (__atomic_load_n(seq, __ATOMIC_ACQUIRE) == want) return PROFK_OK;
         t_err = "sampled attempt: the attempt record was not published";
         return PROFK_EINTERNAL;
