@@ -424,12 +424,14 @@ void update_die_weights(Workspace* w, const u64* split) {
   w->hrec->xt[0] = 0;
 }
 
-// The filter's launch shape for rare hits pays off only while few tiles carry a hit; R
-// varies a lot from draw to draw at small t (exponential at t = 1), so the test takes
-// a high draw of R, E[R] + 3 sd(R), not its mean.
-u32 sparse_hits(const profk_params& p, u64 N) {
+// The filter's launch shape by the expected density of hits.  The shape for rare hits
+// pays off only while few tiles carry a hit; R varies a lot from draw to draw at small t
+// (exponential at t = 1), so that test takes a high draw of R, E[R] + 3 sd(R), not its
+// mean.  Dense hits (E[R] >= N / 2048) take a fourth block per CU.
+u32 filter_shape(const profk_params& p, u64 N) {
   const double hi = p.E_R + 3.0 * std::sqrt(p.Var_R > 0.0 ? p.Var_R : 0.0);
-  return hi * 8192.0 <= (double)N ? 1u : 0u;
+  if (hi * 8192.0 <= (double)N) return kShapeSparse;
+  return p.E_R * 2048.0 >= (double)N ? kShapeDenseHits : 0u;
 }
 
 // One sampled attempt of one row, enqueued; returns after the record is back.
@@ -452,7 +454,7 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   FilterArgs fa = flat_filter_args(w, L, x, N, k, M);
   fa.hrec = w->hrec_dev;
   fa.seq = seq;
-  fa.sparse = sparse_hits(p, N);
+  fa.sparse = filter_shape(p, N);
   u64 split[kXcds + 1];
   if (timing) HIPCHK(hipEventRecord(w->ev0, s), "hipEventRecord");
   HIPCHK(launch_filter(fa, 0, s, split), "launch filter");
@@ -652,7 +654,7 @@ int topk_approx_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* o
   sa.rec = at<AttemptRecord>(w, L.rec);
   HIPCHK(launch_sample(sa, s), "launch sample");
   FilterArgs fa = flat_filter_args(w, L, x, N, k, M);
-  fa.sparse = sparse_hits(p, N);
+  fa.sparse = filter_shape(p, N);
   HIPCHK(launch_filter(fa, 0, s), "launch filter");
   RefineArgs ra = refine_args(w, L, x, N, k, M, out_vals, out_idx);
   ra.msd_cap = 0xFFFFFFFFu;  // no host to hand an oversized bin to
@@ -753,6 +755,7 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[x];
     fa.rec = rec;
     fa.sels = nullptr;
+    fa.sparse = filter_shape(p, N);
     HIPCHK(launch_filter(fa, 0, s), "launch filter");
     HIPCHK(launch_b_refine(a, s), "launch b_refine");
     HIPCHK(hipMemcpyAsync(w->host, rec, B * sizeof(AttemptRecord), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");

@@ -484,10 +484,13 @@ hipError_t launch_filter_shape(const FilterArgs& a0, u32 grid, u32 blocks_per_cu
 // fastest while hits are rare (598 us against 617 us per 2^30 values at k = 32), but
 // a wavefront that stages hits stops issuing loads, and with one wavefront per SIMD
 // nothing covers for it (939 us at k = 2^19).  Three blocks of 4-float4 tiles keep the
-// rate when many tiles carry hits (645 us at k = 2^19, 1.0 ms for the batched rows).
+// rate when many tiles carry hits (645 us at k = 2^19, 1.0 ms for the batched rows), and
+// a fourth block per CU gains another ~1% once hits come in one value in 2048 or more
+// (k = 2^19 under the MI355X rule: one in ~820), while it costs ~1% where they are rarer.
 hipError_t launch_filter(const FilterArgs& a, u32 grid, hipStream_t s, u64* split_out) {
-  if (a.sparse) return launch_filter_shape<8>(a, grid, 1, s, split_out);
-  return launch_filter_shape<4>(a, grid, kFilterBlocksPerCU, s, split_out);
+  if (a.sparse == kShapeSparse) return launch_filter_shape<8>(a, grid, 1, s, split_out);
+  const u32 bpc = a.sparse == kShapeDenseHits ? kFilterBlocksPerCU + 1 : kFilterBlocksPerCU;
+  return launch_filter_shape<4>(a, grid, bpc, s, split_out);
 }
 
 }  // namespace profk
