@@ -201,26 +201,29 @@ __device__ __forceinline__ void test_tile(const FilterArgs& a, Stage& st, const 
     maybe |= mu[u];
   }
   if (__ballot(maybe)) {
-    // exact test, only for the float4 slots where some lane may hold a hit
-    // (4 ballots each); a sparse tile usually has one such slot
+    // exact test only for the float4 slots, and within them the components, where some
+    // lane may hold a hit: when hits are dense (one in a few hundred values) a slot
+    // usually has one such component, and the exact keys of the other three would
+    // cost three times the instructions
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (!__ballot(mu[u])) continue;
       const u64 vi = t.v0 + (u64)u * kWave + lane;
       const u32 i0 = (u32)(t.geo.head + 4 * vi);
       const float c[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      u64 masks[4];
-      bool hit[4];
-      u64 key[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        if (!__ballot(valid[u] && !(c[q] < tv))) continue;
         const u32 o = ord32(__float_as_uint(c[q]));
         const u32 i = i0 + q;
-        hit[q] = valid[u] && (o > tk || (o == tk && i <= ti));
-        key[q] = ((u64)o << 32) | (u64)(~i);
-        masks[q] = __ballot(hit[q]);
+        u64 masks[1];
+        bool hit[1];
+        u64 key[1];
+        hit[0] = valid[u] && (o > tk || (o == tk && i <= ti));
+        key[0] = ((u64)o << 32) | (u64)(~i);
+        masks[0] = __ballot(hit[0]);
+        stage_hits<1>(st, t.row, masks, hit, key, a.ctls, a.cand, a.M);
       }
-      stage_hits<4>(st, t.row, masks, hit, key, a.ctls, a.cand, a.M);
     }
   }
   if (t.tile == 0 && (t.geo.head | t.geo.tail)) {
