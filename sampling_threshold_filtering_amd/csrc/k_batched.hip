@@ -12,8 +12,9 @@
 //                     sort buffer).  It also clears the row's counter for the filter.
 //   filter_kernel     (k_filter.hip) one streaming pass over all listed rows.
 //   b_refine_kernel   one 256-thread workgroup per row: the min(R, M) <= 8192
-//                     candidates are sorted in LDS (sized to M) and the first k
-//                     written out.
+//                     candidates are loaded into LDS (sized to M), the k-th largest
+//                     is selected there (radix select), and the k keys at or above
+//                     it are sorted and written out.
 //   b_rowsort_kernel  rows of at most 8192 values: exact top-k by sorting the row
 //                     in LDS (the sample would not pay off there).
 #include "block_select.h"
@@ -279,13 +280,13 @@ __global__ __launch_bounds__(kBThreads) void b_sample_kernel(BatchedArgs a) {
   }
 }
 
-// Rows of at most kWaveRow candidates: one wavefront each, sorted in registers
-// (64*M keys, M per lane).  Larger rows: the whole workgroup; for k <= kWaveRow its
-// wavefronts sort chunks of kWaveRow in registers and a merge tree in LDS combines
-// their k largest (pow2(M) keys of dynamic LDS at most), else one LDS sort.
+// One workgroup per row (persistent over the listed rows).  A row of at most 64
+// candidates is sorted by one wavefront in registers.  Otherwise the candidates are
+// loaded into LDS, the k-th largest is found by a radix select there, the k keys at or
+// above it are gathered and sorted (one wavefront in registers up to 64, else an LDS
+// bitonic sort) and written out; for k above kSelCap the whole row is sorted in LDS.
 constexpr u32 kRefineThreads = 256;
-constexpr u32 kRefineWaves = kRefineThreads / kWave;
-constexpr u32 kWaveRow = 1024;
+constexpr u32 kSelCap = 1024;
 
 namespace {
 // Value bits from a key's order code, except the codes that fold encodings (+-0, NaN).
@@ -300,97 +301,81 @@ __device__ __forceinline__ void write_row_key(u64 key, u64 j, const float* row, 
   oi[j] = idx < N ? (int64_t)idx : -1;
   if (idx < N) reinterpret_cast<u32*>(ov)[j] = row_value_bits(key, row, idx);
 }
-
-template <int M>
-__device__ __forceinline__ void wave_row(const BatchedArgs& a, u32 row, const u64* cand, u32 n) {
-  const u32 lane = lane_id();
-  u64 v[M];
-#pragma unroll
-  for (int r = 0; r < M; ++r) {
-    const u32 i = (u32)r * kWave + lane;
-    v[r] = i < n ? cand[i] : 0ull;
-  }
-  wave_sort_regs_desc<M>(v);
-  const float* xr = a.x + (u64)row * a.ld;
-  float* ov = a.out_vals + (u64)row * a.k;
-  int64_t* oi = a.out_idx + (u64)row * a.k;
-#pragma unroll
-  for (int r = 0; r < M; ++r) {
-    const u32 i = (u32)r * kWave + lane;
-    if (i < a.k) write_row_key(v[r], i, xr, a.N, ov, oi);
-  }
-}
 }  // namespace
 
 __global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a) {
-  extern __shared__ u64 s[];
-  __shared__ u32 s_big[kRefineThreads];
-  __shared__ u32 s_nbig;
-  const u32 wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const u64 nwaves = (u64)gridDim.x * kRefineWaves;
-  if (threadIdx.x == 0) s_nbig = 0;
-  __syncthreads();
-  u32 nmine = 0;
-  for (u64 li = (u64)blockIdx.x * kRefineWaves + wid; li < a.nrows; li += nwaves) {
+  extern __shared__ u64 s[];  // pow2(M) keys
+  __shared__ u64 s_top[kSelCap];
+  __shared__ LdsSelect s_sel;
+  __shared__ u32 s_n;
+  const u32 tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  for (u64 li = blockIdx.x; li < a.nrows; li += gridDim.x) {
     const u32 row = a.rows ? (u32)a.rows[li] : (u32)li;
     const RowCtl* c = &a.ctls[row];
-    if (c->status != 0) continue;  // uniform per wavefront
-    const u64 R = c->R;
-    const u32 n = (u32)(R < a.M ? R : a.M);
-    const u64* cand = a.cand + (u64)row * a.M;
-    if (n > kWaveRow) {
-      if (lane_id() == 0 && nmine < kRefineThreads / kRefineWaves) s_big[atomicAdd(&s_nbig, 1u)] = row;
-      ++nmine;
-      continue;
-    }
-    if (n <= 64) wave_row<1>(a, row, cand, n);
-    else if (n <= 128) wave_row<2>(a, row, cand, n);
-    else if (n <= 256) wave_row<4>(a, row, cand, n);
-    else if (n <= 512) wave_row<8>(a, row, cand, n);
-    else wave_row<16>(a, row, cand, n);
-  }
-  __syncthreads();
-  const u32 nbig = s_nbig;
-  u32 T = 1;
-  while (T < a.k) T <<= 1;
-  for (u32 q = 0; q < nbig; ++q) {
-    const u32 row = s_big[q];
-    const RowCtl* c = &a.ctls[row];
+    if (c->status != 0) continue;  // uniform per workgroup
     const u64 R = c->R;
     const u32 n = (u32)(R < a.M ? R : a.M);
     const u64* cand = a.cand + (u64)row * a.M;
     const float* xr = a.x + (u64)row * a.ld;
+    float* ov = a.out_vals + (u64)row * a.k;
+    int64_t* oi = a.out_idx + (u64)row * a.k;
+    if (n <= (u32)kWave) {
+      if (wid == 0) {
+        const u64 v = wave_sort_desc(lane < n ? cand[lane] : 0ull);
+        if (lane < a.k) write_row_key(v, lane, xr, a.N, ov, oi);
+      }
+      continue;
+    }
+    __syncthreads();  // the previous row's users of s are done
+    constexpr u32 kILP = 8;
+    for (u32 base = 0; base < n; base += kRefineThreads * kILP) {
+      u64 kk[kILP];
+#pragma unroll
+      for (u32 q = 0; q < kILP; ++q) {
+        const u32 i = base + q * kRefineThreads + tid;
+        kk[q] = i < n ? cand[i] : 0ull;
+      }
+#pragma unroll
+      for (u32 q = 0; q < kILP; ++q) {
+        const u32 i = base + q * kRefineThreads + tid;
+        if (i < n) s[i] = kk[q];
+      }
+    }
     __syncthreads();
-    if (T <= kWaveRow) {
-      // chunks of kWaveRow candidates sorted by the wavefronts in registers, each
-      // keeping its T largest; the lists (at most pow2(M) keys) are then merged
-      const u32 nch = (n + kWaveRow - 1) / kWaveRow;
-      for (u32 ch = wid; ch < nch; ch += kRefineWaves) {
-        const u32 lane = lane_id();
-        u64 v[kWaveRow / kWave];
-#pragma unroll
-        for (u32 r = 0; r < kWaveRow / kWave; ++r) {
-          const u32 i = ch * kWaveRow + r * kWave + lane;
-          v[r] = i < n ? cand[i] : 0ull;
-        }
-        wave_sort_regs_desc<kWaveRow / kWave>(v);
-#pragma unroll
-        for (u32 r = 0; r < kWaveRow / kWave; ++r) {
-          const u32 e = r * kWave + lane;  // element e of the sorted chunk
-          if (e < T) s[ch * T + e] = v[r];
+    if (a.k <= kSelCap) {
+      const u64 kth = lds_select_desc(s, n, (u32)a.k, &s_sel);
+      if (tid == 0) s_n = 0;
+      __syncthreads();
+      for (u32 i = tid; i < n; i += kRefineThreads) {
+        const u64 key = s[i];
+        if (key >= kth) {
+          const u32 slot = atomicAdd(&s_n, 1u);
+          if (slot < kSelCap) s_top[slot] = key;
         }
       }
       __syncthreads();
-      block_merge_lists(s, nch, T);
+      const u32 m = s_n < a.k ? s_n : (u32)a.k;  // exactly k: the keys are distinct
+      if (m <= (u32)kWave) {
+        if (wid == 0) {
+          const u64 v = wave_sort_desc(lane < m ? s_top[lane] : 0ull);
+          if (lane < m) write_row_key(v, lane, xr, a.N, ov, oi);
+        }
+      } else {
+        u32 P = 1;
+        while (P < m) P <<= 1;
+        for (u32 i = m + tid; i < P; i += kRefineThreads) s_top[i] = 0ull;
+        __syncthreads();
+        block_bitonic_desc(s_top, P);
+        for (u32 j = tid; j < m; j += kRefineThreads) write_row_key(s_top[j], j, xr, a.N, ov, oi);
+      }
     } else {
       u32 P = 1;
       while (P < n) P <<= 1;
-      for (u32 i = threadIdx.x; i < P; i += blockDim.x) s[i] = i < n ? cand[i] : 0ull;
+      for (u32 i = n + tid; i < P; i += kRefineThreads) s[i] = 0ull;
       __syncthreads();
       block_bitonic_desc(s, P);
+      for (u32 j = tid; j < a.k; j += kRefineThreads) write_row_key(s[j], j, xr, a.N, ov, oi);
     }
-    for (u32 j = threadIdx.x; j < a.k; j += blockDim.x)
-      write_row_key(s[j], j, xr, a.N, a.out_vals + (u64)row * a.k, a.out_idx + (u64)row * a.k);
   }
 }
 
@@ -428,16 +413,8 @@ hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s) {
 
 hipError_t launch_b_refine(const BatchedArgs& a, hipStream_t s) {
   u32 P = 1;
-  while (P < a.M) P <<= 1;  // M <= kSmallSort: at most 64 KB
-  // one wavefront per row; each workgroup meets at most kRefineThreads / kRefineWaves
-  // rows per wavefront, which bounds its list of rows for the LDS path
-  u64 g = (a.nrows + kRefineWaves - 1) / kRefineWaves;
-  const u64 gmin = (a.nrows + (u64)kRefineThreads - 1) / kRefineThreads;
-  const u64 gmax = 8ull * device_cu_count();
-  if (g > gmax) g = gmax;
-  if (g < gmin) g = gmin;
-  if (g < 1) g = 1;
-  b_refine_kernel<<<(u32)g, kRefineThreads, (size_t)P * sizeof(u64), s>>>(a);
+  while (P < a.M) P <<= 1;  // M <= kSmallSort: at most 64 KB, so two workgroups per CU
+  b_refine_kernel<<<row_grid(a.nrows, 2), kRefineThreads, (size_t)P * sizeof(u64), s>>>(a);
   return hipGetLastError();
 }
 

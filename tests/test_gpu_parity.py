@@ -343,6 +343,8 @@ def check_batched(x2d, vals, idx, k):
     ("normal", 2, 1 << 21, 300, {}),                   # rows longer than the per-row kernels take
     ("normal", 16, 1 << 20, 3000, {"s_override": 32768}),  # radix-select sampler (t > 64), LDS row sorts
     ("with_nan", 24, 100000, 40, {"s_override": 8000}),    # many repeats and a long top-up; NaN at the top
+    ("uniform", 4, 1 << 17, 1024, {}),                 # k at the refinement's select-and-sort limit
+    ("pareto", 8, 1 << 16, 65, {}),                    # k just above one wavefront's sort
 ])
 def test_batched_shapes(kind, B, N, k, opts):
     say("batched", kind, B, N, k, opts)
