@@ -348,7 +348,7 @@ def check_batched(x2d, vals, idx, k):
 ])
 def test_batched_shapes(kind, B, N, k, opts):
     say("batched", kind, B, N, k, opts)
-    x = (generate(kind, B * N, seed=31) if kind in ("normal", "uniform") else edge_case(kind, B * N, 31)).reshape(B, N)
+    x = (generate(kind, B * N, seed=31) if kind in ("normal", "uniform", "pareto") else edge_case(kind, B * N, 31)).reshape(B, N)
     vals, idx, st = stf.topk_batched(dev(x), k, options=opts or None, stats=True)
     check_batched(x, vals, idx, k)
 
