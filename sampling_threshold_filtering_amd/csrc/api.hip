@@ -427,10 +427,11 @@ void update_die_weights(Workspace* w, const u64* split) {
 // The filter's launch shape by the expected density of hits.  The shape for rare hits
 // pays off only while few tiles carry a hit; R varies a lot from draw to draw at small t
 // (exponential at t = 1), so that test takes a high draw of R, E[R] + 3 sd(R), not its
-// mean.  Dense hits (E[R] >= N / 2048) take a fourth block per CU.
+// mean.  Dense hits (E[R] >= N / 2048, and N / 256) take more blocks per CU.
 u32 filter_shape(const profk_params& p, u64 N) {
   const double hi = p.E_R + 3.0 * std::sqrt(p.Var_R > 0.0 ? p.Var_R : 0.0);
   if (hi * 8192.0 <= (double)N) return kShapeSparse;
+  if (p.E_R * 256.0 >= (double)N) return kShapeVeryDenseHits;
   return p.E_R * 2048.0 >= (double)N ? kShapeDenseHits : 0u;
 }
 

@@ -481,18 +481,25 @@ hipError_t launch_filter_shape(const FilterArgs& a0, u32 grid, u32 blocks_per_cu
 }
 }  // namespace
 
-// Launch shape by the expected share of hits (measured on MI355X over 2^30 values, a
-// sweep of 4..16 float4 per lane and 1..8 blocks per CU): what matters is the bytes in
-// flight per CU.  One block of four wavefronts per CU with 8-float4 tiles streams
-// fastest while hits are rare (598 us against 617 us per 2^30 values at k = 32), but
-// a wavefront that stages hits stops issuing loads, and with one wavefront per SIMD
-// nothing covers for it (939 us at k = 2^19).  Three blocks of 4-float4 tiles keep the
-// rate when many tiles carry hits (645 us at k = 2^19, 1.0 ms for the batched rows), and
-// a fourth block per CU gains another ~1% once hits come in one value in 2048 or more
-// (k = 2^19 under the MI355X rule: one in ~820), while it costs ~1% where they are rarer.
+// Launch shape by the expected share of hits (measured on MI355X; 1..8 blocks per CU,
+// 4..16 float4 per lane).  One block of four wavefronts per CU with 8-float4 tiles
+// streams fastest while hits are rare (598 us per 2^30 values at k = 32), but a
+// wavefront that stages hits stops issuing loads, and with one wavefront per SIMD
+// nothing covers for it (939 us at k = 2^19).  Two blocks of 4-float4 tiles keep the
+// rate when tiles carry hits; a third costs 3-4 us per 2^30 values at k <= 2^15 and
+// 5-10% at 2^22..2^28 values (more blocks queue their end-of-stream reservations on R).
+// Four blocks per CU cover for the wavefronts that stage hits when hits come in one
+// value in 256 or more over 2^25 values or more (k = 2^19 over 2^26 values: 0.144
+// against 0.168 ms per call), or in one in 2048 or more over 2^29 values or more (k = 2^19
+// over 2^30 values under the MI355X rule: one in ~820, 692-696 against 706-708 us; the
+// batched rows).  Shorter passes keep two even then (2^22 values, k = 2^15: 0.068
+// against 0.078 ms).
 hipError_t launch_filter(const FilterArgs& a, u32 grid, hipStream_t s, u64* split_out) {
   if (a.sparse == kShapeSparse) return launch_filter_shape<8>(a, grid, 1, s, split_out);
-  const u32 bpc = a.sparse == kShapeDenseHits ? kFilterBlocksPerCU + 1 : kFilterBlocksPerCU;
+  const u64 n = a.N * a.nrows;
+  const bool four = (a.sparse == kShapeVeryDenseHits && n >= (1ull << 25)) ||
+                    (a.sparse == kShapeDenseHits && n >= (1ull << 29));
+  const u32 bpc = four ? 2 * kFilterBlocksPerCU : kFilterBlocksPerCU;
   return launch_filter_shape<4>(a, grid, bpc, s, split_out);
 }
 

@@ -13,9 +13,10 @@ constexpr u32 kFilterGroups = 32;
 constexpr u32 kFilterGroupStride = 32;  // u32 words between group counters
 constexpr u32 kTicketWords = kTickets + kFilterGroups * kFilterGroupStride + 32;
 constexpr u32 kXtimeWord = kTickets + kFilterGroups * kFilterGroupStride;  // u64-aligned, 2 x (kXcds + 1) words
-constexpr u32 kFilterBlocksPerCU = 3;  // persistent filter grid: 3 blocks x 4 waves per CU
+constexpr u32 kFilterBlocksPerCU = 2;  // persistent filter grid: 2 blocks x 4 waves per CU (4 for dense hits)
 constexpr u32 kShapeSparse = 1;        // filter launch shapes by expected hit density
-constexpr u32 kShapeDenseHits = 2;
+constexpr u32 kShapeDenseHits = 2;     // hits in one value in 2048 or more
+constexpr u32 kShapeVeryDenseHits = 3; // hits in one value in 256 or more
 constexpr u64 kFilterRun = 64;         // consecutive tiles per chunk when there are several rows
 
 // Compute units of the current device (cached per device).
@@ -48,8 +49,8 @@ struct FilterArgs {
   u32 seq;             // with hrec: the attempt's sequence number for hrec->early (row 0)
   u64 split[kXcds + 1];  // chunk ranges per die (set by launch_filter from weights)
   float weight[kXcds];   // relative speed of each die (input to launch_filter; 0 = equal)
-  u32 sparse;            // launch shape: kShapeSparse when hits are expected in fewer than one
-                         // value in 8192, kShapeDenseHits in one in 2048 or more, else 0
+  u32 sparse;            // launch shape by the expected density of hits: kShapeSparse (fewer
+                         // than one value in 8192), kShapeDenseHits, kShapeVeryDenseHits, or 0
   AttemptRecord* rec;  // per row, or nullptr
   SelState* sels;      // per row refinement selection to arm, or nullptr
   u64 tiles_per_row;   // set by launch_filter
