@@ -371,6 +371,7 @@ RefineArgs refine_args(Workspace* w, const Layout& L, const float* x, u64 N, u64
   ra.out_vals = out_vals;
   ra.out_idx = out_idx;
   ra.pool = at<u64>(w, L.pool);
+  ra.ticket = at<u32>(w, L.ticket) + kTicketRefine;
   return ra;
 }
 

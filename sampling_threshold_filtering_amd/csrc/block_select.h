@@ -217,97 +217,241 @@ __device__ inline u64 block_select_finish(const u64* keys, u64 n, u64* buf, u32 
   return result;
 }
 
-struct LdsSelect {
-  u32 hist[256];
-  u64 prefix, mask;
-  u32 rank, count, state;  // state: 0 = running, 1 = at most kWave keys match, 2 = too few keys
+constexpr u32 kMaxWaves = 16;  // wavefronts of a 1024-thread block
+
+constexpr u32 kSelCopies = 8;  // interleaved copies of the digit histogram, by lane & 7
+
+struct alignas(16) LdsSelect {
+  // digit d's count in hist[d * kSelCopies .. + kSelCopies); past them one slot per lane
+  // for keys that do not match
+  u32 hist[256 * kSelCopies + kWave];
+  u64 prefix;
+  u32 rank, state;  // state: 0 = running, 1 = at most kWave keys match, 2 = too few keys
   u32 nsmall;
   u64 small[kWave];
   u64 result;
+  u64 wand[kMaxWaves], wor[kMaxWaves];  // per-wavefront AND / OR of the nonzero keys
+  u32 wnz[kMaxWaves];                   // per-wavefront count of the nonzero keys
 };
 
-// The key of descending rank `rank` (1-based) among the nonzero, distinct keys
-// s[0..n) held in LDS, by the whole block: 8-bit digits from the top, each pass a
-// histogram of the keys that match the digits fixed so far, until at most kWave keys
-// match; those are ranked against each other by one wavefront.  Returns 0 when fewer
-// than `rank` nonzero keys are present.
-__device__ inline u64 lds_select_desc(const u64* s, u32 n, u32 rank, LdsSelect* L) {
+// Radix selection of the key of descending rank `rank` (1-based) among distinct nonzero
+// keys, by the whole block (256 to 1024 threads), in steps that share this state: the
+// leading bits that all the keys share (where their AND and OR agree) are fixed first;
+// 8-bit digits follow from there, each pass a histogram of the keys that match the
+// digits fixed so far, until at most kWave keys match; those are ranked against each
+// other.  With one wavefront per SIMD nothing hides latency, so the steps avoid
+// dependent chains: cross-lane work goes through DPP and readlane rather than the LDS
+// crossbar, counting is branch-free, and the gather reserves one range per wavefront.
+struct SelPass {
+  u64 prefix, mask;
+  u32 want, state, d0;
+};
+
+__device__ __forceinline__ u64 wave_and64(u64 v) {
+  auto f = [](u32 x, u32 y) { return x & y; };
+  return ((u64)wave_reduce_u32((u32)(v >> 32), f) << 32) | wave_reduce_u32((u32)v, f);
+}
+__device__ __forceinline__ u64 wave_or64(u64 v) {
+  auto f = [](u32 x, u32 y) { return x | y; };
+  return ((u64)wave_reduce_u32((u32)(v >> 32), f) << 32) | wave_reduce_u32((u32)v, f);
+}
+__device__ __forceinline__ u32 wave_sum32(u32 v) {
+  return wave_reduce_u32(v, [](u32 x, u32 y) { return x + y; });
+}
+
+// Per-thread AND / OR / count of its nonzero keys in; the block's combined state out.
+__device__ __forceinline__ SelPass sel_begin(u64 va, u64 vo, u32 nz, u32 rank, LdsSelect* L) {
   const u32 tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  const u32 nw = blockDim.x / kWave;
+  va = wave_and64(va);
+  vo = wave_or64(vo);
+  nz = wave_sum32(nz);
+  if (lane == 0) {
+    L->wand[wid] = va;
+    L->wor[wid] = vo;
+    L->wnz[wid] = nz;
+  }
   if (tid == 0) {
-    L->prefix = 0;
-    L->mask = 0;
-    L->rank = rank;
-    L->count = 0xFFFFFFFFu;
-    L->state = 0;
     L->nsmall = 0;
     L->result = 0;
   }
-  for (u32 d = 0; d < 8; ++d) {
-    for (u32 b = tid; b < 256; b += blockDim.x) L->hist[b] = 0;
-    __syncthreads();
-    const u64 prefix = L->prefix, mask = L->mask;
-    const u32 shift = 56u - 8u * d;
-    for (u32 i = tid; i < n; i += blockDim.x) {
-      const u64 k = s[i];
-      if (k != 0 && (k & mask) == prefix) atomicAdd(&L->hist[(u32)(k >> shift) & 255u], 1u);
+  __syncthreads();
+  // lane w takes wavefront w's values; then the same reductions over the lanes
+  const bool in = lane < nw;
+  const u64 a = wave_and64(in ? L->wand[lane] : ~0ull);
+  const u64 o = wave_or64(in ? L->wor[lane] : 0ull);
+  const u32 n = wave_sum32(in ? L->wnz[lane] : 0u);
+  // bits above the highest one where the keys differ are common to all of them
+  const u64 diff = a ^ o;
+  SelPass p;
+  p.d0 = diff ? (u32)__clzll((long long)diff) / 8u : 8u;
+  p.mask = p.d0 ? ~0ull << (64u - 8u * p.d0) : 0ull;
+  p.prefix = a & p.mask;
+  p.want = rank;
+  p.state = n < rank ? 2u : n <= (u32)kWave ? 1u : 0u;
+  return p;
+}
+
+// After a digit histogram in L->hist: wavefront 0 finds the digit that holds the rank;
+// every thread takes the new state.  Ends with the block synchronised.
+__device__ __forceinline__ void sel_choose(SelPass& p, u32 shift, LdsSelect* L) {
+  const u32 lane = lane_id();
+  if (threadIdx.x < (u32)kWave) {
+    if (lane == 0) L->state = 2u;  // replaced by the lane whose digit holds the rank
+    // descending digits: lane owns 255 - 4*lane .. 255 - 4*lane - 3
+    u32 c[4], sum = 0;
+#pragma unroll
+    for (u32 r = 0; r < 4; ++r) {
+      const uint4* h = reinterpret_cast<const uint4*>(L->hist + (255u - (4u * lane + r)) * kSelCopies);
+      const uint4 x = h[0], y = h[1];
+      c[r] = x.x + x.y + x.z + x.w + y.x + y.y + y.z + y.w;
+      sum += c[r];
     }
-    __syncthreads();
-    if (wid == 0) {
-      // descending digits: lane owns 255 - 4*lane .. 255 - 4*lane - 3
-      u32 c[4], sum = 0;
+    u32 run = wave_incl_scan_add(sum, lane) - sum;
 #pragma unroll
-      for (u32 r = 0; r < 4; ++r) {
-        c[r] = L->hist[255u - (4u * lane + r)];
-        sum += c[r];
+    for (u32 r = 0; r < 4; ++r) {
+      if (run < p.want && run + c[r] >= p.want) {
+        const u32 dg = 255u - (4u * lane + r);
+        L->rank = p.want - run;
+        L->prefix = p.prefix | ((u64)dg << shift);
+        L->state = c[r] <= (u32)kWave ? 1u : 0u;
       }
-      u32 incl = sum;
-#pragma unroll
-      for (u32 o = 1; o < (u32)kWave; o <<= 1) {
-        const u32 v = __shfl_up(incl, o);
-        if (lane >= o) incl += v;
-      }
-      const u32 want = L->rank;
-      const u32 total = __shfl(incl, kWave - 1);
-      u32 run = incl - sum;
-#pragma unroll
-      for (u32 r = 0; r < 4; ++r) {
-        if (run < want && run + c[r] >= want) {
-          const u32 dg = 255u - (4u * lane + r);
-          L->rank = want - run;
-          L->count = c[r];
-          L->prefix = prefix | ((u64)dg << shift);
-          L->mask = mask | (0xFFull << shift);
-          L->state = c[r] <= (u32)kWave ? 1u : 0u;
-        }
-        run += c[r];
-      }
-      if (lane == 0 && total < want) L->state = 2;
+      run += c[r];
     }
-    __syncthreads();
-    if (L->state != 0) break;
   }
-  if (L->state == 1) {
-    const u64 prefix = L->prefix, mask = L->mask;
-    for (u32 i = tid; i < n; i += blockDim.x) {
-      const u64 k = s[i];
-      if (k != 0 && (k & mask) == prefix) {
-        const u32 slot = atomicAdd(&L->nsmall, 1u);
-        if (slot < (u32)kWave) L->small[slot] = k;
-      }
-    }
-    __syncthreads();
+  __syncthreads();
+  p.prefix = L->prefix;
+  p.mask |= 0xFFull << shift;
+  p.want = L->rank;
+  p.state = L->state;
+}
+
+__device__ __forceinline__ bool sel_match(u64 k, const SelPass& p) { return k != 0 && (k & p.mask) == p.prefix; }
+
+// Key k's digit counted into L->hist with no branch and one LDS atomic: lane l adds to
+// copy l & 7 of the digit's count, so a digit that a whole wavefront shares costs
+// eight-way conflicts on eight banks rather than 64 on one address; a key that does
+// not match adds to its lane's spare slot.
+__device__ __forceinline__ void sel_count(u64 k, const SelPass& p, u32 shift, u32 lane, LdsSelect* L) {
+  const u32 b = sel_match(k, p) ? ((u32)(k >> shift) & 255u) * kSelCopies + (lane & (kSelCopies - 1)) : 256u * kSelCopies + lane;
+  atomicAdd(&L->hist[b], 1u);
+}
+
+__device__ __forceinline__ void sel_clear_hist(LdsSelect* L) {
+  uint4* h = reinterpret_cast<uint4*>(L->hist);
+  for (u32 b = threadIdx.x; b < 256 * kSelCopies / 4; b += blockDim.x) h[b] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+}
+
+// Slot in L->small of a thread's first matching key, the wavefront's keys taking one
+// contiguous range: an exclusive scan of the per-thread counts and one LDS atomic.
+__device__ __forceinline__ u32 sel_reserve(u32 cnt, u32 lane, LdsSelect* L) {
+  const u32 incl = wave_incl_scan_add(cnt, lane);
+  const u32 total = (u32)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+  u32 base = 0;
+  if (total != 0 && lane == 0) base = atomicAdd(&L->nsmall, total);
+  return (u32)__builtin_amdgcn_readlane((int)base, 0) + incl - cnt;
+}
+
+// The (at most kWave) keys gathered in L->small are ranked against each other, four
+// threads per key, sixteen comparisons each; the key of rank p.want is the result.
+__device__ __forceinline__ u64 sel_finish(const SelPass& p, LdsSelect* L) {
+  __syncthreads();
+  if (p.state == 1) {
     const u32 m = L->nsmall < (u32)kWave ? L->nsmall : (u32)kWave;
-    if (wid == 0 && lane < m) {
-      const u64 k = L->small[lane];
+    for (u32 t = threadIdx.x; t < 4u * kWave; t += blockDim.x) {
+      const u32 i = t >> 2, part = t & 3u;
+      const u64 k = L->small[i];
+      u64 o[16];
+#pragma unroll
+      for (u32 j = 0; j < 16; ++j) o[j] = L->small[part * 16u + j];
       u32 r = 0;
-      for (u32 j = 0; j < m; ++j) r += L->small[j] > k ? 1u : 0u;
-      if (r + 1u == L->rank) L->result = k;
+#pragma unroll
+      for (u32 j = 0; j < 16; ++j) r += (part * 16u + j < m && o[j] > k) ? 1u : 0u;
+      r += (u32)__builtin_amdgcn_update_dpp(0, (int)r, 0xB1, 0xF, 0xF, false);
+      r += (u32)__builtin_amdgcn_update_dpp(0, (int)r, 0x4E, 0xF, 0xF, false);
+      if (part == 0 && i < m && r + 1u == p.want) L->result = k;
     }
   }
   __syncthreads();
   const u64 result = L->result;
   __syncthreads();
   return result;
+}
+
+// The key of descending rank `rank` (1-based) among the nonzero, distinct keys s[0..n)
+// held in LDS.  Returns 0 when fewer than `rank` nonzero keys are present.
+__device__ inline u64 lds_select_desc(const u64* s, u32 n, u32 rank, LdsSelect* L) {
+  const u32 tid = threadIdx.x, lane = lane_id();
+  u64 va = ~0ull, vo = 0;
+  u32 nz = 0;
+  for (u32 i = tid; i < n; i += blockDim.x) {
+    const u64 k = s[i];
+    const bool h = k != 0;
+    va &= h ? k : ~0ull;
+    vo |= k;
+    nz += h ? 1u : 0u;
+  }
+  SelPass p = sel_begin(va, vo, nz, rank, L);
+  for (u32 d = p.d0; d < 8 && p.state == 0; ++d) {
+    sel_clear_hist(L);
+    const u32 shift = 56u - 8u * d;
+    for (u32 i = tid; i < n; i += blockDim.x) sel_count(s[i], p, shift, lane, L);
+    __syncthreads();
+    sel_choose(p, shift, L);
+  }
+  if (p.state == 1) {
+    u32 cnt = 0;
+    for (u32 i = tid; i < n; i += blockDim.x) cnt += sel_match(s[i], p) ? 1u : 0u;
+    u32 slot = sel_reserve(cnt, lane, L);
+    for (u32 i = tid; i < n && cnt; i += blockDim.x) {
+      const u64 k = s[i];
+      if (sel_match(k, p)) {
+        if (slot < (u32)kWave) L->small[slot] = k;
+        ++slot;
+        --cnt;
+      }
+    }
+  }
+  return sel_finish(p, L);
+}
+
+// The same selection with the keys in registers: thread t holds v[0..P), zero for no
+// key.  A pass then reads no keys, it only counts digits.
+template <u32 P>
+__device__ inline u64 reg_select_desc(const u64 (&v)[P], u32 rank, LdsSelect* L) {
+  const u32 lane = lane_id();
+  u64 va = ~0ull, vo = 0;
+  u32 nz = 0;
+#pragma unroll
+  for (u32 q = 0; q < P; ++q) {
+    const bool h = v[q] != 0;
+    va &= h ? v[q] : ~0ull;
+    vo |= v[q];
+    nz += h ? 1u : 0u;
+  }
+  SelPass p = sel_begin(va, vo, nz, rank, L);
+  for (u32 d = p.d0; d < 8 && p.state == 0; ++d) {
+    sel_clear_hist(L);
+    const u32 shift = 56u - 8u * d;
+#pragma unroll
+    for (u32 q = 0; q < P; ++q) sel_count(v[q], p, shift, lane, L);
+    __syncthreads();
+    sel_choose(p, shift, L);
+  }
+  if (p.state == 1) {
+    u32 cnt = 0;
+#pragma unroll
+    for (u32 q = 0; q < P; ++q) cnt += sel_match(v[q], p) ? 1u : 0u;
+    u32 slot = sel_reserve(cnt, lane, L);
+#pragma unroll
+    for (u32 q = 0; q < P; ++q)
+      if (sel_match(v[q], p)) {
+        if (slot < (u32)kWave) L->small[slot] = v[q];
+        ++slot;
+      }
+  }
+  return sel_finish(p, L);
 }
 
 // Convenience: the whole selection from scratch.

@@ -644,6 +644,113 @@ __global__ __launch_bounds__(kSortThreads) void refine_binsort_kernel(RefineArgs
   }
 }
 
+// One launch for small k (k <= kSmallK), in place of the three above.  Each of the
+// first G workgroups takes a contiguous share of at most kSmallShare candidates into
+// registers and keeps its k largest (an 8-bit radix select over them, then the keys at
+// or above the k-th) in a list of k slots in tmp, zero-padded; the last of them to
+// finish takes the G lists, selects the k-th largest of their union the same way and
+// sorts the k keys at or above it (one wavefront, in registers).  The k largest
+// candidates are among the lists, since each is among the k largest of its own share.
+// The workgroups past the first G only clear the sampler's hash set (16-byte stores).
+constexpr u32 kSmallK = 64;
+constexpr u32 kSmallThreads = 256;
+constexpr u32 kSmallPer = 16;                               // candidates per thread
+constexpr u32 kSmallShare = kSmallThreads * kSmallPer;      // per workgroup
+constexpr u32 kSmallLists = 2 * kSmallShare;                // keys of the union
+constexpr u32 kClearPerBlock = kSmallThreads * 4;           // 16-byte words per clearing workgroup
+
+// g[0..m) into registers, thread t taking g[t + q * kSmallThreads]; zero past m.
+template <u32 P>
+__device__ __forceinline__ void small_load(u64 (&v)[P], const u64* g, u32 m) {
+#pragma unroll
+  for (u32 q = 0; q < P; ++q) {
+    const u32 i = q * kSmallThreads + threadIdx.x;
+    v[q] = i < m ? g[i] : 0ull;
+  }
+}
+
+// The keys of v at or above kth (all nonzero ones when kth is 0) into dst, at most cap.
+template <u32 P>
+__device__ __forceinline__ void small_gather(const u64 (&v)[P], u64 kth, u64* dst, u32 cap, u32* n) {
+#pragma unroll
+  for (u32 q = 0; q < P; ++q)
+    if (v[q] != 0 && v[q] >= kth) {
+      const u32 slot = atomicAdd(n, 1u);
+      if (slot < cap) dst[slot] = v[q];
+    }
+}
+
+__global__ __launch_bounds__(kSmallThreads) void refine_small_kernel(RefineArgs a, u32 G) {
+  __shared__ LdsSelect s_sel;
+  __shared__ u64 s_top[kSmallK];
+  __shared__ u32 s_n, s_last;
+  const u32 tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  if (blockIdx.x >= G) {  // leave the sampler's hash set zero for the next attempt
+    uint4* t = reinterpret_cast<uint4*>(a.table);
+    const u64 words = a.table_slots / 4, gs = (u64)(gridDim.x - G) * kSmallThreads;
+    for (u64 i = (u64)(blockIdx.x - G) * kSmallThreads + tid; i < words; i += gs) t[i] = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  const RowCtl* c = a.ctl;
+  if (blockIdx.x == 0 && tid == 0) {
+    if (a.rec) a.rec->generic = 0;
+    publish(a, c, 0u);
+  }
+  const bool live = refine_live(a, c);
+  const u64 n = live ? cand_count(c, a.M) : 0;
+  const u32 k = (u32)a.k;
+  if (a.approx) {
+    const u64 gt = (u64)blockIdx.x * kSmallThreads + tid, gs = (u64)G * kSmallThreads;
+    if (gt == 0 && a.info) {
+      a.info->R = (int64_t)c->R;
+      a.info->M = (int64_t)a.M;
+      a.info->status = (int32_t)c->status;
+      a.info->exact_path = 0;
+    }
+    for (u64 p = n + gt; p < a.k; p += gs) {
+      a.out_idx[p] = -1;
+      reinterpret_cast<u32*>(a.out_vals)[p] = 0xFF800000u;  // -inf
+    }
+  }
+  if (!live) return;
+  // this workgroup's share (at most kSmallShare: the grid is sized to M) and its k largest
+  const u64 per = (n + G - 1) / G;
+  const u64 lo = (u64)blockIdx.x * per < n ? (u64)blockIdx.x * per : n;
+  const u32 m = (u32)((lo + per < n ? lo + per : n) - lo);
+  {
+    u64 v[kSmallPer];
+    small_load(v, a.cand + lo, m);
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    u64* list = a.tmp + (u64)blockIdx.x * k;
+    // the keys are distinct and nonzero: exactly k of them are at or above the k-th
+    const u64 kth = m <= k ? 0ull : reg_select_desc(v, k, &s_sel);
+    if (m <= k)
+      for (u32 i = m + tid; i < k; i += kSmallThreads) list[i] = 0ull;
+    small_gather(v, kth, list, k, &s_n);
+  }
+  // every thread releases its list writes; then elect the last workgroup
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(a.ticket, 1u) == G - 1 ? 1u : 0u;
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  u64 v[kSmallLists / kSmallThreads];
+  small_load(v, a.tmp, G * k);  // <= kSmallLists: the grid is sized for it
+  if (tid == 0) s_n = 0;
+  // the k-th largest of the union; with fewer than k candidates (approximate mode) all
+  const u64 kth = reg_select_desc(v, k, &s_sel);
+  small_gather(v, kth, s_top, k, &s_n);
+  __syncthreads();
+  const u32 nt = s_n < k ? s_n : k;
+  if (wid == 0) {
+    const u64 key = wave_sort_desc(lane < nt ? s_top[lane] : 0ull);
+    if (lane < nt) write_out(a, lane, key);
+  }
+  if (tid == 0) atomic_store_agent(a.ticket, 0u);
+}
+
 __global__ void approx_info_exact_kernel(ApproxInfo* info, u64 N) {
   if (threadIdx.x == 0) {
     info->R = (int64_t)N;
@@ -659,6 +766,15 @@ hipError_t launch_approx_info_exact(ApproxInfo* info, u64 N, hipStream_t s) {
 }
 
 hipError_t launch_refine(const RefineArgs& a, hipStream_t s) {
+  // small k: one launch, when the union of the workgroups' lists fits in LDS
+  const u64 gsm = (a.M + kSmallShare - 1) / kSmallShare;
+  if (a.k <= kSmallK && gsm * a.k <= kSmallLists) {
+    const u32 G = (u32)(gsm ? gsm : 1);
+    const u64 words = a.table ? a.table_slots / 4 : 0;  // slots: a power of two >= 16
+    const u64 z = (words + kClearPerBlock - 1) / kClearPerBlock;
+    refine_small_kernel<<<G + (u32)(z < 256 ? z : 256), kSmallThreads, 0, s>>>(a, G);
+    return hipGetLastError();
+  }
   // about 4 candidates per thread at R = M (R is mostly well below M): more blocks keep
   // more candidate loads in flight, but each adds its nonzero bins to the global
   // histogram and reserves its runs with atomics (measured on MI355X over 2^30 Pareto

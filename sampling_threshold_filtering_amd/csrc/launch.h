@@ -65,6 +65,7 @@ constexpr u32 kTicketFilter = 0;  // filter kernel
 constexpr u32 kTicketSample = 8;  // sampling kernel: one u64 at slots 8-9 (8-byte aligned),
                                   // (blocks done << 32) | distinct draws so far
 constexpr u32 kCountStage = 4;    // output counter of the stage entry points
+constexpr u32 kTicketRefine = 16; // one-launch refinement for small k
 constexpr u32 kTopT = 64;         // largest t of the per-block-list threshold path
 constexpr u32 kTopBlocks = 128;   // most sampling blocks of that path (S <= 131072)
 
@@ -151,6 +152,7 @@ struct RefineArgs {
   float* out_vals;
   int64_t* out_idx;
   u64* pool;        // msd_pool_words(M) words: work lists of the oversized-bin partition
+  u32* ticket;      // zero, left zero: the one-launch refinement's last-block election
   u32 msd_cap;      // largest needed bin partitioned in-kernel; larger ones defer to the
                     // multi-pass refinement (the host reads the flag)
   u32 approx;       // 1: no run-time check (approximate mode): refine whatever the buffer

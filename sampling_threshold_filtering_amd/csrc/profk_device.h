@@ -117,6 +117,33 @@ __device__ __forceinline__ u32 wave_reserve32(u32* counter, bool pred) {
 
 // Exchange with lane ^ J.  Strides 1, 2, 4, 8 use DPP lane moves (plain ALU
 // operations); 16 and 32 go through the LDS crossbar (ds_bpermute).
+// Reduction over the whole wavefront with an associative, commutative f: DPP within
+// rows of 16 (quad_perm xor 1 and xor 2, then row_ror 4 and 8), then the four row
+// results read out to scalars.  Every lane gets the result.
+template <class F>
+__device__ __forceinline__ u32 wave_reduce_u32(u32 v, F f) {
+  v = f(v, (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = f(v, (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = f(v, (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+  v = f(v, (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+  const u32 r0 = (u32)__builtin_amdgcn_readlane((int)v, 0), r1 = (u32)__builtin_amdgcn_readlane((int)v, 16);
+  const u32 r2 = (u32)__builtin_amdgcn_readlane((int)v, 32), r3 = (u32)__builtin_amdgcn_readlane((int)v, 48);
+  return f(f(r0, r1), f(r2, r3));
+}
+
+// Inclusive prefix sum over the wavefront: row_shr 1, 2, 4, 8 within rows of 16 (lanes
+// whose source falls before the row start add zero), then the totals of the rows below.
+__device__ __forceinline__ u32 wave_incl_scan_add(u32 v, u32 lane) {
+  v += (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);
+  v += (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);
+  v += (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);
+  v += (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);
+  const u32 s1 = (u32)__builtin_amdgcn_readlane((int)v, 15), s2 = (u32)__builtin_amdgcn_readlane((int)v, 31);
+  const u32 s3 = (u32)__builtin_amdgcn_readlane((int)v, 47);
+  const u32 row = lane >> 4;
+  return v + (row >= 1 ? s1 : 0u) + (row >= 2 ? s2 : 0u) + (row >= 3 ? s3 : 0u);
+}
+
 template <u32 J>
 __device__ __forceinline__ u32 lane_xor_u32(u32 v, u32 lane) {
   if constexpr (J == 1) {  // quad_perm [1,0,3,2]
