@@ -659,25 +659,60 @@ constexpr u32 kSmallShare = kSmallThreads * kSmallPer;      // per workgroup
 constexpr u32 kSmallLists = 2 * kSmallShare;                // keys of the union
 constexpr u32 kClearPerBlock = kSmallThreads * 4;           // 16-byte words per clearing workgroup
 
+// The lists pass between workgroups through agent-scope atomic stores and loads, which
+// the compiler issues with the device-coherence cache bit (written through, read from
+// the coherence point), and an explicit wait for the stores before the election
+// counter's increment.  An agent-scope release / acquire fence would do the same but also
+// write back / invalidate the whole L2 of the die, which the hash-set clearing
+// workgroups have just filled with dirty lines: about 4 us per call.
+__device__ __forceinline__ u64 ld_agent(const u64* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_agent(u64* p, u64 v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// All of this thread's memory operations complete (s_waitcnt 0), with compiler fences
+// around it so that none of them moves past it.
+__device__ __forceinline__ void drain_memory_ops() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // g[0..m) into registers, thread t taking g[t + q * kSmallThreads]; zero past m.
-template <u32 P>
+// kShared: g holds another workgroup's lists, read with agent-scope atomic loads.
+template <bool kShared, u32 P>
 __device__ __forceinline__ void small_load(u64 (&v)[P], const u64* g, u32 m) {
 #pragma unroll
   for (u32 q = 0; q < P; ++q) {
     const u32 i = q * kSmallThreads + threadIdx.x;
-    v[q] = i < m ? g[i] : 0ull;
+    v[q] = i < m ? (kShared ? ld_agent(g + i) : g[i]) : 0ull;
   }
 }
 
 // The keys of v at or above kth (all nonzero ones when kth is 0) into dst, at most cap.
-template <u32 P>
+// kShared: dst is a list another workgroup reads, written with agent-scope atomic stores.
+template <bool kShared, u32 P>
 __device__ __forceinline__ void small_gather(const u64 (&v)[P], u64 kth, u64* dst, u32 cap, u32* n) {
 #pragma unroll
   for (u32 q = 0; q < P; ++q)
     if (v[q] != 0 && v[q] >= kth) {
       const u32 slot = atomicAdd(n, 1u);
-      if (slot < cap) dst[slot] = v[q];
+      if (slot < cap) {
+        if (kShared) st_agent(dst + slot, v[q]);
+        else dst[slot] = v[q];
+      }
     }
+}
+
+// The k largest of g[0..m) (all of them when fewer than k are nonzero) into dst, in no
+// particular order, P keys per thread in registers; *cnt is zero on entry.  The number of
+// registers is a template constant, so the caller picks the smallest P that holds m.
+// kIn / kOut: g / dst are lists shared between workgroups (see small_load, small_gather).
+template <bool kIn, bool kOut, u32 P>
+__device__ __forceinline__ void small_keep(const u64* g, u32 m, u32 k, u64* dst, LdsSelect* L, u32* cnt) {
+  u64 v[P];
+  small_load<kIn>(v, g, m);
+  // distinct nonzero keys: exactly k of them are at or above the k-th
+  const u64 kth = reg_select_desc(v, k, L);
+  small_gather<kOut>(v, kth, dst, k, cnt);
 }
 
 __global__ __launch_bounds__(kSmallThreads) void refine_small_kernel(RefineArgs a, u32 G) {
@@ -717,31 +752,30 @@ __global__ __launch_bounds__(kSmallThreads) void refine_small_kernel(RefineArgs 
   const u64 per = (n + G - 1) / G;
   const u64 lo = (u64)blockIdx.x * per < n ? (u64)blockIdx.x * per : n;
   const u32 m = (u32)((lo + per < n ? lo + per : n) - lo);
+  if (tid == 0) s_n = 0;
+  __syncthreads();
   {
-    u64 v[kSmallPer];
-    small_load(v, a.cand + lo, m);
-    if (tid == 0) s_n = 0;
-    __syncthreads();
     u64* list = a.tmp + (u64)blockIdx.x * k;
-    // the keys are distinct and nonzero: exactly k of them are at or above the k-th
-    const u64 kth = m <= k ? 0ull : reg_select_desc(v, k, &s_sel);
-    if (m <= k)
-      for (u32 i = m + tid; i < k; i += kSmallThreads) list[i] = 0ull;
-    small_gather(v, kth, list, k, &s_n);
+    if (m <= k) {
+      for (u32 i = tid; i < k; i += kSmallThreads) st_agent(list + i, i < m ? a.cand[lo + i] : 0ull);
+    } else if (m <= 4 * kSmallThreads) {
+      small_keep<false, true, 4>(a.cand + lo, m, k, list, &s_sel, &s_n);
+    } else {
+      small_keep<false, true, kSmallPer>(a.cand + lo, m, k, list, &s_sel, &s_n);
+    }
   }
-  // every thread releases its list writes; then elect the last workgroup
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // every thread's list stores complete; then elect the last workgroup
+  drain_memory_ops();
   __syncthreads();
   if (tid == 0) s_last = atomicAdd(a.ticket, 1u) == G - 1 ? 1u : 0u;
   __syncthreads();
   if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  u64 v[kSmallLists / kSmallThreads];
-  small_load(v, a.tmp, G * k);  // <= kSmallLists: the grid is sized for it
   if (tid == 0) s_n = 0;
   // the k-th largest of the union; with fewer than k candidates (approximate mode) all
-  const u64 kth = reg_select_desc(v, k, &s_sel);
-  small_gather(v, kth, s_top, k, &s_n);
+  const u32 nl = G * k;  // <= kSmallLists: the grid is sized for it
+  if (nl <= 4 * kSmallThreads) small_keep<true, false, 4>(a.tmp, nl, k, s_top, &s_sel, &s_n);
+  else if (nl <= kSmallPer * kSmallThreads) small_keep<true, false, kSmallPer>(a.tmp, nl, k, s_top, &s_sel, &s_n);
+  else small_keep<true, false, kSmallLists / kSmallThreads>(a.tmp, nl, k, s_top, &s_sel, &s_n);
   __syncthreads();
   const u32 nt = s_n < k ? s_n : k;
   if (wid == 0) {
