@@ -659,22 +659,11 @@ constexpr u32 kSmallShare = kSmallThreads * kSmallPer;      // per workgroup
 constexpr u32 kSmallLists = 2 * kSmallShare;                // keys of the union
 constexpr u32 kClearPerBlock = kSmallThreads * 4;           // 16-byte words per clearing workgroup
 
-// The lists pass between workgroups through agent-scope atomic stores and loads, which
-// the compiler issues with the device-coherence cache bit (written through, read from
-// the coherence point), and an explicit wait for the stores before the election
-// counter's increment.  An agent-scope release / acquire fence would do the same but also
-// write back / invalidate the whole L2 of the die, which the hash-set clearing
-// workgroups have just filled with dirty lines: about 4 us per call.
-__device__ __forceinline__ u64 ld_agent(const u64* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ void st_agent(u64* p, u64 v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-
-// All of this thread's memory operations complete (s_waitcnt 0), with compiler fences
-// around it so that none of them moves past it.
-__device__ __forceinline__ void drain_memory_ops() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
+// The lists pass between workgroups through agent-scope atomic stores and loads and a
+// store-completion wait before the election counter's increment (ld_agent, st_agent,
+// drain_memory_ops): an agent-scope release / acquire fence would also write back /
+// invalidate the whole L2 of the die, which the hash-set clearing workgroups have just
+// filled with dirty lines, about 4 us per call.
 
 // g[0..m) into registers, thread t taking g[t + q * kSmallThreads]; zero past m.
 // kShared: g holds another workgroup's lists, read with agent-scope atomic loads.

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
     const u32 bits = __float_as_uint(a.x[idx]);  // issued before the insert: both in flight
     fresh = hash_insert(a.table, a.tmask, idx);
     if (fresh) key = make_key(bits, idx);
-    a.keys[j] = key;
+    st_agent(a.keys + j, key);
   }
   const u64 fm = __ballot(fresh);
   if (lane == 0) s_wcnt[wid] = (u32)__popcll(fm);
@@ -148,16 +148,16 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
       if (s_sel.hist[b]) atomicAdd(&a.top_hist[b], s_sel.hist[b]);
   } else if (a.fast) {
     block_merge_lists(s_buf, kSampleWaves, T);  // the block's T largest keys
-    for (u32 i = threadIdx.x; i < T; i += blockDim.x) a.tops[(u64)blockIdx.x * T + i] = s_buf[i];
+    for (u32 i = threadIdx.x; i < T; i += blockDim.x) st_agent(a.tops + (u64)blockIdx.x * T + i, s_buf[i]);
   }
-  // release this block's keys and lists, then elect the last block: one atomic adds
-  // the block to the ticket and its distinct draws to the count, so the last block
-  // has the total from the atomic's return value
+  // this block's keys and lists complete (written through at agent scope), then elect
+  // the last block: one atomic adds the block to the ticket and its distinct draws to
+  // the count, so the last block has the total from the atomic's return value
+  drain_memory_ops();
   __syncthreads();
   if (threadIdx.x == 0) {
     u32 tot = 0;
     for (u32 w = 0; w < kSampleWaves; ++w) tot += s_wcnt[w];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const u64 old = atomicAdd(a.ticket, (1ull << 32) | (u64)tot);
     const bool last = (u32)(old >> 32) == gridDim.x - 1;
     s_last = last ? 1u : 0u;

@@ -117,6 +117,24 @@ __device__ __forceinline__ u32 wave_reserve32(u32* counter, bool pred) {
 
 // Exchange with lane ^ J.  Strides 1, 2, 4, 8 use DPP lane moves (plain ALU
 // operations); 16 and 32 go through the LDS crossbar (ds_bpermute).
+// Hand-off of data between workgroups without cache maintenance.  Agent-scope atomic
+// loads and stores are issued with the device-coherence cache bit (stores written
+// through, loads served from the coherence point), so they need no L2 writeback or
+// invalidate; a writer makes its stores complete (drain_memory_ops) before the atomic
+// that publishes them, and the reader reads them with ld_agent after seeing that
+// atomic.  An agent-scope release / acquire fence orders the same way but also writes
+// back / invalidates the die's whole L2 (every dirty line in it, not just the writer's).
+__device__ __forceinline__ u64 ld_agent(const u64* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_agent(u64* p, u64 v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// All of this thread's memory operations complete (s_waitcnt 0), with compiler fences
+// around it so that none of them moves past it.
+__device__ __forceinline__ void drain_memory_ops() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Reduction over the whole wavefront with an associative, commutative f: DPP within
 // rows of 16 (quad_perm xor 1 and xor 2, then row_ror 4 and 8), then the four row
 // results read out to scalars.  Every lane gets the result.
