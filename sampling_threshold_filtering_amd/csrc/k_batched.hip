@@ -304,7 +304,7 @@ __device__ __forceinline__ void write_row_key(u64 key, u64 j, const float* row, 
 }  // namespace
 
 __global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a) {
-  extern __shared__ u64 s[];  // pow2(M) keys
+  extern __shared__ u64 s[];  // pow2(M) keys, M <= kBatchedMaxM
   __shared__ u64 s_top[kSelCap];
   __shared__ LdsSelect s_sel;
   __shared__ u32 s_n;
@@ -413,8 +413,14 @@ hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s) {
 
 hipError_t launch_b_refine(const BatchedArgs& a, hipStream_t s) {
   u32 P = 1;
-  while (P < a.M) P <<= 1;  // M <= kSmallSort: at most 64 KB, so two workgroups per CU
-  b_refine_kernel<<<row_grid(a.nrows, 2), kRefineThreads, (size_t)P * sizeof(u64), s>>>(a);
+  while (P < a.M) P <<= 1;  // M <= kBatchedMaxM: at most 128 KB (two workgroups per CU up to 64 KB)
+  const size_t lds = (size_t)P * sizeof(u64);
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&b_refine_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  b_refine_kernel<<<row_grid(a.nrows, 2), kRefineThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 

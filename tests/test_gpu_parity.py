@@ -353,6 +353,38 @@ def test_batched_shapes(kind, B, N, k, opts):
     check_batched(x, vals, idx, k)
 
 
+@pytest.mark.parametrize("B,k", [(128, 512), (64, 1024), (64, 2048)])
+def test_batched_buffers_past_8192_keys_stay_on_the_batched_kernels(B, k):
+    """Rows of 2^20 under the MI355X S rule with k = 512 / 1024 / 2048 need per-row
+    buffers of 8710 / 10054 / 13069 keys; the batched refinement holds up to 16384 in
+    LDS (select then sort for k <= 1024, a full LDS sort above), so these rows run on the
+    batched kernels.  A row-by-row loop would take some 40 times the k = 64 call."""
+    import torch
+    say("batched large buffers", B, k)
+    N = 1 << 20
+    o = stf.make_options(s_rule=2)
+    assert 8192 < stf.solve(N, k, 1e-3 / B, options=o)["M"] <= 16384
+    x = generate("pareto", B * N, seed=k).reshape(B, N)
+    xd = dev(x)
+
+    def timed(kk):
+        stf.topk_batched(xd, kk, options=o)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        out = stf.topk_batched(xd, kk, seed=1, options=o)
+        e1.record()
+        e1.synchronize()
+        return out, e0.elapsed_time(e1)
+
+    _, t64 = timed(64)
+    (vals, idx), tk = timed(k)
+    print("[case] ms k=64", round(t64, 3), "k", k, round(tk, 3), flush=True)
+    check_batched(x, vals, idx, k)
+    assert tk < 8 * t64
+
+
 def test_batched_strided_rows():
     say("batched strided ld = N + 3")
     B, N, ld, k = 24, 1 << 18, (1 << 18) + 3, 50
