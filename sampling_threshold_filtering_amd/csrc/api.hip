@@ -667,8 +667,9 @@ int topk_approx_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* o
   return PROFK_OK;
 }
 
-// Batched form with per-row kernels (rows of at most kBatchedMaxN values whose
-// buffer, at most kBatchedMaxM keys, fits one workgroup's LDS).  Returns PROFK_EUNSUPPORTED when the shape
+// Batched form with per-row kernels (rows of at most kBatchedMaxN values, k at most
+// kBatchedMaxM: the refinement holds a row's buffer in LDS up to kBatchedMaxM keys,
+// and beyond that selects over it in global memory and sorts the k in LDS).  Returns PROFK_EUNSUPPORTED when the shape
 // is outside those limits, so that the caller takes the row-by-row path.
 int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u64 seed, float* out_vals,
                       int64_t* out_idx, hipStream_t s, const profk_options* opt, profk_stats* st) {
@@ -699,7 +700,7 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
   int rc = solve_memo((int64_t)N, (int64_t)k, eps / (double)B, opt, &p);  // P1 App. E.2: eps / B per row
   if (rc) return rc;
   const int max_att = max_attempts_of(opt);
-  if (p.direct_exact || max_att == 0 || N > kBatchedMaxN || (u64)p.M > kBatchedMaxM || (u64)p.S > kBatchedMaxN / 8)
+  if (p.direct_exact || max_att == 0 || N > kBatchedMaxN || k > kBatchedMaxM || (u64)p.S > kBatchedMaxN / 8)
     return PROFK_EUNSUPPORTED;
   const u64 S = (u64)p.S, M = (u64)p.M, t = (u64)p.t;
   const u64 G = batched_sample_blocks(B);

@@ -304,9 +304,10 @@ __device__ __forceinline__ void write_row_key(u64 key, u64 j, const float* row, 
 }  // namespace
 
 __global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a) {
-  extern __shared__ u64 s[];  // pow2(M) keys, M <= kBatchedMaxM
+  extern __shared__ u64 s[];  // pow2(min(M, kBatchedMaxM)) keys
   __shared__ u64 s_top[kSelCap];
   __shared__ LdsSelect s_sel;
+  __shared__ BlockSelectLds s_bsel;
   __shared__ u32 s_n;
   const u32 tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   for (u64 li = blockIdx.x; li < a.nrows; li += gridDim.x) {
@@ -327,6 +328,31 @@ __global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a)
       continue;
     }
     __syncthreads();  // the previous row's users of s are done
+    if (n > kBatchedMaxM) {
+      // more candidates than LDS holds: the k-th largest by the one-workgroup radix
+      // select over the buffer in global memory, then the k keys at or above it (k <=
+      // kBatchedMaxM, the host's bound) are gathered into LDS and sorted there
+      bool ok = false;
+      const u64 kth = block_select_rank(cand, n, a.k, s, (u32)kBatchedMaxM, &s_bsel, &ok);
+      if (tid == 0) s_n = 0;
+      __syncthreads();
+      for (u32 i = tid; i < n; i += kRefineThreads) {
+        const u64 key = cand[i];
+        if (key >= kth) {
+          const u32 slot = atomicAdd(&s_n, 1u);
+          if (slot < (u32)kBatchedMaxM) s[slot] = key;
+        }
+      }
+      __syncthreads();
+      const u32 m = s_n < a.k ? s_n : (u32)a.k;  // exactly k: the keys are distinct
+      u32 P = 1;
+      while (P < m) P <<= 1;
+      for (u32 i = m + tid; i < P; i += kRefineThreads) s[i] = 0ull;
+      __syncthreads();
+      block_bitonic_desc(s, P);
+      for (u32 j = tid; j < m; j += kRefineThreads) write_row_key(s[j], j, xr, a.N, ov, oi);
+      continue;
+    }
     constexpr u32 kILP = 8;
     for (u32 base = 0; base < n; base += kRefineThreads * kILP) {
       u64 kk[kILP];
@@ -413,7 +439,7 @@ hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s) {
 
 hipError_t launch_b_refine(const BatchedArgs& a, hipStream_t s) {
   u32 P = 1;
-  while (P < a.M) P <<= 1;  // M <= kBatchedMaxM: at most 128 KB (two workgroups per CU up to 64 KB)
+  while (P < a.M && P < kBatchedMaxM) P <<= 1;  // at most 128 KB (two workgroups per CU up to 64 KB)
   const size_t lds = (size_t)P * sizeof(u64);
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&b_refine_kernel),

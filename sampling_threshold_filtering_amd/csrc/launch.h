@@ -166,7 +166,8 @@ hipError_t launch_approx_info_exact(ApproxInfo* info, u64 N, hipStream_t s);
 
 // Batched form (k_batched.hip): rows of at most kBatchedMaxN values.
 constexpr u64 kBatchedMaxN = 1ull << 20;
-// Per-row candidate buffer the batched refinement holds in LDS: pow2(M) keys, 128 KB.
+// Batched refinement: a row buffer of up to this many keys is held in LDS (128 KB); k
+// is at most this.
 constexpr u64 kBatchedMaxM = 1ull << 14;
 
 struct BatchedArgs {
