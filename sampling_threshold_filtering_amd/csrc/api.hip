@@ -674,8 +674,14 @@ int topk_approx_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* o
 int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u64 seed, float* out_vals,
                       int64_t* out_idx, hipStream_t s, const profk_options* opt, profk_stats* st) {
   if (B >= (1ull << 31)) return PROFK_EUNSUPPORTED;
-  if (N <= kSmallSort) {
-    // rows this short: exact top-k by an LDS sort of each row
+  profk_params p{};
+  if (N > kSmallSort) {
+    const int rc = solve_memo((int64_t)N, (int64_t)k, eps / (double)B, opt, &p);  // P1 App. E.2: eps / B per row
+    if (rc) return rc;
+  }
+  if (N <= kSmallSort || (N <= kBatchedMaxM && p.direct_exact)) {
+    // rows this short, or short rows where the sample would not pay off: exact top-k by
+    // an LDS sort of each row
     Layout L;
     Workspace* w = nullptr;
     int rc = get_workspace(s, Need{B, 0, 0, 1}, &w, &L);
@@ -696,9 +702,7 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     }
     return PROFK_OK;
   }
-  profk_params p{};
-  int rc = solve_memo((int64_t)N, (int64_t)k, eps / (double)B, opt, &p);  // P1 App. E.2: eps / B per row
-  if (rc) return rc;
+  int rc = PROFK_OK;
   const int max_att = max_attempts_of(opt);
   if (p.direct_exact || max_att == 0 || N > kBatchedMaxN || k > kBatchedMaxM || (u64)p.S > kBatchedMaxN / 8)
     return PROFK_EUNSUPPORTED;

@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a)
 }
 
 __global__ __launch_bounds__(kBThreads) void b_rowsort_kernel(BatchedArgs a) {
-  __shared__ u64 s[kSmallSort];
+  extern __shared__ u64 s[];  // pow2(N) keys, N <= kBatchedMaxM
   u32 P = 1;
   while (P < a.N) P <<= 1;
   for (u64 li = blockIdx.x; li < a.nrows; li += gridDim.x) {
@@ -451,7 +451,16 @@ hipError_t launch_b_refine(const BatchedArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_b_rowsort(const BatchedArgs& a, hipStream_t s) {
-  b_rowsort_kernel<<<row_grid(a.nrows, 2), kBThreads, 0, s>>>(a);
+  if (a.N > kBatchedMaxM) return hipErrorInvalidValue;
+  u32 P = 1;
+  while (P < a.N) P <<= 1;
+  const size_t lds = (size_t)P * sizeof(u64);  // at most 128 KB
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&b_rowsort_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  b_rowsort_kernel<<<row_grid(a.nrows, 2), kBThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 

@@ -387,6 +387,19 @@ def test_batched_buffers_past_8192_keys_stay_on_the_batched_kernels(B, k):
     assert tk < 8 * t64
 
 
+@pytest.mark.parametrize("kind,B,N,k", [("normal", 64, 9000, 1024), ("uniform", 20, 16384, 3000)])
+def test_batched_short_rows_without_a_paying_sample_are_sorted_whole(kind, B, N, k):
+    """Rows of up to 16384 values for which the solver finds that the sample does not pay
+    off (k a large share of the row) are sorted whole in LDS, one workgroup per row,
+    instead of running the exact selection row by row."""
+    say("batched direct rows", kind, B, N, k)
+    assert stf.solve(N, k, 1e-3 / B)["direct_exact"]
+    x = generate(kind, B * N, seed=N).reshape(B, N)
+    vals, idx, st = stf.topk_batched(dev(x), k, stats=True)
+    check_batched(x, vals, idx, k)
+    assert st["rows_fallback"] == B and st["attempts"] == 0
+
+
 def test_batched_strided_rows():
     say("batched strided ld = N + 3")
     B, N, ld, k = 24, 1 << 18, (1 << 18) + 3, 50
