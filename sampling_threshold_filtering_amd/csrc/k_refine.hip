@@ -1,7 +1,9 @@
 // Stage 4 of Prof-K ("Prof-K: Probabilistic One-Pass Filtering for Efficient Top-k
 // Selection", §3 stage 4): the exact top-k of the R buffered candidates, sorted.
-// The pages call a library top-k here (App. C); this is a binned refinement for
-// gfx950 that takes three launches whatever k is:
+// The pages call a library top-k here (App. C).  For k <= kSmallK one launch does it
+// (refine_small_kernel, below: per-workgroup top-k lists and a select over their union
+// by the last workgroup).  Larger k take a binned refinement for gfx950 in three
+// launches:
 //
 //   refine_hist_kernel     histogram of the candidates over kBins equal bins of the
 //                          key range [tau, cmax] (cmax = the largest candidate key,
