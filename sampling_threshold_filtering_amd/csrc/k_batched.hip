@@ -304,7 +304,7 @@ __device__ __forceinline__ void write_row_key(u64 key, u64 j, const float* row, 
 }  // namespace
 
 __global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a) {
-  extern __shared__ u64 s[];  // pow2(min(M, kBatchedMaxM)) keys
+  extern __shared__ u64 s[];  // M keys (k <= kSelCap), pow2(M) (k > kSelCap) or kBatchedMaxM (M above it)
   __shared__ u64 s_top[kSelCap];
   __shared__ LdsSelect s_sel;
   __shared__ BlockSelectLds s_bsel;
@@ -438,9 +438,17 @@ hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_b_refine(const BatchedArgs& a, hipStream_t s) {
-  u32 P = 1;
-  while (P < a.M && P < kBatchedMaxM) P <<= 1;  // at most 128 KB (two workgroups per CU up to 64 KB)
-  const size_t lds = (size_t)P * sizeof(u64);
+  // keys of LDS the rows need: the select path holds at most M, the whole-buffer sort
+  // pow2(M), and a buffer past kBatchedMaxM is selected over in global memory with an
+  // LDS buffer of kBatchedMaxM.  Two workgroups per CU while this stays near 64 KB.
+  u64 keys = a.M;
+  if (a.M > kBatchedMaxM) {
+    keys = kBatchedMaxM;
+  } else if (a.k > kSelCap) {
+    keys = 1;
+    while (keys < a.M) keys <<= 1;
+  }
+  const size_t lds = (size_t)keys * sizeof(u64);
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&b_refine_kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
