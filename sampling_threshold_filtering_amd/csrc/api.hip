@@ -746,6 +746,7 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     a.k = k;
     a.out_vals = out_vals;
     a.out_idx = out_idx;
+    a.rec = rec;
     HIPCHK(launch_b_sample(a, s), "launch b_sample");
     FilterArgs fa{};
     fa.x = x;

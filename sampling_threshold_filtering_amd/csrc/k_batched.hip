@@ -11,12 +11,18 @@
 //                     sample up, and the workgroup selects tau (LDS reused as the
 //                     sort buffer).  It also clears the row's counter for the filter.
 //   filter_kernel     (k_filter.hip) one streaming pass over all listed rows.
-//   b_refine_kernel   one 256-thread workgroup per row: the min(R, M) <= 8192
-//                     candidates are loaded into LDS (sized to M), the k-th largest
-//                     is selected there (radix select), and the k keys at or above
-//                     it are sorted and written out.
-//   b_rowsort_kernel  rows of at most 8192 values: exact top-k by sorting the row
-//                     in LDS (the sample would not pay off there).
+//   b_refine_kernel   one 256-thread workgroup per row, dynamic LDS sized per path.
+//                     Buffers of up to kBatchedMaxM = 16384 keys are loaded into LDS:
+//                     for k <= kSelCap the k-th largest is found by a radix select
+//                     there and the k keys at or above it are sorted (one wavefront in
+//                     registers up to 64, else an LDS bitonic sort); for larger k the
+//                     whole buffer is sorted (LDS of pow2(M) keys).  Larger buffers
+//                     select the k-th over global memory (the one-workgroup radix
+//                     select over L2) and sort the k keys at or above it in LDS; an
+//                     inconsistent select is reported in the row's attempt record.
+//   b_rowsort_kernel  rows of up to 16384 values where the sample would not pay off
+//                     (all rows of at most 8192): exact top-k by sorting the whole row
+//                     in LDS.
 #include "block_select.h"
 #include "launch.h"
 
@@ -334,6 +340,12 @@ __global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a)
       // kBatchedMaxM, the host's bound) are gathered into LDS and sorted there
       bool ok = false;
       const u64 kth = block_select_rank(cand, n, a.k, s, (u32)kBatchedMaxM, &s_bsel, &ok);
+      if (!ok) {
+        // the select came back inconsistent (never expected): report it instead of
+        // writing k arbitrary keys; the host turns it into PROFK_EINTERNAL
+        if (tid == 0 && a.rec) a.rec[row].error = 1u;
+        continue;  // uniform per workgroup
+      }
       if (tid == 0) s_n = 0;
       __syncthreads();
       for (u32 i = tid; i < n; i += kRefineThreads) {

@@ -186,6 +186,7 @@ struct BatchedArgs {
   u64 k;
   float* out_vals; // B x k
   int64_t* out_idx;
+  AttemptRecord* rec;  // per row: the refinement flags an internal error here, or nullptr
 };
 
 u32 batched_sample_blocks(u64 nrows);

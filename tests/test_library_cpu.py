@@ -160,7 +160,9 @@ def test_cost_model_rule_takes_the_given_cost_ratio(a, b):
 def test_mi355x_rule_is_proposition_7_with_the_measured_ratio():
     """The MI355X S rule: Algorithm 1 lines 1-4 with one constant 1/r, clipped to
     [2^12, 2^17], against the oracle's Proposition 7; S only changes speed, so the
-    exact (t*, M*) for that S must match the oracle too."""
+    exact (t*, M*) for that S must match the oracle too.  Parity unpinned for the
+    constants: 1/r = 0.022 and the clip range are measured on MI355X, so this only
+    checks that both sides apply Proposition 7 the same way to the same inputs."""
     for N in (1 << 22, 1 << 24, 1 << 26, 1 << 28, 1 << 30, 50331648, (1 << 32) - 1):
         for k in (32, 1024, 1 << 15, 1 << 17, 1 << 19):
             if k > N:
