@@ -218,6 +218,24 @@ int profk_stage_threshold(const float* x, int64_t N, int64_t S, int64_t t, uint6
                           int32_t attempt, float* out_tau_val, int64_t* out_tau_idx, void* stream);
 
 /*
+ * profk_stage_batched_sample: stages 1-2 of the batched form (P1 §3: the
+ *   procedure applied to each batch element; App. C: a threshold per row) for
+ *   rows 0..B-1 of x (row r at x + r*ld_x, N values).  Row r's sample is drawn
+ *   from the counter space of (seed, attempt, row r), exactly as in
+ *   profk_topk_batched.  Outputs (device):
+ *     out_idx      B*S int64: row r's S distinct sampled indices (in [0, N), in
+ *                  unspecified order) at out_idx[r*S .. r*S+S)
+ *     out_tau_val  B floats, out_tau_idx B int64: tau_r = the t-th entry of row
+ *                  r's sample in the total order (index within the row)
+ *   1 <= t <= S, 2S <= N <= 2^20 (rows longer than that: PROFK_EUNSUPPORTED),
+ *   ld_x >= N.  Synchronises the stream.  A device-side inconsistency in any
+ *   row gives PROFK_EINTERNAL.
+ */
+int profk_stage_batched_sample(const float* x, int64_t B, int64_t N, int64_t ld_x, int64_t S, int64_t t,
+                               uint64_t seed, int32_t attempt, int64_t* out_idx, float* out_tau_val,
+                               int64_t* out_tau_idx, void* stream);
+
+/*
  * profk_stage_filter: stage 3 (P1 §3; App. C "The Filter Kernel"): with the
  *   given tau = (tau_val, tau_idx), out_R[0] = R = number of entries at or
  *   before tau in the total order (exact, even past capacity), and the
@@ -226,6 +244,18 @@ int profk_stage_threshold(const float* x, int64_t N, int64_t S, int64_t t, uint6
  */
 int profk_stage_filter(const float* x, int64_t N, float tau_val, int64_t tau_idx, int64_t M,
                        int64_t* out_cand_idx, int64_t* out_R, void* stream);
+
+/*
+ * profk_read_ceiling: measurement helper, not part of the selection.  Reads
+ *   x[0..N) once with the filter's loads (dwordx4, non-temporal; stage 3 of P1
+ *   §3 reads every value once, App. C) and nothing else, and XORs the XOR of
+ *   all N values' bit patterns into *out_fold (device, one uint64).  Its
+ *   time on the same buffer is the practical ceiling of the filter's one-read
+ *   roofline on the device at hand.  x must be 16-byte aligned;
+ *   blocks_per_cu in 0..16 (0: 4) sets the persistent grid (256 threads per
+ *   block).  Enqueued on `stream`; does not wait.
+ */
+int profk_read_ceiling(const float* x, int64_t N, int32_t blocks_per_cu, uint64_t* out_fold, void* stream);
 
 /* Message for a status code (thread-local detail for PROFK_EHIP). */
 const char* profk_strerror(int code);

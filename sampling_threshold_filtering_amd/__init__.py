@@ -32,8 +32,8 @@ STATS_ATTEMPTS = 8
 
 EXPORTED = ("profk_topk", "profk_topk_ex", "profk_topk_approx", "profk_topk_batched", "profk_topk_batched_ex",
             "profk_solve",
-            "profk_stage_sample", "profk_stage_threshold", "profk_stage_filter", "profk_strerror",
-            "profk_release")
+            "profk_stage_sample", "profk_stage_threshold", "profk_stage_batched_sample", "profk_stage_filter",
+            "profk_read_ceiling", "profk_strerror", "profk_release")
 
 
 class Options(ctypes.Structure):
@@ -114,14 +114,17 @@ def load_library():
     lib.profk_solve.argtypes = [i64, i64, f64, ctypes.POINTER(Options), ctypes.POINTER(Params)]
     lib.profk_stage_sample.argtypes = [vp, i64, i64, u64, i32, vp, vp]
     lib.profk_stage_threshold.argtypes = [vp, i64, i64, i64, u64, i32, vp, vp, vp]
+    lib.profk_stage_batched_sample.argtypes = [vp, i64, i64, i64, i64, i64, u64, i32, vp, vp, vp, vp]
     lib.profk_stage_filter.argtypes = [vp, i64, ctypes.c_float, i64, i64, vp, vp, vp]
+    lib.profk_read_ceiling.argtypes = [vp, i64, i32, vp, vp]
+    lib.profk_read_ceiling.restype = ctypes.c_int
     lib.profk_strerror.argtypes = [ctypes.c_int]
     lib.profk_strerror.restype = ctypes.c_char_p
     lib.profk_release.argtypes = []
     lib.profk_release.restype = None
     for name in ("profk_topk", "profk_topk_ex", "profk_topk_approx", "profk_topk_batched", "profk_topk_batched_ex",
                  "profk_solve",
-                 "profk_stage_sample", "profk_stage_threshold", "profk_stage_filter"):
+                 "profk_stage_sample", "profk_stage_threshold", "profk_stage_batched_sample", "profk_stage_filter"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -304,6 +307,25 @@ def stage_threshold(x, S: int, t: int, seed: int = 0, attempt: int = 0):
     return v, i
 
 
+def stage_batched_sample(x, S: int, t: int, seed: int = 0, attempt: int = 0):
+    """Batched stages 1-2 on a 2-D float32 device tensor (rows may be strided):
+    (sample indices [B, S] int64, each row unordered; tau values [B]; tau indices [B])."""
+    import torch
+    if x.dim() != 2 or x.dtype != torch.float32 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 device tensor with unit column stride")
+    B, N = x.shape
+    ld = x.stride(0) if B > 1 else N
+    out = torch.empty((B, S), dtype=torch.int64, device=x.device)
+    tv = torch.empty(B, dtype=torch.float32, device=x.device)
+    ti = torch.empty(B, dtype=torch.int64, device=x.device)
+    with torch.cuda.device(x.device):
+        rc = load_library().profk_stage_batched_sample(ctypes.c_void_p(x.data_ptr()), B, N, ld, S, t, seed, attempt,
+                                                       ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(tv.data_ptr()),
+                                                       ctypes.c_void_p(ti.data_ptr()), _stream_ptr(torch, x.device))
+    _check(rc)
+    return out, tv, ti
+
+
 def stage_filter(x, tau_val: float, tau_idx: int, M: int):
     """(R, candidate indices of the min(R, M) kept entries, unordered)."""
     import torch
@@ -316,6 +338,23 @@ def stage_filter(x, tau_val: float, tau_idx: int, M: int):
     _check(rc)
     r = int(R.item())
     return r, cand[: min(r, M)]
+
+
+def read_ceiling(x, blocks_per_cu: int = 0, out=None):
+    """Measurement helper: one dwordx4 non-temporal read of a 1-D float32 device tensor
+    (16-byte aligned), nothing else; enqueued on the current stream.  XORs the XOR
+    of all values' bits into `out` (a one-word int64 tensor, or a new zero one) and
+    returns it."""
+    import torch
+    if x.dim() != 1 or x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 1-D float32 device tensor")
+    if out is None:
+        out = torch.zeros(1, dtype=torch.int64, device=x.device)
+    with torch.cuda.device(x.device):
+        rc = load_library().profk_read_ceiling(ctypes.c_void_p(x.data_ptr()), x.numel(), blocks_per_cu,
+                                               ctypes.c_void_p(out.data_ptr()), _stream_ptr(torch, x.device))
+    _check(rc)
+    return out
 
 
 def release():

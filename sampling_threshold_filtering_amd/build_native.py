@@ -18,7 +18,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libprofk.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "k_sample.hip", "k_select.hip", "k_filter.hip", "k_refine.hip", "k_sort.hip", "k_batched.hip", "k_merge.hip",
+SOURCES = ["api.hip", "k_sample.hip", "k_select.hip", "k_filter.hip", "k_refine.hip", "k_sort.hip", "k_batched.hip", "k_merge.hip", "k_probe.hip",
            "solver.cpp"]
 
 COMMON = [

@@ -931,6 +931,55 @@ int profk_stage_threshold(const float* x, int64_t N, int64_t S, int64_t t, uint6
   return PROFK_OK;
 }
 
+int profk_stage_batched_sample(const float* x, int64_t B, int64_t N, int64_t ld_x, int64_t S, int64_t t,
+                               uint64_t seed, int32_t attempt, int64_t* out_idx, float* out_tau_val,
+                               int64_t* out_tau_idx, void* stream) {
+  if (!x || !out_idx || !out_tau_val || !out_tau_idx || B < 1 || N < 2 || ld_x < N || S < 1 || 2 * S > N || t < 1 ||
+      t > S || attempt < 0)
+    return PROFK_EINVAL;
+  if ((u64)N > kBatchedMaxN || (u64)S > kBatchedMaxN / 8 || B >= (int64_t(1) << 31)) return PROFK_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  Layout L;
+  Workspace* w = nullptr;
+  const u64 nb = (u64)B;
+  int rc = get_workspace(s, Need{nb, 0, 1, 1, nb * 2 * (u64)S}, &w, &L);
+  if (rc) return rc;
+  rc = clean_if_dirty(w, L, s);
+  if (rc) return rc;
+  w->dirty = true;
+  RowCtl* ctl = at<RowCtl>(w, L.ctl);
+  AttemptRecord* rec = at<AttemptRecord>(w, L.rec);
+  u64* scratch = at<u64>(w, L.scratch);
+  HIPCHK(launch_attempt_init(ctl, nullptr, rec, at<u32>(w, L.ticket), (u32)nb, nullptr, s), "launch attempt_init");
+  // every row's 2S key slots start at zero, so that the nonzero ones are its sample
+  HIPCHK(launch_clear_sample(reinterpret_cast<u32*>(scratch), nb * 4 * (u64)S, at<u32>(w, L.ticket), s),
+         "launch clear scratch");
+  BatchedArgs a{};
+  a.x = x;
+  a.ld = (u64)ld_x;
+  a.N = (u64)N;
+  a.rows = nullptr;
+  a.nrows = nb;
+  a.S = (u64)S;
+  a.t = (u64)t;
+  a.seed = seed;
+  a.attempt = (u32)attempt;
+  a.ctls = ctl;
+  a.scratch = scratch;
+  HIPCHK(launch_b_sample(a, s, (u32)nb), "launch b_sample");
+  HIPCHK(launch_b_stage_out(x, (u64)ld_x, (u64)N, nb, (u64)S, scratch, ctl, out_idx, out_tau_val, out_tau_idx, rec, s),
+         "launch b_stage_out");
+  HIPCHK(hipMemcpyAsync(w->host, rec, nb * sizeof(AttemptRecord), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+  HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  w->dirty = false;
+  for (u64 r = 0; r < nb; ++r)
+    if (w->host[r].status != 0) {
+      t_err = "batched sample: device consistency check failed in row " + std::to_string(r);
+      return PROFK_EINTERNAL;
+    }
+  return PROFK_OK;
+}
+
 int profk_stage_filter(const float* x, int64_t N, float tau_val, int64_t tau_idx, int64_t M, int64_t* out_cand_idx,
                        int64_t* out_R, void* stream) {
   if (!x || !out_cand_idx || !out_R || N < 1 || M < 1 || tau_idx < 0 || tau_idx >= N) return PROFK_EINVAL;
@@ -966,6 +1015,15 @@ int profk_stage_filter(const float* x, int64_t N, float tau_val, int64_t tau_idx
   HIPCHK(launch_r_to_output(ctl, out_R, s), "launch r_to_output");
   HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
   w->dirty = false;
+  return PROFK_OK;
+}
+
+int profk_read_ceiling(const float* x, int64_t N, int32_t blocks_per_cu, uint64_t* out_fold, void* stream) {
+  if (!x || !out_fold || N < 1 || blocks_per_cu < 0 || blocks_per_cu > 16) return PROFK_EINVAL;
+  if ((uintptr_t)x & 15u) return PROFK_EINVAL;
+  HIPCHK(launch_read_ceiling(x, (u64)N, (u32)blocks_per_cu, reinterpret_cast<unsigned long long*>(out_fold),
+                             (hipStream_t)stream),
+         "launch read_ceiling");
   return PROFK_OK;
 }
 

@@ -444,8 +444,43 @@ u32 row_grid(u64 nrows, u32 per_cu) {
 
 u32 batched_sample_blocks(u64 nrows) { return row_grid(nrows, 1); }
 
-hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s) {
-  b_sample_kernel<<<batched_sample_blocks(a.nrows), kBThreads, 0, s>>>(a);
+hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s, u32 grid) {
+  b_sample_kernel<<<grid ? grid : batched_sample_blocks(a.nrows), kBThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// Stage entry point of the batched sampler (one sampling workgroup per row, so row r's
+// keys stay in scratch[r * 2S .. r * 2S + 2S), zero on entry): row r's sample indices
+// in any order to out_idx[r * S ..], its threshold to out_tau_*[r], its status to rec[r].
+__global__ __launch_bounds__(256) void b_stage_out_kernel(const float* x, u64 ld, u64 N, u64 S, const u64* scratch,
+                                                          const RowCtl* ctls, int64_t* out_idx, float* out_tau_val,
+                                                          int64_t* out_tau_idx, AttemptRecord* rec) {
+  __shared__ u32 s_cnt;
+  const u32 row = blockIdx.x;
+  if (threadIdx.x == 0) s_cnt = 0;
+  __syncthreads();
+  const u64* keys = scratch + (u64)row * 2 * S;
+  for (u64 i0 = 0; i0 < 2 * S; i0 += blockDim.x) {
+    const u64 i = i0 + threadIdx.x;
+    const u64 key = i < 2 * S ? keys[i] : 0ull;
+    const u32 slot = wave_reserve32(&s_cnt, key != 0);
+    if (key != 0 && slot < S) out_idx[(u64)row * S + slot] = (int64_t)key_index(key);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const RowCtl* c = &ctls[row];
+    const u32 idx = key_index(c->tau);
+    const bool ok = c->status == 0 && idx < N && s_cnt == S;
+    out_tau_idx[row] = ok ? (int64_t)idx : -1;
+    if (ok) reinterpret_cast<u32*>(out_tau_val)[row] = reinterpret_cast<const u32*>(x + (u64)row * ld)[idx];
+    rec[row].status = ok ? 0u : 3u;
+  }
+}
+
+hipError_t launch_b_stage_out(const float* x, u64 ld, u64 N, u64 B, u64 S, const u64* scratch, const RowCtl* ctls,
+                              int64_t* out_idx, float* out_tau_val, int64_t* out_tau_idx, AttemptRecord* rec,
+                              hipStream_t s) {
+  b_stage_out_kernel<<<(u32)B, 256, 0, s>>>(x, ld, N, S, scratch, ctls, out_idx, out_tau_val, out_tau_idx, rec);
   return hipGetLastError();
 }
 

@@ -190,7 +190,12 @@ struct BatchedArgs {
 };
 
 u32 batched_sample_blocks(u64 nrows);
-hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s);
+// grid 0: the persistent grid (batched_sample_blocks); the stage entry point takes one
+// workgroup per row so that every row keeps its keys in its own scratch slice
+hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s, u32 grid = 0);
+hipError_t launch_b_stage_out(const float* x, u64 ld, u64 N, u64 B, u64 S, const u64* scratch, const RowCtl* ctls,
+                              int64_t* out_idx, float* out_tau_val, int64_t* out_tau_idx, AttemptRecord* rec,
+                              hipStream_t s);
 hipError_t launch_b_refine(const BatchedArgs& a, hipStream_t s);
 hipError_t launch_b_rowsort(const BatchedArgs& a, hipStream_t s);
 
@@ -206,6 +211,9 @@ struct SegmentLists {
   u64 base[kMaxSegments];    // first global index of segment g
 };
 hipError_t launch_merge_segments(const SegmentLists& L, float* out_vals, int64_t* out_idx, hipStream_t s);
+
+// Measurement helper (k_probe.hip): one dwordx4 non-temporal streaming read of x.
+hipError_t launch_read_ceiling(const float* x, u64 N, u32 blocks_per_cu, unsigned long long* out, hipStream_t s);
 
 hipError_t launch_sort_and_write(u64* buf0, u64* buf1, u32* hist, u32 k, const float* row, u64 N, float* out_vals,
                                  int64_t* out_idx, RowCtl* ctl, AttemptRecord* rec, hipStream_t s);

@@ -436,3 +436,14 @@ def test_rare_hit_cases_take_the_sparse_filter_shape():
     for kind, N, k, opts in SMALL[-2:]:
         p = stf.solve(N, k, 1e-3, options=opts)
         assert (p["E_R"] + 3 * math.sqrt(p["Var_R"])) * 8192 <= N, (N, k, p["E_R"], p["Var_R"])
+
+
+@pytest.mark.parametrize("N", [1 << 24, (1 << 20) + 3, 5])
+def test_read_ceiling_probe_reads_every_value(N):
+    """The measurement helper behind the read ceiling must read every value once: its
+    fold is the XOR of all bit patterns."""
+    say("read ceiling probe", N)
+    x = generate("normal", N, seed=50)
+    out = stf.read_ceiling(dev(x))
+    want = int(np.bitwise_xor.reduce(x.view(np.uint32)))
+    assert int(host(out)[0]) == want
