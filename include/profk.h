@@ -56,6 +56,7 @@ extern "C" {
 #define PROFK_ENOMEM (-3)       /* workspace allocation failed */
 #define PROFK_EHIP (-4)         /* a HIP runtime call failed */
 #define PROFK_EINTERNAL (-5)    /* a device-side consistency check failed */
+#define PROFK_ESCRATCH (-6)     /* profk_topk_approx_noalloc: the call needs more than the static scratch */
 
 /* Overrides for tests and experiments.  Zero-initialise for defaults. */
 typedef struct profk_options {
@@ -171,6 +172,32 @@ typedef struct profk_approx_info {
 
 int profk_topk_approx(const float* x, int64_t N, int64_t k, double eps, uint64_t seed, float* out_vals,
                       int64_t* out_idx, profk_approx_info* info, void* stream, const profk_options* opt);
+
+/*
+ * profk_topk_approx_noalloc: profk_topk_approx for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It calls no hipMalloc,
+ * hipFree, hipHostMalloc or other allocating runtime routine; its workspace is
+ * a static device array of PROFK_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds from the time the library is loaded until the process
+ * ends.  The first call on a device looks up the array's device address
+ * (hipGetSymbolAddress): make that call outside graph capture.  The first call
+ * for a (N, k, eps, options) configuration computes and memoises its
+ * parameters on the host (host heap only).
+ *   Arguments, outputs and *info are those of profk_topk_approx; the results
+ *   are bit-identical to profk_topk_approx's for the same arguments.
+ *   Returns PROFK_ESCRATCH, without enqueuing anything, when the configuration
+ *   needs more workspace than the array holds (64 MiB: every k up to 2^19 at
+ *   N up to 2^30 under every S rule; larger k or N may not fit).
+ * Every call on one GPU uses that GPU's single array, which keeps what the last
+ * call left in it; each call first clears the parts that must start at zero.
+ * Calls that overlap in time on one GPU (other streams, other threads) race on
+ * the array and give wrong results: serialise them.
+ */
+#define PROFK_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+int profk_topk_approx_noalloc(const float* x, int64_t N, int64_t k, double eps, uint64_t seed, float* out_vals,
+                              int64_t* out_idx, profk_approx_info* info, void* stream, const profk_options* opt);
 
 /*
  * profk_topk_batched: row-wise exact top-k of B rows (P1 §3: the procedure

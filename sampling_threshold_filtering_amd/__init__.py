@@ -27,10 +27,12 @@ PROFK_EUNSUPPORTED = -2
 PROFK_ENOMEM = -3
 PROFK_EHIP = -4
 PROFK_EINTERNAL = -5
+PROFK_ESCRATCH = -6
 
 STATS_ATTEMPTS = 8
 
-EXPORTED = ("profk_topk", "profk_topk_ex", "profk_topk_approx", "profk_topk_batched", "profk_topk_batched_ex",
+EXPORTED = ("profk_topk", "profk_topk_ex", "profk_topk_approx", "profk_topk_approx_noalloc", "profk_topk_batched",
+            "profk_topk_batched_ex",
             "profk_solve",
             "profk_stage_sample", "profk_stage_threshold", "profk_stage_batched_sample", "profk_stage_filter",
             "profk_read_ceiling", "profk_strerror", "profk_release")
@@ -108,6 +110,7 @@ def load_library():
     lib.profk_topk_ex.argtypes = [vp, i64, i64, f64, u64, vp, vp, vp, ctypes.POINTER(Options),
                                   ctypes.POINTER(Stats)]
     lib.profk_topk_approx.argtypes = [vp, i64, i64, f64, u64, vp, vp, vp, vp, ctypes.POINTER(Options)]
+    lib.profk_topk_approx_noalloc.argtypes = [vp, i64, i64, f64, u64, vp, vp, vp, vp, ctypes.POINTER(Options)]
     lib.profk_topk_batched.argtypes = [vp, i64, i64, i64, i64, f64, u64, vp, vp, vp]
     lib.profk_topk_batched_ex.argtypes = [vp, i64, i64, i64, i64, f64, u64, vp, vp, vp, ctypes.POINTER(Options),
                                           ctypes.POINTER(Stats)]
@@ -122,7 +125,8 @@ def load_library():
     lib.profk_strerror.restype = ctypes.c_char_p
     lib.profk_release.argtypes = []
     lib.profk_release.restype = None
-    for name in ("profk_topk", "profk_topk_ex", "profk_topk_approx", "profk_topk_batched", "profk_topk_batched_ex",
+    for name in ("profk_topk", "profk_topk_ex", "profk_topk_approx", "profk_topk_approx_noalloc", "profk_topk_batched",
+                 "profk_topk_batched_ex",
                  "profk_solve",
                  "profk_stage_sample", "profk_stage_threshold", "profk_stage_batched_sample", "profk_stage_filter"):
         getattr(lib, name).restype = ctypes.c_int
@@ -216,6 +220,18 @@ def topk_approx(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, out=N
     indices, info) where info is an int64 device tensor of 3 words holding the
     profk_approx_info record; decode it with approx_info().  `out` and `info`
     reuse caller buffers."""
+    return _topk_approx("profk_topk_approx", x, k, eps, seed, options, out, info)
+
+
+def topk_approx_noalloc(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, out=None, info=None):
+    """profk_topk_approx_noalloc: topk_approx on the library's static scratch (the
+    library allocates no device memory).  Pass `out` and `info` to keep torch's
+    allocator out of it as well.  Raises ProfkError (code PROFK_ESCRATCH) when the
+    call needs more scratch than the static array holds."""
+    return _topk_approx("profk_topk_approx_noalloc", x, k, eps, seed, options, out, info)
+
+
+def _topk_approx(entry, x, k, eps, seed, options, out, info):
     import torch
     if x.dim() != 1 or x.dtype != torch.float32 or not x.is_cuda:
         raise ValueError("x must be a 1-D float32 device tensor")
@@ -235,11 +251,12 @@ def topk_approx(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, out=N
     args = (ctypes.c_void_p(x.data_ptr()), x.numel(), k, eps, seed & (2**64 - 1), ctypes.c_void_p(vals.data_ptr()),
             ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(info.data_ptr()),
             ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream), _opt_ptr(options))
+    fn = getattr(lib, entry)
     if dev.index == torch.cuda.current_device():
-        rc = lib.profk_topk_approx(*args)
+        rc = fn(*args)
     else:
         with torch.cuda.device(dev):
-            rc = lib.profk_topk_approx(*args)
+            rc = fn(*args)
     _check(rc)
     return vals, idx, info
 

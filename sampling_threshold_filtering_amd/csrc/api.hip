@@ -631,17 +631,12 @@ int topk_segmented(const float* x, u64 N, u64 k, double eps, u64 seed, float* ou
 
 // Approximate mode: one sampled attempt, everything enqueued on the stream, no host
 // read (P1 App. D: omitting the check).  The refinement runs on whatever the buffer
-// holds and reports the check's outcome in *info.
-int topk_approx_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* out_vals, int64_t* out_idx,
-                    ApproxInfo* info, hipStream_t s, const profk_options* opt) {
-  profk_params p{};
-  int rc = solve_memo((int64_t)N, (int64_t)k, eps, opt, &p);
-  if (rc) return rc;
-  const bool sampled = !p.direct_exact && !(opt && opt->force_fallback);
-  Layout L;
-  Workspace* w = nullptr;
-  rc = get_workspace(s, Need{1, sampled ? (u64)p.S : 0, sampled ? (u64)p.M : 0, k}, &w, &L);
-  if (rc) return rc;
+// holds and reports the check's outcome in *info.  Enqueues into the workspace w
+// laid out as L (the cached one, or the static scratch of the entry point that
+// allocates nothing); allocates nothing itself.
+int approx_enqueue(Workspace* w, const Layout& L, const profk_params& p, bool sampled, const float* x, u64 N, u64 k,
+                   u64 seed, float* out_vals, int64_t* out_idx, ApproxInfo* info, hipStream_t s) {
+  int rc = PROFK_OK;
   if (!sampled) {
     rc = run_exact(w, L, x, N, k, out_vals, out_idx, s, false);
     if (rc) return rc;
@@ -665,6 +660,95 @@ int topk_approx_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* o
   HIPCHK(launch_refine(ra, s), "launch refine");
   w->dirty = false;
   return PROFK_OK;
+}
+
+int topk_approx_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* out_vals, int64_t* out_idx,
+                    ApproxInfo* info, hipStream_t s, const profk_options* opt) {
+  profk_params p{};
+  int rc = solve_memo((int64_t)N, (int64_t)k, eps, opt, &p);
+  if (rc) return rc;
+  const bool sampled = !p.direct_exact && !(opt && opt->force_fallback);
+  Layout L;
+  Workspace* w = nullptr;
+  rc = get_workspace(s, Need{1, sampled ? (u64)p.S : 0, sampled ? (u64)p.M : 0, k}, &w, &L);
+  if (rc) return rc;
+  return approx_enqueue(w, L, p, sampled, x, N, k, seed, out_vals, out_idx, info, s);
+}
+
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing (profk_topk_approx_noalloc).  Its workspace is
+// the static device array `scratch` below: every GPU the library runs on holds its own
+// copy for the life of the process.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in for the device symbol): the device
+// address is looked up once per device with hipGetSymbolAddress, with that device
+// current, and kept in g_scratch_ptr.
+constexpr size_t kStaticScratchBytes = (size_t)PROFK_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+}  // namespace profk
+
+static __device__ __align__(256) unsigned char scratch[profk::kStaticScratchBytes];
+
+namespace profk {
+namespace {
+
+// Device address of this device's copy of `scratch` (looked up on the first call on the
+// device).  No allocation: the array exists since the library's code object was loaded.
+int static_scratch(char** out) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    t_err = "device index beyond the static scratch table";
+    return PROFK_EINVAL;
+  }
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    HIPCHK(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!ptr) {
+      t_err = "hipGetSymbolAddress(scratch) returned a null address";
+      return PROFK_EHIP;
+    }
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return PROFK_OK;
+}
+
+// profk_topk_approx on the static scratch.  The array keeps whatever the last call on
+// this GPU left in it, so the regions the kernels expect zero (hash set, tickets,
+// control blocks, histograms) are cleared first, by kernels (no memset node, so that
+// the call stays capturable in a HIP graph).  Calls that overlap in time on one GPU
+// share the array and race.
+int topk_approx_static(const float* x, u64 N, u64 k, double eps, u64 seed, float* out_vals, int64_t* out_idx,
+                       ApproxInfo* info, hipStream_t s, const profk_options* opt) {
+  profk_params p{};
+  int rc = solve_memo((int64_t)N, (int64_t)k, eps, opt, &p);
+  if (rc) return rc;
+  const bool sampled = !p.direct_exact && !(opt && opt->force_fallback);
+  const Layout L = make_layout(1, sampled ? (u64)p.S : 0, sampled ? (u64)p.M : 0, k, 0, 0, 0);
+  if (L.total > kStaticScratchBytes) {
+    t_err = "the call needs " + std::to_string(L.total) + " bytes of workspace; the static scratch holds " +
+            std::to_string(kStaticScratchBytes);
+    return PROFK_ESCRATCH;
+  }
+  char* base = nullptr;
+  rc = static_scratch(&base);
+  if (rc) return rc;
+  Workspace w;  // a view of the static array; nothing in it is allocated
+  w.stream = s;
+  w.dev = base;
+  w.bytes = kStaticScratchBytes;
+  w.hash_cap = L.hash_slots;
+  w.rows_cap = L.rows_cap;
+  HIPCHK(launch_clear_sample(at<u32>(&w, L.hash), L.hash_slots, at<u32>(&w, L.ticket), s), "launch clear_sample");
+  HIPCHK(launch_attempt_init(at<RowCtl>(&w, L.ctl), at<SelState>(&w, L.sel), at<AttemptRecord>(&w, L.rec),
+                             at<u32>(&w, L.ticket), 1, at<u32>(&w, L.rhist), s),
+         "launch attempt_init");
+  return approx_enqueue(&w, L, p, sampled, x, N, k, seed, out_vals, out_idx, info, s);
 }
 
 // Batched form with per-row kernels (rows of at most kBatchedMaxN values, k at most
@@ -835,6 +919,13 @@ int profk_topk_approx(const float* x, int64_t N, int64_t k, double eps, uint64_t
   int rc = validate(x, N, k, eps, out_vals, out_idx);
   if (rc) return rc;
   return topk_approx_row(x, (u64)N, (u64)k, eps, seed, out_vals, out_idx, info, (hipStream_t)stream, opt);
+}
+
+int profk_topk_approx_noalloc(const float* x, int64_t N, int64_t k, double eps, uint64_t seed, float* out_vals,
+                              int64_t* out_idx, profk_approx_info* info, void* stream, const profk_options* opt) {
+  int rc = validate(x, N, k, eps, out_vals, out_idx);
+  if (rc) return rc;
+  return topk_approx_static(x, (u64)N, (u64)k, eps, seed, out_vals, out_idx, info, (hipStream_t)stream, opt);
 }
 
 int profk_topk(const float* x, int64_t N, int64_t k, double eps, uint64_t seed, float* out_vals, int64_t* out_idx,
@@ -1041,6 +1132,8 @@ const char* profk_strerror(int code) {
       return t_err.empty() ? "HIP runtime error" : t_err.c_str();
     case PROFK_EINTERNAL:
       return t_err.empty() ? "device consistency check failed" : t_err.c_str();
+    case PROFK_ESCRATCH:
+      return t_err.empty() ? "the call needs more workspace than the static scratch holds" : t_err.c_str();
     default:
       return "unknown status";
   }

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_messages():
     lib = stf.load_library()
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert lib.profk_strerror(code)
 
 
