@@ -1,18 +1,19 @@
 #!/usr/bin/env python3
 """Throughput of Prof-K exact top-k on one MI355X.
 
-Workload: one flat fp32 tensor of N = 2^30 Pareto(alpha = 1.5, x_m = 1) values
-(seed 0, generated on the host by workloads.py and copied to HBM before
-timing), exact top-k for k in {2^5, 2^10, 2^15, 2^19}, eps = 1e-3.  One
-"step" is the whole k sweep: four exact top-k calls over the resident tensor,
-each including its sampling, threshold, filter, refinement and the host's wait
-for the count R that the device publishes.  Each k is timed over K calls back
-to back (HIP events on the stream around them; the host calls in turn, each
+Headline workload: flat fp32 tensors of N = 2^30 Pareto(alpha = 1.5, x_m = 1)
+values (three input tensors, seeds 0, 1, 2, generated on the host by
+workloads.py and copied to HBM before timing), exact top-k for k in {2^5, 2^10,
+2^15, 2^19}, eps = 1e-3.  One "step" is the whole k sweep: four exact top-k
+calls, each including its sampling, threshold, filter, refinement and the host's
+wait for the count R that the device publishes.  Each k is timed over K calls
+back to back (HIP events on the stream around them; the host calls in turn, each
 returning once its run-time check is known, so the next call queues behind the
-previous refinement); `value` = 4 N / (sum over k of the mean call time).
-The sample size follows the rule calibrated on MI355X (--s-rule 2: Algorithm 1
-of the page with the cost ratio that `--calibrate-s` measures); the same sweep
-under the library's default (k N)^(1/3) rule is printed beside it.
+previous refinement), the calls rotating over the input tensors; `value` =
+4 N / (sum over k of the mean call time).  The sample size follows the rule
+calibrated on MI355X (--s-rule 2: Algorithm 1 of the page with the cost ratio
+that `--calibrate-s` measures); the same sweep under the library's default
+(k N)^(1/3) rule is printed beside it.
 
 Also printed (same JSON line):
   per_k        ms, Gelem/s and algorithmic GB/s (4N bytes per call) per k
@@ -20,9 +21,23 @@ Also printed (same JSON line):
                launch / its launch time from HIP events recorded by the library
                around the filter on the same stream (in a second pass over the
                same calls, so that the events do not enter `value`); peak 8 TB/s
-  batched      1024 rows x 2^20, top-64 per row (same tensor, reshaped)
+  read_ceiling one dwordx4 non-temporal read of the 2^30 buffer and nothing else
+               (profk_read_ceiling), best of a blocks-per-CU sweep: the practical
+               ceiling of the filter on this device
+  configs      every other workload of the hot-path scope: uniform 2^22 k = 32;
+               normal and uniform 2^26 with k in {32, 1024, 32768}; the SAE pool
+               (4096 x 12288, k = 131072); the two radix-adversarial readings at
+               2^30 with k = 2^19 and eps = 1e-4, plus the forced-overflow run
+               (M = k: six failed attempts, then the exact full selection) and
+               the exact full selection alone.  Inputs below 2^27 values rotate
+               over copies totalling at least 768 MB, so that the 256 MB last-
+               level cache does not serve the reads.  Each entry gives ms per call,
+               Gelem/s, the fraction of the one-read roofline (4N bytes at 8 TB/s)
+               and the workspace the library held.
+  batched      1024 rows x 2^20, top-64 per row (input tensor 0, reshaped)
   large        N = 4.3e9 (beyond 32-bit indexing), k in {2^10, 2^18, 2^22}
-  cpu_baseline the CPU oracle (plain C heap top-k) on a bounded sample
+  cpu_baseline the CPU oracle (plain C heap top-k) on a bounded sample, with
+               the threads it used, and a single-thread figure
 """
 from __future__ import annotations
 
@@ -58,6 +73,11 @@ def parse():
                     help="sample-size rule: 0 the (kN)^(1/3) rule clamped to [2^15, 2^17] (the library default), "
                          "1 Algorithm 1 with the page's cost ratio, 2 Algorithm 1 with the ratio measured on "
                          "MI355X (default here)")
+    ap.add_argument("--inputs", type=int, default=3,
+                    help="input tensors of the headline workload (Pareto seeds 0, 1, ...); calls rotate over them")
+    ap.add_argument("--only", default="",
+                    help="comma list of parts to run (flat, ceiling, configs, c1, c2, c3, c5, batched, large, cpu); "
+                         "default all.  c1/c2/c3/c5 select single entries of configs, e.g. for a profile")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-batched", action="store_true", help="skip the batched variant")
     ap.add_argument("--no-large", action="store_true", help="skip the N = 4.3e9 (beyond 2^32) measurement")
@@ -145,27 +165,40 @@ def summarize_pmc(paths):
 
 
 def cpu_baseline(x: np.ndarray):
+    """The CPU oracle on the host cores of this machine: the multi-thread heap top-k over
+    the whole k sweep of the 2^30 input for about 10 s, and the single-thread one on a
+    2^26-value prefix for about 10 s (both scaled to Gelem/s)."""
     import oracle
     try:
-        cores = len(os.sched_getaffinity(0))
+        host_cores = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count() or 1
-    threads = max(1, min(16, cores))
+        host_cores = os.cpu_count() or 1
+    threads = max(1, min(16, host_cores))
     n = x.size
-    sample = x[:n]
-    oracle.topk(sample[: 1 << 20], 32, nthreads=threads)  # warm the library and pages
-    t0 = time.perf_counter()
-    reps = 0
-    while True:  # whole k sweeps until about 10 s of CPU work
-        for k in KS:
-            oracle.topk(sample, k, nthreads=threads)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or reps >= 32:
-            break
-    return {"value": round(reps * len(KS) * n / dt / 1e9, 4), "unit": "Gelem/s", "cores": threads, "kind": "oracle",
-            "sample": f"the same 2^{n.bit_length() - 1}-value tensor, k sweep {list(KS)} repeated {reps} times, "
-                      f"{dt:.2f} s total; plain C heap top-k, {threads} threads"}
+    oracle.topk(x[: 1 << 20], 32, nthreads=threads)  # warm the library and pages
+
+    def run(sample, nthreads, budget):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:  # whole k sweeps until about `budget` seconds of CPU work
+            for k in KS:
+                oracle.topk(sample, k, nthreads=nthreads)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget or reps >= 32:
+                return reps, dt
+
+    reps, dt = run(x, threads, 10.0)
+    m = 1 << 26
+    reps1, dt1 = run(x[:m], 1, 10.0)
+    return {"value": round(reps * len(KS) * n / dt / 1e9, 4), "unit": "Gelem/s", "cores": threads,
+            "host_cores": host_cores, "kind": "oracle",
+            "sample": f"the 2^{n.bit_length() - 1}-value Pareto tensor (seed 0), k sweep {list(KS)} repeated {reps} "
+                      f"times, {dt:.2f} s; plain C heap top-k on {threads} threads (the box has {host_cores} "
+                      f"host cores available)",
+            "single_thread": {"value": round(reps1 * len(KS) * m / dt1 / 1e9, 4), "unit": "Gelem/s", "cores": 1,
+                              "sample": f"its first 2^26 values, k sweep {list(KS)} repeated {reps1} times, "
+                                        f"{dt1:.2f} s on one thread"}}
 
 
 # ---------------------------------------------------------------------------
@@ -369,6 +402,134 @@ def bench_large(stf, torch, dev, stream, args, opts):
     return res
 
 
+def progress(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_calls(stf, torch, bufs, k, eps, opts, calls, warmup, stream, out):
+    """Mean ms per exact call over `calls` calls back to back, rotating over `bufs`
+    (seed = call number), after `warmup` untimed calls."""
+    for w in range(warmup):
+        stf.topk(bufs[w % len(bufs)], k, eps=eps, seed=w, options=opts, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record(stream)
+    for c in range(calls):
+        stf.topk(bufs[c % len(bufs)], k, eps=eps, seed=c, options=opts, out=out)
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / calls
+
+
+MALL_DEFEAT_BYTES = 768 << 20  # > 512 MB: twice the 256 MB last-level cache, and more
+
+
+def rotation(torch, xd):
+    """Device copies of xd totalling at least MALL_DEFEAT_BYTES when xd is smaller than
+    that (the same values at other addresses), else [xd]."""
+    n = xd.numel()
+    c = -(-MALL_DEFEAT_BYTES // (4 * n))
+    if c <= 1:
+        return [xd]
+    big = torch.empty((c, n), dtype=torch.float32, device=xd.device)
+    big.copy_(xd.unsqueeze(0).expand(c, n))
+    return [big[i] for i in range(c)]
+
+
+def out_pair(torch, dev, k):
+    return torch.empty(k, dtype=torch.float32, device=dev), torch.empty(k, dtype=torch.int64, device=dev)
+
+
+def entry(N, k, eps, ms, p, copies):
+    return {"N": N, "k": k, "eps": eps, "ms": round(ms, 4), "gelem_s": round(N / ms / 1e6, 2),
+            "frac_of_roofline": round(4.0 * N / ms / 1e6 / HBM_PEAK_GBPS, 4), "S": p["S"], "t": p["t"], "M": p["M"],
+            "input_copies": copies}
+
+
+def read_ceiling(stf, torch, xd, stream, reps=10):
+    """profk_read_ceiling on xd for 1, 2, 4, 8 blocks per CU: GB/s of one read."""
+    fold = torch.zeros(1, dtype=torch.int64, device=xd.device)
+    sweep = {}
+    for bpc in (1, 2, 4, 8):
+        for _ in range(3):
+            stf.read_ceiling(xd, bpc, out=fold)
+        torch.cuda.synchronize()
+        e0, e1 = _events(torch)
+        e0.record(stream)
+        for _ in range(reps):
+            stf.read_ceiling(xd, bpc, out=fold)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        sweep[str(bpc)] = {"us": round(ms * 1e3, 1), "GBps": round(4.0 * xd.numel() / ms / 1e6, 1)}
+    best = max(sweep, key=lambda b: sweep[b]["GBps"])
+    return {"kernel": "read_ceiling_kernel (dwordx4 non-temporal, 8 float4 per lane per tile)",
+            "N": xd.numel(), "best_blocks_per_cu": int(best), "GBps": sweep[best]["GBps"],
+            "frac_of_peak": round(sweep[best]["GBps"] / HBM_PEAK_GBPS, 4), "sweep": sweep}
+
+
+def bench_configs(stf, torch, dev, stream, args, opts, want, keep):
+    """The other workloads of the hot-path scope, each at its own sizes; `keep` collects
+    (name, tensor, k, eps, options) for the workspace pass."""
+    from workloads import generate, sae_pool
+    res = {}
+    calls = max(args.steps, 30)
+    warm = max(args.warmup, 5)
+    if "c1" in want:
+        N, k = 1 << 22, 32
+        bufs = rotation(torch, torch.from_numpy(generate("uniform", N, seed=0)).to(dev))
+        ms = time_calls(stf, torch, bufs, k, EPS, opts, calls, warm, stream, out_pair(torch, dev, k))
+        res["uniform_2p22"] = {"32": entry(N, k, EPS, ms, stf.solve(N, k, EPS, options=opts), len(bufs))}
+        progress("uniform 2^22", round(ms, 4), "ms")
+        keep.append(("uniform_2p22/32", bufs[0], k, EPS, opts))
+    if "c2" in want:
+        N = 1 << 26
+        for kind in ("normal", "uniform"):
+            bufs = rotation(torch, torch.from_numpy(generate(kind, N, seed=0)).to(dev))
+            r = {}
+            for k in (32, 1024, 32768):
+                ms = time_calls(stf, torch, bufs, k, EPS, opts, calls, warm, stream, out_pair(torch, dev, k))
+                r[str(k)] = entry(N, k, EPS, ms, stf.solve(N, k, EPS, options=opts), len(bufs))
+                progress(kind, "2^26 k", k, round(ms, 4), "ms")
+                keep.append((f"{kind}_2p26/{k}", bufs[0], k, EPS, opts))
+            res[f"{kind}_2p26"] = r
+        a = [res["normal_2p26"][str(k)]["ms"] for k in (32, 1024, 32768)]
+        b = [res["uniform_2p26"][str(k)]["ms"] for k in (32, 1024, 32768)]
+        res["normal_vs_uniform_2p26_ms_ratio"] = [round(x / y, 3) for x, y in zip(a, b)]
+    if "c3" in want:
+        N, k = 50331648, 131072
+        bufs = rotation(torch, torch.from_numpy(sae_pool(0).reshape(-1)).to(dev))
+        ms = time_calls(stf, torch, bufs, k, EPS, opts, calls, warm, stream, out_pair(torch, dev, k))
+        res["sae_pool_4096x12288"] = {"131072": entry(N, k, EPS, ms, stf.solve(N, k, EPS, options=opts), len(bufs))}
+        progress("sae pool", round(ms, 4), "ms")
+        keep.append(("sae_pool_4096x12288/131072", bufs[0], k, EPS, opts))
+    if "c5" in want:
+        N, k, eps = 1 << 30, 1 << 19, 1e-4
+        for kind in ("adv_levels", "adv_noise"):
+            xd = torch.from_numpy(generate(kind, N, seed=0)).to(dev)
+            out = out_pair(torch, dev, k)
+            ms = time_calls(stf, torch, [xd], k, eps, opts, args.steps, args.warmup, stream, out)
+            e = entry(N, k, eps, ms, stf.solve(N, k, eps, options=opts), 1)
+            keep.append((f"{kind}_2p30/{k}", xd, k, eps, opts))
+            if kind == "adv_levels":
+                # forced overflow: M = k fails every attempt (R > M), then the exact full selection
+                fo = stf.make_options(s_rule=opts.s_rule, force_M=k)
+                _, _, st = stf.topk(xd, k, eps=eps, seed=0, options=fo, stats=True, out=out)
+                fms = time_calls(stf, torch, [xd], k, eps, fo, 3, 1, stream, out)
+                ex = stf.make_options(s_rule=opts.s_rule, force_fallback=1)
+                xms = time_calls(stf, torch, [xd], k, eps, ex, 3, 1, stream, out)
+                e["forced_overflow_M_eq_k"] = {"ms": round(fms, 4), "attempts": st["attempts"],
+                                               "fallback": st["fallback"], "R_first_attempt": st["R"][0]}
+                e["exact_full_selection_ms"] = round(xms, 4)
+            res[f"{kind}_2p30"] = {str(k): e}
+            progress(kind, "2^30", e)
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -389,132 +550,155 @@ def main():
     import sampling_threshold_filtering_amd as stf
     from workloads import generate
 
-    N = 1 << args.log2n
-    t_gen = time.perf_counter()
-    x = generate("pareto", N, seed=0)
-    gen_s = time.perf_counter() - t_gen
+    parts = {"flat", "ceiling", "configs", "c1", "c2", "c3", "c5", "batched", "large", "cpu"}
+    want = set(p.strip() for p in args.only.split(",") if p.strip()) or set(parts)
+    if not want <= parts:
+        sys.exit(f"--only: unknown parts {sorted(want - parts)}")
+    if "configs" in want:
+        want |= {"c1", "c2", "c3", "c5"}
+    if args.no_cpu:
+        want.discard("cpu")
+    if args.no_batched:
+        want.discard("batched")
+    if args.no_large:
+        want.discard("large")
+    need_pareto = bool(want & {"flat", "ceiling", "batched", "cpu"})
+
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    xd = torch.from_numpy(x).to(dev)
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
+    N = 1 << args.log2n
     opts = stf.make_options(s_rule=args.s_rule)
     opts_t = stf.make_options(timing=1, s_rule=args.s_rule)
+    keep = []
 
-    per_k = {}
-    filt_bytes = 0.0
-    filt_ms = 0.0
-    total_ms = 0.0
-    retries = 0
-    for k in KS:
-        out = (torch.empty(k, dtype=torch.float32, device=dev), torch.empty(k, dtype=torch.int64, device=dev))
-        for _ in range(args.warmup):
-            stf.topk(xd, k, eps=EPS, seed=0, options=opts, out=out)
+    x0 = None
+    xds = []
+    gen_s = 0.0
+    if need_pareto:
+        t_gen = time.perf_counter()
+        for i in range(max(1, args.inputs) if "flat" in want else 1):
+            x = generate("pareto", N, seed=i)
+            if i == 0:
+                x0 = x
+            xds.append(torch.from_numpy(x).to(dev))
+            del x
+        gen_s = time.perf_counter() - t_gen
         torch.cuda.synchronize()
-        # K calls back to back, bracketed by events on the stream (each call waits
-        # only for its run-time check; the next one is enqueued behind it).  No stats
-        # are requested here: building them on the host delays the next call's launch.
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for s in range(args.steps):
-            stf.topk(xd, k, eps=EPS, seed=s, options=opts, out=out)
-        e1.record(stream)
-        e1.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
-        # the filter's own launch time, from HIP events the library records around it,
-        # and the attempts of the same seeds (a separate pass: neither is part of the
-        # timed calls above)
-        for s in range(args.steps):
-            _, _, st = stf.topk(xd, k, eps=EPS, seed=s, options=opts_t, stats=True, out=out)
-            retries += st["attempts"] - 1
-            filt_ms += st["filter_ms"]
-            filt_bytes += 4.0 * N + 8.0 * st["R"][-1]
-        total_ms += ms
-        per_k[str(k)] = {"ms": round(ms, 4), "gelem_s": round(N / ms / 1e6, 2),
-                         "alg_GBps": round(4.0 * N / ms / 1e6, 1),
-                         "frac_of_hbm_peak": round(4.0 * N / ms / 1e6 / HBM_PEAK_GBPS, 4)}
-    torch.cuda.synchronize()
 
-    # the same sweep with the library's default sample-size rule, for comparison
-    other_rule = None
-    if args.s_rule != 0:
-        other_rule = {}
-        o0 = stf.make_options(s_rule=0)
+    per_k, other_rule, roofline, value, total_ms, retries = None, None, None, None, None, 0
+    if "flat" in want:
+        per_k = {}
+        filt_bytes = filt_ms = total_ms = 0.0
         for k in KS:
-            out = (torch.empty(k, dtype=torch.float32, device=dev), torch.empty(k, dtype=torch.int64, device=dev))
-            for _ in range(args.warmup):
-                stf.topk(xd, k, eps=EPS, seed=0, options=o0, out=out)
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for s in range(args.steps):
-                stf.topk(xd, k, eps=EPS, seed=s, options=o0, out=out)
-            e1.record(stream)
-            e1.synchronize()
-            other_rule[str(k)] = {"ms": round(e0.elapsed_time(e1) / args.steps, 4),
-                                  "S": stf.solve(N, k, EPS, options=o0)["S"]}
+            out = out_pair(torch, dev, k)
+            # K calls back to back, bracketed by events on the stream (each call waits
+            # only for its run-time check; the next one is enqueued behind it).  No stats
+            # are requested here: building them on the host delays the next call's launch.
+            ms = time_calls(stf, torch, xds, k, EPS, opts, args.steps, args.warmup, stream, out)
+            # the filter's own launch time, from HIP events the library records around it,
+            # and the attempts of the same calls (a separate pass: neither is part of the
+            # timed calls above)
+            for c in range(args.steps):
+                _, _, st = stf.topk(xds[c % len(xds)], k, eps=EPS, seed=c, options=opts_t, stats=True, out=out)
+                retries += st["attempts"] - 1
+                filt_ms += st["filter_ms"]
+                filt_bytes += 4.0 * N + 8.0 * st["R"][-1]
+            total_ms += ms
+            progress("pareto 2^30 k", k, round(ms, 4), "ms")
+            per_k[str(k)] = {"ms": round(ms, 4), "gelem_s": round(N / ms / 1e6, 2),
+                             "alg_GBps": round(4.0 * N / ms / 1e6, 1),
+                             "frac_of_hbm_peak": round(4.0 * N / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+            keep.append((f"pareto_2p30/{k}", xds[0], k, EPS, opts))
+        torch.cuda.synchronize()
+        value = len(KS) * N / (total_ms / 1e3) / 1e9
+        # the same sweep with the library's default sample-size rule, for comparison
+        if args.s_rule != 0:
+            other_rule = {}
+            o0 = stf.make_options(s_rule=0)
+            for k in KS:
+                ms = time_calls(stf, torch, xds, k, EPS, o0, args.steps, args.warmup, stream, out_pair(torch, dev, k))
+                other_rule[str(k)] = {"ms": round(ms, 4), "S": stf.solve(N, k, EPS, options=o0)["S"]}
+        n_filter = args.steps * len(KS)
+        achieved = filt_bytes / n_filter / (filt_ms / n_filter / 1e3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_record(N),
+                    "kernel": "filter_kernel", "filter_ms_avg": round(filt_ms / n_filter, 4),
+                    "bytes_per_launch_alg": round(filt_bytes / n_filter)}
 
-    n_filter = args.steps * len(KS)
-    achieved = filt_bytes / n_filter / (filt_ms / n_filter / 1e3) / 1e9
-    traffic = traffic_record(N)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "filter_kernel", "filter_ms_avg": round(filt_ms / n_filter, 4),
-                "bytes_per_launch_alg": round(filt_bytes / n_filter)}
+    ceiling = read_ceiling(stf, torch, xds[0], stream) if "ceiling" in want else None
+    if ceiling:
+        progress("read ceiling", ceiling["GBps"], "GB/s")
+    if ceiling and roofline:
+        roofline["frac_of_read_ceiling"] = round(roofline["achieved"] / ceiling["GBps"], 4)
 
     batched = None
-    if not args.no_batched and N >= (1 << 20) * 16:
+    if "batched" in want and N >= (1 << 20) * 16:
         B = min(1024, N >> 20)
-        xb = xd[: B << 20].view(B, 1 << 20)
+        xb = xds[0][: B << 20].view(B, 1 << 20)
         bopts = stf.make_options(s_rule=args.s_rule)
         for _ in range(max(1, args.warmup)):
             stf.topk_batched(xb, 64, eps=EPS, seed=0, options=bopts)
         torch.cuda.synchronize()
         nb = max(1, args.steps // 2)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        e0, e1 = _events(torch)
         e0.record(stream)
-        for s in range(nb):
-            stf.topk_batched(xb, 64, eps=EPS, seed=s, options=bopts)
+        for c in range(nb):
+            stf.topk_batched(xb, 64, eps=EPS, seed=c, options=bopts)
         e1.record(stream)
         e1.synchronize()
-        bt = [e0.elapsed_time(e1) / nb]
-        bms = float(np.mean(bt))
+        bms = e0.elapsed_time(e1) / nb
         batched = {"rows": B, "row_len": 1 << 20, "k": 64, "ms": round(bms, 4),
                    "gelem_s": round((B << 20) / bms / 1e6, 2),
+                   "frac_of_roofline": round(4.0 * (B << 20) / bms / 1e6 / HBM_PEAK_GBPS, 4),
                    "S_per_row": stf.solve(1 << 20, 64, EPS / B, options=bopts)["S"]}
 
-    large = None if args.no_large else bench_large(stf, torch, dev, stream, args, opts)
+    configs = bench_configs(stf, torch, dev, stream, args, opts, want, keep) if want & {"c1", "c2", "c3", "c5"} else None
 
-    cpu = None if args.no_cpu else cpu_baseline(x)
+    large = bench_large(stf, torch, dev, stream, args, opts) if "large" in want else None
+    progress("large done")
 
-    value = len(KS) * N / (total_ms / 1e3) / 1e9
+    # device workspace each configuration holds (sized for it alone: the cache is
+    # released first, so this is its need plus the library's 25% growth margin)
+    workspace = {}
+    for name, xd, k, eps, o in keep:
+        stf.release()
+        _, _, st = stf.topk(xd, k, eps=eps, seed=0, options=o, stats=True)
+        workspace[name] = st["workspace_bytes"]
+    stf.release()
+    del keep, xds
+    torch.cuda.synchronize()
+
+    progress("workspace pass done")
+    cpu = cpu_baseline(x0) if "cpu" in want and x0 is not None else None
+
     line = {
         "metric": "Gelem/s + % of HBM peak, exact top-k N=2^30 fp32, k=2^5..2^19, 1 GPU",
-        "value": round(value, 2),
+        "value": round(value, 2) if value else None,
         "unit": "Gelem/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(total_ms, 4),
+        "ms_per_step": round(total_ms, 4) if total_ms else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"Pareto(1.5) fp32 flat tensor N=2^{args.log2n}, seed 0, exact top-k k sweep "
-                               f"{list(KS)}, eps=1e-3", "N": N, "ks": list(KS), "eps": EPS,
-                   "s_rule": S_RULE_NAMES[args.s_rule],
+        "config": {"workload": f"Pareto(1.5) fp32 flat tensor N=2^{args.log2n} ({args.inputs} input tensors, seeds "
+                               f"0..{args.inputs - 1}), exact top-k k sweep {list(KS)}, eps=1e-3",
+                   "N": N, "ks": list(KS), "eps": EPS, "inputs": args.inputs, "s_rule": S_RULE_NAMES[args.s_rule],
                    "S": {str(k): stf.solve(N, k, EPS, options=opts)["S"] for k in KS}},
-        "hbm_frac_alg": round(4.0 * N * len(KS) / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "hbm_frac_alg": round(4.0 * N * len(KS) / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4) if total_ms else None,
         "per_k": per_k,
         "per_k_cube_root_rule": other_rule,
         "retries": retries,
         "roofline": roofline,
+        "read_ceiling": ceiling,
+        "configs": configs,
         "batched": batched,
         "large": large,
+        "workspace_bytes": workspace,
         "cpu_baseline": cpu,
         "host_gen_s": round(gen_s, 2),
     }
