@@ -279,7 +279,7 @@ int profk_stage_filter(const float* x, int64_t N, float tau_val, int64_t tau_idx
  *   all N values' bit patterns into *out_fold (device, one uint64).  Its
  *   time on the same buffer is the practical ceiling of the filter's one-read
  *   roofline on the device at hand.  x must be 16-byte aligned;
- *   blocks_per_cu in 0..16 (0: 4) sets the persistent grid (256 threads per
+ *   blocks_per_cu in 0..16 (0: 2) sets the persistent grid (256 threads per
  *   block).  Enqueued on `stream`; does not wait.
  */
 int profk_read_ceiling(const float* x, int64_t N, int32_t blocks_per_cu, uint64_t* out_fold, void* stream);

@@ -334,7 +334,7 @@ int run_exact(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, float
   HIPCHK(launch_attempt_init(ctl, sel, rec, at<u32>(w, L.ticket), 1, at<u32>(w, L.rhist), s), "launch attempt_init");
   HIPCHK(launch_arm_select(sel, k, N, ctl, s), "launch arm_select");
   HIPCHK(launch_select_x(x, N, sel, at<u64>(w, L.col), &ctl->kth, &ctl->status, s), "launch select_x");
-  HIPCHK(launch_compact_x(x, N, ctl, at<u64>(w, L.topk0), k, s), "launch compact_x");
+  HIPCHK(launch_compact_x(x, N, ctl, at<u64>(w, L.topk0), k, at<u32>(w, L.ticket), s), "launch compact_x");
   HIPCHK(launch_sort_and_write(at<u64>(w, L.topk0), at<u64>(w, L.topk1), at<u32>(w, L.hist), (u32)k, x, N,
                                out_vals, out_idx, ctl, rec, s),
          "launch sort");
@@ -465,15 +465,22 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   ra.hrec = w->hrec_dev;
   ra.seq = seq;
   ra.rec = rec;
-  ra.msd_cap = kMsdCapExact;
-  ra.early_cap = kMsdCapExact;  // the same cap wait_record applies to the early word
+  // One-launch refinement (small k): no value bins, so the filter's early word settles
+  // the attempt (a bin cap of R <= kMsdCapExact is always met there).  Binned
+  // refinement: a needed value bin beyond one workgroup's LDS sort (kBinCap keys: a
+  // group of equal values, or a narrow value range) goes to the multi-block radix
+  // select, which the host enqueues; so the host always takes the scan's record (the
+  // next call is still enqueued while the bin sort runs).  The in-kernel partition of
+  // such bins (one workgroup per bin: milliseconds for a 10^5-key tie group) is left to
+  // approximate mode, which has no host.
+  const bool one = refine_one_launch(ra);
+  ra.msd_cap = one ? kMsdCapExact : kBinCap;
+  ra.early_cap = one ? kMsdCapExact : 0;  // the same cap wait_record applies to the early word
   HIPCHK(launch_refine(ra, s), "launch refine");
-  // The filter publishes R and the check, the scan the full record; the host needs the
-  // scan's only when a value bin may exceed the in-kernel partition's cap.  The
-  // refinement launches may still run when this returns (outputs are complete in
-  // stream order).
+  // The filter publishes R and the check, the scan the full record.  The refinement
+  // launches may still run when this returns (outputs are complete in stream order).
   bool early = false;
-  rc = wait_record(w, s, seq, kMsdCapExact, &early);
+  rc = wait_record(w, s, seq, ra.early_cap, &early);
   if (rc) return rc;
   if (N >= kTimedMinN) update_die_weights(w, split);
   w->host[0].R = w->hrec->R;

@@ -790,10 +790,15 @@ hipError_t launch_approx_info_exact(ApproxInfo* info, u64 N, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_refine(const RefineArgs& a, hipStream_t s) {
+bool refine_one_launch(const RefineArgs& a) {
   // small k: one launch, when the union of the workgroups' lists fits in LDS
   const u64 gsm = (a.M + kSmallShare - 1) / kSmallShare;
-  if (a.k <= kSmallK && gsm * a.k <= kSmallLists) {
+  return a.k <= kSmallK && gsm * a.k <= kSmallLists;
+}
+
+hipError_t launch_refine(const RefineArgs& a, hipStream_t s) {
+  const u64 gsm = (a.M + kSmallShare - 1) / kSmallShare;
+  if (refine_one_launch(a)) {
     const u32 G = (u32)(gsm ? gsm : 1);
     const u64 words = a.table ? a.table_slots / 4 : 0;  // slots: a power of two >= 16
     const u64 z = (words + kClearPerBlock - 1) / kClearPerBlock;

@@ -7,7 +7,8 @@
 //   * stage 4 (§3): the k-th largest of the R buffered candidates, after which the
 //     compaction keeps exactly the k keys at or above it;
 //   * the exact full selection after the last failed attempt (§3 stage 4), over all
-//     N entries with keys formed on the fly.
+//     N entries with keys formed on the fly (select_pass_x_kernel: dwordx4 loads), after
+//     which the compaction is the filter itself with tau = the k-th key (k_filter.hip).
 // The pages use a library top-k for these steps (App. C); this is a radix select
 // written for gfx950.
 //
@@ -32,13 +33,6 @@ struct KeyArraySrc {
     return n < n_cap ? n : n_cap;
   }
   __device__ __forceinline__ u64 key(u64 i) const { return keys[i]; }
-};
-
-struct FloatSrc {
-  const float* x;
-  u64 N;
-  __device__ __forceinline__ u64 size() const { return N; }
-  __device__ __forceinline__ u64 key(u64 i) const { return make_key(__float_as_uint(x[i]), (u32)i); }
 };
 
 namespace {
@@ -67,35 +61,45 @@ __device__ void bitonic_desc(u64* s, u32 P) {
 
 }  // namespace
 
-template <class Src>
-__global__ __launch_bounds__(kSelThreads) void select_pass_kernel(Src src, SelState* st, u64* col, u64* result,
-                                                                  u32* status) {
-  __shared__ u32 s_hist[256];
-  __shared__ u64 s_col[kCollectCap];
-  __shared__ u32 s_last;
-  if (st->done) return;
-  const u64 n = src.size();
-  const u64 prefix = st->prefix, mask = st->mask, count = st->count;
-  const bool collect = count <= kCollectCap;
-  const u32 digit = st->digit;
-  const u32 shift = 56u - 8u * digit;
-  if (!collect) {
-    for (u32 b = threadIdx.x; b < 256; b += blockDim.x) s_hist[b] = 0;
-    __syncthreads();
+// One digit of one pass: the histogram of the digit of the matching keys (or, in
+// collect mode, the matching keys themselves) for a wavefront's keys.  Every lane of
+// the wavefront calls it (wave-collective).
+__device__ __forceinline__ void select_take(u64 key, bool match, bool collect, u32 shift, u32* s_hist, SelState* st,
+                                            u64* col) {
+  if (collect) {
+    const u32 slot = wave_reserve32(&st->ncol, match);
+    if (match && slot < kCollectCap) col[slot] = key;
+    return;
   }
-  const u64 stride = (u64)gridDim.x * blockDim.x;
-  for (u64 base = (u64)blockIdx.x * blockDim.x; base < n; base += stride) {
-    const u64 i = base + threadIdx.x;
-    const bool in = i < n;
-    const u64 key = in ? src.key(i) : 0ull;
-    const bool match = in && ((key & mask) == prefix);
-    if (collect) {
-      const u32 slot = wave_reserve32(&st->ncol, match);
-      if (match && slot < kCollectCap) col[slot] = key;
-    } else {
-      wave_hist_add(s_hist, (u32)(key >> shift) & 255u, match);
+  const u32 d = (u32)(key >> shift) & 255u;
+  // The lanes on the wavefront's most common digit (one of the first and the last
+  // matching lane's digits: inputs whose values share their leading bits put most lanes
+  // on one digit) add with one LDS atomic; the others add one each (the LDS serialises
+  // lanes on one address, so a shared digit must not be left to per-lane atomics).
+  const u64 m = __ballot(match);
+  if (!m) return;
+  const int la = __ffsll((long long)m) - 1, lb = 63 - __clzll((long long)m);
+  const u32 da = (u32)__builtin_amdgcn_readlane((int)d, la);
+  u64 g = __ballot(match && d == da);
+  u32 dg = da;
+  int lg = la;
+  if (2 * __popcll(g) < __popcll(m)) {
+    const u32 db = (u32)__builtin_amdgcn_readlane((int)d, lb);
+    const u64 gb = __ballot(match && d == db);
+    if (__popcll(gb) > __popcll(g)) {
+      g = gb;
+      dg = db;
+      lg = lb;
     }
   }
+  if ((int)lane_id() == lg) atomicAdd(&s_hist[dg], (u32)__popcll(g));
+  if (match && d != dg) atomicAdd(&s_hist[d], 1u);
+}
+
+// End of a pass: the block's histogram into the global one, then the last block fixes
+// the digit (or, in collect mode, sorts the collected keys and reads off the result).
+__device__ void select_finish(SelState* st, u64* col, u64* result, u32* status, bool collect, u64 prefix, u64 mask,
+                              u64 count, u32 digit, u32 shift, u32* s_hist, u64* s_col, u32* s_last) {
   if (!collect) {
     __syncthreads();
     for (u32 b = threadIdx.x; b < 256; b += blockDim.x)
@@ -103,9 +107,9 @@ __global__ __launch_bounds__(kSelThreads) void select_pass_kernel(Src src, SelSt
   }
   __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&st->ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
+  if (threadIdx.x == 0) *s_last = (atomicAdd(&st->ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
   __syncthreads();
-  if (!s_last) return;
+  if (!*s_last) return;
   __threadfence();
 
   if (!collect) {
@@ -172,6 +176,115 @@ __global__ __launch_bounds__(kSelThreads) void select_pass_kernel(Src src, SelSt
     st->ticket = 0;
     *result = ans;
   }
+}
+
+template <class Src>
+__global__ __launch_bounds__(kSelThreads) void select_pass_kernel(Src src, SelState* st, u64* col, u64* result,
+                                                                  u32* status) {
+  __shared__ u32 s_hist[256];
+  __shared__ u64 s_col[kCollectCap];
+  __shared__ u32 s_last;
+  if (st->done) return;
+  const u64 n = src.size();
+  const u64 prefix = st->prefix, mask = st->mask, count = st->count;
+  const bool collect = count <= kCollectCap;
+  const u32 digit = st->digit;
+  const u32 shift = 56u - 8u * digit;
+  if (!collect) {
+    for (u32 b = threadIdx.x; b < 256; b += blockDim.x) s_hist[b] = 0;
+    __syncthreads();
+  }
+  // kSelILP keys per thread in flight, then taken
+  constexpr u32 kSelILP = 8;
+  const u64 stride = (u64)gridDim.x * blockDim.x * kSelILP;
+  for (u64 base = (u64)blockIdx.x * blockDim.x * kSelILP; base < n; base += stride) {
+    u64 kk[kSelILP];
+#pragma unroll
+    for (u32 q = 0; q < kSelILP; ++q) {
+      const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
+      kk[q] = i < n ? src.key(i) : 0ull;
+    }
+#pragma unroll
+    for (u32 q = 0; q < kSelILP; ++q) {
+      const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
+      select_take(kk[q], i < n && ((kk[q] & mask) == prefix), collect, shift, s_hist, st, col);
+    }
+  }
+  select_finish(st, col, result, status, collect, prefix, mask, count, digit, shift, s_hist, s_col, &s_last);
+}
+
+// The same pass over the input values themselves (the exact full selection), with the
+// keys formed on the fly: dwordx4 loads, wave-tiles of 64 lanes x kSelXU float4 in a
+// grid-stride order, the next tile's loads issued before the current tile's keys are
+// taken (two register sets); the scalar head (before the first 16-byte boundary) and
+// tail by the first wavefront.
+constexpr u32 kSelXU = 4;
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kSelThreads) void select_pass_x_kernel(const float* x, u64 N, SelState* st, u64* col,
+                                                                    u64* result, u32* status) {
+  __shared__ u32 s_hist[256];
+  __shared__ u64 s_col[kCollectCap];
+  __shared__ u32 s_last;
+  if (st->done) return;
+  const u64 prefix = st->prefix, mask = st->mask, count = st->count;
+  const bool collect = count <= kCollectCap;
+  const u32 digit = st->digit;
+  const u32 shift = 56u - 8u * digit;
+  if (!collect) {
+    for (u32 b = threadIdx.x; b < 256; b += blockDim.x) s_hist[b] = 0;
+    __syncthreads();
+  }
+  const u32 lane = lane_id(), wid = threadIdx.x / kWave;
+  u64 head = (4ull - (((u64)(uintptr_t)x >> 2) & 3ull)) & 3ull;
+  if (head > N) head = N;
+  const u64 nvec = (N - head) >> 2, tail = N - head - 4 * nvec;
+  const f4* xv = reinterpret_cast<const f4*>(x + head);
+  const u64 per_tile = (u64)kSelXU * kWave;
+  const u64 ntiles = (nvec + per_tile - 1) / per_tile;
+  const u64 nw = (u64)gridDim.x * (kSelThreads / kWave);
+  auto load = [&](u64 tl, f4 (&v)[kSelXU]) {
+#pragma unroll
+    for (u32 u = 0; u < kSelXU; ++u) {
+      const u64 vi = tl * per_tile + (u64)u * kWave + lane;
+      v[u] = vi < nvec ? __builtin_nontemporal_load(xv + vi) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto take = [&](u64 tl, const f4 (&v)[kSelXU]) {
+#pragma unroll
+    for (u32 u = 0; u < kSelXU; ++u) {
+      const u64 vi = tl * per_tile + (u64)u * kWave + lane;
+      const u32 i0 = (u32)(head + 4 * vi);
+      const float c[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (u32 q = 0; q < 4; ++q) {
+        const u64 key = make_key(__float_as_uint(c[q]), i0 + q);
+        select_take(key, vi < nvec && ((key & mask) == prefix), collect, shift, s_hist, st, col);
+      }
+    }
+  };
+  f4 va[kSelXU], vb[kSelXU];
+  u64 tile = (u64)blockIdx.x * (kSelThreads / kWave) + wid;
+  if (tile < ntiles) load(tile, va);
+  while (tile < ntiles) {
+    const u64 t1 = tile + nw;
+    if (t1 < ntiles) load(t1, vb);
+    take(tile, va);
+    if (t1 >= ntiles) break;
+    const u64 t2 = t1 + nw;
+    if (t2 < ntiles) load(t2, va);
+    take(t1, vb);
+    tile = t2;
+  }
+  if (blockIdx.x == 0 && wid == 0 && (head | tail)) {
+    u64 i = N;
+    if (lane < head) i = lane;
+    else if (lane < head + tail) i = head + 4 * nvec + (lane - head);
+    const bool in = i < N;
+    const u64 key = in ? make_key(__float_as_uint(x[i]), (u32)i) : 0ull;
+    select_take(key, in && ((key & mask) == prefix), collect, shift, s_hist, st, col);
+  }
+  select_finish(st, col, result, status, collect, prefix, mask, count, digit, shift, s_hist, s_col, &s_last);
 }
 
 // Writes every key >= *kth_ptr (exactly k of them when the selection is
@@ -264,9 +377,13 @@ hipError_t launch_select_keys(const u64* keys, const u64* n_ptr, u64 n_cap, SelS
 }
 
 hipError_t launch_select_x(const float* x, u64 N, SelState* st, u64* col, u64* result, u32* status, hipStream_t s) {
-  FloatSrc src{x, N};
-  const u32 g = select_grid(N, 4096);
-  for (int p = 0; p < 8; ++p) select_pass_kernel<FloatSrc><<<g, kSelThreads, 0, s>>>(src, st, col, result, status);
+  // a persistent grid of four blocks per CU (fewer for short inputs): each block adds
+  // its nonzero bins to the global histogram and takes the ticket once per pass
+  u64 g = (N + 4095) / 4096;
+  const u64 cap = 4ull * device_cu_count();
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  for (int p = 0; p < 8; ++p) select_pass_x_kernel<<<(u32)g, kSelThreads, 0, s>>>(x, N, st, col, result, status);
   return hipGetLastError();
 }
 
@@ -278,10 +395,73 @@ hipError_t launch_compact_keys(const u64* keys, const u64* n_ptr, u64 n_cap, Row
   return hipGetLastError();
 }
 
-hipError_t launch_compact_x(const float* x, u64 N, RowCtl* ctl, u64* out, u64 k, hipStream_t s) {
-  FloatSrc src{x, N};
-  const u32 g = select_grid(N, 4 * kCompactMaxBlocks);
-  compact_kernel<FloatSrc><<<g, 256, 0, s>>>(src, ctl, out, k);
+// The exact full selection's compaction is the filter itself (one streaming pass with
+// tau = the k-th key and capacity k, k_filter.hip); these two kernels frame it.
+__global__ void arm_compact_kernel(RowCtl* ctl) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    RowCtl* c = ctl;
+    c->tau = c->kth;  // keep exactly the keys at or above the k-th
+    c->R = 0;
+    c->cmax = 0;
+    c->nsel = 0;
+    c->key_or = 0;
+    c->key_and = ~0ull;
+  }
+}
+
+// After the filter: the count must be exactly k (the keys are distinct); the OR / AND
+// of the k keys tells the sort which digits vary.
+__global__ __launch_bounds__(256) void finish_compact_kernel(RowCtl* ctl, const u64* __restrict__ keys, u64 k) {
+  const RowCtl* c = ctl;
+  if (c->status != 0) return;
+  if (c->R != k) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) ctl->status = 3u;
+    return;
+  }
+  u64 v_or = 0, v_and = ~0ull;
+  for (u64 i = (u64)blockIdx.x * blockDim.x + threadIdx.x; i < k; i += (u64)gridDim.x * blockDim.x) {
+    v_or |= keys[i];
+    v_and &= keys[i];
+  }
+  for (int d = 32; d >= 1; d >>= 1) {
+    v_or |= __shfl_xor(v_or, d);
+    v_and &= __shfl_xor(v_and, d);
+  }
+  if (lane_id() == 0) {
+    atomicOr(&ctl->key_or, v_or);
+    atomicAnd(&ctl->key_and, v_and);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) ctl->nsel = k;
+}
+
+hipError_t launch_compact_x(const float* x, u64 N, RowCtl* ctl, u64* out, u64 k, u32* tickets, hipStream_t s) {
+  arm_compact_kernel<<<1, 64, 0, s>>>(ctl);
+  FilterArgs fa{};
+  fa.x = x;
+  fa.ld = N;
+  fa.N = N;
+  fa.rows = nullptr;
+  fa.nrows = 1;
+  fa.ctls = ctl;
+  fa.cand = out;
+  fa.M = k;
+  fa.k = k;
+  fa.ticket = tickets + kTicketFilter;
+  fa.groups = tickets + kTickets;
+  fa.xtime = nullptr;
+  fa.hrec = nullptr;
+  fa.rec = nullptr;
+  fa.sels = nullptr;
+  // launch shape by the density of the k hits, as for a sampled attempt
+  fa.sparse = (double)k * 8192.0 <= (double)N ? kShapeSparse
+              : (double)k * 256.0 >= (double)N ? kShapeVeryDenseHits
+              : (double)k * 2048.0 >= (double)N ? kShapeDenseHits : 0u;
+  hipError_t e = launch_filter(fa, 0, s);
+  if (e != hipSuccess) return e;
+  u64 g = (k + 1023) / 1024;
+  if (g > 256) g = 256;
+  if (g < 1) g = 1;
+  finish_compact_kernel<<<(u32)g, 256, 0, s>>>(ctl, out, k);
   return hipGetLastError();
 }
 

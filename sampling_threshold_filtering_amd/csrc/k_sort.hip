@@ -107,6 +107,7 @@ __global__ __launch_bounds__(kSortThreads) void lsd_hist_kernel(u64* buf0, u64* 
 // digit-major layout makes this one exclusive scan of the 256*G words in array
 // order: each thread scans a contiguous run, the run totals are scanned in LDS.
 constexpr int kScanThreads = 1024;
+constexpr u32 kScanRegWords = 64;  // runs up to this many words stay in registers
 __global__ __launch_bounds__(kScanThreads) void lsd_scan_kernel(u32* hist, u32 G, u32 d, const RowCtl* ctl) {
   __shared__ u32 s_tot[kScanThreads];
   if (ctl->status != 0 || !digit_varies(ctl, d)) return;
@@ -116,6 +117,45 @@ __global__ __launch_bounds__(kScanThreads) void lsd_scan_kernel(u32* hist, u32 G
   const u32 per = ((total + kScanThreads - 1) / kScanThreads + 15u) & ~15u;
   const u32 lo = threadIdx.x * per < total ? threadIdx.x * per : total;
   const u32 hi = lo + per < total ? lo + per : total;
+  if (per <= kScanRegWords) {
+    // the thread's run (at most kScanRegWords words) loaded at once and kept in
+    // registers for the rewrite: one round trip each way
+    uint4 q[kScanRegWords / 4];
+#pragma unroll
+    for (u32 j = 0; j < kScanRegWords / 4; ++j)
+      q[j] = lo + 4 * j < hi ? reinterpret_cast<const uint4*>(hist + lo)[j] : make_uint4(0, 0, 0, 0);
+    u32 run = 0;
+#pragma unroll
+    for (u32 j = 0; j < kScanRegWords / 4; ++j) run += q[j].x + q[j].y + q[j].z + q[j].w;
+    // exclusive scan of the run totals: within each wavefront by DPP, then over the
+    // sixteen wavefront totals
+    const u32 lane = lane_id(), w = threadIdx.x / kWave;
+    const u32 incl = wave_incl_scan_add(run, lane);
+    if (lane == kWave - 1) s_tot[w] = incl;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      u32 a = 0;
+      for (u32 i = 0; i < kScanThreads / kWave; ++i) {
+        const u32 t = s_tot[i];
+        s_tot[i] = a;
+        a += t;
+      }
+    }
+    __syncthreads();
+    u32 acc = s_tot[w] + incl - run;
+#pragma unroll
+    for (u32 j = 0; j < kScanRegWords / 4; ++j) {
+      const uint4 c = q[j];
+      uint4 o;
+      o.x = acc;
+      o.y = acc + c.x;
+      o.z = acc + c.x + c.y;
+      o.w = acc + c.x + c.y + c.z;
+      acc += c.x + c.y + c.z + c.w;
+      if (lo + 4 * j < hi) reinterpret_cast<uint4*>(hist + lo)[j] = o;
+    }
+    return;
+  }
   u32 run = 0;
   for (u32 i = lo; i < hi; i += 16) {
     const uint4* p = reinterpret_cast<const uint4*>(hist + i);

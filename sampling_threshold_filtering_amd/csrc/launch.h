@@ -106,7 +106,9 @@ hipError_t launch_select_x(const float* x, u64 N, SelState* st, u64* col, u64* r
                            hipStream_t s);
 hipError_t launch_compact_keys(const u64* keys, const u64* n_ptr, u64 n_cap, RowCtl* ctl, u64* out, u64 k,
                                hipStream_t s);
-hipError_t launch_compact_x(const float* x, u64 N, RowCtl* ctl, u64* out, u64 k, hipStream_t s);
+// The compaction of the exact full selection: the filter with tau = ctl->kth and
+// capacity k (tickets: the workspace's ticket words, zero, left zero).
+hipError_t launch_compact_x(const float* x, u64 N, RowCtl* ctl, u64* out, u64 k, u32* tickets, hipStream_t s);
 hipError_t launch_arm_select(SelState* st, u64 rank, u64 count, RowCtl* ctl, hipStream_t s);
 
 // split_out (host, kXcds + 1 words, or nullptr): the per-die chunk ranges used.
@@ -161,6 +163,8 @@ struct RefineArgs {
 };
 
 hipError_t launch_refine(const RefineArgs& a, hipStream_t s);
+// Whether launch_refine takes the one-launch refinement for small k (else the binned one).
+bool refine_one_launch(const RefineArgs& a);
 // Approximate mode routed to the exact selection: *info = {N, 0, 0, 1}.
 hipError_t launch_approx_info_exact(ApproxInfo* info, u64 N, hipStream_t s);
 

@@ -182,11 +182,13 @@ def test_binned_and_multipass_refinement_both_run():
     check_topk(x, vals, idx, 3000)
     assert st["refine_multipass"] == 0
     # two values, ~210K copies of the larger within a value range that puts each tie
-    # group in one bin: the last refinement kernel partitions those bins itself
+    # group in one bin: bins beyond one workgroup's LDS sort go to the multi-block radix
+    # select (the in-kernel partition of such bins runs in approximate mode,
+    # test_gpu_approx.py)
     x = edge_case("two_levels", 1 << 21, 43)
     vals, idx, st = stf.topk(dev(x), 250000, stats=True)
     check_topk(x, vals, idx, 250000)
-    assert st["refine_multipass"] == 0
+    assert st["refine_multipass"] >= 1
     # 419K copies of the larger: beyond what one workgroup partitions, so the host hands
     # the bin to the multi-block radix select
     x = edge_case("two_levels", 1 << 22, 42)
@@ -195,13 +197,30 @@ def test_binned_and_multipass_refinement_both_run():
     assert st["refine_multipass"] >= 1
 
 
+@pytest.mark.parametrize("kind,log2n,k", [("adv_levels", 26, 1 << 15), ("adv_levels", 24, 5000),
+                                         ("adv_levels", 26, 64)])
+def test_tie_groups_in_single_bins_take_the_multipass_select(kind, log2n, k):
+    """Radix-adversarial levels: ~6500 (2^26) or ~1600 (2^24) copies of each of 1024
+    values.  A whole level falls in one value bin of the binned refinement: bins beyond
+    one workgroup's LDS sort (4096 keys) go to the multi-block radix select, smaller
+    ones stay in the bin sort; k <= 64 takes the one-launch refinement (no bins)."""
+    N = 1 << log2n
+    say("tie groups", kind, N, k)
+    x = generate(kind, N, seed=45)
+    vals, idx, st = stf.topk(dev(x), k, stats=True)
+    check_topk(x, vals, idx, k)
+    print("[case] multipass", st["refine_multipass"], "R", st["R"], flush=True)
+    assert st["refine_multipass"] == (1 if (log2n == 26 and k > 64) else 0)
+
+
 def heavy_bins_input(n: int, seed: int) -> np.ndarray:
     """Background noise below 1.5, plus clusters that each fill one value bin of the
     refinement with more keys than one wavefront sorts: 2000 keys within 512 ulps
     (counting pass, ranks by scan and small sub-bucket sorts), 300 copies of one value
     among 200 neighbours (a sub-bucket sorted by one wavefront), 1000 copies (a
     sub-bucket too large for that: the bin goes to the LDS bitonic sort), 5000 copies
-    (a bin beyond one workgroup's LDS: the digit partition), and light bins."""
+    (a bin beyond one workgroup's LDS: the multi-block radix select in exact mode, the
+    in-kernel digit partition in approximate mode), and light bins."""
     rng = np.random.default_rng(seed)
     x = (rng.standard_normal(n) * 0.25).astype(np.float32)
     def ulps(base, off):
@@ -225,7 +244,15 @@ def test_heavy_bins_take_every_sort_path(k):
     x = heavy_bins_input(1 << 21, 44)
     vals, idx, st = stf.topk(dev(x), k, stats=True)
     check_topk(x, vals, idx, k)
-    assert st["refine_multipass"] == 0 and not st["fallback"]
+    # the 5000-copy bin of 7.0 is needed at every k here; the candidates hold all of it
+    # when tau lies below 7.0, else the copies up to tau's index (R minus the values above
+    # 7.0): beyond one workgroup's LDS sort (4096 keys) the multi-block radix select takes it
+    in_bin = min(5000, st["R"][-1] - int(np.count_nonzero(x > np.float32(7.0))))
+    assert st["refine_multipass"] == (1 if in_bin > 4096 else 0) and not st["fallback"]
+    # approximate mode has no host to hand it to: the bin sort's digit partition runs
+    vals, idx, info = stf.topk_approx(dev(x), k)
+    assert stf.approx_info(info)["status"] == 0
+    check_topk(x, vals, idx, k)
 
 
 def test_forced_overflow_goes_to_fallback_and_stays_exact():
@@ -261,6 +288,22 @@ def test_fallback_with_huge_tie_group():
     x = generate("adv_noise", 1 << 22, seed=6)
     vals, idx = stf.topk(dev(x), 20000, options={"force_fallback": 1})
     check_topk(x, vals, idx, 20000)
+
+
+@pytest.mark.parametrize("kind,N,k,offset", [("normal", 1000003, 1, 1), ("adv_levels", (1 << 22) + 5, 70000, 2),
+                                             ("with_nan", 300001, 1000, 3), ("signed_zeros", 200000, 150000, 0),
+                                             ("uniform", 7, 7, 1), ("normal", 5, 1, 3), ("pareto", 1 << 24, 1 << 17, 0),
+                                             ("adv_noise", 1 << 20, 5000, 1)])
+def test_exact_full_selection_on_ragged_views(kind, N, k, offset):
+    """The exact full selection (radix-select passes over x with dwordx4 loads, then the
+    filter as the compaction at tau = the k-th key) on misaligned views with scalar
+    heads and tails, ties, NaN and signed zeros."""
+    say("exact full selection", kind, N, k, offset)
+    edge = ("with_nan", "signed_zeros")
+    x = edge_case(kind, N + offset, 7) if kind in edge else generate(kind, N + offset, seed=7)
+    vals, idx, st = stf.topk(dev(x)[offset:], k, options={"force_fallback": 1}, stats=True)
+    check_topk(x[offset:], vals, idx, k)
+    assert st["fallback"]
 
 
 def test_interleaved_calls_leave_the_workspace_clean():
