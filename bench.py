@@ -648,10 +648,36 @@ def main():
         e1.record(stream)
         e1.synchronize()
         bms = e0.elapsed_time(e1) / nb
+        progress("batched 1024 x 2^20", round(bms, 4), "ms")
         batched = {"rows": B, "row_len": 1 << 20, "k": 64, "ms": round(bms, 4),
                    "gelem_s": round((B << 20) / bms / 1e6, 2),
                    "frac_of_roofline": round(4.0 * (B << 20) / bms / 1e6 / HBM_PEAK_GBPS, 4),
                    "S_per_row": stf.solve(1 << 20, 64, EPS / B, options=bopts)["S"]}
+
+    batched_long = None
+    if "batched" in want and N >= (1 << 26):
+        # rows longer than 2^20 (the page's N = 2^22, B = 16), next to one flat call over
+        # the same 2^26 values
+        xl = xds[0][: 1 << 26]
+        xb = xl.view(16, 1 << 22)
+        bopts = stf.make_options(s_rule=args.s_rule)
+        batched_long = {"rows": 16, "row_len": 1 << 22}
+        for k in (64, 1024):
+            for _ in range(max(1, args.warmup)):
+                stf.topk_batched(xb, k, eps=EPS, seed=0, options=bopts)
+            torch.cuda.synchronize()
+            e0, e1 = _events(torch)
+            e0.record(stream)
+            for c in range(args.steps):
+                stf.topk_batched(xb, k, eps=EPS, seed=c, options=bopts)
+            e1.record(stream)
+            e1.synchronize()
+            bms = e0.elapsed_time(e1) / args.steps
+            fms = time_calls(stf, torch, [xl], k, EPS, bopts, args.steps, args.warmup, stream, out_pair(torch, dev, k))
+            batched_long[str(k)] = {"ms": round(bms, 4), "gelem_s": round((1 << 26) / bms / 1e6, 2),
+                                    "flat_call_same_values_ms": round(fms, 4),
+                                    "S_per_row": stf.solve(1 << 22, k, EPS / 16, options=bopts)["S"]}
+        progress("batched long rows", batched_long)
 
     configs = bench_configs(stf, torch, dev, stream, args, opts, want, keep) if want & {"c1", "c2", "c3", "c5"} else None
 
@@ -697,6 +723,7 @@ def main():
         "read_ceiling": ceiling,
         "configs": configs,
         "batched": batched,
+        "batched_long_rows": batched_long,
         "large": large,
         "workspace_bytes": workspace,
         "cpu_baseline": cpu,

@@ -215,6 +215,27 @@ int profk_topk_batched_ex(const float* x, int64_t B, int64_t N, int64_t ld_x, in
                           const profk_options* opt, profk_stats* st);
 
 /*
+ * profk_topk_batched_approx: the batched form in approximate mode (P1 App. E.2,
+ * "Batched Inputs" and Table 6: approximate mode on batches, the budget split
+ * eps/B per row; App. D: no run-time check).  One sampled attempt per row, every
+ * step enqueued on `stream`, no host wait: the call returns at once and, once a
+ * first call has sized the workspace, can be captured in a HIP graph.  Row r's
+ * output is the exact top-k of the candidates its attempt kept, which is its
+ * exact top-k whenever k <= R <= M held for it (probability at least
+ * 1 - eps/B); the outcome goes to info[r] as in profk_topk_approx (status 1:
+ * positions R..k-1 hold index -1 and value -inf; status 2: the top-k of the M
+ * kept).  Rows short enough that the sample would not pay off are sorted whole
+ * (exact, exact_path = 1).  Shapes outside the batched kernels (k > 16384) run
+ * profk_topk_approx row by row, still stream-ordered.
+ *   info     device pointer to B profk_approx_info records (required)
+ *   other arguments as profk_topk_batched_ex (opt may be NULL; max_attempts,
+ *   force_fallback and timing are ignored)
+ */
+int profk_topk_batched_approx(const float* x, int64_t B, int64_t N, int64_t ld_x, int64_t k, double eps,
+                              uint64_t seed, float* out_vals, int64_t* out_idx, profk_approx_info* info, void* stream,
+                              const profk_options* opt);
+
+/*
  * profk_solve: host-only parameter choice (P1 §4 Theorem 4 / Eq. 5-7; the
  * S rule and closed forms of P2 §4 Theorem 5, Corollary 4, Algorithm 1).
  * Memoised per (N, k, eps, options) (P1 §4 "Fast Approximate Parameter
@@ -254,9 +275,10 @@ int profk_stage_threshold(const float* x, int64_t N, int64_t S, int64_t t, uint6
  *                  unspecified order) at out_idx[r*S .. r*S+S)
  *     out_tau_val  B floats, out_tau_idx B int64: tau_r = the t-th entry of row
  *                  r's sample in the total order (index within the row)
- *   1 <= t <= S, 2S <= N <= 2^20 (rows longer than that: PROFK_EUNSUPPORTED),
- *   ld_x >= N.  Synchronises the stream.  A device-side inconsistency in any
- *   row gives PROFK_EINTERNAL.
+ *   1 <= t <= S, 2S <= N, ld_x >= N, B <= 65535.  Rows of up to 2^20 values use
+ *   the per-row bitmap sampler (then S <= 2^17), longer rows the grid sampler,
+ *   as profk_topk_batched does.  Synchronises the stream.  A device-side
+ *   inconsistency in any row gives PROFK_EINTERNAL.
  */
 int profk_stage_batched_sample(const float* x, int64_t B, int64_t N, int64_t ld_x, int64_t S, int64_t t,
                                uint64_t seed, int32_t attempt, int64_t* out_idx, float* out_tau_val,

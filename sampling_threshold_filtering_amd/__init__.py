@@ -32,7 +32,7 @@ PROFK_ESCRATCH = -6
 STATS_ATTEMPTS = 8
 
 EXPORTED = ("profk_topk", "profk_topk_ex", "profk_topk_approx", "profk_topk_approx_noalloc", "profk_topk_batched",
-            "profk_topk_batched_ex",
+            "profk_topk_batched_ex", "profk_topk_batched_approx",
             "profk_solve",
             "profk_stage_sample", "profk_stage_threshold", "profk_stage_batched_sample", "profk_stage_filter",
             "profk_read_ceiling", "profk_strerror", "profk_release")
@@ -114,6 +114,8 @@ def load_library():
     lib.profk_topk_batched.argtypes = [vp, i64, i64, i64, i64, f64, u64, vp, vp, vp]
     lib.profk_topk_batched_ex.argtypes = [vp, i64, i64, i64, i64, f64, u64, vp, vp, vp, ctypes.POINTER(Options),
                                           ctypes.POINTER(Stats)]
+    lib.profk_topk_batched_approx.argtypes = [vp, i64, i64, i64, i64, f64, u64, vp, vp, vp, vp,
+                                              ctypes.POINTER(Options)]
     lib.profk_solve.argtypes = [i64, i64, f64, ctypes.POINTER(Options), ctypes.POINTER(Params)]
     lib.profk_stage_sample.argtypes = [vp, i64, i64, u64, i32, vp, vp]
     lib.profk_stage_threshold.argtypes = [vp, i64, i64, i64, u64, i32, vp, vp, vp]
@@ -126,7 +128,7 @@ def load_library():
     lib.profk_release.argtypes = []
     lib.profk_release.restype = None
     for name in ("profk_topk", "profk_topk_ex", "profk_topk_approx", "profk_topk_approx_noalloc", "profk_topk_batched",
-                 "profk_topk_batched_ex",
+                 "profk_topk_batched_ex", "profk_topk_batched_approx",
                  "profk_solve",
                  "profk_stage_sample", "profk_stage_threshold", "profk_stage_batched_sample", "profk_stage_filter"):
         getattr(lib, name).restype = ctypes.c_int
@@ -282,15 +284,54 @@ def topk_batched(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, stat
     lib = load_library()
     vals = torch.empty((B, k), dtype=torch.float32, device=x.device)
     idx = torch.empty((B, k), dtype=torch.int64, device=x.device)
-    st = Stats()
+    st = Stats() if stats else None  # statistics make the call wait for every row's record
     with torch.cuda.device(x.device):
         rc = lib.profk_topk_batched_ex(ctypes.c_void_p(x.data_ptr()), B, N, ld, k, eps, seed & (2**64 - 1),
                                        ctypes.c_void_p(vals.data_ptr()), ctypes.c_void_p(idx.data_ptr()),
-                                       _stream_ptr(torch, x.device), _opt_ptr(options), ctypes.byref(st))
+                                       _stream_ptr(torch, x.device), _opt_ptr(options),
+                                       ctypes.byref(st) if st is not None else None)
     _check(rc)
     if stats:
         return vals, idx, stats_to_dict(st)
     return vals, idx
+
+
+def topk_batched_approx(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, out=None, info=None):
+    """Batched approximate mode on a 2-D float32 device tensor (rows may be strided):
+    one attempt per row, enqueued without any host wait.  Returns (values [B,k],
+    column indices [B,k], info) where info is an int64 device tensor [B, 3] of
+    profk_approx_info records (decode with approx_info_rows(info)).  `out` and
+    `info` reuse caller buffers."""
+    import torch
+    if x.dim() != 2 or x.dtype != torch.float32 or not x.is_cuda:
+        raise ValueError("x must be a 2-D float32 device tensor")
+    if x.stride(1) != 1:
+        x = x.contiguous()
+    B, N = x.shape
+    ld = x.stride(0) if B > 1 else N
+    dev = x.device
+    if out is None:
+        vals = torch.empty((B, k), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, k), dtype=torch.int64, device=dev)
+    else:
+        vals, idx = _check_out(out, (B, k), dev)
+    if info is None:
+        info = torch.empty((B, APPROX_INFO_WORDS), dtype=torch.int64, device=dev)
+    elif (info.dtype != torch.int64 or tuple(info.shape) != (B, APPROX_INFO_WORDS) or info.device != dev
+          or not info.is_contiguous()):
+        raise ValueError("info must be a contiguous int64 device tensor of shape (B, 3)")
+    with torch.cuda.device(dev):
+        rc = load_library().profk_topk_batched_approx(
+            ctypes.c_void_p(x.data_ptr()), B, N, ld, k, eps, seed & (2**64 - 1), ctypes.c_void_p(vals.data_ptr()),
+            ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(info.data_ptr()), _stream_ptr(torch, dev),
+            _opt_ptr(options))
+    _check(rc)
+    return vals, idx, info
+
+
+def approx_info_rows(info) -> list:
+    """Decode a [B, 3] batch of profk_approx_info records on the host."""
+    return [approx_info(r) for r in info.detach().cpu()]
 
 
 def solve(N: int, k: int, eps: float = 1e-3, options=None) -> dict:

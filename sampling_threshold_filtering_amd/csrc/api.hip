@@ -14,6 +14,7 @@
 #include <immintrin.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -56,12 +57,12 @@ u64 pow2_at_least(u64 v) {
 }
 
 struct Layout {
-  size_t hash = 0, ctl = 0, sel = 0, rec = 0, ticket = 0, keys = 0, tops = 0, cand = 0, col = 0, topk0 = 0,
-         topk1 = 0, hist = 0, rows = 0, scratch = 0, rtmp = 0, rhist = 0, rbin_off = 0, rbin_cnt = 0, rcursor = 0,
-         pool = 0, total = 0;
+  size_t hash = 0, ctl = 0, sel = 0, rec = 0, rtick = 0, ticket = 0, keys = 0, tops = 0, btops = 0, cand = 0, col = 0,
+         topk0 = 0, topk1 = 0, hist = 0, rows = 0, scratch = 0, rtmp = 0, rhist = 0, rbin_off = 0, rbin_cnt = 0,
+         rcursor = 0, pool = 0, total = 0;
   u64 hash_slots = 0;  // slots of the hash region (the allocation's capacity)
   u64 rows_cap = 0;    // rows of the control regions (the allocation's capacity)
-  u64 hash_used = 0;   // slots this request's sample uses: a power of two >= 2S
+  u64 hash_used = 0;   // slots this request's sample uses (per row with several rows): a power of two >= 2S
 };
 
 // Regions that kernels leave zero for the next call (hash set, tickets and counters,
@@ -69,14 +70,19 @@ struct Layout {
 // offsets that depend only on the allocation's capacities (hash slots, rows); the
 // per-request regions follow.  A later request with other sizes therefore finds them
 // where the previous call cleaned them.
-Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap, u64 rows_cap) {
+// grid_rows > 0: the batched sampler with one hash set, key slots and block lists per
+// row of the attempt's list (4 slots per draw, so that B rows' sets stay small), and
+// grid_tops words of block lists per row.
+Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap, u64 rows_cap, u64 grid_rows = 0,
+                   u64 grid_tops = 0) {
   Layout L;
   // hash set of the sample: 16 slots per draw (up to 2^21 slots) keeps probes and
   // contention on the device-scope CAS low; at least 2 per draw for larger samples
   const u64 s1 = S ? S : 1;
   const u64 sparse = 16 * s1 < (1ull << 21) ? 16 * s1 : (1ull << 21);
-  L.hash_used = pow2_at_least(sparse > 2 * s1 ? sparse : 2 * s1);
-  L.hash_slots = L.hash_used < hash_cap ? hash_cap : L.hash_used;
+  L.hash_used = grid_rows ? pow2_at_least(4 * s1) : pow2_at_least(sparse > 2 * s1 ? sparse : 2 * s1);
+  const u64 hash_need = L.hash_used * (grid_rows ? grid_rows : 1);
+  L.hash_slots = hash_need < hash_cap ? hash_cap : hash_need;
   const u64 rows = B < rows_cap ? rows_cap : B;
   L.rows_cap = rows;
   size_t off = 0;
@@ -89,6 +95,7 @@ Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap, 
   L.ctl = take(rows * sizeof(RowCtl));
   L.sel = take(rows * sizeof(SelState));
   L.rec = take(rows * sizeof(AttemptRecord));
+  L.rtick = take(rows * sizeof(u64));  // per-row sampling tickets of the batched sampler
   L.ticket = take(kTicketWords * sizeof(u32));
   L.rhist = take(kBins * sizeof(u32));
   L.rbin_off = take(kBins * sizeof(u32));
@@ -96,7 +103,8 @@ Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap, 
   L.rcursor = take(kBins * sizeof(u32));
   L.tops = take((size_t)kTopBlocks * kTopT * sizeof(u64));
   // per request
-  L.keys = take(2 * (S ? S : 1) * sizeof(u64));  // S draw slots + the top-up
+  L.keys = take(2 * (S ? S : 1) * (grid_rows ? grid_rows : 1) * sizeof(u64));  // S draw slots + the top-up
+  L.btops = take((grid_rows * grid_tops ? grid_rows * grid_tops : 1) * sizeof(u64));
   L.cand = take(B * (M ? M : 1) * sizeof(u64));
   L.col = take((size_t)kCollectCap * sizeof(u64));
   L.topk0 = take((k ? k : 1) * sizeof(u64));
@@ -141,6 +149,8 @@ std::map<std::pair<int, hipStream_t>, Workspace*> g_ws;
 struct Need {
   u64 B, S, M, k;
   u64 scratch_words = 0;
+  u64 grid_rows = 0;  // the batched sampler's rows (see make_layout)
+  u64 grid_tops = 0;
 };
 
 int get_workspace(hipStream_t s, const Need& need, Workspace** out, Layout* out_layout) {
@@ -154,7 +164,8 @@ int get_workspace(hipStream_t s, const Need& need, Workspace** out, Layout* out_
     w->device = dev;
     w->stream = s;
   }
-  Layout L = make_layout(need.B, need.S, need.M, need.k, need.scratch_words, w->hash_cap, w->rows_cap);
+  Layout L = make_layout(need.B, need.S, need.M, need.k, need.scratch_words, w->hash_cap, w->rows_cap,
+                         need.grid_rows, need.grid_tops);
   if (w->bytes < L.total || w->hash_cap < L.hash_slots || w->rows_cap < L.rows_cap) {
     if (w->dev) {
       HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
@@ -223,6 +234,7 @@ T* at(Workspace* w, size_t off) {
 int clean_if_dirty(Workspace* w, const Layout& L, hipStream_t s) {
   if (!w->dirty) return PROFK_OK;
   HIPCHK(hipMemsetAsync(w->dev + L.hash, 0, L.hash_slots * sizeof(u32), s), "hipMemsetAsync");
+  HIPCHK(hipMemsetAsync(w->dev + L.rtick, 0, L.rows_cap * sizeof(u64), s), "hipMemsetAsync");
   HIPCHK(launch_attempt_init(at<RowCtl>(w, L.ctl), at<SelState>(w, L.sel), at<AttemptRecord>(w, L.rec),
                              at<u32>(w, L.ticket), 1, at<u32>(w, L.rhist), s),
          "launch attempt_init");
@@ -266,6 +278,31 @@ int wait_record(Workspace* w, hipStream_t s, u32 want, u64 early_cap = 0, bool* 
         if (take_early()) return PROFK_OK;
         if (__atomic_load_n(seq, __ATOMIC_ACQUIRE) == want) return PROFK_OK;
         t_err = "sampled attempt: the attempt record was not published";
+        return PROFK_EINTERNAL;
+      }
+      if (q != hipErrorNotReady) return hip_fail(q, "hipStreamQuery");
+    }
+    _mm_pause();
+  }
+}
+
+// Batched form: waits for the filter's summary word of attempt `want` (every listed
+// row passed, or how many failed), spinning on the pinned host word like wait_record.
+int wait_summary(Workspace* w, hipStream_t s, u32 want, bool* all_ok) {
+  const u64* ew = &w->hrec->early;
+  auto take = [&]() -> bool {
+    const u64 e = __atomic_load_n(ew, __ATOMIC_ACQUIRE);
+    if ((u32)(e >> 42) != (want & 0x3FFFFFu)) return false;
+    *all_ok = ((e >> 40) & 3u) == 0;
+    return true;
+  };
+  for (u64 it = 0;; ++it) {
+    if (take()) return PROFK_OK;
+    if ((it & 255) == 255) {
+      const hipError_t q = hipStreamQuery(s);
+      if (q == hipSuccess) {
+        if (take()) return PROFK_OK;
+        t_err = "batched attempt: the filter's summary was not published";
         return PROFK_EINTERNAL;
       }
       if (q != hipErrorNotReady) return hip_fail(q, "hipStreamQuery");
@@ -758,19 +795,35 @@ int topk_approx_static(const float* x, u64 N, u64 k, double eps, u64 seed, float
   return approx_enqueue(&w, L, p, sampled, x, N, k, seed, out_vals, out_idx, info, s);
 }
 
-// Batched form with per-row kernels (rows of at most kBatchedMaxN values, k at most
-// kBatchedMaxM: the refinement holds a row's buffer in LDS up to kBatchedMaxM keys,
-// and beyond that selects over it in global memory and sorts the k in LDS).  Returns PROFK_EUNSUPPORTED when the shape
-// is outside those limits, so that the caller takes the row-by-row path.
+// Which sampler the batched form takes for rows of N values: the per-row workgroup
+// with an LDS bitmap of the row (rows of at most kBatchedMaxN values), or the grid of
+// one-draw-per-thread blocks per row with a hash set per row in device memory (any
+// row length).
+bool batched_grid_sampler(u64 N) {
+  static const char* force = std::getenv("PROFK_BATCHED_SAMPLER");
+  if (force && force[0] == 'g') return true;
+  if (force && force[0] == 'b') return N > kBatchedMaxN;
+  return N > kBatchedMaxN;
+}
+
+// Batched form with per-row kernels (k at most kBatchedMaxM: the refinement holds a
+// row's buffer in LDS up to kBatchedMaxM keys, and beyond that selects over it in
+// global memory and sorts the k in LDS).  Returns PROFK_EUNSUPPORTED when the shape is
+// outside those limits, so that the caller takes the row-by-row path.  With info
+// (approximate mode): one attempt per row, everything enqueued on the stream, no host
+// wait, each row's check reported in info[row].
 int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u64 seed, float* out_vals,
-                      int64_t* out_idx, hipStream_t s, const profk_options* opt, profk_stats* st) {
+                      int64_t* out_idx, hipStream_t s, const profk_options* opt, profk_stats* st,
+                      ApproxInfo* info = nullptr) {
+  const bool approx = info != nullptr;
   if (B >= (1ull << 31)) return PROFK_EUNSUPPORTED;
   profk_params p{};
   if (N > kSmallSort) {
     const int rc = solve_memo((int64_t)N, (int64_t)k, eps / (double)B, opt, &p);  // P1 App. E.2: eps / B per row
     if (rc) return rc;
   }
-  if (N <= kSmallSort || (N <= kBatchedMaxM && p.direct_exact)) {
+  const bool whole = N <= kSmallSort || (N <= kBatchedMaxM && (p.direct_exact || (opt && opt->force_fallback)));
+  if (whole) {
     // rows this short, or short rows where the sample would not pay off: exact top-k by
     // an LDS sort of each row
     Layout L;
@@ -786,6 +839,10 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     a.out_vals = out_vals;
     a.out_idx = out_idx;
     HIPCHK(launch_b_rowsort(a, s), "launch b_rowsort");
+    if (approx) {
+      HIPCHK(launch_b_info_exact(info, B, N, s), "launch b_info_exact");
+      return PROFK_OK;
+    }
     HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
     if (st) {
       st->fallback = 1;
@@ -794,16 +851,44 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     return PROFK_OK;
   }
   int rc = PROFK_OK;
-  const int max_att = max_attempts_of(opt);
-  if (p.direct_exact || max_att == 0 || N > kBatchedMaxN || k > kBatchedMaxM || (u64)p.S > kBatchedMaxN / 8)
+  if (!p.direct_exact && p.M > (int64_t)kBatchedMaxM && k <= kBatchedSelCap && !(opt && opt->s_override)) {
+    // A row buffer beyond the refinement's LDS (kBatchedMaxM keys) is selected over in
+    // global memory by one workgroup, several times slower than the LDS select that
+    // k <= kBatchedSelCap takes; a larger sample shrinks M (about N t / S), so double S
+    // while that stays within N/64 and 2^17 (S changes the work of a call, never its
+    // result).  Larger k sort the whole buffer when it fits LDS, which costs more than
+    // the select over global memory, and keep the rule's S.
+    profk_options o{};
+    if (opt) o = *opt;
+    for (int64_t S2 = 2 * p.S; S2 <= (int64_t)(N / 64) && S2 <= (int64_t)(1 << 17); S2 *= 2) {
+      o.s_override = S2;
+      profk_params q{};
+      rc = solve_memo((int64_t)N, (int64_t)k, eps / (double)B, &o, &q);
+      if (rc) return rc;
+      if (q.direct_exact) break;
+      p = q;
+      if (q.M <= (int64_t)kBatchedMaxM) break;
+    }
+  }
+  const int max_att = approx ? 1 : max_attempts_of(opt);
+  const bool grid = batched_grid_sampler(N);
+  if (p.direct_exact || max_att == 0 || (opt && opt->force_fallback) || k > kBatchedMaxM ||
+      (!grid && (N > kBatchedMaxN || (u64)p.S > kBatchedMaxN / 8)))
     return PROFK_EUNSUPPORTED;
   const u64 S = (u64)p.S, M = (u64)p.M, t = (u64)p.t;
   const u64 G = batched_sample_blocks(B);
+  // the grid sampler's per-row block lists: pow2(t) keys per sampling block
+  u64 T = 1;
+  while (T < t) T <<= 1;
+  const bool fast = t >= 1 && t <= kTopT && sample_blocks(S, t) <= kTopBlocks;
+  const u64 tops_per_row = fast ? (u64)sample_blocks(S, t) * T : 1;
   Layout L;
   Workspace* w = nullptr;
-  rc = get_workspace(s, Need{B, 0, M, 1, G * 2 * S}, &w, &L);  // per sampling workgroup: S slots + top-up
+  rc = grid ? get_workspace(s, Need{B, S, M, 1, 0, B, tops_per_row}, &w, &L)
+            : get_workspace(s, Need{B, 0, M, 1, G * 2 * S}, &w, &L);  // per sampling workgroup: S slots + top-up
   if (rc) return rc;
   RowCtl* ctl = at<RowCtl>(w, L.ctl);
+  SelState* sel = at<SelState>(w, L.sel);
   AttemptRecord* rec = at<AttemptRecord>(w, L.rec);
   int* rows_dev = at<int>(w, L.rows);
   if (st) {
@@ -815,7 +900,9 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
   rc = clean_if_dirty(w, L, s);
   if (rc) return rc;
   w->dirty = true;
-  HIPCHK(launch_attempt_init(ctl, nullptr, rec, at<u32>(w, L.ticket), (u32)B, nullptr, s), "launch attempt_init");
+  // control blocks, records and (grid sampler) the rows' top-digit histograms
+  HIPCHK(launch_attempt_init(ctl, grid ? sel : nullptr, rec, at<u32>(w, L.ticket), (u32)B, nullptr, s),
+         "launch attempt_init");
   const int* rows = nullptr;  // all rows on the first attempt
   u64 nrows = B;
   std::vector<int> failed;
@@ -838,7 +925,43 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     a.out_vals = out_vals;
     a.out_idx = out_idx;
     a.rec = rec;
-    HIPCHK(launch_b_sample(a, s), "launch b_sample");
+    a.approx = approx ? 1u : 0u;
+    a.info = info;
+    if (grid) {
+      // one grid row of sampling blocks per listed row (at most 65535 per launch)
+      a.table = at<u32>(w, L.hash);
+      a.table_slots = L.hash_used;
+      for (u64 l0 = 0; l0 < nrows; l0 += 65535) {
+        SampleArgs sa{};
+        sa.x = x;
+        sa.N = N;
+        sa.S = S;
+        sa.seed = seed;
+        sa.attempt = (u32)att;
+        sa.table = at<u32>(w, L.hash) + l0 * L.hash_used;
+        sa.tmask = L.hash_used - 1;
+        sa.keys = at<u64>(w, L.keys) + l0 * 2 * S;
+        sa.tops = at<u64>(w, L.btops) + l0 * tops_per_row;
+        sa.ctl = ctl;
+        sa.rec = rec;
+        sa.ticket = at<u64>(w, L.rtick) + l0;
+        sa.top_hist = sel->hist;
+        sa.t = t;
+        sa.fast = fast ? 1u : 0u;
+        sa.rows = rows ? rows + l0 : nullptr;
+        sa.nrows = (u32)(nrows - l0 < 65535 ? nrows - l0 : 65535);
+        sa.row0 = (u32)l0;
+        sa.ld = ld;
+        sa.table_stride = L.hash_used;
+        sa.keys_stride = 2 * S;
+        sa.tops_stride = tops_per_row;
+        sa.ticket_stride = 1;
+        sa.hist_stride = sizeof(SelState) / sizeof(u32);
+        HIPCHK(launch_sample(sa, s), "launch sample (batched)");
+      }
+    } else {
+      HIPCHK(launch_b_sample(a, s), "launch b_sample");
+    }
     FilterArgs fa{};
     fa.x = x;
     fa.ld = ld;
@@ -851,12 +974,33 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     fa.k = k;
     fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
     fa.groups = at<u32>(w, L.ticket) + kTickets;
-    for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[x];
+    for (u32 xd = 0; xd < kXcds; ++xd) fa.weight[xd] = w->xw[xd];
     fa.rec = rec;
     fa.sels = nullptr;
     fa.sparse = filter_shape(p, N);
+    // exact mode without statistics: the filter's last block publishes whether every
+    // listed row passed into pinned host memory, and when they all did the call returns
+    // on that word while the refinement still runs (outputs complete in stream order)
+    const bool summary = !approx && !st;
+    u32 seq = 0;
+    if (summary) {
+      seq = ++w->seq;
+      fa.hrec = w->hrec_dev;
+      fa.seq = seq;
+      fa.summary = 1;
+    }
     HIPCHK(launch_filter(fa, 0, s), "launch filter");
     HIPCHK(launch_b_refine(a, s), "launch b_refine");
+    if (approx) break;
+    if (summary) {
+      bool all_ok = false;
+      rc = wait_summary(w, s, seq, &all_ok);
+      if (rc) return rc;
+      if (all_ok) {
+        nrows = 0;
+        break;
+      }
+    }
     HIPCHK(hipMemcpyAsync(w->host, rec, B * sizeof(AttemptRecord), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
     HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
     failed.clear();
@@ -885,7 +1029,7 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     }
   }
   w->dirty = false;
-  if (nrows == 0) return PROFK_OK;
+  if (approx || nrows == 0) return PROFK_OK;
   // rows that failed every attempt: exact full selection, row by row
   std::vector<int> rest(failed);
   if (st) st->rows_fallback = (int64_t)rest.size();
@@ -967,6 +1111,26 @@ int profk_topk_batched_ex(const float* x, int64_t B, int64_t N, int64_t ld_x, in
   return PROFK_OK;
 }
 
+int profk_topk_batched_approx(const float* x, int64_t B, int64_t N, int64_t ld_x, int64_t k, double eps,
+                              uint64_t seed, float* out_vals, int64_t* out_idx, profk_approx_info* info, void* stream,
+                              const profk_options* opt) {
+  int rc = validate(x, N, k, eps, out_vals, out_idx);
+  if (rc) return rc;
+  if (B < 1 || ld_x < N || !info) return PROFK_EINVAL;
+  rc = topk_batched_rows(x, (u64)B, (u64)N, (u64)ld_x, (u64)k, eps, seed, out_vals, out_idx, (hipStream_t)stream, opt,
+                         nullptr, info);
+  if (rc != PROFK_EUNSUPPORTED) return rc;
+  // shapes outside the batched kernels: the flat approximate call row by row (budget
+  // eps / B each), all stream-ordered
+  const double eps_row = eps / (double)B;
+  for (int64_t r = 0; r < B; ++r) {
+    rc = topk_approx_row(x + r * ld_x, (u64)N, (u64)k, eps_row, seed, out_vals + r * k, out_idx + r * k, info + r,
+                         (hipStream_t)stream, opt);
+    if (rc) return rc;
+  }
+  return PROFK_OK;
+}
+
 int profk_topk_batched(const float* x, int64_t B, int64_t N, int64_t ld_x, int64_t k, double eps, uint64_t seed,
                        float* out_vals, int64_t* out_idx, void* stream) {
   return profk_topk_batched_ex(x, B, N, ld_x, k, eps, seed, out_vals, out_idx, stream, nullptr, nullptr);
@@ -1035,38 +1199,78 @@ int profk_stage_batched_sample(const float* x, int64_t B, int64_t N, int64_t ld_
   if (!x || !out_idx || !out_tau_val || !out_tau_idx || B < 1 || N < 2 || ld_x < N || S < 1 || 2 * S > N || t < 1 ||
       t > S || attempt < 0)
     return PROFK_EINVAL;
-  if ((u64)N > kBatchedMaxN || (u64)S > kBatchedMaxN / 8 || B >= (int64_t(1) << 31)) return PROFK_EUNSUPPORTED;
+  const bool grid = batched_grid_sampler((u64)N);
+  if (B >= (int64_t(1) << 31) || B > 65535 || (!grid && ((u64)N > kBatchedMaxN || (u64)S > kBatchedMaxN / 8)))
+    return PROFK_EUNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   Layout L;
   Workspace* w = nullptr;
-  const u64 nb = (u64)B;
-  int rc = get_workspace(s, Need{nb, 0, 1, 1, nb * 2 * (u64)S}, &w, &L);
+  const u64 nb = (u64)B, uS = (u64)S, ut = (u64)t;
+  u64 T = 1;
+  while (T < ut) T <<= 1;
+  const bool fast = ut <= kTopT && sample_blocks(uS, ut) <= kTopBlocks;
+  const u64 tops_per_row = fast ? (u64)sample_blocks(uS, ut) * T : 1;
+  int rc = grid ? get_workspace(s, Need{nb, uS, 1, 1, 0, nb, tops_per_row}, &w, &L)
+                : get_workspace(s, Need{nb, 0, 1, 1, nb * 2 * uS}, &w, &L);
   if (rc) return rc;
   rc = clean_if_dirty(w, L, s);
   if (rc) return rc;
   w->dirty = true;
   RowCtl* ctl = at<RowCtl>(w, L.ctl);
+  SelState* sel = at<SelState>(w, L.sel);
   AttemptRecord* rec = at<AttemptRecord>(w, L.rec);
-  u64* scratch = at<u64>(w, L.scratch);
-  HIPCHK(launch_attempt_init(ctl, nullptr, rec, at<u32>(w, L.ticket), (u32)nb, nullptr, s), "launch attempt_init");
-  // every row's 2S key slots start at zero, so that the nonzero ones are its sample
-  HIPCHK(launch_clear_sample(reinterpret_cast<u32*>(scratch), nb * 4 * (u64)S, at<u32>(w, L.ticket), s),
-         "launch clear scratch");
-  BatchedArgs a{};
-  a.x = x;
-  a.ld = (u64)ld_x;
-  a.N = (u64)N;
-  a.rows = nullptr;
-  a.nrows = nb;
-  a.S = (u64)S;
-  a.t = (u64)t;
-  a.seed = seed;
-  a.attempt = (u32)attempt;
-  a.ctls = ctl;
-  a.scratch = scratch;
-  HIPCHK(launch_b_sample(a, s, (u32)nb), "launch b_sample");
-  HIPCHK(launch_b_stage_out(x, (u64)ld_x, (u64)N, nb, (u64)S, scratch, ctl, out_idx, out_tau_val, out_tau_idx, rec, s),
+  // row r's 2S key slots (a slice of the per-workgroup scratch, or of the grid
+  // sampler's key region) start at zero, so that the nonzero ones are its sample
+  u64* keys = grid ? at<u64>(w, L.keys) : at<u64>(w, L.scratch);
+  HIPCHK(launch_attempt_init(ctl, grid ? sel : nullptr, rec, at<u32>(w, L.ticket), (u32)nb, nullptr, s),
+         "launch attempt_init");
+  HIPCHK(launch_clear_sample(reinterpret_cast<u32*>(keys), nb * 4 * uS, at<u32>(w, L.ticket), s), "launch clear keys");
+  if (grid) {
+    SampleArgs sa{};
+    sa.x = x;
+    sa.N = (u64)N;
+    sa.S = uS;
+    sa.seed = seed;
+    sa.attempt = (u32)attempt;
+    sa.table = at<u32>(w, L.hash);
+    sa.tmask = L.hash_used - 1;
+    sa.keys = keys;
+    sa.tops = at<u64>(w, L.btops);
+    sa.ctl = ctl;
+    sa.rec = rec;
+    sa.ticket = at<u64>(w, L.rtick);
+    sa.top_hist = sel->hist;
+    sa.t = ut;
+    sa.fast = fast ? 1u : 0u;
+    sa.rows = nullptr;
+    sa.nrows = (u32)nb;
+    sa.row0 = 0;
+    sa.ld = (u64)ld_x;
+    sa.table_stride = L.hash_used;
+    sa.keys_stride = 2 * uS;
+    sa.tops_stride = tops_per_row;
+    sa.ticket_stride = 1;
+    sa.hist_stride = sizeof(SelState) / sizeof(u32);
+    HIPCHK(launch_sample(sa, s), "launch sample (batched)");
+  } else {
+    BatchedArgs a{};
+    a.x = x;
+    a.ld = (u64)ld_x;
+    a.N = (u64)N;
+    a.rows = nullptr;
+    a.nrows = nb;
+    a.S = uS;
+    a.t = ut;
+    a.seed = seed;
+    a.attempt = (u32)attempt;
+    a.ctls = ctl;
+    a.scratch = keys;
+    HIPCHK(launch_b_sample(a, s, (u32)nb), "launch b_sample");
+  }
+  HIPCHK(launch_b_stage_out(x, (u64)ld_x, (u64)N, nb, uS, keys, ctl, out_idx, out_tau_val, out_tau_idx, rec, s),
          "launch b_stage_out");
+  if (grid)  // the per-row hash sets back to zero (the refinement does this in a call)
+    HIPCHK(launch_clear_sample(at<u32>(w, L.hash), nb * L.hash_used, at<u32>(w, L.ticket), s), "launch clear hash");
   HIPCHK(hipMemcpyAsync(w->host, rec, nb * sizeof(AttemptRecord), hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
   HIPCHK(hipStreamSynchronize(s), "hipStreamSynchronize");
   w->dirty = false;

@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kBThreads) void b_sample_kernel(BatchedArgs a) {
 // above it are gathered and sorted (one wavefront in registers up to 64, else an LDS
 // bitonic sort) and written out; for k above kSelCap the whole row is sorted in LDS.
 constexpr u32 kRefineThreads = 256;
-constexpr u32 kSelCap = 1024;
+constexpr u32 kSelCap = kBatchedSelCap;
 
 namespace {
 // Value bits from a key's order code, except the codes that fold encodings (+-0, NaN).
@@ -301,6 +301,8 @@ __device__ __forceinline__ u32 row_value_bits(u64 key, const float* row, u32 idx
   if (o == 0x80000000u || o == 0xFFFFFFFFu) return reinterpret_cast<const u32*>(row)[idx];
   return bits_of_ord32(o);
 }
+
+__device__ __forceinline__ u64 cand_at(const BatchedArgs& a, u32 row, u32 i) { return a.cand[(u64)row * a.M + i]; }
 
 __device__ __forceinline__ void write_row_key(u64 key, u64 j, const float* row, u64 N, float* ov, int64_t* oi) {
   const u32 idx = key_index(key);
@@ -318,28 +320,50 @@ __global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a)
   const u32 tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   for (u64 li = blockIdx.x; li < a.nrows; li += gridDim.x) {
     const u32 row = a.rows ? (u32)a.rows[li] : (u32)li;
+    if (a.table) {  // this position's sample hash set, zero again for the next attempt
+      uint4* t = reinterpret_cast<uint4*>(a.table + li * a.table_slots);
+      for (u64 i = tid; i < a.table_slots / 4; i += kRefineThreads) t[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
     const RowCtl* c = &a.ctls[row];
-    if (c->status != 0) continue;  // uniform per workgroup
+    const u32 status = c->status;  // uniform per workgroup
+    // exact mode refines rows whose check held; approximate mode also the others
+    const bool live = status == 0 || (a.approx && (status == 1u || status == 2u));
     const u64 R = c->R;
-    const u32 n = (u32)(R < a.M ? R : a.M);
-    const u64* cand = a.cand + (u64)row * a.M;
+    const u32 n = live ? (u32)(R < a.M ? R : a.M) : 0u;
     const float* xr = a.x + (u64)row * a.ld;
     float* ov = a.out_vals + (u64)row * a.k;
     int64_t* oi = a.out_idx + (u64)row * a.k;
+    if (a.approx) {
+      if (tid == 0 && a.info) {
+        ApproxInfo inf;
+        inf.R = (int64_t)R;
+        inf.M = (int64_t)a.M;
+        inf.status = (int32_t)status;
+        inf.exact_path = 0;
+        a.info[row] = inf;
+      }
+      for (u64 p = n + tid; p < a.k; p += kRefineThreads) {  // fewer than k kept
+        oi[p] = -1;
+        reinterpret_cast<u32*>(ov)[p] = 0xFF800000u;  // -inf
+      }
+    }
+    if (n == 0) continue;
+    const u32 kk = (u32)(a.k < n ? a.k : n);  // outputs this row gets (k unless fewer were kept)
     if (n <= (u32)kWave) {
       if (wid == 0) {
-        const u64 v = wave_sort_desc(lane < n ? cand[lane] : 0ull);
-        if (lane < a.k) write_row_key(v, lane, xr, a.N, ov, oi);
+        const u64 v = wave_sort_desc(lane < n ? cand_at(a, row, lane) : 0ull);
+        if (lane < kk) write_row_key(v, lane, xr, a.N, ov, oi);
       }
       continue;
     }
+    const u64* cand = a.cand + (u64)row * a.M;
     __syncthreads();  // the previous row's users of s are done
     if (n > kBatchedMaxM) {
       // more candidates than LDS holds: the k-th largest by the one-workgroup radix
       // select over the buffer in global memory, then the k keys at or above it (k <=
       // kBatchedMaxM, the host's bound) are gathered into LDS and sorted there
       bool ok = false;
-      const u64 kth = block_select_rank(cand, n, a.k, s, (u32)kBatchedMaxM, &s_bsel, &ok);
+      const u64 kth = block_select_rank(cand, n, kk, s, (u32)kBatchedMaxM, &s_bsel, &ok);
       if (!ok) {
         // the select came back inconsistent (never expected): report it instead of
         // writing k arbitrary keys; the host turns it into PROFK_EINTERNAL
@@ -356,7 +380,7 @@ __global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a)
         }
       }
       __syncthreads();
-      const u32 m = s_n < a.k ? s_n : (u32)a.k;  // exactly k: the keys are distinct
+      const u32 m = s_n < kk ? s_n : kk;  // exactly kk: the keys are distinct
       u32 P = 1;
       while (P < m) P <<= 1;
       for (u32 i = m + tid; i < P; i += kRefineThreads) s[i] = 0ull;
@@ -367,21 +391,21 @@ __global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a)
     }
     constexpr u32 kILP = 8;
     for (u32 base = 0; base < n; base += kRefineThreads * kILP) {
-      u64 kk[kILP];
+      u64 kv[kILP];
 #pragma unroll
       for (u32 q = 0; q < kILP; ++q) {
         const u32 i = base + q * kRefineThreads + tid;
-        kk[q] = i < n ? cand[i] : 0ull;
+        kv[q] = i < n ? cand[i] : 0ull;
       }
 #pragma unroll
       for (u32 q = 0; q < kILP; ++q) {
         const u32 i = base + q * kRefineThreads + tid;
-        if (i < n) s[i] = kk[q];
+        if (i < n) s[i] = kv[q];
       }
     }
     __syncthreads();
     if (a.k <= kSelCap) {
-      const u64 kth = lds_select_desc(s, n, (u32)a.k, &s_sel);
+      const u64 kth = lds_select_desc(s, n, kk, &s_sel);
       if (tid == 0) s_n = 0;
       __syncthreads();
       for (u32 i = tid; i < n; i += kRefineThreads) {
@@ -392,7 +416,7 @@ __global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a)
         }
       }
       __syncthreads();
-      const u32 m = s_n < a.k ? s_n : (u32)a.k;  // exactly k: the keys are distinct
+      const u32 m = s_n < kk ? s_n : kk;  // exactly kk: the keys are distinct
       if (m <= (u32)kWave) {
         if (wid == 0) {
           const u64 v = wave_sort_desc(lane < m ? s_top[lane] : 0ull);
@@ -412,7 +436,7 @@ __global__ __launch_bounds__(kRefineThreads) void b_refine_kernel(BatchedArgs a)
       for (u32 i = n + tid; i < P; i += kRefineThreads) s[i] = 0ull;
       __syncthreads();
       block_bitonic_desc(s, P);
-      for (u32 j = tid; j < a.k; j += kRefineThreads) write_row_key(s[j], j, xr, a.N, ov, oi);
+      for (u32 j = tid; j < kk; j += kRefineThreads) write_row_key(s[j], j, xr, a.N, ov, oi);
     }
   }
 }
@@ -434,6 +458,25 @@ __global__ __launch_bounds__(kBThreads) void b_rowsort_kernel(BatchedArgs a) {
   }
 }
 
+// Approximate mode, rows sorted whole (the exact result): info[r] = {N, 0, 0, 1}.
+__global__ void b_info_exact_kernel(ApproxInfo* info, u64 nrows, u64 N) {
+  for (u64 r = (u64)blockIdx.x * blockDim.x + threadIdx.x; r < nrows; r += (u64)gridDim.x * blockDim.x) {
+    ApproxInfo inf;
+    inf.R = (int64_t)N;
+    inf.M = 0;
+    inf.status = 0;
+    inf.exact_path = 1;
+    info[r] = inf;
+  }
+}
+
+hipError_t launch_b_info_exact(ApproxInfo* info, u64 nrows, u64 N, hipStream_t s) {
+  u64 g = (nrows + 255) / 256;
+  if (g > 1024) g = 1024;
+  b_info_exact_kernel<<<(u32)(g ? g : 1), 256, 0, s>>>(info, nrows, N);
+  return hipGetLastError();
+}
+
 namespace {
 u32 row_grid(u64 nrows, u32 per_cu) {
   u64 g = (u64)device_cu_count() * per_cu;
@@ -445,7 +488,8 @@ u32 row_grid(u64 nrows, u32 per_cu) {
 u32 batched_sample_blocks(u64 nrows) { return row_grid(nrows, 1); }
 
 hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s, u32 grid) {
-  b_sample_kernel<<<grid ? grid : batched_sample_blocks(a.nrows), kBThreads, 0, s>>>(a);
+  if (!grid) grid = batched_sample_blocks(a.nrows);
+  b_sample_kernel<<<grid, kBThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -253,6 +253,7 @@ template <int U, bool NT>
 __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   __shared__ u64 s_stage[kWavesPerBlock][kStageCap];
   __shared__ u32 s_last;
+  __shared__ u32 s_nfail;  // last block: listed rows whose check failed
   // wave-uniform: tile coordinates, row, threshold live in scalar registers, and their
   // loads wait on the scalar counter, not behind the tile's vector loads
   const u32 wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -412,6 +413,8 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
       if (a.hrec) a.hrec->xt[i] = i == 0 ? (t ? ~t : 0ull) : t;
     }
   }
+  if (threadIdx.x == 0) s_nfail = 0;
+  __syncthreads();
   for (u64 lr = threadIdx.x; lr < a.nrows; lr += blockDim.x) {
     const u32 row = a.rows ? (u32)a.rows[lr] : (u32)lr;
     RowCtl* c = &a.ctls[row];
@@ -419,11 +422,12 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     u32 status = c->status;
     if (status == 0) status = R < a.k ? 1u : (R > a.M ? 2u : 0u);
     c->status = status;
+    if (status) atomicAdd(&s_nfail, 1u);
     if (a.rec) {
       a.rec[row].R = R;
       a.rec[row].status = status;
     }
-    if (lr == 0 && a.hrec && a.seq) {
+    if (lr == 0 && a.hrec && a.seq && !a.summary) {
       // the host learns the check here, before the refinement runs
       const u64 word = ((u64)(a.seq & 0x3FFFFFu) << 42) | ((u64)(status & 3u) << 40) | (R & ((1ull << 40) - 1));
       __hip_atomic_store(&a.hrec->early, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -440,6 +444,17 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
       s->ncol = 0;
     }
   }
+  if (a.summary && a.hrec && a.seq) {
+    // several rows: the host learns here whether every row passed (status 0, and the
+    // number of rows listed), else the number that failed (status 1)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const u32 nf = s_nfail;
+      const u64 cnt = nf ? (u64)nf : a.nrows;
+      const u64 word = ((u64)(a.seq & 0x3FFFFFu) << 42) | ((u64)(nf ? 1u : 0u) << 40) | (cnt & ((1ull << 40) - 1));
+      __hip_atomic_store(&a.hrec->early, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  }
   if (threadIdx.x == 0) atomic_store_agent(a.ticket, 0u);
 }
 
@@ -452,11 +467,18 @@ hipError_t launch_filter_shape(const FilterArgs& a0, u32 grid, u32 blocks_per_cu
   a.tiles_per_row = (max_vec + vec_per_tile - 1) / vec_per_tile;
   if (a.tiles_per_row == 0) a.tiles_per_row = 1;
   a.total_tiles = a.tiles_per_row * a.nrows;
-  a.run = a.nrows == 1 ? 1 : kFilterRun;
   u64 need = (a.total_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
   if (need < 1) need = 1;
   if (grid == 0) grid = blocks_per_cu * device_cu_count();
   if ((u64)grid > need) grid = (u32)need;
+  // several rows: chunks of up to kFilterRun tiles, but short enough that every
+  // wavefront gets about four (16 rows of 2^22 values are only 256 chunks of 64 tiles,
+  // which would leave most wavefronts idle)
+  a.run = 1;
+  if (a.nrows > 1) {
+    const u64 per = a.total_tiles / ((u64)grid * kWavesPerBlock * 4);
+    a.run = per < 1 ? 1 : (per > kFilterRun ? kFilterRun : per);
+  }
   // chunk ranges per die, in proportion to (blocks on the die) x (the die's weight)
   const u64 nchunks = (a.total_tiles + a.run - 1) / a.run;
   double share[kXcds], tot = 0.0;

@@ -104,8 +104,22 @@ __global__ __launch_bounds__(1024) void attempt_init_kernel(RowCtl* ctl, SelStat
 constexpr u32 kTauCap = 8192;  // keys the last block sorts or selects from in LDS (64 KB)
 
 template <u32 kSampleThreads>
-__global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a0) {
   constexpr u32 kSampleWaves = kSampleThreads / kWave;
+  SampleArgs a = a0;  // this row's view (wave-uniform)
+  if (a0.nrows) {
+    const u64 li = blockIdx.y;
+    const u32 row = a0.rows ? (u32)a0.rows[li] : a0.row0 + (u32)li;
+    a.row = row;
+    a.x = a0.x + (u64)row * a0.ld;
+    a.ctl = a0.ctl + row;
+    a.rec = a0.rec ? a0.rec + row : nullptr;
+    a.top_hist = a0.top_hist + (u64)row * a0.hist_stride;
+    a.table = a0.table + li * a0.table_stride;
+    a.keys = a0.keys + li * a0.keys_stride;
+    a.tops = a0.tops + li * a0.tops_stride;
+    a.ticket = a0.ticket + li * a0.ticket_stride;
+  }
   __shared__ u64 s_buf[kTauCap];
   __shared__ BlockSelectLds s_sel;
   __shared__ LdsSelect s_lsel;
@@ -374,10 +388,11 @@ u32 sample_blocks(u64 S, u64 t) {
 
 hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
   const u32 th = sample_threads(a.S, a.t), blocks = sample_blocks(a.S, a.t);
+  const dim3 grid(blocks, a.nrows ? a.nrows : 1u);
   if (th == 256)
-    sample_kernel<256><<<blocks, 256, 0, s>>>(a);
+    sample_kernel<256><<<grid, 256, 0, s>>>(a);
   else
-    sample_kernel<1024><<<blocks, 1024, 0, s>>>(a);
+    sample_kernel<1024><<<grid, 1024, 0, s>>>(a);
   return hipGetLastError();
 }
 

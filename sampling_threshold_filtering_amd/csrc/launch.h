@@ -47,6 +47,8 @@ struct FilterArgs {
   u64* xtime;          // kXcds + 1 words: start (min) and per-die stream ends (max); zero, left zero
   HostRecord* hrec;    // where the last block copies xtime for the host, or nullptr
   u32 seq;             // with hrec: the attempt's sequence number for hrec->early (row 0)
+  u32 summary;         // with hrec, several rows: hrec->early says whether every listed row
+                       // passed its check instead of row 0's R
   u64 split[kXcds + 1];  // chunk ranges per die (set by launch_filter from weights)
   float weight[kXcds];   // relative speed of each die (input to launch_filter; 0 = equal)
   u32 sparse;            // launch shape by the expected density of hits: kShapeSparse (fewer
@@ -84,6 +86,20 @@ struct SampleArgs {
   u32* top_hist;    // 256 words, zero on entry, left zero
   u64 t;            // threshold rank (0: sample only)
   u32 fast;         // 1: per-block lists (t <= kTopT, at most kTopBlocks blocks)
+  // Several rows at once (the batched form): the grid has one row of blocks per row
+  // in the list (blockIdx.y is the position in it).  The pointers above are for row 0
+  // (x, ctl, rec, top_hist, indexed by row id) or list position 0 (table, keys, tops,
+  // ticket) and advance by these strides; the Philox counter takes the row id.
+  // nrows = 0: one row, the fields above as they are.
+  const int* rows;  // row ids, or nullptr for rows row0 .. row0 + nrows - 1
+  u32 nrows;
+  u32 row0;
+  u64 ld;           // elements between rows of x
+  u64 table_stride; // u32 slots between positions' hash sets
+  u64 keys_stride;  // u64 words between positions' key slots
+  u64 tops_stride;  // u64 words between positions' block lists
+  u64 ticket_stride;  // u64 words between positions' tickets
+  u64 hist_stride;  // u32 words between rows' top-digit histograms
 };
 
 // Sampling launch shape for (S, t): 256-thread workgroups while the per-block-list
@@ -173,6 +189,9 @@ constexpr u64 kBatchedMaxN = 1ull << 20;
 // Batched refinement: a row buffer of up to this many keys is held in LDS (128 KB); k
 // is at most this.
 constexpr u64 kBatchedMaxM = 1ull << 14;
+// Batched refinement: up to this k the k-th largest is selected in LDS and only the k
+// keys at or above it are sorted; above it the whole buffer is sorted.
+constexpr u32 kBatchedSelCap = 1024;
 
 struct BatchedArgs {
   const float* x;  // row 0
@@ -184,16 +203,23 @@ struct BatchedArgs {
   u64 seed;
   u32 attempt;
   RowCtl* ctls;    // per row
-  u64* scratch;    // sample keys: S per sampling workgroup
+  u64* scratch;    // sample keys: 2S per sampling workgroup
   u64* cand;       // per row M keys (row stride M)
   u64 M;
   u64 k;
   float* out_vals; // B x k
   int64_t* out_idx;
   AttemptRecord* rec;  // per row: the refinement flags an internal error here, or nullptr
+  u32* table;      // the batched sampler's hash sets, one per list position, which the
+                   // refinement clears; nullptr with the per-row bitmap sampler
+  u64 table_slots; // slots per position (a multiple of 4)
+  u32 approx;      // 1: approximate mode (refine whatever each row's buffer holds, pad,
+                   // and report each row's check in info[row])
+  ApproxInfo* info;
 };
 
 u32 batched_sample_blocks(u64 nrows);
+
 // grid 0: the persistent grid (batched_sample_blocks); the stage entry point takes one
 // workgroup per row so that every row keeps its keys in its own scratch slice
 hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s, u32 grid = 0);
@@ -202,6 +228,7 @@ hipError_t launch_b_stage_out(const float* x, u64 ld, u64 N, u64 B, u64 S, const
                               hipStream_t s);
 hipError_t launch_b_refine(const BatchedArgs& a, hipStream_t s);
 hipError_t launch_b_rowsort(const BatchedArgs& a, hipStream_t s);
+hipError_t launch_b_info_exact(ApproxInfo* info, u64 nrows, u64 N, hipStream_t s);
 
 // Inputs of 2^32 values or more (k_merge.hip): G sorted per-segment top-k lists.
 constexpr u32 kMaxSegments = 64;

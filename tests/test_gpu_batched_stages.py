@@ -67,13 +67,18 @@ def test_batched_sample_and_threshold_match_oracle(kind, B, N, S, t, seed, attem
         assert tau_v[r:r + 1].view(np.uint32)[0] == np.float32(rv).view(np.uint32), r
 
 
-def test_batched_stage_rejects_long_rows():
-    import torch
-    say("batched stage, rows above 2^20")
-    x = torch.zeros((2, (1 << 20) + 64), dtype=torch.float32, device="cuda")
-    with pytest.raises(stf.ProfkError) as e:
-        stf.stage_batched_sample(x, 1024, 4)
-    assert e.value.code == stf.PROFK_EUNSUPPORTED
+GRID_CASES = [
+    # rows longer than 2^20: the grid sampler (one draw per thread, a hash set per row)
+    ("normal", 8, (1 << 21) + 5, 32768, 13, 9, 0, 0),   # block lists (t <= 64), ragged rows
+    ("pareto", 4, 1 << 22, 4096, 100, 10, 1, 0),        # t > 64, every key slot in LDS
+    ("uniform", 4, 1 << 21, 16384, 70, 11, 0, 7),       # t > 64, slots beyond LDS: select over L2
+    ("adv_noise", 4, 1 << 21, 8192, 30, 12, 2, 0),      # 256 distinct values
+]
+
+
+@pytest.mark.parametrize("kind,B,N,S,t,seed,attempt,pad", GRID_CASES)
+def test_batched_grid_sampler_matches_oracle(kind, B, N, S, t, seed, attempt, pad):
+    test_batched_sample_and_threshold_match_oracle(kind, B, N, S, t, seed, attempt, pad)
 
 
 def check_batched(x, vals, idx, k):
@@ -105,3 +110,23 @@ def test_batched_retry_with_mixed_passing_and_failing_rows(mode):
     assert 0 < st["rows_retried"] < B
     assert st["attempts"] >= 2
     assert st["rows_fallback"] < B // 4
+    # without statistics the host first takes the filter's summary word, which reports
+    # the failed rows; it then reads the per-row records and redraws those rows
+    vals, idx = stf.topk_batched(dev(x), k, eps=eps, seed=3, options=opts)
+    check_batched(x, vals, idx, k)
+
+
+@pytest.mark.parametrize("kind,B,N,k,pad", [("pareto", 16, 1 << 22, 64, 0), ("normal", 16, 1 << 22, 1024, 0),
+                                           ("uniform", 5, (1 << 21) + 3, 500, 5), ("adv_levels", 4, 1 << 22, 3000, 0),
+                                           ("normal", 3, 1 << 21, 20000, 0)])
+def test_batched_long_rows(kind, B, N, k, pad):
+    """Rows longer than 2^20 (P1 App. E.2 runs N = 2^22 with B = 16) on the batched
+    kernels (grid sampler, multi-row filter, per-row refinement); k above 16384 runs
+    the flat path row by row."""
+    say("batched long rows", kind, B, N, k, pad)
+    ld = N + pad
+    full = generate(kind, B * ld, seed=N % 1000 + k).reshape(B, ld)
+    vals, idx, st = stf.topk_batched(dev(full)[:, :N], k, stats=True)
+    print("[case] stats", {kk: st[kk] for kk in ("S", "t", "M", "attempts", "rows_retried", "rows_fallback")},
+          flush=True)
+    check_batched(np.ascontiguousarray(full[:, :N]), vals, idx, k)
