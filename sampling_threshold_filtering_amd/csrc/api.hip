@@ -328,7 +328,11 @@ SampleArgs sample_args(Workspace* w, const Layout& L, const float* x, u64 N, u64
   a.ticket = reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kTicketSample);
   a.top_hist = at<SelState>(w, L.sel)->hist;
   a.t = t;
-  a.fast = (t >= 1 && t <= kTopT && sample_blocks(S, t) <= kTopBlocks) ? 1u : 0u;
+  const SampleShape sh = sample_shape(S, t, N, true);
+  a.mode = sh.mode;
+  a.threads = sh.threads;
+  a.sel = at<SelState>(w, L.sel);
+  a.col = at<u64>(w, L.col);
   return a;
 }
 
@@ -877,11 +881,9 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     return PROFK_EUNSUPPORTED;
   const u64 S = (u64)p.S, M = (u64)p.M, t = (u64)p.t;
   const u64 G = batched_sample_blocks(B);
-  // the grid sampler's per-row block lists: pow2(t) keys per sampling block
-  u64 T = 1;
-  while (T < t) T <<= 1;
-  const bool fast = t >= 1 && t <= kTopT && sample_blocks(S, t) <= kTopBlocks;
-  const u64 tops_per_row = fast ? (u64)sample_blocks(S, t) * T : 1;
+  // the grid sampler's per-row block lists (each row's tau in its own last block)
+  const SampleShape sh = sample_shape(S, t, N, false);
+  const u64 tops_per_row = sh.tops_words;
   Layout L;
   Workspace* w = nullptr;
   rc = grid ? get_workspace(s, Need{B, S, M, 1, 0, B, tops_per_row}, &w, &L)
@@ -947,7 +949,8 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
         sa.ticket = at<u64>(w, L.rtick) + l0;
         sa.top_hist = sel->hist;
         sa.t = t;
-        sa.fast = fast ? 1u : 0u;
+        sa.mode = sh.mode;
+        sa.threads = sh.threads;
         sa.rows = rows ? rows + l0 : nullptr;
         sa.nrows = (u32)(nrows - l0 < 65535 ? nrows - l0 : 65535);
         sa.row0 = (u32)l0;
@@ -1206,10 +1209,8 @@ int profk_stage_batched_sample(const float* x, int64_t B, int64_t N, int64_t ld_
   Layout L;
   Workspace* w = nullptr;
   const u64 nb = (u64)B, uS = (u64)S, ut = (u64)t;
-  u64 T = 1;
-  while (T < ut) T <<= 1;
-  const bool fast = ut <= kTopT && sample_blocks(uS, ut) <= kTopBlocks;
-  const u64 tops_per_row = fast ? (u64)sample_blocks(uS, ut) * T : 1;
+  const SampleShape sh = sample_shape(uS, ut, (u64)N, false);
+  const u64 tops_per_row = sh.tops_words;
   int rc = grid ? get_workspace(s, Need{nb, uS, 1, 1, 0, nb, tops_per_row}, &w, &L)
                 : get_workspace(s, Need{nb, 0, 1, 1, nb * 2 * uS}, &w, &L);
   if (rc) return rc;
@@ -1241,7 +1242,8 @@ int profk_stage_batched_sample(const float* x, int64_t B, int64_t N, int64_t ld_
     sa.ticket = at<u64>(w, L.rtick);
     sa.top_hist = sel->hist;
     sa.t = ut;
-    sa.fast = fast ? 1u : 0u;
+    sa.mode = sh.mode;
+    sa.threads = sh.threads;
     sa.rows = nullptr;
     sa.nrows = (u32)nb;
     sa.row0 = 0;

@@ -3,8 +3,10 @@
 //
 // Used where the whole selection is small enough for one compute unit: the
 // threshold tau of Prof-K ("Prof-K: Probabilistic One-Pass Filtering for Efficient
-// Top-k Selection", §3 stage 2: the t-th largest of the S sampled values, S at most
-// 131072) and the per-row stages of the batched form.  Each pass reads the keys
+// Top-k Selection", §3 stage 2: the t-th largest of the S sampled values) from block
+// lists or key slots staged in LDS (lds_select_desc), a block's own t-th largest
+// (reg_select_desc), the per-row stages of the batched form, and, from L2, the
+// threshold of batched rows whose sample exceeds LDS with t > 1024.  Each pass reads the keys
 // that still match the fixed prefix from L2 (eight loads in flight per thread),
 // histograms the next 8-bit digit in LDS (one LDS atomic per distinct digit per
 // wavefront) and fixes it; once at most `cap` keys match they are gathered into

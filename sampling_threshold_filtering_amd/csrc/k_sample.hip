@@ -7,27 +7,40 @@
 // (see profk_device.h for the draw).  That rule is symmetric under relabelling of
 // [N], so every S-subset is equally likely, and it is deterministic per seed.
 //
-//   sample_kernel   one thread per draw 0..S-1, in workgroups of 256 threads when
-//                   the per-block lists below apply and S <= 32768 (the random
-//                   gathers then spread over 4x as many CUs, which halves their
-//                   latency on MI355X), else 1024.  Each index goes into a hash set of
+//   sample_kernel   one thread per draw 0..S-1, in workgroups of 256, 512 or 1024
+//                   threads (sample_shape).  Each index goes into a hash set of
 //                   32-bit slots in device memory (idx + 1, 0 = empty, one CAS per
 //                   probe; the set is zero on entry and cleared again after the
 //                   attempt), while the gather of x[idx] is already in flight.  Draw
 //                   j keeps its key in keys[j], or 0 when it repeats an earlier draw
-//                   (no valid key is 0).  For t <= kTopT each block also sorts its
-//                   wavefronts' keys in registers and stores its own t largest keys.
-//                   Each block adds itself and its distinct draws to one 64-bit ticket.
-//                   The last block (a) tops up: while fewer than S distinct indices
-//                   are held, wavefront 0 takes further draws S, S+1, ... in order,
-//                   64 at a time, keeping those that are new and not repeated earlier
-//                   in the same chunk (expected extra draws about S^2 / (2N)), into
-//                   keys[S..]; and (b) selects tau.  With the per-block lists, only
-//                   the first t keys of each list (and the top-up keys) can be among
-//                   the t largest: those are loaded into LDS and a radix select
-//                   there finds the t-th.  Otherwise, while all key slots fit in
-//                   LDS, the same select runs over them, and beyond that a
-//                   one-workgroup radix select reads them from L2 pass by pass.
+//                   (no valid key is 0).  Each block adds itself and its distinct
+//                   draws to one 64-bit ticket.  The last block tops up: while fewer
+//                   than S distinct indices are held, wavefront 0 takes further draws
+//                   S, S+1, ... in order, 64 at a time, keeping those that are new and
+//                   not repeated earlier in the same chunk (expected extra draws about
+//                   S^2 / (2N)), into keys[S..].
+//
+// tau (stage 2) is found in one of four ways (sample_shape picks the first that fits):
+//   sorted lists    t <= 64: each block sorts its wavefronts' keys in registers and
+//                   merges them into its pow2(t) largest, sorted;
+//   top-t lists     t <= 1024: each block finds its own t-th largest key by a radix
+//                   select on the keys in registers and keeps the t keys at or above
+//                   it, in no order.
+//                   In both, only a block's t largest draws can be among the t largest
+//                   of all: the last block stages the lists in LDS (its other
+//                   wavefronts load them while wavefront 0 tops up), appends the top-up
+//                   keys, and a radix select in LDS finds the t-th.  The lists are sized
+//                   so that they and a bound on the top-up fit in LDS.
+//   key slots       every draw slot fits in LDS: the same select over all of them;
+//   select passes   (one row) beyond that: the last block arms the multi-block radix
+//                   select of k_select.hip over the key slots, whose passes follow this
+//                   launch on the stream and leave tau in the row's control block.
+// Rows of the batched form whose slots exceed LDS with t > 1024 keep one workgroup per
+// row reading the slots from L2 (the rows run side by side); so does a list launch
+// whose top-up ever exceeds its bound.
+
+#include <cmath>
+
 #include "block_select.h"
 #include "launch.h"
 
@@ -124,12 +137,15 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a0) {
   __shared__ BlockSelectLds s_sel;
   __shared__ LdsSelect s_lsel;
   __shared__ u32 s_wcnt[kSampleWaves];
+  __shared__ u32 s_wkeep[kSampleWaves];
   __shared__ u32 s_n;
   __shared__ u32 s_last;
   __shared__ u64 s_D, s_E;
   const u32 lane = lane_id(), wid = threadIdx.x / kWave;
   const bool select = a.t > 0;
-  const bool use_hist = select && !a.fast;
+  const u32 mode = select ? a.mode : kTauKeys;
+  // the top-digit histogram starts the one-workgroup select over L2 (key slots beyond LDS)
+  const bool use_hist = mode == kTauKeys && select && a.S > kTauCap;
   for (u32 b = threadIdx.x; b < 256; b += blockDim.x) s_sel.hist[b] = 0;
   if (threadIdx.x == 0) s_n = 0;
 
@@ -149,9 +165,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a0) {
   // fast path: lists of T = pow2(t) keys, each sorted descending
   u32 T = 1;
   while (T < a.t) T <<= 1;
-  if (a.fast) {
-    key = wave_sort_desc(key);
-    if (lane < T) s_buf[wid * T + lane] = key;  // this wavefront's T largest (0-padded)
+  if (mode == kTauSortedLists) {
+    const u64 sk = wave_sort_desc(key);
+    if (lane < T) s_buf[wid * T + lane] = sk;  // this wavefront's T largest (0-padded)
   }
   __syncthreads();
   if (use_hist) {
@@ -160,9 +176,28 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a0) {
     __syncthreads();
     for (u32 b = threadIdx.x; b < 256; b += blockDim.x)
       if (s_sel.hist[b]) atomicAdd(&a.top_hist[b], s_sel.hist[b]);
-  } else if (a.fast) {
+  } else if (mode == kTauSortedLists) {
     block_merge_lists(s_buf, kSampleWaves, T);  // the block's T largest keys
     for (u32 i = threadIdx.x; i < T; i += blockDim.x) st_agent(a.tops + (u64)blockIdx.x * T + i, s_buf[i]);
+  } else if (mode == kTauTopLists) {
+    // the block's t largest keys, in no order: the t-th largest by a radix select on
+    // the keys in registers (0 when the block holds fewer than t), then every key at
+    // or above it (exactly t of them, the keys being distinct), zero-padded to t
+    const u64 v1[1] = {key};
+    const u64 kb = reg_select_desc(v1, (u32)a.t, &s_lsel);
+    const bool keep = key != 0 && key >= kb;
+    const u64 km = __ballot(keep);
+    if (lane == 0) s_wkeep[wid] = (u32)__popcll(km);
+    __syncthreads();
+    u32 off = 0, tot = 0;
+    for (u32 w = 0; w < kSampleWaves; ++w) {
+      off += w < wid ? s_wkeep[w] : 0u;
+      tot += s_wkeep[w];
+    }
+    u64* dst = a.tops + (u64)blockIdx.x * a.t;
+    const u32 slot = off + count_below(km);
+    if (keep && slot < a.t) st_agent(dst + slot, key);
+    for (u32 i = tot + threadIdx.x; i < a.t; i += blockDim.x) st_agent(dst + i, 0ull);
   }
   // this block's keys and lists complete (written through at agent scope), then elect
   // the last block: one atomic adds the block to the ticket and its distinct draws to
@@ -180,7 +215,15 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a0) {
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  // top-up by wavefront 0
+  // What the select reads, known before the top-up: the block lists (only a block's t
+  // largest draws can be among the t largest of all: the first t of each sorted list,
+  // stride T, or each unordered top-t list, stride t), or every draw slot when they
+  // fit.  The other wavefronts stage it in LDS while wavefront 0 tops the sample up
+  // and appends the top-up keys behind it.
+  const bool lists = mode == kTauSortedLists || mode == kTauTopLists;
+  const u32 tt = (u32)a.t;
+  const u64 nbase = lists ? (u64)gridDim.x * tt : (mode == kTauKeys && select && a.S <= kTauCap ? a.S : 0ull);
+  const bool staged = select && nbase > 0 && nbase <= kTauCap;
   if (wid == 0) {
     const u64 D = s_D;
     u64 E = 0, j0 = a.S;
@@ -202,6 +245,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a0) {
         hash_insert(a.table, a.tmask, idx2);
         const u64 key2 = make_key(__float_as_uint(a.x[idx2]), idx2);
         a.keys[a.S + E + r] = key2;
+        if (staged && nbase + E + r < kTauCap) s_buf[nbase + E + r] = key2;
         if (use_hist) atomicAdd(&a.top_hist[key2 >> 56], 1u);
       }
       const u64 got = (u64)__popcll(m2);
@@ -213,6 +257,28 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a0) {
       }
     }
     if (lane == 0) s_E = failed ? ~0ull : E;
+  } else if (staged) {
+    const u64 ls = mode == kTauSortedLists ? (u64)T : (u64)tt;
+    const u32 nl = (u32)nbase, lt = threadIdx.x - kWave, nt = kSampleThreads - kWave;
+    constexpr u32 kILP = 8;
+    for (u32 base = 0; base < nl; base += nt * kILP) {
+      u64 kk[kILP];
+#pragma unroll
+      for (u32 q = 0; q < kILP; ++q) {
+        const u32 i = base + q * nt + lt;
+        u64 src = i;
+        if (lists) {
+          const u32 b = i / tt;
+          src = (u64)b * ls + (i - b * tt);
+        }
+        kk[q] = i < nl ? (lists ? a.tops[src] : a.keys[src]) : 0ull;
+      }
+#pragma unroll
+      for (u32 q = 0; q < kILP; ++q) {
+        const u32 i = base + q * nt + lt;
+        if (i < nl) s_buf[i] = kk[q];
+      }
+    }
   }
   __syncthreads();
   const u64 E = s_E;
@@ -221,51 +287,29 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a0) {
   bool ok = sample_ok;
   u64 tau = 0;
   if (select) {
-    if (a.fast && sample_ok && (u64)gridDim.x * a.t + E <= kTauCap) {
-      // each block's list holds its T largest draws in descending order, so only its
-      // first t can be among the t largest; with the top-up keys they go into LDS
-      const u32 G = gridDim.x, tt = (u32)a.t, nl = G * tt;
-      constexpr u32 kILP = 8;
-      for (u32 base = 0; base < nl; base += blockDim.x * kILP) {
-        u64 kk[kILP];
-#pragma unroll
-        for (u32 q = 0; q < kILP; ++q) {
-          const u32 i = base + q * blockDim.x + threadIdx.x;
-          const u32 b = i / tt;
-          kk[q] = i < nl ? a.tops[(u64)b * T + (i - b * tt)] : 0ull;
-        }
-#pragma unroll
-        for (u32 q = 0; q < kILP; ++q) {
-          const u32 i = base + q * blockDim.x + threadIdx.x;
-          if (i < nl) s_buf[i] = kk[q];
-        }
-      }
-      for (u64 i = threadIdx.x; i < E; i += blockDim.x) s_buf[nl + i] = a.keys[a.S + i];
-      __syncthreads();
-      tau = lds_select_desc(s_buf, nl + (u32)E, tt, &s_lsel);
+    if (staged && sample_ok && nbase + E <= kTauCap) {
+      tau = lds_select_desc(s_buf, (u32)(nbase + E), tt, &s_lsel);
       ok = tau != 0;
-    } else if (sample_ok && nslots <= kTauCap) {
-      // every key slot fits in LDS: select there
-      constexpr u32 kILP = 8;
-      for (u64 base = 0; base < nslots; base += (u64)blockDim.x * kILP) {
-        u64 kk[kILP];
-#pragma unroll
-        for (u32 q = 0; q < kILP; ++q) {
-          const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
-          kk[q] = i < nslots ? a.keys[i] : 0ull;
-        }
-#pragma unroll
-        for (u32 q = 0; q < kILP; ++q) {
-          const u64 i = base + (u64)q * blockDim.x + threadIdx.x;
-          if (i < nslots) s_buf[i] = kk[q];
-        }
+    } else if (mode == kTauPasses) {
+      // the select passes that follow this launch find tau over the nslots key slots
+      // (zero for the repeated draws: below every key, so the rank t <= S still lands
+      // on a drawn key); a failed sample leaves them nothing to do
+      if (threadIdx.x == 0) {
+        SelState* q = a.sel;
+        q->prefix = 0;
+        q->mask = 0;
+        q->rank = a.t;
+        q->count = nslots;
+        q->done = sample_ok ? 0u : 1u;
+        q->digit = 0;
+        q->ticket = 0;
+        q->ncol = 0;
+        q->error = 0;
       }
-      if (use_hist)
-        for (u32 b = threadIdx.x; b < 256; b += blockDim.x) a.top_hist[b] = 0;  // left zero for the next launch
-      __syncthreads();
-      tau = lds_select_desc(s_buf, (u32)nslots, (u32)a.t, &s_lsel);
-      ok = tau != 0;
     } else {
+      // one workgroup over the key slots in L2 (a top-up beyond the room in LDS, or
+      // rows of the batched form with t > 1024): starting from the top-digit
+      // histogram the sampling blocks built, if they built one
       if (use_hist) {
         for (u32 b = threadIdx.x; b < 256; b += blockDim.x) {
           s_sel.hist[b] = atomicAdd(&a.top_hist[b], 0u);
@@ -376,24 +420,70 @@ hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u
   return hipGetLastError();
 }
 
-u32 sample_threads(u64 S, u64 t) {
-  const bool lists = t == 0 || t <= kTopT;
-  return lists && (S + 255) / 256 <= kTopBlocks ? 256u : 1024u;
-}
+namespace {
+// Blocks of the sorted-list path: 256 threads while at most kTopBlocks of them cover S.
+u32 list_threads(u64 S) { return (S + 255) / 256 <= kTopBlocks ? 256u : 1024u; }
 
-u32 sample_blocks(u64 S, u64 t) {
-  const u32 th = sample_threads(S, t);
-  return (u32)((S + th - 1) / th);
+// A bound on the top-up draws E (the repeats among the first S draws): their mean is
+// at most S^2 / (2N) (the first term of an alternating series), their spread about
+// its square root; six of those past it are not reached in practice.  A launch whose
+// top-up does exceed the room left in LDS still ends correctly (the select over the
+// key slots).
+u64 topup_bound(u64 S, u64 N) {
+  const double mu = (double)S * (double)S / (2.0 * (double)(N ? N : 1));
+  return (u64)(mu + 6.0 * std::sqrt(mu) + 64.0);
+}
+}  // namespace
+
+SampleShape sample_shape(u64 S, u64 t, u64 N, bool passes) {
+  SampleShape sh{kTauKeys, 1024u, 0u, 1ull};
+  const u64 E = topup_bound(S, N);
+  const u32 tl = list_threads(S);
+  const u64 gl = (S + tl - 1) / tl;
+  if (t == 0) {
+    sh.threads = tl;
+  } else if (t <= kTopT && gl <= kTopBlocks && gl * t + E <= kTauCap) {
+    u64 T = 1;
+    while (T < t) T <<= 1;
+    sh.mode = kTauSortedLists;
+    sh.threads = tl;
+    sh.tops_words = gl * T;
+  } else {
+    // unordered top-t lists: the smallest workgroups (the most CUs gathering) whose
+    // lists still fit in LDS beside the top-up
+    for (u32 th = 256; th <= 1024; th <<= 1) {
+      const u64 g = (S + th - 1) / th;
+      if (t <= 1024 && g * t + E <= kTauCap) {
+        sh.mode = kTauTopLists;
+        sh.threads = th;
+        sh.tops_words = g * t;
+        break;
+      }
+    }
+    // else the key slots (S plus the top-up): in LDS when they fit, else several
+    // workgroups read them, pass by pass (one row), or one workgroup per row over L2
+    if (sh.mode == kTauKeys && S + E > kTauCap && passes) sh.mode = kTauPasses;
+  }
+  sh.blocks = (u32)((S + sh.threads - 1) / sh.threads);
+  return sh;
 }
 
 hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
-  const u32 th = sample_threads(a.S, a.t), blocks = sample_blocks(a.S, a.t);
-  const dim3 grid(blocks, a.nrows ? a.nrows : 1u);
+  const u32 th = a.threads;
+  const dim3 grid((u32)((a.S + th - 1) / th), a.nrows ? a.nrows : 1u);
+  if (a.mode == kTauPasses && (a.nrows || !a.sel || !a.col)) return hipErrorInvalidValue;
   if (th == 256)
     sample_kernel<256><<<grid, 256, 0, s>>>(a);
-  else
+  else if (th == 512)
+    sample_kernel<512><<<grid, 512, 0, s>>>(a);
+  else if (th == 1024)
     sample_kernel<1024><<<grid, 1024, 0, s>>>(a);
-  return hipGetLastError();
+  else
+    return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.mode != kTauPasses || a.t == 0) return e;
+  // tau into ctl->tau by the multi-block passes (a failed check into ctl->status)
+  return launch_select_keys(a.keys, &a.ctl->D, 2 * a.S, a.sel, a.col, &a.ctl->tau, &a.ctl->status, s);
 }
 
 hipError_t launch_clear_sample(u32* table, u64 slots, u32* tickets, hipStream_t s) {

@@ -68,8 +68,13 @@ constexpr u32 kTicketSample = 8;  // sampling kernel: one u64 at slots 8-9 (8-by
                                   // (blocks done << 32) | distinct draws so far
 constexpr u32 kCountStage = 4;    // output counter of the stage entry points
 constexpr u32 kTicketRefine = 16; // one-launch refinement for small k
-constexpr u32 kTopT = 64;         // largest t of the per-block-list threshold path
+constexpr u32 kTopT = 64;         // largest t of the sorted per-block lists
 constexpr u32 kTopBlocks = 128;   // most sampling blocks of that path (S <= 131072)
+// How a sampling launch finds tau, the t-th largest of its S draws (sample_mode):
+constexpr u32 kTauKeys = 0;         // from the key slots: in LDS when they fit, else one workgroup over L2
+constexpr u32 kTauSortedLists = 1;  // per-block sorted lists of pow2(t) keys (t <= kTopT), merged in LDS
+constexpr u32 kTauTopLists = 2;     // per-block unordered top t (t <= 1024), selected from in LDS
+constexpr u32 kTauPasses = 3;       // multi-block radix select passes over the key slots (one row)
 
 struct SampleArgs {
   const float* x;
@@ -79,13 +84,16 @@ struct SampleArgs {
   u32* table;       // hash set, tmask + 1 slots, zero on entry
   u64 tmask;
   u64* keys;        // 2S slots: draw j < S at keys[j] (0 = repeat), top-up from keys[S]
-  u64* tops;        // per block its t largest keys (fast path), kTopBlocks * kTopT
+  u64* tops;        // per-block lists (kTauSortedLists, kTauTopLists): tops_words of sample_shape
   RowCtl* ctl;      // tau out; the per-attempt fields are reset
   AttemptRecord* rec;  // reset, or nullptr
   u64* ticket;      // (blocks done << 32) | distinct draws; zero on entry, left zero
   u32* top_hist;    // 256 words, zero on entry, left zero
   u64 t;            // threshold rank (0: sample only)
-  u32 fast;         // 1: per-block lists (t <= kTopT, at most kTopBlocks blocks)
+  u32 mode;         // how tau is found: one of kTau* (sample_shape)
+  u32 threads;      // workgroup size (sample_shape)
+  SelState* sel;    // kTauPasses: armed by the last block for the select passes (one row)
+  u64* col;         // kTauPasses: kCollectCap keys of collect space for the passes
   // Several rows at once (the batched form): the grid has one row of blocks per row
   // in the list (blockIdx.y is the position in it).  The pointers above are for row 0
   // (x, ctl, rec, top_hist, indexed by row id) or list position 0 (table, keys, tops,
@@ -104,8 +112,14 @@ struct SampleArgs {
 
 // Sampling launch shape for (S, t): 256-thread workgroups while the per-block-list
 // threshold path applies and needs at most kTopBlocks of them, else 1024 threads.
-u32 sample_threads(u64 S, u64 t);
-u32 sample_blocks(u64 S, u64 t);
+// The launch for S draws of N and rank t: how tau is found (kTau*; kTauPasses only
+// where `passes`: one row with a SelState), the workgroup size and count, and the u64
+// words of per-block lists one row needs (at least 1).
+struct SampleShape {
+  u32 mode, threads, blocks;
+  u64 tops_words;
+};
+SampleShape sample_shape(u64 S, u64 t, u64 N, bool passes);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
 hipError_t launch_clear_sample(u32* table, u64 slots, u32* tickets, hipStream_t s);
 hipError_t launch_keys_to_index_compact(const u64* keys, const u64* n_ptr, u64 n_cap, int64_t* out, u32* counter,

@@ -69,10 +69,12 @@ def test_batched_sample_and_threshold_match_oracle(kind, B, N, S, t, seed, attem
 
 GRID_CASES = [
     # rows longer than 2^20: the grid sampler (one draw per thread, a hash set per row)
-    ("normal", 8, (1 << 21) + 5, 32768, 13, 9, 0, 0),   # block lists (t <= 64), ragged rows
-    ("pareto", 4, 1 << 22, 4096, 100, 10, 1, 0),        # t > 64, every key slot in LDS
-    ("uniform", 4, 1 << 21, 16384, 70, 11, 0, 7),       # t > 64, slots beyond LDS: select over L2
+    ("normal", 8, (1 << 21) + 5, 32768, 13, 9, 0, 0),   # sorted block lists (t <= 64), ragged rows
+    ("pareto", 4, 1 << 22, 4096, 100, 10, 1, 0),        # unordered top-t block lists (t > 64)
+    ("uniform", 4, 1 << 21, 16384, 70, 11, 0, 7),       # the same over 16 blocks, strided rows
+    ("uniform", 3, (1 << 21) + 3, 9221, 200, 14, 0, 0),  # a last block with fewer than t draws
     ("adv_noise", 4, 1 << 21, 8192, 30, 12, 2, 0),      # 256 distinct values
+    ("normal", 2, 1 << 21, 32768, 2000, 13, 0, 0),      # t > 1024: one workgroup per row over L2
 ]
 
 

@@ -50,9 +50,8 @@ def test_sample_matches_oracle(N, S, seed, attempt):
                                              ("adv_noise", 1 << 20, 32768, 7, 2),
                                              ("signed_zeros", 50000, 10000, 3000, 4),
                                              ("uniform", 1 << 22, 131072, 1, 9),
-                                             # per-block-list path (t <= 64): boundary t, ragged last block,
-                                             # heavy top-up (S = N/2), special values, ties
-                                             ("pareto", 1 << 24, 131072, 64, 11),
+                                             # sorted per-block lists (t <= 64): boundary t, ragged last
+                                             # block, heavy top-up (S = N/2), special values, ties
                                              ("normal", 100003, 3001, 50, 12),
                                              ("uniform", 5000, 2500, 10, 13),
                                              ("with_inf", 1 << 20, 32768, 20, 14),
@@ -60,17 +59,26 @@ def test_sample_matches_oracle(N, S, seed, attempt):
                                              ("all_equal", 100000, 20000, 64, 16),
                                              ("negative", 1 << 20, 32768, 33, 17),
                                              ("ascending", 1 << 20, 8192, 64, 18),
-                                             # lists overflow the LDS buffer (128 x 64 + top-up): radix select
-                                             ("uniform", 1 << 22, 131072, 64, 19),
-                                             # t just above the list path
-                                             ("normal", 1 << 20, 32768, 65, 20),
                                              # 256-thread sampling workgroups up to S = 32768, then 1024
                                              ("pareto", 1 << 24, 16357, 1, 21), ("pareto", 1 << 24, 16357, 20, 22),
                                              ("normal", 1 << 20, 32769, 40, 23),
-                                             # t above the list path with every key slot in LDS (with and
-                                             # without a large top-up), and just beyond it
-                                             ("normal", 1 << 20, 8192, 100, 24), ("uniform", 12000, 6000, 300, 25),
-                                             ("uniform", 20000, 8000, 200, 26)])
+                                             # unordered per-block top-t lists (t <= 1024) in workgroups of
+                                             # 256 / 512 / 1024: t just above the sorted lists, the SAE
+                                             # pool's and the adversarial workload's (S, t) under the
+                                             # default rule, t = 1024, a last block with fewer than t
+                                             # draws, large top-ups
+                                             ("normal", 1 << 20, 32768, 65, 20), ("normal", 1 << 20, 8192, 100, 24),
+                                             ("normal", 1 << 20, 16384, 65, 35), ("normal", 1 << 26, 32768, 118, 34),
+                                             ("adv_levels", 1 << 24, 82557, 68, 28), ("normal", 1 << 20, 7000, 1024, 29),
+                                             ("uniform", 1 << 20, 9221, 200, 30), ("uniform", 12000, 6000, 300, 25),
+                                             ("uniform", 20000, 8000, 200, 26),
+                                             # every key slot in LDS (t > 1024, S + top-up <= 8192)
+                                             ("uniform", 12000, 5000, 2000, 27),
+                                             # multi-block select passes over the key slots: lists beyond
+                                             # the LDS (128 x 64 + top-up), t > 1024, ties, top-up ~ S / 4
+                                             ("pareto", 1 << 24, 131072, 64, 11), ("uniform", 1 << 22, 131072, 64, 19),
+                                             ("normal", 1 << 22, 131072, 5000, 31), ("all_equal", 1 << 20, 65536, 3000, 32),
+                                             ("uniform", 40000, 20000, 2000, 33)])
 def test_threshold_matches_oracle(kind, N, S, t, seed):
     say("threshold", kind, N, S, t, seed)
     edge = ("few_levels", "signed_zeros", "with_inf", "with_nan", "all_equal", "negative", "ascending")
