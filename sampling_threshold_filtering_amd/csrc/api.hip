@@ -803,12 +803,7 @@ int topk_approx_static(const float* x, u64 N, u64 k, double eps, u64 seed, float
 // with an LDS bitmap of the row (rows of at most kBatchedMaxN values), or the grid of
 // one-draw-per-thread blocks per row with a hash set per row in device memory (any
 // row length).
-bool batched_grid_sampler(u64 N) {
-  static const char* force = std::getenv("PROFK_BATCHED_SAMPLER");
-  if (force && force[0] == 'g') return true;
-  if (force && force[0] == 'b') return N > kBatchedMaxN;
-  return N > kBatchedMaxN;
-}
+bool batched_grid_sampler(u64 N) { return N > kBatchedMaxN; }
 
 // Batched form with per-row kernels (k at most kBatchedMaxM: the refinement holds a
 // row's buffer in LDS up to kBatchedMaxM keys, and beyond that selects over it in
