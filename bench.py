@@ -63,7 +63,7 @@ EPS = 1e-3
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=30)
     # untimed calls per k before the timed ones: the filter's per-die shares settle over
     # about ten calls after the library starts (measured: 620-625 us per filter pass in
     # calls 2-5 at 2^30 values, ~600 us from call 10 on)
@@ -76,8 +76,8 @@ def parse():
     ap.add_argument("--inputs", type=int, default=3,
                     help="input tensors of the headline workload (Pareto seeds 0, 1, ...); calls rotate over them")
     ap.add_argument("--only", default="",
-                    help="comma list of parts to run (flat, ceiling, configs, c1, c2, c3, c5, batched, large, cpu); "
-                         "default all.  c1/c2/c3/c5 select single entries of configs, e.g. for a profile")
+                    help="comma list of parts to run (flat, ceiling, configs, c1, c2, c3, c5, t7, batched, large, cpu); "
+                         "default all.  c1/c2/c3/c5/t7 select single entries of configs, e.g. for a profile")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-batched", action="store_true", help="skip the batched variant")
     ap.add_argument("--no-large", action="store_true", help="skip the N = 4.3e9 (beyond 2^32) measurement")
@@ -402,6 +402,21 @@ def bench_large(stf, torch, dev, stream, args, opts):
     return res
 
 
+INPUT_DIGESTS = {}  # name -> digest of every host-generated input tensor (see digest())
+
+
+def digest(name: str, x: np.ndarray) -> None:
+    """Record a SHA-256 of the tensor's bytes, taken as the SHA-256 of the concatenated
+    SHA-256 digests of its 2^24-value chunks (so that the chunks hash on several threads)."""
+    from concurrent.futures import ThreadPoolExecutor
+    b = np.ascontiguousarray(x).reshape(-1).view(np.uint8)
+    step = 4 << 24
+    parts = [b[i:i + step] for i in range(0, b.size, step)]
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        ds = list(ex.map(lambda c: hashlib.sha256(memoryview(c)).digest(), parts))
+    INPUT_DIGESTS[name] = hashlib.sha256(b"".join(ds)).hexdigest()[:16]
+
+
 def progress(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -481,7 +496,9 @@ def bench_configs(stf, torch, dev, stream, args, opts, want, keep):
     warm = max(args.warmup, 5)
     if "c1" in want:
         N, k = 1 << 22, 32
-        bufs = rotation(torch, torch.from_numpy(generate("uniform", N, seed=0)).to(dev))
+        xh = generate("uniform", N, seed=0)
+        digest("uniform_2p22", xh)
+        bufs = rotation(torch, torch.from_numpy(xh).to(dev))
         ms = time_calls(stf, torch, bufs, k, EPS, opts, calls, warm, stream, out_pair(torch, dev, k))
         res["uniform_2p22"] = {"32": entry(N, k, EPS, ms, stf.solve(N, k, EPS, options=opts), len(bufs))}
         progress("uniform 2^22", round(ms, 4), "ms")
@@ -489,7 +506,9 @@ def bench_configs(stf, torch, dev, stream, args, opts, want, keep):
     if "c2" in want:
         N = 1 << 26
         for kind in ("normal", "uniform"):
-            bufs = rotation(torch, torch.from_numpy(generate(kind, N, seed=0)).to(dev))
+            xh = generate(kind, N, seed=0)
+            digest(f"{kind}_2p26", xh)
+            bufs = rotation(torch, torch.from_numpy(xh).to(dev))
             r = {}
             for k in (32, 1024, 32768):
                 ms = time_calls(stf, torch, bufs, k, EPS, opts, calls, warm, stream, out_pair(torch, dev, k))
@@ -502,7 +521,9 @@ def bench_configs(stf, torch, dev, stream, args, opts, want, keep):
         res["normal_vs_uniform_2p26_ms_ratio"] = [round(x / y, 3) for x, y in zip(a, b)]
     if "c3" in want:
         N, k = 50331648, 131072
-        bufs = rotation(torch, torch.from_numpy(sae_pool(0).reshape(-1)).to(dev))
+        xh = sae_pool(0).reshape(-1)
+        digest("sae_pool_4096x12288", xh)
+        bufs = rotation(torch, torch.from_numpy(xh).to(dev))
         ms = time_calls(stf, torch, bufs, k, EPS, opts, calls, warm, stream, out_pair(torch, dev, k))
         res["sae_pool_4096x12288"] = {"131072": entry(N, k, EPS, ms, stf.solve(N, k, EPS, options=opts), len(bufs))}
         progress("sae pool", round(ms, 4), "ms")
@@ -510,7 +531,10 @@ def bench_configs(stf, torch, dev, stream, args, opts, want, keep):
     if "c5" in want:
         N, k, eps = 1 << 30, 1 << 19, 1e-4
         for kind in ("adv_levels", "adv_noise"):
-            xd = torch.from_numpy(generate(kind, N, seed=0)).to(dev)
+            xh = generate(kind, N, seed=0)
+            digest(f"{kind}_2p30", xh)
+            xd = torch.from_numpy(xh).to(dev)
+            del xh
             out = out_pair(torch, dev, k)
             ms = time_calls(stf, torch, [xd], k, eps, opts, args.steps, args.warmup, stream, out)
             e = entry(N, k, eps, ms, stf.solve(N, k, eps, options=opts), 1)
@@ -527,6 +551,34 @@ def bench_configs(stf, torch, dev, stream, args, opts, want, keep):
                 e["exact_full_selection_ms"] = round(xms, 4)
             res[f"{kind}_2p30"] = {str(k): e}
             progress(kind, "2^30", e)
+    if "t7" in want:
+        # the page's distribution sweep (Table 7): uniform [0,1) for reference, then
+        # uniform [1,2), uniform [128.6, 128.7], log-normal, exponential, Cauchy, at 2^27
+        # (rotated past the MALL) and 2^30 values, k in {2^8, 2^13}, eps = 1e-3
+        t7 = {}
+        for log2n in (27, 30):
+            N = 1 << log2n
+            for kind in ("uniform", "uniform12", "narrow", "lognormal", "exponential", "cauchy"):
+                xh = generate(kind, N, seed=0)
+                digest(f"{kind}_2p{log2n}", xh)
+                xd = torch.from_numpy(xh).to(dev)
+                del xh
+                bufs = rotation(torch, xd)
+                r = {}
+                for k in (1 << 8, 1 << 13):
+                    c, w = (args.steps, args.warmup) if log2n >= 30 else (calls, warm)
+                    ms = time_calls(stf, torch, bufs, k, EPS, opts, c, w, stream, out_pair(torch, dev, k))
+                    r[str(k)] = entry(N, k, EPS, ms, stf.solve(N, k, EPS, options=opts), len(bufs))
+                t7[f"{kind}_2p{log2n}"] = r
+                progress("table 7", kind, f"2^{log2n}", {k: v["ms"] for k, v in r.items()})
+                del bufs, xd
+                torch.cuda.empty_cache()
+            for k in ("256", "8192"):
+                ref = t7[f"uniform_2p{log2n}"][k]["ms"]
+                t7.setdefault(f"ms_over_uniform_2p{log2n}", {})[k] = {
+                    kind: round(t7[f"{kind}_2p{log2n}"][k]["ms"] / ref, 3)
+                    for kind in ("uniform12", "narrow", "lognormal", "exponential", "cauchy")}
+        res["table7_distributions"] = t7
     return res
 
 
@@ -550,12 +602,12 @@ def main():
     import sampling_threshold_filtering_amd as stf
     from workloads import generate
 
-    parts = {"flat", "ceiling", "configs", "c1", "c2", "c3", "c5", "batched", "large", "cpu"}
+    parts = {"flat", "ceiling", "configs", "c1", "c2", "c3", "c5", "t7", "batched", "large", "cpu"}
     want = set(p.strip() for p in args.only.split(",") if p.strip()) or set(parts)
     if not want <= parts:
         sys.exit(f"--only: unknown parts {sorted(want - parts)}")
     if "configs" in want:
-        want |= {"c1", "c2", "c3", "c5"}
+        want |= {"c1", "c2", "c3", "c5", "t7"}
     if args.no_cpu:
         want.discard("cpu")
     if args.no_batched:
@@ -579,6 +631,7 @@ def main():
         t_gen = time.perf_counter()
         for i in range(max(1, args.inputs) if "flat" in want else 1):
             x = generate("pareto", N, seed=i)
+            digest(f"pareto_2p{args.log2n}_seed{i}", x)
             if i == 0:
                 x0 = x
             xds.append(torch.from_numpy(x).to(dev))
@@ -679,7 +732,7 @@ def main():
                                     "S_per_row": stf.solve(1 << 22, k, EPS / 16, options=bopts)["S"]}
         progress("batched long rows", batched_long)
 
-    configs = bench_configs(stf, torch, dev, stream, args, opts, want, keep) if want & {"c1", "c2", "c3", "c5"} else None
+    configs = bench_configs(stf, torch, dev, stream, args, opts, want, keep) if want & {"c1", "c2", "c3", "c5", "t7"} else None
 
     large = bench_large(stf, torch, dev, stream, args, opts) if "large" in want else None
     progress("large done")
@@ -728,6 +781,9 @@ def main():
         "workspace_bytes": workspace,
         "cpu_baseline": cpu,
         "host_gen_s": round(gen_s, 2),
+        "inputs": {"generator": "numpy PCG64, workloads.generate / sae_pool, 2^24-value chunks on child seeds",
+                   "numpy": np.__version__, "digest": "sha256 over the chunks' sha256 digests (2^24 values each)",
+                   "sha256_16": INPUT_DIGESTS},
     }
     print(json.dumps(line), flush=True)
 
