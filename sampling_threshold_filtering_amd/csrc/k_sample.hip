@@ -85,32 +85,36 @@ __device__ bool hash_contains(const u32* table, u64 tmask, u32 idx) {
 }  // namespace
 
 // Clears every per-attempt counter, record and selection state (histograms
-// included) so that nothing depends on what the workspace held before.
+// included) so that nothing depends on what the workspace held before.  Block b
+// takes rows b, b + gridDim.x, ...; block 0 also the tickets and the refinement's
+// histogram.
 __global__ __launch_bounds__(1024) void attempt_init_kernel(RowCtl* ctl, SelState* sel, AttemptRecord* rec,
                                                           u32* tickets, u32 nrows, u32* refine_hist) {
-  if (tickets)
-    for (u32 i = threadIdx.x; i < kTicketWords; i += blockDim.x) tickets[i] = 0;
-  if (refine_hist)
-    for (u32 b = threadIdx.x; b < kBins; b += blockDim.x) refine_hist[b] = 0;
+  if (blockIdx.x == 0) {
+    if (tickets)
+      for (u32 i = threadIdx.x; i < kTicketWords; i += blockDim.x) tickets[i] = 0;
+    if (refine_hist)
+      for (u32 b = threadIdx.x; b < kBins; b += blockDim.x) refine_hist[b] = 0;
+  }
   if (sel)
-    for (u32 r = 0; r < nrows; ++r)
+    for (u32 r = blockIdx.x; r < nrows; r += gridDim.x)
       for (u32 b = threadIdx.x; b < 256; b += blockDim.x) sel[r].hist[b] = 0;
-  for (u32 r = threadIdx.x; r < nrows; r += blockDim.x) {
+  for (u32 r = blockIdx.x * blockDim.x + threadIdx.x; r < nrows; r += gridDim.x * blockDim.x) {
     RowCtl c{};
     c.key_and = ~0ull;
     ctl[r] = c;
     if (rec) rec[r] = AttemptRecord{0ull, 0u, 0u, 0u, 0u};
     if (!sel) continue;
-    SelState* s = &sel[r];
-    s->prefix = 0;
-    s->mask = 0;
-    s->rank = 1;
-    s->count = 0;
-    s->done = 1;
-    s->digit = 0;
-    s->ticket = 0;
-    s->ncol = 0;
-    s->error = 0;
+    SelState* q = &sel[r];
+    q->prefix = 0;
+    q->mask = 0;
+    q->rank = 1;
+    q->count = 0;
+    q->done = 1;
+    q->digit = 0;
+    q->ticket = 0;
+    q->ncol = 0;
+    q->error = 0;
   }
 }
 
@@ -416,7 +420,11 @@ __global__ void r_to_output_kernel(const RowCtl* ctl, int64_t* out_R) {
 // ---------------------------------------------------------------------------
 hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u32* tickets, u32 nrows,
                                u32* refine_hist, hipStream_t s) {
-  attempt_init_kernel<<<1, 1024, 0, s>>>(ctl, sel, rec, tickets, nrows, refine_hist);
+  // the rows' histograms (256 words each) over up to 256 blocks; without them one
+  // thread per row
+  u32 blocks = sel ? (nrows < 256 ? nrows : 256u) : (nrows + 1023) / 1024;
+  if (blocks < 1) blocks = 1;
+  attempt_init_kernel<<<blocks, 1024, 0, s>>>(ctl, sel, rec, tickets, nrows, refine_hist);
   return hipGetLastError();
 }
 

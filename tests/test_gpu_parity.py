@@ -263,6 +263,27 @@ def test_heavy_bins_take_every_sort_path(k):
     check_topk(x, vals, idx, k)
 
 
+@pytest.mark.parametrize("kind,log2n,k,rule", [("uniform", 22, 1 << 18, 0), ("normal", 24, 1 << 20, 2)])
+def test_large_k_share_thresholds_stay_exact(kind, log2n, k, rule):
+    # k a large share of N: under the default rule t = 2194 (S = 32768), so tau comes from
+    # the multi-block select passes over the key slots; under the MI355X rule t = 338 from
+    # the unordered per-block top-t lists.  Exact and approximate mode.
+    N = 1 << log2n
+    p = stf.solve(N, k, 1e-3, options={"s_rule": rule})
+    say("large k share", kind, N, k, "rule", rule, "S", p["S"], "t", p["t"])
+    assert not p["direct_exact"] and p["t"] > 64
+    x = generate(kind, N, seed=21)
+    xd = dev(x)
+    vals, idx, st = stf.topk(xd, k, seed=3, options={"s_rule": rule}, stats=True)
+    check_topk(x, vals, idx, k)
+    assert not st["fallback"]
+    av, ai, info = stf.topk_approx(xd, k, seed=3, options={"s_rule": rule})
+    rec = stf.approx_info(info)
+    assert rec["status"] in (0, 1, 2)
+    if rec["status"] == 0:  # the check held (probability >= 1 - eps): the exact top-k
+        check_topk(x, av, ai, k)
+
+
 def test_forced_overflow_goes_to_fallback_and_stays_exact():
     say("forced overflow M = k")
     N, k = 1 << 22, 4096
