@@ -3,13 +3,18 @@
 // batched inputs are handled per row; App. C: per-row threshold, buffer and
 // counter; App. E.2: the budget is split eps/B per row).
 //
-//   b_sample_kernel   one workgroup per row (persistent over the listed rows):
-//                     the row's sample without replacement is tracked in an LDS
-//                     bitmap of N bits (N <= 2^20: 128 KB), draws are made four at a
-//                     time per thread, the keys go to a per-workgroup scratch, the
-//                     top-digit histogram is built on the way, wavefront 0 tops the
-//                     sample up, and the workgroup selects tau (LDS reused as the
-//                     sort buffer).  It also clears the row's counter for the filter.
+//   b_sample_kernel   rows of at most 2^20 values, one workgroup per row (persistent
+//                     over the listed rows): the row's sample without replacement is
+//                     tracked in an LDS bitmap of N bits (128 KB) and the keys go to a
+//                     per-workgroup scratch.  With t <= 64 and S <= 8192 every thread
+//                     holds its draws' keys in registers, each wavefront keeps its
+//                     pow2(t) largest and the workgroup merges the sixteen lists;
+//                     otherwise draws are made four at a time per thread, the
+//                     top-digit histogram is built on the way and tau comes from a
+//                     radix select (LDS reused as the sort buffer).  Wavefront 0 tops
+//                     the sample up.  It also clears the row's counter for the filter.
+//                     Longer rows take sample_kernel (k_sample.hip) with a row
+//                     dimension instead: one hash set per row in device memory.
 //   filter_kernel     (k_filter.hip) one streaming pass over all listed rows.
 //   b_refine_kernel   one 256-thread workgroup per row, dynamic LDS sized per path.
 //                     Buffers of up to kBatchedMaxM = 16384 keys are loaded into LDS:
