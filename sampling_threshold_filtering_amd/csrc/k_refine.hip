@@ -646,13 +646,15 @@ __global__ __launch_bounds__(kSortThreads) void refine_binsort_kernel(RefineArgs
   }
 }
 
-// One launch for small k (k <= kSmallK), in place of the three above.  Each of the
-// first G workgroups takes a contiguous share of at most kSmallShare candidates into
-// registers and keeps its k largest (an 8-bit radix select over them, then the keys at
-// or above the k-th) in a list of k slots in tmp, zero-padded; the last of them to
-// finish takes the G lists, selects the k-th largest of their union the same way and
-// sorts the k keys at or above it (one wavefront, in registers).  The k largest
-// candidates are among the lists, since each is among the k largest of its own share.
+// One launch for small k (k <= kSmallK), in place of the three above.  When at most
+// kSmallShare candidates were kept (the usual case), workgroup 0 takes them all into
+// registers, selects the k-th largest (an 8-bit radix select) and sorts the k keys at
+// or above it (one wavefront, in registers).  Otherwise each of the first G workgroups
+// takes a contiguous share of at most kSmallShare candidates and keeps its k largest
+// in a list of k slots in tmp, zero-padded; the last of them to finish takes the G
+// lists, selects the k-th largest of their union the same way and sorts.  The k
+// largest candidates are among the lists, since each is among the k largest of its
+// own share.
 // The workgroups past the first G only clear the sampler's hash set (16-byte stores).
 constexpr u32 kSmallK = 64;
 constexpr u32 kSmallThreads = 256;
@@ -739,6 +741,23 @@ __global__ __launch_bounds__(kSmallThreads) void refine_small_kernel(RefineArgs 
     }
   }
   if (!live) return;
+  if (n <= kSmallShare) {
+    // every candidate fits one workgroup's registers (the usual case: R is mostly well
+    // below M): workgroup 0 selects and sorts alone, with no lists, no hand-off and no
+    // second select; the election counter is left untouched (zero)
+    if (blockIdx.x != 0) return;
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    if (n <= 4 * kSmallThreads) small_keep<false, false, 4>(a.cand, (u32)n, k, s_top, &s_sel, &s_n);
+    else small_keep<false, false, kSmallPer>(a.cand, (u32)n, k, s_top, &s_sel, &s_n);
+    __syncthreads();
+    const u32 nt1 = s_n < k ? s_n : k;
+    if (wid == 0) {
+      const u64 key = wave_sort_desc(lane < nt1 ? s_top[lane] : 0ull);
+      if (lane < nt1) write_out(a, lane, key);
+    }
+    return;
+  }
   // this workgroup's share (at most kSmallShare: the grid is sized to M) and its k largest
   const u64 per = (n + G - 1) / G;
   const u64 lo = (u64)blockIdx.x * per < n ? (u64)blockIdx.x * per : n;
