@@ -6,10 +6,10 @@
 //   b_sample_kernel   rows of at most 2^20 values, one workgroup per row (persistent
 //                     over the listed rows): the row's sample without replacement is
 //                     tracked in an LDS bitmap of N bits (128 KB) and the keys go to a
-//                     per-workgroup scratch.  With t <= 64 and S <= 8192 every thread
-//                     holds its draws' keys in registers, each wavefront keeps its
-//                     pow2(t) largest and the workgroup merges the sixteen lists;
-//                     otherwise draws are made four at a time per thread, the
+//                     per-workgroup scratch.  With S <= 8192 every thread holds its
+//                     draws' keys in registers and one register radix select over
+//                     them and the top-up keys gives tau; otherwise draws are made
+//                     four at a time per thread, the
 //                     top-digit histogram is built on the way and tau comes from a
 //                     radix select (LDS reused as the sort buffer).  Wavefront 0 tops
 //                     the sample up.  It also clears the row's counter for the filter.
@@ -47,20 +47,15 @@ __device__ __forceinline__ void write_row_out(u64 key, u64 j, const float* row, 
 
 constexpr u32 kDrawMax = 8;  // draws per thread held in registers on the fast path
 
-template <int T>
-__device__ __forceinline__ void wave_top_to_list(u64 (&key)[kDrawMax], u64* list, u32 lane) {
-  u64 top[T];
-  wave_top_lanes<kDrawMax, T>(key, top);
-  if (lane == 0) {
-#pragma unroll
-    for (int i = 0; i < T; ++i) list[i] = top[i];
-  }
-}
-
-// One row of the fast path; s_bits / s_D / s_fail are clear on entry.
+// One row of the fast path; s_bits / s_D / s_fail are clear on entry.  Every thread
+// holds its draws' keys in registers; after the top-up (whose keys wavefront 0 also
+// stages in s_list) one radix select over the registers and the staged keys gives the
+// t-th largest, with the select's state in the bitmap's LDS (the row is drawn by then).
+// (Sorting each wavefront's keys in registers and merging the sixteen lists took about
+// 20 us per row, the select a few.)
 __device__ __forceinline__ void b_sample_fast_row(const BatchedArgs& a, u32 row, const float* xr, u64* keys,
                                                   u32* s_bits, u64* s_list, BlockSelectLds* s_sel, u32* s_D,
-                                                  u32* s_fail, u32* s_n, u32 T) {
+                                                  u32* s_fail) {
   const u32 lane = lane_id(), wid = threadIdx.x / kWave;
   u32 idx[kDrawMax];
   bool fr[kDrawMax];
@@ -88,18 +83,6 @@ __device__ __forceinline__ void b_sample_fast_row(const BatchedArgs& a, u32 row,
     nf += (u32)__popcll(__ballot(fr[q]));
   }
   if (lane == 0 && nf) atomicAdd(s_D, nf);
-  if (T <= kDrawMax) {
-    // per-lane sort, then six merge levels across lanes: only the T largest move
-    switch (T) {
-      case 1: wave_top_to_list<1>(key, s_list + wid * T, lane); break;
-      case 2: wave_top_to_list<2>(key, s_list + wid * T, lane); break;
-      case 4: wave_top_to_list<4>(key, s_list + wid * T, lane); break;
-      default: wave_top_to_list<8>(key, s_list + wid * T, lane); break;
-    }
-  } else {
-    wave_sort_regs_desc<kDrawMax>(key);
-    if (lane < T) s_list[wid * T + lane] = key[0];  // elements 0..T-1 of the sorted wavefront
-  }
   __syncthreads();
   const u32 D0 = *s_D;
   // top-up by wavefront 0 into keys[S..]
@@ -121,7 +104,9 @@ __device__ __forceinline__ void b_sample_fast_row(const BatchedArgs& a, u32 row,
       const u32 r = count_below(m2);
       if (ok2 && r < need) {
         atomicOr(&s_bits[id2 >> 5], 1u << (id2 & 31u));
-        keys[a.S + (D - D0) + r] = make_key(__float_as_uint(xr[id2]), id2);
+        const u64 k2 = make_key(__float_as_uint(xr[id2]), id2);
+        keys[a.S + (D - D0) + r] = k2;
+        if ((D - D0) + r < kBThreads) s_list[(D - D0) + r] = k2;
       }
       const u64 got = (u64)__popcll(m2);
       D += got < need ? got : need;
@@ -136,38 +121,20 @@ __device__ __forceinline__ void b_sample_fast_row(const BatchedArgs& a, u32 row,
   __syncthreads();
   const bool sample_ok = !*s_fail && *s_D == a.S;
   const u64 E = sample_ok ? a.S - D0 : 0;
-  block_merge_lists(s_list, kBThreads / kWave, T);  // the row's T largest drawn keys
   u64 tau = 0;
   bool ok = sample_ok;
-  if (sample_ok && E > 0) {
-    // top-up keys at or above the t-th largest draw join its t largest
-    const u64 L = s_list[a.t - 1];
-    if (threadIdx.x == 0) *s_n = (u32)a.t;
-    __syncthreads();
-    for (u64 i = threadIdx.x; i < E; i += blockDim.x) {
-      const u64 kk = keys[a.S + i];
-      if (kk >= L) {
-        const u32 pos = atomicAdd(s_n, 1u);
-        if (pos < kBThreads) s_list[pos] = kk;
-      }
-    }
-    __syncthreads();
-    const u32 nc = *s_n;
-    if (nc <= kBThreads) {
-      u32 P = 1;
-      while (P < nc) P <<= 1;
-      for (u32 i = nc + threadIdx.x; i < P; i += blockDim.x) s_list[i] = 0ull;
-      __syncthreads();
-      block_bitonic_desc(s_list, P);
-      tau = s_list[a.t - 1];
-    } else {
-      // many top-up keys: radix select over all key slots (repeats are empty slots)
-      if (threadIdx.x == 0) block_select_start(s_sel, a.S, a.t);
-      __syncthreads();
-      tau = block_select_finish(keys, a.S + E, reinterpret_cast<u64*>(s_bits), kBitmapWords / 2, s_sel, &ok);
-    }
+  if (sample_ok && E <= kBThreads) {
+    u64 v[kDrawMax + 1];
+#pragma unroll
+    for (u32 q = 0; q < kDrawMax; ++q) v[q] = key[q];
+    v[kDrawMax] = threadIdx.x < E ? s_list[threadIdx.x] : 0ull;  // top-up key threadIdx.x
+    tau = reg_select_desc(v, (u32)a.t, reinterpret_cast<LdsSelect*>(s_bits));
+    ok = tau != 0;
   } else if (sample_ok) {
-    tau = s_list[a.t - 1];
+    // many top-up keys: radix select over all key slots (repeats are empty slots)
+    if (threadIdx.x == 0) block_select_start(s_sel, a.S, a.t);
+    __syncthreads();
+    tau = block_select_finish(keys, a.S + E, reinterpret_cast<u64*>(s_bits), kBitmapWords / 2, s_sel, &ok);
   }
   if (threadIdx.x == 0) {
     RowCtl* c = &a.ctls[row];
@@ -178,21 +145,17 @@ __device__ __forceinline__ void b_sample_fast_row(const BatchedArgs& a, u32 row,
 }
 
 __global__ __launch_bounds__(kBThreads) void b_sample_kernel(BatchedArgs a) {
-  __shared__ u32 s_bits[kBitmapWords];
+  __shared__ __align__(16) u32 s_bits[kBitmapWords];
   __shared__ BlockSelectLds s_sel;
-  __shared__ u64 s_list[kBThreads];  // fast path: 16 wavefront lists of T <= 64 keys
+  __shared__ u64 s_list[kBThreads];  // fast path: the top-up keys
   __shared__ u32 s_D;
   __shared__ u32 s_fail;
-  __shared__ u32 s_n;
   const u32 lane = lane_id(), wid = threadIdx.x / kWave;
   u64* keys = a.scratch + (u64)blockIdx.x * 2 * a.S;  // S draw slots + the top-up
   const u32 nwords = (u32)((a.N + 31) / 32);
-  // Fast path (t <= 64, S <= 1024 * kDrawMax): every thread holds its draws' keys in
-  // registers; each wavefront sorts them and keeps its T = pow2(t) largest, and the
-  // workgroup merges the sixteen lists (bitonic merge tree in LDS).
-  const bool fast = a.t >= 1 && a.t <= 64 && a.S <= (u64)kBThreads * kDrawMax;
-  u32 T = 1;
-  while (T < a.t) T <<= 1;
+  // Fast path (S <= 1024 * kDrawMax): every thread holds its draws' keys in registers
+  // and one register radix select gives tau (b_sample_fast_row).
+  const bool fast = a.t >= 1 && a.S <= (u64)kBThreads * kDrawMax;
   for (u64 li = blockIdx.x; li < a.nrows; li += gridDim.x) {
     const u32 row = a.rows ? (u32)a.rows[li] : (u32)li;
     const float* xr = a.x + (u64)row * a.ld;
@@ -205,7 +168,7 @@ __global__ __launch_bounds__(kBThreads) void b_sample_kernel(BatchedArgs a) {
     }
     __syncthreads();
     if (fast) {
-      b_sample_fast_row(a, row, xr, keys, s_bits, s_list, &s_sel, &s_D, &s_fail, &s_n, T);
+      b_sample_fast_row(a, row, xr, keys, s_bits, s_list, &s_sel, &s_D, &s_fail);
       continue;
     }
     // draws 0..S-1, kDrawILP per thread per round
