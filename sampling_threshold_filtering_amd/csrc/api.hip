@@ -1262,6 +1262,7 @@ int profk_stage_batched_sample(const float* x, int64_t B, int64_t N, int64_t ld_
     a.attempt = (u32)attempt;
     a.ctls = ctl;
     a.scratch = keys;
+    a.keep_keys = 1;
     HIPCHK(launch_b_sample(a, s, (u32)nb), "launch b_sample");
   }
   HIPCHK(launch_b_stage_out(x, (u64)ld_x, (u64)N, nb, uS, keys, ctl, out_idx, out_tau_val, out_tau_idx, rec, s),

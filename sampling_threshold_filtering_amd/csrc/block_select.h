@@ -232,8 +232,12 @@ struct alignas(16) LdsSelect {
   u32 nsmall;
   u64 small[kWave];
   u64 result;
-  u64 wand[kMaxWaves], wor[kMaxWaves];  // per-wavefront AND / OR of the nonzero keys
-  u32 wnz[kMaxWaves];                   // per-wavefront count of the nonzero keys
+  // per wavefront: AND / OR / count of its nonzero keys (one record, so that one
+  // address register serves the three fields)
+  struct alignas(8) Wave {
+    u64 vand, vor;
+    u32 nz, pad;
+  } w[kMaxWaves];
 };
 
 // Radix selection of the key of descending rank `rank` (1-based) among distinct nonzero
@@ -263,15 +267,15 @@ __device__ __forceinline__ u32 wave_sum32(u32 v) {
 
 // Per-thread AND / OR / count of its nonzero keys in; the block's combined state out.
 __device__ __forceinline__ SelPass sel_begin(u64 va, u64 vo, u32 nz, u32 rank, LdsSelect* L) {
-  const u32 tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  const u32 tid = opaque_u32(threadIdx.x), lane = tid & (kWave - 1), wid = tid / kWave;
   const u32 nw = blockDim.x / kWave;
   va = wave_and64(va);
   vo = wave_or64(vo);
   nz = wave_sum32(nz);
   if (lane == 0) {
-    L->wand[wid] = va;
-    L->wor[wid] = vo;
-    L->wnz[wid] = nz;
+    L->w[wid].vand = va;
+    L->w[wid].vor = vo;
+    L->w[wid].nz = nz;
   }
   if (tid == 0) {
     L->nsmall = 0;
@@ -280,9 +284,9 @@ __device__ __forceinline__ SelPass sel_begin(u64 va, u64 vo, u32 nz, u32 rank, L
   __syncthreads();
   // lane w takes wavefront w's values; then the same reductions over the lanes
   const bool in = lane < nw;
-  const u64 a = wave_and64(in ? L->wand[lane] : ~0ull);
-  const u64 o = wave_or64(in ? L->wor[lane] : 0ull);
-  const u32 n = wave_sum32(in ? L->wnz[lane] : 0u);
+  const u64 a = wave_and64(in ? L->w[lane].vand : ~0ull);
+  const u64 o = wave_or64(in ? L->w[lane].vor : 0ull);
+  const u32 n = wave_sum32(in ? L->w[lane].nz : 0u);
   // bits above the highest one where the keys differ are common to all of them
   const u64 diff = a ^ o;
   SelPass p;
@@ -297,8 +301,8 @@ __device__ __forceinline__ SelPass sel_begin(u64 va, u64 vo, u32 nz, u32 rank, L
 // After a digit histogram in L->hist: wavefront 0 finds the digit that holds the rank;
 // every thread takes the new state.  Ends with the block synchronised.
 __device__ __forceinline__ void sel_choose(SelPass& p, u32 shift, LdsSelect* L) {
-  const u32 lane = lane_id();
-  if (threadIdx.x < (u32)kWave) {
+  const u32 tid = opaque_u32(threadIdx.x), lane = tid & (kWave - 1);
+  if (tid < (u32)kWave) {
     if (lane == 0) L->state = 2u;  // replaced by the lane whose digit holds the rank
     // descending digits: lane owns 255 - 4*lane .. 255 - 4*lane - 3
     u32 c[4], sum = 0;
@@ -341,7 +345,7 @@ __device__ __forceinline__ void sel_count(u64 k, const SelPass& p, u32 shift, u3
 
 __device__ __forceinline__ void sel_clear_hist(LdsSelect* L) {
   uint4* h = reinterpret_cast<uint4*>(L->hist);
-  for (u32 b = threadIdx.x; b < 256 * kSelCopies / 4; b += blockDim.x) h[b] = make_uint4(0, 0, 0, 0);
+  for (u32 b = opaque_u32(threadIdx.x); b < 256 * kSelCopies / 4; b += blockDim.x) h[b] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 }
 
@@ -361,7 +365,7 @@ __device__ __forceinline__ u64 sel_finish(const SelPass& p, LdsSelect* L) {
   __syncthreads();
   if (p.state == 1) {
     const u32 m = L->nsmall < (u32)kWave ? L->nsmall : (u32)kWave;
-    for (u32 t = threadIdx.x; t < 4u * kWave; t += blockDim.x) {
+    for (u32 t = opaque_u32(threadIdx.x); t < 4u * kWave; t += blockDim.x) {
       const u32 i = t >> 2, part = t & 3u;
       const u64 k = L->small[i];
       u64 o[16];
@@ -384,7 +388,7 @@ __device__ __forceinline__ u64 sel_finish(const SelPass& p, LdsSelect* L) {
 // The key of descending rank `rank` (1-based) among the nonzero, distinct keys s[0..n)
 // held in LDS.  Returns 0 when fewer than `rank` nonzero keys are present.
 __device__ inline u64 lds_select_desc(const u64* s, u32 n, u32 rank, LdsSelect* L) {
-  const u32 tid = threadIdx.x, lane = lane_id();
+  const u32 tid = opaque_u32(threadIdx.x), lane = tid & (kWave - 1);
   u64 va = ~0ull, vo = 0;
   u32 nz = 0;
   for (u32 i = tid; i < n; i += blockDim.x) {
@@ -422,7 +426,7 @@ __device__ inline u64 lds_select_desc(const u64* s, u32 n, u32 rank, LdsSelect* 
 // key.  A pass then reads no keys, it only counts digits.
 template <u32 P>
 __device__ inline u64 reg_select_desc(const u64 (&v)[P], u32 rank, LdsSelect* L) {
-  const u32 lane = lane_id();
+  const u32 lane = opaque_u32(threadIdx.x) & (kWave - 1);
   u64 va = ~0ull, vo = 0;
   u32 nz = 0;
 #pragma unroll

@@ -3,18 +3,25 @@
 // batched inputs are handled per row; App. C: per-row threshold, buffer and
 // counter; App. E.2: the budget is split eps/B per row).
 //
-//   b_sample_kernel   rows of at most 2^20 values, one workgroup per row (persistent
-//                     over the listed rows): the row's sample without replacement is
-//                     tracked in an LDS bitmap of N bits (128 KB) and the keys go to a
-//                     per-workgroup scratch.  With S <= 8192 every thread holds its
-//                     draws' keys in registers and one register radix select over
-//                     them and the top-up keys gives tau; otherwise draws are made
-//                     four at a time per thread, the
-//                     top-digit histogram is built on the way and tau comes from a
-//                     radix select (LDS reused as the sort buffer).  Wavefront 0 tops
-//                     the sample up.  It also clears the row's counter for the filter.
-//                     Longer rows take sample_kernel (k_sample.hip) with a row
-//                     dimension instead: one hash set per row in device memory.
+//   b_sample_pipe_kernel  rows of at most 2^20 values with S <= 4096: one 1024-thread
+//                     workgroup per CU, persistent over the listed rows.  Each row's
+//                     sample is tracked in an LDS hash set (two, used in turn); its
+//                     keys stay in registers (four draws per thread), and the top-up
+//                     keys fill the register slots that repeats left empty before one
+//                     register radix select gives tau.  A row's top-up and select run
+//                     while the next row's gathers are in flight.
+//   b_sample_kernel   the other rows of at most 2^20 values, one workgroup per row
+//                     (persistent over the listed rows): the row's sample without
+//                     replacement is tracked in an LDS bitmap of N bits (128 KB) and the
+//                     keys go to a per-workgroup scratch.  With S <= 8192 every thread
+//                     holds its draws' keys in registers and one register radix select
+//                     over them and the top-up keys gives tau; otherwise draws are made
+//                     four at a time per thread, the top-digit histogram is built on the
+//                     way and tau comes from a radix select (LDS reused as the sort
+//                     buffer).  Wavefront 0 tops the sample up.  Both samplers also
+//                     clear the row's counter for the filter.  Longer rows take
+//                     sample_kernel (k_sample.hip) with a row dimension instead: one
+//                     hash set per row in device memory.
 //   filter_kernel     (k_filter.hip) one streaming pass over all listed rows.
 //   b_refine_kernel   one 256-thread workgroup per row, dynamic LDS sized per path.
 //                     Buffers of up to kBatchedMaxM = 16384 keys are loaded into LDS:
@@ -262,6 +269,263 @@ __global__ __launch_bounds__(kBThreads) void b_sample_kernel(BatchedArgs a) {
 constexpr u32 kRefineThreads = 256;
 constexpr u32 kSelCap = kBatchedSelCap;
 
+// ---------------------------------------------------------------------------------
+// Pipelined sampler for S <= kPipeMaxS: while one row's top-up and threshold select
+// run, the next row's draws are already in their own LDS hash set and their gathers are
+// in flight, so the memory system is not left idle between a workgroup's rows (a
+// barrier does not wait for vector loads on this part, so they stay in flight across
+// the select's barriers).  Membership is a linear-probing hash set of row indices
+// (kPipeH slots, load at most one half) instead of an N-bit map, so that two rows' sets
+// fit in LDS at once.
+// Wavefront 0 gathers the first kWave top-up draws of a row together with the row's
+// own draws; the top-up then needs a further gather only when more than those are
+// needed (rows whose sample repeats itself a lot: S close to N / 2).
+constexpr u32 kPipeDraws = 4;                    // draws per thread
+constexpr u32 kPipeMaxS = kBThreads * kPipeDraws;  // 4096
+constexpr u32 kPipeHBits = 13;
+constexpr u32 kPipeH = 1u << kPipeHBits;  // >= 2 kPipeMaxS: the set is never full
+constexpr u32 kPipeEmpty = ~0u;           // no row index (N <= 2^20)
+
+__device__ __forceinline__ u32 pipe_slot(u32 idx) { return (idx * 0x9E3779B1u) >> (32u - kPipeHBits); }
+
+// Adds idx to the set; true when it was not there.  Ends: the set holds at most
+// kPipeMaxS < kPipeH indices, so the probe reaches an empty slot.
+__device__ __forceinline__ bool pipe_insert(u32* T, u32 idx) {
+  u32 s = pipe_slot(idx);
+  for (;;) {
+    const u32 old = atomicCAS(&T[s], kPipeEmpty, idx);
+    if (old == kPipeEmpty) return true;
+    if (old == idx) return false;
+    s = (s + 1u) & (kPipeH - 1u);
+  }
+}
+
+__device__ __forceinline__ bool pipe_held(const u32* T, u32 idx) {
+  u32 s = pipe_slot(idx);
+  for (;;) {
+    const u32 v = T[s];
+    if (v == idx) return true;
+    if (v == kPipeEmpty) return false;
+    s = (s + 1u) & (kPipeH - 1u);
+  }
+}
+
+// One row in flight: its draws, their gathered bits (loads possibly outstanding), which
+// draws were new to the set, and (wavefront 0) the first top-up draw and its bits.
+struct PipeRow {
+  u32 row;
+  u32 idx[kPipeDraws];
+  u32 val[kPipeDraws];
+  u32 fresh;  // bit q: draw q put its index into the set (one draw per distinct index)
+  u32 sidx, sval;
+};
+
+struct PipeLds {
+  u32 T[2][kPipeH];
+  u64 list[kPipeMaxS];  // top-up keys of the row being selected
+  LdsSelect sel;
+  u32 wempty[kBThreads / kWave];  // per wavefront: its empty register slots
+  u32 D[2];                        // distinct indices among a row's S draws
+  u32 Dfin, fail;
+};
+
+// Row `row`'s draws (indices only).  S = 0 (no next row) draws nothing, and its loads
+// (pipe_gather) then read index 0, so that the number of loads in flight does not depend
+// on the path taken.
+__device__ __forceinline__ void pipe_draw(const BatchedArgs& a, u32 row, u64 S, PipeRow& p) {
+  const u32 wid = threadIdx.x / kWave;
+  p.row = row;
+  // opaque thread index: otherwise the row-independent part of each draw's first
+  // round is hoisted out of the row loop and held in registers across it
+  const u32 tid = opaque_u32(threadIdx.x);
+#pragma unroll
+  for (u32 q = 0; q < kPipeDraws; ++q) {
+    const u64 j = (u64)q * kBThreads + tid;
+    p.idx[q] = j < S ? (u32)sample_draw(j, row, a.attempt, a.seed, a.N) : 0u;
+  }
+  // wavefront 0: the first top-up draw (the other wavefronts repeat their first load)
+  p.sidx = wid == 0 && S ? (u32)sample_draw(a.S + (tid & (kWave - 1)), row, a.attempt, a.seed, a.N) : p.idx[0];
+}
+
+// The drawn row's gathers issued, then its draws added to set T (cleared, and the block
+// synchronised since); the count of new indices is added to *D.
+__device__ __forceinline__ void pipe_gather(const BatchedArgs& a, u64 S, u32* T, u32* D, PipeRow& p) {
+  const u32 lane = lane_id();
+  const u32* xr = reinterpret_cast<const u32*>(a.x + (u64)p.row * a.ld);
+#pragma unroll
+  for (u32 q = 0; q < kPipeDraws; ++q) p.val[q] = xr[p.idx[q]];
+  p.sval = xr[p.sidx];
+  p.fresh = 0;
+  u32 nf = 0;
+#pragma unroll
+  for (u32 q = 0; q < kPipeDraws; ++q) {
+    const u64 j = (u64)q * kBThreads + threadIdx.x;
+    if (j < S && pipe_insert(T, p.idx[q])) p.fresh |= 1u << q;
+    nf += (u32)__popcll(__ballot((p.fresh >> q) & 1u));
+  }
+  if (lane == 0 && nf) atomicAdd(D, nf);
+}
+
+// Every wavefront waits here for all of row p's loads, on every path, so that none is
+// still in flight when its register is next written.
+__device__ __forceinline__ void pipe_wait(const PipeRow& p) {
+  static_assert(kPipeDraws == 4, "the wait names every draw");
+  asm volatile("" ::"v"(p.val[0]), "v"(p.val[1]), "v"(p.val[2]), "v"(p.val[3]), "v"(p.sval));
+}
+
+// The row's top-up (wavefront 0), its threshold and its control block; p's set is T,
+// its count of new indices D0.  The kPipeMaxS register slots of the block hold the D0
+// distinct draws and kPipeMaxS - D0 >= S - D0 empty slots (repeats, and draws past
+// S), so the top-up keys, staged in L.list, fill empty slots: a block-wide scan of the
+// empty slots gives each thread its range of L.list, and one register radix select over
+// the slots gives tau.
+__device__ __forceinline__ void pipe_finish(const BatchedArgs& a, PipeRow& p, u32* T, PipeLds& L, u32 D0,
+                                            bool has_row) {
+  const u32 lane = lane_id(), wid = threadIdx.x / kWave;
+  if (!has_row) return;  // the loads of a step with no next row (block-uniform)
+  u64 key[kPipeDraws];
+#pragma unroll
+  for (u32 q = 0; q < kPipeDraws; ++q) key[q] = (p.fresh >> q) & 1u ? make_key(p.val[q], p.idx[q]) : 0ull;
+  u64* keep = a.keep_keys ? a.scratch + (u64)p.row * 2 * a.S : nullptr;
+  if (keep) {
+#pragma unroll
+    for (u32 q = 0; q < kPipeDraws; ++q) {
+      const u64 j = (u64)q * kBThreads + threadIdx.x;
+      if (j < a.S) keep[j] = key[q];
+    }
+  }
+  const u32 empty = kPipeDraws - (u32)__popc(p.fresh);
+  const u32 incl = wave_incl_scan_add(empty, lane);
+  if (lane == kWave - 1) L.wempty[wid] = incl;
+  if (wid == 0) {
+    const u32* xr = reinterpret_cast<const u32*>(a.x + (u64)p.row * a.ld);
+    u64 D = D0;
+    u64 j0 = a.S;
+    u32 guard = 0;
+    bool first = true;
+    while (D < a.S) {
+      u32 id2, v2;
+      if (first) {
+        id2 = p.sidx;
+        v2 = p.sval;
+      } else {
+        id2 = (u32)sample_draw(j0 + lane, p.row, a.attempt, a.seed, a.N);
+        v2 = xr[id2];
+        asm volatile("" ::"v"(v2));  // waited here even where no lane takes it
+      }
+      first = false;
+      const bool held = pipe_held(T, id2);
+      bool repeat = false;
+      for (int d = 1; d < kWave; ++d) {
+        const u32 other = __shfl_up(id2, d, kWave);
+        if ((int)lane >= d && other == id2) repeat = true;
+      }
+      const bool ok2 = !held && !repeat;
+      const u64 m2 = __ballot(ok2);
+      const u64 need = a.S - D;
+      const u32 r = count_below(m2);
+      if (ok2 && r < need) {
+        pipe_insert(T, id2);
+        L.list[(D - D0) + r] = make_key(v2, id2);
+        if (keep) keep[a.S + (D - D0) + r] = make_key(v2, id2);
+      }
+      const u64 got = (u64)__popcll(m2);
+      D += got < need ? got : need;
+      j0 += kWave;
+      if (++guard > (1u << 22)) {  // bounded: S <= N/2 makes each draw new with prob >= 1/2
+        if (lane == 0) L.fail = 1;
+        break;
+      }
+    }
+    if (lane == 0) L.Dfin = (u32)D;
+  }
+  __syncthreads();
+  const bool sample_ok = !L.fail && L.Dfin == a.S;
+  u64 tau = 0;
+  if (sample_ok) {
+    const u32 E = (u32)(a.S - D0);
+    // first empty slot of this thread in the block's order (wavefronts, then lanes)
+    u32 e = incl - empty + wave_sum32(lane < wid ? L.wempty[lane] : 0u);
+#pragma unroll
+    for (u32 q = 0; q < kPipeDraws; ++q)
+      if (key[q] == 0) {
+        if (e < E) key[q] = L.list[e];
+        ++e;
+      }
+    tau = reg_select_desc(key, (u32)a.t, &L.sel);
+  } else {
+    __syncthreads();  // every thread has read L.fail and L.Dfin before they are reset
+  }
+  if (threadIdx.x == 0) {
+    RowCtl* c = &a.ctls[p.row];
+    c->tau = tau;
+    c->R = 0;
+    c->status = tau != 0 ? 0u : 3u;
+  }
+}
+
+__device__ __forceinline__ void pipe_clear(u32* T) {
+  uint4* t = reinterpret_cast<uint4*>(T);
+  for (u32 i = threadIdx.x; i < kPipeH / 4; i += kBThreads) t[i] = make_uint4(kPipeEmpty, kPipeEmpty, kPipeEmpty, kPipeEmpty);
+}
+
+// Listed row l, read through the scalar cache: its wait then does not wait for the
+// gathers in flight (the list is not written while the kernel runs).
+__device__ __forceinline__ u32 pipe_row_of(const BatchedArgs& a, u64 l) {
+  if (!a.rows) return (u32)l;
+  const __attribute__((address_space(4))) int* r = (const __attribute__((address_space(4))) int*)a.rows;
+  return (u32)r[l];
+}
+
+// One step: row `cur` (set T[c]; none when !has_cur) is finished while listed row li2
+// (set T[c ^ 1]) is drawn and gathered into `nxt`, if there is one.
+__device__ __forceinline__ void pipe_step(const BatchedArgs& a, PipeLds& L, u32 c, PipeRow& cur, PipeRow& nxt,
+                                          bool has_cur, u64 li2) {
+  const bool more = li2 < a.nrows;
+  pipe_clear(L.T[c ^ 1u]);
+  if (threadIdx.x == 0) {
+    L.D[c ^ 1u] = 0;
+    L.fail = 0;
+  }
+  __syncthreads();  // cur's count complete; T[c ^ 1] clear; the last select's users done
+  const u32 D0 = L.D[c];
+  const u64 S2 = more ? a.S : 0;
+  pipe_draw(a, more ? pipe_row_of(a, li2) : cur.row, S2, nxt);
+  // One row's gathers in flight at a time: with two, random gathers ran at about 42 G/s
+  // against about 49 G/s with one (a probe of this launch shape on MI355X).  The next
+  // row's gathers are issued as soon as cur's have arrived, and cur's top-up and
+  // threshold run while they are in flight.
+  pipe_wait(cur);
+  pipe_gather(a, S2, L.T[c ^ 1u], &L.D[c ^ 1u], nxt);
+  pipe_finish(a, cur, L.T[c], L, D0, has_cur);
+}
+
+__global__ __launch_bounds__(kBThreads) void b_sample_pipe_kernel(BatchedArgs a) {
+  __shared__ PipeLds L;
+  PipeRow ra, rb;
+  u64 li = blockIdx.x;
+  if (li >= a.nrows) return;
+  pipe_clear(L.T[0]);
+  if (threadIdx.x == 0) {
+    L.D[0] = 0;
+    L.fail = 0;
+  }
+  __syncthreads();
+  pipe_draw(a, pipe_row_of(a, li), a.S, ra);
+  pipe_gather(a, a.S, L.T[0], &L.D[0], ra);
+  // two register sets used in turn, so that no row's in-flight loads are copied.  The
+  // loop's one exit is at the bottom: an exit between the two steps would give the wait
+  // analysis a path from the first step's loads to the loop head, where it would then
+  // wait for them before the first step issues the next row's.
+  for (;;) {
+    const u64 li2 = li + gridDim.x, li3 = li2 + gridDim.x;
+    pipe_step(a, L, 0, ra, rb, true, li2);
+    pipe_step(a, L, 1, rb, ra, li2 < a.nrows, li3);
+    if (li3 >= a.nrows) return;
+    li = li3;
+  }
+}
+
 namespace {
 // Value bits from a key's order code, except the codes that fold encodings (+-0, NaN).
 __device__ __forceinline__ u32 row_value_bits(u64 key, const float* row, u32 idx) {
@@ -456,6 +720,10 @@ u32 row_grid(u64 nrows, u32 per_cu) {
 u32 batched_sample_blocks(u64 nrows) { return row_grid(nrows, 1); }
 
 hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s, u32 grid) {
+  if (a.t >= 1 && a.S <= kPipeMaxS && a.N <= kBatchedMaxN) {
+    b_sample_pipe_kernel<<<batched_sample_blocks(a.nrows), kBThreads, 0, s>>>(a);
+    return hipGetLastError();
+  }
   if (!grid) grid = batched_sample_blocks(a.nrows);
   b_sample_kernel<<<grid, kBThreads, 0, s>>>(a);
   return hipGetLastError();

@@ -230,12 +230,16 @@ struct BatchedArgs {
   u32 approx;      // 1: approximate mode (refine whatever each row's buffer holds, pad,
                    // and report each row's check in info[row])
   ApproxInfo* info;
+  u32 keep_keys;   // stage entry point: row r's sample keys stay in scratch[r * 2S ..)
 };
 
 u32 batched_sample_blocks(u64 nrows);
 
-// grid 0: the persistent grid (batched_sample_blocks); the stage entry point takes one
-// workgroup per row so that every row keeps its keys in its own scratch slice
+// The pipelined sampler (S <= 4096 and t >= 1) runs on the persistent grid
+// (batched_sample_blocks) and keeps no keys unless keep_keys is set; otherwise the
+// bitmap sampler runs on `grid` workgroups (0: the persistent grid), and the stage entry
+// point gives it one workgroup per row so that every row keeps its keys in its own
+// scratch slice.
 hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s, u32 grid = 0);
 hipError_t launch_b_stage_out(const float* x, u64 ld, u64 N, u64 B, u64 S, const u64* scratch, const RowCtl* ctls,
                               int64_t* out_idx, float* out_tau_val, int64_t* out_tau_idx, AttemptRecord* rec,

@@ -70,6 +70,14 @@ __device__ __forceinline__ u64 sample_draw(u64 j, u32 row, u32 attempt, u64 seed
 // Wave helpers
 __device__ __forceinline__ u32 lane_id() { return __lane_id(); }
 
+// v unchanged, but opaque to the optimiser: expressions of it stay where they are
+// written instead of being hoisted out of an enclosing loop and held in registers
+// across it (used where a loop body is register-bound).
+__device__ __forceinline__ u32 opaque_u32(u32 v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 __device__ __forceinline__ u32 count_below(u64 mask) {
   // number of set bits of mask in lanes below this one
   return __builtin_amdgcn_mbcnt_hi((u32)(mask >> 32), __builtin_amdgcn_mbcnt_lo((u32)mask, 0u));
