@@ -343,22 +343,27 @@ __device__ __forceinline__ void pipe_draw(const BatchedArgs& a, u32 row, u64 S, 
     const u64 j = (u64)q * kBThreads + tid;
     p.idx[q] = j < S ? (u32)sample_draw(j, row, a.attempt, a.seed, a.N) : 0u;
   }
-  // wavefront 0: the first top-up draw (the other wavefronts repeat their first load)
-  p.sidx = wid == 0 && S ? (u32)sample_draw(a.S + (tid & (kWave - 1)), row, a.attempt, a.seed, a.N) : p.idx[0];
+  // wavefront 0: the first top-up draw
+  p.sidx = wid == 0 && S ? (u32)sample_draw(a.S + (tid & (kWave - 1)), row, a.attempt, a.seed, a.N) : 0u;
 }
 
-// The drawn row's gathers issued, then its draws added to set T (cleared, and the block
-// synchronised since); the count of new indices is added to *D.
+// Draws Q0..Q1-1 of the drawn row: their gathers issued, then the draws added to set T
+// (cleared, and the block synchronised since); the count of new indices is added to *D.
+template <u32 Q0, u32 Q1>
 __device__ __forceinline__ void pipe_gather(const BatchedArgs& a, u64 S, u32* T, u32* D, PipeRow& p) {
-  const u32 lane = lane_id();
+  const u32 lane = lane_id(), wid = threadIdx.x / kWave;
   const u32* xr = reinterpret_cast<const u32*>(a.x + (u64)p.row * a.ld);
 #pragma unroll
-  for (u32 q = 0; q < kPipeDraws; ++q) p.val[q] = xr[p.idx[q]];
-  p.sval = xr[p.sidx];
-  p.fresh = 0;
+  for (u32 q = Q0; q < Q1; ++q) p.val[q] = xr[p.idx[q]];
+  if (Q0 == 0) {
+    // only wavefront 0 takes the top-up's first draw: every load is another request
+    // in the CU's queue, which the gathers of a row fill
+    p.sval = wid == 0 ? xr[p.sidx] : 0u;
+    p.fresh = 0;
+  }
   u32 nf = 0;
 #pragma unroll
-  for (u32 q = 0; q < kPipeDraws; ++q) {
+  for (u32 q = Q0; q < Q1; ++q) {
     const u64 j = (u64)q * kBThreads + threadIdx.x;
     if (j < S && pipe_insert(T, p.idx[q])) p.fresh |= 1u << q;
     nf += (u32)__popcll(__ballot((p.fresh >> q) & 1u));
@@ -379,14 +384,19 @@ __device__ __forceinline__ void pipe_wait(const PipeRow& p) {
 // S), so the top-up keys, staged in L.list, fill empty slots: a block-wide scan of the
 // empty slots gives each thread its range of L.list, and one register radix select over
 // the slots gives tau.
+// `mid` runs once the top-up is done, before the select (it issues the next row's
+// remaining gathers).
+template <class Mid>
 __device__ __forceinline__ void pipe_finish(const BatchedArgs& a, PipeRow& p, u32* T, PipeLds& L, u32 D0,
-                                            bool has_row) {
+                                            bool has_row, Mid&& mid) {
+  // has_row is false (block-uniformly) in a workgroup's last step, whose row is the
+  // loads of index 0 that stand in for a next row; mid() still runs, in the one place
+  // both cases share, so that the wait analysis sees one path through the loads
   const u32 lane = lane_id(), wid = threadIdx.x / kWave;
-  if (!has_row) return;  // the loads of a step with no next row (block-uniform)
   u64 key[kPipeDraws];
 #pragma unroll
   for (u32 q = 0; q < kPipeDraws; ++q) key[q] = (p.fresh >> q) & 1u ? make_key(p.val[q], p.idx[q]) : 0ull;
-  u64* keep = a.keep_keys ? a.scratch + (u64)p.row * 2 * a.S : nullptr;
+  u64* keep = a.keep_keys && has_row ? a.scratch + (u64)p.row * 2 * a.S : nullptr;
   if (keep) {
 #pragma unroll
     for (u32 q = 0; q < kPipeDraws; ++q) {
@@ -397,7 +407,7 @@ __device__ __forceinline__ void pipe_finish(const BatchedArgs& a, PipeRow& p, u3
   const u32 empty = kPipeDraws - (u32)__popc(p.fresh);
   const u32 incl = wave_incl_scan_add(empty, lane);
   if (lane == kWave - 1) L.wempty[wid] = incl;
-  if (wid == 0) {
+  if (has_row && wid == 0) {
     const u32* xr = reinterpret_cast<const u32*>(a.x + (u64)p.row * a.ld);
     u64 D = D0;
     u64 j0 = a.S;
@@ -414,18 +424,28 @@ __device__ __forceinline__ void pipe_finish(const BatchedArgs& a, PipeRow& p, u3
         asm volatile("" ::"v"(v2));  // waited here even where no lane takes it
       }
       first = false;
+      // A draw is taken when its index is neither in the set nor drawn by a lower lane
+      // of this chunk.  Every draw not in the set is inserted; a draw that then finds
+      // its index inserted by another lane of the chunk is a repeat within the chunk,
+      // and only then (about one chunk in 500 at S = 4096, N = 2^20) do the lanes
+      // compare indices to find which of the equal draws is the first.  The set then
+      // holds the chunk's new indices, the taken ones among them; the others can only
+      // be there when the chunk is the last one.
       const bool held = pipe_held(T, id2);
-      bool repeat = false;
-      for (int d = 1; d < kWave; ++d) {
-        const u32 other = __shfl_up(id2, d, kWave);
-        if ((int)lane >= d && other == id2) repeat = true;
+      const bool dup = !held && !pipe_insert(T, id2);
+      bool repeat = dup;
+      if (__ballot(dup)) {
+        repeat = false;
+        for (int d = 1; d < kWave; ++d) {
+          const u32 other = __shfl_up(id2, d, kWave);
+          if ((int)lane >= d && other == id2) repeat = true;
+        }
       }
       const bool ok2 = !held && !repeat;
       const u64 m2 = __ballot(ok2);
       const u64 need = a.S - D;
       const u32 r = count_below(m2);
       if (ok2 && r < need) {
-        pipe_insert(T, id2);
         L.list[(D - D0) + r] = make_key(v2, id2);
         if (keep) keep[a.S + (D - D0) + r] = make_key(v2, id2);
       }
@@ -440,6 +460,8 @@ __device__ __forceinline__ void pipe_finish(const BatchedArgs& a, PipeRow& p, u3
     if (lane == 0) L.Dfin = (u32)D;
   }
   __syncthreads();
+  mid();
+  if (!has_row) return;
   const bool sample_ok = !L.fail && L.Dfin == a.S;
   u64 tau = 0;
   if (sample_ok) {
@@ -496,8 +518,11 @@ __device__ __forceinline__ void pipe_step(const BatchedArgs& a, PipeLds& L, u32 
   // row's gathers are issued as soon as cur's have arrived, and cur's top-up and
   // threshold run while they are in flight.
   pipe_wait(cur);
-  pipe_gather(a, S2, L.T[c ^ 1u], &L.D[c ^ 1u], nxt);
-  pipe_finish(a, cur, L.T[c], L, D0, has_cur);
+  // half of them now, the rest after cur's top-up: a wavefront that issues a load while
+  // the CU's request queue is full stalls, and with it every barrier of cur's select
+  pipe_gather<0, kPipeDraws / 2>(a, S2, L.T[c ^ 1u], &L.D[c ^ 1u], nxt);
+  pipe_finish(a, cur, L.T[c], L, D0, has_cur,
+              [&] { pipe_gather<kPipeDraws / 2, kPipeDraws>(a, S2, L.T[c ^ 1u], &L.D[c ^ 1u], nxt); });
 }
 
 __global__ __launch_bounds__(kBThreads) void b_sample_pipe_kernel(BatchedArgs a) {
@@ -512,7 +537,7 @@ __global__ __launch_bounds__(kBThreads) void b_sample_pipe_kernel(BatchedArgs a)
   }
   __syncthreads();
   pipe_draw(a, pipe_row_of(a, li), a.S, ra);
-  pipe_gather(a, a.S, L.T[0], &L.D[0], ra);
+  pipe_gather<0, kPipeDraws>(a, a.S, L.T[0], &L.D[0], ra);
   // two register sets used in turn, so that no row's in-flight loads are copied.  The
   // loop's one exit is at the bottom: an exit between the two steps would give the wait
   // analysis a path from the first step's loads to the loop head, where it would then
