@@ -987,13 +987,20 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
       fa.seq = seq;
       fa.summary = 1;
     }
-    HIPCHK(launch_filter(fa, 0, s), "launch filter");
+    // the per-die stream times go back with the summary word, as in the flat path: the
+    // dies' shares of a long multi-row pass matter as much (1024 x 2^20 at k = 64: about
+    // 20 us per call between equal and learned shares)
+    const bool timed = summary && N * nrows >= kTimedMinN;
+    fa.xtime = timed ? reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kXtimeWord) : nullptr;
+    u64 split[kXcds + 1];
+    HIPCHK(launch_filter(fa, 0, s, split), "launch filter");
     HIPCHK(launch_b_refine(a, s), "launch b_refine");
     if (approx) break;
     if (summary) {
       bool all_ok = false;
       rc = wait_summary(w, s, seq, &all_ok);
       if (rc) return rc;
+      if (timed) update_die_weights(w, split);
       if (all_ok) {
         nrows = 0;
         break;
