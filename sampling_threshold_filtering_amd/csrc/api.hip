@@ -897,9 +897,12 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
   rc = clean_if_dirty(w, L, s);
   if (rc) return rc;
   w->dirty = true;
-  // control blocks, records and (grid sampler) the rows' top-digit histograms
-  HIPCHK(launch_attempt_init(ctl, grid ? sel : nullptr, rec, at<u32>(w, L.ticket), (u32)B, nullptr, s),
-         "launch attempt_init");
+  // control blocks, records and (grid sampler) the rows' top-digit histograms; the
+  // pipelined sampler sets up every row it samples, and the first attempt samples all
+  const bool pipelined = !grid && b_sample_pipelined(S, t, N);
+  if (!pipelined)
+    HIPCHK(launch_attempt_init(ctl, grid ? sel : nullptr, rec, at<u32>(w, L.ticket), (u32)B, nullptr, s),
+           "launch attempt_init");
   const int* rows = nullptr;  // all rows on the first attempt
   u64 nrows = B;
   std::vector<int> failed;
@@ -924,6 +927,7 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     a.rec = rec;
     a.approx = approx ? 1u : 0u;
     a.info = info;
+    a.tickets = pipelined && att == 0 ? at<u32>(w, L.ticket) : nullptr;
     if (grid) {
       // one grid row of sampling blocks per listed row (at most 65535 per launch)
       a.table = at<u32>(w, L.hash);

@@ -479,10 +479,13 @@ __device__ __forceinline__ void pipe_finish(const BatchedArgs& a, PipeRow& p, u3
     __syncthreads();  // every thread has read L.fail and L.Dfin before they are reset
   }
   if (threadIdx.x == 0) {
-    RowCtl* c = &a.ctls[p.row];
-    c->tau = tau;
-    c->R = 0;
-    c->status = tau != 0 ? 0u : 3u;
+    // the row's whole control block, as attempt_init leaves it, with tau and its status
+    RowCtl c{};
+    c.key_and = ~0ull;
+    c.tau = tau;
+    c.status = tau != 0 ? 0u : 3u;
+    a.ctls[p.row] = c;
+    if (a.rec) a.rec[p.row] = AttemptRecord{0ull, 0u, 0u, 0u, 0u};
   }
 }
 
@@ -529,6 +532,8 @@ __global__ __launch_bounds__(kBThreads) void b_sample_pipe_kernel(BatchedArgs a)
   __shared__ PipeLds L;
   PipeRow ra, rb;
   u64 li = blockIdx.x;
+  if (blockIdx.x == 0 && a.tickets)
+    for (u32 i = threadIdx.x; i < kTicketWords; i += kBThreads) a.tickets[i] = 0;
   if (li >= a.nrows) return;
   pipe_clear(L.T[0]);
   if (threadIdx.x == 0) {
@@ -744,8 +749,10 @@ u32 row_grid(u64 nrows, u32 per_cu) {
 
 u32 batched_sample_blocks(u64 nrows) { return row_grid(nrows, 1); }
 
+bool b_sample_pipelined(u64 S, u64 t, u64 N) { return t >= 1 && S <= kPipeMaxS && N <= kBatchedMaxN; }
+
 hipError_t launch_b_sample(const BatchedArgs& a, hipStream_t s, u32 grid) {
-  if (a.t >= 1 && a.S <= kPipeMaxS && a.N <= kBatchedMaxN) {
+  if (b_sample_pipelined(a.S, a.t, a.N)) {
     b_sample_pipe_kernel<<<batched_sample_blocks(a.nrows), kBThreads, 0, s>>>(a);
     return hipGetLastError();
   }

@@ -231,7 +231,12 @@ struct BatchedArgs {
                    // and report each row's check in info[row])
   ApproxInfo* info;
   u32 keep_keys;   // stage entry point: row r's sample keys stay in scratch[r * 2S ..)
+  u32* tickets;    // pipelined sampler: kTicketWords words it zeroes (nullptr: none)
 };
+
+// Whether launch_b_sample runs the pipelined sampler, which also leaves every row it
+// samples with a fresh control block and attempt record (what attempt_init does).
+bool b_sample_pipelined(u64 S, u64 t, u64 N);
 
 u32 batched_sample_blocks(u64 nrows);
 
