@@ -980,6 +980,7 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     fa.rec = rec;
     fa.sels = nullptr;
     fa.sparse = filter_shape(p, N);
+    fa.hits_per_row = p.E_R;
     // exact mode without statistics: the filter's last block publishes whether every
     // listed row passed into pinned host memory, and when they all did the call returns
     // on that word while the refinement still runs (outputs complete in stream order)

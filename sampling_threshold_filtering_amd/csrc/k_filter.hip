@@ -129,6 +129,114 @@ __device__ __forceinline__ void stage_hits(Stage& st, u32 row, const u64 (&masks
   st.n = run;
 }
 
+// Several rows of at most 2^20 values, read in the flat pass's order (FO): a wavefront's
+// tiles change rows every few tiles, so its stage holds the keys of many rows.  Each
+// staged key carries its row's list position l in the index word's top 12 bits (all set
+// in ~i while i < 2^20), and the wavefront's keys are staged in list-position order, so
+// the flush at the end of the stream reserves one run of R per stretch of equal
+// positions.
+constexpr u32 kFoRows = 1024;  // listed rows whose positions and thresholds a block holds in LDS
+constexpr u64 kFoMaxN = 1ull << 20;
+
+__device__ __forceinline__ u64 fo_pack(u64 key, u32 l) { return (key & ~(0xFFFull << 20)) | ((u64)l << 20); }
+__device__ __forceinline__ u32 fo_list(u64 p) { return (u32)p >> 20; }
+__device__ __forceinline__ u64 fo_unpack(u64 p) { return p | (0xFFFull << 20); }
+
+// The first key of key j's stretch of equal positions, for the keys c0 + lane of one pass
+// over the stage (carry: the last stretch start before c0).
+__device__ __forceinline__ u32 fo_stretch(const Stage& st, u32 c0, u32& carry, bool* start_out, u32* l_out) {
+  const u32 lane = lane_id(), j = c0 + lane;
+  const bool in = j < st.n;
+  const u32 l = in ? fo_list(st.buf[j]) : 0u;
+  const u32 lp = in && j > 0 ? fo_list(st.buf[j - 1]) : ~0u;
+  const bool start = in && l != lp;
+  const u64 m = __ballot(start);
+  const u64 le = m & ((2ull << lane) - 1ull);  // starts at or below this lane
+  const u32 first = le ? c0 + 63u - (u32)__clzll((long long)le) : carry;
+  if (m) carry = c0 + 63u - (u32)__clzll((long long)m);
+  *start_out = start;
+  *l_out = l;
+  return first;
+}
+
+// The stage's keys to their rows' buffers: one returning atomic on R per stretch.
+// sbase: this wavefront's kStageCap words of LDS; lrow: listed row of each position.
+__device__ __forceinline__ void stage_flush_fo(Stage& st, u32* sbase, const u32* lrow, RowCtl* ctls, u64* cand,
+                                               u64 M) {
+  if (st.n == 0) return;
+  const u32 lane = lane_id();
+  wave_lds_sync();
+  for (u32 j = lane; j < st.n; j += kWave) sbase[j] = 0;
+  wave_lds_sync();
+  u32 carry = 0;
+  for (u32 c0 = 0; c0 < st.n; c0 += kWave) {
+    bool start;
+    u32 l;
+    const u32 first = fo_stretch(st, c0, carry, &start, &l);
+    if (c0 + lane < st.n) atomicAdd(&sbase[first], 1u);
+  }
+  wave_lds_sync();
+  carry = 0;
+  for (u32 c0 = 0; c0 < st.n; c0 += kWave) {
+    bool start;
+    u32 l;
+    fo_stretch(st, c0, carry, &start, &l);
+    const u32 j = c0 + lane;
+    if (start) sbase[j] = (u32)atomicAdd(&ctls[lrow[l]].R, (u64)sbase[j]);  // R < 2^32: rows of <= 2^20
+  }
+  wave_lds_sync();
+  carry = 0;
+  for (u32 c0 = 0; c0 < st.n; c0 += kWave) {
+    bool start;
+    u32 l;
+    const u32 first = fo_stretch(st, c0, carry, &start, &l);
+    const u32 j = c0 + lane;
+    if (j < st.n) {
+      const u64 pos = (u64)sbase[first] + (j - first);
+      if (pos < M) cand[(u64)lrow[l] * M + pos] = fo_unpack(st.buf[j]);
+    }
+  }
+  wave_lds_sync();
+  st.n = 0;
+}
+
+template <int NB>
+__device__ __forceinline__ void stage_hits_fo(Stage& st, u32 l, const u64 (&masks)[NB], const bool (&hit)[NB],
+                                              const u64 (&key)[NB], u32* sbase, const u32* lrow, RowCtl* ctls,
+                                              u64* cand, u64 M) {
+  u32 total = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) total += (u32)__popcll(masks[b]);
+  if (total == 0) return;
+  if (st.n + total > kStageCap) {
+    // stage full (the launch takes this order only while a wavefront's expected hits
+    // fill at most 80% of it): this batch straight to its row's buffer with one atomic; the
+    // stage itself is flushed at the end of the stream, where few registers are live
+    const u32 row = lrow[l];
+    u64 base = 0;
+    if (lane_id() == 0) base = atomicAdd(&ctls[row].R, (u64)total);
+    base = __shfl(base, 0);
+    u64* dst = cand + (u64)row * M;
+    u32 run = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (hit[b]) {
+        const u64 pos = base + run + count_below(masks[b]);
+        if (pos < M) dst[pos] = key[b];
+      }
+      run += (u32)__popcll(masks[b]);
+    }
+    return;
+  }
+  u32 run = st.n;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (hit[b]) st.buf[run + count_below(masks[b])] = fo_pack(key[b], l);
+    run += (u32)__popcll(masks[b]);
+  }
+  st.n = run;
+}
+
 }  // namespace
 
 // One wave-tile's place: its row, the row's threshold and the tile's first float4.
@@ -138,13 +246,23 @@ struct TileAt {
   u64 tau;
   u64 v0;
   u64 tile;
+  u32 lr;  // the row's list position
 };
 
 // The current row of a wavefront, reloaded only when the row changes: the row list
 // and the threshold are read with vector loads (the kernel's atomics on the same
 // control blocks rule out scalar ones), and waiting for them would also wait for the
-// tile loads in flight.
-struct RowCache {
+// tile loads in flight.  In the flat order (FO) rows change every few tiles, and the
+// block holds every listed row's index and threshold in LDS instead (lrow, ltau).
+template <bool FO>
+struct RowLds {};
+template <>
+struct RowLds<true> {
+  const u32* lrow = nullptr;
+  const u64* ltau = nullptr;
+};
+template <bool FO>
+struct RowCache : RowLds<FO> {
   u64 lr = ~0ull;
   u32 row = 0;
   RowGeom geo{};
@@ -152,9 +270,15 @@ struct RowCache {
   __device__ __forceinline__ TileAt at(const FilterArgs& a, u64 l, u64 tile, u32 U) {
     if (l != lr) {
       lr = l;
-      row = a.rows ? (u32)a.rows[l] : (u32)l;
-      geo = row_geom(a.x, a.ld, a.N, row);
-      tau = a.ctls[row].tau;
+      if constexpr (FO) {
+        row = this->lrow[l];
+        geo = row_geom(a.x, a.ld, a.N, row);
+        tau = this->ltau[l];
+      } else {
+        row = a.rows ? (u32)a.rows[l] : (u32)l;
+        geo = row_geom(a.x, a.ld, a.N, row);
+        tau = a.ctls[row].tau;
+      }
     }
     TileAt t;
     t.row = row;
@@ -162,6 +286,7 @@ struct RowCache {
     t.tau = tau;
     t.v0 = tile * (u64)(U * kWave);
     t.tile = tile;
+    t.lr = (u32)l;
     return t;
   }
 };
@@ -184,10 +309,26 @@ __device__ __forceinline__ void load_tile(const TileAt& t, f4 (&v)[U], bool (&va
   }
 }
 
+// FO staging state of a wavefront: its LDS words for a flush, and the row list.
+struct FoCtx {
+  u32* sbase;
+  const u32* lrow;
+};
+
+// Stage one batch of hits of tile t (FO: with the tile's list position).
+template <bool FO, int NB>
+__device__ __forceinline__ void stage_tile_hits(const FilterArgs& a, Stage& st, const FoCtx& fo, const TileAt& t,
+                                                const u64 (&masks)[NB], const bool (&hit)[NB], const u64 (&key)[NB]) {
+  if constexpr (FO)
+    stage_hits_fo<NB>(st, t.lr, masks, hit, key, fo.sbase, fo.lrow, a.ctls, a.cand, a.M);
+  else
+    stage_hits<NB>(st, t.row, masks, hit, key, a.ctls, a.cand, a.M);
+}
+
 // Tests one loaded wave-tile (and, on a row's first tile, the row's scalar edges).
-template <int U>
-__device__ __forceinline__ void test_tile(const FilterArgs& a, Stage& st, const TileAt& t, const f4 (&v)[U],
-                                          const bool (&valid)[U]) {
+template <int U, bool FO>
+__device__ __forceinline__ void test_tile(const FilterArgs& a, Stage& st, const FoCtx& fo, const TileAt& t,
+                                          const f4 (&v)[U], const bool (&valid)[U]) {
   const u32 lane = lane_id();
   const u32 tk = (u32)(t.tau >> 32);
   const u32 ti = key_index(t.tau);
@@ -222,7 +363,7 @@ __device__ __forceinline__ void test_tile(const FilterArgs& a, Stage& st, const 
         hit[0] = valid[u] && (o > tk || (o == tk && i <= ti));
         key[0] = ((u64)o << 32) | (u64)(~i);
         masks[0] = __ballot(hit[0]);
-        stage_hits<1>(st, t.row, masks, hit, key, a.ctls, a.cand, a.M);
+        stage_tile_hits<FO, 1>(a, st, fo, t, masks, hit, key);
       }
     }
   }
@@ -245,11 +386,11 @@ __device__ __forceinline__ void test_tile(const FilterArgs& a, Stage& st, const 
     hit[0] = in && (o > tk || (o == tk && i <= ti));
     key[0] = ((u64)o << 32) | (u64)(~i);
     masks[0] = __ballot(hit[0]);
-    stage_hits<1>(st, t.row, masks, hit, key, a.ctls, a.cand, a.M);
+    stage_tile_hits<FO, 1>(a, st, fo, t, masks, hit, key);
   }
 }
 
-template <int U, bool NT>
+template <int U, bool NT, bool FO>
 __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   __shared__ u64 s_stage[kWavesPerBlock][kStageCap];
   __shared__ u32 s_last;
@@ -296,6 +437,21 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     }
   };
   auto advance = [&](Cursor& c) {
+    if constexpr (FO) {
+      // one tile per chunk: the next is nwx tiles on, the row kept by subtraction
+      c.chunk += nwx;
+      if (c.chunk >= cend) {
+        c.g = gend;
+        return;
+      }
+      c.g = c.chunk;
+      c.tile += nwx;
+      while (c.tile >= tpr) {
+        c.tile -= tpr;
+        ++c.lr;
+      }
+      return;
+    }
     if (c.in + 1 < run && c.g + 1 < gend) {
       ++c.in;
       ++c.g;
@@ -317,7 +473,24 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   TileAt ta{}, tb{};
   f4 va[U], vb[U];
   bool oka[U], okb[U];
-  RowCache rc;
+  RowCache<FO> rc;
+  FoCtx fo{nullptr, nullptr};
+  if constexpr (FO) {
+    // every listed row's index and threshold, and each wavefront's flush words
+    __shared__ u64 s_ltau[kFoRows];
+    __shared__ u32 s_lrow[kFoRows];
+    __shared__ u32 s_sbase[kWavesPerBlock][kStageCap];
+    for (u32 l = threadIdx.x; l < (u32)a.nrows; l += kFilterThreads) {
+      const u32 row = a.rows ? (u32)a.rows[l] : l;
+      s_lrow[l] = row;
+      s_ltau[l] = a.ctls[row].tau;
+    }
+    __syncthreads();
+    rc.lrow = s_lrow;
+    rc.ltau = s_ltau;
+    fo.sbase = s_sbase[wid];
+    fo.lrow = s_lrow;
+  }
   const f4* safe = reinterpret_cast<const f4*>(a.ctls);
   if (cur.g < gend) {
     ta = rc.at(a, cur.lr, cur.tile, U);
@@ -329,19 +502,22 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     // past the end: reload the current tile (the loads stay unconditional)
     tb = nx.g < gend ? rc.at(a, nx.lr, nx.tile, U) : ta;
     load_tile<U, NT>(tb, vb, okb, safe);
-    test_tile<U>(a, st, ta, va, oka);
+    test_tile<U, FO>(a, st, fo, ta, va, oka);
     cur = nx;
     if (cur.g >= gend) break;
     advance(nx);
     ta = nx.g < gend ? rc.at(a, nx.lr, nx.tile, U) : tb;
     load_tile<U, NT>(ta, va, oka, safe);
-    test_tile<U>(a, st, tb, vb, okb);
+    test_tile<U, FO>(a, st, fo, tb, vb, okb);
     cur = nx;
   }
   if (a.xtime) {
     __syncthreads();
     if (threadIdx.x == 0) atomicMax(&a.xtime[1 + xcd], wall_clock64());
   }
+  if constexpr (FO) {
+    stage_flush_fo(st, fo.sbase, fo.lrow, a.ctls, a.cand, a.M);
+  } else {
   // End of the stream: the block's waves reserve their staged keys with one
   // atomic per row they hold (one in the flat case) instead of one per wave.
   __shared__ u32 s_n[kWavesPerBlock], s_row[kWavesPerBlock];
@@ -381,6 +557,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     u64* dst = a.cand + (u64)st.row * a.M;
     for (u32 j = lane; j < st.n; j += kWave)
       if (base + j < a.M) dst[base + j] = st.buf[j];
+  }
   }
 
   // Last block: run-time check per row, host record, arm the refinement selection.
@@ -473,9 +650,12 @@ hipError_t launch_filter_shape(const FilterArgs& a0, u32 grid, u32 blocks_per_cu
   if ((u64)grid > need) grid = (u32)need;
   // several rows: chunks of up to kFilterRun tiles, but short enough that every
   // wavefront gets about four (16 rows of 2^22 values are only 256 chunks of 64 tiles,
-  // which would leave most wavefronts idle)
+  // which would leave most wavefronts idle); rows of at most 2^20 values, up to
+  // kFoRows of them, are read in the flat pass's order instead (FO)
+  const bool fo = a.nrows > 1 && a.nrows <= kFoRows && a.N <= kFoMaxN &&
+                  a.hits_per_row * (double)a.nrows <= 0.8 * kStageCap * (double)grid * kWavesPerBlock;
   a.run = 1;
-  if (a.nrows > 1) {
+  if (a.nrows > 1 && !fo) {
     const u64 per = a.total_tiles / ((u64)grid * kWavesPerBlock * 4);
     a.run = per < 1 ? 1 : (per > kFilterRun ? kFilterRun : per);
   }
@@ -498,7 +678,10 @@ hipError_t launch_filter_shape(const FilterArgs& a0, u32 grid, u32 blocks_per_cu
   }
   if (split_out)
     for (u32 x = 0; x <= kXcds; ++x) split_out[x] = a.split[x];
-  filter_kernel<U, true><<<grid, kFilterThreads, 0, s>>>(a);
+  if (fo)
+    filter_kernel<U, true, true><<<grid, kFilterThreads, 0, s>>>(a);
+  else
+    filter_kernel<U, true, false><<<grid, kFilterThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 }  // namespace

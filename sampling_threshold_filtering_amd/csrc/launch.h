@@ -58,6 +58,7 @@ struct FilterArgs {
   u64 tiles_per_row;   // set by launch_filter
   u64 total_tiles;
   u64 run;             // tiles per chunk of the block-cyclic order (set by launch_filter)
+  double hits_per_row; // several rows: the expected hits per row, E[R] (0: unknown)
 };
 
 hipError_t launch_attempt_init(RowCtl* ctl, SelState* sel, AttemptRecord* rec, u32* tickets, u32 nrows,
