@@ -132,9 +132,7 @@ __device__ __forceinline__ void stage_hits(Stage& st, u32 row, const u64 (&masks
 // Several rows of at most 2^20 values, read in the flat pass's order (FO): a wavefront's
 // tiles change rows every few tiles, so its stage holds the keys of many rows.  Each
 // staged key carries its row's list position l in the index word's top 12 bits (all set
-// in ~i while i < 2^20), and the wavefront's keys are staged in list-position order, so
-// the flush at the end of the stream reserves one run of R per stretch of equal
-// positions.
+// in ~i while i < 2^20); the block places its wavefronts' keys at the end of the stream.
 constexpr u32 kFoRows = 1024;  // listed rows whose positions and thresholds a block holds in LDS
 constexpr u64 kFoMaxN = 1ull << 20;
 
@@ -142,68 +140,9 @@ __device__ __forceinline__ u64 fo_pack(u64 key, u32 l) { return (key & ~(0xFFFul
 __device__ __forceinline__ u32 fo_list(u64 p) { return (u32)p >> 20; }
 __device__ __forceinline__ u64 fo_unpack(u64 p) { return p | (0xFFFull << 20); }
 
-// The first key of key j's stretch of equal positions, for the keys c0 + lane of one pass
-// over the stage (carry: the last stretch start before c0).
-__device__ __forceinline__ u32 fo_stretch(const Stage& st, u32 c0, u32& carry, bool* start_out, u32* l_out) {
-  const u32 lane = lane_id(), j = c0 + lane;
-  const bool in = j < st.n;
-  const u32 l = in ? fo_list(st.buf[j]) : 0u;
-  const u32 lp = in && j > 0 ? fo_list(st.buf[j - 1]) : ~0u;
-  const bool start = in && l != lp;
-  const u64 m = __ballot(start);
-  const u64 le = m & ((2ull << lane) - 1ull);  // starts at or below this lane
-  const u32 first = le ? c0 + 63u - (u32)__clzll((long long)le) : carry;
-  if (m) carry = c0 + 63u - (u32)__clzll((long long)m);
-  *start_out = start;
-  *l_out = l;
-  return first;
-}
-
-// The stage's keys to their rows' buffers: one returning atomic on R per stretch.
-// sbase: this wavefront's kStageCap words of LDS; lrow: listed row of each position.
-__device__ __forceinline__ void stage_flush_fo(Stage& st, u32* sbase, const u32* lrow, RowCtl* ctls, u64* cand,
-                                               u64 M) {
-  if (st.n == 0) return;
-  const u32 lane = lane_id();
-  wave_lds_sync();
-  for (u32 j = lane; j < st.n; j += kWave) sbase[j] = 0;
-  wave_lds_sync();
-  u32 carry = 0;
-  for (u32 c0 = 0; c0 < st.n; c0 += kWave) {
-    bool start;
-    u32 l;
-    const u32 first = fo_stretch(st, c0, carry, &start, &l);
-    if (c0 + lane < st.n) atomicAdd(&sbase[first], 1u);
-  }
-  wave_lds_sync();
-  carry = 0;
-  for (u32 c0 = 0; c0 < st.n; c0 += kWave) {
-    bool start;
-    u32 l;
-    fo_stretch(st, c0, carry, &start, &l);
-    const u32 j = c0 + lane;
-    if (start) sbase[j] = (u32)atomicAdd(&ctls[lrow[l]].R, (u64)sbase[j]);  // R < 2^32: rows of <= 2^20
-  }
-  wave_lds_sync();
-  carry = 0;
-  for (u32 c0 = 0; c0 < st.n; c0 += kWave) {
-    bool start;
-    u32 l;
-    const u32 first = fo_stretch(st, c0, carry, &start, &l);
-    const u32 j = c0 + lane;
-    if (j < st.n) {
-      const u64 pos = (u64)sbase[first] + (j - first);
-      if (pos < M) cand[(u64)lrow[l] * M + pos] = fo_unpack(st.buf[j]);
-    }
-  }
-  wave_lds_sync();
-  st.n = 0;
-}
-
 template <int NB>
 __device__ __forceinline__ void stage_hits_fo(Stage& st, u32 l, const u64 (&masks)[NB], const bool (&hit)[NB],
-                                              const u64 (&key)[NB], u32* sbase, const u32* lrow, RowCtl* ctls,
-                                              u64* cand, u64 M) {
+                                              const u64 (&key)[NB], const u32* lrow, RowCtl* ctls, u64* cand, u64 M) {
   u32 total = 0;
 #pragma unroll
   for (int b = 0; b < NB; ++b) total += (u32)__popcll(masks[b]);
@@ -309,9 +248,9 @@ __device__ __forceinline__ void load_tile(const TileAt& t, f4 (&v)[U], bool (&va
   }
 }
 
-// FO staging state of a wavefront: its LDS words for a flush, and the row list.
+// FO: the block's row list and its per-position counters for the end of the stream.
 struct FoCtx {
-  u32* sbase;
+  u32* cnt;
   const u32* lrow;
 };
 
@@ -320,7 +259,7 @@ template <bool FO, int NB>
 __device__ __forceinline__ void stage_tile_hits(const FilterArgs& a, Stage& st, const FoCtx& fo, const TileAt& t,
                                                 const u64 (&masks)[NB], const bool (&hit)[NB], const u64 (&key)[NB]) {
   if constexpr (FO)
-    stage_hits_fo<NB>(st, t.lr, masks, hit, key, fo.sbase, fo.lrow, a.ctls, a.cand, a.M);
+    stage_hits_fo<NB>(st, t.lr, masks, hit, key, fo.lrow, a.ctls, a.cand, a.M);
   else
     stage_hits<NB>(st, t.row, masks, hit, key, a.ctls, a.cand, a.M);
 }
@@ -476,10 +415,10 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   RowCache<FO> rc;
   FoCtx fo{nullptr, nullptr};
   if constexpr (FO) {
-    // every listed row's index and threshold, and each wavefront's flush words
+    // every listed row's index and threshold, and a counter per list position
     __shared__ u64 s_ltau[kFoRows];
     __shared__ u32 s_lrow[kFoRows];
-    __shared__ u32 s_sbase[kWavesPerBlock][kStageCap];
+    __shared__ u32 s_cnt[kFoRows];
     for (u32 l = threadIdx.x; l < (u32)a.nrows; l += kFilterThreads) {
       const u32 row = a.rows ? (u32)a.rows[l] : l;
       s_lrow[l] = row;
@@ -488,7 +427,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     __syncthreads();
     rc.lrow = s_lrow;
     rc.ltau = s_ltau;
-    fo.sbase = s_sbase[wid];
+    fo.cnt = s_cnt;
     fo.lrow = s_lrow;
   }
   const f4* safe = reinterpret_cast<const f4*>(a.ctls);
@@ -516,7 +455,24 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     if (threadIdx.x == 0) atomicMax(&a.xtime[1 + xcd], wall_clock64());
   }
   if constexpr (FO) {
-    stage_flush_fo(st, fo.sbase, fo.lrow, a.ctls, a.cand, a.M);
+    // End of the stream: the block's keys per list position counted in LDS, one atomic
+    // on R per position the block holds, then every key placed from its position's run
+    // (the block's four wavefronts sweep the same rows side by side)
+    u32* cnt = fo.cnt;
+    __syncthreads();
+    for (u32 l = threadIdx.x; l < (u32)a.nrows; l += kFilterThreads) cnt[l] = 0;
+    __syncthreads();
+    for (u32 j = lane; j < st.n; j += kWave) atomicAdd(&cnt[fo_list(st.buf[j])], 1u);
+    __syncthreads();
+    for (u32 l = threadIdx.x; l < (u32)a.nrows; l += kFilterThreads)
+      if (cnt[l]) cnt[l] = (u32)atomicAdd(&a.ctls[fo.lrow[l]].R, (u64)cnt[l]);  // R < 2^32: rows of <= 2^20
+    __syncthreads();
+    for (u32 j = lane; j < st.n; j += kWave) {
+      const u64 p = st.buf[j];
+      const u32 l = fo_list(p);
+      const u64 pos = atomicAdd(&cnt[l], 1u);
+      if (pos < a.M) a.cand[(u64)fo.lrow[l] * a.M + pos] = fo_unpack(p);
+    }
   } else {
   // End of the stream: the block's waves reserve their staged keys with one
   // atomic per row they hold (one in the flat case) instead of one per wave.
@@ -592,6 +548,56 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   }
   if (threadIdx.x == 0) s_nfail = 0;
   __syncthreads();
+  if constexpr (FO) {
+    // up to kFoRows rows: each thread reads its rows' counts and statuses together (one
+    // round trip to L2, not one per row), then checks them
+    constexpr u32 kTail = kFoRows / kFilterThreads;
+    u32 rowv[kTail];
+    u64 Rv[kTail];
+    u32 sv[kTail];
+#pragma unroll
+    for (u32 q = 0; q < kTail; ++q) {
+      const u32 lr = q * kFilterThreads + threadIdx.x;
+      rowv[q] = 0;
+      Rv[q] = 0;
+      sv[q] = 0;
+      if (lr < a.nrows) {
+        rowv[q] = rc.lrow[lr];
+        Rv[q] = atomicAdd(&a.ctls[rowv[q]].R, 0ull);  // read at the coherence point
+        sv[q] = a.ctls[rowv[q]].status;
+      }
+    }
+#pragma unroll
+    for (u32 q = 0; q < kTail; ++q) {
+      const u32 lr = q * kFilterThreads + threadIdx.x;
+      if (lr >= a.nrows) continue;
+      const u32 row = rowv[q];
+      const u64 R = Rv[q];
+      u32 status = sv[q];
+      if (status == 0) status = R < a.k ? 1u : (R > a.M ? 2u : 0u);
+      a.ctls[row].status = status;
+      if (status) atomicAdd(&s_nfail, 1u);
+      if (a.rec) {
+        a.rec[row].R = R;
+        a.rec[row].status = status;
+      }
+      if (lr == 0 && a.hrec && a.seq && !a.summary) {
+        const u64 word = ((u64)(a.seq & 0x3FFFFFu) << 42) | ((u64)(status & 3u) << 40) | (R & ((1ull << 40) - 1));
+        __hip_atomic_store(&a.hrec->early, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+      if (a.sels) {
+        SelState* s = &a.sels[row];
+        s->prefix = 0;
+        s->mask = 0;
+        s->rank = a.k;
+        s->count = R < a.M ? R : a.M;
+        s->done = status ? 1u : 0u;
+        s->digit = 0;
+        s->ticket = 0;
+        s->ncol = 0;
+      }
+    }
+  } else
   for (u64 lr = threadIdx.x; lr < a.nrows; lr += blockDim.x) {
     const u32 row = a.rows ? (u32)a.rows[lr] : (u32)lr;
     RowCtl* c = &a.ctls[row];
