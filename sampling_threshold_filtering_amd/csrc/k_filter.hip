@@ -129,20 +129,23 @@ __device__ __forceinline__ void stage_hits(Stage& st, u32 row, const u64 (&masks
   st.n = run;
 }
 
-// Several rows of at most 2^20 values, read in the flat pass's order (FO): a wavefront's
-// tiles change rows every few tiles, so its stage holds the keys of many rows.  Each
-// staged key carries its row's list position l in the index word's top 12 bits (all set
-// in ~i while i < 2^20); the block places its wavefronts' keys at the end of the stream.
+// Several rows, read in the flat pass's order (FO): a wavefront's tiles change rows every
+// few tiles, so its stage holds the keys of many rows.  Each staged key carries its row's
+// list position l in the index word's bits above the index (all set in ~i, i < N: the
+// launch takes this order only where the positions fit there); the block places its
+// wavefronts' keys at the end of the stream.
 constexpr u32 kFoRows = 1024;  // listed rows whose positions and thresholds a block holds in LDS
-constexpr u64 kFoMaxN = 1ull << 20;
 
-__device__ __forceinline__ u64 fo_pack(u64 key, u32 l) { return (key & ~(0xFFFull << 20)) | ((u64)l << 20); }
-__device__ __forceinline__ u32 fo_list(u64 p) { return (u32)p >> 20; }
-__device__ __forceinline__ u64 fo_unpack(u64 p) { return p | (0xFFFull << 20); }
+// The index word's bits at and above `shift` (= the bits of N - 1) hold the position.
+__device__ __forceinline__ u64 fo_high(u32 shift) { return (u64)(0xFFFFFFFFu << shift); }
+__device__ __forceinline__ u64 fo_pack(u64 key, u32 l, u32 shift) { return (key & ~fo_high(shift)) | ((u64)l << shift); }
+__device__ __forceinline__ u32 fo_list(u64 p, u32 shift) { return (u32)p >> shift; }
+__device__ __forceinline__ u64 fo_unpack(u64 p, u32 shift) { return p | fo_high(shift); }
 
 template <int NB>
 __device__ __forceinline__ void stage_hits_fo(Stage& st, u32 l, const u64 (&masks)[NB], const bool (&hit)[NB],
-                                              const u64 (&key)[NB], const u32* lrow, RowCtl* ctls, u64* cand, u64 M) {
+                                              const u64 (&key)[NB], const u32* lrow, u32 shift, RowCtl* ctls, u64* cand,
+                                              u64 M) {
   u32 total = 0;
 #pragma unroll
   for (int b = 0; b < NB; ++b) total += (u32)__popcll(masks[b]);
@@ -170,7 +173,7 @@ __device__ __forceinline__ void stage_hits_fo(Stage& st, u32 l, const u64 (&mask
   u32 run = st.n;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    if (hit[b]) st.buf[run + count_below(masks[b])] = fo_pack(key[b], l);
+    if (hit[b]) st.buf[run + count_below(masks[b])] = fo_pack(key[b], l, shift);
     run += (u32)__popcll(masks[b]);
   }
   st.n = run;
@@ -252,6 +255,7 @@ __device__ __forceinline__ void load_tile(const TileAt& t, f4 (&v)[U], bool (&va
 struct FoCtx {
   u32* cnt;
   const u32* lrow;
+  u32 shift;  // bits of N - 1: the position's place in the index word
 };
 
 // Stage one batch of hits of tile t (FO: with the tile's list position).
@@ -259,7 +263,7 @@ template <bool FO, int NB>
 __device__ __forceinline__ void stage_tile_hits(const FilterArgs& a, Stage& st, const FoCtx& fo, const TileAt& t,
                                                 const u64 (&masks)[NB], const bool (&hit)[NB], const u64 (&key)[NB]) {
   if constexpr (FO)
-    stage_hits_fo<NB>(st, t.lr, masks, hit, key, fo.lrow, a.ctls, a.cand, a.M);
+    stage_hits_fo<NB>(st, t.lr, masks, hit, key, fo.lrow, fo.shift, a.ctls, a.cand, a.M);
   else
     stage_hits<NB>(st, t.row, masks, hit, key, a.ctls, a.cand, a.M);
 }
@@ -413,7 +417,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   f4 va[U], vb[U];
   bool oka[U], okb[U];
   RowCache<FO> rc;
-  FoCtx fo{nullptr, nullptr};
+  FoCtx fo{nullptr, nullptr, 0u};
   if constexpr (FO) {
     // every listed row's index and threshold, and a counter per list position
     __shared__ u64 s_ltau[kFoRows];
@@ -429,6 +433,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     rc.ltau = s_ltau;
     fo.cnt = s_cnt;
     fo.lrow = s_lrow;
+    fo.shift = 32u - (u32)__clz((u32)(a.N - 1));  // N >= 2
   }
   const f4* safe = reinterpret_cast<const f4*>(a.ctls);
   if (cur.g < gend) {
@@ -462,16 +467,16 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     __syncthreads();
     for (u32 l = threadIdx.x; l < (u32)a.nrows; l += kFilterThreads) cnt[l] = 0;
     __syncthreads();
-    for (u32 j = lane; j < st.n; j += kWave) atomicAdd(&cnt[fo_list(st.buf[j])], 1u);
+    for (u32 j = lane; j < st.n; j += kWave) atomicAdd(&cnt[fo_list(st.buf[j], fo.shift)], 1u);
     __syncthreads();
     for (u32 l = threadIdx.x; l < (u32)a.nrows; l += kFilterThreads)
       if (cnt[l]) cnt[l] = (u32)atomicAdd(&a.ctls[fo.lrow[l]].R, (u64)cnt[l]);  // R < 2^32: rows of <= 2^20
     __syncthreads();
     for (u32 j = lane; j < st.n; j += kWave) {
       const u64 p = st.buf[j];
-      const u32 l = fo_list(p);
+      const u32 l = fo_list(p, fo.shift);
       const u64 pos = atomicAdd(&cnt[l], 1u);
-      if (pos < a.M) a.cand[(u64)fo.lrow[l] * a.M + pos] = fo_unpack(p);
+      if (pos < a.M) a.cand[(u64)fo.lrow[l] * a.M + pos] = fo_unpack(p, fo.shift);
     }
   } else {
   // End of the stream: the block's waves reserve their staged keys with one
@@ -658,7 +663,9 @@ hipError_t launch_filter_shape(const FilterArgs& a0, u32 grid, u32 blocks_per_cu
   // wavefront gets about four (16 rows of 2^22 values are only 256 chunks of 64 tiles,
   // which would leave most wavefronts idle); rows of at most 2^20 values, up to
   // kFoRows of them, are read in the flat pass's order instead (FO)
-  const bool fo = a.nrows > 1 && a.nrows <= kFoRows && a.N <= kFoMaxN &&
+  // positions fit above the index: bits(N - 1) + bits(nrows - 1) <= 32
+  auto bits = [](u64 v) { u32 b = 0; while (v) { ++b; v >>= 1; } return b; };
+  const bool fo = a.nrows > 1 && a.nrows <= kFoRows && a.N >= 2 && bits(a.N - 1) + bits(a.nrows - 1) <= 32 &&
                   a.hits_per_row * (double)a.nrows <= 0.8 * kStageCap * (double)grid * kWavesPerBlock;
   a.run = 1;
   if (a.nrows > 1 && !fo) {
