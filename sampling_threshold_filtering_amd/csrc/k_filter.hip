@@ -16,6 +16,11 @@
 //   * Compaction: ballot + mbcnt give each hit its slot; hits are staged in a
 //     per-wavefront LDS ring (512 keys) and flushed with ONE global atomic on the
 //     row counter per flush, so dense tiles cost one atomic per ~512 hits.
+//   * Several rows (the batched form): up to 1024 rows whose list positions fit in the
+//     index word above the index are read in the flat order too (FO), their thresholds
+//     from an LDS copy of the row list; staged keys carry their row's position, and the
+//     block places them at the end of the stream with one atomic per row it holds.
+//     Other row sets are read in chunks of up to 64 tiles, flushing at row changes.
 //   * The last block to finish (ticket) evaluates k <= R <= M per row, writes the
 //     host-visible record, and arms the refinement selection of each row.
 #include "launch.h"
