@@ -290,6 +290,35 @@ __device__ __forceinline__ void test_tile(const FilterArgs& a, Stage& st, const 
     maybe |= mu[u];
   }
   if (__ballot(maybe)) {
+    // candidate components of this lane (passing the pre-test), bit 4u + q
+    u32 cm = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      cm |= (u32)(valid[u] && !(v[u].x < tv)) << (4 * u);
+      cm |= (u32)(valid[u] && !(v[u].y < tv)) << (4 * u + 1);
+      cm |= (u32)(valid[u] && !(v[u].z < tv)) << (4 * u + 2);
+      cm |= (u32)(valid[u] && !(v[u].w < tv)) << (4 * u + 3);
+    }
+    if (!__ballot((cm & (cm - 1u)) != 0u)) {
+      // no lane holds two candidates (all but about 1% of the tiles with any at 1.25 hits
+      // per tile): each lane picks its candidate with selects, and one batch stages them
+      const bool has = cm != 0u;
+      const u32 e = has ? (u32)__builtin_ctz(cm) : 0u;
+      const u32 eu = e >> 2, eq = e & 3u;
+      f4 vs = v[0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) vs = eu == (u32)u ? v[u] : vs;
+      const float c = eq == 0u ? vs.x : eq == 1u ? vs.y : eq == 2u ? vs.z : vs.w;
+      const u32 o = ord32(__float_as_uint(c));
+      const u32 i = (u32)(t.geo.head + 4 * (t.v0 + (u64)eu * kWave + lane)) + eq;
+      u64 masks[1];
+      bool hit[1];
+      u64 key[1];
+      hit[0] = has && (o > tk || (o == tk && i <= ti));
+      key[0] = ((u64)o << 32) | (u64)(~i);
+      masks[0] = __ballot(hit[0]);
+      stage_tile_hits<FO, 1>(a, st, fo, t, masks, hit, key);
+    } else {
     // exact test only for the float4 slots, and within them the components, where some
     // lane may hold a hit: when hits are dense (one in a few hundred values) a slot
     // usually has one such component, and the exact keys of the other three would
@@ -313,6 +342,7 @@ __device__ __forceinline__ void test_tile(const FilterArgs& a, Stage& st, const 
         masks[0] = __ballot(hit[0]);
         stage_tile_hits<FO, 1>(a, st, fo, t, masks, hit, key);
       }
+    }
     }
   }
   if (t.tile == 0 && (t.geo.head | t.geo.tail)) {
