@@ -423,9 +423,11 @@ __device__ inline u64 lds_select_desc(const u64* s, u32 n, u32 rank, LdsSelect* 
 }
 
 // The same selection with the keys in registers: thread t holds v[0..P), zero for no
-// key.  A pass then reads no keys, it only counts digits.
-template <u32 P>
-__device__ inline u64 reg_select_desc(const u64 (&v)[P], u32 rank, LdsSelect* L) {
+// key.  A pass then reads no keys, it only counts digits.  `after_begin` runs once, by
+// every thread, after the first barrier (a caller's independent work, such as loads it
+// wants issued while the select runs).
+template <u32 P, class Hook>
+__device__ inline u64 reg_select_desc(const u64 (&v)[P], u32 rank, LdsSelect* L, Hook&& after_begin) {
   const u32 lane = opaque_u32(threadIdx.x) & (kWave - 1);
   u64 va = ~0ull, vo = 0;
   u32 nz = 0;
@@ -437,6 +439,7 @@ __device__ inline u64 reg_select_desc(const u64 (&v)[P], u32 rank, LdsSelect* L)
     nz += h ? 1u : 0u;
   }
   SelPass p = sel_begin(va, vo, nz, rank, L);
+  after_begin();
   for (u32 d = p.d0; d < 8 && p.state == 0; ++d) {
     sel_clear_hist(L);
     const u32 shift = 56u - 8u * d;
@@ -458,6 +461,11 @@ __device__ inline u64 reg_select_desc(const u64 (&v)[P], u32 rank, LdsSelect* L)
       }
   }
   return sel_finish(p, L);
+}
+
+template <u32 P>
+__device__ inline u64 reg_select_desc(const u64 (&v)[P], u32 rank, LdsSelect* L) {
+  return reg_select_desc(v, rank, L, [] {});
 }
 
 // Convenience: the whole selection from scratch.

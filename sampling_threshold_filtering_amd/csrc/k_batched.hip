@@ -384,11 +384,11 @@ __device__ __forceinline__ void pipe_wait(const PipeRow& p) {
 // S), so the top-up keys, staged in L.list, fill empty slots: a block-wide scan of the
 // empty slots gives each thread its range of L.list, and one register radix select over
 // the slots gives tau.
-// `mid` runs once the top-up is done, before the select (it issues the next row's
-// remaining gathers).
-template <class Mid>
+// `mid` runs once the top-up is done, before the select, and `late` inside the select
+// after its first barrier (they issue the next row's remaining gathers).
+template <class Mid, class Late>
 __device__ __forceinline__ void pipe_finish(const BatchedArgs& a, PipeRow& p, u32* T, PipeLds& L, u32 D0,
-                                            bool has_row, Mid&& mid) {
+                                            bool has_row, Mid&& mid, Late&& late) {
   // has_row is false (block-uniformly) in a workgroup's last step, whose row is the
   // loads of index 0 that stand in for a next row; mid() still runs, in the one place
   // both cases share, so that the wait analysis sees one path through the loads
@@ -461,9 +461,7 @@ __device__ __forceinline__ void pipe_finish(const BatchedArgs& a, PipeRow& p, u3
   }
   __syncthreads();
   mid();
-  if (!has_row) return;
-  const bool sample_ok = !L.fail && L.Dfin == a.S;
-  u64 tau = 0;
+  const bool sample_ok = has_row && !L.fail && L.Dfin == a.S;
   if (sample_ok) {
     const u32 E = (u32)(a.S - D0);
     // first empty slot of this thread in the block's order (wavefronts, then lanes)
@@ -474,10 +472,14 @@ __device__ __forceinline__ void pipe_finish(const BatchedArgs& a, PipeRow& p, u3
         if (e < E) key[q] = L.list[e];
         ++e;
       }
-    tau = reg_select_desc(key, (u32)a.t, &L.sel);
   } else {
-    __syncthreads();  // every thread has read L.fail and L.Dfin before they are reset
+#pragma unroll
+    for (u32 q = 0; q < kPipeDraws; ++q) key[q] = 0;  // no keys: the select returns 0
   }
+  // the select runs on every path (also with no row: its barriers order the reads of
+  // L.fail / L.Dfin before their reset, and `late` has one place)
+  const u64 tau = reg_select_desc(key, (u32)a.t, &L.sel, late);
+  if (!has_row) return;
   if (threadIdx.x == 0) {
     // the row's whole control block, as attempt_init leaves it, with tau and its status
     RowCtl c{};
@@ -521,11 +523,13 @@ __device__ __forceinline__ void pipe_step(const BatchedArgs& a, PipeLds& L, u32 
   // row's gathers are issued as soon as cur's have arrived, and cur's top-up and
   // threshold run while they are in flight.
   pipe_wait(cur);
-  // half of them now, the rest after cur's top-up: a wavefront that issues a load while
-  // the CU's request queue is full stalls, and with it every barrier of cur's select
-  pipe_gather<0, kPipeDraws / 2>(a, S2, L.T[c ^ 1u], &L.D[c ^ 1u], nxt);
-  pipe_finish(a, cur, L.T[c], L, D0, has_cur,
-              [&] { pipe_gather<kPipeDraws / 2, kPipeDraws>(a, S2, L.T[c ^ 1u], &L.D[c ^ 1u], nxt); });
+  // in three slices: now, after cur's top-up, and inside cur's select (a wavefront that
+  // issues a load while the CU's request queue is full stalls, and with it every
+  // barrier of the block)
+  pipe_gather<0, 1>(a, S2, L.T[c ^ 1u], &L.D[c ^ 1u], nxt);
+  pipe_finish(
+      a, cur, L.T[c], L, D0, has_cur, [&] { pipe_gather<1, 2>(a, S2, L.T[c ^ 1u], &L.D[c ^ 1u], nxt); },
+      [&] { pipe_gather<2, kPipeDraws>(a, S2, L.T[c ^ 1u], &L.D[c ^ 1u], nxt); });
 }
 
 __global__ __launch_bounds__(kBThreads) void b_sample_pipe_kernel(BatchedArgs a) {
