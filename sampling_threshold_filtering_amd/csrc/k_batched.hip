@@ -99,18 +99,24 @@ __device__ __forceinline__ void b_sample_fast_row(const BatchedArgs& a, u32 row,
     u32 guard = 0;
     while (D < a.S) {
       const u32 id2 = (u32)sample_draw(j0 + lane, row, a.attempt, a.seed, a.N);
-      const bool held = (s_bits[id2 >> 5] >> (id2 & 31u)) & 1u;
-      bool repeat = false;
-      for (int d = 1; d < kWave; ++d) {
-        const u32 other = __shfl_up(id2, d, kWave);
-        if ((int)lane >= d && other == id2) repeat = true;
+      // a draw whose bit another lane of this chunk set first repeats within the chunk;
+      // only then do the lanes compare indices (see pipe_finish)
+      const u32 bit = 1u << (id2 & 31u);
+      const bool held = (s_bits[id2 >> 5] & bit) != 0u;
+      const bool dup = !held && (atomicOr(&s_bits[id2 >> 5], bit) & bit) != 0u;
+      bool repeat = dup;
+      if (__ballot(dup)) {
+        repeat = false;
+        for (int d = 1; d < kWave; ++d) {
+          const u32 other = __shfl_up(id2, d, kWave);
+          if ((int)lane >= d && other == id2) repeat = true;
+        }
       }
       const bool ok2 = !held && !repeat;
       const u64 m2 = __ballot(ok2);
       const u64 need = a.S - D;
       const u32 r = count_below(m2);
       if (ok2 && r < need) {
-        atomicOr(&s_bits[id2 >> 5], 1u << (id2 & 31u));
         const u64 k2 = make_key(__float_as_uint(xr[id2]), id2);
         keys[a.S + (D - D0) + r] = k2;
         if ((D - D0) + r < kBThreads) s_list[(D - D0) + r] = k2;
@@ -219,18 +225,22 @@ __global__ __launch_bounds__(kBThreads) void b_sample_kernel(BatchedArgs a) {
       u32 guard = 0;
       while (D < a.S) {
         const u32 id2 = (u32)sample_draw(j0 + lane, row, a.attempt, a.seed, a.N);
-        const bool held = (s_bits[id2 >> 5] >> (id2 & 31u)) & 1u;
-        bool repeat = false;
-        for (int d = 1; d < kWave; ++d) {
-          const u32 other = __shfl_up(id2, d, kWave);
-          if ((int)lane >= d && other == id2) repeat = true;
+        const u32 bit = 1u << (id2 & 31u);
+        const bool held = (s_bits[id2 >> 5] & bit) != 0u;
+        const bool dup = !held && (atomicOr(&s_bits[id2 >> 5], bit) & bit) != 0u;
+        bool repeat = dup;
+        if (__ballot(dup)) {
+          repeat = false;
+          for (int d = 1; d < kWave; ++d) {
+            const u32 other = __shfl_up(id2, d, kWave);
+            if ((int)lane >= d && other == id2) repeat = true;
+          }
         }
         const bool ok2 = !held && !repeat;
         const u64 m2 = __ballot(ok2);
         const u64 need = a.S - D;
         const u32 r = count_below(m2);
         if (ok2 && r < need) {
-          atomicOr(&s_bits[id2 >> 5], 1u << (id2 & 31u));
           const u64 key2 = make_key(__float_as_uint(xr[id2]), id2);
           keys[D + r] = key2;
           atomicAdd(&s_sel.hist[key2 >> 56], 1u);
