@@ -77,10 +77,13 @@ Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap, 
                    u64 grid_tops = 0) {
   Layout L;
   // hash set of the sample: 16 slots per draw (up to 2^21 slots) keeps probes and
-  // contention on the device-scope CAS low; at least 2 per draw for larger samples
+  // contention on the device-scope CAS low; at least 2 per draw for larger samples, and
+  // room for the S indices plus a last top-up chunk's kWave new ones on top
   const u64 s1 = S ? S : 1;
   const u64 sparse = 16 * s1 < (1ull << 21) ? 16 * s1 : (1ull << 21);
-  L.hash_used = grid_rows ? pow2_at_least(4 * s1) : pow2_at_least(sparse > 2 * s1 ? sparse : 2 * s1);
+  const u64 least = 2 * s1 + kWave;
+  L.hash_used = grid_rows ? pow2_at_least(4 * s1 > least ? 4 * s1 : least)
+                          : pow2_at_least(sparse > least ? sparse : least);
   const u64 hash_need = L.hash_used * (grid_rows ? grid_rows : 1);
   L.hash_slots = hash_need < hash_cap ? hash_cap : hash_need;
   const u64 rows = B < rows_cap ? rows_cap : B;

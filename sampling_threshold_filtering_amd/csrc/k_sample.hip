@@ -235,18 +235,26 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a0) {
     bool failed = false;
     while (D + E < a.S) {
       const u32 idx2 = (u32)sample_draw(j0 + lane, a.row, a.attempt, a.seed, a.N);
+      // every new draw is inserted; one that finds its index inserted by another lane of
+      // this chunk repeats within the chunk, and only then (rare: 64^2 / 2N per chunk) do
+      // the lanes compare indices to find which of the equal draws came first.  The set
+      // then holds the chunk's new indices; those not taken can only be there when the
+      // chunk is the last one.
       const bool held = hash_contains(a.table, a.tmask, idx2);
-      bool repeat = false;
-      for (int d = 1; d < kWave; ++d) {
-        const u32 other = __shfl_up(idx2, d, kWave);
-        if ((int)lane >= d && other == idx2) repeat = true;
+      const bool dup = !held && !hash_insert(a.table, a.tmask, idx2);
+      bool repeat = dup;
+      if (__ballot(dup)) {
+        repeat = false;
+        for (int d = 1; d < kWave; ++d) {
+          const u32 other = __shfl_up(idx2, d, kWave);
+          if ((int)lane >= d && other == idx2) repeat = true;
+        }
       }
       const bool ok2 = !held && !repeat;
       const u64 m2 = __ballot(ok2);
       const u64 need = a.S - D - E;
       const u32 r = count_below(m2);
       if (ok2 && r < need) {
-        hash_insert(a.table, a.tmask, idx2);
         const u64 key2 = make_key(__float_as_uint(a.x[idx2]), idx2);
         a.keys[a.S + E + r] = key2;
         if (staged && nbase + E + r < kTauCap) s_buf[nbase + E + r] = key2;
