@@ -132,3 +132,22 @@ def test_batched_long_rows(kind, B, N, k, pad):
     print("[case] stats", {kk: st[kk] for kk in ("S", "t", "M", "attempts", "rows_retried", "rows_fallback")},
           flush=True)
     check_batched(np.ascontiguousarray(full[:, :N]), vals, idx, k)
+
+
+@pytest.mark.parametrize("B,N,k", [(64, 1 << 18, 64), (512, 1 << 16, 32)])
+def test_batched_rows_whose_hits_overflow_the_filter_stage(B, N, k):
+    """Rows read in the flat order (several rows, positions packed above the index bits)
+    stage every wavefront's hits until the end of the stream.  In a row of equal values the
+    keys order by index, so the entries at or above tau are the row's first R: whole tiles
+    of hits, 1024 per tile, which fill a wavefront's stage and send each further batch
+    straight to the row's buffer (a row whose first half holds one value that tops the
+    rest does the same).  Every row must match the oracle."""
+    x = generate("normal", B * N, seed=B + N).reshape(B, N)
+    for r in (3, B // 2, B - 1):
+        x[r, :] = np.float32(0.5)  # all ties: tau is decided by the index
+    x[B // 2 + 1, : N // 2] = np.float32(1e30)  # the top values: the row's first half
+    say("batched stage overflow", B, N, k)
+    vals, idx, st = stf.topk_batched(dev(x), k, seed=7, stats=True)
+    print("[case] stats", {kk: st[kk] for kk in ("S", "t", "M", "attempts", "rows_retried", "rows_fallback")},
+          flush=True)
+    check_batched(x, vals, idx, k)
