@@ -47,6 +47,9 @@ constexpr int kDefaultAttempts = 6;  // P1 §3 stage 4: exact fallback after six
 // kernel; a larger one (a tie group of that size within a wide value range) is left to
 // the multi-block radix select, which the host enqueues after reading the flag.
 constexpr u32 kMsdCapExact = 1u << 18;
+// Bound on the fused histogram-and-scatter launch's wait for all of its blocks: 0.25 s of
+// the 100 MHz clock (the wait itself takes microseconds when every block is resident).
+constexpr u64 kRefineWaitTicks = 25000000;
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -58,7 +61,7 @@ u64 pow2_at_least(u64 v) {
 
 struct Layout {
   size_t hash = 0, ctl = 0, sel = 0, rec = 0, rtick = 0, ticket = 0, keys = 0, tops = 0, btops = 0, cand = 0, col = 0,
-         topk0 = 0, topk1 = 0, hist = 0, rows = 0, scratch = 0, rtmp = 0, rhist = 0, rbin_off = 0, rbin_cnt = 0,
+         topk0 = 0, topk1 = 0, hist = 0, rows = 0, scratch = 0, rtmp = 0, rhist = 0, rchunk = 0,
          rcursor = 0, pool = 0, total = 0;
   u64 hash_slots = 0;  // slots of the hash region (the allocation's capacity)
   u64 rows_cap = 0;    // rows of the control regions (the allocation's capacity)
@@ -101,8 +104,6 @@ Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap, 
   L.rtick = take(rows * sizeof(u64));  // per-row sampling tickets of the batched sampler
   L.ticket = take(kTicketWords * sizeof(u32));
   L.rhist = take(kBins * sizeof(u32));
-  L.rbin_off = take(kBins * sizeof(u32));
-  L.rbin_cnt = take(kBins * sizeof(u32));
   L.rcursor = take(kBins * sizeof(u32));
   L.tops = take((size_t)kTopBlocks * kTopT * sizeof(u64));
   // per request
@@ -116,6 +117,7 @@ Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap, 
   L.rows = take(B * sizeof(int));
   L.scratch = take((scratch_words ? scratch_words : 1) * sizeof(u64));
   L.rtmp = take((M ? M : 1) * sizeof(u64));
+  L.rchunk = take(chunk_entries(M) * 4 * sizeof(u32));
   L.pool = take(msd_pool_words(M) * sizeof(u64));
   L.total = off;
   return L;
@@ -407,8 +409,7 @@ RefineArgs refine_args(Workspace* w, const Layout& L, const float* x, u64 N, u64
   ra.x = x;
   ra.tmp = at<u64>(w, L.rtmp);
   ra.hist = at<u32>(w, L.rhist);
-  ra.bin_off = at<u32>(w, L.rbin_off);
-  ra.bin_cnt = at<u32>(w, L.rbin_cnt);
+  ra.chunk = at<u32>(w, L.rchunk);
   ra.cursor = at<u32>(w, L.rcursor);
   ra.table = at<u32>(w, L.hash);
   ra.table_slots = L.hash_used;
@@ -416,6 +417,7 @@ RefineArgs refine_args(Workspace* w, const Layout& L, const float* x, u64 N, u64
   ra.out_idx = out_idx;
   ra.pool = at<u64>(w, L.pool);
   ra.ticket = at<u32>(w, L.ticket) + kTicketRefine;
+  ra.wait_ticks = kRefineWaitTicks;
   return ra;
 }
 

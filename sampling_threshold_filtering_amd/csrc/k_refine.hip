@@ -2,32 +2,36 @@
 // Selection", §3 stage 4): the exact top-k of the R buffered candidates, sorted.
 // The pages call a library top-k here (App. C).  For k <= kSmallK one launch does it
 // (refine_small_kernel, below: per-workgroup top-k lists and a select over their union
-// by the last workgroup).  Larger k take a binned refinement for gfx950 in three
-// launches:
+// by the last workgroup).  Larger k take a binned refinement for gfx950:
 //
 //   refine_hist_kernel     histogram of the candidates over kBins equal bins of the
 //                          key range [tau, cmax] (cmax = the largest candidate key,
 //                          tracked by the filter), added into a global histogram.
 //   refine_scatter_kernel  every block scans the global histogram from the top bin
 //                          down in LDS: the bin b* that holds the k-th largest
-//                          candidate and the output offset of every bin >= b*
-//                          (block 0 publishes them).  If one of those bins holds more
-//                          keys than one workgroup sorts in LDS (ties, narrow-range
-//                          inputs), the row is marked for the multi-pass refinement
-//                          instead.  Otherwise each block writes its candidates of
-//                          bins >= b* into bin order: one global atomic per (block,
-//                          bin) reserves the run, LDS atomics place the keys.  Block 0
-//                          also publishes the attempt record (R, check, multi-pass
-//                          flag) to the host, which needs nothing later to decide.
-//   refine_binsort_kernel  sorts every bin >= b* (four 256-thread workgroups per CU:
-//                          one wavefront in registers up to kWaveMax keys, a workgroup
-//                          up to kBinCap by one 8-bit counting pass in LDS) and writes
-//                          out_vals / out_idx for positions < k.  A larger bin (large
-//                          tie groups, narrow ranges) is partitioned by one workgroup
-//                          on successive 12-bit digits of (key - tau), from the top
-//                          down, until every part that reaches a position below k fits
-//                          those sorts.  It also leaves the histogram and the
-//                          sampler's hash set zero for the next attempt.
+//                          candidate and the output offset of every bin >= b*.  If one
+//                          of those bins holds more keys than one workgroup sorts in
+//                          LDS (ties, narrow-range inputs), the row is marked for the
+//                          multi-pass refinement instead.  Otherwise each block writes
+//                          its candidates of bins >= b* into bin order: one global
+//                          atomic per (block, bin) reserves the run, LDS atomics place
+//                          the keys.  Block 0 also publishes the attempt record (R,
+//                          check, multi-pass flag) to the host, which needs nothing
+//                          later to decide, and the bin sort's chunk boundaries.
+//   refine_bin_kernel      exact mode: the two above in one launch (the histogram's
+//                          atomics return each block's run start in its bins; one
+//                          launch-wide wait between counting and placing).
+//   refine_binsort_kernel  sorts every bin >= b* (256-thread workgroups, at least four
+//                          per CU; each wavefront the bins that start in its equal
+//                          share of the output positions, in registers up to kWaveMax
+//                          keys, a workgroup a bin up to kBinCap by one 8-bit counting
+//                          pass in LDS) and writes out_vals / out_idx for positions
+//                          < k.  A larger bin (large tie groups, narrow ranges) is
+//                          partitioned by one workgroup on successive 12-bit digits of
+//                          (key - tau), from the top down, until every part that
+//                          reaches a position below k fits those sorts.  It also
+//                          leaves the histogram and the sampler's hash set zero for
+//                          the next attempt.
 // Bins larger than RefineArgs::msd_cap are instead left to the multi-pass refinement,
 // which the host enqueues after reading the flag (exact mode only).
 // Bins partition the keys by value, so sorted bins laid out from the top bin down
@@ -125,30 +129,58 @@ __global__ __launch_bounds__(kHistThreads) void refine_hist_kernel(RefineArgs a)
     if (s_h[b]) atomicAdd(&a.hist[b], s_h[b]);
 }
 
-__global__ __launch_bounds__(kHistThreads) void refine_scatter_kernel(RefineArgs a) {
-  __shared__ u32 s_off[kBins + kBins / kPer + 1];  // by padded descending position; last = total
-  __shared__ u32 s_pos[kBins];
-  __shared__ u32 s_wsum[kHistThreads / kWave];
-  __shared__ u32 s_q, s_big;
-  RowCtl* c = a.ctl;
-  if (!refine_live(a, c)) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) publish(a, c, 0u);
-    return;
+namespace {
+struct ScanLds {
+  u32 off[kBins + kBins / kPer + 1];  // by padded descending position; last = total
+  u32 wsum[kHistThreads / kWave];
+  u32 q, big;
+};
+
+// The bin sort's chunk boundaries from the scan in LDS (every block holds it whole), split
+// over the blocks by bin: boundary m gets the bin that holds output position m P - 1
+// (P = ceil(T / W) for the T keys of the bins >= b*), written by the thread of that bin.
+__device__ void write_chunks(const RefineArgs& a, const ScanLds* S, u32 qstar) {
+  const u32 T = S->off[pad_q(qstar + 1)];
+  const u32 W = a.sort_waves;
+  const u32 P = T > W ? (T + W - 1) / W : 1u;
+  const u64 inv = ((1ull << 32) + P - 1) / P;
+  auto chunk_of = [&](u32 e) {  // floor(e / P) by a multiply, corrected
+    u32 m = (u32)(((u64)e * inv) >> 32);
+    if ((u64)m * P > e) --m;
+    if ((u64)(m + 1) * P <= e) ++m;
+    return m;
+  };
+  uint4* ch = reinterpret_cast<uint4*>(a.chunk);
+  const u32 per = (qstar + gridDim.x) / gridDim.x;  // bins 0..qstar per block
+  for (u32 q = blockIdx.x * per + threadIdx.x; q < (blockIdx.x + 1) * per && q <= qstar; q += blockDim.x) {
+    const u32 e = S->off[pad_q(q)], f = S->off[pad_q(q + 1)];
+    if (f == e) continue;
+    const u32 mf = chunk_of(f), m2 = mf < W ? mf : W;
+    for (u32 m = chunk_of(e) + 1; m <= m2; ++m) ch[m] = make_uint4(e, f, q, 0u);
   }
+  for (u32 m = (T + P) / P + blockIdx.x * blockDim.x + threadIdx.x; m <= W; m += gridDim.x * blockDim.x)
+    ch[m] = make_uint4(T, T, qstar + 1u, 0u);
+  if (blockIdx.x == 0 && threadIdx.x == 0) ch[0] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Every block of the scatter: the global histogram (loaded by ld(b)) scanned from the top
+// bin down in LDS, the bin b* that holds the k-th largest candidate (returned as its
+// descending position q*) and whether a bin at or above it is too large for the in-kernel
+// sorts (then the attempt takes the multi-pass refinement).  Block 0 publishes b* and
+// the record.  Returns true for the multi-pass case.
+template <class Load>
+__device__ bool bin_scan(const RefineArgs& a, RowCtl* c, u32 shift, Load&& ld, ScanLds* S, u32* qstar_out) {
   const u32 tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
-  const u64 n = cand_count(c, a.M);
-  const u64 tau = c->tau;
-  const u32 shift = bin_shift_of(c);
   {
     u32 v[kPer];  // all loads in flight, then the LDS stores
 #pragma unroll
-    for (u32 j = 0; j < kPer; ++j) v[j] = a.hist[j * kHistThreads + tid];
+    for (u32 j = 0; j < kPer; ++j) v[j] = ld(j * kHistThreads + tid);
 #pragma unroll
-    for (u32 j = 0; j < kPer; ++j) s_off[pad_q(kBins - 1u - (j * kHistThreads + tid))] = v[j];
+    for (u32 j = 0; j < kPer; ++j) S->off[pad_q(kBins - 1u - (j * kHistThreads + tid))] = v[j];
   }
   if (tid == 0) {
-    s_q = 0xFFFFFFFFu;
-    s_big = 0;
+    S->q = 0xFFFFFFFFu;
+    S->big = 0;
   }
   __syncthreads();
   // exclusive offsets over descending positions: thread tid owns q = tid*kPer + j
@@ -156,7 +188,7 @@ __global__ __launch_bounds__(kHistThreads) void refine_scatter_kernel(RefineArgs
   u32 sum = 0;
 #pragma unroll
   for (u32 j = 0; j < kPer; ++j) {
-    cnt[j] = s_off[pad_q(tid * kPer + j)];
+    cnt[j] = S->off[pad_q(tid * kPer + j)];
     sum += cnt[j];
   }
   u32 incl = sum;
@@ -165,46 +197,58 @@ __global__ __launch_bounds__(kHistThreads) void refine_scatter_kernel(RefineArgs
     const u32 v = __shfl_up(incl, d);
     if (lane >= d) incl += v;
   }
-  if (lane == kWave - 1) s_wsum[wid] = incl;
+  if (lane == kWave - 1) S->wsum[wid] = incl;
   __syncthreads();
   u32 run = incl - sum;
-  for (u32 w = 0; w < wid; ++w) run += s_wsum[w];
+  for (u32 w = 0; w < wid; ++w) run += S->wsum[w];
   const u64 k = a.k;
 #pragma unroll
   for (u32 j = 0; j < kPer; ++j) {
     const u32 q = tid * kPer + j;
-    s_off[pad_q(q)] = run;
-    if (run < k && run + cnt[j] >= k) s_q = q;  // exactly one bin holds the k-th largest
+    S->off[pad_q(q)] = run;
+    if (run < k && run + cnt[j] >= k) S->q = q;  // exactly one bin holds the k-th largest
     run += cnt[j];
   }
-  if (tid == blockDim.x - 1) s_off[pad_q(kBins)] = run;
+  if (tid == blockDim.x - 1) S->off[pad_q(kBins)] = run;
   __syncthreads();
   // fewer than k candidates (approximate mode only): every bin is needed
-  const u32 qstar = s_q == 0xFFFFFFFFu && a.approx ? kBins - 1u : s_q;
+  const u32 qstar = S->q == 0xFFFFFFFFu && a.approx ? kBins - 1u : S->q;
   // every bin at or above b* must fit the in-kernel sorts and partition
   bool big = qstar == 0xFFFFFFFFu;
 #pragma unroll
   for (u32 j = 0; j < kPer; ++j)
     if (tid * kPer + j <= qstar && cnt[j] > a.msd_cap) big = true;
-  if (big) s_big = 1;
+  if (big) S->big = 1;
   __syncthreads();
-  const bool generic = s_big != 0;
-  if (blockIdx.x == 0) {
-    if (!generic)
-      for (u32 q = tid; q <= qstar; q += blockDim.x) {
-        const u32 b = kBins - 1u - q;
-        a.bin_off[b] = s_off[pad_q(q)];
-        a.bin_cnt[b] = s_off[pad_q(q + 1)] - s_off[pad_q(q)];
-      }
-    if (tid == 0) {
-      c->bin_shift = shift;
-      c->bstar = generic ? 0u : kBins - 1u - qstar;
-      c->c_above = generic ? 0u : s_off[pad_q(qstar)];
-      c->generic = generic ? 1u : 0u;
-      if (a.rec) a.rec->generic = generic ? 1u : 0u;
-      publish(a, c, generic ? 1u : 0u);
-    }
+  const bool generic = S->big != 0;
+  if (blockIdx.x == 0 && tid == 0) {
+    c->bin_shift = shift;
+    c->bstar = generic ? 0u : kBins - 1u - qstar;
+    c->c_above = generic ? 0u : S->off[pad_q(qstar)];
+    c->generic = generic ? 1u : 0u;
+    if (a.rec) a.rec->generic = generic ? 1u : 0u;
+    publish(a, c, generic ? 1u : 0u);
   }
+  *qstar_out = qstar;
+  return generic;
+}
+}  // namespace
+
+__global__ __launch_bounds__(kHistThreads) void refine_scatter_kernel(RefineArgs a) {
+  __shared__ ScanLds s_scan;
+  __shared__ u32 s_pos[kBins];
+  RowCtl* c = a.ctl;
+  if (!refine_live(a, c)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) publish(a, c, 0u);
+    return;
+  }
+  const u32 tid = threadIdx.x;
+  const u64 n = cand_count(c, a.M);
+  const u64 tau = c->tau;
+  const u32 shift = bin_shift_of(c);
+  u32 qstar;
+  const bool generic = bin_scan(a, c, shift, [&](u32 b) { return a.hist[b]; }, &s_scan, &qstar);
+  const u32* s_off = s_scan.off;
   if (generic) return;
   const u32 bstar = kBins - 1u - qstar;
 
@@ -260,6 +304,151 @@ __global__ __launch_bounds__(kHistThreads) void refine_scatter_kernel(RefineArgs
       }
     }
   }
+  write_chunks(a, &s_scan, qstar);
+}
+
+namespace {
+constexpr u32 kGridMark = 1u << 30;
+constexpr u32 kKeep = 16;  // candidates per thread refine_bin_kernel keeps in registers  // added to the launch-wide counter when a wait ran out
+
+// Thread 0 of each block: arrive at the launch-wide counter ctr (zero on entry) and wait
+// until all G blocks have.  A wait longer than `limit` ticks of the 100 MHz clock (a
+// block could not be made resident) marks the counter, which only succeeds while some
+// block has not arrived, so no block can have passed it yet; every block then sees the
+// mark, the late ones in the value their own arrival returns.  True: all arrived.
+__device__ bool grid_wait(u32* ctr, u32 G, u64 limit) {
+  u32 v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  const u64 t0 = wall_clock64();
+  while (v < G) {
+    if (wall_clock64() - t0 >= limit) {
+      u32 seen = v;
+      if (__hip_atomic_compare_exchange_strong(ctr, &seen, v + kGridMark, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        return false;
+      v = seen;
+      continue;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    v = atomic_load_agent(ctr);
+  }
+  return v < kGridMark;
+}
+}  // namespace
+
+// Exact mode: the histogram and the scatter in one launch.  Each block counts its
+// contiguous share of the candidates per bin in LDS and adds the counts into the global
+// histogram with returning atomics: the value each returns is where the block's run
+// starts within that bin, so no second reservation is needed.  The blocks then wait for
+// each other once (a counter in the workspace; at most one 1024-thread block per two
+// CUs, so all are resident), scan the finished histogram as refine_scatter_kernel does
+// and place their candidates of the bins >= b*.  A wait that runs out (a.wait_ticks)
+// sends the attempt to the multi-pass refinement instead, before any block has placed a
+// key.  The bin sort clears the counter.
+__global__ __launch_bounds__(kHistThreads) void refine_bin_kernel(RefineArgs a) {
+  __shared__ ScanLds s_scan;
+  __shared__ u32 s_pos[kBins];  // this block's count per bin, then its next position in it
+  __shared__ u32 s_ok;
+  RowCtl* c = a.ctl;
+  if (!refine_live(a, c)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) publish(a, c, 0u);
+    return;
+  }
+  const u32 tid = threadIdx.x;
+  const u64 n = cand_count(c, a.M);
+  const u64 tau = c->tau;
+  const u32 shift = bin_shift_of(c);
+  for (u32 b = tid; b < kBins; b += kHistThreads) s_pos[b] = 0;
+  __syncthreads();
+  u64 lo, hi;
+  block_range(n, &lo, &hi);
+  // a share of up to kKeep keys per thread stays in registers until the placement, with
+  // each key's rank among the block's keys of its bin (from the counting atomic)
+  const bool kept = hi - lo <= (u64)kKeep * kHistThreads;
+  u64 kk[kKeep];
+  u32 rk[kKeep];
+  if (kept) {
+#pragma unroll
+    for (u32 q = 0; q < kKeep; ++q) {
+      const u64 i = lo + (u64)q * kHistThreads + tid;
+      kk[q] = i < hi ? a.cand[i] : 0ull;
+    }
+#pragma unroll
+    for (u32 q = 0; q < kKeep; ++q)
+      rk[q] = lo + (u64)q * kHistThreads + tid < hi ? atomicAdd(&s_pos[bin_of(kk[q], tau, shift)], 1u) : 0u;
+  } else {
+    for (u64 base = lo; base < hi; base += (u64)kHistThreads * kILP) {
+      u64 kl[kILP];
+#pragma unroll
+      for (u32 q = 0; q < kILP; ++q) {
+        const u64 i = base + (u64)q * kHistThreads + tid;
+        kl[q] = i < hi ? a.cand[i] : 0ull;
+      }
+#pragma unroll
+      for (u32 q = 0; q < kILP; ++q)
+        if (base + (u64)q * kHistThreads + tid < hi) atomicAdd(&s_pos[bin_of(kl[q], tau, shift)], 1u);
+    }
+  }
+  __syncthreads();
+  {
+    // all of this thread's atomics in flight together; storing their results waits for
+    // them, so they are complete at the barrier below
+    u32 m[kPer], got[kPer];
+#pragma unroll
+    for (u32 j = 0; j < kPer; ++j) m[j] = s_pos[j * kHistThreads + tid];
+#pragma unroll
+    for (u32 j = 0; j < kPer; ++j) got[j] = m[j] ? atomicAdd(&a.hist[j * kHistThreads + tid], m[j]) : 0u;
+#pragma unroll
+    for (u32 j = 0; j < kPer; ++j) s_pos[j * kHistThreads + tid] = got[j];
+  }
+  __syncthreads();
+  if (tid == 0) s_ok = grid_wait(a.ticket, gridDim.x, a.wait_ticks) ? 1u : 0u;
+  __syncthreads();
+  if (!s_ok) {
+    if (blockIdx.x == 0 && tid == 0) {
+      c->bin_shift = shift;
+      c->bstar = 0;
+      c->c_above = 0;
+      c->generic = 1;
+      if (a.rec) a.rec->generic = 1u;
+      publish(a, c, 1u);
+    }
+    return;
+  }
+  u32 qstar;
+  const bool generic = bin_scan(a, c, shift, [&](u32 b) { return atomic_load_agent(&a.hist[b]); }, &s_scan, &qstar);
+  if (generic) return;
+  const u32 bstar = kBins - 1u - qstar;
+  for (u32 b = bstar + tid; b < kBins; b += kHistThreads) s_pos[b] += s_scan.off[pad_q(kBins - 1u - b)];
+  __syncthreads();
+  if (kept) {
+#pragma unroll
+    for (u32 q = 0; q < kKeep; ++q) {
+      const u32 b = bin_of(kk[q], tau, shift);
+      if (lo + (u64)q * kHistThreads + tid < hi && b >= bstar) {
+        const u32 pos = s_pos[b] + rk[q];
+        if (pos < a.M) a.tmp[pos] = kk[q];
+      }
+    }
+    write_chunks(a, &s_scan, qstar);  // for the next launch, off this launch's critical path
+    return;
+  }
+  for (u64 base = lo; base < hi; base += (u64)kHistThreads * kILP) {
+    u64 kl[kILP];
+#pragma unroll
+    for (u32 q = 0; q < kILP; ++q) {
+      const u64 i = base + (u64)q * kHistThreads + tid;
+      kl[q] = i < hi ? a.cand[i] : 0ull;
+    }
+#pragma unroll
+    for (u32 q = 0; q < kILP; ++q) {
+      const u32 b = bin_of(kl[q], tau, shift);
+      if (base + (u64)q * kHistThreads + tid < hi && b >= bstar) {
+        const u32 pos = atomicAdd(&s_pos[b], 1u);
+        if (pos < a.M) a.tmp[pos] = kl[q];
+      }
+    }
+  }
+  write_chunks(a, &s_scan, qstar);
 }
 
 #ifndef PROFK_WAVE_MAX
@@ -321,6 +510,90 @@ __device__ __forceinline__ void light_sort(const RefineArgs& a, const u64 (&v)[4
     const u32 i = (u32)r * kWave + lane;
     if (i < n && out0 + i < a.k) write_out(a, out0 + i, w[r]);
   }
+}
+
+constexpr u32 kTieCap = 16;  // largest digit bucket wave_range_sort ranks by comparisons
+constexpr u32 kWaveLds = 8 * kWave;  // u64 words of LDS per wavefront: 256 keys, counts, starts
+
+// A range of kWave < n <= R kWave keys (v[r], element r*64 + lane) sorted by one
+// wavefront and written from output position out0: one counting pass on an 8-bit digit
+// of g = (key - tau) >> sub (g is monotone in the key), scaled to the range's span of g,
+// then each key's position is its digit bucket's start plus the number of larger keys
+// in the bucket.  About 250 instructions for 256 keys against some 1350 for the
+// register bitonic sort.  Returns false, writing nothing, when a bucket holds more than
+// kTieCap keys (runs of near-equal values).  w: the wavefront's kWaveLds words of LDS.
+// (Bins of 257..512 keys sorted this way, 8 keys per lane in twice the LDS, measured no
+// faster than the workgroup's counting pass.)
+template <int R>
+__device__ bool wave_range_sort(const RefineArgs& a, const u64 (&v)[R], u32 n, u64 out0, u64 tau, u32 sub, u64* w) {
+  static_assert(R * kWave + 2 * 2 * kWave <= kWaveLds, "keys, counts and starts fit the wavefront's LDS");
+  const u32 lane = lane_id();
+  u32* cnt = reinterpret_cast<u32*>(w + 4 * kWave);
+  u32* beg = cnt + 4 * kWave;
+  u32 g[R];
+  bool ok[R];
+  u32 gmin = 0xFFFFFFFFu, gmax = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    ok[r] = (u32)r * kWave + lane < n;
+    g[r] = (u32)((v[r] - tau) >> sub);
+    if (ok[r]) {
+      gmin = g[r] < gmin ? g[r] : gmin;
+      gmax = g[r] > gmax ? g[r] : gmax;
+    }
+  }
+  gmin = wave_reduce_u32(gmin, [](u32 x, u32 y) { return x < y ? x : y; });
+  gmax = wave_reduce_u32(gmax, [](u32 x, u32 y) { return x > y ? x : y; });
+  const u32 span = gmax - gmin;
+  const u32 extra = span < 256u ? 0u : 24u - (u32)__clz(span);  // (span >> extra) < 256
+#pragma unroll
+  for (u32 j = 0; j < 4; ++j) cnt[4 * lane + j] = 0;
+  wave_lds_sync();
+  u32 d[R], rk[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    d[r] = ok[r] ? (g[r] - gmin) >> extra : 0u;
+    rk[r] = ok[r] ? atomicAdd(&cnt[d[r]], 1u) : 0u;
+  }
+  wave_lds_sync();
+  // bucket starts over descending digits: lane owns digits 255 - 4 lane - j
+  u32 c[4], sum = 0, cm = 0;
+#pragma unroll
+  for (u32 j = 0; j < 4; ++j) {
+    c[j] = cnt[255u - 4 * lane - j];
+    sum += c[j];
+    cm = c[j] > cm ? c[j] : cm;
+  }
+  u32 run = wave_incl_scan_add(sum, lane) - sum;
+#pragma unroll
+  for (u32 j = 0; j < 4; ++j) {
+    beg[255u - 4 * lane - j] = run;
+    run += c[j];
+  }
+  const u32 maxb = wave_reduce_u32(cm, [](u32 x, u32 y) { return x > y ? x : y; });
+  wave_lds_sync();
+  if (maxb > kTieCap) return false;
+  u32 b0[R], bc[R], gt[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    b0[r] = beg[d[r]];
+    bc[r] = ok[r] ? cnt[d[r]] : 0u;
+    gt[r] = 0;
+    if (ok[r]) w[b0[r] + rk[r]] = v[r];
+  }
+  wave_lds_sync();
+  for (u32 it = 0; it < maxb; ++it) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (it < bc[r]) gt[r] += w[b0[r] + it] > v[r] ? 1u : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const u64 p = out0 + b0[r] + gt[r];
+    if (ok[r] && p < a.k) write_out(a, p, v[r]);
+  }
+  wave_lds_sync();  // the next range reuses w
+  return true;
 }
 
 // A part of cnt <= kBinCap keys at src[start..), sorted by the workgroup in LDS.
@@ -547,23 +820,34 @@ __device__ void msd_bin(const RefineArgs& a, u64* s, u32 b, u32 start, u32 cnt, 
   }
 }
 
-// Bin q (descending position; bin kBins - 1 - q) belongs to workgroup q mod G, and
-// within it to wavefront (q / G) mod 4: the heavy bins, which are neighbours (next to
-// tau on skewed inputs), go to different workgroups.  Bins of up to kWaveMax keys are
-// sorted by their wavefront in registers; larger ones by the whole workgroup, after
-// its wavefronts are done: the counting pass above up to kBinCap keys, else the
-// partition by 12-bit digits.
-constexpr u32 kPrefetch = 4;  // bins whose extent a wavefront loads at once
+// Wavefront w of the launch takes output chunk w: the bins that start in positions
+// [w P, (w + 1) P), from the chunk boundaries the scan wrote, so that every wavefront
+// sorts about P keys whatever the bins' sizes.  Ranges of up to kWaveMax keys are
+// sorted in registers; a last bin beyond that goes to the whole workgroup after its
+// wavefronts are done (at most one per wavefront): the counting pass above up to
+// kBinCap keys, else the partition by 12-bit digits.
 
 __global__ __launch_bounds__(kSortThreads) void refine_binsort_kernel(RefineArgs a) {
   __shared__ u64 s[kBinCap];
-  __shared__ u32 s_big[kSortThreads];
+  __shared__ uint4 s_big[kSortThreads / kWave];  // {start, end, position} of the block's heavy bins
   __shared__ u32 s_nbig;
   __shared__ MsdLds s_msd;
   __shared__ HeavyLds s_heavy;
+  constexpr u32 kWaves = kSortThreads / kWave;
+  const u32 lane = lane_id();
+  const u32 wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  // this wavefront's chunk boundaries, loaded with the control block (they are only
+  // used when the scan wrote them: a live attempt with no oversized bin).  A workgroup
+  // takes four consecutive chunks (dealing them out across the workgroups, so that the
+  // heavy bins near b* meet different workgroups, measured slower: their counting
+  // passes then share every CU's LDS at once).
+  const u32 m = blockIdx.x * kWaves + wid;
+  const uint4* ch = reinterpret_cast<const uint4*>(a.chunk);
+  const uint4 c0 = ch[m], c1 = ch[m + 1];
   {  // leave the histogram and the sampler's hash set zero for the next attempt
     const u64 gt = (u64)blockIdx.x * blockDim.x + threadIdx.x, gs = (u64)gridDim.x * blockDim.x;
     for (u64 i = gt; i < kBins; i += gs) a.hist[i] = 0;
+    if (gt == 0 && a.ticket) *a.ticket = 0;  // refine_bin_kernel's counter
     if (a.table)
       for (u64 i = gt; i < a.table_slots; i += gs) a.table[i] = 0;
   }
@@ -585,64 +869,70 @@ __global__ __launch_bounds__(kSortThreads) void refine_binsort_kernel(RefineArgs
     }
   }
   if (!refine_live(a, c) || c->generic) return;
-  const u32 qmax = kBins - 1u - c->bstar;
   const u64 k = a.k;
-  const u32 lane = lane_id();
-  const u32 wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  constexpr u32 kWaves = kSortThreads / kWave;
-  const u32 G = gridDim.x;
-  if (threadIdx.x == 0) s_nbig = 0;
-  __syncthreads();
-  for (u32 i = wid; blockIdx.x + (u64)G * i <= qmax; i += kWaves * kPrefetch) {
-    u32 cnt[kPrefetch], start[kPrefetch], bin[kPrefetch];
-#pragma unroll
-    for (u32 r = 0; r < kPrefetch; ++r) {  // unconditional loads, all in flight
-      const u64 q = blockIdx.x + (u64)G * (i + kWaves * r);
-      bin[r] = q <= qmax ? kBins - 1u - (u32)q : kBins;
-      const u32 bl = bin[r] < kBins ? bin[r] : kBins - 1u;
-      cnt[r] = a.bin_cnt[bl];
-      start[r] = a.bin_off[bl];
-    }
-    // the keys of every light bin of the group in flight before the first sort
-    static_assert(kWaveMax <= 4 * kWave, "light bins take at most 4 keys per lane");
-    u64 v[kPrefetch][4];
-    u32 n[kPrefetch];
-#pragma unroll
-    for (u32 r = 0; r < kPrefetch; ++r) {
-      n[r] = bin[r] < kBins ? cnt[r] : 0u;
-      if (start[r] >= k || start[r] + (u64)n[r] > a.M) n[r] = 0;  // uniform per wavefront
-      const bool light = n[r] <= kWaveMax;
-#pragma unroll
-      for (u32 j = 0; j < 4; ++j) {
-        const u32 e = j * kWave + lane;
-        v[r][j] = light && e < n[r] ? a.tmp[start[r] + e] : 0ull;
-      }
-    }
-#pragma unroll
-    for (u32 r = 0; r < kPrefetch; ++r) {
-      if (n[r] == 0) continue;
-      if (n[r] > kWaveMax) {
-        if (lane == 0) s_big[atomicAdd(&s_nbig, 1u)] = bin[r];  // the block meets at most kSortThreads bins
-        continue;
-      }
-      if (n[r] <= kWave) light_sort<1>(a, v[r], n[r], start[r]);
-      else if (n[r] <= 2 * kWave) light_sort<2>(a, v[r], n[r], start[r]);
-      else light_sort<4>(a, v[r], n[r], start[r]);
-    }
-  }
-  __syncthreads();
-  const u32 nbig = s_nbig;
   const u64 tau = c->tau;
   const u32 width = c->bin_shift;
   const u32 sub = width > 8u ? width - 8u : 0u;
+  if (threadIdx.x == 0) s_nbig = 0;
+  __syncthreads();
+  {
+    // The chunk's bins occupy tmp[rs, re).  Every bin but the last holds fewer than
+    // kChunkKeys keys (it starts and ends inside the chunk); the last one, [ls, re),
+    // may run past it.  Up to kWaveMax keys: one sort of the whole range (the bins are
+    // ordered, so sorting them together sorts each); else the bins before the last,
+    // then the last one if it is light, or the workgroup takes it below.
+    const u32 rs = c0.y, re = c1.y, ls = c1.x;
+    u32 st[2] = {rs, ls}, n[2] = {0u, 0u};
+    bool heavy = false;
+    if (re > rs && rs < k && re <= a.M) {
+      if (re - rs <= kWaveMax) {
+        n[0] = re - rs;
+      } else {
+        n[0] = ls - rs;
+        if (ls < k) {
+          if (re - ls <= kWaveMax) n[1] = re - ls;
+          else heavy = true;
+        }
+      }
+    }
+    static_assert(kWaveMax == 4 * kWave && kChunkKeys <= kWaveMax, "light ranges take 4 keys per lane");
+    u64* wl = s + wid * kWaveLds;
+    u64 v[2][4];
+#pragma unroll
+    for (u32 r = 0; r < 2; ++r)
+#pragma unroll
+      for (u32 j = 0; j < 4; ++j) {
+        const u32 e = j * kWave + lane;
+        v[r][j] = e < n[r] ? a.tmp[st[r] + e] : 0ull;
+      }
+    // one range at a time from the front, which then moves up: one copy of each sort
+#pragma unroll 1
+    for (u32 r = 0; r < 2; ++r) {
+      const u32 nn = n[0], s0 = st[0];
+      const u64 cur[4] = {v[0][0], v[0][1], v[0][2], v[0][3]};
+      n[0] = n[1];
+      st[0] = st[1];
+#pragma unroll
+      for (u32 j = 0; j < 4; ++j) v[0][j] = v[1][j];
+      n[1] = 0;
+      if (nn == 0) continue;
+      if (nn <= kWave) light_sort<1>(a, cur, nn, s0);
+      else if (!wave_range_sort<4>(a, cur, nn, s0, tau, sub, wl)) {
+        if (nn <= 2 * kWave) light_sort<2>(a, cur, nn, s0);
+        else light_sort<4>(a, cur, nn, s0);
+      }
+    }
+    if (heavy && lane == 0) s_big[atomicAdd(&s_nbig, 1u)] = make_uint4(ls, re, c1.z, 0u);
+  }
+  __syncthreads();
+  const u32 nbig = s_nbig;
   for (u32 q = 0; q < nbig; ++q) {
-    const u32 b = s_big[q];
-    const u32 cnt = a.bin_cnt[b];
-    const u32 start = a.bin_off[b];
+    const uint4 h = s_big[q];
+    const u32 start = h.x, cnt = h.y - h.x;
     if (cnt <= kBinCap)
       heavy_part(a, s, &s_heavy, start, cnt, tau, sub);
     else
-      msd_bin(a, s, b, start, cnt, width, tau, &s_msd);
+      msd_bin(a, s, kBins - 1u - h.z, start, cnt, width, tau, &s_msd);
   }
 }
 
@@ -824,6 +1114,16 @@ hipError_t launch_refine(const RefineArgs& a, hipStream_t s) {
     refine_small_kernel<<<G + (u32)(z < 256 ? z : 256), kSmallThreads, 0, s>>>(a, G);
     return hipGetLastError();
   }
+  // the bin sort: four workgroups per CU, and enough wavefronts for chunks of at most
+  // kChunkKeys keys (the needed bins hold T <= M keys, and T < k + msd_cap, since a
+  // needed bin beyond msd_cap keys takes the multi-pass refinement)
+  const u64 tmax = a.k + (u64)a.msd_cap < a.M ? a.k + a.msd_cap : a.M;
+  u64 gs = 4ull * device_cu_count();
+  if (gs > kSortBlocksCap) gs = kSortBlocksCap;
+  const u64 gneed = (tmax + 4ull * kChunkKeys - 1) / (4ull * kChunkKeys);
+  if (gs < gneed) gs = gneed;
+  RefineArgs b = a;
+  b.sort_waves = (u32)(4 * gs);
   // about 4 candidates per thread at R = M (R is mostly well below M): more blocks keep
   // more candidate loads in flight, but each adds its nonzero bins to the global
   // histogram and reserves its runs with atomics (measured on MI355X over 2^30 Pareto
@@ -831,13 +1131,19 @@ hipError_t launch_refine(const RefineArgs& a, hipStream_t s) {
   u32 gh = (u32)((a.M + 4095) / 4096);
   if (gh < 1) gh = 1;
   if (gh > 128) gh = 128;
-  refine_hist_kernel<<<gh, kHistThreads, 0, s>>>(a);
-  refine_scatter_kernel<<<gh, kHistThreads, 0, s>>>(a);
-  // at least 64 workgroups: a workgroup then owns at most kBins / 64 = kSortThreads
-  // bins (s_big)
-  u32 gs = 4 * device_cu_count();
-  if (gs < 64) gs = 64;
-  refine_binsort_kernel<<<gs, kSortThreads, 0, s>>>(a);
+  if (a.approx) {
+    refine_hist_kernel<<<gh, kHistThreads, 0, s>>>(b);
+    refine_scatter_kernel<<<gh, kHistThreads, 0, s>>>(b);
+  } else {
+    // one block per two CUs at most: every block of the fused launch is resident
+    u32 half = device_cu_count() / 2;
+#ifdef PROFK_BIN_GRID
+    if (half > PROFK_BIN_GRID) half = PROFK_BIN_GRID;
+#endif
+    if (gh > half) gh = half > 0 ? half : 1;
+    refine_bin_kernel<<<gh, kHistThreads, 0, s>>>(b);
+  }
+  refine_binsort_kernel<<<(u32)gs, kSortThreads, 0, s>>>(b);
   return hipGetLastError();
 }
 

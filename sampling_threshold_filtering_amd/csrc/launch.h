@@ -161,6 +161,15 @@ constexpr u32 kWaveBin = 1u << kWaveBinBits;
 // Work-list entries (start | count << 32) of the in-kernel partition of oversized
 // bins: two lists per oversized bin, at most kBins + M / kWaveBin + 2 pairs in all.
 __host__ __device__ inline u64 msd_pool_words(u64 M) { return 2 * (M / kWaveBin + kBins + 2); }
+// The bin sort's wavefront w sorts the bins that start in output positions
+// [w P, (w + 1) P), P = ceil(T / W) for the T keys of the needed bins.  Chunk boundary m
+// (0 <= m <= W) holds {start, end, descending position} of the bin that holds position
+// m P - 1 ({T, T, -} past T).  The launch makes W >= T_max / kChunkKeys, so that the bins
+// before the last one of a chunk hold fewer than kChunkKeys keys; at most kSortBlocksCap
+// workgroups of four wavefronts beyond that.
+constexpr u32 kChunkKeys = 128;
+constexpr u32 kSortBlocksCap = 1024;
+__host__ __device__ inline u64 chunk_entries(u64 M) { return 4ull * kSortBlocksCap + M / kChunkKeys + 8; }
 
 struct RefineArgs {
   RowCtl* ctl;
@@ -171,8 +180,8 @@ struct RefineArgs {
   const float* x;   // the row (outputs copy x[idx])
   u64* tmp;         // M keys: candidates of bins >= b* in bin order
   u32* hist;        // kBins, zero on entry, left zero
-  u32* bin_off;     // kBins
-  u32* bin_cnt;     // kBins
+  u32* chunk;       // chunk_entries(M) x 4 words: the bin sort's output chunks (below)
+  u32 sort_waves;   // W, wavefronts of the bin sort; set by launch_refine
   u32* cursor;      // kBins
   u32* table;       // sampler hash set cleared by the last launch, or nullptr
   u64 table_slots;
@@ -185,7 +194,9 @@ struct RefineArgs {
   float* out_vals;
   int64_t* out_idx;
   u64* pool;        // msd_pool_words(M) words: work lists of the oversized-bin partition
-  u32* ticket;      // zero, left zero: the one-launch refinement's last-block election
+  u32* ticket;      // zero, left zero: the one-launch refinement's last-block election, the
+                    // fused histogram-and-scatter launch's counter
+  u64 wait_ticks;   // bound on that launch's wait for its blocks (100 MHz clock ticks)
   u32 msd_cap;      // largest needed bin partitioned in-kernel; larger ones defer to the
                     // multi-pass refinement (the host reads the flag)
   u32 approx;       // 1: no run-time check (approximate mode): refine whatever the buffer
