@@ -81,6 +81,11 @@ typedef struct profk_options {
                              k/N > 2^-10; defaults s_min = 2^12, s_max = 2^17) */
   double cost_a, cost_b;  /* PROFK_S_RULE_COST_MODEL: 1/r(k) = cost_a log2(k) - cost_b for k > 2^7 (P1 App.
                              E.1); both <= 0: the page's calibration, 0.594 and 4.29 */
+  int64_t refine_wait_ticks; /* exact mode, k > 64: bound on the refinement's one wait for all of its
+                             workgroups, in ticks of the device's 100 MHz clock (0: 25,000,000,
+                             i.e. 0.25 s); a wait that runs out sends the attempt to the multi-pass
+                             refinement (same result).  < 0: the wait counts as run out at once
+                             (a hook for tests of that path) */
 } profk_options;
 
 #define PROFK_PARAMS_EXACT 0

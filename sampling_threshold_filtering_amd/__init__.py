@@ -54,6 +54,7 @@ class Options(ctypes.Structure):
         ("s_rule", ctypes.c_int32),
         ("cost_a", ctypes.c_double),
         ("cost_b", ctypes.c_double),
+        ("refine_wait_ticks", ctypes.c_int64),
     ]
 
 

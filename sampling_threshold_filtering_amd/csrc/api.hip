@@ -484,8 +484,9 @@ u32 filter_shape(const profk_params& p, u64 N) {
 
 // One sampled attempt of one row, enqueued; returns after the record is back.
 int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, const profk_params& p, u64 seed,
-                u32 attempt, float* out_vals, int64_t* out_idx, hipStream_t s, bool timing, AttemptRecord* out_rec,
-                float* filter_ms) {
+                u32 attempt, float* out_vals, int64_t* out_idx, hipStream_t s, const profk_options* opt,
+                AttemptRecord* out_rec, float* filter_ms) {
+  const bool timing = opt && opt->timing;
   RowCtl* ctl = at<RowCtl>(w, L.ctl);
   SelState* sel = at<SelState>(w, L.sel);
   AttemptRecord* rec = at<AttemptRecord>(w, L.rec);
@@ -520,6 +521,8 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   // such bins (one workgroup per bin: milliseconds for a 10^5-key tie group) is left to
   // approximate mode, which has no host.
   const bool one = refine_one_launch(ra);
+  if (opt && opt->refine_wait_ticks)
+    ra.wait_ticks = opt->refine_wait_ticks > 0 ? (u64)opt->refine_wait_ticks : 0ull;  // 0: at once
   ra.msd_cap = one ? kMsdCapExact : kBinCap;
   ra.early_cap = one ? kMsdCapExact : 0;  // the same cap wait_record applies to the early word
   HIPCHK(launch_refine(ra, s), "launch refine");
@@ -579,7 +582,7 @@ int topk_row(const float* x, u64 N, u64 k, double eps, u64 seed, float* out_vals
     for (int a = 0; a < max_att; ++a) {
       AttemptRecord r{};
       float fms = 0.f;
-      rc = run_attempt(w, L, x, N, k, p, seed, (u32)a, out_vals, out_idx, s, opt && opt->timing, &r, &fms);
+      rc = run_attempt(w, L, x, N, k, p, seed, (u32)a, out_vals, out_idx, s, opt, &r, &fms);
       if (rc) return rc;
       if (st) {
         st->attempts = a + 1;

@@ -316,7 +316,12 @@ constexpr u32 kKeep = 16;  // candidates per thread refine_bin_kernel keeps in r
 // block could not be made resident) marks the counter, which only succeeds while some
 // block has not arrived, so no block can have passed it yet; every block then sees the
 // mark, the late ones in the value their own arrival returns.  True: all arrived.
+// limit = 0: the wait counts as run out at once (every block marks the counter).
 __device__ bool grid_wait(u32* ctr, u32 G, u64 limit) {
+  if (limit == 0) {  // the wait counts as run out at once (every block marks the counter)
+    __hip_atomic_fetch_or(ctr, kGridMark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
+  }
   u32 v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   const u64 t0 = wall_clock64();
   while (v < G) {

@@ -196,7 +196,8 @@ struct RefineArgs {
   u64* pool;        // msd_pool_words(M) words: work lists of the oversized-bin partition
   u32* ticket;      // zero, left zero: the one-launch refinement's last-block election, the
                     // fused histogram-and-scatter launch's counter
-  u64 wait_ticks;   // bound on that launch's wait for its blocks (100 MHz clock ticks)
+  u64 wait_ticks;   // bound on that launch's wait for its blocks (100 MHz clock ticks; 0: the
+                    // wait counts as run out at once)
   u32 msd_cap;      // largest needed bin partitioned in-kernel; larger ones defer to the
                     // multi-pass refinement (the host reads the flag)
   u32 approx;       // 1: no run-time check (approximate mode): refine whatever the buffer

@@ -205,6 +205,23 @@ def test_binned_and_multipass_refinement_both_run():
     assert st["refine_multipass"] >= 1
 
 
+@pytest.mark.parametrize("kind,log2n,k", [("normal", 22, 3000), ("pareto", 24, 1 << 15)])
+def test_refinement_wait_that_runs_out_takes_the_multipass_refinement(kind, log2n, k):
+    """The fused histogram-and-scatter launch waits once for all of its workgroups; a wait
+    that runs out (forced here from the host) must leave no key placed and send the attempt
+    to the multi-pass refinement, and the next call must find the launch-wide counter clear."""
+    say("refinement wait runs out", kind, log2n, k)
+    x = generate(kind, 1 << log2n, seed=44)
+    xd = dev(x)
+    vals, idx, st = stf.topk(xd, k, seed=5, options={"refine_wait_ticks": -1}, stats=True)
+    check_topk(x, vals, idx, k)
+    assert st["refine_multipass"] == st["attempts"] >= 1
+    for _ in range(2):
+        vals, idx, st = stf.topk(xd, k, seed=5, stats=True)
+        check_topk(x, vals, idx, k)
+        assert st["refine_multipass"] == 0
+
+
 @pytest.mark.parametrize("kind,log2n,k", [("adv_levels", 26, 1 << 15), ("adv_levels", 24, 5000),
                                          ("adv_levels", 26, 64)])
 def test_tie_groups_in_single_bins_take_the_multipass_select(kind, log2n, k):
