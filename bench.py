@@ -643,6 +643,12 @@ def main():
     if "flat" in want:
         per_k = {}
         filt_bytes = filt_ms = total_ms = 0.0
+        # warm-up steps: whole sweeps over the k values first (the first ~20 calls on a
+        # fresh process run 1-1.5% slower while the GPU settles), then per k below
+        for w in range(args.warmup):
+            for k in KS:
+                stf.topk(xds[w % len(xds)], k, eps=EPS, seed=2000 + w, options=opts, out=out_pair(torch, dev, k))
+        torch.cuda.synchronize()
         for k in KS:
             out = out_pair(torch, dev, k)
             # K calls back to back, bracketed by events on the stream (each call waits

@@ -173,6 +173,12 @@ def _stream_ptr(torch, device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _raw_stream(torch, index: int) -> int:
+    """The current stream of device `index` as a raw handle (no Stream object is built:
+    the per-call host time matters where the call returns before the GPU work ends)."""
+    return torch._C._cuda_getCurrentRawStream(index)
+
+
 def _check_out(out, shape, device):
     import torch
     vals, idx = out
@@ -193,20 +199,19 @@ def topk(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, stats: bool 
     if not x.is_contiguous():
         x = x.contiguous()
     lib = _lib if _lib is not None else load_library()
-    dev = x.device
+    di = x.get_device()
     if out is None:
-        vals = torch.empty(k, dtype=torch.float32, device=dev)
-        idx = torch.empty(k, dtype=torch.int64, device=dev)
+        vals = torch.empty(k, dtype=torch.float32, device=x.device)
+        idx = torch.empty(k, dtype=torch.int64, device=x.device)
     else:
-        vals, idx = _check_out(out, (k,), dev)
+        vals, idx = _check_out(out, (k,), x.device)
     st = Stats() if stats else None
-    args = (ctypes.c_void_p(x.data_ptr()), x.numel(), k, eps, seed & (2**64 - 1), ctypes.c_void_p(vals.data_ptr()),
-            ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream),
-            _opt_ptr(options), ctypes.byref(st) if st is not None else None)
-    if dev.index == torch.cuda.current_device():
+    args = (x.data_ptr(), x.numel(), k, eps, seed & (2**64 - 1), vals.data_ptr(), idx.data_ptr(),
+            _raw_stream(torch, di), _opt_ptr(options), ctypes.byref(st) if st is not None else None)
+    if di == torch._C._cuda_getDevice():
         rc = lib.profk_topk_ex(*args)
     else:
-        with torch.cuda.device(dev):
+        with torch.cuda.device(di):
             rc = lib.profk_topk_ex(*args)
     _check(rc)
     if stats:
@@ -242,6 +247,7 @@ def _topk_approx(entry, x, k, eps, seed, options, out, info):
         x = x.contiguous()
     lib = _lib if _lib is not None else load_library()
     dev = x.device
+    di = x.get_device()
     if out is None:
         vals = torch.empty(k, dtype=torch.float32, device=dev)
         idx = torch.empty(k, dtype=torch.int64, device=dev)
@@ -251,14 +257,13 @@ def _topk_approx(entry, x, k, eps, seed, options, out, info):
         info = torch.empty(APPROX_INFO_WORDS, dtype=torch.int64, device=dev)
     elif info.dtype != torch.int64 or info.numel() < APPROX_INFO_WORDS or info.device != dev:
         raise ValueError("info must be an int64 device tensor of 3 words on the input's device")
-    args = (ctypes.c_void_p(x.data_ptr()), x.numel(), k, eps, seed & (2**64 - 1), ctypes.c_void_p(vals.data_ptr()),
-            ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(info.data_ptr()),
-            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream), _opt_ptr(options))
+    args = (x.data_ptr(), x.numel(), k, eps, seed & (2**64 - 1), vals.data_ptr(), idx.data_ptr(), info.data_ptr(),
+            _raw_stream(torch, di), _opt_ptr(options))
     fn = getattr(lib, entry)
-    if dev.index == torch.cuda.current_device():
+    if di == torch._C._cuda_getDevice():
         rc = fn(*args)
     else:
-        with torch.cuda.device(dev):
+        with torch.cuda.device(di):
             rc = fn(*args)
     _check(rc)
     return vals, idx, info

@@ -123,6 +123,8 @@ Layout make_layout(u64 B, u64 S, u64 M, u64 k, u64 scratch_words, u64 hash_cap, 
   return L;
 }
 
+constexpr u32 kWeightSets = 4;  // die-weight sets, one per filter launch shape (0..3)
+
 struct Workspace {
   int device = -1;
   hipStream_t stream = nullptr;
@@ -142,8 +144,15 @@ struct Workspace {
   bool dirty = false;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   // Relative streaming speed of each die, from the filter's per-die times on earlier
-  // calls (moving average); the filter sizes the dies' shares of the input by it.
-  float xw[kXcds] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+  // calls (moving average); the filter sizes the dies' shares of the input by it.  One
+  // set per filter launch shape (blocks per CU and tile width change the dies' relative
+  // speeds), shared by the flat and the multi-row filter.
+  float xw[kWeightSets][kXcds];
+  u32 xw_updates[kWeightSets] = {};  // calls that have updated each set
+  Workspace() {
+    for (u32 c = 0; c < kWeightSets; ++c)
+      for (u32 x = 0; x < kXcds; ++x) xw[c][x] = 1.f;
+  }
   char* seg = nullptr;  // per-segment top-k lists of inputs of 2^32 values or more
   size_t seg_bytes = 0;
 };
@@ -439,15 +448,19 @@ FilterArgs flat_filter_args(Workspace* w, const Layout& L, const float* x, u64 N
   fa.groups = at<u32>(w, L.ticket) + kTickets;
   // per-die stream times only where the host updates the die weights from them
   fa.xtime = N >= kTimedMinN ? reinterpret_cast<u64*>(at<u32>(w, L.ticket) + kXtimeWord) : nullptr;
-  for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[x];
   fa.rec = at<AttemptRecord>(w, L.rec);
   fa.sels = at<SelState>(w, L.sel);
   return fa;
 }
 
+// The dies' shares for a filter launch of this weight set (its launch shape).
+void set_die_weights(Workspace* w, FilterArgs& fa, u32 set) {
+  for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[set][x];
+}
+
 // Moving average of the dies' streaming speeds from the filter's per-die times of the
 // attempt just read back (a performance hint only: the shares never change results).
-void update_die_weights(Workspace* w, const u64* split) {
+void update_die_weights(Workspace* w, const u64* split, u32 set) {
   const u64* xt = w->hrec->xt;
   if (xt[0] == 0) return;
   double rate[kXcds], mean = 0.0;
@@ -457,15 +470,19 @@ void update_die_weights(Workspace* w, const u64* split) {
     if (work == 0 || xt[1 + x] <= xt[0]) return;  // a die without work or without a time
     // work on die x was in proportion to (its blocks) x (its weight), so its speed per
     // block is in proportion to weight / time
-    rate[x] = (double)w->xw[x] / (double)(xt[1 + x] - xt[0]);
+    rate[x] = (double)w->xw[set][x] / (double)(xt[1 + x] - xt[0]);
     mean += rate[x];
     ++n;
   }
   mean /= n;
+  // the first measurement sets the weights (the dies keep their relative speeds from call
+  // to call); later ones are averaged in
+  const double keep = w->xw_updates[set] == 0 ? 0.0 : 0.5;
+  ++w->xw_updates[set];
   for (u32 x = 0; x < kXcds; ++x) {
-    double v = 0.5 * (double)w->xw[x] + 0.5 * rate[x] / mean;
+    double v = keep * (double)w->xw[set][x] + (1.0 - keep) * rate[x] / mean;
     v = v < 0.5 ? 0.5 : (v > 2.0 ? 2.0 : v);
-    w->xw[x] = (float)v;
+    w->xw[set][x] = (float)v;
   }
   for (u32 x = 0; x < kXcds; ++x) w->hrec->xt[x + 1] = 0;
   w->hrec->xt[0] = 0;
@@ -504,6 +521,7 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   fa.hrec = w->hrec_dev;
   fa.seq = seq;
   fa.sparse = filter_shape(p, N);
+  set_die_weights(w, fa, fa.sparse);
   u64 split[kXcds + 1];
   if (timing) HIPCHK(hipEventRecord(w->ev0, s), "hipEventRecord");
   HIPCHK(launch_filter(fa, 0, s, split), "launch filter");
@@ -531,7 +549,7 @@ int run_attempt(Workspace* w, const Layout& L, const float* x, u64 N, u64 k, con
   bool early = false;
   rc = wait_record(w, s, seq, ra.early_cap, &early);
   if (rc) return rc;
-  if (N >= kTimedMinN) update_die_weights(w, split);
+  if (N >= kTimedMinN) update_die_weights(w, split, fa.sparse);
   w->host[0].R = w->hrec->R;
   w->host[0].status = w->hrec->status;
   w->host[0].error = w->hrec->error;
@@ -708,6 +726,7 @@ int approx_enqueue(Workspace* w, const Layout& L, const profk_params& p, bool sa
   HIPCHK(launch_sample(sa, s), "launch sample");
   FilterArgs fa = flat_filter_args(w, L, x, N, k, M);
   fa.sparse = filter_shape(p, N);
+  set_die_weights(w, fa, fa.sparse);
   HIPCHK(launch_filter(fa, 0, s), "launch filter");
   RefineArgs ra = refine_args(w, L, x, N, k, M, out_vals, out_idx);
   ra.msd_cap = 0xFFFFFFFFu;  // no host to hand an oversized bin to
@@ -984,10 +1003,10 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
     fa.k = k;
     fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
     fa.groups = at<u32>(w, L.ticket) + kTickets;
-    for (u32 xd = 0; xd < kXcds; ++xd) fa.weight[xd] = w->xw[xd];
     fa.rec = rec;
     fa.sels = nullptr;
     fa.sparse = filter_shape(p, N);
+    set_die_weights(w, fa, fa.sparse);
     fa.hits_per_row = p.E_R;
     // exact mode without statistics: the filter's last block publishes whether every
     // listed row passed into pinned host memory, and when they all did the call returns
@@ -1013,7 +1032,7 @@ int topk_batched_rows(const float* x, u64 B, u64 N, u64 ld, u64 k, double eps, u
       bool all_ok = false;
       rc = wait_summary(w, s, seq, &all_ok);
       if (rc) return rc;
-      if (timed) update_die_weights(w, split);
+      if (timed) update_die_weights(w, split, fa.sparse);
       if (all_ok) {
         nrows = 0;
         break;
@@ -1327,7 +1346,7 @@ int profk_stage_filter(const float* x, int64_t N, float tau_val, int64_t tau_idx
   fa.k = 1;
   fa.ticket = at<u32>(w, L.ticket) + kTicketFilter;
   fa.groups = at<u32>(w, L.ticket) + kTickets;
-  for (u32 x = 0; x < kXcds; ++x) fa.weight[x] = w->xw[x];
+  set_die_weights(w, fa, 0);
   fa.rec = nullptr;
   fa.sels = nullptr;
   HIPCHK(launch_filter(fa, 0, s), "launch filter");
