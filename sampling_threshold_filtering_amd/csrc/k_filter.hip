@@ -69,6 +69,13 @@ __device__ __forceinline__ u64 wave_max_u64(u64 v) {
   return v;
 }
 
+// The largest candidate key of this block's ticket group (one row): a u64 on the group
+// counter's 128-byte line; zero, left zero.
+__device__ __forceinline__ u64* group_max(const FilterArgs& a) {
+  const u32 ng = gridDim.x < kFilterGroups ? gridDim.x : kFilterGroups;
+  return reinterpret_cast<u64*>(a.groups + (u64)(blockIdx.x % ng) * kFilterGroupStride + 2);
+}
+
 __device__ __forceinline__ void stage_flush(Stage& st, RowCtl* ctls, u64* cand, u64 M) {
   if (st.n == 0) return;
   wave_lds_sync();
@@ -371,7 +378,7 @@ __device__ __forceinline__ void test_tile(const FilterArgs& a, Stage& st, const 
 template <int U, bool NT, bool FO>
 __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
   __shared__ u64 s_stage[kWavesPerBlock][kStageCap];
-  __shared__ u32 s_last;
+  __shared__ u32 s_last, s_fwd;
   __shared__ u32 s_nfail;  // last block: listed rows whose check failed
   // wave-uniform: tile coordinates, row, threshold live in scalar registers, and their
   // loads wait on the scalar counter, not behind the tile's vector loads
@@ -540,9 +547,15 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
           mx = s_max[v] > mx ? s_max[v] : mx;
         }
       // R's atomic returns, so it is performed before this block's ticket; cmax is
-      // only read by the next kernel
+      // only read by the next kernel.  One row: the block raises its ticket group's
+      // maximum, and the group's last block raises the row's once (where all blocks end
+      // together, on short inputs, one atomic per block on the line of R and cmax
+      // queues them all)
+      // (the group maximum's atomic goes first: the wait for R's result, in issue
+      // order, also covers it, so it is in place before this block's ticket)
+      if (a.nrows == 1) atomicMax(group_max(a), mx);
       const u64 b = atomicAdd(&a.ctls[s_row[w]].R, tot);
-      atomicMax(&a.ctls[s_row[w]].cmax, mx);
+      if (a.nrows != 1) atomicMax(&a.ctls[s_row[w]].cmax, mx);
       for (int v = w; v < kWavesPerBlock; ++v)
         if (s_n[v] && s_row[v] == s_row[w]) s_base[v] += b;
     }
@@ -570,14 +583,30 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     const u32 gsize = (gridDim.x - g + ng - 1) / ng;  // blocks b with b mod ng = g
     u32 last = 0;
     u32* gc = a.groups + (u64)g * kFilterGroupStride;
+    u32 fwd = 0;
     if (atomicAdd(gc, 1u) == gsize - 1) {
       atomic_store_agent(gc, 0u);  // every block of the group has counted: left zero
       last = atomicAdd(a.ticket, 1u) == ng - 1 ? 1u : 0u;
+      fwd = 1;
     }
     s_last = last;
+    s_fwd = fwd;
   }
   __syncthreads();
-  if (!s_last) return;
+  // One row: the group's last block raises the row's maximum by the group's, off the
+  // last block's path to the check (the next kernel reads cmax)
+  auto forward_group_max = [&]() {
+    if constexpr (!FO) {
+      if (threadIdx.x == 0 && s_fwd && a.nrows == 1) {
+        const u64 gm = atomicExch(group_max(a), 0ull);  // the word left zero
+        if (gm) atomicMax(&a.ctls[a.rows ? (u32)a.rows[0] : 0u].cmax, gm);
+      }
+    }
+  };
+  if (!s_last) {
+    forward_group_max();
+    return;
+  }
   __threadfence();
   if (threadIdx.x == 0 && a.xtime) {
     // hand the timing to the host with the attempt record, and leave the words zero
@@ -679,6 +708,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     }
   }
   if (threadIdx.x == 0) atomic_store_agent(a.ticket, 0u);
+  forward_group_max();
 }
 
 namespace {
