@@ -782,7 +782,13 @@ hipError_t launch_filter(const FilterArgs& a, u32 grid, hipStream_t s, u64* spli
   const u64 n = a.N * a.nrows;
   const bool four = (a.sparse == kShapeVeryDenseHits && n >= (1ull << 25)) ||
                     (a.sparse == kShapeDenseHits && n >= (1ull << 29));
-  const u32 bpc = four ? 2 * kFilterBlocksPerCU : kFilterBlocksPerCU;
+#ifndef PROFK_SHORT_FILTER_LOG2
+#define PROFK_SHORT_FILTER_LOG2 23
+#endif
+  // short inputs: one block per CU (the blocks end their streams together, and each adds
+  // to R once)
+  const bool short_in = n <= (1ull << PROFK_SHORT_FILTER_LOG2);
+  const u32 bpc = four ? 2 * kFilterBlocksPerCU : (short_in ? 1u : kFilterBlocksPerCU);
   return launch_filter_shape<4>(a, grid, bpc, s, split_out);
 }
 
