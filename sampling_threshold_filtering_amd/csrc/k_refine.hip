@@ -308,35 +308,51 @@ __global__ __launch_bounds__(kHistThreads) void refine_scatter_kernel(RefineArgs
 }
 
 namespace {
-constexpr u32 kGridMark = 1u << 30;
-constexpr u32 kKeep = 16;  // candidates per thread refine_bin_kernel keeps in registers  // added to the launch-wide counter when a wait ran out
+constexpr u32 kGridMark = 1u << 30;  // added to the launch-wide counter when a wait ran out
+constexpr u32 kGoOffset = 16;        // the go word, u32 words after the counter: the next 128-byte line
+constexpr u32 kKeep = 16;            // candidates per thread refine_bin_kernel keeps in registers
 
 // Thread 0 of each block: arrive at the launch-wide counter ctr (zero on entry) and wait
-// until all G blocks have.  A wait longer than `limit` ticks of the 100 MHz clock (a
-// block could not be made resident) marks the counter, which only succeeds while some
-// block has not arrived, so no block can have passed it yet; every block then sees the
-// mark, the late ones in the value their own arrival returns.  True: all arrived.
-// limit = 0: the wait counts as run out at once (every block marks the counter).
-__device__ bool grid_wait(u32* ctr, u32 G, u64 limit) {
+// until all G blocks have: the last to arrive sets the go word (zero on entry), which
+// the others poll.  A wait longer than `limit` ticks of the 100 MHz clock (a block could
+// not be made resident) marks the counter, which only succeeds while some block has not
+// arrived, so no block can have passed it yet; the marking block tells the waiters
+// through the go word, and the late blocks see the mark in the value their own arrival
+// returns.  True: all arrived.  limit = 0: the wait counts as run out at once (every
+// block marks the counter).
+__device__ bool grid_wait(u32* ctr, u32* go, u32 G, u64 limit) {
   if (limit == 0) {  // the wait counts as run out at once (every block marks the counter)
     __hip_atomic_fetch_or(ctr, kGridMark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return false;
   }
+  // arrivals add to ctr; the last one raises `go` (another line, which the waiters poll,
+  // so that their loads do not queue in front of the arrivals' atomics)
   u32 v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  if (v >= kGridMark) return false;
+  if (v == G) {
+    atomic_store_agent(go, 1u);
+    return true;
+  }
   const u64 t0 = wall_clock64();
-  while (v < G) {
+  for (;;) {
+    const u32 g = atomic_load_agent(go);
+    if (g) return g == 1u;
     if (wall_clock64() - t0 >= limit) {
-      u32 seen = v;
-      if (__hip_atomic_compare_exchange_strong(ctr, &seen, v + kGridMark, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT))
-        return false;
-      v = seen;
-      continue;
+      // mark the counter while some block has not arrived (then none has passed), and
+      // tell the other waiters
+      u32 seen = atomic_load_agent(ctr);
+      while (seen < G) {
+        if (__hip_atomic_compare_exchange_strong(ctr, &seen, seen + kGridMark, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)) {
+          atomic_store_agent(go, 2u);
+          return false;
+        }
+      }
+      // every block arrived meanwhile (the last one raises go) or another block marked
+      if (seen >= kGridMark) return false;
     }
     __builtin_amdgcn_s_sleep(1);
-    v = atomic_load_agent(ctr);
   }
-  return v < kGridMark;
 }
 }  // namespace
 
@@ -406,7 +422,7 @@ __global__ __launch_bounds__(kHistThreads) void refine_bin_kernel(RefineArgs a) 
     for (u32 j = 0; j < kPer; ++j) s_pos[j * kHistThreads + tid] = got[j];
   }
   __syncthreads();
-  if (tid == 0) s_ok = grid_wait(a.ticket, gridDim.x, a.wait_ticks) ? 1u : 0u;
+  if (tid == 0) s_ok = grid_wait(a.ticket, a.ticket + kGoOffset, gridDim.x, a.wait_ticks) ? 1u : 0u;
   __syncthreads();
   if (!s_ok) {
     if (blockIdx.x == 0 && tid == 0) {
@@ -852,7 +868,10 @@ __global__ __launch_bounds__(kSortThreads) void refine_binsort_kernel(RefineArgs
   {  // leave the histogram and the sampler's hash set zero for the next attempt
     const u64 gt = (u64)blockIdx.x * blockDim.x + threadIdx.x, gs = (u64)gridDim.x * blockDim.x;
     for (u64 i = gt; i < kBins; i += gs) a.hist[i] = 0;
-    if (gt == 0 && a.ticket) *a.ticket = 0;  // refine_bin_kernel's counter
+    if (gt == 0 && a.ticket) {  // refine_bin_kernel's counter and go word
+      a.ticket[0] = 0;
+      a.ticket[kGoOffset] = 0;
+    }
     if (a.table)
       for (u64 i = gt; i < a.table_slots; i += gs) a.table[i] = 0;
   }
