@@ -607,7 +607,9 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     forward_group_max();
     return;
   }
-  __threadfence();
+  // No fence: what the last block reads from other blocks (R, the die times) it reads
+  // with atomics at the coherence point, and each row's status (written by an earlier
+  // launch) with agent-scope loads; its own writes are read by later launches only.
   if (threadIdx.x == 0 && a.xtime) {
     // hand the timing to the host with the attempt record, and leave the words zero
     for (u32 i = 0; i <= kXcds; ++i) {
@@ -633,7 +635,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
       if (lr < a.nrows) {
         rowv[q] = rc.lrow[lr];
         Rv[q] = atomicAdd(&a.ctls[rowv[q]].R, 0ull);  // read at the coherence point
-        sv[q] = a.ctls[rowv[q]].status;
+        sv[q] = atomic_load_agent(&a.ctls[rowv[q]].status);
       }
     }
 #pragma unroll
@@ -671,7 +673,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(FilterArgs a) {
     const u32 row = a.rows ? (u32)a.rows[lr] : (u32)lr;
     RowCtl* c = &a.ctls[row];
     const u64 R = atomicAdd(&c->R, 0ull);  // read at the coherence point
-    u32 status = c->status;
+    u32 status = atomic_load_agent(&c->status);
     if (status == 0) status = R < a.k ? 1u : (R > a.M ? 2u : 0u);
     c->status = status;
     if (status) atomicAdd(&s_nfail, 1u);
