@@ -176,7 +176,15 @@ def _stream_ptr(torch, device):
 def _raw_stream(torch, index: int) -> int:
     """The current stream of device `index` as a raw handle (no Stream object is built:
     the per-call host time matters where the call returns before the GPU work ends)."""
-    return torch._C._cuda_getCurrentRawStream(index)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(index)
+    return torch.cuda.current_stream(index).cuda_stream
+
+
+def _current_device(torch) -> int:
+    get = getattr(torch._C, "_cuda_getDevice", None)
+    return get() if get is not None else torch.cuda.current_device()
 
 
 def _check_out(out, shape, device):
@@ -208,7 +216,7 @@ def topk(x, k: int, eps: float = 1e-3, seed: int = 0, options=None, stats: bool 
     st = Stats() if stats else None
     args = (x.data_ptr(), x.numel(), k, eps, seed & (2**64 - 1), vals.data_ptr(), idx.data_ptr(),
             _raw_stream(torch, di), _opt_ptr(options), ctypes.byref(st) if st is not None else None)
-    if di == torch._C._cuda_getDevice():
+    if di == _current_device(torch):
         rc = lib.profk_topk_ex(*args)
     else:
         with torch.cuda.device(di):
@@ -260,7 +268,7 @@ def _topk_approx(entry, x, k, eps, seed, options, out, info):
     args = (x.data_ptr(), x.numel(), k, eps, seed & (2**64 - 1), vals.data_ptr(), idx.data_ptr(), info.data_ptr(),
             _raw_stream(torch, di), _opt_ptr(options))
     fn = getattr(lib, entry)
-    if di == torch._C._cuda_getDevice():
+    if di == _current_device(torch):
         rc = fn(*args)
     else:
         with torch.cuda.device(di):

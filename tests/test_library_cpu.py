@@ -211,3 +211,24 @@ def test_fast_mode_is_microseconds_and_not_memoised():
         stf.solve((1 << 30) - i, 1 << 15, 1e-3, options=o)  # a new configuration every call
     per_call = (time.perf_counter() - t0) / n
     assert per_call < 200e-6, per_call  # Python marshalling included
+
+
+def test_binding_stream_and_device_fall_back_to_the_public_torch_calls():
+    """The binding reads the current stream and device through torch's private fast calls
+    when they exist, else through the public ones (no GPU needed: stand-in objects)."""
+    import types
+    import sampling_threshold_filtering_amd as stf
+
+    class Stream:
+        cuda_stream = 1234
+
+    public = types.SimpleNamespace(_C=types.SimpleNamespace(),
+                                   cuda=types.SimpleNamespace(current_stream=lambda i: Stream(),
+                                                              current_device=lambda: 3))
+    assert stf._raw_stream(public, 0) == 1234
+    assert stf._current_device(public) == 3
+    private = types.SimpleNamespace(_C=types.SimpleNamespace(_cuda_getCurrentRawStream=lambda i: 77 + i,
+                                                             _cuda_getDevice=lambda: 5),
+                                    cuda=public.cuda)
+    assert stf._raw_stream(private, 2) == 79
+    assert stf._current_device(private) == 5
